@@ -1,0 +1,41 @@
+"""CPU oracle for the scaled narrow-format (FP8) cast.
+
+TEST INFRASTRUCTURE ONLY.  Nothing in the product path may import, call or
+execute this package: only the tests, the smoke check and the CPU-baseline leg
+of the benchmark use it.  It shares no code, table or constant generator with
+the HIP kernels and imports nothing from them.
+
+Two tiers implement the same definitions:
+
+* ``oracle.formats`` / ``oracle.cast`` / ``oracle.policy`` -- tier 0, the
+  specification, in exact rational arithmetic (``fractions.Fraction``) with an
+  explicit sign bit on every value, zero included.
+* ``oracle.bulk`` -- tier 1, the same definitions vectorised with numpy in
+  binary64, where every step used is exact for the inputs it is given (fp32 and
+  bf16 values times powers of two, rounding to an integer with ``np.rint``).
+  Sums are formed exactly and rounded once.
+
+Sources, cited by page title and section throughout:
+
+* [MP-card]  "Mixed Precision FP16/BF16/FP8" (talentme.airsota.com mind-map
+  card), items (1) FP16, (2) BF16, (3) FP8.
+* [Drift]    "what actually breaks low precision training"
+  (aarohigandhi.vercel.app/writing/drift), sections "First, catching myself",
+  "What the measurements said", "The part I would rather not write".
+* [E3]       practice exercise c06/E3, "Worked solution"
+  (deeper.gabrielebattimelli.com).
+* [MaxWin]   "Max-Window Scale Estimation for Near-Lossless HiF8 W8A8
+  Quantization-Aware Training" (gist.science explainer), sections
+  "Experimental Variables" and "Key Contributions".
+* [SP]       "Which parts of a mixed-precision training step must stay in
+  single precision, and why?" (katajob.com).
+
+Pinning: every function here is checked by ``tests/test_oracle_*.py`` against
+facts fixed independently of this code (constants printed on the pages, closed
+forms, library routines such as numpy's float16 and torch's float8 casts,
+brute force and invariants).  One part is not fully pinned: the hysteresis
+semantics of the scale-update state machine beyond its stated properties
+(``oracle.policy``) -- parity unpinned there.
+"""
+
+from .formats import BF16, E4M3, E5M2, FP16, FP32, FORMATS, Fmt, Val  # noqa: F401

@@ -1,0 +1,154 @@
+"""Tier 1 (vectorised binary64) against tier 0 (exact rationals), and the
+exact summation against a library routine (math.fsum, which returns the
+correctly rounded sum)."""
+
+import math
+import random
+
+import numpy as np
+import pytest
+
+from oracle import E4M3, E5M2, Val
+from oracle import bulk
+from oracle import cast as t0
+
+FMTS = [E4M3, E5M2]
+
+
+def _tier0_codes(fmt, x64, K):
+    vals = bulk.to_vals(x64)
+    Ks = np.broadcast_to(np.asarray(K), x64.shape).ravel().tolist()
+    return [t0.cast_element(fmt, v, int(k)) for v, k in zip(vals, Ks)]
+
+
+def _compare(fmt, x64, K):
+    ref = _tier0_codes(fmt, x64, K)
+    codes, clip, uf, nf = bulk.cast_f64(fmt, x64, K)
+    for i, (c, cl, u, n) in enumerate(ref):
+        assert (int(codes.ravel()[i]), bool(clip.ravel()[i]), bool(uf.ravel()[i]),
+                bool(nf.ravel()[i])) == (c, cl, u, n), (float(x64.ravel()[i]), K)
+
+
+@pytest.mark.parametrize("fmt", FMTS, ids=["e4m3", "e5m2"])
+@pytest.mark.parametrize("K", [0, 7, -9, 21, -40, 127, -127])
+def test_all_bf16_patterns(fmt, K):
+    x = bulk.bf16_bits_to_f64(np.arange(65536, dtype=np.uint32).astype(np.uint16))
+    _compare(fmt, x, K)
+
+
+def _fp32_boundary_set(fmt, K):
+    """Every code's value and every midpoint between neighbouring codes,
+    moved to the input scale (times 2^-K), with their fp32 neighbours."""
+    mags = sorted({fmt.decode(c).mag for c in range(128) if fmt.decode(c).kind == "num"})
+    pts = list(mags) + [(a + b) / 2 for a, b in zip(mags, mags[1:])]
+    pts += [fmt.maxval * 2, fmt.maxval + fmt.maxval / 64]
+    xs = []
+    for p in pts:
+        v = np.float32(math.ldexp(float(p), -K))
+        if not np.isfinite(v):
+            continue
+        xs += [np.nextafter(v, np.float32(0)), v, np.nextafter(v, np.float32(np.inf))]
+    xs = np.array(xs, dtype=np.float32)
+    return np.concatenate([xs, -xs]).astype(np.float64)
+
+
+@pytest.mark.parametrize("fmt", FMTS, ids=["e4m3", "e5m2"])
+@pytest.mark.parametrize("K", [0, 3, -17, 60, -100, 140, 127])
+def test_fp32_boundaries(fmt, K):
+    _compare(fmt, _fp32_boundary_set(fmt, K), K)
+
+
+@pytest.mark.parametrize("fmt", FMTS, ids=["e4m3", "e5m2"])
+def test_random_fp32_bits_including_specials(fmt):
+    rng = np.random.default_rng(7)
+    bits = rng.integers(0, 2 ** 32, size=4000, dtype=np.uint64).astype(np.uint32)
+    bits[:8] = [0, 0x80000000, 1, 0x80000001, 0x7F800000, 0xFF800000, 0x7FC00001, 0x007FFFFF]
+    x = bulk.f32_bits_to_f64(bits)
+    for K in (0, 90, -90, 149 + 6):
+        _compare(fmt, x, K)
+
+
+@pytest.mark.parametrize("fmt", FMTS, ids=["e4m3", "e5m2"])
+@pytest.mark.parametrize("rule", ["ocp", "plus1", "ceil"])
+def test_mx_tier0_vs_tier1(fmt, rule):
+    rng = np.random.default_rng(11)
+    rows, cols = 6, 64
+    x = (np.tanh(rng.normal(0, 1.5, rows * cols)) * 2.0 ** rng.integers(-30, 30, rows * cols))
+    x = x.astype(np.float32).astype(np.float64)
+    x[5] = np.inf
+    x[64:96] = 0.0                       # an all-zero block (block 2)
+    x[100] = np.nan
+    x[192:224] = np.nan                  # an all-NaN block (block 6)
+    codes, scales, counts = bulk.cast_mx_f64(fmt, x, cols, rule)
+    c0, s0, n0 = t0.cast_mx(fmt, bulk.to_vals(x), cols, rule)
+    assert codes.tolist() == c0 and scales.tolist() == s0
+    for key in ("n_finite", "n_clip", "n_underflow", "n_nonfinite"):
+        assert counts[key] == n0[key]
+    assert counts["amax"] == float(n0["amax"])
+    assert scales[2] == 0 and scales[6] == 0    # X = -127 for empty blocks
+
+
+@pytest.mark.parametrize("fmt", FMTS, ids=["e4m3", "e5m2"])
+def test_stats_tier0_vs_tier1(fmt):
+    rng = np.random.default_rng(5)
+    x = (rng.standard_t(3, 3000) * 10.0 ** rng.uniform(-3, 3, 3000)).astype(np.float32).astype(np.float64)
+    x[7] = np.inf
+    x[8] = -0.0
+    for K in (4, -3, 20):
+        codes = bulk.cast_f64(fmt, x, K)[0]
+        s1 = bulk.stats_f64(fmt, x, codes, K)
+        s0 = t0.stats(fmt, bulk.to_vals(x), codes.tolist(), K)
+        assert s1 == s0
+
+
+def test_stats_clipped_far_outside_range_is_exact():
+    """An element far above the clip point has an error needing more than
+    53 bits; tier 1 must fall back to exact rationals for it."""
+    x = np.array([2.0 ** 100 + 2.0 ** 77, 1.0, 3.0], dtype=np.float64)
+    assert np.float32(x[0]) == x[0]
+    codes = bulk.cast_f64(E4M3, x, 0)[0]
+    assert bulk.stats_f64(E4M3, x, codes, 0) == t0.stats(E4M3, bulk.to_vals(x), codes.tolist(), 0)
+
+
+def test_stats_from_histogram_matches_elementwise():
+    rng = np.random.default_rng(9)
+    bits = rng.integers(0, 65536, 20000).astype(np.uint16)
+    x = bulk.bf16_bits_to_f64(bits)
+    codes = bulk.cast_f64(E4M3, x, 3)[0]
+    direct = bulk.stats_f64(E4M3, x, codes, 3)
+    hist = np.bincount(bits, minlength=65536)
+    allx = bulk.bf16_bits_to_f64(np.arange(65536).astype(np.uint16))
+    allc = bulk.cast_f64(E4M3, allx, 3)[0]
+    assert bulk.stats_from_histogram(E4M3, allx, allc, 3, hist) == direct
+
+
+def test_exact_sum_matches_fsum():
+    rng = np.random.default_rng(3)
+    for _ in range(5):
+        t = rng.standard_normal(20000) * 10.0 ** rng.uniform(-30, 30, 20000)
+        t[::7] *= -1e12
+        assert float(bulk.exact_sum(t)) == math.fsum(t.tolist())
+    w = rng.integers(0, 1 << 30, 3000)
+    t = rng.standard_normal(3000)
+    rep = np.repeat(t[:40], w[:40] % 50)
+    assert float(bulk.exact_sum(t[:40], w[:40] % 50)) == math.fsum(rep.tolist())
+
+
+@pytest.mark.parametrize("fmt", FMTS, ids=["e4m3", "e5m2"])
+def test_dequant_tier0_vs_tier1(fmt):
+    codes = np.arange(256, dtype=np.uint8)
+    for K in (0, 5, -127, 127, -120, 126, 140):
+        t1 = bulk.dequant_bf16_f64(fmt, codes, K)
+        for c in range(256):
+            assert int(t1[c]) == t0.dequant_bf16(fmt, c, K), (c, K)
+
+
+def test_amax_with_unscale():
+    x = np.array([3.0, -7.5, np.inf, np.nan, 2.0 ** -140], dtype=np.float64)
+    assert bulk.amax_f64(x) == 7.5 == float(t0.amax(bulk.to_vals(x)))
+    assert bulk.amax_f64(x, 16) == 7.5 * 2 ** -16 == float(t0.amax(bulk.to_vals(x), 16))
+    tiny = np.array([2.0 ** -126 * 1.5], dtype=np.float64)         # unscale rounds (subnormal)
+    assert bulk.amax_f64(tiny, 24) == float(t0.amax(bulk.to_vals(tiny), 24))
+    random.seed(1)
+    assert bulk.amax_f64(np.array([np.nan, np.inf])) == 0.0
+    assert t0.count_nonfinite([Val.of(math.nan), Val.of(1.0)]) == 1

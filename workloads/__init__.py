@@ -1,0 +1,100 @@
+"""Seeded synthetic inputs shaped like the workloads the pages describe.
+
+This module generates inputs only.  It holds none of the cast's arithmetic
+and is shared by the tests (which hand the same arrays to the HIP path and to
+the oracle) and by the benchmark.  Every generator is deterministic in its
+seed.  Rounding to the input dtype (fp64 -> fp32 -> bf16, nearest even) is
+done by numpy and torch.
+
+Workloads (standard deviations are the second argument of N(0, s)):
+
+* ``per_tensor_small``: 65,536 fp32 values ~ N(0, 1), seed 101.
+* ``tanh_activations``: a rows x cols bf16 matrix of tanh(N(0, 1.5)) -- tanh
+  outputs pile up just below 1.0, where the OCP block rule clips most
+  ([Drift, "What the measurements said"]).  Seed 102.
+* ``gradient_steps``: 64 fp32 gradient tensors of 2^12 .. 2^22 elements with
+  per-tensor magnitudes 10^U[-10, 2], fresh N(0, 1) values each step and
+  100x spikes on 5% of steps ([MaxWin, "Key Contributions"]: a spike beyond
+  the delayed estimate saturates).  Seed 103.
+* ``heavy_tailed_rows``: 2^30 bf16 values, 262,144 rows of 4096, row r =
+  10^(v_r) * t_3 with v_r ~ U(-3, 3) ([E3, "Worked solution"]: one global
+  scale cannot serve a layer a thousand times smaller).  Seed 105.
+"""
+
+import numpy as np
+import torch
+
+
+def to_bf16_bits(x64: np.ndarray) -> np.ndarray:
+    """fp64 -> fp32 -> bf16 (nearest even at each step), as uint16 bits."""
+    t = torch.from_numpy(np.ascontiguousarray(x64, dtype=np.float64).astype(np.float32))
+    return t.to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+
+
+def per_tensor_small(n: int = 65536, seed: int = 101) -> np.ndarray:
+    return np.random.default_rng(seed).standard_normal(n).astype(np.float32)
+
+
+def tanh_activations(rows: int = 4096, cols: int = 4096, seed: int = 102) -> np.ndarray:
+    z = np.random.default_rng(seed).normal(0.0, 1.5, rows * cols)
+    return to_bf16_bits(np.tanh(z)).reshape(rows, cols)
+
+
+class GradientSteps:
+    """64 fp32 tensors per step; tensor i has 2^(12 + (i mod 11)) elements
+    and log10-magnitude u_i ~ U[-10, 2], drawn once.  Step t draws fresh
+    N(0, 1) values from seed + 1000 t.  Exactly round(5% of steps) spike steps
+    are drawn from steps 1 .. steps-1; on each, one uniformly drawn tensor is
+    multiplied by 100."""
+
+    def __init__(self, n_tensors: int = 64, steps: int = 32, seed: int = 103,
+                 log2_min: int = 12, n_sizes: int = 11):
+        rng = np.random.default_rng(seed)
+        self.seed = seed
+        self.sizes = [1 << (log2_min + (i % n_sizes)) for i in range(n_tensors)]
+        self.log10_mag = rng.uniform(-10.0, 2.0, n_tensors)
+        n_spikes = int(round(0.05 * steps))
+        self.spike_steps = sorted(rng.choice(np.arange(1, steps), n_spikes, replace=False).tolist())
+        self.spike_tensor = {t: int(rng.integers(0, n_tensors)) for t in self.spike_steps}
+        self.steps = steps
+
+    def step(self, t: int):
+        rng = np.random.default_rng(self.seed + 1000 * t)
+        out = []
+        for i, n in enumerate(self.sizes):
+            mag = 10.0 ** self.log10_mag[i]
+            if self.spike_tensor.get(t) == i:
+                mag *= 100.0
+            out.append((mag * rng.standard_normal(n)).astype(np.float32))
+        return out
+
+
+def heavy_tailed_rows(row0: int, nrows: int, cols: int = 4096, seed: int = 105,
+                      chunk_rows: int = 1024) -> np.ndarray:
+    """Rows [row0, row0 + nrows) of the heavy-tailed bf16 matrix, as uint16
+    bits of shape (nrows, cols).  Rows are generated in chunks of
+    ``chunk_rows`` with one child seed per chunk, so any chunk can be
+    regenerated on its own (row0 and nrows must be multiples of it)."""
+    assert row0 % chunk_rows == 0 and nrows % chunk_rows == 0
+    out = np.empty((nrows, cols), dtype=np.uint16)
+    for c in range(nrows // chunk_rows):
+        chunk = row0 // chunk_rows + c
+        rng = np.random.default_rng([seed, chunk])
+        v = rng.uniform(-3.0, 3.0, chunk_rows)
+        t = rng.standard_t(3, (chunk_rows, cols))
+        out[c * chunk_rows:(c + 1) * chunk_rows] = to_bf16_bits(t * (10.0 ** v)[:, None])
+    return out
+
+
+def random_fp32_bits(n: int, seed: int) -> np.ndarray:
+    """Uniform 32-bit patterns (all classes: subnormals, Inf, NaN)."""
+    return np.random.default_rng(seed).integers(0, 1 << 32, n, dtype=np.uint64).astype(np.uint32)
+
+
+def mixed_magnitude_fp32(n: int, seed: int, log2_lo: int = -140, log2_hi: int = 127) -> np.ndarray:
+    """Signed fp32 values with log-uniform magnitudes over [2^lo, 2^hi)."""
+    rng = np.random.default_rng(seed)
+    e = rng.uniform(log2_lo, log2_hi, n)
+    s = rng.choice([-1.0, 1.0], n)
+    with np.errstate(over="ignore"):
+        return (s * np.exp2(e)).astype(np.float32)
