@@ -1,0 +1,217 @@
+/*
+ * libnarrowcast -- the scaled narrow-format (FP8) cast on AMD Instinct
+ * MI355X (gfx950).
+ *
+ * Sources (web pages, cited by title and section):
+ *   [E3]      practice exercise c06/E3, "Worked solution"
+ *             (deeper.gabrielebattimelli.com): which quantity is measured and
+ *             when, the rule that turns it into a scale, what the run claims.
+ *   [MP-card] "Mixed Precision FP16/BF16/FP8" (talentme.airsota.com mind-map
+ *             card), items (1)-(3): formats, loss scaling.
+ *   [Drift]   "what actually breaks low precision training"
+ *             (aarohigandhi.vercel.app/writing/drift), "What the measurements
+ *             said": MX blocks of 32, the OCP rule and +1 headroom, clip and
+ *             bias measurements.
+ *   [MaxWin]  "Max-Window Scale Estimation for Near-Lossless HiF8 W8A8
+ *             Quantization-Aware Training" (gist.science explainer),
+ *             "Experimental Variables": amax estimators.
+ *
+ * Conventions shared by every call
+ * --------------------------------
+ * - Pointers marked (device) are HIP device memory owned by the caller; the
+ *   library allocates nothing and keeps no state between calls.  Pointers
+ *   marked (host) are read during the call only.
+ * - Every call is asynchronous on `stream` (a hipStream_t; NULL is the null
+ *   stream): argument checks happen on the host before anything is enqueued
+ *   and return an error code; results land in device memory and the caller
+ *   synchronises.  Calls on different streams are independent.
+ * - Counts and statistics ACCUMULATE into caller-zeroed buffers (integer
+ *   max/add, fixed-order binary64 sums), so a tensor may be processed in
+ *   several calls.  All integer outputs are deterministic.
+ * - Element data (x, codes, y) must be 16-byte aligned.  n == 0 is a valid
+ *   no-op; any n >= 0 is accepted (ragged tails are handled in the kernels).
+ * - Scale exponents: a per-tensor scale is 2^k -- the cast quantises
+ *   x * 2^k and code q stands for decode(q) * 2^-k.  An MX block exponent is
+ *   X -- elements are quantised as x * 2^-X and stand for decode(q) * 2^X; its
+ *   scale byte is X + 127.  k and X lie in [-127, 127].
+ * - The cast rounds to nearest, ties to even, saturating at the format's
+ *   largest finite value (E4M3: 448, E5M2: 57344 [MP-card, item (3)]).
+ *   NaN inputs become code 0x7F; +-Inf become +-max; a zero keeps its sign.
+ *   clip: finite x with |x * 2^K| > max (the exact product, never the fp32
+ *   one).  underflow: finite nonzero x that rounds to a zero code.
+ */
+#ifndef NARROWCAST_H
+#define NARROWCAST_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  NC_OK = 0,
+  NC_E_ARG = 1,          /* null pointer, negative size, bad policy field */
+  NC_E_ALIGN = 2,        /* element pointer not 16-byte aligned */
+  NC_E_SHAPE = 3,        /* MX: cols not a positive multiple of 32, or n % cols != 0 */
+  NC_E_UNSUPPORTED = 4,  /* unknown enum value */
+  NC_E_HIP = 5,          /* a HIP launch failed */
+  NC_E_WORKSPACE = 6     /* workspace missing or smaller than nc_workspace_bytes() */
+} nc_status;
+
+typedef enum { NC_F32 = 0, NC_BF16 = 1 } nc_dtype;
+typedef enum { NC_E4M3 = 0, NC_E5M2 = 1 } nc_fmt;
+
+/* MX shared-exponent rules for a block with finite amax a = m * 2^e, m in [1,2)
+ * ([Drift, "What the measurements said" and "The part I would rather not
+ * write"]):  OCP (floor based): X = e - emax_F;  PLUS1: one extra bit of
+ * exponent headroom, X = e - emax_F + 1;  CEIL: the scale rounded up, the
+ * smallest X with a * 2^-X <= max_F.  a == 0 gives X = -127. */
+typedef enum { NC_MX_OCP = 0, NC_MX_PLUS1 = 1, NC_MX_CEIL = 2 } nc_mx_rule;
+
+/* amax estimators ([MaxWin, "Experimental Variables"]): CURRENT uses the
+ * amax passed in for this step (the two-pass "current scaling");
+ * MOST_RECENT the last amax pushed into the history; MAX_WINDOW the largest
+ * of the last `window` pushes. */
+typedef enum { NC_EST_CURRENT = 0, NC_EST_MOST_RECENT = 1, NC_EST_MAX_WINDOW = 2 } nc_est;
+
+/* One tensor of a batch (host array of these). */
+typedef struct {
+  const void *x;     /* (device) n input elements, fp32 or bf16; for nc_dequant unused */
+  uint8_t *codes;    /* (device) n FP8 codes: written by the casts, read by dequant/stats */
+  int64_t n;         /* element count, >= 0 */
+  int64_t cols;      /* MX calls only: row length, a multiple of 32 dividing n;
+                        blocks are 32 consecutive elements of a row */
+  uint8_t *scales;   /* MX calls only (device): n / 32 block-scale bytes X + 127,
+                        row-major (rows x cols/32) */
+} nc_tensor;
+
+/* Per-tensor counts (device array, one per tensor; zero before first use). */
+typedef struct {
+  uint64_t n_finite;
+  uint64_t n_clip;
+  uint64_t n_underflow;
+  uint64_t n_nonfinite;  /* > 0 is the tensor's non-finite flag */
+  uint32_t amax_bits;    /* fp32 bits of the largest finite |x| (after unscale),
+                            rounded to nearest even if it falls below fp32's normal range */
+  uint32_t reserved;
+} nc_counts;
+
+/* Per-tensor error statistics over finite elements (device array, zeroed),
+ * e = xhat - x with xhat the exact value the code stands for and x the
+ * (unscaled) input: how much the cast changes the tensor, and separately
+ * which way the change points ([Drift, "What the measurements said"]). */
+typedef struct {
+  double sum_e, sum_abs_e, sum_e2;
+  double sum_dir_e;  /* sum of sign(x) * e: negative when magnitudes shrink */
+  double sum_xe;     /* with sum_x2: the kept fraction 1 + sum_xe / sum_x2 */
+  double sum_x2;
+} nc_stats;
+
+/* Per-tensor scale state (device array; all-zero is a fresh state). */
+typedef struct {
+  int32_t k;            /* scale exponent used by the next cast */
+  uint32_t a_ref_bits;  /* fp32 estimate at the last change of k (hysteresis) */
+  int32_t has_ref;      /* 0 until the first recompute */
+  int32_t n_hist;       /* valid history entries, <= window */
+  int32_t head;         /* next history slot */
+  int32_t step;         /* history pushes so far */
+} nc_scale_state;
+
+/* Loss scale S = 2^s_log2 (device, one per batch). */
+typedef struct {
+  int32_t s_log2;
+  int32_t clean_steps;
+} nc_loss_scale;
+
+/* Scale policy (host).  [E3, "Worked solution"]: watch amax over a window
+ * of steps; largest power of two keeping it at or below the format's max
+ * with a margin; recompute every `interval` steps; hysteresis of a factor of
+ * two.  [MP-card, item (1)]: dynamic loss scaling. */
+typedef struct {
+  int32_t fmt;                /* nc_fmt: the format the scale is for */
+  int32_t est;                /* nc_est */
+  int32_t window;             /* history length W, 1..1024 */
+  int32_t margin;             /* binades of margin, 0..32 */
+  int32_t hysteresis;         /* 0/1 */
+  int32_t interval;           /* recompute every I pushes, >= 1 */
+  int32_t skip_on_nonfinite;  /* 0/1: a batch with any Inf/NaN changes no scale state */
+  int32_t ls_enable;          /* 0/1: run the loss-scale machine */
+  int32_t ls_growth_interval; /* clean steps before S doubles, >= 1 */
+  int32_t ls_log2_min;        /* bounds on s_log2, 0 <= min <= max <= 64 */
+  int32_t ls_log2_max;
+} nc_policy;
+
+/* Per-tensor amax pass ("a pass over the tensor", [E3, "Worked solution"];
+ * the second look at the data that current scaling needs, [MaxWin,
+ * "Experimental Variables"]).  Reads x only.  For each tensor: max-accumulates
+ * amax_bits of |x| * 2^-s over finite elements and adds n_finite and
+ * n_nonfinite into out[i].  ls (device, nullable): unscale by 2^-ls->s_log2.
+ * Input bytes per element: 4 (fp32) or 2 (bf16). */
+nc_status nc_amax(const nc_tensor *t, int32_t count, nc_dtype dtype,
+                  const nc_loss_scale *ls, nc_counts *out, void *stream);
+
+/* Scale update for a batch of `count` tensors ([E3, "Worked solution"];
+ * [MaxWin, "Experimental Variables"]).  in[i] holds tensor i's counts from
+ * the pass just run.  est == CURRENT: k is set from in[i].amax now (no
+ * history).  Otherwise in[i].amax is pushed into tensor i's ring
+ * hist[i*window .. i*window+window-1] (device fp32) and, every `interval`
+ * pushes, k is recomputed from the estimator.  The rule: the largest k in
+ * [-127, 127] with A * 2^k <= max_F * 2^-margin (A == 0 gives 127).
+ * Hysteresis: k is reset when A * 2^k would exceed that bound or when
+ * A <= a_ref / 2, and kept otherwise.  With skip_on_nonfinite, a batch in
+ * which any tensor has n_nonfinite > 0 changes no scale state.  ls
+ * (device, nullable): when policy->ls_enable, halves S on a non-finite batch
+ * and doubles it after ls_growth_interval clean batches, within bounds. */
+nc_status nc_scale_update(const nc_policy *policy, int32_t count, nc_scale_state *st,
+                          float *hist, const nc_counts *in, nc_loss_scale *ls, void *stream);
+
+/* Per-tensor scaled cast ([MP-card, item (3)]; [E3, "Worked solution"]).
+ * Element i of tensor j becomes RNE-sat(x * 2^(st[j].k - s)), s =
+ * ls->s_log2 or 0 -- the loss-scale unscale fused in front ([MP-card, item
+ * (1)]).  Fused: counts (n_finite, n_clip, n_underflow, n_nonfinite) and the
+ * next step's amax (of x * 2^-s) accumulate into out[j].  stats (device,
+ * nullable): also accumulate the error statistics (then ws must hold
+ * nc_workspace_bytes(t, count) bytes).  Bytes per element: in 4|2, out 1. */
+nc_status nc_cast_tensor(const nc_tensor *t, int32_t count, nc_dtype dtype, nc_fmt fmt,
+                         const nc_scale_state *st, const nc_loss_scale *ls, nc_counts *out,
+                         nc_stats *stats, void *ws, size_t ws_bytes, void *stream);
+
+/* MX block-scaled cast ([Drift, "What the measurements said"]): blocks of
+ * 32 consecutive row elements share X from the block's finite amax by
+ * `rule`; codes = RNE-sat(x * 2^-X), scales = X + 127.  Counts, tensor amax
+ * and optional statistics accumulate as in nc_cast_tensor.  Bytes per
+ * element: in 4|2, out 1 + 1/32. */
+nc_status nc_cast_mx(const nc_tensor *t, int32_t count, nc_dtype dtype, nc_fmt fmt,
+                     nc_mx_rule rule, nc_counts *out, nc_stats *stats, void *ws,
+                     size_t ws_bytes, void *stream);
+
+/* Dequantise codes to bf16: y = RNE_bf16(decode(q) * 2^-k) (per-tensor, st
+ * non-NULL) or RNE_bf16(decode(q) * 2^X) (MX, st == NULL, scales read), with
+ * IEEE overflow to +-Inf; NaN codes give 0x7FC0.  y (host array of `count`
+ * device pointers) receives n bf16 values per tensor.  out_dtype must be
+ * NC_BF16.  Bytes per element: in 1 (+1/32), out 2. */
+nc_status nc_dequant(const nc_tensor *t, int32_t count, nc_fmt fmt, const nc_scale_state *st,
+                     void *const *y, nc_dtype out_dtype, void *stream);
+
+/* Error statistics as a separate pass over x and the codes already written
+ * (per-tensor with st, or MX with st == NULL); accumulates into out.  ws must
+ * hold nc_workspace_bytes(t, count) bytes.  Bytes per element: 4|2 + 1
+ * (+1/32). */
+nc_status nc_cast_stats(const nc_tensor *t, int32_t count, nc_dtype dtype, nc_fmt fmt,
+                        const nc_scale_state *st, const nc_loss_scale *ls, nc_stats *out,
+                        void *ws, size_t ws_bytes, void *stream);
+
+/* Workspace bytes the statistics need for this batch (binary64 partial sums
+ * per 4096-element tile, reduced in a fixed order). */
+size_t nc_workspace_bytes(const nc_tensor *t, int32_t count);
+
+/* Static description of a status code. */
+const char *nc_status_string(nc_status s);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* NARROWCAST_H */

@@ -1,0 +1,207 @@
+"""scaled_fp8_casting_amd: the scaled FP8 cast on MI355X (gfx950).
+
+A thin Python binding over libnarrowcast's C-ABI (include/narrowcast.h).
+Functions carry the C names and only marshal arguments: torch tensors
+provide device memory and the current HIP stream; every step of the cast
+runs in the library's HIP kernels.  There is no CPU fallback: calls raise if
+the library is not built or a tensor is not on the GPU.
+
+Device buffers used by the calls, as torch tensors:
+
+* counts: int64 [count, 5] -- n_finite, n_clip, n_underflow, n_nonfinite,
+  then amax (fp32 bits in the low 32 bits of the fifth word);
+* stats:  float64 [count, 6] -- sum e, |e|, e^2, sign(x) e, x e, x^2;
+* state:  int32 [count, 6] -- k, a_ref bits, has_ref, n_hist, head, step;
+* hist:   float32 [count, window];
+* loss scale: int32 [2] -- s_log2, clean_steps.
+"""
+
+import ctypes
+import struct
+from typing import Optional, Sequence
+
+import torch
+
+from . import _lib
+from ._lib import (NC_BF16, NC_E4M3, NC_E5M2, NC_EST_CURRENT, NC_EST_MAX_WINDOW,  # noqa: F401
+                   NC_EST_MOST_RECENT, NC_F32, NC_MX_CEIL, NC_MX_OCP, NC_MX_PLUS1, NcPolicy,
+                   NcTensor)
+
+COUNT_FIELDS = ("n_finite", "n_clip", "n_underflow", "n_nonfinite")
+STAT_FIELDS = ("sum_e", "sum_abs_e", "sum_e2", "sum_dir_e", "sum_xe", "sum_x2")
+STATE_FIELDS = ("k", "a_ref_bits", "has_ref", "n_hist", "head", "step")
+
+FMT = {"e4m3": NC_E4M3, "e5m2": NC_E5M2}
+MX_RULE = {"ocp": NC_MX_OCP, "plus1": NC_MX_PLUS1, "ceil": NC_MX_CEIL}
+EST = {"current": NC_EST_CURRENT, "most_recent": NC_EST_MOST_RECENT, "max_window": NC_EST_MAX_WINDOW}
+
+
+class NarrowcastError(RuntimeError):
+    def __init__(self, status: int, call: str):
+        msg = _lib.load().nc_status_string(status).decode()
+        super().__init__(f"{call}: status {status}: {msg}")
+        self.status = status
+
+
+def _check(status: int, call: str):
+    if status != 0:
+        raise NarrowcastError(status, call)
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.float32:
+        return NC_F32
+    if t.dtype == torch.bfloat16:
+        return NC_BF16
+    raise TypeError(f"input dtype {t.dtype} (float32 or bfloat16 expected)")
+
+
+def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError("device tensor expected (no CPU path)")
+    return t.data_ptr()
+
+
+def _stream(stream) -> Optional[int]:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def tensors(xs: Sequence[Optional[torch.Tensor]], codes: Sequence[Optional[torch.Tensor]],
+            cols: Optional[Sequence[int]] = None, scales: Optional[Sequence[torch.Tensor]] = None,
+            n: Optional[Sequence[int]] = None):
+    """A host array of nc_tensor descriptors (contiguous device tensors)."""
+    count = len(codes)
+    arr = (NcTensor * max(count, 1))()
+    for i in range(count):
+        x = xs[i] if xs is not None else None
+        c = codes[i]
+        for t in (x, c):
+            if t is not None and not t.is_contiguous():
+                raise ValueError("contiguous tensors expected")
+        arr[i].x = _ptr(x) if x is not None and x.numel() else None
+        arr[i].codes = _ptr(c) if c is not None and c.numel() else None
+        arr[i].n = n[i] if n is not None else (x.numel() if x is not None else c.numel())
+        arr[i].cols = cols[i] if cols is not None else 0
+        arr[i].scales = _ptr(scales[i]) if scales is not None and scales[i].numel() else None
+    return arr, count
+
+
+# -- device buffers ---------------------------------------------------------
+
+def new_counts(count: int, device="cuda") -> torch.Tensor:
+    return torch.zeros((count, 5), dtype=torch.int64, device=device)
+
+
+def new_stats(count: int, device="cuda") -> torch.Tensor:
+    return torch.zeros((count, 6), dtype=torch.float64, device=device)
+
+
+def new_state(count: int, device="cuda") -> torch.Tensor:
+    return torch.zeros((count, 6), dtype=torch.int32, device=device)
+
+
+def new_history(count: int, window: int, device="cuda") -> torch.Tensor:
+    return torch.zeros((count, window), dtype=torch.float32, device=device)
+
+
+def new_loss_scale(s_log2: int, device="cuda") -> torch.Tensor:
+    return torch.tensor([s_log2, 0], dtype=torch.int32, device=device)
+
+
+def policy(fmt="e4m3", est="max_window", window=16, margin=0, hysteresis=True, interval=1,
+           skip_on_nonfinite=False, ls_enable=False, ls_growth_interval=2000, ls_log2_min=0,
+           ls_log2_max=24) -> NcPolicy:
+    return NcPolicy(FMT[fmt] if isinstance(fmt, str) else fmt, EST[est] if isinstance(est, str) else est,
+                    window, margin, int(hysteresis), interval, int(skip_on_nonfinite), int(ls_enable),
+                    ls_growth_interval, ls_log2_min, ls_log2_max)
+
+
+def counts_list(counts: torch.Tensor):
+    """Host view of a counts tensor: one dict per tensor (amax as a float)."""
+    rows = counts.cpu().tolist()
+    out = []
+    for r in rows:
+        d = dict(zip(COUNT_FIELDS, r[:4]))
+        d["amax_bits"] = r[4] & 0xFFFFFFFF
+        d["amax"] = struct.unpack("<f", struct.pack("<I", d["amax_bits"]))[0]
+        out.append(d)
+    return out
+
+
+def workspace_bytes(desc, count: int) -> int:
+    return int(_lib.load().nc_workspace_bytes(desc, count))
+
+
+def new_workspace(desc, count: int, device="cuda") -> torch.Tensor:
+    return torch.empty(max(workspace_bytes(desc, count), 8), dtype=torch.uint8, device=device)
+
+
+# -- the C-ABI calls ----------------------------------------------------------
+
+def nc_amax(xs: Sequence[torch.Tensor], out: torch.Tensor, ls: Optional[torch.Tensor] = None,
+            stream=None):
+    desc, count = tensors(xs, [None] * len(xs))
+    dt = _dtype_code(xs[0]) if xs else NC_F32
+    _check(_lib.load().nc_amax(desc, count, dt, _ptr(ls), _ptr(out), _stream(stream)), "nc_amax")
+
+
+def nc_scale_update(pol: NcPolicy, st: torch.Tensor, in_counts: torch.Tensor,
+                    hist: Optional[torch.Tensor] = None, ls: Optional[torch.Tensor] = None,
+                    stream=None):
+    count = st.shape[0]
+    _check(_lib.load().nc_scale_update(ctypes.byref(pol), count, _ptr(st), _ptr(hist),
+                                       _ptr(in_counts), _ptr(ls), _stream(stream)), "nc_scale_update")
+
+
+def nc_cast_tensor(xs: Sequence[torch.Tensor], codes: Sequence[torch.Tensor], fmt, st: torch.Tensor,
+                   out: torch.Tensor, ls: Optional[torch.Tensor] = None,
+                   stats: Optional[torch.Tensor] = None, ws: Optional[torch.Tensor] = None,
+                   stream=None):
+    desc, count = tensors(xs, codes)
+    dt = _dtype_code(xs[0]) if xs else NC_F32
+    f = FMT[fmt] if isinstance(fmt, str) else fmt
+    if stats is not None and ws is None:
+        raise ValueError("stats need a workspace (new_workspace)")
+    _check(_lib.load().nc_cast_tensor(desc, count, dt, f, _ptr(st), _ptr(ls), _ptr(out), _ptr(stats),
+                                      _ptr(ws), ws.numel() if ws is not None else 0, _stream(stream)),
+           "nc_cast_tensor")
+
+
+def nc_cast_mx(xs: Sequence[torch.Tensor], codes: Sequence[torch.Tensor], scales: Sequence[torch.Tensor],
+               cols: Sequence[int], fmt, rule, out: torch.Tensor, stats: Optional[torch.Tensor] = None,
+               ws: Optional[torch.Tensor] = None, stream=None):
+    desc, count = tensors(xs, codes, cols=cols, scales=scales)
+    dt = _dtype_code(xs[0]) if xs else NC_BF16
+    f = FMT[fmt] if isinstance(fmt, str) else fmt
+    r = MX_RULE[rule] if isinstance(rule, str) else rule
+    if stats is not None and ws is None:
+        raise ValueError("stats need a workspace (new_workspace)")
+    _check(_lib.load().nc_cast_mx(desc, count, dt, f, r, _ptr(out), _ptr(stats), _ptr(ws),
+                                  ws.numel() if ws is not None else 0, _stream(stream)), "nc_cast_mx")
+
+
+def nc_dequant(codes: Sequence[torch.Tensor], ys: Sequence[torch.Tensor], fmt,
+               st: Optional[torch.Tensor] = None, scales: Optional[Sequence[torch.Tensor]] = None,
+               cols: Optional[Sequence[int]] = None, stream=None):
+    desc, count = tensors(None, codes, cols=cols, scales=scales)
+    f = FMT[fmt] if isinstance(fmt, str) else fmt
+    yp = (ctypes.c_void_p * max(count, 1))(*[_ptr(y) if y.numel() else None for y in ys])
+    for y in ys:
+        if y.dtype != torch.bfloat16 or not y.is_contiguous():
+            raise TypeError("dequant output must be contiguous bfloat16")
+    _check(_lib.load().nc_dequant(desc, count, f, _ptr(st), yp, NC_BF16, _stream(stream)), "nc_dequant")
+
+
+def nc_cast_stats(xs: Sequence[torch.Tensor], codes: Sequence[torch.Tensor], fmt, out: torch.Tensor,
+                  ws: torch.Tensor, st: Optional[torch.Tensor] = None, ls: Optional[torch.Tensor] = None,
+                  scales: Optional[Sequence[torch.Tensor]] = None, cols: Optional[Sequence[int]] = None,
+                  stream=None):
+    desc, count = tensors(xs, codes, cols=cols, scales=scales)
+    dt = _dtype_code(xs[0]) if xs else NC_F32
+    f = FMT[fmt] if isinstance(fmt, str) else fmt
+    _check(_lib.load().nc_cast_stats(desc, count, dt, f, _ptr(st), _ptr(ls), _ptr(out), _ptr(ws),
+                                     ws.numel(), _stream(stream)), "nc_cast_stats")

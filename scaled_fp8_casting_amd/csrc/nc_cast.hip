@@ -1,0 +1,324 @@
+// Streaming kernels that read the input tensor: the per-tensor amax pass,
+// the per-tensor cast (unscale + cast + counts + next-step amax, optional
+// statistics) and the MX block-scaled cast.
+//
+// Work distribution: a launch covers up to kMaxSeg tensors cut into tiles
+// of 256 threads x four 16-byte loads (4096 fp32 or 8192 bf16 elements).
+// Workgroups stride over the flat tile range; a workgroup keeps per-tensor
+// totals while it stays on one tensor and flushes them with one set of
+// integer atomics when it moves on.  Each 16-byte load instruction of a wave
+// covers 1 KiB of contiguous input and each code store 256-512 B of
+// contiguous output.  A ragged last tile runs the same code with lanes past
+// the end fed zeros (a zero is finite and never counted) and their stores
+// masked, so the wave-ballot counts stay uniform.
+#include "nc_launch.h"
+
+namespace nc {
+namespace {
+
+// ---------------------------------------------------------------------------
+// Per-tensor amax pass.
+template <int DT>
+__global__ void __launch_bounds__(kThreads)
+k_amax(const SegBatch b, const nc_loss_scale* __restrict__ ls, nc_counts* __restrict__ out) {
+  constexpr int VEC = In<DT>::VEC;
+  constexpr int64_t TILE = (int64_t)kThreads * VEC * kUnroll;
+  __shared__ uint32_t lds_max[kWaves];
+  __shared__ uint64_t lds_cnt[kWaves * 3];
+  const int s_log2 = ls ? ls->s_log2 : 0;
+  const int64_t total = b.tile0[b.count];
+  Acc acc;
+  acc.reset();
+  int seg = -1;
+  uint64_t elems = 0;
+  for (int64_t tile = blockIdx.x; tile < total; tile += gridDim.x) {
+    const int s = seg_of(b, tile, seg);
+    if (s != seg) {
+      if (seg >= 0) flush_counts(acc, out + b.first + seg, s_log2, elems, lds_max, lds_cnt);
+      seg = s;
+      elems = 0;
+    }
+    const Seg& g = b.s[s];
+    const int64_t e0 = (tile - b.tile0[s]) * TILE;
+    const int64_t rem = min(g.n - e0, TILE);
+    const u32x4* src = reinterpret_cast<const u32x4*>(static_cast<const uint8_t*>(g.x) + e0 * In<DT>::BYTES);
+    if (rem == TILE) {
+      u32x4 v[kUnroll];
+#pragma unroll
+      for (int u = 0; u < kUnroll; ++u) v[u] = src[u * kThreads + threadIdx.x];
+      __builtin_amdgcn_sched_barrier(0);   // all loads in flight before any use
+#pragma unroll
+      for (int u = 0; u < kUnroll; ++u) {
+        uint32_t xb[VEC];
+        unpack<DT>(v[u], xb);
+#pragma unroll
+        for (int i = 0; i < VEC; ++i) {
+          const uint32_t ax = xb[i] & kAbsMask;
+          const bool nf = ax > kMaxFinite;
+          acc.amax = max(acc.amax, nf ? 0u : ax);
+          const uint64_t c = wave_count(nf);
+          acc.n_nf += c;
+          acc.n_big += c;   // the amax pass reports no clips
+        }
+      }
+    } else {
+      for (int64_t base = 0; base < rem; base += kThreads) {
+        const int64_t i = base + threadIdx.x;
+        const uint32_t ax = (i < rem ? load_one<DT>(g.x, e0 + i) : 0u) & kAbsMask;
+        const bool nf = ax > kMaxFinite;
+        acc.amax = max(acc.amax, nf ? 0u : ax);
+        const uint64_t c = wave_count(nf);
+        acc.n_nf += c;
+        acc.n_big += c;
+      }
+    }
+    elems += rem;
+  }
+  if (seg >= 0) flush_counts(acc, out + b.first + seg, s_log2, elems, lds_max, lds_cnt);
+}
+
+// ---------------------------------------------------------------------------
+// Per-tensor cast: code = RNE-sat(x * 2^(k - s)).
+template <int FMT, int DT, bool STATS>
+__global__ void __launch_bounds__(kThreads)
+k_cast_pt(const SegBatch b, const nc_scale_state* __restrict__ st,
+          const nc_loss_scale* __restrict__ ls, nc_counts* __restrict__ out,
+          double* __restrict__ part) {
+  constexpr int VEC = In<DT>::VEC;
+  constexpr int64_t TILE = (int64_t)kThreads * VEC * kUnroll;
+  __shared__ uint32_t lds_max[kWaves];
+  __shared__ uint64_t lds_cnt[kWaves * 3];
+  __shared__ double lds_st[STATS ? kWaves * 6 : 1];
+  __shared__ uint32_t dec[STATS ? 256 : 1];
+  if constexpr (STATS) {
+    dec[threadIdx.x] = decode_bits<FMT>(threadIdx.x);
+    __syncthreads();
+  }
+  const int s_log2 = ls ? ls->s_log2 : 0;
+  const int64_t total = b.tile0[b.count];
+  Acc acc;
+  acc.reset();
+  StatAcc sa;
+  if constexpr (STATS) sa.reset();
+  int seg = -1, k = 0;
+  CastParams p = cast_params<FMT>(0);
+  uint64_t elems = 0;
+  for (int64_t tile = blockIdx.x; tile < total; tile += gridDim.x) {
+    const int s = seg_of(b, tile, seg);
+    if (s != seg) {
+      if (seg >= 0) flush_counts(acc, out + b.first + seg, s_log2, elems, lds_max, lds_cnt);
+      seg = s;
+      elems = 0;
+      k = st[b.first + s].k;
+      p = cast_params<FMT>(k - s_log2);
+    }
+    const Seg& g = b.s[s];
+    const int64_t e0 = (tile - b.tile0[s]) * TILE;
+    const int64_t rem = min(g.n - e0, TILE);
+    const u32x4* src = reinterpret_cast<const u32x4*>(static_cast<const uint8_t*>(g.x) + e0 * In<DT>::BYTES);
+    uint8_t* dst = g.codes + e0;
+    if (rem == TILE) {
+      u32x4 v[kUnroll];
+#pragma unroll
+      for (int u = 0; u < kUnroll; ++u) v[u] = src[u * kThreads + threadIdx.x];
+      __builtin_amdgcn_sched_barrier(0);   // all loads in flight before any use
+#pragma unroll
+      for (int u = 0; u < kUnroll; ++u) {
+        uint32_t xb[VEC], q[VEC];
+        unpack<DT>(v[u], xb);
+#pragma unroll
+        for (int i = 0; i < VEC; ++i) q[i] = cast_elem<FMT>(xb[i], p, acc);
+        if constexpr (STATS) {
+#pragma unroll
+          for (int i = 0; i < VEC; ++i) stat_elem(xb[i], q[i], s_log2, k, dec, sa);
+        }
+        const int vi = u * kThreads + threadIdx.x;
+        if constexpr (DT == NC_F32) {
+          reinterpret_cast<uint32_t*>(dst)[vi] = q[0] | (q[1] << 8) | (q[2] << 16) | (q[3] << 24);
+        } else {
+          u32x2 w;
+          w.x = q[0] | (q[1] << 8) | (q[2] << 16) | (q[3] << 24);
+          w.y = q[4] | (q[5] << 8) | (q[6] << 16) | (q[7] << 24);
+          reinterpret_cast<u32x2*>(dst)[vi] = w;
+        }
+      }
+    } else {
+      for (int64_t base = 0; base < rem; base += kThreads) {
+        const int64_t i = base + threadIdx.x;
+        const bool act = i < rem;
+        const uint32_t xb = act ? load_one<DT>(g.x, e0 + i) : 0u;
+        const uint32_t q = cast_elem<FMT>(xb, p, acc);
+        if constexpr (STATS) stat_elem(xb, q, s_log2, k, dec, sa);
+        if (act) dst[i] = (uint8_t)q;
+      }
+    }
+    elems += rem;
+    if constexpr (STATS) stats_tile_flush(sa, part + tile * 6, lds_st);
+  }
+  if (seg >= 0) flush_counts(acc, out + b.first + seg, s_log2, elems, lds_max, lds_cnt);
+}
+
+// ---------------------------------------------------------------------------
+// MX: shared block exponent X ([Drift, "What the measurements said"]) from
+// the finite amax a of each 32-element block (a = 0 -> -127).
+template <int FMT>
+__device__ __forceinline__ int mx_exponent(uint32_t a, int rule) {
+  using F = Fp8<FMT>;
+  if (a == 0) return -127;
+  int e;
+  uint32_t frac;
+  if (a >= 0x800000u) {
+    e = (int)(a >> 23) - 127;
+    frac = a & 0x7FFFFFu;
+  } else {  // subnormal fp32 amax: normalise
+    const int lz = __clz(a);
+    e = (31 - lz) - 149;
+    frac = (a << (lz - 8)) & 0x7FFFFFu;
+  }
+  int X = e - F::EMAX;                                   // OCP: floor based
+  if (rule == NC_MX_PLUS1) X += 1;                       // one bit of headroom
+  else if (rule == NC_MX_CEIL) X += (frac > 0x600000u);  // smallest X that fits
+  return min(127, max(-127, X));
+}
+
+// Max over the lanes of one block: 4 lanes (bf16, 8 elements each) or 8
+// lanes (fp32, 4 each), by DPP moves inside rows of the wave.
+template <int GROUP>
+__device__ __forceinline__ uint32_t group_max(uint32_t v) {
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0xB1, 0xF, 0xF, false));  // quad_perm [1,0,3,2]
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x4E, 0xF, 0xF, false));  // quad_perm [2,3,0,1]
+  if constexpr (GROUP == 8)
+    v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x141, 0xF, 0xF, false));  // row_half_mirror
+  return v;
+}
+
+template <int FMT, int DT, bool STATS>
+__global__ void __launch_bounds__(kThreads)
+k_cast_mx(const SegBatch b, const int rule, nc_counts* __restrict__ out, double* __restrict__ part) {
+  constexpr int VEC = In<DT>::VEC;
+  constexpr int GROUP = 32 / VEC;
+  constexpr int64_t TILE = (int64_t)kThreads * VEC * kUnroll;
+  __shared__ uint32_t lds_max[kWaves];
+  __shared__ uint64_t lds_cnt[kWaves * 3];
+  __shared__ double lds_st[STATS ? kWaves * 6 : 1];
+  __shared__ uint32_t dec[STATS ? 256 : 1];
+  if constexpr (STATS) {
+    dec[threadIdx.x] = decode_bits<FMT>(threadIdx.x);
+    __syncthreads();
+  }
+  const int64_t total = b.tile0[b.count];
+  Acc acc;
+  acc.reset();
+  StatAcc sa;
+  if constexpr (STATS) sa.reset();
+  int seg = -1;
+  uint64_t elems = 0;
+  const bool leader = (threadIdx.x % GROUP) == 0;
+  for (int64_t tile = blockIdx.x; tile < total; tile += gridDim.x) {
+    const int s = seg_of(b, tile, seg);
+    if (s != seg) {
+      if (seg >= 0) flush_counts(acc, out + b.first + seg, 0, elems, lds_max, lds_cnt);
+      seg = s;
+      elems = 0;
+    }
+    const Seg& g = b.s[s];
+    const int64_t e0 = (tile - b.tile0[s]) * TILE;
+    const int64_t rem = min(g.n - e0, TILE);      // a multiple of 32
+    const u32x4* src = reinterpret_cast<const u32x4*>(static_cast<const uint8_t*>(g.x) + e0 * In<DT>::BYTES);
+    uint8_t* dst = g.codes + e0;
+    uint8_t* sdst = g.scales + e0 / 32;
+    const bool full = rem == TILE;
+    u32x4 v[kUnroll];
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      const int vi = u * kThreads + threadIdx.x;
+      v[u] = (full || (int64_t)vi * VEC < rem) ? src[vi] : u32x4{0u, 0u, 0u, 0u};
+    }
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      const int vi = u * kThreads + threadIdx.x;
+      const bool act = full || (int64_t)vi * VEC < rem;
+      uint32_t xb[VEC], q[VEC];
+      unpack<DT>(v[u], xb);
+      uint32_t m = 0;
+#pragma unroll
+      for (int i = 0; i < VEC; ++i) {
+        const uint32_t ax = xb[i] & kAbsMask;
+        m = max(m, ax > kMaxFinite ? 0u : ax);
+      }
+      const int X = mx_exponent<FMT>(group_max<GROUP>(m), rule);
+      const CastParams p = cast_params<FMT>(-X);
+#pragma unroll
+      for (int i = 0; i < VEC; ++i) q[i] = cast_elem<FMT>(xb[i], p, acc);
+      if constexpr (STATS) {
+#pragma unroll
+        for (int i = 0; i < VEC; ++i) stat_elem(xb[i], q[i], 0, -X, dec, sa);
+      }
+      if (act) {
+        if constexpr (DT == NC_F32) {
+          reinterpret_cast<uint32_t*>(dst)[vi] = q[0] | (q[1] << 8) | (q[2] << 16) | (q[3] << 24);
+        } else {
+          u32x2 w;
+          w.x = q[0] | (q[1] << 8) | (q[2] << 16) | (q[3] << 24);
+          w.y = q[4] | (q[5] << 8) | (q[6] << 16) | (q[7] << 24);
+          reinterpret_cast<u32x2*>(dst)[vi] = w;
+        }
+        if (leader) sdst[vi / GROUP] = (uint8_t)(X + 127);
+      }
+    }
+    elems += rem;
+    if constexpr (STATS) stats_tile_flush(sa, part + tile * 6, lds_st);
+  }
+  if (seg >= 0) flush_counts(acc, out + b.first + seg, 0, elems, lds_max, lds_cnt);
+}
+
+template <int FMT, int DT>
+hipError_t cast_pt_t(const SegBatch& b, const nc_scale_state* st, const nc_loss_scale* ls,
+                     nc_counts* out, double* part, const Launch& l) {
+  if (part)
+    hipLaunchKernelGGL((k_cast_pt<FMT, DT, true>), dim3(l.grid), dim3(kThreads), 0, l.stream, b, st, ls, out, part);
+  else
+    hipLaunchKernelGGL((k_cast_pt<FMT, DT, false>), dim3(l.grid), dim3(kThreads), 0, l.stream, b, st, ls, out, part);
+  return hipGetLastError();
+}
+
+template <int FMT, int DT>
+hipError_t cast_mx_t(const SegBatch& b, int rule, nc_counts* out, double* part, const Launch& l) {
+  if (part)
+    hipLaunchKernelGGL((k_cast_mx<FMT, DT, true>), dim3(l.grid), dim3(kThreads), 0, l.stream, b, rule, out, part);
+  else
+    hipLaunchKernelGGL((k_cast_mx<FMT, DT, false>), dim3(l.grid), dim3(kThreads), 0, l.stream, b, rule, out, part);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_amax(const SegBatch& b, int dtype, const nc_loss_scale* ls, nc_counts* out,
+                       const Launch& l) {
+  if (dtype == NC_F32)
+    hipLaunchKernelGGL((k_amax<NC_F32>), dim3(l.grid), dim3(kThreads), 0, l.stream, b, ls, out);
+  else
+    hipLaunchKernelGGL((k_amax<NC_BF16>), dim3(l.grid), dim3(kThreads), 0, l.stream, b, ls, out);
+  return hipGetLastError();
+}
+
+hipError_t launch_cast_pt(const SegBatch& b, int dtype, int fmt, const nc_scale_state* st,
+                          const nc_loss_scale* ls, nc_counts* out, double* part, const Launch& l) {
+  if (fmt == NC_E4M3)
+    return dtype == NC_F32 ? cast_pt_t<NC_E4M3, NC_F32>(b, st, ls, out, part, l)
+                           : cast_pt_t<NC_E4M3, NC_BF16>(b, st, ls, out, part, l);
+  return dtype == NC_F32 ? cast_pt_t<NC_E5M2, NC_F32>(b, st, ls, out, part, l)
+                         : cast_pt_t<NC_E5M2, NC_BF16>(b, st, ls, out, part, l);
+}
+
+hipError_t launch_cast_mx(const SegBatch& b, int dtype, int fmt, int rule, nc_counts* out,
+                          double* part, const Launch& l) {
+  if (fmt == NC_E4M3)
+    return dtype == NC_F32 ? cast_mx_t<NC_E4M3, NC_F32>(b, rule, out, part, l)
+                           : cast_mx_t<NC_E4M3, NC_BF16>(b, rule, out, part, l);
+  return dtype == NC_F32 ? cast_mx_t<NC_E5M2, NC_F32>(b, rule, out, part, l)
+                         : cast_mx_t<NC_E5M2, NC_BF16>(b, rule, out, part, l);
+}
+
+}  // namespace nc

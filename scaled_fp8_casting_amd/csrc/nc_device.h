@@ -1,0 +1,332 @@
+// Device-side building blocks of libnarrowcast for CDNA4 (gfx950).
+//
+// The cast of a finite input x at exponent K (the value quantised is
+// y = x * 2^K, formed exactly) is round-to-nearest-even onto the FP8 grid,
+// saturating at the largest finite value ([MP-card, item (3)]: E4M3 max 448,
+// E5M2 max 57344).  It is done in three exact steps:
+//
+//  1. y = ldexp(|x|, K) in fp32.  Exact whenever y is at least fp32's
+//     smallest normal and not above fp32's range.  Outside that: a y above
+//     range is a clip and is replaced below; a y below 2^-126 is far below
+//     half the smallest FP8 subnormal, so its code is zero however it rounds.
+//  2a. Normal FP8 target (y >= 2^emin): re-bias the fp32 exponent and round
+//     the 23-bit mantissa to MB bits on the integer pattern (add half an ulp
+//     minus one plus the kept lsb, then shift); a carry out of the mantissa
+//     moves to the next binade, as it should.
+//  2b. Subnormal FP8 target: y + 2^(emin - MB + 23) in fp32 rounds y to a
+//     multiple of the subnormal quantum 2^(emin - MB) (the float's ulp), and
+//     the difference of the bit patterns is the code.
+//  3. Clip, underflow and non-finite are decided on |x|'s bit pattern
+//     against per-scale thresholds (exact comparisons on the input, never on
+//     the fp32 product).
+//
+// Sources cited by title and section: [MP-card] "Mixed Precision
+// FP16/BF16/FP8", [Drift] "what actually breaks low precision training",
+// [E3] practice exercise c06/E3 "Worked solution", [MaxWin] "Max-Window
+// Scale Estimation for Near-Lossless HiF8 W8A8 Quantization-Aware Training".
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "narrowcast.h"
+
+namespace nc {
+
+constexpr int kThreads = 256;       // 4 wave64s per workgroup
+constexpr int kStatTile = 4096;     // smallest tile: statistics partials are per tile
+constexpr int kMaxSeg = 32;         // tensors per launch (descriptors travel as kernel arguments)
+constexpr int kWaves = kThreads / 64;
+
+// ---------------------------------------------------------------------------
+// Formats.  E4M3: bias 7, no Inf, S.1111.111 is NaN, max 1.75*2^8 = 448.
+// E5M2: bias 15, IEEE specials, max 1.75*2^15 = 57344.  Both maxima are
+// 1.75 * 2^EMAX.
+template <int FMT> struct Fp8;
+template <> struct Fp8<NC_E4M3> {
+  static constexpr int MB = 3, BIAS = 7, EMIN = -6, EMAX = 8;
+  static constexpr uint32_t MAXCODE = 0x7E;
+};
+template <> struct Fp8<NC_E5M2> {
+  static constexpr int MB = 2, BIAS = 15, EMIN = -14, EMAX = 15;
+  static constexpr uint32_t MAXCODE = 0x7B;
+};
+
+constexpr uint32_t kAbsMask = 0x7FFFFFFFu;
+constexpr uint32_t kMaxFinite = 0x7F7FFFFFu;   // |x| bits above this: Inf/NaN
+constexpr uint32_t kInfBits = 0x7F800000u;     // |x| bits above this: NaN
+constexpr uint32_t kNaNCode = 0x7Fu;
+
+// Largest fp32 pattern whose value is <= 1.75 * 2^j (the clip bound at
+// exponent K is 1.75 * 2^(EMAX - K)).
+__host__ __device__ inline uint32_t clip_threshold(int j) {
+  if (j > 127) return kMaxFinite;
+  if (j >= -126) return ((uint32_t)(j + 127) << 23) | 0x600000u;
+  // subnormal range: 1.75 * 2^j = 7 * 2^(j + 147) units of 2^-149
+  const int up = j + 147;
+  if (up >= 0) return 7u << up;
+  return (-up >= 3) ? 0u : (7u >> (-up));
+}
+
+// Largest fp32 pattern whose value is <= 2^j (the underflow bound at
+// exponent K is half the smallest subnormal: 2^(EMIN - MB - 1 - K)).
+__host__ __device__ inline uint32_t pow2_threshold(int j) {
+  if (j > 127) return kMaxFinite;
+  if (j >= -126) return (uint32_t)(j + 127) << 23;
+  if (j >= -149) return 1u << (j + 149);
+  return 0u;
+}
+
+// Thresholds of a cast at exponent K.
+struct CastParams {
+  int K;
+  uint32_t t_clip;  // finite |x| bits > t_clip  <=>  |x| * 2^K > max
+  uint32_t t_uf;    // 0 < |x| bits <= t_uf      <=>  rounds to a zero code
+};
+
+template <int FMT>
+__host__ __device__ inline CastParams cast_params(int K) {
+  using F = Fp8<FMT>;
+  CastParams p;
+  p.K = K;
+  p.t_clip = clip_threshold(F::EMAX - K);
+  p.t_uf = pow2_threshold(F::EMIN - F::MB - 1 - K);
+  return p;
+}
+
+// Magnitude code of a finite |x| that does not clip (steps 1-2 above).
+template <int FMT>
+__device__ __forceinline__ uint32_t encode_mag(uint32_t ax, int K) {
+  using F = Fp8<FMT>;
+  constexpr uint32_t kMinNormalBits = (uint32_t)(F::EMIN + 127) << 23;
+  constexpr uint32_t kMagicBits = (uint32_t)(F::EMIN - F::MB + 23 + 127) << 23;
+  constexpr uint32_t kRebias = (uint32_t)(127 - F::BIAS) << 23;
+  constexpr int kShift = 23 - F::MB;
+  const float y = __builtin_amdgcn_ldexpf(__uint_as_float(ax), K);
+  const uint32_t yb = __float_as_uint(y);
+  const uint32_t lsb = (yb >> kShift) & 1u;
+  const uint32_t qn = (yb + ((1u << (kShift - 1)) - 1u) + lsb - kRebias) >> kShift;
+  const uint32_t qs = __float_as_uint(y + __uint_as_float(kMagicBits)) - kMagicBits;
+  return yb < kMinNormalBits ? qs : qn;
+}
+
+// Per-wave running totals.  The counts come from wave ballots and stay
+// wave-uniform (scalar registers); amax is per lane until the flush.
+struct Acc {
+  uint64_t n_nf;     // non-finite elements
+  uint64_t n_big;    // |x| bits above t_clip: every clip plus every non-finite
+  uint64_t n_uf;
+  uint32_t amax;     // largest finite |x| bits (lane-local)
+  __device__ void reset() { n_nf = n_big = n_uf = 0; amax = 0; }
+};
+
+__device__ __forceinline__ uint64_t wave_count(bool p) {
+  return (uint64_t)__popcll(__ballot(p));
+}
+
+// The full element cast: returns the 8-bit code, updates the wave totals.
+template <int FMT>
+__device__ __forceinline__ uint32_t cast_elem(uint32_t xb, const CastParams& p, Acc& acc) {
+  using F = Fp8<FMT>;
+  const uint32_t ax = xb & kAbsMask;
+  uint32_t q = encode_mag<FMT>(ax, p.K);
+  const bool nf = ax > kMaxFinite;
+  const bool big = ax > p.t_clip;
+  const bool uf = (ax - 1u) < p.t_uf;
+  q = big ? F::MAXCODE : q;                 // saturate clips and +-Inf
+  q |= (xb >> 24) & 0x80u;                  // sign (signed zero included)
+  q = (ax > kInfBits) ? kNaNCode : q;       // NaN: canonical 0x7F
+  acc.amax = max(acc.amax, nf ? 0u : ax);
+  acc.n_nf += wave_count(nf);
+  acc.n_big += wave_count(big);
+  acc.n_uf += wave_count(uf);
+  return q;
+}
+
+// fp32 bits of RNE(value(a) * 2^-s) for finite non-negative a, s >= 0 (the
+// unscaled amax; exact unless the result is below fp32's normal range).
+__host__ __device__ inline uint32_t unscale_bits(uint32_t a, int s) {
+  if (s <= 0 || a == 0) return a;
+  const uint32_t E = a >> 23;
+  if (E > (uint32_t)s) return a - ((uint32_t)s << 23);
+  const uint32_t sig = E ? ((a & 0x7FFFFFu) | 0x800000u) : (a & 0x7FFFFFu);
+  const int sh = s + 1 - (E ? (int)E : 1);   // result in units of 2^-149
+  if (sh > 26) return 0u;
+  const uint32_t half_m1 = (1u << (sh - 1)) - 1u;
+  return (sig + half_m1 + ((sig >> sh) & 1u)) >> sh;
+}
+
+// Wave64 reductions (used at flushes only, never per element).
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+  for (int o = 32; o > 0; o >>= 1) v = max(v, (uint32_t)__shfl_xor((int)v, o, 64));
+  return v;
+}
+__device__ __forceinline__ double wave_sum_f64(double v) {
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+
+// ---------------------------------------------------------------------------
+// Batches.  Up to kMaxSeg tensors per launch; tensor s owns tiles
+// [tile0[s], tile0[s+1]) of the launch's flat tile range.
+struct Seg {
+  const void* x;
+  uint8_t* codes;
+  uint8_t* scales;
+  void* y;
+  int64_t n;
+};
+
+struct SegBatch {
+  Seg s[kMaxSeg];
+  int64_t tile0[kMaxSeg + 1];
+  int32_t count;   // tensors in this launch
+  int32_t first;   // index of s[0] in the caller's arrays (counts, states, stats)
+};
+
+// Tensor owning `tile`, scanning forward from `hint` (tiles visited by a
+// workgroup only increase, so the scan is amortised O(1)).
+__device__ __forceinline__ int seg_of(const SegBatch& b, int64_t tile, int hint) {
+  int s = hint < 0 ? 0 : hint;
+  while (tile >= b.tile0[s + 1]) ++s;
+  return s;
+}
+
+// Workgroup flush of one tensor's totals into its nc_counts (integer
+// atomics: order-independent, so deterministic).
+__device__ inline void flush_counts(Acc& acc, nc_counts* out, int unscale_log2,
+                                    uint64_t n_elems, uint32_t* lds_max, uint64_t* lds_cnt) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const uint32_t m = wave_max_u32(acc.amax);
+  if (lane == 0) {
+    lds_max[wave] = m;
+    lds_cnt[wave * 3 + 0] = acc.n_nf;
+    lds_cnt[wave * 3 + 1] = acc.n_big;
+    lds_cnt[wave * 3 + 2] = acc.n_uf;
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    uint32_t mx = 0;
+    uint64_t nf = 0, big = 0, uf = 0;
+    for (int w = 0; w < kWaves; ++w) {
+      mx = max(mx, lds_max[w]);
+      nf += lds_cnt[w * 3 + 0];
+      big += lds_cnt[w * 3 + 1];
+      uf += lds_cnt[w * 3 + 2];
+    }
+    atomicMax(&out->amax_bits, unscale_bits(mx, unscale_log2));
+    if (n_elems - nf) atomicAdd((unsigned long long*)&out->n_finite, (unsigned long long)(n_elems - nf));
+    if (nf) atomicAdd((unsigned long long*)&out->n_nonfinite, (unsigned long long)nf);
+    if (big - nf) atomicAdd((unsigned long long*)&out->n_clip, (unsigned long long)(big - nf));
+    if (uf) atomicAdd((unsigned long long*)&out->n_underflow, (unsigned long long)uf);
+  }
+  __syncthreads();
+  acc.reset();
+}
+
+// ---------------------------------------------------------------------------
+// Decoding.  fp32 bits of the value a code stands for (at exponent 0);
+// NaN codes give 0x7FC00000, E5M2 Inf codes give +-Inf.
+template <int FMT>
+__host__ __device__ inline uint32_t decode_bits(uint32_t q) {
+  using F = Fp8<FMT>;
+  const uint32_t sign = (q & 0x80u) << 24;
+  const uint32_t e = (q >> F::MB) & ((1u << (7 - F::MB)) - 1u);
+  const uint32_t m = q & ((1u << F::MB) - 1u);
+  constexpr uint32_t etop = (1u << (7 - F::MB)) - 1u;
+  if (FMT == NC_E4M3 && e == etop && m == 7u) return 0x7FC00000u;
+  if (FMT == NC_E5M2 && e == etop) return m ? 0x7FC00000u : (sign | kInfBits);
+  if (e == 0) {
+    // m * 2^(EMIN - MB): m < 2^MB, normalise into fp32
+    if (m == 0) return sign;
+    int lz = 0;
+    while (!(m & (1u << (F::MB - 1 - lz)))) ++lz;
+    const int top = F::MB - 1 - lz;                      // value = 1.f * 2^(top + EMIN - MB)
+    const uint32_t frac = (m ^ (1u << top)) << (23 - top);
+    return sign | ((uint32_t)(top + F::EMIN - F::MB + 127) << 23) | frac;
+  }
+  return sign | ((uint32_t)((int)e - F::BIAS + 127) << 23) | (m << (23 - F::MB));
+}
+
+// bf16 pattern of RNE(fp32 value) -- IEEE overflow to Inf; quiet NaN kept.
+__device__ __forceinline__ uint32_t f32_to_bf16_rne(uint32_t b) {
+  return (b + 0x7FFFu + ((b >> 16) & 1u)) >> 16;
+}
+
+// ---------------------------------------------------------------------------
+// Input vectors and error statistics (shared by the casts and the
+// separate statistics pass).
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr int kUnroll = 4;
+
+template <int DT> struct In;
+template <> struct In<NC_F32> { static constexpr int VEC = 4, BYTES = 4; };
+template <> struct In<NC_BF16> { static constexpr int VEC = 8, BYTES = 2; };
+
+// 16 input bytes -> VEC fp32 bit patterns (bf16 widens exactly by a shift).
+template <int DT>
+__device__ __forceinline__ void unpack(const u32x4 v, uint32_t* xb) {
+  if constexpr (DT == NC_F32) {
+    xb[0] = v.x; xb[1] = v.y; xb[2] = v.z; xb[3] = v.w;
+  } else {
+    xb[0] = v.x << 16; xb[1] = v.x & 0xFFFF0000u;
+    xb[2] = v.y << 16; xb[3] = v.y & 0xFFFF0000u;
+    xb[4] = v.z << 16; xb[5] = v.z & 0xFFFF0000u;
+    xb[6] = v.w << 16; xb[7] = v.w & 0xFFFF0000u;
+  }
+}
+
+template <int DT>
+__device__ __forceinline__ uint32_t load_one(const void* x, int64_t i) {
+  if constexpr (DT == NC_F32) return static_cast<const uint32_t*>(x)[i];
+  else return (uint32_t)static_cast<const uint16_t*>(x)[i] << 16;
+}
+
+// ---------------------------------------------------------------------------
+// Error statistics ([Drift, "What the measurements said"]): per element of
+// finite x, e = xhat - x with xhat = decode(q) * 2^-kq; sums of e, |e|, e^2,
+// sign(x) e, x e, x^2 in binary64.  x is taken after the unscale by 2^-s.
+struct StatAcc {
+  double s[6];
+  __device__ void reset() {
+#pragma unroll
+    for (int j = 0; j < 6; ++j) s[j] = 0.0;
+  }
+};
+
+__device__ __forceinline__ void stat_elem(uint32_t xb, uint32_t q, int s_log2, int kq,
+                                          const uint32_t* dec, StatAcc& a) {
+  if ((xb & kAbsMask) > kMaxFinite) return;
+  const double x = ldexp((double)__uint_as_float(xb), -s_log2);
+  const double xh = ldexp((double)__uint_as_float(dec[q]), -kq);
+  const double e = xh - x;
+  a.s[0] += e;
+  a.s[1] += fabs(e);
+  a.s[2] = fma(e, e, a.s[2]);
+  a.s[3] += (x < 0.0) ? -e : e;
+  a.s[4] = fma(x, e, a.s[4]);
+  a.s[5] = fma(x, x, a.s[5]);
+}
+
+// One tile's partial sums -> part[0..5], in a fixed order (lanes by
+// butterfly, then waves in index order): deterministic.
+__device__ inline void stats_tile_flush(StatAcc& a, double* part_tile, double* lds) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+#pragma unroll
+  for (int j = 0; j < 6; ++j) {
+    const double v = wave_sum_f64(a.s[j]);
+    if (lane == 0) lds[wave * 6 + j] = v;
+  }
+  __syncthreads();
+  if (threadIdx.x < 6) {
+    double t = 0.0;
+    for (int w = 0; w < kWaves; ++w) t += lds[w * 6 + threadIdx.x];
+    part_tile[threadIdx.x] = t;
+  }
+  __syncthreads();
+  a.reset();
+}
+
+}  // namespace nc

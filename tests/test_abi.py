@@ -1,0 +1,114 @@
+"""The C-ABI library loads and exports every entry point include/narrowcast.h
+declares; argument checks that return before any HIP call behave as the
+header states.  No compute call is made (no GPU needed)."""
+
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+from scaled_fp8_casting_amd import _lib
+from scaled_fp8_casting_amd._lib import NcPolicy, NcTensor
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "narrowcast.h")
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(nc_[a-z_]+)\s*\(", src)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(_lib.LIB_PATH):
+        pytest.fail("libnarrowcast.so is not built (python -m scaled_fp8_casting_amd.build)")
+    return _lib.load()
+
+
+def test_header_declares_the_six_calls():
+    fns = declared_functions()
+    for name in ("nc_amax", "nc_scale_update", "nc_cast_tensor", "nc_cast_mx", "nc_dequant", "nc_cast_stats"):
+        assert name in fns
+    assert set(fns) == set(_lib.EXPORTS)
+
+
+def test_every_declared_symbol_is_exported(lib):
+    out = subprocess.run(["nm", "-D", "--defined-only", _lib.LIB_PATH], capture_output=True, text=True).stdout
+    exported = set(re.findall(r"\bT (nc_\w+)", out))
+    for name in declared_functions():
+        assert name in exported, name
+        assert hasattr(lib, name)
+
+
+def test_struct_sizes_match_header():
+    assert ctypes.sizeof(NcTensor) == 40
+    assert ctypes.sizeof(_lib.NcCounts) == 40
+    assert ctypes.sizeof(_lib.NcStats) == 48
+    assert ctypes.sizeof(_lib.NcScaleState) == 24
+    assert ctypes.sizeof(_lib.NcLossScale) == 8
+    assert ctypes.sizeof(NcPolicy) == 44
+
+
+def _desc(*specs):
+    arr = (NcTensor * len(specs))()
+    for i, (x, c, n, cols, sc) in enumerate(specs):
+        arr[i].x, arr[i].codes, arr[i].n, arr[i].cols, arr[i].scales = x, c, n, cols, sc
+    return arr
+
+
+def test_argument_checks_before_any_launch(lib):
+    A = 0x10000  # fake, aligned, never dereferenced: every call below fails its checks first
+    assert lib.nc_amax(None, -1, 0, None, None, None) == _lib.NC_E_ARG
+    assert lib.nc_amax(None, 1, 0, None, A, None) == _lib.NC_E_ARG
+    assert lib.nc_amax(_desc((A, None, 8, 0, None)), 1, 7, None, A, None) == _lib.NC_E_UNSUPPORTED
+    assert lib.nc_amax(_desc((A + 4, None, 8, 0, None)), 1, 0, None, A, None) == _lib.NC_E_ALIGN
+    assert lib.nc_amax(_desc((A, None, -1, 0, None)), 1, 0, None, A, None) == _lib.NC_E_ARG
+    assert lib.nc_amax(_desc((A, None, 8, 0, None)), 1, 0, None, None, None) == _lib.NC_E_ARG
+    # empty batches are valid no-ops
+    assert lib.nc_amax(None, 0, 0, None, None, None) == _lib.NC_OK
+    assert lib.nc_amax(_desc((None, None, 0, 0, None)), 1, 0, None, A, None) == _lib.NC_OK
+    # MX shapes
+    for cols, n in ((48, 96), (0, 64), (64, 96)):
+        assert lib.nc_cast_mx(_desc((A, A, n, cols, A)), 1, 1, 0, 0, A, None, None, 0, None) == _lib.NC_E_SHAPE
+    assert lib.nc_cast_mx(_desc((A, A, 64, 64, None)), 1, 1, 0, 0, A, None, None, 0, None) == _lib.NC_E_ARG
+    assert lib.nc_cast_mx(_desc((A, A, 64, 64, A)), 1, 1, 0, 9, A, None, None, 0, None) == _lib.NC_E_UNSUPPORTED
+    # per-tensor cast
+    assert lib.nc_cast_tensor(_desc((A, A + 1, 8, 0, None)), 1, 0, 0, A, None, A, None, None, 0, None) == _lib.NC_E_ALIGN
+    assert lib.nc_cast_tensor(_desc((A, A, 8, 0, None)), 1, 0, 0, None, None, A, None, None, 0, None) == _lib.NC_E_ARG
+    assert lib.nc_cast_tensor(_desc((A, A, 8, 0, None)), 1, 0, 2, A, None, A, None, None, 0, None) == _lib.NC_E_UNSUPPORTED
+    # statistics need a large enough workspace
+    d = _desc((A, A, 10000, 0, None))
+    need = lib.nc_workspace_bytes(d, 1)
+    assert need == 3 * 6 * 8
+    assert lib.nc_cast_tensor(d, 1, 0, 0, A, None, A, A, A, need - 8, None) == _lib.NC_E_WORKSPACE
+    assert lib.nc_cast_stats(d, 1, 0, 0, A, None, A, None, 0, None) == _lib.NC_E_WORKSPACE
+    # dequant writes bf16 only
+    assert lib.nc_dequant(d, 1, 0, A, None, 0, None) == _lib.NC_E_UNSUPPORTED
+    assert lib.nc_dequant(d, 1, 0, A, None, 1, None) == _lib.NC_E_ARG
+
+
+def test_policy_checks(lib):
+    A = 0x10000
+    good = dict(fmt=0, est=2, window=16, margin=0, hysteresis=1, interval=1, skip_on_nonfinite=0,
+                ls_enable=0, ls_growth_interval=1, ls_log2_min=0, ls_log2_max=24)
+    for field, bad, want in (("window", 0, _lib.NC_E_ARG), ("window", 2000, _lib.NC_E_ARG),
+                             ("interval", 0, _lib.NC_E_ARG), ("margin", -1, _lib.NC_E_ARG),
+                             ("est", 5, _lib.NC_E_UNSUPPORTED), ("fmt", 3, _lib.NC_E_UNSUPPORTED)):
+        p = NcPolicy(**{**good, field: bad})
+        assert lib.nc_scale_update(ctypes.byref(p), 1, A, A, A, None, None) == want, field
+    p = NcPolicy(**{**good, "ls_enable": 1, "ls_log2_min": 5, "ls_log2_max": 4})
+    assert lib.nc_scale_update(ctypes.byref(p), 1, A, A, A, None, None) == _lib.NC_E_ARG
+    p = NcPolicy(**good)
+    assert lib.nc_scale_update(ctypes.byref(p), 1, A, None, A, None, None) == _lib.NC_E_ARG   # no history
+    assert lib.nc_scale_update(ctypes.byref(p), 0, None, None, None, None, None) == _lib.NC_OK
+    assert lib.nc_scale_update(None, 1, A, A, A, None, None) == _lib.NC_E_ARG
+
+
+def test_status_strings(lib):
+    for s in range(7):
+        assert lib.nc_status_string(s)
+    assert b"unknown" in lib.nc_status_string(99)

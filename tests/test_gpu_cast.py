@@ -1,0 +1,266 @@
+"""GPU parity of the per-tensor cast, the amax pass and the MX cast against
+the oracle (bit-exact codes, scale bytes, counts and amax)."""
+
+import numpy as np
+import pytest
+import torch
+
+import scaled_fp8_casting_amd as nc
+from oracle import E4M3, E5M2
+from oracle import bulk
+from oracle import cast as t0
+import workloads
+from tests._gpu import (assert_counts, codes_like, dev_bf16, dev_f32, host_u8, state_with_k)
+
+pytestmark = pytest.mark.gpu
+FMTS = [("e4m3", E4M3), ("e5m2", E5M2)]
+
+
+def _cast_pt(xs_dev, ks, fmt, ls=None):
+    codes = [codes_like(x.numel()) for x in xs_dev]
+    out = nc.new_counts(len(xs_dev))
+    nc.nc_cast_tensor(xs_dev, codes, fmt, state_with_k(ks), out, ls=ls)
+    torch.cuda.synchronize()
+    return [host_u8(c) for c in codes], nc.counts_list(out)
+
+
+def _expect_pt(fmt, x64, k, s=0):
+    codes, clip, uf, nf = bulk.cast_f64(fmt, x64, k - s)
+    return codes, bulk.counts_of(clip, uf, nf, bulk.amax_f64(x64, s), x64.size)
+
+
+@pytest.mark.parametrize("name,fmt", FMTS)
+def test_all_bf16_patterns_every_K(name, fmt):
+    """All 65,536 bf16 patterns at every exponent K in [-140, 140], one
+    tensor per K in a single batched call (several launches of 32)."""
+    bits = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    x64 = bulk.bf16_bits_to_f64(bits)
+    Ks = list(range(-140, 141))
+    xd = dev_bf16(bits)
+    codes, counts = _cast_pt([xd] * len(Ks), Ks, name)
+    for K, c, n in zip(Ks, codes, counts):
+        want_c, want_n = _expect_pt(fmt, x64, K)
+        bad = np.flatnonzero(c != want_c)
+        assert bad.size == 0, (K, [(hex(bits[i]), hex(c[i]), hex(want_c[i])) for i in bad[:5]])
+        assert_counts(n, want_n)
+
+
+@pytest.mark.parametrize("name,fmt", FMTS)
+def test_fp32_boundaries_and_random_patterns(name, fmt):
+    """Every code value and midpoint (+-1 fp32 ulp) moved to the input scale,
+    plus uniform 32-bit patterns (subnormals, Inf, NaN), at many K."""
+    mags = sorted({float(fmt.decode(c).mag) for c in range(128) if fmt.decode(c).kind == "num"})
+    pts = np.array(mags + [(a + b) / 2 for a, b in zip(mags, mags[1:])] + [float(fmt.maxval) * 1.01])
+    rnd = bulk.f32_bits_to_f64(workloads.random_fp32_bits(50000, 3))
+    xs, Ks = [], []
+    for K in (-150, -127, -60, -9, 0, 1, 7, 33, 100, 127, 140, 180):
+        with np.errstate(over="ignore"):
+            v = np.ldexp(pts, -K).astype(np.float32)
+        v = v[np.isfinite(v)]
+        nb = np.concatenate([np.nextafter(v, np.float32(0)), v, np.nextafter(v, np.float32(np.inf))])
+        xs.append(np.concatenate([nb, -nb, rnd.astype(np.float32)]))
+        Ks.append(K)
+    codes, counts = _cast_pt([dev_f32(x) for x in xs], Ks, name)
+    for K, x, c, n in zip(Ks, xs, codes, counts):
+        x64 = x.astype(np.float64)
+        want_c, want_n = _expect_pt(fmt, x64, K)
+        bad = np.flatnonzero(c != want_c)
+        assert bad.size == 0, (K, [(x[i], hex(c[i]), hex(want_c[i])) for i in bad[:5]])
+        assert_counts(n, want_n)
+
+
+@pytest.mark.parametrize("name,fmt", FMTS)
+def test_all_code_pairs_products_and_sums(name, fmt, consts):
+    """The exhaustive 65,536-pair self-check on the GPU: every exact product
+    and sum of two codes that is an fp32 value, cast at k = 0."""
+    d = bulk.decode_table(fmt)
+    a, b = np.meshgrid(d, d, indexing="ij")
+    for op in (np.multiply, np.add):
+        with np.errstate(invalid="ignore", over="ignore"):
+            r = op(a, b).ravel()
+        r32 = r.astype(np.float32)
+        ok = (r32.astype(np.float64) == r) | np.isnan(r)
+        codes, counts = _cast_pt([dev_f32(r32[ok])], [0], name)
+        want_c, want_n = _expect_pt(fmt, r32[ok].astype(np.float64), 0)
+        assert np.array_equal(codes[0], want_c)
+        assert_counts(counts[0], want_n)
+        assert ok.sum() >= 57024 if (fmt is E5M2 and op is np.add) else ok.sum() == 65536
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("n", [0, 1, 3, 17, 4095, 4096, 4097, 8191, 8192, 8193, 3 * 8192 + 5, 100003])
+def test_ragged_sizes(dtype, n):
+    rng = np.random.default_rng(n)
+    x = (rng.standard_normal(n) * 10.0 ** rng.uniform(-6, 6, n)).astype(np.float32)
+    if n > 10:
+        x[n // 2] = np.inf
+        x[n - 1] = np.nan
+    if dtype == "bf16":
+        bits = workloads.to_bf16_bits(x.astype(np.float64))
+        xd, x64 = dev_bf16(bits), bulk.bf16_bits_to_f64(bits)
+    else:
+        xd, x64 = dev_f32(x), x.astype(np.float64)
+    for name, fmt in FMTS:
+        codes, counts = _cast_pt([xd], [5], name)
+        want_c, want_n = _expect_pt(fmt, x64, 5)
+        assert np.array_equal(codes[0], want_c)
+        assert_counts(counts[0], want_n)
+
+
+def test_per_tensor_small_current_scaling():
+    """65,536 fp32 N(0, 1): amax pass -> scale update (current) -> cast.
+    k comes from the GPU's own amax; the oracle derives its own."""
+    x = workloads.per_tensor_small()
+    x64 = x.astype(np.float64)
+    xd = dev_f32(x)
+    am = nc.new_counts(1)
+    nc.nc_amax([xd], am)
+    st = nc.new_state(1)
+    nc.nc_scale_update(nc.policy("e4m3", "current", hysteresis=False), st, am)
+    codes = codes_like(x.size)
+    out = nc.new_counts(1)
+    nc.nc_cast_tensor([xd], [codes], "e4m3", st, out)
+    torch.cuda.synchronize()
+    from fractions import Fraction
+    a = bulk.amax_f64(x64)
+    k = t0.scale_exponent(E4M3, Fraction(a))
+    assert nc.counts_list(am)[0]["amax"] == a
+    assert int(st[0, 0]) == k == 6
+    want_c, want_n = _expect_pt(E4M3, x64, k)
+    assert np.array_equal(host_u8(codes), want_c)
+    assert_counts(nc.counts_list(out)[0], want_n)
+    assert want_n["n_clip"] == 0
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_amax_pass_and_unscale(dtype):
+    rng = np.random.default_rng(8)
+    x = (rng.standard_normal(70001) * 3e-3).astype(np.float32)
+    x[5], x[77], x[900] = np.inf, -np.inf, np.nan
+    x[1000] = -2.0 ** -126 * 1.5   # rounds when unscaled by 2^24
+    if dtype == "bf16":
+        bits = workloads.to_bf16_bits(x.astype(np.float64))
+        xd, x64 = dev_bf16(bits), bulk.bf16_bits_to_f64(bits)
+    else:
+        xd, x64 = dev_f32(x), x.astype(np.float64)
+    for s in (0, 16, 24, 64):
+        am = nc.new_counts(1)
+        nc.nc_amax([xd], am, ls=nc.new_loss_scale(s))
+        torch.cuda.synchronize()
+        got = nc.counts_list(am)[0]
+        assert got["amax"] == bulk.amax_f64(x64, s)
+        assert got["n_nonfinite"] == 3 and got["n_finite"] == x.size - 3 and got["n_clip"] == 0
+    # tiny tensor whose amax becomes subnormal after the unscale
+    t = np.array([2.0 ** -120 * 1.75, -(2.0 ** -125) * 1.25], dtype=np.float32)
+    am = nc.new_counts(1)
+    nc.nc_amax([dev_f32(t)], am, ls=nc.new_loss_scale(17))
+    torch.cuda.synchronize()
+    assert nc.counts_list(am)[0]["amax"] == bulk.amax_f64(t.astype(np.float64), 17)
+
+
+@pytest.mark.parametrize("name,fmt", FMTS)
+def test_fused_unscale_cast(name, fmt):
+    """x * 2^-s then the cast at k, in one pass, with non-finite counting."""
+    rng = np.random.default_rng(4)
+    x = (2.0 ** 16 * rng.normal(0, 1e-6, 300000)).astype(np.float32)
+    idx = rng.choice(x.size, 40, replace=False)
+    x[idx[:20]] = np.inf
+    x[idx[20:]] = np.nan
+    x64 = x.astype(np.float64)
+    ls = nc.new_loss_scale(16)
+    from fractions import Fraction
+    k = t0.scale_exponent(fmt, Fraction(bulk.amax_f64(x64, 16)))
+    codes, counts = _cast_pt([dev_f32(x)], [k], name, ls=ls)
+    want_c, want_n = _expect_pt(fmt, x64, k, 16)
+    assert np.array_equal(codes[0], want_c)
+    assert_counts(counts[0], want_n)
+    assert counts[0]["n_nonfinite"] == 40 and counts[0]["n_clip"] == 0
+
+
+def test_determinism_and_accumulation():
+    x = workloads.mixed_magnitude_fp32(1 << 20, 12, -30, 30)
+    xd = dev_f32(x)
+    a = _cast_pt([xd], [3], "e4m3")
+    b = _cast_pt([xd], [3], "e4m3")
+    assert np.array_equal(a[0][0], b[0][0]) and a[1] == b[1]
+    # counts accumulate over two calls into the same buffer
+    out = nc.new_counts(1)
+    st = state_with_k([3])
+    c = codes_like(x.size)
+    nc.nc_cast_tensor([xd], [c], "e4m3", st, out)
+    nc.nc_cast_tensor([xd], [c], "e4m3", st, out)
+    torch.cuda.synchronize()
+    got = nc.counts_list(out)[0]
+    for key in ("n_finite", "n_clip", "n_underflow"):
+        assert got[key] == 2 * a[1][0][key]
+    assert got["amax"] == a[1][0]["amax"]
+
+
+# -- MX ----------------------------------------------------------------------------
+
+def _cast_mx(xd, cols, fmt, rule):
+    n = xd.numel()
+    codes = codes_like(n)
+    scales = torch.empty(n // 32, dtype=torch.uint8, device="cuda")
+    out = nc.new_counts(1)
+    nc.nc_cast_mx([xd], [codes], [scales], [cols], fmt, rule, out)
+    torch.cuda.synchronize()
+    return host_u8(codes), host_u8(scales), nc.counts_list(out)[0]
+
+
+def _mx_input(rows, cols, seed):
+    rng = np.random.default_rng(seed)
+    x = np.tanh(rng.normal(0, 1.5, rows * cols)) * np.repeat(np.exp2(rng.integers(-40, 40, rows * cols // 32)), 32)
+    x = x.astype(np.float32)
+    x[0:32] = 0.0                                   # all-zero block
+    x[32:64] = np.nan                               # all-NaN block
+    x[70] = np.inf
+    x[96:128] = (np.arange(32) * 2.0 ** -140).astype(np.float32)   # subnormal block
+    x[128:160] = np.float32(2.0 ** 127) * 1.5       # huge block
+    return x
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("rule", ["ocp", "plus1", "ceil"])
+@pytest.mark.parametrize("name,fmt", FMTS)
+@pytest.mark.parametrize("rows,cols", [(3, 64), (37, 96), (129, 512)])
+def test_mx_parity(dtype, rule, name, fmt, rows, cols):
+    x = _mx_input(rows, cols, rows * cols)
+    if dtype == "bf16":
+        bits = workloads.to_bf16_bits(x.astype(np.float64))
+        xd, x64 = dev_bf16(bits), bulk.bf16_bits_to_f64(bits)
+    else:
+        xd, x64 = dev_f32(x), x.astype(np.float64)
+    codes, scales, counts = _cast_mx(xd, cols, name, rule)
+    wc, ws, wn = bulk.cast_mx_f64(fmt, x64, cols, rule)
+    assert np.array_equal(scales, ws)
+    bad = np.flatnonzero(codes != wc)
+    assert bad.size == 0, [(i, x64[i], hex(codes[i]), hex(wc[i])) for i in bad[:5]]
+    assert_counts(counts, wn)
+    if rule != "ocp":
+        assert counts["n_clip"] == 0
+
+
+def test_tanh_activations_mx_full_size():
+    """4096 x 4096 bf16 tanh(N(0, 1.5)), OCP and +1 rules, in full."""
+    bits = workloads.tanh_activations()
+    x64 = bulk.bf16_bits_to_f64(bits.ravel())
+    xd = dev_bf16(bits.ravel())
+    for rule in ("ocp", "plus1"):
+        codes, scales, counts = _cast_mx(xd, 4096, "e4m3", rule)
+        wc, ws, wn = bulk.cast_mx_f64(E4M3, x64, 4096, rule)
+        assert np.array_equal(scales, ws) and np.array_equal(codes, wc)
+        assert_counts(counts, wn)
+        frac = counts["n_clip"] / x64.size
+        assert (0.175 < frac < 0.181) if rule == "ocp" else frac == 0
+
+
+def test_argument_errors_on_device():
+    x = dev_f32(np.ones(64, np.float32))
+    with pytest.raises(nc.NarrowcastError) as e:
+        nc.nc_cast_mx([x], [codes_like(64)], [torch.empty(2, dtype=torch.uint8, device="cuda")], [48],
+                      "e4m3", "ocp", nc.new_counts(1))
+    assert e.value.status == 3
+    with pytest.raises(nc.NarrowcastError) as e:
+        nc.nc_cast_tensor([x[1:]], [codes_like(63)], "e4m3", state_with_k([0]), nc.new_counts(1))
+    assert e.value.status == 2
