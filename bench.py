@@ -1,0 +1,244 @@
+"""Throughput of the scaled FP8 cast on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--rows R] [--no-cpu]
+
+Workload: a heavy-tailed bf16 tensor of 2^30 elements (262,144 rows of 4096;
+row r = 10^v_r * Student-t(3), v_r ~ U(-3, 3)), resident in HBM before the
+timed region.  One step is one pass of the whole cast path over it:
+
+  1. nc_amax          per-tensor amax pass                     (read 2 B/elem)
+  2. nc_scale_update  current scaling -> k                      (O(1))
+  3. nc_cast_tensor   per-tensor E4M3 cast + counts + amax      (2 + 1)
+  4. nc_cast_mx       MXFP8 E4M3, OCP rule, + counts            (2 + 1 + 1/32)
+  5. nc_dequant       per-tensor codes -> bf16                  (1 + 2)
+  6. nc_dequant       MX codes -> bf16                          (1 + 1/32 + 2)
+  7. nc_cast_stats    error/bias statistics, per-tensor         (2 + 1)
+  8. nc_cast_stats    error/bias statistics, MX                 (2 + 1 + 1/32)
+
+Prints one JSON line.  `value` is elements per second through the whole step
+(Gelem/s); `roofline` is the dominant kernel's algorithmic bytes per launch
+over its mean launch time (HIP events on the launch stream, inside the timed
+region) against 8 TB/s; `cpu_baseline` times the CPU oracle on a bounded
+sample of the same workload.
+"""
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+HBM_PEAK_GBPS = 8000.0
+COLS = 4096
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--rows", type=int, default=262144, help="rows of 4096 (default 2^30 elements)")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--cpu-rows", type=int, default=1024)
+    ap.add_argument("--procs", type=int, default=min(16, os.cpu_count() or 1))
+    return ap.parse_args()
+
+
+def source_hash():
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "scaled_fp8_casting_amd", "csrc")
+    for f in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, f), "rb") as fh:
+            h.update(f.encode() + fh.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_for(kernel: str, src_hash: str):
+    """HBM bytes per launch from the committed rocprofv3 counter runs, if they
+    were taken on the current kernel sources; else None."""
+    p = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(p):
+        return None
+    with open(p) as f:
+        t = json.load(f)
+    if t.get("source_hash") != src_hash:
+        return None
+    k = t.get("kernels", {}).get(kernel)
+    return None if k is None else k.get("bytes_per_launch")
+
+
+def cpu_baseline(rows: int, procs: int):
+    """The oracle (tier 1, vectorised exact binary64) over the same step on
+    `rows` rows of the workload, row chunks spread over a process pool."""
+    import multiprocessing as mp
+    import workloads
+    bits = workloads.heavy_tailed_parallel(rows, COLS, procs=procs)
+    chunk = -(-rows // procs)
+    jobs = [bits[r:r + chunk] for r in range(0, rows, chunk)]
+    workers = min(procs, len(jobs))
+    # the per-tensor scale needs the global amax first (as on the GPU)
+    t0 = time.perf_counter()
+    with mp.get_context("fork").Pool(workers) as pool:
+        amaxes = pool.map(_cpu_amax, jobs)
+        k = _scale_k(max(amaxes))
+        pool.map(_cpu_step, [(j, k) for j in jobs])
+    dt = time.perf_counter() - t0
+    n = rows * COLS
+    return dict(value=n / dt / 1e9, unit="Gelem/s", cores=workers, kind="oracle",
+                sample=f"{rows} rows x {COLS} of the same workload ({n} elements), whole step, "
+                       f"{workers} worker processes, {dt:.1f} s")
+
+
+def _cpu_amax(b):
+    from oracle import bulk
+    return bulk.amax_f64(bulk.bf16_bits_to_f64(b.ravel()))
+
+
+def _scale_k(a):
+    from fractions import Fraction
+    from oracle import E4M3
+    from oracle.cast import scale_exponent
+    return scale_exponent(E4M3, Fraction(a))
+
+
+def _cpu_step(args):
+    b, k = args
+    from oracle import E4M3
+    from oracle import bulk
+    x = bulk.bf16_bits_to_f64(b.ravel())
+    c_pt, clip, uf, nf = bulk.cast_f64(E4M3, x, k)
+    c_mx, sc, _ = bulk.cast_mx_f64(E4M3, x, COLS, "ocp")
+    K_mx = np.repeat(127 - sc.astype(np.int64), 32)
+    bulk.dequant_bf16_f64(E4M3, c_pt, k)
+    bulk.dequant_bf16_f64(E4M3, c_mx, K_mx)
+    bulk.stats_f64(E4M3, x, c_pt, k)
+    bulk.stats_f64(E4M3, x, c_mx, K_mx)
+    return int(np.count_nonzero(clip))
+
+
+def main():
+    a = parse()
+    if a.gpus != 1:
+        print(f"bench.py measures one GPU only: this build has no multi-GPU path "
+              f"(--gpus {a.gpus} requested). Run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    import scaled_fp8_casting_amd as nc
+    import workloads
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    rows = a.rows
+    n = rows * COLS
+    print(f"[bench] generating {rows}x{COLS} bf16 on {a.procs} processes", file=sys.stderr, flush=True)
+    t = time.time()
+    host = workloads.heavy_tailed_parallel(rows, COLS, procs=a.procs)
+    print(f"[bench] generated in {time.time() - t:.1f}s; uploading", file=sys.stderr, flush=True)
+    x = torch.from_numpy(host.view(np.int16).reshape(-1)).cuda().view(torch.bfloat16)
+    del host
+    dev = "cuda"
+    codes_pt = torch.empty(n, dtype=torch.uint8, device=dev)
+    codes_mx = torch.empty(n, dtype=torch.uint8, device=dev)
+    scales = torch.empty(n // 32, dtype=torch.uint8, device=dev)
+    y_pt = torch.empty(n, dtype=torch.bfloat16, device=dev)
+    y_mx = torch.empty(n, dtype=torch.bfloat16, device=dev)
+    desc, cnt = nc.tensors([x], [codes_pt])
+    ws = nc.new_workspace(desc, cnt)
+    pol = nc.policy("e4m3", "current", hysteresis=False)
+    bufs = dict(am=nc.new_counts(1), cpt=nc.new_counts(1), cmx=nc.new_counts(1),
+                spt=nc.new_stats(1), smx=nc.new_stats(1), st=nc.new_state(1))
+
+    names = ["amax", "scale_update", "cast_tensor", "cast_mx", "dequant_pt", "dequant_mx",
+             "stats_pt", "stats_mx"]
+    alg_bytes = {"amax": 2 * n, "scale_update": 0, "cast_tensor": 3 * n, "cast_mx": 3 * n + n // 32,
+                 "dequant_pt": 3 * n, "dequant_mx": 3 * n + n // 32, "stats_pt": 3 * n,
+                 "stats_mx": 3 * n + n // 32}
+    kernel_of = {"amax": "k_amax", "cast_tensor": "k_cast_pt", "cast_mx": "k_cast_mx",
+                 "dequant_pt": "k_dequant", "dequant_mx": "k_dequant", "stats_pt": "k_stats",
+                 "stats_mx": "k_stats"}
+
+    def step(ev=None):
+        for b in ("am", "cpt", "cmx", "spt", "smx"):
+            bufs[b].zero_()
+        calls = [
+            lambda: nc.nc_amax([x], bufs["am"]),
+            lambda: nc.nc_scale_update(pol, bufs["st"], bufs["am"]),
+            lambda: nc.nc_cast_tensor([x], [codes_pt], "e4m3", bufs["st"], bufs["cpt"]),
+            lambda: nc.nc_cast_mx([x], [codes_mx], [scales], [COLS], "e4m3", "ocp", bufs["cmx"]),
+            lambda: nc.nc_dequant([codes_pt], [y_pt], "e4m3", st=bufs["st"]),
+            lambda: nc.nc_dequant([codes_mx], [y_mx], "e4m3", scales=[scales], cols=[COLS]),
+            lambda: nc.nc_cast_stats([x], [codes_pt], "e4m3", bufs["spt"], ws, st=bufs["st"]),
+            lambda: nc.nc_cast_stats([x], [codes_mx], "e4m3", bufs["smx"], ws, scales=[scales], cols=[COLS]),
+        ]
+        for i, c in enumerate(calls):
+            if ev is not None:
+                ev[i][0].record()
+            c()
+            if ev is not None:
+                ev[i][1].record()
+
+    for _ in range(a.warmup):
+        step()
+    torch.cuda.synchronize()
+    print(f"[bench] warmup done; timing {a.steps} steps", file=sys.stderr, flush=True)
+    evs = [[[torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)]
+            for _ in names] for _ in range(a.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(a.steps):
+        step(evs[s])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_per_step = wall * 1e3 / a.steps
+    per = {nm: float(np.mean([evs[s][i][0].elapsed_time(evs[s][i][1]) for s in range(a.steps)]))
+           for i, nm in enumerate(names)}
+    kernels = {}
+    for nm in names:
+        gbps = alg_bytes[nm] / (per[nm] * 1e-3) / 1e9 if alg_bytes[nm] else None
+        kernels[nm] = dict(ms=round(per[nm], 4), gbps=None if gbps is None else round(gbps, 1),
+                           frac=None if gbps is None else round(gbps / HBM_PEAK_GBPS, 4),
+                           gelem_s=round(n / (per[nm] * 1e-3) / 1e9, 2) if alg_bytes[nm] else None)
+    dom = max((nm for nm in names if alg_bytes[nm]), key=lambda nm: per[nm])
+    ach = alg_bytes[dom] / (per[dom] * 1e-3) / 1e9
+    src = source_hash()
+    step_bytes = sum(alg_bytes.values())
+    cc = nc.counts_list(bufs["cpt"])[0]
+    cm = nc.counts_list(bufs["cmx"])[0]
+    out = {
+        "metric": "scaled FP8 cast Gelem/s and achieved HBM GB/s (% of peak), per-tensor + MX",
+        "value": round(n / (ms_per_step * 1e-3) / 1e9, 3),
+        "unit": "Gelem/s",
+        "n_gpus": 1, "steps": a.steps, "warmup": a.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": "heavy-tailed bf16 2^30 (262144x4096, 10^U(-3,3) * t3 rows): amax, "
+                               "current-scaling E4M3 cast, MXFP8 E4M3 OCP cast, dequant x2, stats x2",
+                   "elements": n, "rows": rows, "cols": COLS, "parallelism": "single GPU"},
+        "hbm": {"step_bytes": step_bytes, "achieved_GBps": round(step_bytes / (ms_per_step * 1e-3) / 1e9, 1),
+                "frac_of_peak": round(step_bytes / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4)},
+        "kernels": kernels,
+        "roofline": {"bound": "hbm", "kernel": kernel_of[dom], "call": dom, "achieved": round(ach, 1),
+                     "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(ach / HBM_PEAK_GBPS, 4),
+                     "bytes_per_launch": alg_bytes[dom],
+                     "traffic": traffic_for(kernel_of[dom], src)},
+        "results": {"k": int(bufs["st"][0, 0]), "amax": nc.counts_list(bufs["am"])[0]["amax"],
+                    "pt_clip": cc["n_clip"], "pt_underflow_frac": round(cc["n_underflow"] / n, 5),
+                    "mx_clip_frac": round(cm["n_clip"] / n, 5)},
+        "source_hash": src,
+    }
+    if not a.no_cpu:
+        print(f"[bench] CPU oracle baseline on {a.cpu_rows} rows", file=sys.stderr, flush=True)
+        out["cpu_baseline"] = cpu_baseline(a.cpu_rows, a.procs)
+    else:
+        out["cpu_baseline"] = None
+    print(json.dumps(out))
+
+
+if __name__ == "__main__":
+    main()

@@ -56,9 +56,9 @@ k_amax(const SegBatch b, const nc_loss_scale* __restrict__ ls, nc_counts* __rest
           const uint32_t ax = xb[i] & kAbsMask;
           const bool nf = ax > kMaxFinite;
           acc.amax = max(acc.amax, nf ? 0u : ax);
-          const uint64_t c = wave_count(nf);
-          acc.n_nf += c;
-          acc.n_big += c;   // the amax pass reports no clips
+          const uint32_t c = wave_count(nf);
+          acc.t_nf += c;
+          acc.t_big += c;   // the amax pass reports no clips
         }
       }
     } else {
@@ -67,12 +67,13 @@ k_amax(const SegBatch b, const nc_loss_scale* __restrict__ ls, nc_counts* __rest
         const uint32_t ax = (i < rem ? load_one<DT>(g.x, e0 + i) : 0u) & kAbsMask;
         const bool nf = ax > kMaxFinite;
         acc.amax = max(acc.amax, nf ? 0u : ax);
-        const uint64_t c = wave_count(nf);
-        acc.n_nf += c;
-        acc.n_big += c;
+        const uint32_t c = wave_count(nf);
+        acc.t_nf += c;
+        acc.t_big += c;
       }
     }
     elems += rem;
+    acc.fold();
   }
   if (seg >= 0) flush_counts(acc, out + b.first + seg, s_log2, elems, lds_max, lds_cnt);
 }
@@ -141,6 +142,7 @@ k_cast_pt(const SegBatch b, const nc_scale_state* __restrict__ st,
           w.y = q[4] | (q[5] << 8) | (q[6] << 16) | (q[7] << 24);
           reinterpret_cast<u32x2*>(dst)[vi] = w;
         }
+        __builtin_amdgcn_sched_barrier(0);   // keep each vector's ballots short-lived
       }
     } else {
       for (int64_t base = 0; base < rem; base += kThreads) {
@@ -153,6 +155,7 @@ k_cast_pt(const SegBatch b, const nc_scale_state* __restrict__ st,
       }
     }
     elems += rem;
+    acc.fold();
     if constexpr (STATS) stats_tile_flush(sa, part + tile * 6, lds_st);
   }
   if (seg >= 0) flush_counts(acc, out + b.first + seg, s_log2, elems, lds_max, lds_cnt);
@@ -161,24 +164,19 @@ k_cast_pt(const SegBatch b, const nc_scale_state* __restrict__ st,
 // ---------------------------------------------------------------------------
 // MX: shared block exponent X ([Drift, "What the measurements said"]) from
 // the finite amax a of each 32-element block (a = 0 -> -127).
-template <int FMT>
-__device__ __forceinline__ int mx_exponent(uint32_t a, int rule) {
+template <int FMT, int RULE>
+__device__ __forceinline__ int mx_exponent(uint32_t a) {
   using F = Fp8<FMT>;
-  if (a == 0) return -127;
-  int e;
-  uint32_t frac;
-  if (a >= 0x800000u) {
-    e = (int)(a >> 23) - 127;
-    frac = a & 0x7FFFFFu;
-  } else {  // subnormal fp32 amax: normalise
-    const int lz = __clz(a);
-    e = (31 - lz) - 149;
-    frac = (a << (lz - 8)) & 0x7FFFFFu;
-  }
-  int X = e - F::EMAX;                                   // OCP: floor based
-  if (rule == NC_MX_PLUS1) X += 1;                       // one bit of headroom
-  else if (rule == NC_MX_CEIL) X += (frac > 0x600000u);  // smallest X that fits
-  return min(127, max(-127, X));
+  // binade and fraction of a, normalising a subnormal fp32 amax (selects only)
+  const int lz = __clz(a | 1u);
+  const bool normal = a >= 0x800000u;
+  const int e = normal ? (int)(a >> 23) - 127 : (31 - lz) - 149;
+  const uint32_t frac = normal ? (a & 0x7FFFFFu) : ((a << ((lz - 8) & 31)) & 0x7FFFFFu);
+  int X = e - F::EMAX;                                    // OCP: floor based
+  if constexpr (RULE == NC_MX_PLUS1) X += 1;              // one bit of headroom
+  if constexpr (RULE == NC_MX_CEIL) X += (frac > 0x600000u) ? 1 : 0;   // smallest X that fits
+  X = min(127, max(-127, X));
+  return a == 0 ? -127 : X;
 }
 
 // Max over the lanes of one block: 4 lanes (bf16, 8 elements each) or 8
@@ -192,11 +190,70 @@ __device__ __forceinline__ uint32_t group_max(uint32_t v) {
   return v;
 }
 
-template <int FMT, int DT, bool STATS>
-__global__ void __launch_bounds__(kThreads)
-k_cast_mx(const SegBatch b, const int rule, nc_counts* __restrict__ out, double* __restrict__ part) {
+// One tile of the MX cast.  FULL: every lane's vector is inside the tensor
+// (no predicates at all); otherwise lanes past `rem` load zeros and skip
+// their stores (rem is a multiple of 32, so a block is all in or all out).
+template <int FMT, int DT, int RULE, bool STATS, bool FULL>
+__device__ __forceinline__ void mx_tile(const Seg& g, int64_t e0, int64_t rem, Acc& acc,
+                                        StatAcc& sa, const uint32_t* dec) {
   constexpr int VEC = In<DT>::VEC;
   constexpr int GROUP = 32 / VEC;
+  const u32x4* src = reinterpret_cast<const u32x4*>(static_cast<const uint8_t*>(g.x) + e0 * In<DT>::BYTES);
+  uint8_t* dst = g.codes + e0;
+  uint8_t* sdst = g.scales + e0 / 32;
+  u32x4 v[kUnroll];
+#pragma unroll
+  for (int u = 0; u < kUnroll; ++u) {
+    const int vi = u * kThreads + threadIdx.x;
+    if constexpr (FULL) v[u] = src[vi];
+    else v[u] = ((int64_t)vi * VEC < rem) ? src[vi] : u32x4{0u, 0u, 0u, 0u};
+  }
+  __builtin_amdgcn_sched_barrier(0);   // all loads in flight before any use
+#pragma unroll
+  for (int u = 0; u < kUnroll; ++u) {
+    const int vi = u * kThreads + threadIdx.x;
+    uint32_t xb[VEC], ax[VEC], q[VEC];
+    unpack<DT>(v[u], xb);
+    uint32_t m = 0;
+#pragma unroll
+    for (int i = 0; i < VEC; ++i) {
+      ax[i] = xb[i] & kAbsMask;
+      m = max(m, finite_mag(ax[i], acc));
+      __builtin_amdgcn_sched_barrier(0);   // consume each ballot before the next compare
+    }
+    acc.amax = max(acc.amax, m);
+    const int X = mx_exponent<FMT, RULE>(group_max<GROUP>(m));
+    const CastParams p = cast_params<FMT>(-X);
+#pragma unroll
+    for (int i = 0; i < VEC; ++i) {
+      q[i] = code_of<FMT>(xb[i], ax[i], p, acc);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    if constexpr (STATS) {
+#pragma unroll
+      for (int i = 0; i < VEC; ++i) stat_elem(xb[i], q[i], 0, -X, dec, sa);
+    }
+    if (FULL || (int64_t)vi * VEC < rem) {
+      if constexpr (DT == NC_F32) {
+        reinterpret_cast<uint32_t*>(dst)[vi] = q[0] | (q[1] << 8) | (q[2] << 16) | (q[3] << 24);
+      } else {
+        u32x2 w;
+        w.x = q[0] | (q[1] << 8) | (q[2] << 16) | (q[3] << 24);
+        w.y = q[4] | (q[5] << 8) | (q[6] << 16) | (q[7] << 24);
+        reinterpret_cast<u32x2*>(dst)[vi] = w;
+      }
+      // every lane of the block holds the same X: all store it (same byte,
+      // same value), which keeps the tile free of divergent branches
+      sdst[vi / GROUP] = (uint8_t)(X + 127);
+    }
+    __builtin_amdgcn_sched_barrier(0);   // keep each vector's ballots short-lived
+  }
+}
+
+template <int FMT, int DT, int RULE, bool STATS>
+__global__ void __launch_bounds__(kThreads)
+k_cast_mx(const SegBatch b, nc_counts* __restrict__ out, double* __restrict__ part) {
+  constexpr int VEC = In<DT>::VEC;
   constexpr int64_t TILE = (int64_t)kThreads * VEC * kUnroll;
   __shared__ uint32_t lds_max[kWaves];
   __shared__ uint64_t lds_cnt[kWaves * 3];
@@ -213,7 +270,6 @@ k_cast_mx(const SegBatch b, const int rule, nc_counts* __restrict__ out, double*
   if constexpr (STATS) sa.reset();
   int seg = -1;
   uint64_t elems = 0;
-  const bool leader = (threadIdx.x % GROUP) == 0;
   for (int64_t tile = blockIdx.x; tile < total; tile += gridDim.x) {
     const int s = seg_of(b, tile, seg);
     if (s != seg) {
@@ -224,50 +280,10 @@ k_cast_mx(const SegBatch b, const int rule, nc_counts* __restrict__ out, double*
     const Seg& g = b.s[s];
     const int64_t e0 = (tile - b.tile0[s]) * TILE;
     const int64_t rem = min(g.n - e0, TILE);      // a multiple of 32
-    const u32x4* src = reinterpret_cast<const u32x4*>(static_cast<const uint8_t*>(g.x) + e0 * In<DT>::BYTES);
-    uint8_t* dst = g.codes + e0;
-    uint8_t* sdst = g.scales + e0 / 32;
-    const bool full = rem == TILE;
-    u32x4 v[kUnroll];
-#pragma unroll
-    for (int u = 0; u < kUnroll; ++u) {
-      const int vi = u * kThreads + threadIdx.x;
-      v[u] = (full || (int64_t)vi * VEC < rem) ? src[vi] : u32x4{0u, 0u, 0u, 0u};
-    }
-    __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-    for (int u = 0; u < kUnroll; ++u) {
-      const int vi = u * kThreads + threadIdx.x;
-      const bool act = full || (int64_t)vi * VEC < rem;
-      uint32_t xb[VEC], q[VEC];
-      unpack<DT>(v[u], xb);
-      uint32_t m = 0;
-#pragma unroll
-      for (int i = 0; i < VEC; ++i) {
-        const uint32_t ax = xb[i] & kAbsMask;
-        m = max(m, ax > kMaxFinite ? 0u : ax);
-      }
-      const int X = mx_exponent<FMT>(group_max<GROUP>(m), rule);
-      const CastParams p = cast_params<FMT>(-X);
-#pragma unroll
-      for (int i = 0; i < VEC; ++i) q[i] = cast_elem<FMT>(xb[i], p, acc);
-      if constexpr (STATS) {
-#pragma unroll
-        for (int i = 0; i < VEC; ++i) stat_elem(xb[i], q[i], 0, -X, dec, sa);
-      }
-      if (act) {
-        if constexpr (DT == NC_F32) {
-          reinterpret_cast<uint32_t*>(dst)[vi] = q[0] | (q[1] << 8) | (q[2] << 16) | (q[3] << 24);
-        } else {
-          u32x2 w;
-          w.x = q[0] | (q[1] << 8) | (q[2] << 16) | (q[3] << 24);
-          w.y = q[4] | (q[5] << 8) | (q[6] << 16) | (q[7] << 24);
-          reinterpret_cast<u32x2*>(dst)[vi] = w;
-        }
-        if (leader) sdst[vi / GROUP] = (uint8_t)(X + 127);
-      }
-    }
+    if (rem == TILE) mx_tile<FMT, DT, RULE, STATS, true>(g, e0, rem, acc, sa, dec);
+    else mx_tile<FMT, DT, RULE, STATS, false>(g, e0, rem, acc, sa, dec);
     elems += rem;
+    acc.fold();
     if constexpr (STATS) stats_tile_flush(sa, part + tile * 6, lds_st);
   }
   if (seg >= 0) flush_counts(acc, out + b.first + seg, 0, elems, lds_max, lds_cnt);
@@ -283,13 +299,20 @@ hipError_t cast_pt_t(const SegBatch& b, const nc_scale_state* st, const nc_loss_
   return hipGetLastError();
 }
 
+template <int FMT, int DT, int RULE>
+hipError_t cast_mx_r(const SegBatch& b, nc_counts* out, double* part, const Launch& l) {
+  if (part)
+    hipLaunchKernelGGL((k_cast_mx<FMT, DT, RULE, true>), dim3(l.grid), dim3(kThreads), 0, l.stream, b, out, part);
+  else
+    hipLaunchKernelGGL((k_cast_mx<FMT, DT, RULE, false>), dim3(l.grid), dim3(kThreads), 0, l.stream, b, out, part);
+  return hipGetLastError();
+}
+
 template <int FMT, int DT>
 hipError_t cast_mx_t(const SegBatch& b, int rule, nc_counts* out, double* part, const Launch& l) {
-  if (part)
-    hipLaunchKernelGGL((k_cast_mx<FMT, DT, true>), dim3(l.grid), dim3(kThreads), 0, l.stream, b, rule, out, part);
-  else
-    hipLaunchKernelGGL((k_cast_mx<FMT, DT, false>), dim3(l.grid), dim3(kThreads), 0, l.stream, b, rule, out, part);
-  return hipGetLastError();
+  if (rule == NC_MX_OCP) return cast_mx_r<FMT, DT, NC_MX_OCP>(b, out, part, l);
+  if (rule == NC_MX_PLUS1) return cast_mx_r<FMT, DT, NC_MX_PLUS1>(b, out, part, l);
+  return cast_mx_r<FMT, DT, NC_MX_CEIL>(b, out, part, l);
 }
 
 }  // namespace

@@ -59,22 +59,24 @@ constexpr uint32_t kNaNCode = 0x7Fu;
 
 // Largest fp32 pattern whose value is <= 1.75 * 2^j (the clip bound at
 // exponent K is 1.75 * 2^(EMAX - K)).
+// Written without branches (selects only): it runs per lane per MX block.
 __host__ __device__ inline uint32_t clip_threshold(int j) {
-  if (j > 127) return kMaxFinite;
-  if (j >= -126) return ((uint32_t)(j + 127) << 23) | 0x600000u;
+  const uint32_t normal = ((uint32_t)(j + 127) << 23) | 0x600000u;   // j in [-126, 127]
   // subnormal range: 1.75 * 2^j = 7 * 2^(j + 147) units of 2^-149
   const int up = j + 147;
-  if (up >= 0) return 7u << up;
-  return (-up >= 3) ? 0u : (7u >> (-up));
+  const uint32_t left = 7u << (up < 0 ? 0 : (up > 20 ? 20 : up));
+  const uint32_t right = 7u >> (up >= 0 ? 0 : (-up > 3 ? 3 : -up));
+  const uint32_t sub = up >= 0 ? left : right;
+  return j > 127 ? kMaxFinite : (j >= -126 ? normal : sub);
 }
 
 // Largest fp32 pattern whose value is <= 2^j (the underflow bound at
 // exponent K is half the smallest subnormal: 2^(EMIN - MB - 1 - K)).
 __host__ __device__ inline uint32_t pow2_threshold(int j) {
-  if (j > 127) return kMaxFinite;
-  if (j >= -126) return (uint32_t)(j + 127) << 23;
-  if (j >= -149) return 1u << (j + 149);
-  return 0u;
+  const uint32_t normal = (uint32_t)(j + 127) << 23;
+  const int sh = j + 149;
+  const uint32_t sub = sh < 0 ? 0u : (1u << (sh > 31 ? 31 : sh));
+  return j > 127 ? kMaxFinite : (j >= -126 ? normal : sub);
 }
 
 // Thresholds of a cast at exponent K.
@@ -111,36 +113,59 @@ __device__ __forceinline__ uint32_t encode_mag(uint32_t ax, int K) {
 }
 
 // Per-wave running totals.  The counts come from wave ballots and stay
-// wave-uniform (scalar registers); amax is per lane until the flush.
+// wave-uniform (scalar registers): 32-bit within a tile (at most 64 x 64
+// elements per wave), folded into the 64-bit totals once per tile.  amax is
+// per lane until the flush.
 struct Acc {
   uint64_t n_nf;     // non-finite elements
   uint64_t n_big;    // |x| bits above t_clip: every clip plus every non-finite
   uint64_t n_uf;
+  uint32_t t_nf, t_big, t_uf;   // the current tile's counts
   uint32_t amax;     // largest finite |x| bits (lane-local)
-  __device__ void reset() { n_nf = n_big = n_uf = 0; amax = 0; }
+  __device__ void reset() { n_nf = n_big = n_uf = 0; t_nf = t_big = t_uf = 0; amax = 0; }
+  __device__ void fold() {
+    n_nf += t_nf;
+    n_big += t_big;
+    n_uf += t_uf;
+    t_nf = t_big = t_uf = 0;
+  }
 };
 
-__device__ __forceinline__ uint64_t wave_count(bool p) {
-  return (uint64_t)__popcll(__ballot(p));
+__device__ __forceinline__ uint32_t wave_count(bool p) {
+  return (uint32_t)__popcll(__ballot(p));
+}
+
+// |x| bits with Inf/NaN mapped to 0 (for the amax), counting non-finite
+// elements.  The ballot consumes the compare at once, so no lane mask stays
+// live in scalar registers.
+__device__ __forceinline__ uint32_t finite_mag(uint32_t ax, Acc& acc) {
+  const bool nf = ax > kMaxFinite;
+  acc.t_nf += wave_count(nf);
+  return nf ? 0u : ax;
+}
+
+// The 8-bit code of one element (xb: its fp32 pattern, ax = |xb|); counts
+// clips (together with every non-finite, see Acc::n_big) and underflows.
+template <int FMT>
+__device__ __forceinline__ uint32_t code_of(uint32_t xb, uint32_t ax, const CastParams& p, Acc& acc) {
+  using F = Fp8<FMT>;
+  // Saturation needs no compare: the rounded code grows with |y| and is at
+  // least MAXCODE for every |y| > max (including a y that overflowed fp32 to
+  // Inf, whose pattern encodes far above MAXCODE), so min() saturates exactly.
+  uint32_t q = min(encode_mag<FMT>(ax, p.K), F::MAXCODE);
+  acc.t_big += wave_count(ax > p.t_clip);
+  acc.t_uf += wave_count((ax - 1u) < p.t_uf);
+  q |= (xb >> 24) & 0x80u;                  // sign (signed zero included)
+  q = (ax > kInfBits) ? kNaNCode : q;       // NaN: canonical 0x7F
+  return q;
 }
 
 // The full element cast: returns the 8-bit code, updates the wave totals.
 template <int FMT>
 __device__ __forceinline__ uint32_t cast_elem(uint32_t xb, const CastParams& p, Acc& acc) {
-  using F = Fp8<FMT>;
   const uint32_t ax = xb & kAbsMask;
-  uint32_t q = encode_mag<FMT>(ax, p.K);
-  const bool nf = ax > kMaxFinite;
-  const bool big = ax > p.t_clip;
-  const bool uf = (ax - 1u) < p.t_uf;
-  q = big ? F::MAXCODE : q;                 // saturate clips and +-Inf
-  q |= (xb >> 24) & 0x80u;                  // sign (signed zero included)
-  q = (ax > kInfBits) ? kNaNCode : q;       // NaN: canonical 0x7F
-  acc.amax = max(acc.amax, nf ? 0u : ax);
-  acc.n_nf += wave_count(nf);
-  acc.n_big += wave_count(big);
-  acc.n_uf += wave_count(uf);
-  return q;
+  acc.amax = max(acc.amax, finite_mag(ax, acc));
+  return code_of<FMT>(xb, ax, p, acc);
 }
 
 // fp32 bits of RNE(value(a) * 2^-s) for finite non-negative a, s >= 0 (the
@@ -197,6 +222,7 @@ __device__ __forceinline__ int seg_of(const SegBatch& b, int64_t tile, int hint)
 __device__ inline void flush_counts(Acc& acc, nc_counts* out, int unscale_log2,
                                     uint64_t n_elems, uint32_t* lds_max, uint64_t* lds_cnt) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  acc.fold();
   const uint32_t m = wave_max_u32(acc.amax);
   if (lane == 0) {
     lds_max[wave] = m;

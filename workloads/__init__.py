@@ -98,3 +98,27 @@ def mixed_magnitude_fp32(n: int, seed: int, log2_lo: int = -140, log2_hi: int = 
     s = rng.choice([-1.0, 1.0], n)
     with np.errstate(over="ignore"):
         return (s * np.exp2(e)).astype(np.float32)
+
+
+def _ht_chunk(args):
+    row0, nrows, cols, seed = args
+    return row0, heavy_tailed_rows(row0, nrows, cols, seed)
+
+
+def heavy_tailed_parallel(nrows: int = 262144, cols: int = 4096, seed: int = 105,
+                          procs: int = 8, chunk_rows: int = 1024) -> np.ndarray:
+    """``heavy_tailed_rows(0, nrows)`` generated by a process pool (same
+    values: each chunk has its own child seed)."""
+    import multiprocessing as mp
+    assert nrows % chunk_rows == 0, "nrows must be a multiple of chunk_rows"
+    out = np.empty((nrows, cols), dtype=np.uint16)
+    jobs = [(r, chunk_rows, cols, seed) for r in range(0, nrows, chunk_rows)]
+    if procs <= 1:
+        for j in jobs:
+            r, a = _ht_chunk(j)
+            out[r:r + chunk_rows] = a
+        return out
+    with mp.get_context("fork").Pool(procs) as pool:
+        for r, a in pool.imap_unordered(_ht_chunk, jobs):
+            out[r:r + chunk_rows] = a
+    return out
