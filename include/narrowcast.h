@@ -203,8 +203,11 @@ nc_status nc_cast_stats(const nc_tensor *t, int32_t count, nc_dtype dtype, nc_fm
                         const nc_scale_state *st, const nc_loss_scale *ls, nc_stats *out,
                         void *ws, size_t ws_bytes, void *stream);
 
-/* Workspace bytes the statistics need for this batch (binary64 partial sums
- * per 4096-element tile, reduced in a fixed order). */
+/* Workspace bytes the statistics need for this batch: one slot of six
+ * binary64 partial sums per (tensor of a launch, workgroup), reduced in a
+ * fixed order -- min(count, 32) x 4096 slots of 48 bytes.  The workspace is
+ * caller memory (8-byte aligned) and may be reused once the call's work has
+ * completed on its stream. */
 size_t nc_workspace_bytes(const nc_tensor *t, int32_t count);
 
 /* Static description of a status code. */

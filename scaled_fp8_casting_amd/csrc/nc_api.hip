@@ -19,7 +19,8 @@ int grid_for(int64_t tiles) {
     if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && v > 0)
       cus = v;
   }
-  const int64_t cap = (int64_t)cus * kWGPerCU;
+  int64_t cap = (int64_t)cus * kWGPerCU;
+  if (cap > kMaxGrid) cap = kMaxGrid;
   return (int)(tiles < cap ? tiles : cap);
 }
 
@@ -82,13 +83,6 @@ nc_status hip_status(hipError_t e) { return e == hipSuccess ? NC_OK : NC_E_HIP; 
 bool valid_dtype(nc_dtype d) { return d == NC_F32 || d == NC_BF16; }
 bool valid_fmt(nc_fmt f) { return f == NC_E4M3 || f == NC_E5M2; }
 
-int64_t total_stat_tiles(const nc_tensor* t, int32_t count) {
-  int64_t tiles = 0;
-  for (int32_t i = 0; i < count; ++i)
-    if (t[i].n > 0) tiles += (t[i].n + kStatTile - 1) / kStatTile;
-  return tiles;
-}
-
 nc_status check_ws(const nc_tensor* t, int32_t count, void* ws, size_t ws_bytes) {
   if (ws == nullptr || ((uintptr_t)ws & 7u) != 0) return NC_E_WORKSPACE;
   if (ws_bytes < nc_workspace_bytes(t, count)) return NC_E_WORKSPACE;
@@ -100,8 +94,10 @@ nc_status check_ws(const nc_tensor* t, int32_t count, void* ws, size_t ws_bytes)
 extern "C" {
 
 size_t nc_workspace_bytes(const nc_tensor* t, int32_t count) {
+  // one slot of 6 binary64 per (tensor of a launch, workgroup)
   if (t == nullptr || count <= 0) return 0;
-  return (size_t)total_stat_tiles(t, count) * 6 * sizeof(double);
+  const int32_t per_launch = count < kMaxSeg ? count : kMaxSeg;
+  return (size_t)per_launch * kMaxGrid * 6 * sizeof(double);
 }
 
 const char* nc_status_string(nc_status s) {
@@ -160,7 +156,7 @@ nc_status nc_cast_tensor(const nc_tensor* t, int32_t count, nc_dtype dtype, nc_f
   return for_batches(t, count, tile, nullptr, [&](const SegBatch& b) {
     Launch l{grid_for(b.tile0[b.count]), (hipStream_t)stream};
     nc_status r = hip_status(launch_cast_pt(b, dtype, fmt, st, ls, out, part, l));
-    if (r == NC_OK && stats) r = hip_status(launch_stats_finalize(b, part, stats, l.stream));
+    if (r == NC_OK && stats) r = hip_status(launch_stats_finalize(b, part, l.grid, stats, l.stream));
     return r;
   });
 }
@@ -178,7 +174,7 @@ nc_status nc_cast_mx(const nc_tensor* t, int32_t count, nc_dtype dtype, nc_fmt f
   return for_batches(t, count, tile, nullptr, [&](const SegBatch& b) {
     Launch l{grid_for(b.tile0[b.count]), (hipStream_t)stream};
     nc_status r = hip_status(launch_cast_mx(b, dtype, fmt, rule, out, part, l));
-    if (r == NC_OK && stats) r = hip_status(launch_stats_finalize(b, part, stats, l.stream));
+    if (r == NC_OK && stats) r = hip_status(launch_stats_finalize(b, part, l.grid, stats, l.stream));
     return r;
   });
 }
@@ -215,7 +211,7 @@ nc_status nc_cast_stats(const nc_tensor* t, int32_t count, nc_dtype dtype, nc_fm
   return for_batches(t, count, tile, nullptr, [&](const SegBatch& b) {
     Launch l{grid_for(b.tile0[b.count]), (hipStream_t)stream};
     nc_status r = hip_status(launch_stats(b, dtype, fmt, st, ls, part, l));
-    if (r == NC_OK) r = hip_status(launch_stats_finalize(b, part, out, l.stream));
+    if (r == NC_OK) r = hip_status(launch_stats_finalize(b, part, l.grid, out, l.stream));
     return r;
   });
 }

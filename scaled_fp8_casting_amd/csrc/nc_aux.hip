@@ -181,20 +181,27 @@ k_stats(const SegBatch b, const nc_scale_state* __restrict__ st,
         const nc_loss_scale* __restrict__ ls, double* __restrict__ part) {
   constexpr int VEC = In<DT>::VEC;
   constexpr int64_t TILE = (int64_t)kThreads * VEC * kUnroll;
-  __shared__ uint32_t dec[256];
+  __shared__ double tab[256];
   __shared__ double lds_st[kWaves * 6];
-  dec[threadIdx.x] = decode_bits<FMT>(threadIdx.x);
-  __syncthreads();
+  if constexpr (MX) {
+    fill_stat_table<FMT>(tab, 0);
+    __syncthreads();
+  }
   const int s_log2 = (!MX && ls) ? ls->s_log2 : 0;
   const int64_t total = b.tile0[b.count];
   StatAcc sa;
   sa.reset();
-  int seg = -1, k = 0;
+  int seg = -1;
   for (int64_t tile = blockIdx.x; tile < total; tile += gridDim.x) {
     const int s = seg_of(b, tile, seg);
     if (s != seg) {
+      if (seg >= 0) stats_seg_flush(sa, stat_slot(part, seg, blockIdx.x), lds_st, s_log2);
       seg = s;
-      if constexpr (!MX) k = st[b.first + s].k;
+      if constexpr (!MX) {
+        __syncthreads();
+        fill_stat_table<FMT>(tab, st[b.first + s].k - s_log2);
+        __syncthreads();
+      }
     }
     const Seg& g = b.s[s];
     const int64_t e0 = (tile - b.tile0[s]) * TILE;
@@ -220,33 +227,38 @@ k_stats(const SegBatch b, const nc_scale_state* __restrict__ st,
 #pragma unroll
           for (int i = 0; i < 8; ++i) q[i] = (uint32_t)(w >> (8 * i)) & 0xFFu;
         }
-        int kq = k;
-        if constexpr (MX) kq = 127 - (int)g.scales[(e0 + (int64_t)vi * VEC) / 32];
-#pragma unroll
-        for (int i = 0; i < VEC; ++i) stat_elem(xb[i], q[i], s_log2, kq, dec, sa);
+        double blk = 1.0;
+        if constexpr (MX) blk = pow2_f64((int)g.scales[(e0 + (int64_t)vi * VEC) / 32] - 127);
+        stats_vec<VEC, MX>(xb, q, tab, blk, sa);
       }
     } else {
       for (int64_t i = threadIdx.x; i < rem; i += kThreads) {
         const uint32_t xb = load_one<DT>(g.x, e0 + i);
-        int kq = k;
-        if constexpr (MX) kq = 127 - (int)g.scales[(e0 + i) / 32];
-        stat_elem(xb, cs[i], s_log2, kq, dec, sa);
+        const uint32_t q = cs[i];
+        double blk = 1.0;
+        if constexpr (MX) blk = pow2_f64((int)g.scales[(e0 + i) / 32] - 127);
+        stats_vec<1, MX>(&xb, &q, tab, blk, sa);
       }
     }
-    stats_tile_flush(sa, part + tile * 6, lds_st);
   }
+  if (seg >= 0) stats_seg_flush(sa, stat_slot(part, seg, blockIdx.x), lds_st, s_log2);
 }
 
-// One workgroup per tensor: sum its tiles' partials in a fixed order and add
-// the result into out (only this workgroup writes that tensor's stats).
+// One workgroup per tensor: sum the partials of the workgroups that worked
+// on it, in the order of the tensor's first tiles (the producer grid of G
+// workgroups strides over tiles, so tile t went to workgroup t mod G), and
+// add the result into out (only this workgroup writes that tensor's stats).
 __global__ void __launch_bounds__(kThreads)
-k_stats_finalize(const SegBatch b, const double* __restrict__ part, nc_stats* __restrict__ out) {
+k_stats_finalize(const SegBatch b, const double* __restrict__ part, int grid,
+                 nc_stats* __restrict__ out) {
   __shared__ double lds[kWaves * 6];
   const int s = blockIdx.x;
-  const int64_t t0 = b.tile0[s], t1 = b.tile0[s + 1];
+  const int64_t t0 = b.tile0[s], t1 = min(b.tile0[s + 1], b.tile0[s] + grid);
   double acc[6] = {0, 0, 0, 0, 0, 0};
-  for (int64_t t = t0 + threadIdx.x; t < t1; t += kThreads)
-    for (int j = 0; j < 6; ++j) acc[j] += part[t * 6 + j];
+  for (int64_t t = t0 + threadIdx.x; t < t1; t += kThreads) {
+    const double* p = part + ((int64_t)s * kMaxGrid + t % grid) * 6;
+    for (int j = 0; j < 6; ++j) acc[j] += p[j];
+  }
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   for (int j = 0; j < 6; ++j) {
     const double v = wave_sum_f64(acc[j]);
@@ -301,9 +313,9 @@ hipError_t launch_stats(const SegBatch& b, int dtype, int fmt, const nc_scale_st
                          : stats_t<NC_E5M2, NC_BF16>(b, st, ls, part, l);
 }
 
-hipError_t launch_stats_finalize(const SegBatch& b, const double* part, nc_stats* out,
+hipError_t launch_stats_finalize(const SegBatch& b, const double* part, int grid, nc_stats* out,
                                  hipStream_t stream) {
-  hipLaunchKernelGGL(k_stats_finalize, dim3(b.count), dim3(kThreads), 0, stream, b, part, out);
+  hipLaunchKernelGGL(k_stats_finalize, dim3(b.count), dim3(kThreads), 0, stream, b, part, grid, out);
   return hipGetLastError();
 }
 

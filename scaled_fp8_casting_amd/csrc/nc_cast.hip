@@ -90,11 +90,7 @@ k_cast_pt(const SegBatch b, const nc_scale_state* __restrict__ st,
   __shared__ uint32_t lds_max[kWaves];
   __shared__ uint64_t lds_cnt[kWaves * 3];
   __shared__ double lds_st[STATS ? kWaves * 6 : 1];
-  __shared__ uint32_t dec[STATS ? 256 : 1];
-  if constexpr (STATS) {
-    dec[threadIdx.x] = decode_bits<FMT>(threadIdx.x);
-    __syncthreads();
-  }
+  __shared__ double tab[STATS ? 256 : 1];
   const int s_log2 = ls ? ls->s_log2 : 0;
   const int64_t total = b.tile0[b.count];
   Acc acc;
@@ -107,11 +103,19 @@ k_cast_pt(const SegBatch b, const nc_scale_state* __restrict__ st,
   for (int64_t tile = blockIdx.x; tile < total; tile += gridDim.x) {
     const int s = seg_of(b, tile, seg);
     if (s != seg) {
-      if (seg >= 0) flush_counts(acc, out + b.first + seg, s_log2, elems, lds_max, lds_cnt);
+      if (seg >= 0) {
+        flush_counts(acc, out + b.first + seg, s_log2, elems, lds_max, lds_cnt);
+        if constexpr (STATS) stats_seg_flush(sa, stat_slot(part, seg, blockIdx.x), lds_st, s_log2);
+      }
       seg = s;
       elems = 0;
       k = st[b.first + s].k;
       p = cast_params<FMT>(k - s_log2);
+      if constexpr (STATS) {
+        __syncthreads();
+        fill_stat_table<FMT>(tab, k - s_log2);
+        __syncthreads();
+      }
     }
     const Seg& g = b.s[s];
     const int64_t e0 = (tile - b.tile0[s]) * TILE;
@@ -129,10 +133,7 @@ k_cast_pt(const SegBatch b, const nc_scale_state* __restrict__ st,
         unpack<DT>(v[u], xb);
 #pragma unroll
         for (int i = 0; i < VEC; ++i) q[i] = cast_elem<FMT>(xb[i], p, acc);
-        if constexpr (STATS) {
-#pragma unroll
-          for (int i = 0; i < VEC; ++i) stat_elem(xb[i], q[i], s_log2, k, dec, sa);
-        }
+        if constexpr (STATS) stats_vec<VEC, false>(xb, q, tab, 1.0, sa);
         const int vi = u * kThreads + threadIdx.x;
         if constexpr (DT == NC_F32) {
           reinterpret_cast<uint32_t*>(dst)[vi] = q[0] | (q[1] << 8) | (q[2] << 16) | (q[3] << 24);
@@ -150,15 +151,17 @@ k_cast_pt(const SegBatch b, const nc_scale_state* __restrict__ st,
         const bool act = i < rem;
         const uint32_t xb = act ? load_one<DT>(g.x, e0 + i) : 0u;
         const uint32_t q = cast_elem<FMT>(xb, p, acc);
-        if constexpr (STATS) stat_elem(xb, q, s_log2, k, dec, sa);
+        if constexpr (STATS) stats_vec<1, false>(&xb, &q, tab, 1.0, sa);
         if (act) dst[i] = (uint8_t)q;
       }
     }
     elems += rem;
     acc.fold();
-    if constexpr (STATS) stats_tile_flush(sa, part + tile * 6, lds_st);
   }
-  if (seg >= 0) flush_counts(acc, out + b.first + seg, s_log2, elems, lds_max, lds_cnt);
+  if (seg >= 0) {
+    flush_counts(acc, out + b.first + seg, s_log2, elems, lds_max, lds_cnt);
+    if constexpr (STATS) stats_seg_flush(sa, stat_slot(part, seg, blockIdx.x), lds_st, s_log2);
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -195,7 +198,7 @@ __device__ __forceinline__ uint32_t group_max(uint32_t v) {
 // their stores (rem is a multiple of 32, so a block is all in or all out).
 template <int FMT, int DT, int RULE, bool STATS, bool FULL>
 __device__ __forceinline__ void mx_tile(const Seg& g, int64_t e0, int64_t rem, Acc& acc,
-                                        StatAcc& sa, const uint32_t* dec) {
+                                        StatAcc& sa, const double* tab) {
   constexpr int VEC = In<DT>::VEC;
   constexpr int GROUP = 32 / VEC;
   const u32x4* src = reinterpret_cast<const u32x4*>(static_cast<const uint8_t*>(g.x) + e0 * In<DT>::BYTES);
@@ -229,10 +232,7 @@ __device__ __forceinline__ void mx_tile(const Seg& g, int64_t e0, int64_t rem, A
       q[i] = code_of<FMT>(xb[i], ax[i], p, acc);
       __builtin_amdgcn_sched_barrier(0);
     }
-    if constexpr (STATS) {
-#pragma unroll
-      for (int i = 0; i < VEC; ++i) stat_elem(xb[i], q[i], 0, -X, dec, sa);
-    }
+    if constexpr (STATS) stats_vec<VEC, true>(xb, q, tab, pow2_f64(X), sa);
     if (FULL || (int64_t)vi * VEC < rem) {
       if constexpr (DT == NC_F32) {
         reinterpret_cast<uint32_t*>(dst)[vi] = q[0] | (q[1] << 8) | (q[2] << 16) | (q[3] << 24);
@@ -258,9 +258,9 @@ k_cast_mx(const SegBatch b, nc_counts* __restrict__ out, double* __restrict__ pa
   __shared__ uint32_t lds_max[kWaves];
   __shared__ uint64_t lds_cnt[kWaves * 3];
   __shared__ double lds_st[STATS ? kWaves * 6 : 1];
-  __shared__ uint32_t dec[STATS ? 256 : 1];
+  __shared__ double tab[STATS ? 256 : 1];
   if constexpr (STATS) {
-    dec[threadIdx.x] = decode_bits<FMT>(threadIdx.x);
+    fill_stat_table<FMT>(tab, 0);
     __syncthreads();
   }
   const int64_t total = b.tile0[b.count];
@@ -273,20 +273,25 @@ k_cast_mx(const SegBatch b, nc_counts* __restrict__ out, double* __restrict__ pa
   for (int64_t tile = blockIdx.x; tile < total; tile += gridDim.x) {
     const int s = seg_of(b, tile, seg);
     if (s != seg) {
-      if (seg >= 0) flush_counts(acc, out + b.first + seg, 0, elems, lds_max, lds_cnt);
+      if (seg >= 0) {
+        flush_counts(acc, out + b.first + seg, 0, elems, lds_max, lds_cnt);
+        if constexpr (STATS) stats_seg_flush(sa, stat_slot(part, seg, blockIdx.x), lds_st, 0);
+      }
       seg = s;
       elems = 0;
     }
     const Seg& g = b.s[s];
     const int64_t e0 = (tile - b.tile0[s]) * TILE;
     const int64_t rem = min(g.n - e0, TILE);      // a multiple of 32
-    if (rem == TILE) mx_tile<FMT, DT, RULE, STATS, true>(g, e0, rem, acc, sa, dec);
-    else mx_tile<FMT, DT, RULE, STATS, false>(g, e0, rem, acc, sa, dec);
+    if (rem == TILE) mx_tile<FMT, DT, RULE, STATS, true>(g, e0, rem, acc, sa, tab);
+    else mx_tile<FMT, DT, RULE, STATS, false>(g, e0, rem, acc, sa, tab);
     elems += rem;
     acc.fold();
-    if constexpr (STATS) stats_tile_flush(sa, part + tile * 6, lds_st);
   }
-  if (seg >= 0) flush_counts(acc, out + b.first + seg, 0, elems, lds_max, lds_cnt);
+  if (seg >= 0) {
+    flush_counts(acc, out + b.first + seg, 0, elems, lds_max, lds_cnt);
+    if constexpr (STATS) stats_seg_flush(sa, stat_slot(part, seg, blockIdx.x), lds_st, 0);
+  }
 }
 
 template <int FMT, int DT>

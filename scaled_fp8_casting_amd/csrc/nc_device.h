@@ -34,7 +34,7 @@
 namespace nc {
 
 constexpr int kThreads = 256;       // 4 wave64s per workgroup
-constexpr int kStatTile = 4096;     // smallest tile: statistics partials are per tile
+constexpr int kMaxGrid = 4096;      // workgroups per launch at most (statistics slots)
 constexpr int kMaxSeg = 32;         // tensors per launch (descriptors travel as kernel arguments)
 constexpr int kWaves = kThreads / 64;
 
@@ -311,9 +311,12 @@ __device__ __forceinline__ uint32_t load_one(const void* x, int64_t i) {
 }
 
 // ---------------------------------------------------------------------------
-// Error statistics ([Drift, "What the measurements said"]): per element of
-// finite x, e = xhat - x with xhat = decode(q) * 2^-kq; sums of e, |e|, e^2,
-// sign(x) e, x e, x^2 in binary64.  x is taken after the unscale by 2^-s.
+// Error statistics ([Drift, "What the measurements said"]): over finite
+// x, sums of e, |e|, e^2, sign(x) e, x e, x^2 with e = xhat - x, in binary64.
+// They are accumulated in the kernel's input domain (x as stored, xhat =
+// decode(q) * 2^-K with K = k - s); the loss-scale unscale multiplies x and
+// e by 2^-s, so the tile flush scales the first, second and fourth sums by
+// 2^-s and the others by 2^-2s -- exact power-of-two factors.
 struct StatAcc {
   double s[6];
   __device__ void reset() {
@@ -322,23 +325,58 @@ struct StatAcc {
   }
 };
 
-__device__ __forceinline__ void stat_elem(uint32_t xb, uint32_t q, int s_log2, int kq,
-                                          const uint32_t* dec, StatAcc& a) {
-  if ((xb & kAbsMask) > kMaxFinite) return;
-  const double x = ldexp((double)__uint_as_float(xb), -s_log2);
-  const double xh = ldexp((double)__uint_as_float(dec[q]), -kq);
+// LDS table of decode(q) * 2^-K in binary64 (exact: at most 4 significant
+// bits).  NaN codes never meet a finite x; they hold 0.  Threads 0..255
+// each fill one entry.
+template <int FMT>
+__device__ inline void fill_stat_table(double* tab, int K) {
+  const uint32_t b = decode_bits<FMT>(threadIdx.x);
+  tab[threadIdx.x] = ((b & kAbsMask) > kInfBits) ? 0.0 : ldexp((double)__uint_as_float(b), -K);
+}
+
+__device__ __forceinline__ double pow2_f64(int X) {   // 2^X for |X| <= 1022
+  return __longlong_as_double((long long)(X + 1023) << 52);
+}
+
+__device__ __forceinline__ void stat_term(double x, double xh, StatAcc& a) {
   const double e = xh - x;
   a.s[0] += e;
   a.s[1] += fabs(e);
   a.s[2] = fma(e, e, a.s[2]);
-  a.s[3] += (x < 0.0) ? -e : e;
+  a.s[3] += fabs(xh) - fabs(x);    // = sign(x) e: a code keeps its input's sign
   a.s[4] = fma(x, e, a.s[4]);
   a.s[5] = fma(x, x, a.s[5]);
 }
 
-// One tile's partial sums -> part[0..5], in a fixed order (lanes by
-// butterfly, then waves in index order): deterministic.
-__device__ inline void stats_tile_flush(StatAcc& a, double* part_tile, double* lds) {
+// Terms of VEC elements (fp32 patterns xb, codes q); xhat = tab[q] (* blk
+// for MX, the block's 2^X).  A vector whose wave holds no Inf/NaN takes the
+// unmasked path (a wave-uniform branch).
+template <int VEC, bool MX>
+__device__ __forceinline__ void stats_vec(const uint32_t* xb, const uint32_t* q, const double* tab,
+                                          double blk, StatAcc& a) {
+  uint32_t m = 0;
+#pragma unroll
+  for (int i = 0; i < VEC; ++i) m = max(m, xb[i] & kAbsMask);
+  if (__ballot(m > kMaxFinite) == 0) {
+#pragma unroll
+    for (int i = 0; i < VEC; ++i) {
+      const double xh = MX ? tab[q[i]] * blk : tab[q[i]];
+      stat_term((double)__uint_as_float(xb[i]), xh, a);
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < VEC; ++i) {
+      if ((xb[i] & kAbsMask) > kMaxFinite) continue;
+      const double xh = MX ? tab[q[i]] * blk : tab[q[i]];
+      stat_term((double)__uint_as_float(xb[i]), xh, a);
+    }
+  }
+}
+
+// A workgroup's partial sums for one tensor -> part_slot[0..5], scaled back
+// by the unscale, in a fixed order (lanes by butterfly, then waves in index
+// order): deterministic.  Called when the workgroup leaves the tensor.
+__device__ inline void stats_seg_flush(StatAcc& a, double* part_slot, double* lds, int s_log2) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
 #pragma unroll
   for (int j = 0; j < 6; ++j) {
@@ -349,10 +387,17 @@ __device__ inline void stats_tile_flush(StatAcc& a, double* part_tile, double* l
   if (threadIdx.x < 6) {
     double t = 0.0;
     for (int w = 0; w < kWaves; ++w) t += lds[w * 6 + threadIdx.x];
-    part_tile[threadIdx.x] = t;
+    const int j = threadIdx.x;
+    const int sc = (j == 0 || j == 1 || j == 3) ? -s_log2 : -2 * s_log2;
+    part_slot[j] = ldexp(t, sc);
   }
   __syncthreads();
   a.reset();
+}
+
+// Slot of (tensor s of the launch, workgroup g) in the statistics workspace.
+__device__ __forceinline__ double* stat_slot(double* part, int s, int g) {
+  return part + ((int64_t)s * kMaxGrid + g) * 6;
 }
 
 }  // namespace nc

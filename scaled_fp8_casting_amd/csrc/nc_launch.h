@@ -25,7 +25,7 @@ hipError_t launch_cast_mx(const SegBatch& b, int dtype, int fmt, int rule, nc_co
                           double* part, const Launch& l);
 hipError_t launch_stats(const SegBatch& b, int dtype, int fmt, const nc_scale_state* st,
                         const nc_loss_scale* ls, double* part, const Launch& l);
-hipError_t launch_stats_finalize(const SegBatch& b, const double* part, nc_stats* out,
+hipError_t launch_stats_finalize(const SegBatch& b, const double* part, int grid, nc_stats* out,
                                  hipStream_t stream);
 hipError_t launch_dequant(const SegBatch& b, int fmt, const nc_scale_state* st, const Launch& l);
 hipError_t launch_scale_update(const nc_policy& p, int32_t count, nc_scale_state* st, float* hist,

@@ -83,7 +83,8 @@ def test_argument_checks_before_any_launch(lib):
     # statistics need a large enough workspace
     d = _desc((A, A, 10000, 0, None))
     need = lib.nc_workspace_bytes(d, 1)
-    assert need == 3 * 6 * 8
+    assert need == 1 * 4096 * 6 * 8
+    assert lib.nc_workspace_bytes(_desc(*[(A, A, 10, 0, None)] * 40), 40) == 32 * 4096 * 6 * 8
     assert lib.nc_cast_tensor(d, 1, 0, 0, A, None, A, A, A, need - 8, None) == _lib.NC_E_WORKSPACE
     assert lib.nc_cast_stats(d, 1, 0, 0, A, None, A, None, 0, None) == _lib.NC_E_WORKSPACE
     # dequant writes bf16 only
