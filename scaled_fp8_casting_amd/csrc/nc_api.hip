@@ -8,9 +8,10 @@ using namespace nc;
 
 namespace {
 
-// Workgroups per CU for the streaming kernels: 8 x 256 threads = 32 waves
-// per CU (8 per SIMD), enough 16-byte loads in flight to cover HBM latency.
-constexpr int kWGPerCU = 8;
+// Workgroups per CU for the streaming kernels: 16 x 256 threads of grid
+// (resident as registers allow), enough 16-byte loads in flight to cover
+// HBM latency; measured best for read+write streams on MI355X.
+constexpr int kWGPerCU = 16;
 
 int grid_for(int64_t tiles) {
   int dev = 0, cus = 256;

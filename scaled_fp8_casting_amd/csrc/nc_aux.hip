@@ -5,7 +5,6 @@
 namespace nc {
 namespace {
 
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 // ---------------------------------------------------------------------------
 // Scale rule ([E3, "Worked solution"]): the largest k with
@@ -134,7 +133,7 @@ k_dequant(const SegBatch b, const nc_scale_state* __restrict__ st) {
     if (rem == TILE) {
       u32x4 c[2];
 #pragma unroll
-      for (int u = 0; u < 2; ++u) c[u] = reinterpret_cast<const u32x4*>(src)[u * kThreads + threadIdx.x];
+      for (int u = 0; u < 2; ++u) c[u] = ld_stream(reinterpret_cast<const u32x4*>(src) + u * kThreads + threadIdx.x);
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int u = 0; u < 2; ++u) {
@@ -211,7 +210,7 @@ k_stats(const SegBatch b, const nc_scale_state* __restrict__ st,
     if (rem == TILE) {
       u32x4 v[kUnroll];
 #pragma unroll
-      for (int u = 0; u < kUnroll; ++u) v[u] = reinterpret_cast<const u32x4*>(xs)[u * kThreads + threadIdx.x];
+      for (int u = 0; u < kUnroll; ++u) v[u] = ld_stream(reinterpret_cast<const u32x4*>(xs) + u * kThreads + threadIdx.x);
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int u = 0; u < kUnroll; ++u) {

@@ -45,7 +45,7 @@ k_amax(const SegBatch b, const nc_loss_scale* __restrict__ ls, nc_counts* __rest
     if (rem == TILE) {
       u32x4 v[kUnroll];
 #pragma unroll
-      for (int u = 0; u < kUnroll; ++u) v[u] = src[u * kThreads + threadIdx.x];
+      for (int u = 0; u < kUnroll; ++u) v[u] = ld_stream(src + u * kThreads + threadIdx.x);
       __builtin_amdgcn_sched_barrier(0);   // all loads in flight before any use
 #pragma unroll
       for (int u = 0; u < kUnroll; ++u) {
@@ -125,23 +125,24 @@ k_cast_pt(const SegBatch b, const nc_scale_state* __restrict__ st,
     if (rem == TILE) {
       u32x4 v[kUnroll];
 #pragma unroll
-      for (int u = 0; u < kUnroll; ++u) v[u] = src[u * kThreads + threadIdx.x];
+      for (int u = 0; u < kUnroll; ++u) v[u] = ld_stream(src + u * kThreads + threadIdx.x);
       __builtin_amdgcn_sched_barrier(0);   // all loads in flight before any use
 #pragma unroll
       for (int u = 0; u < kUnroll; ++u) {
-        uint32_t xb[VEC], q[VEC];
+        uint32_t xb[VEC], w[VEC / 4];
         unpack<DT>(v[u], xb);
+        cast_vec<FMT, VEC>(xb, p, acc, w);
+        if constexpr (STATS) {
+          uint32_t q[VEC];
 #pragma unroll
-        for (int i = 0; i < VEC; ++i) q[i] = cast_elem<FMT>(xb[i], p, acc);
-        if constexpr (STATS) stats_vec<VEC, false>(xb, q, tab, 1.0, sa);
+          for (int i = 0; i < VEC; ++i) q[i] = (w[i / 4] >> (8 * (i % 4))) & 0xFFu;
+          stats_vec<VEC, false>(xb, q, tab, 1.0, sa);
+        }
         const int vi = u * kThreads + threadIdx.x;
         if constexpr (DT == NC_F32) {
-          reinterpret_cast<uint32_t*>(dst)[vi] = q[0] | (q[1] << 8) | (q[2] << 16) | (q[3] << 24);
+          reinterpret_cast<uint32_t*>(dst)[vi] = w[0];
         } else {
-          u32x2 w;
-          w.x = q[0] | (q[1] << 8) | (q[2] << 16) | (q[3] << 24);
-          w.y = q[4] | (q[5] << 8) | (q[6] << 16) | (q[7] << 24);
-          reinterpret_cast<u32x2*>(dst)[vi] = w;
+          reinterpret_cast<u32x2*>(dst)[vi] = u32x2{w[0], w[1]};
         }
         __builtin_amdgcn_sched_barrier(0);   // keep each vector's ballots short-lived
       }
@@ -150,7 +151,7 @@ k_cast_pt(const SegBatch b, const nc_scale_state* __restrict__ st,
         const int64_t i = base + threadIdx.x;
         const bool act = i < rem;
         const uint32_t xb = act ? load_one<DT>(g.x, e0 + i) : 0u;
-        const uint32_t q = cast_elem<FMT>(xb, p, acc);
+        const uint32_t q = cast_one<FMT>(xb, p, acc);
         if constexpr (STATS) stats_vec<1, false>(&xb, &q, tab, 1.0, sa);
         if (act) dst[i] = (uint8_t)q;
       }
@@ -208,39 +209,49 @@ __device__ __forceinline__ void mx_tile(const Seg& g, int64_t e0, int64_t rem, A
 #pragma unroll
   for (int u = 0; u < kUnroll; ++u) {
     const int vi = u * kThreads + threadIdx.x;
-    if constexpr (FULL) v[u] = src[vi];
-    else v[u] = ((int64_t)vi * VEC < rem) ? src[vi] : u32x4{0u, 0u, 0u, 0u};
+    if constexpr (FULL) v[u] = ld_stream(src + vi);
+    else v[u] = ((int64_t)vi * VEC < rem) ? ld_stream(src + vi) : u32x4{0u, 0u, 0u, 0u};
   }
   __builtin_amdgcn_sched_barrier(0);   // all loads in flight before any use
 #pragma unroll
   for (int u = 0; u < kUnroll; ++u) {
     const int vi = u * kThreads + threadIdx.x;
-    uint32_t xb[VEC], ax[VEC], q[VEC];
+    uint32_t xb[VEC], ax[VEC], w[VEC / 4];
     unpack<DT>(v[u], xb);
     uint32_t m = 0;
 #pragma unroll
     for (int i = 0; i < VEC; ++i) {
       ax[i] = xb[i] & kAbsMask;
-      m = max(m, finite_mag(ax[i], acc));
-      __builtin_amdgcn_sched_barrier(0);   // consume each ballot before the next compare
+      m = max(m, ax[i]);
+    }
+    const bool clean = __ballot(m > kMaxFinite) == 0;   // wave-uniform
+    if (!clean) {                                       // finite amax, count non-finite
+      m = 0;
+#pragma unroll
+      for (int i = 0; i < VEC; ++i) m = max(m, finite_mag(ax[i], acc));
     }
     acc.amax = max(acc.amax, m);
     const int X = mx_exponent<FMT, RULE>(group_max<GROUP>(m));
     const CastParams p = cast_params<FMT>(-X);
 #pragma unroll
-    for (int i = 0; i < VEC; ++i) {
-      q[i] = code_of<FMT>(xb[i], ax[i], p, acc);
-      __builtin_amdgcn_sched_barrier(0);
+    for (int j = 0; j < VEC / 4; ++j) w[j] = cvt4<FMT>(xb + 4 * j, p.K);
+#pragma unroll
+    for (int i = 0; i < VEC; ++i) count_elem(ax[i], p, acc);
+    if (!clean) {
+#pragma unroll
+      for (int j = 0; j < VEC / 4; ++j) w[j] = fix_nonfinite4<FMT>(w[j], xb + 4 * j);
     }
-    if constexpr (STATS) stats_vec<VEC, true>(xb, q, tab, pow2_f64(X), sa);
+    if constexpr (STATS) {
+      uint32_t q[VEC];
+#pragma unroll
+      for (int i = 0; i < VEC; ++i) q[i] = (w[i / 4] >> (8 * (i % 4))) & 0xFFu;
+      stats_vec<VEC, true>(xb, q, tab, pow2_f64(X), sa);
+    }
     if (FULL || (int64_t)vi * VEC < rem) {
       if constexpr (DT == NC_F32) {
-        reinterpret_cast<uint32_t*>(dst)[vi] = q[0] | (q[1] << 8) | (q[2] << 16) | (q[3] << 24);
+        reinterpret_cast<uint32_t*>(dst)[vi] = w[0];
       } else {
-        u32x2 w;
-        w.x = q[0] | (q[1] << 8) | (q[2] << 16) | (q[3] << 24);
-        w.y = q[4] | (q[5] << 8) | (q[6] << 16) | (q[7] << 24);
-        reinterpret_cast<u32x2*>(dst)[vi] = w;
+        reinterpret_cast<u32x2*>(dst)[vi] = u32x2{w[0], w[1]};
       }
       // every lane of the block holds the same X: all store it (same byte,
       // same value), which keeps the tile free of divergent branches

@@ -1,24 +1,30 @@
 // Device-side building blocks of libnarrowcast for CDNA4 (gfx950).
 //
-// The cast of a finite input x at exponent K (the value quantised is
-// y = x * 2^K, formed exactly) is round-to-nearest-even onto the FP8 grid,
-// saturating at the largest finite value ([MP-card, item (3)]: E4M3 max 448,
-// E5M2 max 57344).  It is done in three exact steps:
+// The cast of an input x at exponent K (the value quantised is y = x * 2^K,
+// formed exactly) is round-to-nearest-even onto the FP8 grid, saturating at
+// the largest finite value ([MP-card, item (3)]: E4M3 max 448, E5M2 max
+// 57344).  On gfx950 it runs as:
 //
-//  1. y = ldexp(|x|, K) in fp32.  Exact whenever y is at least fp32's
-//     smallest normal and not above fp32's range.  Outside that: a y above
-//     range is a clip and is replaced below; a y below 2^-126 is far below
-//     half the smallest FP8 subnormal, so its code is zero however it rounds.
-//  2a. Normal FP8 target (y >= 2^emin): re-bias the fp32 exponent and round
-//     the 23-bit mantissa to MB bits on the integer pattern (add half an ulp
-//     minus one plus the kept lsb, then shift); a carry out of the mantissa
-//     moves to the next binade, as it should.
-//  2b. Subnormal FP8 target: y + 2^(emin - MB + 23) in fp32 rounds y to a
-//     multiple of the subnormal quantum 2^(emin - MB) (the float's ulp), and
-//     the difference of the bit patterns is the code.
-//  3. Clip, underflow and non-finite are decided on |x|'s bit pattern
-//     against per-scale thresholds (exact comparisons on the input, never on
-//     the fp32 product).
+//  1. y = ldexp(x, K) in fp32.  Exact whenever y is at least fp32's smallest
+//     normal and not above fp32's range.  Outside that: a y above range is a
+//     clip (saturated in step 3); a y below 2^-126 is far below half the
+//     smallest FP8 subnormal, so its code is zero however it rounds.
+//  2. The hardware pair convert (v_cvt_pk_fp8_f32 / v_cvt_pk_bf8_f32) rounds
+//     y to nearest even.  Measured against the exact definition over all 2^32
+//     fp32 patterns it agrees on every finite y with |y| <= max -- normals,
+//     subnormals, ties and signed zeros -- and differs only where y is out of
+//     range (E4M3 gives the NaN code S.1111.111, E5M2 gives Inf) or not a
+//     number.
+//  3. Saturation, on four packed codes at once: a byte whose low seven bits
+//     are the overflow code (E4M3 0x7F, E5M2 0x7C) is decremented to the
+//     largest finite code of the same sign; no in-range result has those
+//     bits, so nothing else changes.
+//  4. Inputs that are Inf/NaN are rare: a wave whose current vector holds any
+//     takes a uniform branch that rewrites their codes (NaN -> 0x7F, +-Inf ->
+//     +-max) and masks them out of the amax.
+//  5. Clip, underflow and non-finite are decided on |x|'s bit pattern against
+//     per-scale thresholds (exact comparisons on the input, never on the
+//     fp32 product) and counted by wave ballots.
 //
 // Sources cited by title and section: [MP-card] "Mixed Precision
 // FP16/BF16/FP8", [Drift] "what actually breaks low precision training",
@@ -96,22 +102,6 @@ __host__ __device__ inline CastParams cast_params(int K) {
   return p;
 }
 
-// Magnitude code of a finite |x| that does not clip (steps 1-2 above).
-template <int FMT>
-__device__ __forceinline__ uint32_t encode_mag(uint32_t ax, int K) {
-  using F = Fp8<FMT>;
-  constexpr uint32_t kMinNormalBits = (uint32_t)(F::EMIN + 127) << 23;
-  constexpr uint32_t kMagicBits = (uint32_t)(F::EMIN - F::MB + 23 + 127) << 23;
-  constexpr uint32_t kRebias = (uint32_t)(127 - F::BIAS) << 23;
-  constexpr int kShift = 23 - F::MB;
-  const float y = __builtin_amdgcn_ldexpf(__uint_as_float(ax), K);
-  const uint32_t yb = __float_as_uint(y);
-  const uint32_t lsb = (yb >> kShift) & 1u;
-  const uint32_t qn = (yb + ((1u << (kShift - 1)) - 1u) + lsb - kRebias) >> kShift;
-  const uint32_t qs = __float_as_uint(y + __uint_as_float(kMagicBits)) - kMagicBits;
-  return yb < kMinNormalBits ? qs : qn;
-}
-
 // Per-wave running totals.  The counts come from wave ballots and stay
 // wave-uniform (scalar registers): 32-bit within a tile (at most 64 x 64
 // elements per wave), folded into the 64-bit totals once per tile.  amax is
@@ -144,28 +134,103 @@ __device__ __forceinline__ uint32_t finite_mag(uint32_t ax, Acc& acc) {
   return nf ? 0u : ax;
 }
 
-// The 8-bit code of one element (xb: its fp32 pattern, ax = |xb|); counts
-// clips (together with every non-finite, see Acc::n_big) and underflows.
+// Saturation of four packed codes (step 3).
 template <int FMT>
-__device__ __forceinline__ uint32_t code_of(uint32_t xb, uint32_t ax, const CastParams& p, Acc& acc) {
-  using F = Fp8<FMT>;
-  // Saturation needs no compare: the rounded code grows with |y| and is at
-  // least MAXCODE for every |y| > max (including a y that overflowed fp32 to
-  // Inf, whose pattern encodes far above MAXCODE), so min() saturates exactly.
-  uint32_t q = min(encode_mag<FMT>(ax, p.K), F::MAXCODE);
-  acc.t_big += wave_count(ax > p.t_clip);
-  acc.t_uf += wave_count((ax - 1u) < p.t_uf);
-  q |= (xb >> 24) & 0x80u;                  // sign (signed zero included)
-  q = (ax > kInfBits) ? kNaNCode : q;       // NaN: canonical 0x7F
-  return q;
+__device__ __forceinline__ uint32_t sat4(uint32_t w) {
+  // (low 7 bits) + (0x80 - overflow code) reaches bit 7 exactly for the
+  // overflow code and the codes above it (NaN codes, absent here)
+  constexpr uint32_t kBump = FMT == NC_E4M3 ? 0x01010101u : 0x04040404u;
+  const uint32_t t = ((w & 0x7F7F7F7Fu) + kBump) & 0x80808080u;
+  return w - (t >> 7);
 }
 
-// The full element cast: returns the 8-bit code, updates the wave totals.
+// Two fp32 values -> two codes in the low (HI = false) or high (HI = true)
+// half of `old`.
+template <int FMT, bool HI>
+__device__ __forceinline__ int cvt_pair(float a, float b, int old) {
+  if constexpr (FMT == NC_E4M3) return __builtin_amdgcn_cvt_pk_fp8_f32(a, b, old, HI);
+  else return __builtin_amdgcn_cvt_pk_bf8_f32(a, b, old, HI);
+}
+
+// Four elements (fp32 patterns) at exponent K -> four codes, byte i =
+// element i, saturated (steps 1-3).  Exact for every finite input.
 template <int FMT>
-__device__ __forceinline__ uint32_t cast_elem(uint32_t xb, const CastParams& p, Acc& acc) {
+__device__ __forceinline__ uint32_t cvt4(const uint32_t* xb, int K) {
+  const float y0 = __builtin_amdgcn_ldexpf(__uint_as_float(xb[0]), K);
+  const float y1 = __builtin_amdgcn_ldexpf(__uint_as_float(xb[1]), K);
+  const float y2 = __builtin_amdgcn_ldexpf(__uint_as_float(xb[2]), K);
+  const float y3 = __builtin_amdgcn_ldexpf(__uint_as_float(xb[3]), K);
+  int w = cvt_pair<FMT, false>(y0, y1, 0);
+  w = cvt_pair<FMT, true>(y2, y3, w);
+  return sat4<FMT>((uint32_t)w);
+}
+
+// One element -> its code (for ragged tails), saturated.
+template <int FMT>
+__device__ __forceinline__ uint32_t cvt1(uint32_t xb, int K) {
+  const float y = __builtin_amdgcn_ldexpf(__uint_as_float(xb), K);
+  return sat4<FMT>((uint32_t)cvt_pair<FMT, false>(y, 0.0f, 0) & 0xFFu);
+}
+
+// Code of a non-finite element (step 4): NaN -> 0x7F, +-Inf -> +-max.
+template <int FMT>
+__device__ __forceinline__ uint32_t nonfinite_code(uint32_t xb) {
+  return (xb & kAbsMask) > kInfBits ? kNaNCode : (((xb >> 24) & 0x80u) | Fp8<FMT>::MAXCODE);
+}
+
+// Step 4 on a packed word of four codes of elements xb[0..3].
+template <int FMT>
+__device__ inline uint32_t fix_nonfinite4(uint32_t w, const uint32_t* xb) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    if ((xb[i] & kAbsMask) > kMaxFinite)
+      w = (w & ~(0xFFu << (8 * i))) | (nonfinite_code<FMT>(xb[i]) << (8 * i));
+  return w;
+}
+
+// Clip and underflow counts of one element (step 5).  Clip counts include
+// every non-finite element (Acc::n_big); the flush subtracts them.
+__device__ __forceinline__ void count_elem(uint32_t ax, const CastParams& p, Acc& acc) {
+  acc.t_big += wave_count(ax > p.t_clip);
+  acc.t_uf += wave_count((ax - 1u) < p.t_uf);
+}
+
+// Cast VEC elements (a multiple of 4) at one exponent into VEC/4 packed
+// words; counts and the finite amax go to acc.
+template <int FMT, int VEC>
+__device__ __forceinline__ void cast_vec(const uint32_t* xb, const CastParams& p, Acc& acc,
+                                         uint32_t* w) {
+  uint32_t ax[VEC];
+  uint32_t m = 0;
+#pragma unroll
+  for (int i = 0; i < VEC; ++i) {
+    ax[i] = xb[i] & kAbsMask;
+    m = max(m, ax[i]);
+  }
+#pragma unroll
+  for (int j = 0; j < VEC / 4; ++j) w[j] = cvt4<FMT>(xb + 4 * j, p.K);
+#pragma unroll
+  for (int i = 0; i < VEC; ++i) count_elem(ax[i], p, acc);
+  if (__ballot(m > kMaxFinite) == 0) {        // wave-uniform: no Inf/NaN here
+    acc.amax = max(acc.amax, m);
+  } else {
+    uint32_t mf = 0;
+#pragma unroll
+    for (int i = 0; i < VEC; ++i) mf = max(mf, finite_mag(ax[i], acc));
+    acc.amax = max(acc.amax, mf);
+#pragma unroll
+    for (int j = 0; j < VEC / 4; ++j) w[j] = fix_nonfinite4<FMT>(w[j], xb + 4 * j);
+  }
+}
+
+// One element (ragged tails): its code; counts and amax to acc.
+template <int FMT>
+__device__ __forceinline__ uint32_t cast_one(uint32_t xb, const CastParams& p, Acc& acc) {
   const uint32_t ax = xb & kAbsMask;
+  count_elem(ax, p, acc);
   acc.amax = max(acc.amax, finite_mag(ax, acc));
-  return code_of<FMT>(xb, ax, p, acc);
+  const uint32_t q = cvt1<FMT>(xb, p.K);
+  return ax > kMaxFinite ? nonfinite_code<FMT>(xb) : q;
 }
 
 // fp32 bits of RNE(value(a) * 2^-s) for finite non-negative a, s >= 0 (the
@@ -286,6 +351,10 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kUnroll = 4;
+
+// Streaming loads: every input byte is read once per pass, so the loads are
+// non-temporal (the cache lines are not kept for reuse).
+__device__ __forceinline__ u32x4 ld_stream(const u32x4* p) { return __builtin_nontemporal_load(p); }
 
 template <int DT> struct In;
 template <> struct In<NC_F32> { static constexpr int VEC = 4, BYTES = 4; };
