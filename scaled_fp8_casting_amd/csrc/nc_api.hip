@@ -67,7 +67,9 @@ nc_status for_batches(const nc_tensor* t, int32_t count, int64_t tile, void* con
       s.scales = x.scales;
       s.y = y ? y[i] : nullptr;
       s.n = x.n;
-      b.tile0[b.count + 1] = b.tile0[b.count] + (x.n + tile - 1) / tile;
+      const int64_t tiles = (x.n + tile - 1) / tile;
+      b.tile0[b.count + 1] = b.tile0[b.count] + tiles;
+      b.last[b.count] = tiles ? (int32_t)(x.n - (tiles - 1) * tile) : 0;
       ++b.count;
       ++i;
     }
@@ -120,7 +122,7 @@ nc_status nc_amax(const nc_tensor* t, int32_t count, nc_dtype dtype, const nc_lo
   nc_status s = check_tensors(t, count, true, false, false);
   if (s != NC_OK) return s;
   if (count > 0 && out == nullptr) return NC_E_ARG;
-  const int64_t tile = tile_elems(in_bytes(dtype));
+  const int64_t tile = tile_elems(in_bytes(dtype), kUnrollRead);
   return for_batches(t, count, tile, nullptr, [&](const SegBatch& b) {
     Launch l{grid_for(b.tile0[b.count]), (hipStream_t)stream};
     return hip_status(launch_amax(b, dtype, ls, out, l));
@@ -152,7 +154,7 @@ nc_status nc_cast_tensor(const nc_tensor* t, int32_t count, nc_dtype dtype, nc_f
   if (s != NC_OK) return s;
   if (count > 0 && (out == nullptr || st == nullptr)) return NC_E_ARG;
   if (stats && (s = check_ws(t, count, ws, ws_bytes)) != NC_OK) return s;
-  const int64_t tile = tile_elems(in_bytes(dtype));
+  const int64_t tile = tile_elems(in_bytes(dtype), kUnrollCast);
   double* part = stats ? static_cast<double*>(ws) : nullptr;
   return for_batches(t, count, tile, nullptr, [&](const SegBatch& b) {
     Launch l{grid_for(b.tile0[b.count]), (hipStream_t)stream};
@@ -170,7 +172,7 @@ nc_status nc_cast_mx(const nc_tensor* t, int32_t count, nc_dtype dtype, nc_fmt f
   if (s != NC_OK) return s;
   if (count > 0 && out == nullptr) return NC_E_ARG;
   if (stats && (s = check_ws(t, count, ws, ws_bytes)) != NC_OK) return s;
-  const int64_t tile = tile_elems(in_bytes(dtype));
+  const int64_t tile = tile_elems(in_bytes(dtype), kUnrollCast);
   double* part = stats ? static_cast<double*>(ws) : nullptr;
   return for_batches(t, count, tile, nullptr, [&](const SegBatch& b) {
     Launch l{grid_for(b.tile0[b.count]), (hipStream_t)stream};
@@ -207,7 +209,7 @@ nc_status nc_cast_stats(const nc_tensor* t, int32_t count, nc_dtype dtype, nc_fm
   if (s != NC_OK) return s;
   if (count > 0 && out == nullptr) return NC_E_ARG;
   if (count > 0 && (s = check_ws(t, count, ws, ws_bytes)) != NC_OK) return s;
-  const int64_t tile = tile_elems(in_bytes(dtype));
+  const int64_t tile = tile_elems(in_bytes(dtype), kUnrollRead);
   double* part = static_cast<double*>(ws);
   return for_batches(t, count, tile, nullptr, [&](const SegBatch& b) {
     Launch l{grid_for(b.tile0[b.count]), (hipStream_t)stream};

@@ -104,7 +104,7 @@ __device__ __forceinline__ uint32_t dq_bf16(uint32_t dec_bits, int K) {
 }
 
 template <int FMT, bool MX>
-__global__ void __launch_bounds__(kThreads)
+NC_STREAM_KERNEL
 k_dequant(const SegBatch b, const nc_scale_state* __restrict__ st) {
   constexpr int64_t TILE = kDequantTile;      // 16 codes per lane per step, 2 steps
   __shared__ uint32_t tab[256];               // per-tensor: bf16 result; MX: decode bits
@@ -127,10 +127,10 @@ k_dequant(const SegBatch b, const nc_scale_state* __restrict__ st) {
     }
     const Seg& g = b.s[s];
     const int64_t e0 = (tile - b.tile0[s]) * TILE;
-    const int64_t rem = min(g.n - e0, TILE);
+    const int rem = tile_len<TILE>(b, s, tile);
     const uint8_t* src = g.codes + e0;
     uint16_t* dst = static_cast<uint16_t*>(g.y) + e0;
-    if (rem == TILE) {
+    if (rem == (int)TILE) {
       u32x4 c[2];
 #pragma unroll
       for (int u = 0; u < 2; ++u) c[u] = ld_stream(reinterpret_cast<const u32x4*>(src) + u * kThreads + threadIdx.x);
@@ -159,7 +159,7 @@ k_dequant(const SegBatch b, const nc_scale_state* __restrict__ st) {
         d[1] = u32x4{o[4], o[5], o[6], o[7]};
       }
     } else {
-      for (int64_t i = threadIdx.x; i < rem; i += kThreads) {
+      for (int i = threadIdx.x; i < rem; i += kThreads) {
         const uint32_t q = src[i];
         if constexpr (MX) {
           const int K = 127 - (int)g.scales[(e0 + i) / 32];
@@ -175,11 +175,11 @@ k_dequant(const SegBatch b, const nc_scale_state* __restrict__ st) {
 // ---------------------------------------------------------------------------
 // Statistics as a separate pass over x and the codes (and the MX scales).
 template <int FMT, int DT, bool MX>
-__global__ void __launch_bounds__(kThreads)
+NC_STREAM_KERNEL
 k_stats(const SegBatch b, const nc_scale_state* __restrict__ st,
         const nc_loss_scale* __restrict__ ls, double* __restrict__ part) {
   constexpr int VEC = In<DT>::VEC;
-  constexpr int64_t TILE = (int64_t)kThreads * VEC * kUnroll;
+  constexpr int64_t TILE = (int64_t)kThreads * VEC * kUnrollRead;
   __shared__ double tab[256];
   __shared__ double lds_st[kWaves * 6];
   if constexpr (MX) {
@@ -191,6 +191,9 @@ k_stats(const SegBatch b, const nc_scale_state* __restrict__ st,
   StatAcc sa;
   sa.reset();
   int seg = -1;
+  // buf always holds the current tile when it is full (prefetch invariant)
+  u32x4 buf[kUnrollRead];
+  prefetch_tile<In<DT>::BYTES, kUnrollRead, TILE>(b, blockIdx.x, -1, buf);
   for (int64_t tile = blockIdx.x; tile < total; tile += gridDim.x) {
     const int s = seg_of(b, tile, seg);
     if (s != seg) {
@@ -204,16 +207,16 @@ k_stats(const SegBatch b, const nc_scale_state* __restrict__ st,
     }
     const Seg& g = b.s[s];
     const int64_t e0 = (tile - b.tile0[s]) * TILE;
-    const int64_t rem = min(g.n - e0, TILE);
-    const uint8_t* xs = static_cast<const uint8_t*>(g.x) + e0 * In<DT>::BYTES;
+    const int rem = tile_len<TILE>(b, s, tile);
     const uint8_t* cs = g.codes + e0;
-    if (rem == TILE) {
-      u32x4 v[kUnroll];
+    if (rem == (int)TILE) {
+      u32x4 v[kUnrollRead];
 #pragma unroll
-      for (int u = 0; u < kUnroll; ++u) v[u] = ld_stream(reinterpret_cast<const u32x4*>(xs) + u * kThreads + threadIdx.x);
+      for (int u = 0; u < kUnrollRead; ++u) v[u] = buf[u];
+      prefetch_tile<In<DT>::BYTES, kUnrollRead, TILE>(b, tile + gridDim.x, s, buf);
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-      for (int u = 0; u < kUnroll; ++u) {
+      for (int u = 0; u < kUnrollRead; ++u) {
         const int vi = u * kThreads + threadIdx.x;
         uint32_t xb[VEC], q[VEC];
         unpack<DT>(v[u], xb);
@@ -231,7 +234,8 @@ k_stats(const SegBatch b, const nc_scale_state* __restrict__ st,
         stats_vec<VEC, MX>(xb, q, tab, blk, sa);
       }
     } else {
-      for (int64_t i = threadIdx.x; i < rem; i += kThreads) {
+      prefetch_tile<In<DT>::BYTES, kUnrollRead, TILE>(b, tile + gridDim.x, s, buf);
+      for (int i = threadIdx.x; i < rem; i += kThreads) {
         const uint32_t xb = load_one<DT>(g.x, e0 + i);
         const uint32_t q = cs[i];
         double blk = 1.0;

@@ -19,10 +19,10 @@ namespace {
 // ---------------------------------------------------------------------------
 // Per-tensor amax pass.
 template <int DT>
-__global__ void __launch_bounds__(kThreads)
+NC_STREAM_KERNEL
 k_amax(const SegBatch b, const nc_loss_scale* __restrict__ ls, nc_counts* __restrict__ out) {
   constexpr int VEC = In<DT>::VEC;
-  constexpr int64_t TILE = (int64_t)kThreads * VEC * kUnroll;
+  constexpr int64_t TILE = (int64_t)kThreads * VEC * kUnrollRead;
   __shared__ uint32_t lds_max[kWaves];
   __shared__ uint64_t lds_cnt[kWaves * 3];
   const int s_log2 = ls ? ls->s_log2 : 0;
@@ -31,62 +31,62 @@ k_amax(const SegBatch b, const nc_loss_scale* __restrict__ ls, nc_counts* __rest
   acc.reset();
   int seg = -1;
   uint64_t elems = 0;
+  // buf always holds the current tile when it is full (prefetch invariant)
+  u32x4 buf[kUnrollRead];
+  prefetch_tile<In<DT>::BYTES, kUnrollRead, TILE>(b, blockIdx.x, -1, buf);
   for (int64_t tile = blockIdx.x; tile < total; tile += gridDim.x) {
     const int s = seg_of(b, tile, seg);
     if (s != seg) {
-      if (seg >= 0) flush_counts(acc, out + b.first + seg, s_log2, elems, lds_max, lds_cnt);
+      if (seg >= 0) {
+        acc.n_big = acc.n_nf;   // the amax pass reports no clips
+        flush_counts(acc, out + b.first + seg, s_log2, elems, lds_max, lds_cnt);
+      }
       seg = s;
       elems = 0;
     }
     const Seg& g = b.s[s];
     const int64_t e0 = (tile - b.tile0[s]) * TILE;
-    const int64_t rem = min(g.n - e0, TILE);
-    const u32x4* src = reinterpret_cast<const u32x4*>(static_cast<const uint8_t*>(g.x) + e0 * In<DT>::BYTES);
-    if (rem == TILE) {
-      u32x4 v[kUnroll];
+    const int rem = tile_len<TILE>(b, s, tile);
+    if (rem == (int)TILE) {
+      u32x4 v[kUnrollRead];
 #pragma unroll
-      for (int u = 0; u < kUnroll; ++u) v[u] = ld_stream(src + u * kThreads + threadIdx.x);
-      __builtin_amdgcn_sched_barrier(0);   // all loads in flight before any use
+      for (int u = 0; u < kUnrollRead; ++u) v[u] = buf[u];
+      prefetch_tile<In<DT>::BYTES, kUnrollRead, TILE>(b, tile + gridDim.x, s, buf);
+      __builtin_amdgcn_sched_barrier(0);   // next tile's loads in flight before any use
 #pragma unroll
-      for (int u = 0; u < kUnroll; ++u) {
+      for (int u = 0; u < kUnrollRead; ++u) {
         uint32_t xb[VEC];
         unpack<DT>(v[u], xb);
 #pragma unroll
         for (int i = 0; i < VEC; ++i) {
-          const uint32_t ax = xb[i] & kAbsMask;
-          const bool nf = ax > kMaxFinite;
-          acc.amax = max(acc.amax, nf ? 0u : ax);
-          const uint32_t c = wave_count(nf);
-          acc.t_nf += c;
-          acc.t_big += c;   // the amax pass reports no clips
+          acc.amax = max(acc.amax, finite_mag(xb[i] & kAbsMask, acc));
         }
       }
     } else {
-      for (int64_t base = 0; base < rem; base += kThreads) {
-        const int64_t i = base + threadIdx.x;
+      prefetch_tile<In<DT>::BYTES, kUnrollRead, TILE>(b, tile + gridDim.x, s, buf);
+      for (int base = 0; base < rem; base += kThreads) {
+        const int i = base + (int)threadIdx.x;
         const uint32_t ax = (i < rem ? load_one<DT>(g.x, e0 + i) : 0u) & kAbsMask;
-        const bool nf = ax > kMaxFinite;
-        acc.amax = max(acc.amax, nf ? 0u : ax);
-        const uint32_t c = wave_count(nf);
-        acc.t_nf += c;
-        acc.t_big += c;
+        acc.amax = max(acc.amax, finite_mag(ax, acc));
       }
     }
     elems += rem;
-    acc.fold();
   }
-  if (seg >= 0) flush_counts(acc, out + b.first + seg, s_log2, elems, lds_max, lds_cnt);
+  if (seg >= 0) {
+    acc.n_big = acc.n_nf;   // the amax pass reports no clips
+    flush_counts(acc, out + b.first + seg, s_log2, elems, lds_max, lds_cnt);
+  }
 }
 
 // ---------------------------------------------------------------------------
 // Per-tensor cast: code = RNE-sat(x * 2^(k - s)).
 template <int FMT, int DT, bool STATS>
-__global__ void __launch_bounds__(kThreads)
+NC_STREAM_KERNEL
 k_cast_pt(const SegBatch b, const nc_scale_state* __restrict__ st,
           const nc_loss_scale* __restrict__ ls, nc_counts* __restrict__ out,
           double* __restrict__ part) {
   constexpr int VEC = In<DT>::VEC;
-  constexpr int64_t TILE = (int64_t)kThreads * VEC * kUnroll;
+  constexpr int64_t TILE = (int64_t)kThreads * VEC * kUnrollCast;
   __shared__ uint32_t lds_max[kWaves];
   __shared__ uint64_t lds_cnt[kWaves * 3];
   __shared__ double lds_st[STATS ? kWaves * 6 : 1];
@@ -100,6 +100,9 @@ k_cast_pt(const SegBatch b, const nc_scale_state* __restrict__ st,
   int seg = -1, k = 0;
   CastParams p = cast_params<FMT>(0);
   uint64_t elems = 0;
+  // buf always holds the current tile when it is full (prefetch invariant)
+  u32x4 buf[kUnrollCast];
+  prefetch_tile<In<DT>::BYTES, kUnrollCast, TILE>(b, blockIdx.x, -1, buf);
   for (int64_t tile = blockIdx.x; tile < total; tile += gridDim.x) {
     const int s = seg_of(b, tile, seg);
     if (s != seg) {
@@ -119,16 +122,16 @@ k_cast_pt(const SegBatch b, const nc_scale_state* __restrict__ st,
     }
     const Seg& g = b.s[s];
     const int64_t e0 = (tile - b.tile0[s]) * TILE;
-    const int64_t rem = min(g.n - e0, TILE);
-    const u32x4* src = reinterpret_cast<const u32x4*>(static_cast<const uint8_t*>(g.x) + e0 * In<DT>::BYTES);
+    const int rem = tile_len<TILE>(b, s, tile);
     uint8_t* dst = g.codes + e0;
-    if (rem == TILE) {
-      u32x4 v[kUnroll];
+    if (rem == (int)TILE) {
+      u32x4 v[kUnrollCast];
 #pragma unroll
-      for (int u = 0; u < kUnroll; ++u) v[u] = ld_stream(src + u * kThreads + threadIdx.x);
-      __builtin_amdgcn_sched_barrier(0);   // all loads in flight before any use
+      for (int u = 0; u < kUnrollCast; ++u) v[u] = buf[u];
+      prefetch_tile<In<DT>::BYTES, kUnrollCast, TILE>(b, tile + gridDim.x, s, buf);
+      __builtin_amdgcn_sched_barrier(0);   // next tile's loads in flight before any use
 #pragma unroll
-      for (int u = 0; u < kUnroll; ++u) {
+      for (int u = 0; u < kUnrollCast; ++u) {
         uint32_t xb[VEC], w[VEC / 4];
         unpack<DT>(v[u], xb);
         cast_vec<FMT, VEC>(xb, p, acc, w);
@@ -147,8 +150,9 @@ k_cast_pt(const SegBatch b, const nc_scale_state* __restrict__ st,
         __builtin_amdgcn_sched_barrier(0);   // keep each vector's ballots short-lived
       }
     } else {
-      for (int64_t base = 0; base < rem; base += kThreads) {
-        const int64_t i = base + threadIdx.x;
+      prefetch_tile<In<DT>::BYTES, kUnrollCast, TILE>(b, tile + gridDim.x, s, buf);
+      for (int base = 0; base < rem; base += kThreads) {
+        const int i = base + (int)threadIdx.x;
         const bool act = i < rem;
         const uint32_t xb = act ? load_one<DT>(g.x, e0 + i) : 0u;
         const uint32_t q = cast_one<FMT>(xb, p, acc);
@@ -157,7 +161,6 @@ k_cast_pt(const SegBatch b, const nc_scale_state* __restrict__ st,
       }
     }
     elems += rem;
-    acc.fold();
   }
   if (seg >= 0) {
     flush_counts(acc, out + b.first + seg, s_log2, elems, lds_max, lds_cnt);
@@ -194,27 +197,19 @@ __device__ __forceinline__ uint32_t group_max(uint32_t v) {
   return v;
 }
 
-// One tile of the MX cast.  FULL: every lane's vector is inside the tensor
-// (no predicates at all); otherwise lanes past `rem` load zeros and skip
-// their stores (rem is a multiple of 32, so a block is all in or all out).
+// One tile of the MX cast, from this lane's vectors v.  FULL: every lane's
+// vector is inside the tensor (no predicates at all); otherwise lanes past
+// `rem` hold zeros and skip their stores (rem is a multiple of 32, so a
+// block is all in or all out).
 template <int FMT, int DT, int RULE, bool STATS, bool FULL>
-__device__ __forceinline__ void mx_tile(const Seg& g, int64_t e0, int64_t rem, Acc& acc,
-                                        StatAcc& sa, const double* tab) {
+__device__ __forceinline__ void mx_tile(const Seg& g, int64_t e0, int rem, const u32x4* v,
+                                        Acc& acc, StatAcc& sa, const double* tab) {
   constexpr int VEC = In<DT>::VEC;
   constexpr int GROUP = 32 / VEC;
-  const u32x4* src = reinterpret_cast<const u32x4*>(static_cast<const uint8_t*>(g.x) + e0 * In<DT>::BYTES);
   uint8_t* dst = g.codes + e0;
   uint8_t* sdst = g.scales + e0 / 32;
-  u32x4 v[kUnroll];
 #pragma unroll
-  for (int u = 0; u < kUnroll; ++u) {
-    const int vi = u * kThreads + threadIdx.x;
-    if constexpr (FULL) v[u] = ld_stream(src + vi);
-    else v[u] = ((int64_t)vi * VEC < rem) ? ld_stream(src + vi) : u32x4{0u, 0u, 0u, 0u};
-  }
-  __builtin_amdgcn_sched_barrier(0);   // all loads in flight before any use
-#pragma unroll
-  for (int u = 0; u < kUnroll; ++u) {
+  for (int u = 0; u < kUnrollCast; ++u) {
     const int vi = u * kThreads + threadIdx.x;
     uint32_t xb[VEC], ax[VEC], w[VEC / 4];
     unpack<DT>(v[u], xb);
@@ -247,7 +242,7 @@ __device__ __forceinline__ void mx_tile(const Seg& g, int64_t e0, int64_t rem, A
       for (int i = 0; i < VEC; ++i) q[i] = (w[i / 4] >> (8 * (i % 4))) & 0xFFu;
       stats_vec<VEC, true>(xb, q, tab, pow2_f64(X), sa);
     }
-    if (FULL || (int64_t)vi * VEC < rem) {
+    if (FULL || vi * VEC < rem) {
       if constexpr (DT == NC_F32) {
         reinterpret_cast<uint32_t*>(dst)[vi] = w[0];
       } else {
@@ -262,10 +257,10 @@ __device__ __forceinline__ void mx_tile(const Seg& g, int64_t e0, int64_t rem, A
 }
 
 template <int FMT, int DT, int RULE, bool STATS>
-__global__ void __launch_bounds__(kThreads)
+NC_STREAM_KERNEL
 k_cast_mx(const SegBatch b, nc_counts* __restrict__ out, double* __restrict__ part) {
   constexpr int VEC = In<DT>::VEC;
-  constexpr int64_t TILE = (int64_t)kThreads * VEC * kUnroll;
+  constexpr int64_t TILE = (int64_t)kThreads * VEC * kUnrollCast;
   __shared__ uint32_t lds_max[kWaves];
   __shared__ uint64_t lds_cnt[kWaves * 3];
   __shared__ double lds_st[STATS ? kWaves * 6 : 1];
@@ -281,6 +276,9 @@ k_cast_mx(const SegBatch b, nc_counts* __restrict__ out, double* __restrict__ pa
   if constexpr (STATS) sa.reset();
   int seg = -1;
   uint64_t elems = 0;
+  // buf always holds the current tile when it is full (prefetch invariant)
+  u32x4 buf[kUnrollCast];
+  prefetch_tile<In<DT>::BYTES, kUnrollCast, TILE>(b, blockIdx.x, -1, buf);
   for (int64_t tile = blockIdx.x; tile < total; tile += gridDim.x) {
     const int s = seg_of(b, tile, seg);
     if (s != seg) {
@@ -293,11 +291,25 @@ k_cast_mx(const SegBatch b, nc_counts* __restrict__ out, double* __restrict__ pa
     }
     const Seg& g = b.s[s];
     const int64_t e0 = (tile - b.tile0[s]) * TILE;
-    const int64_t rem = min(g.n - e0, TILE);      // a multiple of 32
-    if (rem == TILE) mx_tile<FMT, DT, RULE, STATS, true>(g, e0, rem, acc, sa, tab);
-    else mx_tile<FMT, DT, RULE, STATS, false>(g, e0, rem, acc, sa, tab);
+    const int rem = tile_len<TILE>(b, s, tile);   // a multiple of 32
+    u32x4 v[kUnrollCast];
+    if (rem == (int)TILE) {
+#pragma unroll
+      for (int u = 0; u < kUnrollCast; ++u) v[u] = buf[u];
+      prefetch_tile<In<DT>::BYTES, kUnrollCast, TILE>(b, tile + gridDim.x, s, buf);
+      __builtin_amdgcn_sched_barrier(0);   // next tile's loads in flight before any use
+      mx_tile<FMT, DT, RULE, STATS, true>(g, e0, rem, v, acc, sa, tab);
+    } else {
+      prefetch_tile<In<DT>::BYTES, kUnrollCast, TILE>(b, tile + gridDim.x, s, buf);
+      const u32x4* src = reinterpret_cast<const u32x4*>(static_cast<const uint8_t*>(g.x) + e0 * In<DT>::BYTES);
+#pragma unroll
+      for (int u = 0; u < kUnrollCast; ++u) {
+        const int vi = u * kThreads + threadIdx.x;
+        v[u] = (vi * VEC < rem) ? ld_stream(src + vi) : u32x4{0u, 0u, 0u, 0u};
+      }
+      mx_tile<FMT, DT, RULE, STATS, false>(g, e0, rem, v, acc, sa, tab);
+    }
     elems += rem;
-    acc.fold();
   }
   if (seg >= 0) {
     flush_counts(acc, out + b.first + seg, 0, elems, lds_max, lds_cnt);

@@ -24,7 +24,7 @@
 //     +-max) and masks them out of the amax.
 //  5. Clip, underflow and non-finite are decided on |x|'s bit pattern against
 //     per-scale thresholds (exact comparisons on the input, never on the
-//     fp32 product) and counted by wave ballots.
+//     fp32 product) and counted per lane.
 //
 // Sources cited by title and section: [MP-card] "Mixed Precision
 // FP16/BF16/FP8", [Drift] "what actually breaks low precision training",
@@ -43,6 +43,16 @@ constexpr int kThreads = 256;       // 4 wave64s per workgroup
 constexpr int kMaxGrid = 4096;      // workgroups per launch at most (statistics slots)
 constexpr int kMaxSeg = 32;         // tensors per launch (descriptors travel as kernel arguments)
 constexpr int kWaves = kThreads / 64;
+
+// Streaming kernels: optional occupancy request (waves per SIMD).
+#ifndef NC_WAVES_PER_EU
+#define NC_WAVES_PER_EU 0
+#endif
+#if NC_WAVES_PER_EU
+#define NC_STREAM_KERNEL __global__ void __launch_bounds__(nc::kThreads) __attribute__((amdgpu_waves_per_eu(NC_WAVES_PER_EU, 8)))
+#else
+#define NC_STREAM_KERNEL __global__ void __launch_bounds__(nc::kThreads)
+#endif
 
 // ---------------------------------------------------------------------------
 // Formats.  E4M3: bias 7, no Inf, S.1111.111 is NaN, max 1.75*2^8 = 448.
@@ -102,35 +112,23 @@ __host__ __device__ inline CastParams cast_params(int K) {
   return p;
 }
 
-// Per-wave running totals.  The counts come from wave ballots and stay
-// wave-uniform (scalar registers): 32-bit within a tile (at most 64 x 64
-// elements per wave), folded into the 64-bit totals once per tile.  amax is
-// per lane until the flush.
+// Per-lane running totals: each lane counts its own elements (a compare
+// and an add per count, no scalar traffic) and the flush reduces them.  A
+// lane handles at most n / (grid x 256) elements of a tensor per visit, far
+// below 2^32.
 struct Acc {
-  uint64_t n_nf;     // non-finite elements
-  uint64_t n_big;    // |x| bits above t_clip: every clip plus every non-finite
-  uint64_t n_uf;
-  uint32_t t_nf, t_big, t_uf;   // the current tile's counts
-  uint32_t amax;     // largest finite |x| bits (lane-local)
-  __device__ void reset() { n_nf = n_big = n_uf = 0; t_nf = t_big = t_uf = 0; amax = 0; }
-  __device__ void fold() {
-    n_nf += t_nf;
-    n_big += t_big;
-    n_uf += t_uf;
-    t_nf = t_big = t_uf = 0;
-  }
+  uint32_t n_nf;     // non-finite elements
+  uint32_t n_big;    // |x| bits above t_clip: every clip plus every non-finite
+  uint32_t n_uf;
+  uint32_t amax;     // largest finite |x| bits
+  __device__ void reset() { n_nf = n_big = n_uf = 0; amax = 0; }
 };
 
-__device__ __forceinline__ uint32_t wave_count(bool p) {
-  return (uint32_t)__popcll(__ballot(p));
-}
-
 // |x| bits with Inf/NaN mapped to 0 (for the amax), counting non-finite
-// elements.  The ballot consumes the compare at once, so no lane mask stays
-// live in scalar registers.
+// elements.
 __device__ __forceinline__ uint32_t finite_mag(uint32_t ax, Acc& acc) {
   const bool nf = ax > kMaxFinite;
-  acc.t_nf += wave_count(nf);
+  acc.n_nf += nf ? 1u : 0u;
   return nf ? 0u : ax;
 }
 
@@ -191,8 +189,8 @@ __device__ inline uint32_t fix_nonfinite4(uint32_t w, const uint32_t* xb) {
 // Clip and underflow counts of one element (step 5).  Clip counts include
 // every non-finite element (Acc::n_big); the flush subtracts them.
 __device__ __forceinline__ void count_elem(uint32_t ax, const CastParams& p, Acc& acc) {
-  acc.t_big += wave_count(ax > p.t_clip);
-  acc.t_uf += wave_count((ax - 1u) < p.t_uf);
+  acc.n_big += (ax > p.t_clip) ? 1u : 0u;
+  acc.n_uf += ((ax - 1u) < p.t_uf) ? 1u : 0u;
 }
 
 // Cast VEC elements (a multiple of 4) at one exponent into VEC/4 packed
@@ -270,9 +268,11 @@ struct Seg {
 struct SegBatch {
   Seg s[kMaxSeg];
   int64_t tile0[kMaxSeg + 1];
+  int32_t last[kMaxSeg];   // elements in tensor s's last tile (1..tile size; 0 if empty)
   int32_t count;   // tensors in this launch
   int32_t first;   // index of s[0] in the caller's arrays (counts, states, stats)
 };
+static_assert(sizeof(SegBatch) <= 4096, "a SegBatch travels as a kernel argument");
 
 // Tensor owning `tile`, scanning forward from `hint` (tiles visited by a
 // workgroup only increase, so the scan is amortised O(1)).
@@ -282,34 +282,51 @@ __device__ __forceinline__ int seg_of(const SegBatch& b, int64_t tile, int hint)
   return s;
 }
 
+// Elements in tile t of tensor s: TILE, except in the tensor's last tile.
+// Written as a 64-bit equality plus a 32-bit select on purpose.  The gfx950
+// backend of this ROCm toolchain has been seen to lower min(n - e0, TILE)
+// (a 64-bit ordered compare whose result feeds both a select and a branch)
+// with the vector compare's copy into the scalar condition code dropped, so
+// the select read a stale carry flag and a ragged tile ran as a full one.
+// The library build scans the device assembly for that signature.
+template <int64_t TILE>
+__device__ __forceinline__ int tile_len(const SegBatch& b, int s, int64_t t) {
+  return t == b.tile0[s + 1] - 1 ? b.last[s] : (int)TILE;
+}
+
 // Workgroup flush of one tensor's totals into its nc_counts (integer
 // atomics: order-independent, so deterministic).
+__device__ __forceinline__ uint32_t wave_sum_u32(uint32_t v) {
+  for (int o = 32; o > 0; o >>= 1) v += (uint32_t)__shfl_xor((int)v, o, 64);
+  return v;
+}
+
 __device__ inline void flush_counts(Acc& acc, nc_counts* out, int unscale_log2,
                                     uint64_t n_elems, uint32_t* lds_max, uint64_t* lds_cnt) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  acc.fold();
   const uint32_t m = wave_max_u32(acc.amax);
+  const uint32_t nf = wave_sum_u32(acc.n_nf), big = wave_sum_u32(acc.n_big), uf = wave_sum_u32(acc.n_uf);
   if (lane == 0) {
     lds_max[wave] = m;
-    lds_cnt[wave * 3 + 0] = acc.n_nf;
-    lds_cnt[wave * 3 + 1] = acc.n_big;
-    lds_cnt[wave * 3 + 2] = acc.n_uf;
+    lds_cnt[wave * 3 + 0] = nf;
+    lds_cnt[wave * 3 + 1] = big;
+    lds_cnt[wave * 3 + 2] = uf;
   }
   __syncthreads();
   if (threadIdx.x == 0) {
     uint32_t mx = 0;
-    uint64_t nf = 0, big = 0, uf = 0;
+    uint64_t tnf = 0, tbig = 0, tuf = 0;
     for (int w = 0; w < kWaves; ++w) {
       mx = max(mx, lds_max[w]);
-      nf += lds_cnt[w * 3 + 0];
-      big += lds_cnt[w * 3 + 1];
-      uf += lds_cnt[w * 3 + 2];
+      tnf += lds_cnt[w * 3 + 0];
+      tbig += lds_cnt[w * 3 + 1];
+      tuf += lds_cnt[w * 3 + 2];
     }
     atomicMax(&out->amax_bits, unscale_bits(mx, unscale_log2));
-    if (n_elems - nf) atomicAdd((unsigned long long*)&out->n_finite, (unsigned long long)(n_elems - nf));
-    if (nf) atomicAdd((unsigned long long*)&out->n_nonfinite, (unsigned long long)nf);
-    if (big - nf) atomicAdd((unsigned long long*)&out->n_clip, (unsigned long long)(big - nf));
-    if (uf) atomicAdd((unsigned long long*)&out->n_underflow, (unsigned long long)uf);
+    if (n_elems - tnf) atomicAdd((unsigned long long*)&out->n_finite, (unsigned long long)(n_elems - tnf));
+    if (tnf) atomicAdd((unsigned long long*)&out->n_nonfinite, (unsigned long long)tnf);
+    if (tbig - tnf) atomicAdd((unsigned long long*)&out->n_clip, (unsigned long long)(tbig - tnf));
+    if (tuf) atomicAdd((unsigned long long*)&out->n_underflow, (unsigned long long)tuf);
   }
   __syncthreads();
   acc.reset();
@@ -350,11 +367,32 @@ __device__ __forceinline__ uint32_t f32_to_bf16_rne(uint32_t b) {
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
-constexpr int kUnroll = 4;
+// 16-byte loads per lane per tile: read-only passes (amax, statistics) keep
+// four in flight, the casts eight (measured best on MI355X).
+constexpr int kUnrollRead = 4;
+constexpr int kUnrollCast = 8;
 
 // Streaming loads: every input byte is read once per pass, so the loads are
 // non-temporal (the cache lines are not kept for reuse).
 __device__ __forceinline__ u32x4 ld_stream(const u32x4* p) { return __builtin_nontemporal_load(p); }
+
+// Register double buffer: while a workgroup computes one tile, the loads of
+// its next tile in the grid-stride sequence are already in flight.  Loads
+// this lane's vectors of tile t into v when t is a full tile of TILE
+// elements of IN_BYTES bytes (from the codes when CODES, else from x);
+// returns t, or -1 when t is past the end or ragged.
+template <int IN_BYTES, int U, int64_t TILE, bool CODES = false>
+__device__ __forceinline__ int64_t prefetch_tile(const SegBatch& b, int64_t t, int hint, u32x4* v) {
+  if (t >= b.tile0[b.count]) return -1;
+  const int s = seg_of(b, t, hint);
+  if (tile_len<TILE>(b, s, t) != (int)TILE) return -1;
+  const int64_t e0 = (t - b.tile0[s]) * TILE;
+  const void* base = CODES ? static_cast<const void*>(b.s[s].codes) : b.s[s].x;
+  const u32x4* src = reinterpret_cast<const u32x4*>(static_cast<const uint8_t*>(base) + e0 * IN_BYTES);
+#pragma unroll
+  for (int u = 0; u < U; ++u) v[u] = ld_stream(src + u * kThreads + threadIdx.x);
+  return t;
+}
 
 template <int DT> struct In;
 template <> struct In<NC_F32> { static constexpr int VEC = 4, BYTES = 4; };

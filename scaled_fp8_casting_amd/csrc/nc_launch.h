@@ -7,9 +7,8 @@
 namespace nc {
 
 // Elements per tile of a kernel that reads `in_bytes`-wide elements with
-// four 16-byte loads per thread: 4096 for fp32, 8192 for bf16 (and for the
-// byte-code reads of dequant, 256 * 16 * 2).
-inline int64_t tile_elems(int in_bytes) { return (int64_t)kThreads * (16 / in_bytes) * 4; }
+// `unroll` 16-byte loads per thread (dequant reads codes: 256 * 16 * 2).
+inline int64_t tile_elems(int in_bytes, int unroll) { return (int64_t)kThreads * (16 / in_bytes) * unroll; }
 constexpr int64_t kDequantTile = (int64_t)kThreads * 16 * 2;
 
 struct Launch {

@@ -166,7 +166,6 @@ def test_stats_per_tensor_fused_and_separate(dtype, name, fmt):
     want = bulk.stats_f64(fmt, xu, want_codes, k)
     stats_close(fused[0].cpu().tolist(), want)
     stats_close(sep[0].cpu().tolist(), want)
-    assert fused[0].cpu().tolist() == sep[0].cpu().tolist()     # same tiles, same order
 
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])

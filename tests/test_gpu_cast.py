@@ -31,11 +31,12 @@ def _expect_pt(fmt, x64, k, s=0):
 
 @pytest.mark.parametrize("name,fmt", FMTS)
 def test_all_bf16_patterns_every_K(name, fmt):
-    """All 65,536 bf16 patterns at every exponent K in [-140, 140], one
-    tensor per K in a single batched call (several launches of 32)."""
+    """All 65,536 bf16 patterns at every exponent K in [-191, 127] (every
+    k in [-127, 127] with unscales up to 2^64), one tensor per K in a single
+    batched call (several launches of 32)."""
     bits = np.arange(65536, dtype=np.uint32).astype(np.uint16)
     x64 = bulk.bf16_bits_to_f64(bits)
-    Ks = list(range(-140, 141))
+    Ks = list(range(-191, 128))
     xd = dev_bf16(bits)
     codes, counts = _cast_pt([xd] * len(Ks), Ks, name)
     for K, c, n in zip(Ks, codes, counts):
@@ -264,3 +265,50 @@ def test_argument_errors_on_device():
     with pytest.raises(nc.NarrowcastError) as e:
         nc.nc_cast_tensor([x[1:]], [codes_like(63)], "e4m3", state_with_k([0]), nc.new_counts(1))
     assert e.value.status == 2
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_no_writes_past_the_end(dtype):
+    """Every output (codes, MX scales, dequantised values, statistics
+    workspace) sits at the head of a larger buffer filled with a sentinel;
+    no call may change a byte past its tensor's end (ragged last tiles,
+    tail-only tensors, several tensors per launch)."""
+    rng = np.random.default_rng(21)
+    sizes = [77, 32 * 3, 8192 + 77, 3 * 8192 + 77, 4096 * 5 + 32]
+    guard = 1 << 15
+    xs = [(rng.standard_normal(n) * 50).astype(np.float32) for n in sizes]
+    if dtype == "bf16":
+        xd = [dev_bf16(workloads.to_bf16_bits(x.astype(np.float64))) for x in xs]
+    else:
+        xd = [dev_f32(x) for x in xs]
+    fill = 0xA5
+
+    def guarded(nbytes):
+        t = torch.full((nbytes + guard,), fill, dtype=torch.uint8, device="cuda")
+        return t, t[:nbytes]
+
+    cbufs = [guarded(n) for n in sizes]
+    codes = [c for _, c in cbufs]
+    desc, cnt = nc.tensors(xd, codes)
+    wsz = nc.workspace_bytes(desc, cnt)
+    wbig, ws = guarded(wsz)
+    out = nc.new_counts(len(sizes))
+    stats = nc.new_stats(len(sizes))
+    nc.nc_cast_tensor(xd, codes, "e4m3", state_with_k([3] * len(sizes)), out, stats=stats, ws=ws)
+    nc.nc_cast_stats(xd, codes, "e4m3", nc.new_stats(len(sizes)), ws, st=state_with_k([3] * len(sizes)))
+    ybufs = [guarded(2 * n) for n in sizes]
+    ys = [y.view(torch.bfloat16) for _, y in ybufs]
+    nc.nc_dequant(codes, ys, "e4m3", st=state_with_k([3] * len(sizes)))
+    mx_sizes = [n for n in sizes if n % 32 == 0]
+    mx_x = [xd[sizes.index(n)] for n in mx_sizes]
+    mbufs = [guarded(n) for n in mx_sizes]
+    sbufs = [guarded(n // 32) for n in mx_sizes]
+    nc.nc_cast_mx(mx_x, [c for _, c in mbufs], [s for _, s in sbufs], [32] * len(mx_sizes), "e5m2", "ocp",
+                  nc.new_counts(len(mx_sizes)), stats=nc.new_stats(len(mx_sizes)), ws=ws)
+    torch.cuda.synchronize()
+    for name, bufs, lens in (("codes", cbufs, sizes), ("dequant", ybufs, [2 * n for n in sizes]),
+                             ("mx codes", mbufs, mx_sizes), ("mx scales", sbufs, [n // 32 for n in mx_sizes]),
+                             ("workspace", [(wbig, ws)], [wsz])):
+        for (big, _), m in zip(bufs, lens):
+            tail = big[m:].cpu().numpy()
+            assert np.all(tail == fill), (name, m, int(np.argmax(tail != fill)))
