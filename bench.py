@@ -1,6 +1,7 @@
 """Throughput of the scaled FP8 cast on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--rows R] [--no-cpu]
+                    [--cpu-rows R] [--copy-probe]
 
 Workload: a heavy-tailed bf16 tensor of 2^30 elements (262,144 rows of 4096;
 row r = 10^v_r * Student-t(3), v_r ~ U(-3, 3)), resident in HBM before the
@@ -43,8 +44,20 @@ def parse():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--rows", type=int, default=262144, help="rows of 4096 (default 2^30 elements)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
-    ap.add_argument("--cpu-rows", type=int, default=1024)
+    ap.add_argument("--cpu-rows", type=int, default=4096,
+                    help="rows of the workload the CPU oracle baseline runs on")
+    ap.add_argument("--copy-probe", action="store_true",
+                    help="after the timed region, copy 1 GiB device-to-device three times with a plain "
+                         "torch copy kernel (the reference point for HBM byte counters)")
     ap.add_argument("--procs", type=int, default=min(16, os.cpu_count() or 1))
+    ap.add_argument("--input-cache", metavar="PATH",
+                    help="raw uint16 file of the workload: read if present (and of the right size), "
+                         "else generated and written there")
+    ap.add_argument("--make-input", action="store_true",
+                    help="only write --input-cache and exit (no GPU use); a profiled run that reads "
+                         "the cache then starts no worker processes")
+    ap.add_argument("--write-traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="write profiles/traffic.json from rocprofv3 --pmc counter files and exit")
     return ap.parse_args()
 
 
@@ -57,18 +70,67 @@ def source_hash():
     return h.hexdigest()[:16]
 
 
-def traffic_for(kernel: str, src_hash: str):
-    """HBM bytes per launch from the committed rocprofv3 counter runs, if they
-    were taken on the current kernel sources; else None."""
-    p = os.path.join(ROOT, "profiles", "traffic.json")
-    if not os.path.exists(p):
+# rocprofv3 kernel names of each call's main kernel (format E4M3 = 0, bf16 = 1)
+KERNEL_SIG = {"amax": "k_amax<1>", "cast_tensor": "k_cast_pt<0, 1, false>",
+              "cast_mx": "k_cast_mx<0, 1, 0, false>", "dequant_pt": "k_dequant<0, false>",
+              "dequant_mx": "k_dequant<0, true>", "stats_pt": "k_stats<0, 1, false>",
+              "stats_mx": "k_stats<0, 1, true>"}
+TRAFFIC_JSON = os.path.join(ROOT, "profiles", "traffic.json")
+
+
+def traffic_for(call: str, src_hash: str):
+    """HBM bytes per launch of a call's kernel from the committed rocprofv3
+    counter runs, if they were taken on the current kernel sources; else None."""
+    if not os.path.exists(TRAFFIC_JSON):
         return None
-    with open(p) as f:
+    with open(TRAFFIC_JSON) as f:
         t = json.load(f)
     if t.get("source_hash") != src_hash:
         return None
-    k = t.get("kernels", {}).get(kernel)
-    return None if k is None else k.get("bytes_per_launch")
+    k = t.get("kernels", {}).get(KERNEL_SIG.get(call, ""))
+    return None if k is None else k.get("hbm_bytes_per_launch")
+
+
+def write_traffic(fetch_csv: str, write_csv: str):
+    """profiles/traffic.json from two rocprofv3 --pmc runs of this script with
+    --copy-probe (FETCH_SIZE, then WRITE_SIZE; KiB per dispatch).  Each counter
+    is scaled by bytes / reading for the plain 1 GiB device copies of the
+    probe (the rocclr copy kernel; that run does no other large copy), then
+    averaged per kernel."""
+    import csv
+    from collections import defaultdict
+    probe_kib = float(1 << 20)
+    out = {"source_hash": source_hash(), "kernels": {}, "scale": {}}
+    per = {}
+    for counter, path in (("FETCH_SIZE", fetch_csv), ("WRITE_SIZE", write_csv)):
+        vals = defaultdict(list)
+        copy = []
+        with open(path) as f:
+            for r in csv.DictReader(f):
+                if r["Counter_Name"] != counter:
+                    continue
+                v = float(r["Counter_Value"])
+                name = r["Kernel_Name"]
+                if name == "__amd_rocclr_copyBuffer":
+                    copy.append(v)
+                for sig in KERNEL_SIG.values():
+                    if sig in name:
+                        vals[sig].append(v)
+        # the probe's copies (the run's other copies are small uploads)
+        copy = [c for c in copy if c > 0.1 * probe_kib]
+        if not copy:
+            raise SystemExit(f"{path}: no 1 GiB copy dispatches (run with --copy-probe)")
+        factor = probe_kib / (sum(copy) / len(copy))
+        out["scale"][counter] = {"copy_kib": round(sum(copy) / len(copy), 1), "bytes_per_count_kib": factor}
+        per[counter] = {sig: 1024.0 * factor * sum(v) / len(v) for sig, v in vals.items()}
+    for sig in KERNEL_SIG.values():
+        if sig in per["FETCH_SIZE"] and sig in per["WRITE_SIZE"]:
+            rd, wr = per["FETCH_SIZE"][sig], per["WRITE_SIZE"][sig]
+            out["kernels"][sig] = {"read_bytes": round(rd), "write_bytes": round(wr),
+                                   "hbm_bytes_per_launch": round(rd + wr)}
+    with open(TRAFFIC_JSON, "w") as f:
+        json.dump(out, f, indent=1)
+    print(json.dumps(out, indent=1))
 
 
 def cpu_baseline(rows: int, procs: int):
@@ -122,6 +184,9 @@ def _cpu_step(args):
 
 def main():
     a = parse()
+    if a.write_traffic:
+        write_traffic(*a.write_traffic)
+        return
     if a.gpus != 1:
         print(f"bench.py measures one GPU only: this build has no multi-GPU path "
               f"(--gpus {a.gpus} requested). Run with --gpus 1.", file=sys.stderr)
@@ -130,15 +195,25 @@ def main():
     import scaled_fp8_casting_amd as nc
     import workloads
 
-    if not torch.cuda.is_available():
+    if not a.make_input and not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(2)
     rows = a.rows
     n = rows * COLS
-    print(f"[bench] generating {rows}x{COLS} bf16 on {a.procs} processes", file=sys.stderr, flush=True)
     t = time.time()
-    host = workloads.heavy_tailed_parallel(rows, COLS, procs=a.procs)
-    print(f"[bench] generated in {time.time() - t:.1f}s; uploading", file=sys.stderr, flush=True)
+    cache = a.input_cache
+    if cache and os.path.exists(cache) and os.path.getsize(cache) == 2 * n:
+        print(f"[bench] loading {rows}x{COLS} bf16 from {cache}", file=sys.stderr, flush=True)
+        host = np.fromfile(cache, dtype=np.uint16).reshape(rows, COLS)
+    else:
+        print(f"[bench] generating {rows}x{COLS} bf16 on {a.procs} processes", file=sys.stderr, flush=True)
+        host = workloads.heavy_tailed_parallel(rows, COLS, procs=a.procs)
+        if cache:
+            host.tofile(cache)
+    if a.make_input:
+        print(f"[bench] wrote {cache}", file=sys.stderr, flush=True)
+        return
+    print(f"[bench] input ready in {time.time() - t:.1f}s; uploading", file=sys.stderr, flush=True)
     x = torch.from_numpy(host.view(np.int16).reshape(-1)).cuda().view(torch.bfloat16)
     del host
     dev = "cuda"
@@ -226,12 +301,48 @@ def main():
         "roofline": {"bound": "hbm", "kernel": kernel_of[dom], "call": dom, "achieved": round(ach, 1),
                      "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(ach / HBM_PEAK_GBPS, 4),
                      "bytes_per_launch": alg_bytes[dom],
-                     "traffic": traffic_for(kernel_of[dom], src)},
+                     "traffic": traffic_for(dom, src)},
         "results": {"k": int(bufs["st"][0, 0]), "amax": nc.counts_list(bufs["am"])[0]["amax"],
                     "pt_clip": cc["n_clip"], "pt_underflow_frac": round(cc["n_underflow"] / n, 5),
                     "mx_clip_frac": round(cm["n_clip"] / n, 5)},
         "source_hash": src,
     }
+    # Beside the step (not part of it): the casts with their statistics fused
+    # (one pass instead of cast + separate statistics pass) and a plain
+    # device-to-device copy moving the cast's byte count (practical ceiling).
+    fused_pt, fused_mx = nc.new_stats(1), nc.new_stats(1)
+    extras = {
+        "cast_tensor+stats": (lambda: nc.nc_cast_tensor([x], [codes_pt], "e4m3", bufs["st"], bufs["cpt"],
+                                                        stats=fused_pt, ws=ws), 3 * n),
+        "cast_mx+stats": (lambda: nc.nc_cast_mx([x], [codes_mx], [scales], [COLS], "e4m3", "ocp", bufs["cmx"],
+                                                stats=fused_mx, ws=ws), 3 * n + n // 32),
+    }
+    if not a.copy_probe:     # (a counter run keeps the probe's copies the only large ones)
+        cp_src = torch.empty(3 * n // 2, dtype=torch.uint8, device=dev).fill_(1)
+        cp_dst = torch.empty_like(cp_src)
+        extras["copy_ceiling"] = (lambda: cp_dst.copy_(cp_src), 3 * n)
+    out["beside_step"] = {}
+    for nm, (fn, nbytes) in extras.items():
+        fn()
+        torch.cuda.synchronize()
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(10)]
+        for e0, e1 in ev:
+            e0.record()
+            fn()
+            e1.record()
+        torch.cuda.synchronize()
+        ms = float(np.mean([e0.elapsed_time(e1) for e0, e1 in ev]))
+        gbps = nbytes / (ms * 1e-3) / 1e9
+        out["beside_step"][nm] = dict(ms=round(ms, 4), gbps=round(gbps, 1), frac=round(gbps / HBM_PEAK_GBPS, 4),
+                                      gelem_s=round(n / (ms * 1e-3) / 1e9, 2))
+    extras.clear()
+    if a.copy_probe:
+        src_b = torch.empty(1 << 30, dtype=torch.uint8, device=dev).fill_(1)
+        dst_b = torch.empty_like(src_b)
+        for _ in range(3):
+            dst_b.copy_(src_b)
+        torch.cuda.synchronize()
+        del src_b, dst_b
     if not a.no_cpu:
         print(f"[bench] CPU oracle baseline on {a.cpu_rows} rows", file=sys.stderr, flush=True)
         out["cpu_baseline"] = cpu_baseline(a.cpu_rows, a.procs)
