@@ -137,16 +137,24 @@ def workspace_bytes(desc, count: int) -> int:
 
 
 def new_workspace(desc, count: int, device="cuda") -> torch.Tensor:
-    return torch.empty(max(workspace_bytes(desc, count), 8), dtype=torch.uint8, device=device)
+    """Device workspace for the calls that reduce (amax, casts, statistics);
+    torch's allocator returns 256-byte aligned memory."""
+    return torch.empty(max(workspace_bytes(desc, count), 16), dtype=torch.uint8, device=device)
+
+
+def _ws(ws, desc, count):
+    return new_workspace(desc, count) if ws is None else ws
 
 
 # -- the C-ABI calls ----------------------------------------------------------
 
 def nc_amax(xs: Sequence[torch.Tensor], out: torch.Tensor, ls: Optional[torch.Tensor] = None,
-            stream=None):
+            ws: Optional[torch.Tensor] = None, stream=None):
     desc, count = tensors(xs, [None] * len(xs))
     dt = _dtype_code(xs[0]) if xs else NC_F32
-    _check(_lib.load().nc_amax(desc, count, dt, _ptr(ls), _ptr(out), _stream(stream)), "nc_amax")
+    ws = _ws(ws, desc, count)
+    _check(_lib.load().nc_amax(desc, count, dt, _ptr(ls), _ptr(out), _ptr(ws), ws.numel(), _stream(stream)),
+           "nc_amax")
 
 
 def nc_scale_update(pol: NcPolicy, st: torch.Tensor, in_counts: torch.Tensor,
@@ -164,11 +172,9 @@ def nc_cast_tensor(xs: Sequence[torch.Tensor], codes: Sequence[torch.Tensor], fm
     desc, count = tensors(xs, codes)
     dt = _dtype_code(xs[0]) if xs else NC_F32
     f = FMT[fmt] if isinstance(fmt, str) else fmt
-    if stats is not None and ws is None:
-        raise ValueError("stats need a workspace (new_workspace)")
+    ws = _ws(ws, desc, count)
     _check(_lib.load().nc_cast_tensor(desc, count, dt, f, _ptr(st), _ptr(ls), _ptr(out), _ptr(stats),
-                                      _ptr(ws), ws.numel() if ws is not None else 0, _stream(stream)),
-           "nc_cast_tensor")
+                                      _ptr(ws), ws.numel(), _stream(stream)), "nc_cast_tensor")
 
 
 def nc_cast_mx(xs: Sequence[torch.Tensor], codes: Sequence[torch.Tensor], scales: Sequence[torch.Tensor],
@@ -178,10 +184,9 @@ def nc_cast_mx(xs: Sequence[torch.Tensor], codes: Sequence[torch.Tensor], scales
     dt = _dtype_code(xs[0]) if xs else NC_BF16
     f = FMT[fmt] if isinstance(fmt, str) else fmt
     r = MX_RULE[rule] if isinstance(rule, str) else rule
-    if stats is not None and ws is None:
-        raise ValueError("stats need a workspace (new_workspace)")
-    _check(_lib.load().nc_cast_mx(desc, count, dt, f, r, _ptr(out), _ptr(stats), _ptr(ws),
-                                  ws.numel() if ws is not None else 0, _stream(stream)), "nc_cast_mx")
+    ws = _ws(ws, desc, count)
+    _check(_lib.load().nc_cast_mx(desc, count, dt, f, r, _ptr(out), _ptr(stats), _ptr(ws), ws.numel(),
+                                  _stream(stream)), "nc_cast_mx")
 
 
 def nc_dequant(codes: Sequence[torch.Tensor], ys: Sequence[torch.Tensor], fmt,
@@ -197,11 +202,13 @@ def nc_dequant(codes: Sequence[torch.Tensor], ys: Sequence[torch.Tensor], fmt,
 
 
 def nc_cast_stats(xs: Sequence[torch.Tensor], codes: Sequence[torch.Tensor], fmt, out: torch.Tensor,
-                  ws: torch.Tensor, st: Optional[torch.Tensor] = None, ls: Optional[torch.Tensor] = None,
+                  ws: Optional[torch.Tensor] = None, st: Optional[torch.Tensor] = None,
+                  ls: Optional[torch.Tensor] = None,
                   scales: Optional[Sequence[torch.Tensor]] = None, cols: Optional[Sequence[int]] = None,
                   stream=None):
     desc, count = tensors(xs, codes, cols=cols, scales=scales)
     dt = _dtype_code(xs[0]) if xs else NC_F32
     f = FMT[fmt] if isinstance(fmt, str) else fmt
+    ws = _ws(ws, desc, count)
     _check(_lib.load().nc_cast_stats(desc, count, dt, f, _ptr(st), _ptr(ls), _ptr(out), _ptr(ws),
                                      ws.numel(), _stream(stream)), "nc_cast_stats")

@@ -63,7 +63,7 @@ def load():
                            "`python -m scaled_fp8_casting_amd.build` (there is no fallback path)")
     lib = ctypes.CDLL(LIB_PATH)
     T = POINTER(NcTensor)
-    lib.nc_amax.argtypes = [T, c_int32, c_int32, c_void_p, c_void_p, c_void_p]
+    lib.nc_amax.argtypes = [T, c_int32, c_int32, c_void_p, c_void_p, c_void_p, c_size_t, c_void_p]
     lib.nc_scale_update.argtypes = [POINTER(NcPolicy), c_int32, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p]
     lib.nc_cast_tensor.argtypes = [T, c_int32, c_int32, c_int32, c_void_p, c_void_p, c_void_p, c_void_p,
                                    c_void_p, c_size_t, c_void_p]

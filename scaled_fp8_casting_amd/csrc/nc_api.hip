@@ -1,5 +1,5 @@
 // The C-ABI of libnarrowcast: argument checks, batching into launches of at
-// most kMaxSeg tensors, grid sizing.  No allocation, no global state.
+// most kMaxSeg tensors, workspace layout.  No allocation, no global state.
 #include <string.h>
 
 #include "nc_launch.h"
@@ -7,23 +7,6 @@
 using namespace nc;
 
 namespace {
-
-// Workgroups per CU for the streaming kernels: 16 x 256 threads of grid
-// (resident as registers allow), enough 16-byte loads in flight to cover
-// HBM latency; measured best for read+write streams on MI355X.
-constexpr int kWGPerCU = 16;
-
-int grid_for(int64_t tiles) {
-  int dev = 0, cus = 256;
-  if (hipGetDevice(&dev) == hipSuccess) {
-    int v = 0;
-    if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && v > 0)
-      cus = v;
-  }
-  int64_t cap = (int64_t)cus * kWGPerCU;
-  if (cap > kMaxGrid) cap = kMaxGrid;
-  return (int)(tiles < cap ? tiles : cap);
-}
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
@@ -46,39 +29,62 @@ nc_status check_tensors(const nc_tensor* t, int32_t count, bool need_x, bool nee
   return NC_OK;
 }
 
-// Walk the batch in launches of at most kMaxSeg tensors; `fn(batch)` enqueues
-// one launch.  Empty tensors are skipped.
+// Launches cover consecutive tensors (so b.first + s indexes the caller's
+// arrays): at most kMaxSeg of them and at most kMaxLaunchElems elements, a
+// rule that does not depend on the tile size, so every call on the same
+// tensors forms the same launches.  A tensor larger than one launch is an
+// error.
+constexpr int64_t kMaxLaunchElems = (int64_t)1 << 34;
+
+// Launch boundaries: calls fn(first, end) for each launch [first, end).
 template <typename Fn>
-nc_status for_batches(const nc_tensor* t, int32_t count, int64_t tile, void* const* y, Fn fn) {
-  SegBatch b;
-  memset(&b, 0, sizeof(b));
+nc_status for_launches(const nc_tensor* t, int32_t count, Fn fn) {
   int32_t i = 0;
   while (i < count) {
-    b.count = 0;
-    b.first = i;
-    b.tile0[0] = 0;
-    // a launch covers consecutive tensors so that b.first + s indexes the
-    // caller's arrays; empty tensors inside keep a zero-tile slot
-    while (i < count && b.count < kMaxSeg) {
-      const nc_tensor& x = t[i];
-      Seg& s = b.s[b.count];
-      s.x = x.x;
-      s.codes = x.codes;
-      s.scales = x.scales;
-      s.y = y ? y[i] : nullptr;
-      s.n = x.n;
-      const int64_t tiles = (x.n + tile - 1) / tile;
-      b.tile0[b.count + 1] = b.tile0[b.count] + tiles;
-      b.last[b.count] = tiles ? (int32_t)(x.n - (tiles - 1) * tile) : 0;
-      ++b.count;
-      ++i;
-    }
-    for (int s = b.count + 1; s <= kMaxSeg; ++s) b.tile0[s] = b.tile0[b.count];
-    if (b.tile0[b.count] == 0) continue;
-    const nc_status st = fn(b);
+    const int32_t first = i;
+    int64_t elems = 0;
+    while (i < count && i - first < kMaxSeg && elems + t[i].n <= kMaxLaunchElems) elems += t[i++].n;
+    if (i == first) return NC_E_ARG;     // one tensor above the per-launch limit
+    const nc_status st = fn(first, i);
     if (st != NC_OK) return st;
   }
   return NC_OK;
+}
+
+// Fills b for tensors [first, end) with tiles of `tile` elements.
+void make_batch(SegBatch& b, const nc_tensor* t, int32_t first, int32_t end, int64_t tile, void* const* y) {
+  memset(&b, 0, sizeof(b));
+  b.first = first;
+  b.count = end - first;
+  for (int32_t s = 0; s < b.count; ++s) {
+    const nc_tensor& x = t[first + s];
+    Seg& g = b.s[s];
+    g.x = x.x;
+    g.codes = x.codes;
+    g.scales = x.scales;
+    g.y = y ? y[first + s] : nullptr;
+    g.n = x.n;
+    const int64_t tiles = (x.n + tile - 1) / tile;
+    b.tile0[s + 1] = b.tile0[s] + tiles;
+    b.chunk0[s + 1] = b.chunk0[s] + (tiles + kChunk - 1) / kChunk;
+    b.last[s] = tiles ? (int32_t)(x.n - (tiles - 1) * tile) : 0;
+  }
+  for (int s = b.count + 1; s <= kMaxSeg; ++s) {
+    b.tile0[s] = b.tile0[b.count];
+    b.chunk0[s] = b.chunk0[b.count];
+  }
+}
+
+// Walk the call in launches; `fn(batch)` enqueues one launch (skipped when
+// the launch has no element at all).
+template <typename Fn>
+nc_status for_batches(const nc_tensor* t, int32_t count, int64_t tile, void* const* y, Fn fn) {
+  SegBatch b;
+  return for_launches(t, count, [&](int32_t first, int32_t end) {
+    make_batch(b, t, first, end, tile, y);
+    if (b.tile0[b.count] == 0) return NC_OK;
+    return fn(b);
+  });
 }
 
 nc_status hip_status(hipError_t e) { return e == hipSuccess ? NC_OK : NC_E_HIP; }
@@ -87,26 +93,36 @@ bool valid_dtype(nc_dtype d) { return d == NC_F32 || d == NC_BF16; }
 bool valid_fmt(nc_fmt f) { return f == NC_E4M3 || f == NC_E5M2; }
 
 nc_status check_ws(const nc_tensor* t, int32_t count, void* ws, size_t ws_bytes) {
-  if (ws == nullptr || ((uintptr_t)ws & 7u) != 0) return NC_E_WORKSPACE;
+  if (ws == nullptr || ((uintptr_t)ws & 15u) != 0) return NC_E_WORKSPACE;
   if (ws_bytes < nc_workspace_bytes(t, count)) return NC_E_WORKSPACE;
   return NC_OK;
 }
+
+Ws ws_of(const SegBatch& b, void* ws) { return ws_layout(ws, b.tile0[b.count], b.chunk0[b.count]); }
 
 }  // namespace
 
 extern "C" {
 
 size_t nc_workspace_bytes(const nc_tensor* t, int32_t count) {
-  // one slot of 6 binary64 per (tensor of a launch, workgroup)
+  // per-workgroup and per-chunk slots of the largest launch, at the smallest
+  // tile any call uses
   if (t == nullptr || count <= 0) return 0;
-  const int32_t per_launch = count < kMaxSeg ? count : kMaxSeg;
-  return (size_t)per_launch * kMaxGrid * 6 * sizeof(double);
+  size_t need = 0;
+  SegBatch b;
+  for_launches(t, count, [&](int32_t first, int32_t end) {
+    make_batch(b, t, first, end, kMinWsTile, nullptr);
+    const size_t v = ws_bytes_for(b.tile0[b.count], b.chunk0[b.count]);
+    if (v > need) need = v;
+    return NC_OK;
+  });
+  return need;
 }
 
 const char* nc_status_string(nc_status s) {
   switch (s) {
     case NC_OK: return "ok";
-    case NC_E_ARG: return "invalid argument (null pointer, negative size or bad policy field)";
+    case NC_E_ARG: return "invalid argument (null pointer, negative size, tensor above 2^34 elements or bad policy field)";
     case NC_E_ALIGN: return "element pointer not 16-byte aligned";
     case NC_E_SHAPE: return "MX shape: cols must be a positive multiple of 32 dividing n";
     case NC_E_UNSUPPORTED: return "unsupported dtype, format, rule or estimator";
@@ -117,15 +133,19 @@ const char* nc_status_string(nc_status s) {
 }
 
 nc_status nc_amax(const nc_tensor* t, int32_t count, nc_dtype dtype, const nc_loss_scale* ls,
-                  nc_counts* out, void* stream) {
+                  nc_counts* out, void* ws, size_t ws_bytes, void* stream) {
   if (!valid_dtype(dtype)) return NC_E_UNSUPPORTED;
   nc_status s = check_tensors(t, count, true, false, false);
   if (s != NC_OK) return s;
-  if (count > 0 && out == nullptr) return NC_E_ARG;
-  const int64_t tile = tile_elems(in_bytes(dtype), kUnrollRead);
+  if (count == 0) return NC_OK;
+  if (out == nullptr) return NC_E_ARG;
+  if ((s = check_ws(t, count, ws, ws_bytes)) != NC_OK) return s;
+  const int64_t tile = tile_elems(in_bytes(dtype), kAmaxVecs);
   return for_batches(t, count, tile, nullptr, [&](const SegBatch& b) {
-    Launch l{grid_for(b.tile0[b.count]), (hipStream_t)stream};
-    return hip_status(launch_amax(b, dtype, ls, out, l));
+    const Ws w = ws_of(b, ws);
+    nc_status r = hip_status(launch_amax(b, dtype, w, Launch{b.tile0[b.count], (hipStream_t)stream}));
+    if (r == NC_OK) r = hip_status(launch_reduce(b, w, out, nullptr, ls, false, (hipStream_t)stream));
+    return r;
   });
 }
 
@@ -152,14 +172,15 @@ nc_status nc_cast_tensor(const nc_tensor* t, int32_t count, nc_dtype dtype, nc_f
   if (!valid_dtype(dtype) || !valid_fmt(fmt)) return NC_E_UNSUPPORTED;
   nc_status s = check_tensors(t, count, true, true, false);
   if (s != NC_OK) return s;
-  if (count > 0 && (out == nullptr || st == nullptr)) return NC_E_ARG;
-  if (stats && (s = check_ws(t, count, ws, ws_bytes)) != NC_OK) return s;
-  const int64_t tile = tile_elems(in_bytes(dtype), kUnrollCast);
-  double* part = stats ? static_cast<double*>(ws) : nullptr;
+  if (count == 0) return NC_OK;
+  if (out == nullptr || st == nullptr) return NC_E_ARG;
+  if ((s = check_ws(t, count, ws, ws_bytes)) != NC_OK) return s;
+  const int64_t tile = tile_elems(in_bytes(dtype), stats ? kCastStatsVecs : kCastVecs);
   return for_batches(t, count, tile, nullptr, [&](const SegBatch& b) {
-    Launch l{grid_for(b.tile0[b.count]), (hipStream_t)stream};
-    nc_status r = hip_status(launch_cast_pt(b, dtype, fmt, st, ls, out, part, l));
-    if (r == NC_OK && stats) r = hip_status(launch_stats_finalize(b, part, l.grid, stats, l.stream));
+    const Ws w = ws_of(b, ws);
+    nc_status r = hip_status(launch_cast_pt(b, dtype, fmt, st, ls, stats != nullptr, w,
+                                            Launch{b.tile0[b.count], (hipStream_t)stream}));
+    if (r == NC_OK) r = hip_status(launch_reduce(b, w, out, stats, ls, true, (hipStream_t)stream));
     return r;
   });
 }
@@ -170,14 +191,15 @@ nc_status nc_cast_mx(const nc_tensor* t, int32_t count, nc_dtype dtype, nc_fmt f
   if (rule != NC_MX_OCP && rule != NC_MX_PLUS1 && rule != NC_MX_CEIL) return NC_E_UNSUPPORTED;
   nc_status s = check_tensors(t, count, true, true, true);
   if (s != NC_OK) return s;
-  if (count > 0 && out == nullptr) return NC_E_ARG;
-  if (stats && (s = check_ws(t, count, ws, ws_bytes)) != NC_OK) return s;
-  const int64_t tile = tile_elems(in_bytes(dtype), kUnrollCast);
-  double* part = stats ? static_cast<double*>(ws) : nullptr;
+  if (count == 0) return NC_OK;
+  if (out == nullptr) return NC_E_ARG;
+  if ((s = check_ws(t, count, ws, ws_bytes)) != NC_OK) return s;
+  const int64_t tile = tile_elems(in_bytes(dtype), stats ? kCastStatsVecs : kCastVecs);
   return for_batches(t, count, tile, nullptr, [&](const SegBatch& b) {
-    Launch l{grid_for(b.tile0[b.count]), (hipStream_t)stream};
-    nc_status r = hip_status(launch_cast_mx(b, dtype, fmt, rule, out, part, l));
-    if (r == NC_OK && stats) r = hip_status(launch_stats_finalize(b, part, l.grid, stats, l.stream));
+    const Ws w = ws_of(b, ws);
+    nc_status r = hip_status(launch_cast_mx(b, dtype, fmt, rule, stats != nullptr, w,
+                                            Launch{b.tile0[b.count], (hipStream_t)stream}));
+    if (r == NC_OK) r = hip_status(launch_reduce(b, w, out, stats, nullptr, true, (hipStream_t)stream));
     return r;
   });
 }
@@ -195,8 +217,7 @@ nc_status nc_dequant(const nc_tensor* t, int32_t count, nc_fmt fmt, const nc_sca
     if (!aligned16(y[i])) return NC_E_ALIGN;
   }
   return for_batches(t, count, kDequantTile, y, [&](const SegBatch& b) {
-    Launch l{grid_for(b.tile0[b.count]), (hipStream_t)stream};
-    return hip_status(launch_dequant(b, fmt, st, l));
+    return hip_status(launch_dequant(b, fmt, st, Launch{b.tile0[b.count], (hipStream_t)stream}));
   });
 }
 
@@ -207,14 +228,14 @@ nc_status nc_cast_stats(const nc_tensor* t, int32_t count, nc_dtype dtype, nc_fm
   const bool mx = st == nullptr;
   nc_status s = check_tensors(t, count, true, true, mx);
   if (s != NC_OK) return s;
-  if (count > 0 && out == nullptr) return NC_E_ARG;
-  if (count > 0 && (s = check_ws(t, count, ws, ws_bytes)) != NC_OK) return s;
-  const int64_t tile = tile_elems(in_bytes(dtype), kUnrollRead);
-  double* part = static_cast<double*>(ws);
+  if (count == 0) return NC_OK;
+  if (out == nullptr) return NC_E_ARG;
+  if ((s = check_ws(t, count, ws, ws_bytes)) != NC_OK) return s;
+  const int64_t tile = tile_elems(in_bytes(dtype), kStatsVecs);
   return for_batches(t, count, tile, nullptr, [&](const SegBatch& b) {
-    Launch l{grid_for(b.tile0[b.count]), (hipStream_t)stream};
-    nc_status r = hip_status(launch_stats(b, dtype, fmt, st, ls, part, l));
-    if (r == NC_OK) r = hip_status(launch_stats_finalize(b, part, l.grid, out, l.stream));
+    const Ws w = ws_of(b, ws);
+    nc_status r = hip_status(launch_stats(b, dtype, fmt, st, ls, w, Launch{b.tile0[b.count], (hipStream_t)stream}));
+    if (r == NC_OK) r = hip_status(launch_reduce(b, w, nullptr, out, mx ? nullptr : ls, false, (hipStream_t)stream));
     return r;
   });
 }

@@ -1,5 +1,5 @@
-// The scale-update state machine, dequant to bf16, and the statistics pass
-// with its fixed-order finalisation.
+// The scale-update state machine, dequant to bf16, the statistics pass, and
+// the fixed-order reductions of the per-workgroup slots.
 #include "nc_launch.h"
 
 namespace nc {
@@ -103,71 +103,73 @@ __device__ __forceinline__ uint32_t dq_bf16(uint32_t dec_bits, int K) {
   return f32_to_bf16_rne(__float_as_uint(v));
 }
 
+// Full tiles decode in hardware: v_cvt_pk_f32_fp8 / _bf8 turns two codes
+// into their exact fp32 values, v_ldexp_f32 applies the scale (exact, as
+// above), v_cvt_pk_bf16_f32 rounds two values to bf16 (nearest even, IEEE
+// overflow).  NaN codes -- the only codes where the hardware result is not
+// the defined one (0x7FC0) -- are rare: a wave whose vector holds any takes
+// a uniform branch that rewrites them.  Every code at every k is checked
+// against the exact definition by the tests.
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+template <int FMT, bool HI>
+__device__ __forceinline__ f32x2 decode_pair(uint32_t w) {
+  if constexpr (FMT == NC_E4M3) return __builtin_amdgcn_cvt_pk_f32_fp8((int)w, HI);
+  else return __builtin_amdgcn_cvt_pk_f32_bf8((int)w, HI);
+}
+
+__device__ __forceinline__ uint32_t bf16_pair(f32x2 v, int sh) {
+  v.x = __builtin_amdgcn_ldexpf(v.x, sh);
+  v.y = __builtin_amdgcn_ldexpf(v.y, sh);
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
+}
+
+// Bytes of w that are NaN codes: bit 7 of each byte set for E4M3 x.1111.111
+// and E5M2 x.11111.01..11.
+template <int FMT>
+__device__ __forceinline__ uint32_t nan_bytes(uint32_t w) {
+  constexpr uint32_t kBump = FMT == NC_E4M3 ? 0x01010101u : 0x03030303u;
+  return ((w & 0x7F7F7F7Fu) + kBump) & 0x80808080u;
+}
+
 template <int FMT, bool MX>
 NC_STREAM_KERNEL
 k_dequant(const SegBatch b, const nc_scale_state* __restrict__ st) {
-  constexpr int64_t TILE = kDequantTile;      // 16 codes per lane per step, 2 steps
-  __shared__ uint32_t tab[256];               // per-tensor: bf16 result; MX: decode bits
-  if constexpr (MX) {
-    tab[threadIdx.x] = decode_bits<FMT>(threadIdx.x);
-    __syncthreads();
-  }
-  const int64_t total = b.tile0[b.count];
-  int seg = -1, k = 0;
-  for (int64_t tile = blockIdx.x; tile < total; tile += gridDim.x) {
-    const int s = seg_of(b, tile, seg);
-    if (s != seg) {
-      seg = s;
-      if constexpr (!MX) {
-        k = st[b.first + s].k;
-        __syncthreads();
-        tab[threadIdx.x] = dq_bf16<FMT>(decode_bits<FMT>(threadIdx.x), k);
-        __syncthreads();
-      }
+  constexpr int64_t TILE = kDequantTile;      // 8 codes per lane
+  const int64_t tile = blockIdx.x;
+  const int s = seg_of(b.tile0, b.count, tile);
+  const Seg& g = b.s[s];
+  const int64_t e0 = (tile - b.tile0[s]) * TILE;
+  const int rem = tile_len<TILE>(b, s, tile);
+  const uint8_t* src = g.codes + e0;
+  uint16_t* dst = static_cast<uint16_t*>(g.y) + e0;
+  if (rem == (int)TILE) {
+    const u32x2 c = ld_stream(reinterpret_cast<const u32x2*>(src) + threadIdx.x);
+    int sh;                                   // the value is decode(q) * 2^sh
+    if constexpr (MX) sh = (int)g.scales[(e0 + (int64_t)threadIdx.x * 8) / 32] - 127;   // X
+    else sh = -st[b.first + s].k;
+    u32x4 o;
+    o.x = bf16_pair(decode_pair<FMT, false>(c.x), sh);
+    o.y = bf16_pair(decode_pair<FMT, true>(c.x), sh);
+    o.z = bf16_pair(decode_pair<FMT, false>(c.y), sh);
+    o.w = bf16_pair(decode_pair<FMT, true>(c.y), sh);
+    const uint32_t nb0 = nan_bytes<FMT>(c.x), nb1 = nan_bytes<FMT>(c.y);
+    if (__ballot((nb0 | nb1) != 0) != 0) {    // wave-uniform, rare
+      uint32_t h[8] = {o.x & 0xFFFFu, o.x >> 16, o.y & 0xFFFFu, o.y >> 16,
+                       o.z & 0xFFFFu, o.z >> 16, o.w & 0xFFFFu, o.w >> 16};
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+        if (((i < 4 ? nb0 : nb1) >> (8 * (i % 4) + 7)) & 1u) h[i] = 0x7FC0u;
+      o = u32x4{h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16), h[6] | (h[7] << 16)};
     }
-    const Seg& g = b.s[s];
-    const int64_t e0 = (tile - b.tile0[s]) * TILE;
-    const int rem = tile_len<TILE>(b, s, tile);
-    const uint8_t* src = g.codes + e0;
-    uint16_t* dst = static_cast<uint16_t*>(g.y) + e0;
-    if (rem == (int)TILE) {
-      u32x4 c[2];
-#pragma unroll
-      for (int u = 0; u < 2; ++u) c[u] = ld_stream(reinterpret_cast<const u32x4*>(src) + u * kThreads + threadIdx.x);
-      __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-      for (int u = 0; u < 2; ++u) {
-        const int vi = u * kThreads + threadIdx.x;
-        int K = 0;
-        if constexpr (MX) K = 127 - (int)g.scales[(e0 + (int64_t)vi * 16) / 32];   // K = -X
-        const uint32_t w[4] = {c[u].x, c[u].y, c[u].z, c[u].w};
-        uint32_t o[8];
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          uint32_t h[4];
-#pragma unroll
-          for (int t = 0; t < 4; ++t) {
-            const uint32_t q = (w[j] >> (8 * t)) & 0xFFu;
-            if constexpr (MX) h[t] = dq_bf16<FMT>(tab[q], K);
-            else h[t] = tab[q];
-          }
-          o[2 * j] = h[0] | (h[1] << 16);
-          o[2 * j + 1] = h[2] | (h[3] << 16);
-        }
-        u32x4* d = reinterpret_cast<u32x4*>(dst) + (int64_t)vi * 2;
-        d[0] = u32x4{o[0], o[1], o[2], o[3]};
-        d[1] = u32x4{o[4], o[5], o[6], o[7]};
-      }
-    } else {
-      for (int i = threadIdx.x; i < rem; i += kThreads) {
-        const uint32_t q = src[i];
-        if constexpr (MX) {
-          const int K = 127 - (int)g.scales[(e0 + i) / 32];
-          dst[i] = (uint16_t)dq_bf16<FMT>(tab[q], K);
-        } else {
-          dst[i] = (uint16_t)tab[q];
-        }
-      }
+    reinterpret_cast<u32x4*>(dst)[threadIdx.x] = o;
+  } else {
+    const int k = MX ? 0 : st[b.first + s].k;
+    for (int i = threadIdx.x; i < rem; i += kThreads) {
+      const uint32_t q = src[i];
+      const int K = MX ? 127 - (int)g.scales[(e0 + i) / 32] : k;
+      dst[i] = (uint16_t)dq_bf16<FMT>(decode_bits<FMT>(q), K);
     }
   }
 }
@@ -177,121 +179,207 @@ k_dequant(const SegBatch b, const nc_scale_state* __restrict__ st) {
 template <int FMT, int DT, bool MX>
 NC_STREAM_KERNEL
 k_stats(const SegBatch b, const nc_scale_state* __restrict__ st,
-        const nc_loss_scale* __restrict__ ls, double* __restrict__ part) {
+        const nc_loss_scale* __restrict__ ls, double* __restrict__ stat_slots) {
   constexpr int VEC = In<DT>::VEC;
-  constexpr int64_t TILE = (int64_t)kThreads * VEC * kUnrollRead;
+  constexpr int64_t TILE = (int64_t)kThreads * VEC * kStatsVecs;
   __shared__ double tab[256];
-  __shared__ double lds_st[kWaves * 6];
-  if constexpr (MX) {
-    fill_stat_table<FMT>(tab, 0);
-    __syncthreads();
-  }
-  const int s_log2 = (!MX && ls) ? ls->s_log2 : 0;
-  const int64_t total = b.tile0[b.count];
+  __shared__ double lds_st[kRows * 6];
+  const int64_t tile = blockIdx.x;
+  const int s = seg_of(b.tile0, b.count, tile);
+  if constexpr (MX) fill_stat_table<FMT>(tab, 0);
+  else fill_stat_table<FMT>(tab, st[b.first + s].k - (ls ? ls->s_log2 : 0));
+  __syncthreads();
+  const Seg& g = b.s[s];
+  const int64_t e0 = (tile - b.tile0[s]) * TILE;
+  const int rem = tile_len<TILE>(b, s, tile);
+  const uint8_t* cs = g.codes + e0;
   StatAcc sa;
   sa.reset();
-  int seg = -1;
-  // buf always holds the current tile when it is full (prefetch invariant)
-  u32x4 buf[kUnrollRead];
-  prefetch_tile<In<DT>::BYTES, kUnrollRead, TILE>(b, blockIdx.x, -1, buf);
-  for (int64_t tile = blockIdx.x; tile < total; tile += gridDim.x) {
-    const int s = seg_of(b, tile, seg);
-    if (s != seg) {
-      if (seg >= 0) stats_seg_flush(sa, stat_slot(part, seg, blockIdx.x), lds_st, s_log2);
-      seg = s;
-      if constexpr (!MX) {
-        __syncthreads();
-        fill_stat_table<FMT>(tab, st[b.first + s].k - s_log2);
-        __syncthreads();
+  if (rem == (int)TILE) {
+    const u32x4* src = reinterpret_cast<const u32x4*>(static_cast<const uint8_t*>(g.x) + e0 * In<DT>::BYTES);
+    u32x4 v[kStatsVecs];
+#pragma unroll
+    for (int u = 0; u < kStatsVecs; ++u) v[u] = ld_stream(src + u * kThreads + threadIdx.x);
+#pragma unroll
+    for (int u = 0; u < kStatsVecs; ++u) {
+      const int vi = u * kThreads + threadIdx.x;
+      uint32_t xb[VEC], q[VEC];
+      unpack<DT>(v[u], xb);
+      if constexpr (DT == NC_F32) {
+        const uint32_t w = reinterpret_cast<const uint32_t*>(cs)[vi];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) q[i] = (w >> (8 * i)) & 0xFFu;
+      } else {
+        const uint64_t w = reinterpret_cast<const uint64_t*>(cs)[vi];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) q[i] = (uint32_t)(w >> (8 * i)) & 0xFFu;
       }
+      double blk = 1.0;
+      if constexpr (MX) blk = pow2_f64((int)g.scales[(e0 + (int64_t)vi * VEC) / 32] - 127);
+      stats_vec<VEC, MX>(xb, q, tab, blk, sa);
     }
-    const Seg& g = b.s[s];
-    const int64_t e0 = (tile - b.tile0[s]) * TILE;
-    const int rem = tile_len<TILE>(b, s, tile);
-    const uint8_t* cs = g.codes + e0;
-    if (rem == (int)TILE) {
-      u32x4 v[kUnrollRead];
-#pragma unroll
-      for (int u = 0; u < kUnrollRead; ++u) v[u] = buf[u];
-      prefetch_tile<In<DT>::BYTES, kUnrollRead, TILE>(b, tile + gridDim.x, s, buf);
-      __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-      for (int u = 0; u < kUnrollRead; ++u) {
-        const int vi = u * kThreads + threadIdx.x;
-        uint32_t xb[VEC], q[VEC];
-        unpack<DT>(v[u], xb);
-        if constexpr (DT == NC_F32) {
-          const uint32_t w = reinterpret_cast<const uint32_t*>(cs)[vi];
-#pragma unroll
-          for (int i = 0; i < 4; ++i) q[i] = (w >> (8 * i)) & 0xFFu;
-        } else {
-          const uint64_t w = reinterpret_cast<const uint64_t*>(cs)[vi];
-#pragma unroll
-          for (int i = 0; i < 8; ++i) q[i] = (uint32_t)(w >> (8 * i)) & 0xFFu;
-        }
-        double blk = 1.0;
-        if constexpr (MX) blk = pow2_f64((int)g.scales[(e0 + (int64_t)vi * VEC) / 32] - 127);
-        stats_vec<VEC, MX>(xb, q, tab, blk, sa);
-      }
-    } else {
-      prefetch_tile<In<DT>::BYTES, kUnrollRead, TILE>(b, tile + gridDim.x, s, buf);
-      for (int i = threadIdx.x; i < rem; i += kThreads) {
-        const uint32_t xb = load_one<DT>(g.x, e0 + i);
-        const uint32_t q = cs[i];
-        double blk = 1.0;
-        if constexpr (MX) blk = pow2_f64((int)g.scales[(e0 + i) / 32] - 127);
-        stats_vec<1, MX>(&xb, &q, tab, blk, sa);
-      }
+  } else {
+    for (int i = threadIdx.x; i < rem; i += kThreads) {
+      const uint32_t xb = load_one<DT>(g.x, e0 + i);
+      const uint32_t q = cs[i];
+      double blk = 1.0;
+      if constexpr (MX) blk = pow2_f64((int)g.scales[(e0 + i) / 32] - 127);
+      stats_vec<1, MX>(&xb, &q, tab, blk, sa);
     }
   }
-  if (seg >= 0) stats_seg_flush(sa, stat_slot(part, seg, blockIdx.x), lds_st, s_log2);
+  write_stat_slot(sa, stat_slots + tile * 6, lds_st);
 }
 
-// One workgroup per tensor: sum the partials of the workgroups that worked
-// on it, in the order of the tensor's first tiles (the producer grid of G
-// workgroups strides over tiles, so tile t went to workgroup t mod G), and
-// add the result into out (only this workgroup writes that tensor's stats).
+// ---------------------------------------------------------------------------
+// Reductions of the per-workgroup slots.  First: workgroup c sums chunk c,
+// at most kChunk consecutive tiles of one tensor, into a chunk slot.
+// Second: workgroup s sums tensor s's chunk slots and adds the totals into
+// the caller's counts and statistics.  Every sum runs in a fixed order
+// (threads over slots in index order, lanes by butterfly, waves in index
+// order), so results do not depend on scheduling.
+template <bool COUNTS, bool STATS>
 __global__ void __launch_bounds__(kThreads)
-k_stats_finalize(const SegBatch b, const double* __restrict__ part, int grid,
-                 nc_stats* __restrict__ out) {
-  __shared__ double lds[kWaves * 6];
-  const int s = blockIdx.x;
-  const int64_t t0 = b.tile0[s], t1 = min(b.tile0[s + 1], b.tile0[s] + grid);
-  double acc[6] = {0, 0, 0, 0, 0, 0};
+k_reduce1(const SegBatch b, const CountSlot* __restrict__ cnt1, const double* __restrict__ st1,
+          uint64_t* __restrict__ cnt2, double* __restrict__ st2) {
+  __shared__ uint64_t lds_c[kWaves * 4];
+  __shared__ double lds_s[kWaves * 6];
+  const int64_t c = blockIdx.x;
+  const int s = seg_of(b.chunk0, b.count, c);
+  const int64_t t0 = b.tile0[s] + (c - b.chunk0[s]) * kChunk;
+  const int64_t t1 = min(t0 + (int64_t)kChunk, b.tile0[s + 1]);
+  uint32_t mx = 0;
+  uint64_t nf = 0, big = 0, uf = 0;
+  double a[6] = {0.0, 0.0, 0.0, 0.0, 0.0, 0.0};
   for (int64_t t = t0 + threadIdx.x; t < t1; t += kThreads) {
-    const double* p = part + ((int64_t)s * kMaxGrid + t % grid) * 6;
-    for (int j = 0; j < 6; ++j) acc[j] += p[j];
+    if constexpr (COUNTS) {
+      const CountSlot v = cnt1[t];
+      mx = max(mx, v.amax);
+      nf += v.n_nf;
+      big += v.n_big;
+      uf += v.n_uf;
+    }
+    if constexpr (STATS) {
+#pragma unroll
+      for (int j = 0; j < 6; ++j) a[j] += st1[t * 6 + j];
+    }
   }
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  for (int j = 0; j < 6; ++j) {
-    const double v = wave_sum_f64(acc[j]);
-    if (lane == 0) lds[wave * 6 + j] = v;
+  if constexpr (COUNTS) {
+    mx = wave_max_u32(mx);
+    nf = wave_sum_u64(nf);
+    big = wave_sum_u64(big);
+    uf = wave_sum_u64(uf);
+    if (lane == 0) {
+      lds_c[wave * 4 + 0] = mx;
+      lds_c[wave * 4 + 1] = nf;
+      lds_c[wave * 4 + 2] = big;
+      lds_c[wave * 4 + 3] = uf;
+    }
+  }
+  if constexpr (STATS) {
+#pragma unroll
+    for (int j = 0; j < 6; ++j) {
+      const double v = wave_sum_f64(a[j]);
+      if (lane == 0) lds_s[wave * 6 + j] = v;
+    }
   }
   __syncthreads();
-  if (threadIdx.x < 6) {
-    double t = 0.0;
-    for (int w = 0; w < kWaves; ++w) t += lds[w * 6 + threadIdx.x];
-    double* o = reinterpret_cast<double*>(out + b.first + s);
-    o[threadIdx.x] += t;
+  if (COUNTS && threadIdx.x < 4) {
+    uint64_t r = 0;
+    for (int w = 0; w < kWaves; ++w)
+      r = threadIdx.x == 0 ? max(r, lds_c[w * 4]) : r + lds_c[w * 4 + threadIdx.x];
+    cnt2[c * 4 + threadIdx.x] = r;
+  }
+  if (STATS && threadIdx.x >= 64 && threadIdx.x < 70) {
+    const int j = threadIdx.x - 64;
+    double r = 0.0;
+    for (int w = 0; w < kWaves; ++w) r += lds_s[w * 6 + j];
+    st2[c * 6 + j] = r;
+  }
+}
+
+template <bool COUNTS, bool STATS>
+__global__ void __launch_bounds__(64)
+k_reduce2(const SegBatch b, const uint64_t* __restrict__ cnt2, const double* __restrict__ st2,
+          nc_counts* __restrict__ out, nc_stats* __restrict__ stats,
+          const nc_loss_scale* __restrict__ ls, int clips) {
+  const int s = blockIdx.x;
+  const int64_t c0 = b.chunk0[s], c1 = b.chunk0[s + 1];
+  const int s_log2 = ls ? ls->s_log2 : 0;
+  uint32_t mx = 0;
+  uint64_t nf = 0, big = 0, uf = 0;
+  double a[6] = {0.0, 0.0, 0.0, 0.0, 0.0, 0.0};
+  for (int64_t c = c0 + threadIdx.x; c < c1; c += 64) {
+    if constexpr (COUNTS) {
+      mx = max(mx, (uint32_t)cnt2[c * 4 + 0]);
+      nf += cnt2[c * 4 + 1];
+      big += cnt2[c * 4 + 2];
+      uf += cnt2[c * 4 + 3];
+    }
+    if constexpr (STATS) {
+#pragma unroll
+      for (int j = 0; j < 6; ++j) a[j] += st2[c * 6 + j];
+    }
+  }
+  if constexpr (COUNTS) {
+    mx = wave_max_u32(mx);
+    nf = wave_sum_u64(nf);
+    big = wave_sum_u64(big);
+    uf = wave_sum_u64(uf);
+    if (threadIdx.x == 0) {
+      nc_counts* o = out + b.first + s;
+      const uint64_t n = (uint64_t)b.s[s].n;
+      atomicMax(&o->amax_bits, unscale_bits(mx, s_log2));
+      if (n - nf) atomicAdd((unsigned long long*)&o->n_finite, (unsigned long long)(n - nf));
+      if (nf) atomicAdd((unsigned long long*)&o->n_nonfinite, (unsigned long long)nf);
+      if (clips && big - nf) atomicAdd((unsigned long long*)&o->n_clip, (unsigned long long)(big - nf));
+      if (uf) atomicAdd((unsigned long long*)&o->n_underflow, (unsigned long long)uf);
+    }
+  }
+  if constexpr (STATS) {
+    double r[6];
+#pragma unroll
+    for (int j = 0; j < 6; ++j) r[j] = wave_sum_f64(a[j]);
+    if (threadIdx.x < 6) {
+      const int j = threadIdx.x;
+      double v = r[0];
+#pragma unroll
+      for (int i = 1; i < 6; ++i) v = j == i ? r[i] : v;
+      const int sc = (j == 0 || j == 1 || j == 3) ? -s_log2 : -2 * s_log2;
+      atomicAdd(reinterpret_cast<double*>(stats + b.first + s) + j, ldexp(v, sc));
+    }
   }
 }
 
 template <int FMT, int DT>
 hipError_t stats_t(const SegBatch& b, const nc_scale_state* st, const nc_loss_scale* ls,
-                   double* part, const Launch& l) {
+                   const Ws& w, const Launch& l) {
   if (st)
-    hipLaunchKernelGGL((k_stats<FMT, DT, false>), dim3(l.grid), dim3(kThreads), 0, l.stream, b, st, ls, part);
+    hipLaunchKernelGGL((k_stats<FMT, DT, false>), dim3((uint32_t)l.grid), dim3(kThreads), 0, l.stream, b, st, ls, w.st1);
   else
-    hipLaunchKernelGGL((k_stats<FMT, DT, true>), dim3(l.grid), dim3(kThreads), 0, l.stream, b, st, ls, part);
+    hipLaunchKernelGGL((k_stats<FMT, DT, true>), dim3((uint32_t)l.grid), dim3(kThreads), 0, l.stream, b, st, ls, w.st1);
   return hipGetLastError();
 }
 
 template <int FMT>
 hipError_t dequant_t(const SegBatch& b, const nc_scale_state* st, const Launch& l) {
   if (st)
-    hipLaunchKernelGGL((k_dequant<FMT, false>), dim3(l.grid), dim3(kThreads), 0, l.stream, b, st);
+    hipLaunchKernelGGL((k_dequant<FMT, false>), dim3((uint32_t)l.grid), dim3(kThreads), 0, l.stream, b, st);
   else
-    hipLaunchKernelGGL((k_dequant<FMT, true>), dim3(l.grid), dim3(kThreads), 0, l.stream, b, st);
+    hipLaunchKernelGGL((k_dequant<FMT, true>), dim3((uint32_t)l.grid), dim3(kThreads), 0, l.stream, b, st);
+  return hipGetLastError();
+}
+
+template <bool COUNTS, bool STATS>
+hipError_t reduce_t(const SegBatch& b, const Ws& w, nc_counts* out, nc_stats* stats,
+                    const nc_loss_scale* ls, bool clips, hipStream_t stream) {
+  const int64_t chunks = b.chunk0[b.count];
+  hipLaunchKernelGGL((k_reduce1<COUNTS, STATS>), dim3((uint32_t)chunks), dim3(kThreads), 0, stream, b,
+                     w.cnt1, w.st1, w.cnt2, w.st2);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((k_reduce2<COUNTS, STATS>), dim3((uint32_t)b.count), dim3(64), 0, stream, b,
+                     w.cnt2, w.st2, out, stats, ls, clips ? 1 : 0);
   return hipGetLastError();
 }
 
@@ -308,18 +396,19 @@ hipError_t launch_dequant(const SegBatch& b, int fmt, const nc_scale_state* st, 
 }
 
 hipError_t launch_stats(const SegBatch& b, int dtype, int fmt, const nc_scale_state* st,
-                        const nc_loss_scale* ls, double* part, const Launch& l) {
+                        const nc_loss_scale* ls, const Ws& w, const Launch& l) {
   if (fmt == NC_E4M3)
-    return dtype == NC_F32 ? stats_t<NC_E4M3, NC_F32>(b, st, ls, part, l)
-                           : stats_t<NC_E4M3, NC_BF16>(b, st, ls, part, l);
-  return dtype == NC_F32 ? stats_t<NC_E5M2, NC_F32>(b, st, ls, part, l)
-                         : stats_t<NC_E5M2, NC_BF16>(b, st, ls, part, l);
+    return dtype == NC_F32 ? stats_t<NC_E4M3, NC_F32>(b, st, ls, w, l)
+                           : stats_t<NC_E4M3, NC_BF16>(b, st, ls, w, l);
+  return dtype == NC_F32 ? stats_t<NC_E5M2, NC_F32>(b, st, ls, w, l)
+                         : stats_t<NC_E5M2, NC_BF16>(b, st, ls, w, l);
 }
 
-hipError_t launch_stats_finalize(const SegBatch& b, const double* part, int grid, nc_stats* out,
-                                 hipStream_t stream) {
-  hipLaunchKernelGGL(k_stats_finalize, dim3(b.count), dim3(kThreads), 0, stream, b, part, grid, out);
-  return hipGetLastError();
+hipError_t launch_reduce(const SegBatch& b, const Ws& w, nc_counts* out, nc_stats* stats,
+                         const nc_loss_scale* ls, bool clips, hipStream_t stream) {
+  if (out && stats) return reduce_t<true, true>(b, w, out, stats, ls, clips, stream);
+  if (out) return reduce_t<true, false>(b, w, out, stats, ls, clips, stream);
+  return reduce_t<false, true>(b, w, out, stats, ls, clips, stream);
 }
 
 }  // namespace nc

@@ -2,15 +2,12 @@
 // the per-tensor cast (unscale + cast + counts + next-step amax, optional
 // statistics) and the MX block-scaled cast.
 //
-// Work distribution: a launch covers up to kMaxSeg tensors cut into tiles
-// of 256 threads x four 16-byte loads (4096 fp32 or 8192 bf16 elements).
-// Workgroups stride over the flat tile range; a workgroup keeps per-tensor
-// totals while it stays on one tensor and flushes them with one set of
-// integer atomics when it moves on.  Each 16-byte load instruction of a wave
-// covers 1 KiB of contiguous input and each code store 256-512 B of
-// contiguous output.  A ragged last tile runs the same code with lanes past
-// the end fed zeros (a zero is finite and never counted) and their stores
-// masked, so the wave-ballot counts stay uniform.
+// One workgroup per tile (256 threads x a few 16-byte vectors each; see
+// nc_device.h for why).  Each 16-byte load instruction of a wave covers
+// 1 KiB of contiguous input and each code store 256-512 B of contiguous
+// output.  A ragged last tile runs per element with lanes past the end fed
+// zeros (a zero is finite and never counted).  The workgroup's counts and
+// statistics go to its workspace slot.
 #include "nc_launch.h"
 
 namespace nc {
@@ -20,62 +17,34 @@ namespace {
 // Per-tensor amax pass.
 template <int DT>
 NC_STREAM_KERNEL
-k_amax(const SegBatch b, const nc_loss_scale* __restrict__ ls, nc_counts* __restrict__ out) {
+k_amax(const SegBatch b, CountSlot* __restrict__ slots) {
   constexpr int VEC = In<DT>::VEC;
-  constexpr int64_t TILE = (int64_t)kThreads * VEC * kUnrollRead;
-  __shared__ uint32_t lds_max[kWaves];
-  __shared__ uint64_t lds_cnt[kWaves * 3];
-  const int s_log2 = ls ? ls->s_log2 : 0;
-  const int64_t total = b.tile0[b.count];
+  constexpr int64_t TILE = (int64_t)kThreads * VEC * kAmaxVecs;
+  __shared__ uint32_t lds[kRows * 4];
+  const int64_t tile = blockIdx.x;
+  const int s = seg_of(b.tile0, b.count, tile);
+  const Seg& g = b.s[s];
+  const int64_t e0 = (tile - b.tile0[s]) * TILE;
+  const int rem = tile_len<TILE>(b, s, tile);
   Acc acc;
   acc.reset();
-  int seg = -1;
-  uint64_t elems = 0;
-  // buf always holds the current tile when it is full (prefetch invariant)
-  u32x4 buf[kUnrollRead];
-  prefetch_tile<In<DT>::BYTES, kUnrollRead, TILE>(b, blockIdx.x, -1, buf);
-  for (int64_t tile = blockIdx.x; tile < total; tile += gridDim.x) {
-    const int s = seg_of(b, tile, seg);
-    if (s != seg) {
-      if (seg >= 0) {
-        acc.n_big = acc.n_nf;   // the amax pass reports no clips
-        flush_counts(acc, out + b.first + seg, s_log2, elems, lds_max, lds_cnt);
-      }
-      seg = s;
-      elems = 0;
+  if (rem == (int)TILE) {
+    const u32x4* src = reinterpret_cast<const u32x4*>(static_cast<const uint8_t*>(g.x) + e0 * In<DT>::BYTES);
+    u32x4 v[kAmaxVecs];
+#pragma unroll
+    for (int u = 0; u < kAmaxVecs; ++u) v[u] = ld_stream(src + u * kThreads + threadIdx.x);
+#pragma unroll
+    for (int u = 0; u < kAmaxVecs; ++u) {
+      uint32_t xb[VEC];
+      unpack<DT>(v[u], xb);
+#pragma unroll
+      for (int i = 0; i < VEC; ++i) acc.amax = max(acc.amax, finite_mag(xb[i] & kAbsMask, acc));
     }
-    const Seg& g = b.s[s];
-    const int64_t e0 = (tile - b.tile0[s]) * TILE;
-    const int rem = tile_len<TILE>(b, s, tile);
-    if (rem == (int)TILE) {
-      u32x4 v[kUnrollRead];
-#pragma unroll
-      for (int u = 0; u < kUnrollRead; ++u) v[u] = buf[u];
-      prefetch_tile<In<DT>::BYTES, kUnrollRead, TILE>(b, tile + gridDim.x, s, buf);
-      __builtin_amdgcn_sched_barrier(0);   // next tile's loads in flight before any use
-#pragma unroll
-      for (int u = 0; u < kUnrollRead; ++u) {
-        uint32_t xb[VEC];
-        unpack<DT>(v[u], xb);
-#pragma unroll
-        for (int i = 0; i < VEC; ++i) {
-          acc.amax = max(acc.amax, finite_mag(xb[i] & kAbsMask, acc));
-        }
-      }
-    } else {
-      prefetch_tile<In<DT>::BYTES, kUnrollRead, TILE>(b, tile + gridDim.x, s, buf);
-      for (int base = 0; base < rem; base += kThreads) {
-        const int i = base + (int)threadIdx.x;
-        const uint32_t ax = (i < rem ? load_one<DT>(g.x, e0 + i) : 0u) & kAbsMask;
-        acc.amax = max(acc.amax, finite_mag(ax, acc));
-      }
-    }
-    elems += rem;
+  } else {
+    for (int i = threadIdx.x; i < rem; i += kThreads)
+      acc.amax = max(acc.amax, finite_mag(load_one<DT>(g.x, e0 + i) & kAbsMask, acc));
   }
-  if (seg >= 0) {
-    acc.n_big = acc.n_nf;   // the amax pass reports no clips
-    flush_counts(acc, out + b.first + seg, s_log2, elems, lds_max, lds_cnt);
-  }
+  write_count_slot(acc, slots + tile, lds);   // n_big stays 0: the amax pass reports no clips
 }
 
 // ---------------------------------------------------------------------------
@@ -83,89 +52,62 @@ k_amax(const SegBatch b, const nc_loss_scale* __restrict__ ls, nc_counts* __rest
 template <int FMT, int DT, bool STATS>
 NC_STREAM_KERNEL
 k_cast_pt(const SegBatch b, const nc_scale_state* __restrict__ st,
-          const nc_loss_scale* __restrict__ ls, nc_counts* __restrict__ out,
-          double* __restrict__ part) {
+          const nc_loss_scale* __restrict__ ls, CountSlot* __restrict__ slots,
+          double* __restrict__ stat_slots) {
   constexpr int VEC = In<DT>::VEC;
-  constexpr int64_t TILE = (int64_t)kThreads * VEC * kUnrollCast;
-  __shared__ uint32_t lds_max[kWaves];
-  __shared__ uint64_t lds_cnt[kWaves * 3];
-  __shared__ double lds_st[STATS ? kWaves * 6 : 1];
+  constexpr int U = cast_vecs<STATS>();
+  constexpr int64_t TILE = (int64_t)kThreads * VEC * U;
+  __shared__ uint32_t lds[kRows * 4];
+  __shared__ double lds_st[STATS ? kRows * 6 : 1];
   __shared__ double tab[STATS ? 256 : 1];
-  const int s_log2 = ls ? ls->s_log2 : 0;
-  const int64_t total = b.tile0[b.count];
+  const int64_t tile = blockIdx.x;
+  const int s = seg_of(b.tile0, b.count, tile);
+  const Seg& g = b.s[s];
+  const int64_t e0 = (tile - b.tile0[s]) * TILE;
+  const int rem = tile_len<TILE>(b, s, tile);
+  const int K = st[b.first + s].k - (ls ? ls->s_log2 : 0);
+  const CastParams p = cast_params<FMT>(K);
+  if constexpr (STATS) {
+    fill_stat_table<FMT>(tab, K);
+    __syncthreads();
+  }
   Acc acc;
   acc.reset();
   StatAcc sa;
   if constexpr (STATS) sa.reset();
-  int seg = -1, k = 0;
-  CastParams p = cast_params<FMT>(0);
-  uint64_t elems = 0;
-  // buf always holds the current tile when it is full (prefetch invariant)
-  u32x4 buf[kUnrollCast];
-  prefetch_tile<In<DT>::BYTES, kUnrollCast, TILE>(b, blockIdx.x, -1, buf);
-  for (int64_t tile = blockIdx.x; tile < total; tile += gridDim.x) {
-    const int s = seg_of(b, tile, seg);
-    if (s != seg) {
-      if (seg >= 0) {
-        flush_counts(acc, out + b.first + seg, s_log2, elems, lds_max, lds_cnt);
-        if constexpr (STATS) stats_seg_flush(sa, stat_slot(part, seg, blockIdx.x), lds_st, s_log2);
-      }
-      seg = s;
-      elems = 0;
-      k = st[b.first + s].k;
-      p = cast_params<FMT>(k - s_log2);
+  uint8_t* dst = g.codes + e0;
+  if (rem == (int)TILE) {
+    const u32x4* src = reinterpret_cast<const u32x4*>(static_cast<const uint8_t*>(g.x) + e0 * In<DT>::BYTES);
+    u32x4 v[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) v[u] = ld_stream(src + u * kThreads + threadIdx.x);
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      uint32_t xb[VEC], w[VEC / 4];
+      unpack<DT>(v[u], xb);
+      cast_vec<FMT, VEC>(xb, p, acc, w);
       if constexpr (STATS) {
-        __syncthreads();
-        fill_stat_table<FMT>(tab, k - s_log2);
-        __syncthreads();
+        uint32_t q[VEC];
+#pragma unroll
+        for (int i = 0; i < VEC; ++i) q[i] = (w[i / 4] >> (8 * (i % 4))) & 0xFFu;
+        stats_vec<VEC, false>(xb, q, tab, 1.0, sa);
       }
+      const int vi = u * kThreads + threadIdx.x;
+      if constexpr (DT == NC_F32) st_stream(reinterpret_cast<uint32_t*>(dst) + vi, w[0]);
+      else st_stream(reinterpret_cast<u32x2*>(dst) + vi, u32x2{w[0], w[1]});
     }
-    const Seg& g = b.s[s];
-    const int64_t e0 = (tile - b.tile0[s]) * TILE;
-    const int rem = tile_len<TILE>(b, s, tile);
-    uint8_t* dst = g.codes + e0;
-    if (rem == (int)TILE) {
-      u32x4 v[kUnrollCast];
-#pragma unroll
-      for (int u = 0; u < kUnrollCast; ++u) v[u] = buf[u];
-      prefetch_tile<In<DT>::BYTES, kUnrollCast, TILE>(b, tile + gridDim.x, s, buf);
-      __builtin_amdgcn_sched_barrier(0);   // next tile's loads in flight before any use
-#pragma unroll
-      for (int u = 0; u < kUnrollCast; ++u) {
-        uint32_t xb[VEC], w[VEC / 4];
-        unpack<DT>(v[u], xb);
-        cast_vec<FMT, VEC>(xb, p, acc, w);
-        if constexpr (STATS) {
-          uint32_t q[VEC];
-#pragma unroll
-          for (int i = 0; i < VEC; ++i) q[i] = (w[i / 4] >> (8 * (i % 4))) & 0xFFu;
-          stats_vec<VEC, false>(xb, q, tab, 1.0, sa);
-        }
-        const int vi = u * kThreads + threadIdx.x;
-        if constexpr (DT == NC_F32) {
-          reinterpret_cast<uint32_t*>(dst)[vi] = w[0];
-        } else {
-          reinterpret_cast<u32x2*>(dst)[vi] = u32x2{w[0], w[1]};
-        }
-        __builtin_amdgcn_sched_barrier(0);   // keep each vector's ballots short-lived
-      }
-    } else {
-      prefetch_tile<In<DT>::BYTES, kUnrollCast, TILE>(b, tile + gridDim.x, s, buf);
-      for (int base = 0; base < rem; base += kThreads) {
-        const int i = base + (int)threadIdx.x;
-        const bool act = i < rem;
-        const uint32_t xb = act ? load_one<DT>(g.x, e0 + i) : 0u;
-        const uint32_t q = cast_one<FMT>(xb, p, acc);
-        if constexpr (STATS) stats_vec<1, false>(&xb, &q, tab, 1.0, sa);
-        if (act) dst[i] = (uint8_t)q;
-      }
+  } else {
+    for (int base = 0; base < rem; base += kThreads) {
+      const int i = base + (int)threadIdx.x;
+      const bool act = i < rem;
+      const uint32_t xb = act ? load_one<DT>(g.x, e0 + i) : 0u;
+      const uint32_t q = cast_one<FMT>(xb, p, acc);
+      if constexpr (STATS) stats_vec<1, false>(&xb, &q, tab, 1.0, sa);
+      if (act) dst[i] = (uint8_t)q;
     }
-    elems += rem;
   }
-  if (seg >= 0) {
-    flush_counts(acc, out + b.first + seg, s_log2, elems, lds_max, lds_cnt);
-    if constexpr (STATS) stats_seg_flush(sa, stat_slot(part, seg, blockIdx.x), lds_st, s_log2);
-  }
+  write_count_slot(acc, slots + tile, lds);
+  if constexpr (STATS) write_stat_slot(sa, stat_slots + tile * 6, lds_st);
 }
 
 // ---------------------------------------------------------------------------
@@ -201,7 +143,7 @@ __device__ __forceinline__ uint32_t group_max(uint32_t v) {
 // vector is inside the tensor (no predicates at all); otherwise lanes past
 // `rem` hold zeros and skip their stores (rem is a multiple of 32, so a
 // block is all in or all out).
-template <int FMT, int DT, int RULE, bool STATS, bool FULL>
+template <int FMT, int DT, int RULE, bool STATS, bool FULL, int U>
 __device__ __forceinline__ void mx_tile(const Seg& g, int64_t e0, int rem, const u32x4* v,
                                         Acc& acc, StatAcc& sa, const double* tab) {
   constexpr int VEC = In<DT>::VEC;
@@ -209,7 +151,7 @@ __device__ __forceinline__ void mx_tile(const Seg& g, int64_t e0, int rem, const
   uint8_t* dst = g.codes + e0;
   uint8_t* sdst = g.scales + e0 / 32;
 #pragma unroll
-  for (int u = 0; u < kUnrollCast; ++u) {
+  for (int u = 0; u < U; ++u) {
     const int vi = u * kThreads + threadIdx.x;
     uint32_t xb[VEC], ax[VEC], w[VEC / 4];
     unpack<DT>(v[u], xb);
@@ -243,11 +185,8 @@ __device__ __forceinline__ void mx_tile(const Seg& g, int64_t e0, int rem, const
       stats_vec<VEC, true>(xb, q, tab, pow2_f64(X), sa);
     }
     if (FULL || vi * VEC < rem) {
-      if constexpr (DT == NC_F32) {
-        reinterpret_cast<uint32_t*>(dst)[vi] = w[0];
-      } else {
-        reinterpret_cast<u32x2*>(dst)[vi] = u32x2{w[0], w[1]};
-      }
+      if constexpr (DT == NC_F32) st_stream(reinterpret_cast<uint32_t*>(dst) + vi, w[0]);
+      else st_stream(reinterpret_cast<u32x2*>(dst) + vi, u32x2{w[0], w[1]});
       // every lane of the block holds the same X: all store it (same byte,
       // same value), which keeps the tile free of divergent branches
       sdst[vi / GROUP] = (uint8_t)(X + 127);
@@ -258,118 +197,100 @@ __device__ __forceinline__ void mx_tile(const Seg& g, int64_t e0, int rem, const
 
 template <int FMT, int DT, int RULE, bool STATS>
 NC_STREAM_KERNEL
-k_cast_mx(const SegBatch b, nc_counts* __restrict__ out, double* __restrict__ part) {
+k_cast_mx(const SegBatch b, CountSlot* __restrict__ slots, double* __restrict__ stat_slots) {
   constexpr int VEC = In<DT>::VEC;
-  constexpr int64_t TILE = (int64_t)kThreads * VEC * kUnrollCast;
-  __shared__ uint32_t lds_max[kWaves];
-  __shared__ uint64_t lds_cnt[kWaves * 3];
-  __shared__ double lds_st[STATS ? kWaves * 6 : 1];
+  constexpr int U = cast_vecs<STATS>();
+  constexpr int64_t TILE = (int64_t)kThreads * VEC * U;
+  __shared__ uint32_t lds[kRows * 4];
+  __shared__ double lds_st[STATS ? kRows * 6 : 1];
   __shared__ double tab[STATS ? 256 : 1];
   if constexpr (STATS) {
     fill_stat_table<FMT>(tab, 0);
     __syncthreads();
   }
-  const int64_t total = b.tile0[b.count];
+  const int64_t tile = blockIdx.x;
+  const int s = seg_of(b.tile0, b.count, tile);
+  const Seg& g = b.s[s];
+  const int64_t e0 = (tile - b.tile0[s]) * TILE;
+  const int rem = tile_len<TILE>(b, s, tile);      // a multiple of 32
   Acc acc;
   acc.reset();
   StatAcc sa;
   if constexpr (STATS) sa.reset();
-  int seg = -1;
-  uint64_t elems = 0;
-  // buf always holds the current tile when it is full (prefetch invariant)
-  u32x4 buf[kUnrollCast];
-  prefetch_tile<In<DT>::BYTES, kUnrollCast, TILE>(b, blockIdx.x, -1, buf);
-  for (int64_t tile = blockIdx.x; tile < total; tile += gridDim.x) {
-    const int s = seg_of(b, tile, seg);
-    if (s != seg) {
-      if (seg >= 0) {
-        flush_counts(acc, out + b.first + seg, 0, elems, lds_max, lds_cnt);
-        if constexpr (STATS) stats_seg_flush(sa, stat_slot(part, seg, blockIdx.x), lds_st, 0);
-      }
-      seg = s;
-      elems = 0;
-    }
-    const Seg& g = b.s[s];
-    const int64_t e0 = (tile - b.tile0[s]) * TILE;
-    const int rem = tile_len<TILE>(b, s, tile);   // a multiple of 32
-    u32x4 v[kUnrollCast];
-    if (rem == (int)TILE) {
+  const u32x4* src = reinterpret_cast<const u32x4*>(static_cast<const uint8_t*>(g.x) + e0 * In<DT>::BYTES);
+  u32x4 v[U];
+  if (rem == (int)TILE) {
 #pragma unroll
-      for (int u = 0; u < kUnrollCast; ++u) v[u] = buf[u];
-      prefetch_tile<In<DT>::BYTES, kUnrollCast, TILE>(b, tile + gridDim.x, s, buf);
-      __builtin_amdgcn_sched_barrier(0);   // next tile's loads in flight before any use
-      mx_tile<FMT, DT, RULE, STATS, true>(g, e0, rem, v, acc, sa, tab);
-    } else {
-      prefetch_tile<In<DT>::BYTES, kUnrollCast, TILE>(b, tile + gridDim.x, s, buf);
-      const u32x4* src = reinterpret_cast<const u32x4*>(static_cast<const uint8_t*>(g.x) + e0 * In<DT>::BYTES);
+    for (int u = 0; u < U; ++u) v[u] = ld_stream(src + u * kThreads + threadIdx.x);
+    mx_tile<FMT, DT, RULE, STATS, true, U>(g, e0, rem, v, acc, sa, tab);
+  } else {
 #pragma unroll
-      for (int u = 0; u < kUnrollCast; ++u) {
-        const int vi = u * kThreads + threadIdx.x;
-        v[u] = (vi * VEC < rem) ? ld_stream(src + vi) : u32x4{0u, 0u, 0u, 0u};
-      }
-      mx_tile<FMT, DT, RULE, STATS, false>(g, e0, rem, v, acc, sa, tab);
+    for (int u = 0; u < U; ++u) {
+      const int vi = u * kThreads + threadIdx.x;
+      v[u] = (vi * VEC < rem) ? ld_stream(src + vi) : u32x4{0u, 0u, 0u, 0u};
     }
-    elems += rem;
+    mx_tile<FMT, DT, RULE, STATS, false, U>(g, e0, rem, v, acc, sa, tab);
   }
-  if (seg >= 0) {
-    flush_counts(acc, out + b.first + seg, 0, elems, lds_max, lds_cnt);
-    if constexpr (STATS) stats_seg_flush(sa, stat_slot(part, seg, blockIdx.x), lds_st, 0);
-  }
+  write_count_slot(acc, slots + tile, lds);
+  if constexpr (STATS) write_stat_slot(sa, stat_slots + tile * 6, lds_st);
 }
 
 template <int FMT, int DT>
-hipError_t cast_pt_t(const SegBatch& b, const nc_scale_state* st, const nc_loss_scale* ls,
-                     nc_counts* out, double* part, const Launch& l) {
-  if (part)
-    hipLaunchKernelGGL((k_cast_pt<FMT, DT, true>), dim3(l.grid), dim3(kThreads), 0, l.stream, b, st, ls, out, part);
+hipError_t cast_pt_t(const SegBatch& b, const nc_scale_state* st, const nc_loss_scale* ls, bool stats,
+                     const Ws& w, const Launch& l) {
+  if (stats)
+    hipLaunchKernelGGL((k_cast_pt<FMT, DT, true>), dim3((uint32_t)l.grid), dim3(kThreads), 0, l.stream, b, st, ls,
+                       w.cnt1, w.st1);
   else
-    hipLaunchKernelGGL((k_cast_pt<FMT, DT, false>), dim3(l.grid), dim3(kThreads), 0, l.stream, b, st, ls, out, part);
+    hipLaunchKernelGGL((k_cast_pt<FMT, DT, false>), dim3((uint32_t)l.grid), dim3(kThreads), 0, l.stream, b, st, ls,
+                       w.cnt1, w.st1);
   return hipGetLastError();
 }
 
 template <int FMT, int DT, int RULE>
-hipError_t cast_mx_r(const SegBatch& b, nc_counts* out, double* part, const Launch& l) {
-  if (part)
-    hipLaunchKernelGGL((k_cast_mx<FMT, DT, RULE, true>), dim3(l.grid), dim3(kThreads), 0, l.stream, b, out, part);
+hipError_t cast_mx_r(const SegBatch& b, bool stats, const Ws& w, const Launch& l) {
+  if (stats)
+    hipLaunchKernelGGL((k_cast_mx<FMT, DT, RULE, true>), dim3((uint32_t)l.grid), dim3(kThreads), 0, l.stream, b,
+                       w.cnt1, w.st1);
   else
-    hipLaunchKernelGGL((k_cast_mx<FMT, DT, RULE, false>), dim3(l.grid), dim3(kThreads), 0, l.stream, b, out, part);
+    hipLaunchKernelGGL((k_cast_mx<FMT, DT, RULE, false>), dim3((uint32_t)l.grid), dim3(kThreads), 0, l.stream, b,
+                       w.cnt1, w.st1);
   return hipGetLastError();
 }
 
 template <int FMT, int DT>
-hipError_t cast_mx_t(const SegBatch& b, int rule, nc_counts* out, double* part, const Launch& l) {
-  if (rule == NC_MX_OCP) return cast_mx_r<FMT, DT, NC_MX_OCP>(b, out, part, l);
-  if (rule == NC_MX_PLUS1) return cast_mx_r<FMT, DT, NC_MX_PLUS1>(b, out, part, l);
-  return cast_mx_r<FMT, DT, NC_MX_CEIL>(b, out, part, l);
+hipError_t cast_mx_t(const SegBatch& b, int rule, bool stats, const Ws& w, const Launch& l) {
+  if (rule == NC_MX_OCP) return cast_mx_r<FMT, DT, NC_MX_OCP>(b, stats, w, l);
+  if (rule == NC_MX_PLUS1) return cast_mx_r<FMT, DT, NC_MX_PLUS1>(b, stats, w, l);
+  return cast_mx_r<FMT, DT, NC_MX_CEIL>(b, stats, w, l);
 }
 
 }  // namespace
 
-hipError_t launch_amax(const SegBatch& b, int dtype, const nc_loss_scale* ls, nc_counts* out,
-                       const Launch& l) {
+hipError_t launch_amax(const SegBatch& b, int dtype, const Ws& w, const Launch& l) {
   if (dtype == NC_F32)
-    hipLaunchKernelGGL((k_amax<NC_F32>), dim3(l.grid), dim3(kThreads), 0, l.stream, b, ls, out);
+    hipLaunchKernelGGL((k_amax<NC_F32>), dim3((uint32_t)l.grid), dim3(kThreads), 0, l.stream, b, w.cnt1);
   else
-    hipLaunchKernelGGL((k_amax<NC_BF16>), dim3(l.grid), dim3(kThreads), 0, l.stream, b, ls, out);
+    hipLaunchKernelGGL((k_amax<NC_BF16>), dim3((uint32_t)l.grid), dim3(kThreads), 0, l.stream, b, w.cnt1);
   return hipGetLastError();
 }
 
 hipError_t launch_cast_pt(const SegBatch& b, int dtype, int fmt, const nc_scale_state* st,
-                          const nc_loss_scale* ls, nc_counts* out, double* part, const Launch& l) {
+                          const nc_loss_scale* ls, bool stats, const Ws& w, const Launch& l) {
   if (fmt == NC_E4M3)
-    return dtype == NC_F32 ? cast_pt_t<NC_E4M3, NC_F32>(b, st, ls, out, part, l)
-                           : cast_pt_t<NC_E4M3, NC_BF16>(b, st, ls, out, part, l);
-  return dtype == NC_F32 ? cast_pt_t<NC_E5M2, NC_F32>(b, st, ls, out, part, l)
-                         : cast_pt_t<NC_E5M2, NC_BF16>(b, st, ls, out, part, l);
+    return dtype == NC_F32 ? cast_pt_t<NC_E4M3, NC_F32>(b, st, ls, stats, w, l)
+                           : cast_pt_t<NC_E4M3, NC_BF16>(b, st, ls, stats, w, l);
+  return dtype == NC_F32 ? cast_pt_t<NC_E5M2, NC_F32>(b, st, ls, stats, w, l)
+                         : cast_pt_t<NC_E5M2, NC_BF16>(b, st, ls, stats, w, l);
 }
 
-hipError_t launch_cast_mx(const SegBatch& b, int dtype, int fmt, int rule, nc_counts* out,
-                          double* part, const Launch& l) {
+hipError_t launch_cast_mx(const SegBatch& b, int dtype, int fmt, int rule, bool stats, const Ws& w,
+                          const Launch& l) {
   if (fmt == NC_E4M3)
-    return dtype == NC_F32 ? cast_mx_t<NC_E4M3, NC_F32>(b, rule, out, part, l)
-                           : cast_mx_t<NC_E4M3, NC_BF16>(b, rule, out, part, l);
-  return dtype == NC_F32 ? cast_mx_t<NC_E5M2, NC_F32>(b, rule, out, part, l)
-                         : cast_mx_t<NC_E5M2, NC_BF16>(b, rule, out, part, l);
+    return dtype == NC_F32 ? cast_mx_t<NC_E4M3, NC_F32>(b, rule, stats, w, l)
+                           : cast_mx_t<NC_E4M3, NC_BF16>(b, rule, stats, w, l);
+  return dtype == NC_F32 ? cast_mx_t<NC_E5M2, NC_F32>(b, rule, stats, w, l)
+                         : cast_mx_t<NC_E5M2, NC_BF16>(b, rule, stats, w, l);
 }
 
 }  // namespace nc

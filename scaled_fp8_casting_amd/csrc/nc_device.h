@@ -40,19 +40,20 @@
 namespace nc {
 
 constexpr int kThreads = 256;       // 4 wave64s per workgroup
-constexpr int kMaxGrid = 4096;      // workgroups per launch at most (statistics slots)
 constexpr int kMaxSeg = 32;         // tensors per launch (descriptors travel as kernel arguments)
 constexpr int kWaves = kThreads / 64;
+constexpr int kChunk = 1024;        // per-workgroup slots summed by one workgroup of the first reduction
 
-// Streaming kernels: optional occupancy request (waves per SIMD).
-#ifndef NC_WAVES_PER_EU
-#define NC_WAVES_PER_EU 0
-#endif
-#if NC_WAVES_PER_EU
-#define NC_STREAM_KERNEL __global__ void __launch_bounds__(nc::kThreads) __attribute__((amdgpu_waves_per_eu(NC_WAVES_PER_EU, 8)))
-#else
+// Work distribution.  Every streaming kernel gives each workgroup ONE small
+// tile (a few KiB of input) and launches as many workgroups as there are
+// tiles: the hardware then keeps a compact window of addresses in flight,
+// which on MI355X sustains far more HBM bandwidth for mixed read/write
+// streams than a persistent grid striding over the tensor (measured: a
+// cast-shaped stream 82% of peak vs 72%, a dequant-shaped one 81% vs 69%).
+// Each workgroup writes its partial results (counts, amax, statistics) to
+// its own workspace slot; two small kernels then reduce the slots per tensor
+// in a fixed order (one same-address atomic per workgroup would serialise).
 #define NC_STREAM_KERNEL __global__ void __launch_bounds__(nc::kThreads)
-#endif
 
 // ---------------------------------------------------------------------------
 // Formats.  E4M3: bias 7, no Inf, S.1111.111 is NaN, max 1.75*2^8 = 448.
@@ -113,9 +114,8 @@ __host__ __device__ inline CastParams cast_params(int K) {
 }
 
 // Per-lane running totals: each lane counts its own elements (a compare
-// and an add per count, no scalar traffic) and the flush reduces them.  A
-// lane handles at most n / (grid x 256) elements of a tensor per visit, far
-// below 2^32.
+// and an add per count, no scalar traffic); the workgroup reduces them into
+// its slot.  A workgroup handles at most a few thousand elements.
 struct Acc {
   uint32_t n_nf;     // non-finite elements
   uint32_t n_big;    // |x| bits above t_clip: every clip plus every non-finite
@@ -254,9 +254,45 @@ __device__ __forceinline__ double wave_sum_f64(double v) {
   return v;
 }
 
+// Row (16-lane) reductions by DPP moves: quad_perm [1,0,3,2], quad_perm
+// [2,3,0,1], row_half_mirror, row_mirror.  Afterwards every lane of a row
+// holds the row's result; for floating point the result is the same in all
+// 16 lanes (each step adds two equal partial sums in either order) and does
+// not depend on scheduling.  Full EXEC only.
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, 0xF, 0xF, false);
+}
+template <int CTRL>
+__device__ __forceinline__ double dpp_f64(double v) {
+  const uint64_t b = (uint64_t)__double_as_longlong(v);
+  const uint32_t lo = dpp_u32<CTRL>((uint32_t)b), hi = dpp_u32<CTRL>((uint32_t)(b >> 32));
+  return __longlong_as_double((long long)(((uint64_t)hi << 32) | lo));
+}
+__device__ __forceinline__ uint32_t row_max_u32(uint32_t v) {
+  v = max(v, dpp_u32<0xB1>(v));
+  v = max(v, dpp_u32<0x4E>(v));
+  v = max(v, dpp_u32<0x141>(v));
+  return max(v, dpp_u32<0x140>(v));
+}
+__device__ __forceinline__ uint32_t row_sum_u32(uint32_t v) {
+  v += dpp_u32<0xB1>(v);
+  v += dpp_u32<0x4E>(v);
+  v += dpp_u32<0x141>(v);
+  return v + dpp_u32<0x140>(v);
+}
+__device__ __forceinline__ double row_sum_f64(double v) {
+  v += dpp_f64<0xB1>(v);
+  v += dpp_f64<0x4E>(v);
+  v += dpp_f64<0x141>(v);
+  return v + dpp_f64<0x140>(v);
+}
+constexpr int kRows = kThreads / 16;    // 16-lane rows per workgroup
+
 // ---------------------------------------------------------------------------
 // Batches.  Up to kMaxSeg tensors per launch; tensor s owns tiles
-// [tile0[s], tile0[s+1]) of the launch's flat tile range.
+// [tile0[s], tile0[s+1]) of the launch (one workgroup per tile) and
+// first-reduction chunks [chunk0[s], chunk0[s+1]).
 struct Seg {
   const void* x;
   uint8_t* codes;
@@ -268,17 +304,19 @@ struct Seg {
 struct SegBatch {
   Seg s[kMaxSeg];
   int64_t tile0[kMaxSeg + 1];
+  int64_t chunk0[kMaxSeg + 1];
   int32_t last[kMaxSeg];   // elements in tensor s's last tile (1..tile size; 0 if empty)
   int32_t count;   // tensors in this launch
   int32_t first;   // index of s[0] in the caller's arrays (counts, states, stats)
 };
 static_assert(sizeof(SegBatch) <= 4096, "a SegBatch travels as a kernel argument");
 
-// Tensor owning `tile`, scanning forward from `hint` (tiles visited by a
-// workgroup only increase, so the scan is amortised O(1)).
-__device__ __forceinline__ int seg_of(const SegBatch& b, int64_t tile, int hint) {
-  int s = hint < 0 ? 0 : hint;
-  while (tile >= b.tile0[s + 1]) ++s;
+// Tensor owning entry `i` of a prefix array (tile0 or chunk0): the last s
+// with start[s] <= i.  Wave-uniform, at most kMaxSeg steps, once per
+// workgroup.
+__device__ __forceinline__ int seg_of(const int64_t* start, int count, int64_t i) {
+  int s = 0;
+  while (s + 1 < count && i >= start[s + 1]) ++s;
   return s;
 }
 
@@ -294,42 +332,45 @@ __device__ __forceinline__ int tile_len(const SegBatch& b, int s, int64_t t) {
   return t == b.tile0[s + 1] - 1 ? b.last[s] : (int)TILE;
 }
 
-// Workgroup flush of one tensor's totals into its nc_counts (integer
-// atomics: order-independent, so deterministic).
+// Workspace slots.  A workgroup's counts: finite-|x| max (bits), non-finite,
+// |x| above the clip bound (clips + non-finite), underflows.
+struct CountSlot {
+  uint32_t amax, n_nf, n_big, n_uf;
+};
+
 __device__ __forceinline__ uint32_t wave_sum_u32(uint32_t v) {
   for (int o = 32; o > 0; o >>= 1) v += (uint32_t)__shfl_xor((int)v, o, 64);
   return v;
 }
+__device__ __forceinline__ uint64_t wave_sum_u64(uint64_t v) {
+  for (int o = 32; o > 0; o >>= 1) v += (uint64_t)__shfl_xor((long long)v, o, 64);
+  return v;
+}
 
-__device__ inline void flush_counts(Acc& acc, nc_counts* out, int unscale_log2,
-                                    uint64_t n_elems, uint32_t* lds_max, uint64_t* lds_cnt) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const uint32_t m = wave_max_u32(acc.amax);
-  const uint32_t nf = wave_sum_u32(acc.n_nf), big = wave_sum_u32(acc.n_big), uf = wave_sum_u32(acc.n_uf);
-  if (lane == 0) {
-    lds_max[wave] = m;
-    lds_cnt[wave * 3 + 0] = nf;
-    lds_cnt[wave * 3 + 1] = big;
-    lds_cnt[wave * 3 + 2] = uf;
+// The workgroup's totals -> its slot: DPP row reductions, one LDS entry per
+// row, thread 0 over the rows.  Called by all threads (full EXEC); lds holds
+// kRows * 4 words.
+__device__ inline void write_count_slot(const Acc& acc, CountSlot* slot, uint32_t* lds) {
+  const uint32_t m = row_max_u32(acc.amax);
+  const uint32_t nf = row_sum_u32(acc.n_nf), big = row_sum_u32(acc.n_big), uf = row_sum_u32(acc.n_uf);
+  if ((threadIdx.x & 15) == 0) {
+    const int r = threadIdx.x >> 4;
+    lds[r * 4 + 0] = m;
+    lds[r * 4 + 1] = nf;
+    lds[r * 4 + 2] = big;
+    lds[r * 4 + 3] = uf;
   }
   __syncthreads();
   if (threadIdx.x == 0) {
-    uint32_t mx = 0;
-    uint64_t tnf = 0, tbig = 0, tuf = 0;
-    for (int w = 0; w < kWaves; ++w) {
-      mx = max(mx, lds_max[w]);
-      tnf += lds_cnt[w * 3 + 0];
-      tbig += lds_cnt[w * 3 + 1];
-      tuf += lds_cnt[w * 3 + 2];
+    CountSlot c{0u, 0u, 0u, 0u};
+    for (int r = 0; r < kRows; ++r) {
+      c.amax = max(c.amax, lds[r * 4 + 0]);
+      c.n_nf += lds[r * 4 + 1];
+      c.n_big += lds[r * 4 + 2];
+      c.n_uf += lds[r * 4 + 3];
     }
-    atomicMax(&out->amax_bits, unscale_bits(mx, unscale_log2));
-    if (n_elems - tnf) atomicAdd((unsigned long long*)&out->n_finite, (unsigned long long)(n_elems - tnf));
-    if (tnf) atomicAdd((unsigned long long*)&out->n_nonfinite, (unsigned long long)tnf);
-    if (tbig - tnf) atomicAdd((unsigned long long*)&out->n_clip, (unsigned long long)(tbig - tnf));
-    if (tuf) atomicAdd((unsigned long long*)&out->n_underflow, (unsigned long long)tuf);
+    *slot = c;
   }
-  __syncthreads();
-  acc.reset();
 }
 
 // ---------------------------------------------------------------------------
@@ -367,32 +408,15 @@ __device__ __forceinline__ uint32_t f32_to_bf16_rne(uint32_t b) {
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
-// 16-byte loads per lane per tile: read-only passes (amax, statistics) keep
-// four in flight, the casts eight (measured best on MI355X).
-constexpr int kUnrollRead = 4;
-constexpr int kUnrollCast = 8;
-
 // Streaming loads: every input byte is read once per pass, so the loads are
 // non-temporal (the cache lines are not kept for reuse).
 __device__ __forceinline__ u32x4 ld_stream(const u32x4* p) { return __builtin_nontemporal_load(p); }
+__device__ __forceinline__ u32x2 ld_stream(const u32x2* p) { return __builtin_nontemporal_load(p); }
 
-// Register double buffer: while a workgroup computes one tile, the loads of
-// its next tile in the grid-stride sequence are already in flight.  Loads
-// this lane's vectors of tile t into v when t is a full tile of TILE
-// elements of IN_BYTES bytes (from the codes when CODES, else from x);
-// returns t, or -1 when t is past the end or ragged.
-template <int IN_BYTES, int U, int64_t TILE, bool CODES = false>
-__device__ __forceinline__ int64_t prefetch_tile(const SegBatch& b, int64_t t, int hint, u32x4* v) {
-  if (t >= b.tile0[b.count]) return -1;
-  const int s = seg_of(b, t, hint);
-  if (tile_len<TILE>(b, s, t) != (int)TILE) return -1;
-  const int64_t e0 = (t - b.tile0[s]) * TILE;
-  const void* base = CODES ? static_cast<const void*>(b.s[s].codes) : b.s[s].x;
-  const u32x4* src = reinterpret_cast<const u32x4*>(static_cast<const uint8_t*>(base) + e0 * IN_BYTES);
-#pragma unroll
-  for (int u = 0; u < U; ++u) v[u] = ld_stream(src + u * kThreads + threadIdx.x);
-  return t;
-}
+// Code stores of the casts are streamed too (measured faster on MI355X for
+// these read-2/write-1 streams).
+__device__ __forceinline__ void st_stream(uint32_t* p, uint32_t v) { __builtin_nontemporal_store(v, p); }
+__device__ __forceinline__ void st_stream(u32x2* p, u32x2 v) { __builtin_nontemporal_store(v, p); }
 
 template <int DT> struct In;
 template <> struct In<NC_F32> { static constexpr int VEC = 4, BYTES = 4; };
@@ -422,8 +446,8 @@ __device__ __forceinline__ uint32_t load_one(const void* x, int64_t i) {
 // x, sums of e, |e|, e^2, sign(x) e, x e, x^2 with e = xhat - x, in binary64.
 // They are accumulated in the kernel's input domain (x as stored, xhat =
 // decode(q) * 2^-K with K = k - s); the loss-scale unscale multiplies x and
-// e by 2^-s, so the tile flush scales the first, second and fourth sums by
-// 2^-s and the others by 2^-2s -- exact power-of-two factors.
+// e by 2^-s, so the final reduction scales the first, second and fourth
+// sums by 2^-s and the others by 2^-2s -- exact power-of-two factors.
 struct StatAcc {
   double s[6];
   __device__ void reset() {
@@ -480,31 +504,22 @@ __device__ __forceinline__ void stats_vec(const uint32_t* xb, const uint32_t* q,
   }
 }
 
-// A workgroup's partial sums for one tensor -> part_slot[0..5], scaled back
-// by the unscale, in a fixed order (lanes by butterfly, then waves in index
-// order): deterministic.  Called when the workgroup leaves the tensor.
-__device__ inline void stats_seg_flush(StatAcc& a, double* part_slot, double* lds, int s_log2) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+// The workgroup's six partial sums -> its slot: DPP row sums, one LDS entry
+// per row, then thread j (< 6) adds the rows in index order -- a fixed
+// order, so the sums are reproducible.  Called by all threads (full EXEC);
+// lds holds kRows * 6 doubles.
+__device__ inline void write_stat_slot(const StatAcc& a, double* slot, double* lds) {
 #pragma unroll
   for (int j = 0; j < 6; ++j) {
-    const double v = wave_sum_f64(a.s[j]);
-    if (lane == 0) lds[wave * 6 + j] = v;
+    const double v = row_sum_f64(a.s[j]);
+    if ((threadIdx.x & 15) == 0) lds[(threadIdx.x >> 4) * 6 + j] = v;
   }
   __syncthreads();
   if (threadIdx.x < 6) {
     double t = 0.0;
-    for (int w = 0; w < kWaves; ++w) t += lds[w * 6 + threadIdx.x];
-    const int j = threadIdx.x;
-    const int sc = (j == 0 || j == 1 || j == 3) ? -s_log2 : -2 * s_log2;
-    part_slot[j] = ldexp(t, sc);
+    for (int r = 0; r < kRows; ++r) t += lds[r * 6 + threadIdx.x];
+    slot[threadIdx.x] = t;
   }
-  __syncthreads();
-  a.reset();
-}
-
-// Slot of (tensor s of the launch, workgroup g) in the statistics workspace.
-__device__ __forceinline__ double* stat_slot(double* part, int s, int g) {
-  return part + ((int64_t)s * kMaxGrid + g) * 6;
 }
 
 }  // namespace nc

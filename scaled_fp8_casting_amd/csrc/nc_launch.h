@@ -6,26 +6,68 @@
 
 namespace nc {
 
-// Elements per tile of a kernel that reads `in_bytes`-wide elements with
-// `unroll` 16-byte loads per thread (dequant reads codes: 256 * 16 * 2).
-inline int64_t tile_elems(int in_bytes, int unroll) { return (int64_t)kThreads * (16 / in_bytes) * unroll; }
-constexpr int64_t kDequantTile = (int64_t)kThreads * 16 * 2;
+// Elements per workgroup tile: 256 lanes x a few 16-byte input vectors --
+// two for the casts, four when they also form statistics, eight for the
+// statistics pass and four for the amax pass (read only: tile size does not
+// matter for bandwidth there, and larger tiles spread the per-workgroup
+// reductions over more elements); dequant: 256 lanes x 8 codes (one
+// 16-byte bf16 store per lane).
+constexpr int kCastVecs = 2;
+constexpr int kCastStatsVecs = 4;   // casts with fused statistics (more work per element)
+constexpr int kStatsVecs = 8;       // the statistics pass (read only)
+constexpr int kAmaxVecs = 4;
+template <bool STATS> constexpr int cast_vecs() { return STATS ? kCastStatsVecs : kCastVecs; }
+constexpr int64_t kDequantTile = (int64_t)kThreads * 8;
+inline int64_t tile_elems(int in_bytes, int vecs) { return (int64_t)kThreads * (16 / in_bytes) * vecs; }
+// smallest tile of any call that uses the workspace (fp32 cast / statistics)
+constexpr int64_t kMinWsTile = (int64_t)kThreads * 4 * kCastVecs;
+
+// Workspace of one launch: per-tile slots, then per-chunk slots.
+struct Ws {
+  CountSlot* cnt1;      // [tiles]
+  double* st1;          // [tiles][6]    (statistics only)
+  uint64_t* cnt2;       // [chunks][4]
+  double* st2;          // [chunks][6]   (statistics only)
+};
+
+// Byte size of the workspace a launch with `tiles` tiles and `chunks`
+// chunks needs (statistics included), and its layout inside `base`.
+inline size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
+inline size_t ws_bytes_for(int64_t tiles, int64_t chunks) {
+  return align256((size_t)tiles * sizeof(CountSlot)) + align256((size_t)tiles * 48) +
+         align256((size_t)chunks * 32) + align256((size_t)chunks * 48);
+}
+inline Ws ws_layout(void* base, int64_t tiles, int64_t chunks) {
+  uint8_t* p = static_cast<uint8_t*>(base);
+  Ws w;
+  w.cnt1 = reinterpret_cast<CountSlot*>(p);
+  p += align256((size_t)tiles * sizeof(CountSlot));
+  w.st1 = reinterpret_cast<double*>(p);
+  p += align256((size_t)tiles * 48);
+  w.cnt2 = reinterpret_cast<uint64_t*>(p);
+  p += align256((size_t)chunks * 32);
+  w.st2 = reinterpret_cast<double*>(p);
+  return w;
+}
 
 struct Launch {
-  int grid;            // workgroups
+  int64_t grid;        // workgroups (one per tile)
   hipStream_t stream;
 };
 
-hipError_t launch_amax(const SegBatch& b, int dtype, const nc_loss_scale* ls, nc_counts* out,
-                       const Launch& l);
+hipError_t launch_amax(const SegBatch& b, int dtype, const Ws& w, const Launch& l);
 hipError_t launch_cast_pt(const SegBatch& b, int dtype, int fmt, const nc_scale_state* st,
-                          const nc_loss_scale* ls, nc_counts* out, double* part, const Launch& l);
-hipError_t launch_cast_mx(const SegBatch& b, int dtype, int fmt, int rule, nc_counts* out,
-                          double* part, const Launch& l);
+                          const nc_loss_scale* ls, bool stats, const Ws& w, const Launch& l);
+hipError_t launch_cast_mx(const SegBatch& b, int dtype, int fmt, int rule, bool stats, const Ws& w,
+                          const Launch& l);
 hipError_t launch_stats(const SegBatch& b, int dtype, int fmt, const nc_scale_state* st,
-                        const nc_loss_scale* ls, double* part, const Launch& l);
-hipError_t launch_stats_finalize(const SegBatch& b, const double* part, int grid, nc_stats* out,
-                                 hipStream_t stream);
+                        const nc_loss_scale* ls, const Ws& w, const Launch& l);
+// The two reductions of a launch's slots into the caller's counts (nullable)
+// and statistics (nullable).  ls: unscale of the amax and of the statistics
+// (nullable; the MX calls pass none).  clips: the counts report clips (the
+// amax pass reports none).
+hipError_t launch_reduce(const SegBatch& b, const Ws& w, nc_counts* out, nc_stats* stats,
+                         const nc_loss_scale* ls, bool clips, hipStream_t stream);
 hipError_t launch_dequant(const SegBatch& b, int fmt, const nc_scale_state* st, const Launch& l);
 hipError_t launch_scale_update(const nc_policy& p, int32_t count, nc_scale_state* st, float* hist,
                                const nc_counts* in, nc_loss_scale* ls, hipStream_t stream);

@@ -60,32 +60,54 @@ def _desc(*specs):
     return arr
 
 
+def _ws_expect(sizes):
+    """Workspace bytes as the header documents them: per launch (at most 32
+    tensors), 16 + 48 bytes per tile of 2048 elements and 32 + 48 bytes per
+    chunk of 1024 tiles, each array rounded up to 256 bytes; the largest
+    launch counts."""
+    r = lambda v: (v + 255) // 256 * 256
+    best = 0
+    for i in range(0, len(sizes), 32):
+        tiles = [-(-n // 2048) for n in sizes[i:i + 32]]
+        T, C = sum(tiles), sum(-(-t // 1024) for t in tiles)
+        best = max(best, r(16 * T) + r(48 * T) + r(32 * C) + r(48 * C))
+    return best
+
+
 def test_argument_checks_before_any_launch(lib):
     A = 0x10000  # fake, aligned, never dereferenced: every call below fails its checks first
-    assert lib.nc_amax(None, -1, 0, None, None, None) == _lib.NC_E_ARG
-    assert lib.nc_amax(None, 1, 0, None, A, None) == _lib.NC_E_ARG
-    assert lib.nc_amax(_desc((A, None, 8, 0, None)), 1, 7, None, A, None) == _lib.NC_E_UNSUPPORTED
-    assert lib.nc_amax(_desc((A + 4, None, 8, 0, None)), 1, 0, None, A, None) == _lib.NC_E_ALIGN
-    assert lib.nc_amax(_desc((A, None, -1, 0, None)), 1, 0, None, A, None) == _lib.NC_E_ARG
-    assert lib.nc_amax(_desc((A, None, 8, 0, None)), 1, 0, None, None, None) == _lib.NC_E_ARG
+    W = 1 << 40  # a workspace size that passes the size check
+    assert lib.nc_amax(None, -1, 0, None, None, None, 0, None) == _lib.NC_E_ARG
+    assert lib.nc_amax(None, 1, 0, None, A, A, W, None) == _lib.NC_E_ARG
+    assert lib.nc_amax(_desc((A, None, 8, 0, None)), 1, 7, None, A, A, W, None) == _lib.NC_E_UNSUPPORTED
+    assert lib.nc_amax(_desc((A + 4, None, 8, 0, None)), 1, 0, None, A, A, W, None) == _lib.NC_E_ALIGN
+    assert lib.nc_amax(_desc((A, None, -1, 0, None)), 1, 0, None, A, A, W, None) == _lib.NC_E_ARG
+    assert lib.nc_amax(_desc((A, None, 8, 0, None)), 1, 0, None, None, A, W, None) == _lib.NC_E_ARG
+    assert lib.nc_amax(_desc((A, None, 8, 0, None)), 1, 0, None, A, None, W, None) == _lib.NC_E_WORKSPACE
+    assert lib.nc_amax(_desc((A, None, 8, 0, None)), 1, 0, None, A, A + 8, W, None) == _lib.NC_E_WORKSPACE
+    # one tensor above 2^34 elements cannot be launched
+    assert lib.nc_amax(_desc((A, None, (1 << 34) + 1, 0, None)), 1, 0, None, A, A, W, None) == _lib.NC_E_ARG
     # empty batches are valid no-ops
-    assert lib.nc_amax(None, 0, 0, None, None, None) == _lib.NC_OK
-    assert lib.nc_amax(_desc((None, None, 0, 0, None)), 1, 0, None, A, None) == _lib.NC_OK
+    assert lib.nc_amax(None, 0, 0, None, None, None, 0, None) == _lib.NC_OK
+    assert lib.nc_amax(_desc((None, None, 0, 0, None)), 1, 0, None, A, A, W, None) == _lib.NC_OK
     # MX shapes
     for cols, n in ((48, 96), (0, 64), (64, 96)):
-        assert lib.nc_cast_mx(_desc((A, A, n, cols, A)), 1, 1, 0, 0, A, None, None, 0, None) == _lib.NC_E_SHAPE
-    assert lib.nc_cast_mx(_desc((A, A, 64, 64, None)), 1, 1, 0, 0, A, None, None, 0, None) == _lib.NC_E_ARG
-    assert lib.nc_cast_mx(_desc((A, A, 64, 64, A)), 1, 1, 0, 9, A, None, None, 0, None) == _lib.NC_E_UNSUPPORTED
+        assert lib.nc_cast_mx(_desc((A, A, n, cols, A)), 1, 1, 0, 0, A, None, A, W, None) == _lib.NC_E_SHAPE
+    assert lib.nc_cast_mx(_desc((A, A, 64, 64, None)), 1, 1, 0, 0, A, None, A, W, None) == _lib.NC_E_ARG
+    assert lib.nc_cast_mx(_desc((A, A, 64, 64, A)), 1, 1, 0, 9, A, None, A, W, None) == _lib.NC_E_UNSUPPORTED
     # per-tensor cast
-    assert lib.nc_cast_tensor(_desc((A, A + 1, 8, 0, None)), 1, 0, 0, A, None, A, None, None, 0, None) == _lib.NC_E_ALIGN
-    assert lib.nc_cast_tensor(_desc((A, A, 8, 0, None)), 1, 0, 0, None, None, A, None, None, 0, None) == _lib.NC_E_ARG
-    assert lib.nc_cast_tensor(_desc((A, A, 8, 0, None)), 1, 0, 2, A, None, A, None, None, 0, None) == _lib.NC_E_UNSUPPORTED
-    # statistics need a large enough workspace
+    assert lib.nc_cast_tensor(_desc((A, A + 1, 8, 0, None)), 1, 0, 0, A, None, A, None, A, W, None) == _lib.NC_E_ALIGN
+    assert lib.nc_cast_tensor(_desc((A, A, 8, 0, None)), 1, 0, 0, None, None, A, None, A, W, None) == _lib.NC_E_ARG
+    assert lib.nc_cast_tensor(_desc((A, A, 8, 0, None)), 1, 0, 2, A, None, A, None, A, W, None) == _lib.NC_E_UNSUPPORTED
+    # workspace size
     d = _desc((A, A, 10000, 0, None))
     need = lib.nc_workspace_bytes(d, 1)
-    assert need == 1 * 4096 * 6 * 8
-    assert lib.nc_workspace_bytes(_desc(*[(A, A, 10, 0, None)] * 40), 40) == 32 * 4096 * 6 * 8
+    assert need == _ws_expect([10000]) == 1024
+    sizes = [10] * 40 + [(1 << 22) + 5, 0, 3 * 2048 * 1024]
+    assert lib.nc_workspace_bytes(_desc(*[(A, A, n, 0, None) for n in sizes]), len(sizes)) == _ws_expect(sizes)
+    assert lib.nc_workspace_bytes(None, 0) == 0
     assert lib.nc_cast_tensor(d, 1, 0, 0, A, None, A, A, A, need - 8, None) == _lib.NC_E_WORKSPACE
+    assert lib.nc_cast_tensor(d, 1, 0, 0, A, None, A, None, A, need - 8, None) == _lib.NC_E_WORKSPACE
     assert lib.nc_cast_stats(d, 1, 0, 0, A, None, A, None, 0, None) == _lib.NC_E_WORKSPACE
     # dequant writes bf16 only
     assert lib.nc_dequant(d, 1, 0, A, None, 0, None) == _lib.NC_E_UNSUPPORTED

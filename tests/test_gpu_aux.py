@@ -211,3 +211,44 @@ def test_stats_batch_of_many_tensors():
         wc = bulk.cast_f64(E5M2, x.astype(np.float64), ks[i])[0]
         assert np.array_equal(host_u8(codes[i]), wc)
         stats_close(got[i], bulk.stats_f64(E5M2, x.astype(np.float64), wc, ks[i]))
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_stats_and_counts_over_many_chunks(dtype):
+    """A tensor of more than 1024 workgroup tiles (several chunks in the
+    first reduction) plus a tiny one in the same launch: codes, counts and
+    both statistics paths against the oracle."""
+    rng = np.random.default_rng(8)
+    n_big = 3 * 1024 * 2048 + 1234
+    xs, x64s = [], []
+    for n in (n_big, 100):
+        x = (rng.standard_t(4, n) * 10.0 ** rng.uniform(-2, 2, n)).astype(np.float32)
+        x[::100003] = np.inf
+        if dtype == "bf16":
+            bits = workloads.to_bf16_bits(x.astype(np.float64))
+            xs.append(dev_bf16(bits))
+            x64s.append(bulk.bf16_bits_to_f64(bits))
+        else:
+            xs.append(dev_f32(x))
+            x64s.append(x.astype(np.float64))
+    ks = [5, -3]
+    codes = [codes_like(x.numel()) for x in xs]
+    out, fused, sep = nc.new_counts(2), nc.new_stats(2), nc.new_stats(2)
+    st = state_with_k(ks)
+    nc.nc_cast_tensor(xs, codes, "e4m3", st, out, stats=fused)
+    nc.nc_cast_stats(xs, codes, "e4m3", sep, st=st)
+    am = nc.new_counts(2)
+    nc.nc_amax(xs, am)
+    torch.cuda.synchronize()
+    got = nc.counts_list(out)
+    got_am = nc.counts_list(am)
+    for i, x64 in enumerate(x64s):
+        wc, want = bulk.cast_tensor_f64(E4M3, x64, ks[i])
+        assert np.array_equal(host_u8(codes[i]), wc), i
+        for f in ("n_finite", "n_clip", "n_underflow", "n_nonfinite", "amax"):
+            assert got[i][f] == want[f], (i, f, got[i][f], want[f])
+        assert got_am[i]["amax"] == want["amax"] and got_am[i]["n_nonfinite"] == want["n_nonfinite"]
+        assert got_am[i]["n_clip"] == 0
+        ws_ = bulk.stats_f64(E4M3, x64, wc, ks[i])
+        stats_close(fused[i].cpu().tolist(), ws_)
+        stats_close(sep[i].cpu().tolist(), ws_)
