@@ -176,47 +176,94 @@ k_dequant(const SegBatch b, const nc_scale_state* __restrict__ st) {
 
 // ---------------------------------------------------------------------------
 // Statistics as a separate pass over x and the codes (and the MX scales).
+
+// Vector vi of a full tile: its elements, their codes and (MX) the block's 2^X.
+// Codes of vector vi of a tile (VEC per 16-byte input vector).
+template <int DT>
+struct CodeVec;
+template <> struct CodeVec<NC_F32> {
+  typedef uint32_t T;
+  __device__ static T load(const uint8_t* cs, int vi) {
+    return __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(cs) + vi);
+  }
+  __device__ static void split(T w, uint32_t* q) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) q[i] = (w >> (8 * i)) & 0xFFu;
+  }
+};
+template <> struct CodeVec<NC_BF16> {
+  typedef u32x2 T;
+  __device__ static T load(const uint8_t* cs, int vi) { return ld_stream(reinterpret_cast<const u32x2*>(cs) + vi); }
+  __device__ static void split(T w, uint32_t* q) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) q[i] = (w.x >> (8 * i)) & 0xFFu;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) q[4 + i] = (w.y >> (8 * i)) & 0xFFu;
+  }
+};
+
 template <int FMT, int DT, bool MX>
 NC_STREAM_KERNEL
 k_stats(const SegBatch b, const nc_scale_state* __restrict__ st,
         const nc_loss_scale* __restrict__ ls, double* __restrict__ stat_slots) {
   constexpr int VEC = In<DT>::VEC;
-  constexpr int64_t TILE = (int64_t)kThreads * VEC * kStatsVecs;
+  constexpr int U = kStatsVecs;
+  constexpr int64_t TILE = (int64_t)kThreads * VEC * U;
+  typedef typename CodeVec<DT>::T CT;
   __shared__ double tab[256];
   __shared__ double lds_st[kRows * 6];
   const int64_t tile = blockIdx.x;
   const int s = seg_of(b.tile0, b.count, tile);
-  if constexpr (MX) fill_stat_table<FMT>(tab, 0);
-  else fill_stat_table<FMT>(tab, st[b.first + s].k - (ls ? ls->s_log2 : 0));
-  __syncthreads();
   const Seg& g = b.s[s];
   const int64_t e0 = (tile - b.tile0[s]) * TILE;
   const int rem = tile_len<TILE>(b, s, tile);
   const uint8_t* cs = g.codes + e0;
+  const u32x4* src = reinterpret_cast<const u32x4*>(static_cast<const uint8_t*>(g.x) + e0 * In<DT>::BYTES);
+  const bool full = rem == (int)TILE;
+  // a full tile's loads go out first; the table fill overlaps them
+  u32x4 v[U];
+  CT c[U];
+  uint32_t sc[MX ? U : 1];
+  if (full) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) v[u] = ld_stream(src + u * kThreads + threadIdx.x);
+#pragma unroll
+    for (int u = 0; u < U; ++u) c[u] = CodeVec<DT>::load(cs, u * kThreads + threadIdx.x);
+    if constexpr (MX) {
+#pragma unroll
+      for (int u = 0; u < U; ++u) sc[u] = g.scales[(e0 + (int64_t)(u * kThreads + threadIdx.x) * VEC) / 32];
+    }
+  }
+  __builtin_amdgcn_sched_barrier(0);
+  if constexpr (MX) fill_stat_table<FMT>(tab, 0);
+  else fill_stat_table<FMT>(tab, st[b.first + s].k - (ls ? ls->s_log2 : 0));
+  __syncthreads();
   StatAcc sa;
   sa.reset();
-  if (rem == (int)TILE) {
-    const u32x4* src = reinterpret_cast<const u32x4*>(static_cast<const uint8_t*>(g.x) + e0 * In<DT>::BYTES);
-    u32x4 v[kStatsVecs];
+  if (full) {
+    // every element unmasked; a lane that met an Inf/NaN starts over with
+    // the masked form (rare)
 #pragma unroll
-    for (int u = 0; u < kStatsVecs; ++u) v[u] = ld_stream(src + u * kThreads + threadIdx.x);
-#pragma unroll
-    for (int u = 0; u < kStatsVecs; ++u) {
-      const int vi = u * kThreads + threadIdx.x;
+    for (int u = 0; u < U; ++u) {
       uint32_t xb[VEC], q[VEC];
       unpack<DT>(v[u], xb);
-      if constexpr (DT == NC_F32) {
-        const uint32_t w = reinterpret_cast<const uint32_t*>(cs)[vi];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) q[i] = (w >> (8 * i)) & 0xFFu;
-      } else {
-        const uint64_t w = reinterpret_cast<const uint64_t*>(cs)[vi];
-#pragma unroll
-        for (int i = 0; i < 8; ++i) q[i] = (uint32_t)(w >> (8 * i)) & 0xFFu;
-      }
+      CodeVec<DT>::split(c[u], q);
       double blk = 1.0;
-      if constexpr (MX) blk = pow2_f64((int)g.scales[(e0 + (int64_t)vi * VEC) / 32] - 127);
-      stats_vec<VEC, MX>(xb, q, tab, blk, sa);
+      if constexpr (MX) blk = pow2_f64((int)sc[u] - 127);
+      stats_vec<VEC, MX, true>(xb, q, tab, blk, sa);
+      __builtin_amdgcn_sched_barrier(0);   // one vector's table reads at a time (register pressure)
+    }
+    if (!stats_all_finite(sa)) {
+      sa.reset();
+      for (int u = 0; u < U; ++u) {       // reloads: the vectors above are not kept
+        const int vi = u * kThreads + threadIdx.x;
+        uint32_t xb[VEC], q[VEC];
+        unpack<DT>(src[vi], xb);
+        CodeVec<DT>::split(CodeVec<DT>::load(cs, vi), q);
+        double blk = 1.0;
+        if constexpr (MX) blk = pow2_f64((int)g.scales[(e0 + (int64_t)vi * VEC) / 32] - 127);
+        stats_vec<VEC, MX, false>(xb, q, tab, blk, sa);
+      }
     }
   } else {
     for (int i = threadIdx.x; i < rem; i += kThreads) {
@@ -224,7 +271,7 @@ k_stats(const SegBatch b, const nc_scale_state* __restrict__ st,
       const uint32_t q = cs[i];
       double blk = 1.0;
       if constexpr (MX) blk = pow2_f64((int)g.scales[(e0 + i) / 32] - 127);
-      stats_vec<1, MX>(&xb, &q, tab, blk, sa);
+      stats_vec<1, MX, false>(&xb, &q, tab, blk, sa);
     }
   }
   write_stat_slot(sa, stat_slots + tile * 6, lds_st);

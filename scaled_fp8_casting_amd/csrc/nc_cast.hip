@@ -33,6 +33,7 @@ k_amax(const SegBatch b, CountSlot* __restrict__ slots) {
     u32x4 v[kAmaxVecs];
 #pragma unroll
     for (int u = 0; u < kAmaxVecs; ++u) v[u] = ld_stream(src + u * kThreads + threadIdx.x);
+    __builtin_amdgcn_sched_barrier(0);   // all loads in flight before any use
 #pragma unroll
     for (int u = 0; u < kAmaxVecs; ++u) {
       uint32_t xb[VEC];
@@ -65,6 +66,15 @@ k_cast_pt(const SegBatch b, const nc_scale_state* __restrict__ st,
   const Seg& g = b.s[s];
   const int64_t e0 = (tile - b.tile0[s]) * TILE;
   const int rem = tile_len<TILE>(b, s, tile);
+  const bool full = rem == (int)TILE;
+  const u32x4* src = reinterpret_cast<const u32x4*>(static_cast<const uint8_t*>(g.x) + e0 * In<DT>::BYTES);
+  // a full tile's loads go out first; the scale and table set-up overlap them
+  u32x4 v[U];
+  if (full) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) v[u] = ld_stream(src + u * kThreads + threadIdx.x);
+  }
+  __builtin_amdgcn_sched_barrier(0);
   const int K = st[b.first + s].k - (ls ? ls->s_log2 : 0);
   const CastParams p = cast_params<FMT>(K);
   if constexpr (STATS) {
@@ -76,25 +86,23 @@ k_cast_pt(const SegBatch b, const nc_scale_state* __restrict__ st,
   StatAcc sa;
   if constexpr (STATS) sa.reset();
   uint8_t* dst = g.codes + e0;
-  if (rem == (int)TILE) {
-    const u32x4* src = reinterpret_cast<const u32x4*>(static_cast<const uint8_t*>(g.x) + e0 * In<DT>::BYTES);
-    u32x4 v[U];
-#pragma unroll
-    for (int u = 0; u < U; ++u) v[u] = ld_stream(src + u * kThreads + threadIdx.x);
+  if (full) {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       uint32_t xb[VEC], w[VEC / 4];
       unpack<DT>(v[u], xb);
-      cast_vec<FMT, VEC>(xb, p, acc, w);
+      const bool clean = cast_vec<FMT, VEC>(xb, p, acc, w);
       if constexpr (STATS) {
         uint32_t q[VEC];
 #pragma unroll
         for (int i = 0; i < VEC; ++i) q[i] = (w[i / 4] >> (8 * (i % 4))) & 0xFFu;
-        stats_vec<VEC, false>(xb, q, tab, 1.0, sa);
+        if (clean) stats_vec<VEC, false, true>(xb, q, tab, 1.0, sa);
+        else stats_vec<VEC, false, false>(xb, q, tab, 1.0, sa);
       }
       const int vi = u * kThreads + threadIdx.x;
       if constexpr (DT == NC_F32) st_stream(reinterpret_cast<uint32_t*>(dst) + vi, w[0]);
       else st_stream(reinterpret_cast<u32x2*>(dst) + vi, u32x2{w[0], w[1]});
+      if constexpr (STATS) __builtin_amdgcn_sched_barrier(0);   // one vector at a time (register pressure)
     }
   } else {
     for (int base = 0; base < rem; base += kThreads) {
@@ -102,7 +110,7 @@ k_cast_pt(const SegBatch b, const nc_scale_state* __restrict__ st,
       const bool act = i < rem;
       const uint32_t xb = act ? load_one<DT>(g.x, e0 + i) : 0u;
       const uint32_t q = cast_one<FMT>(xb, p, acc);
-      if constexpr (STATS) stats_vec<1, false>(&xb, &q, tab, 1.0, sa);
+      if constexpr (STATS) stats_vec<1, false, false>(&xb, &q, tab, 1.0, sa);
       if (act) dst[i] = (uint8_t)q;
     }
   }
@@ -182,7 +190,8 @@ __device__ __forceinline__ void mx_tile(const Seg& g, int64_t e0, int rem, const
       uint32_t q[VEC];
 #pragma unroll
       for (int i = 0; i < VEC; ++i) q[i] = (w[i / 4] >> (8 * (i % 4))) & 0xFFu;
-      stats_vec<VEC, true>(xb, q, tab, pow2_f64(X), sa);
+      if (clean) stats_vec<VEC, true, true>(xb, q, tab, pow2_f64(X), sa);
+      else stats_vec<VEC, true, false>(xb, q, tab, pow2_f64(X), sa);
     }
     if (FULL || vi * VEC < rem) {
       if constexpr (DT == NC_F32) st_stream(reinterpret_cast<uint32_t*>(dst) + vi, w[0]);
@@ -204,33 +213,32 @@ k_cast_mx(const SegBatch b, CountSlot* __restrict__ slots, double* __restrict__ 
   __shared__ uint32_t lds[kRows * 4];
   __shared__ double lds_st[STATS ? kRows * 6 : 1];
   __shared__ double tab[STATS ? 256 : 1];
-  if constexpr (STATS) {
-    fill_stat_table<FMT>(tab, 0);
-    __syncthreads();
-  }
   const int64_t tile = blockIdx.x;
   const int s = seg_of(b.tile0, b.count, tile);
   const Seg& g = b.s[s];
   const int64_t e0 = (tile - b.tile0[s]) * TILE;
   const int rem = tile_len<TILE>(b, s, tile);      // a multiple of 32
+  const u32x4* src = reinterpret_cast<const u32x4*>(static_cast<const uint8_t*>(g.x) + e0 * In<DT>::BYTES);
+  // loads first (a ragged tile: lanes past the end hold zeros); the table
+  // fill overlaps them
+  u32x4 v[U];
+  const bool full = rem == (int)TILE;
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    const int vi = u * kThreads + threadIdx.x;
+    v[u] = (full || vi * VEC < rem) ? ld_stream(src + vi) : u32x4{0u, 0u, 0u, 0u};
+  }
+  __builtin_amdgcn_sched_barrier(0);
+  if constexpr (STATS) {
+    fill_stat_table<FMT>(tab, 0);
+    __syncthreads();
+  }
   Acc acc;
   acc.reset();
   StatAcc sa;
   if constexpr (STATS) sa.reset();
-  const u32x4* src = reinterpret_cast<const u32x4*>(static_cast<const uint8_t*>(g.x) + e0 * In<DT>::BYTES);
-  u32x4 v[U];
-  if (rem == (int)TILE) {
-#pragma unroll
-    for (int u = 0; u < U; ++u) v[u] = ld_stream(src + u * kThreads + threadIdx.x);
-    mx_tile<FMT, DT, RULE, STATS, true, U>(g, e0, rem, v, acc, sa, tab);
-  } else {
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int vi = u * kThreads + threadIdx.x;
-      v[u] = (vi * VEC < rem) ? ld_stream(src + vi) : u32x4{0u, 0u, 0u, 0u};
-    }
-    mx_tile<FMT, DT, RULE, STATS, false, U>(g, e0, rem, v, acc, sa, tab);
-  }
+  if (full) mx_tile<FMT, DT, RULE, STATS, true, U>(g, e0, rem, v, acc, sa, tab);
+  else mx_tile<FMT, DT, RULE, STATS, false, U>(g, e0, rem, v, acc, sa, tab);
   write_count_slot(acc, slots + tile, lds);
   if constexpr (STATS) write_stat_slot(sa, stat_slots + tile * 6, lds_st);
 }

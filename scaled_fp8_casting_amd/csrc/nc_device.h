@@ -195,8 +195,9 @@ __device__ __forceinline__ void count_elem(uint32_t ax, const CastParams& p, Acc
 
 // Cast VEC elements (a multiple of 4) at one exponent into VEC/4 packed
 // words; counts and the finite amax go to acc.
+// Returns the wave-uniform "no Inf/NaN in this vector anywhere in the wave".
 template <int FMT, int VEC>
-__device__ __forceinline__ void cast_vec(const uint32_t* xb, const CastParams& p, Acc& acc,
+__device__ __forceinline__ bool cast_vec(const uint32_t* xb, const CastParams& p, Acc& acc,
                                          uint32_t* w) {
   uint32_t ax[VEC];
   uint32_t m = 0;
@@ -211,14 +212,15 @@ __device__ __forceinline__ void cast_vec(const uint32_t* xb, const CastParams& p
   for (int i = 0; i < VEC; ++i) count_elem(ax[i], p, acc);
   if (__ballot(m > kMaxFinite) == 0) {        // wave-uniform: no Inf/NaN here
     acc.amax = max(acc.amax, m);
-  } else {
-    uint32_t mf = 0;
-#pragma unroll
-    for (int i = 0; i < VEC; ++i) mf = max(mf, finite_mag(ax[i], acc));
-    acc.amax = max(acc.amax, mf);
-#pragma unroll
-    for (int j = 0; j < VEC / 4; ++j) w[j] = fix_nonfinite4<FMT>(w[j], xb + 4 * j);
+    return true;
   }
+  uint32_t mf = 0;
+#pragma unroll
+  for (int i = 0; i < VEC; ++i) mf = max(mf, finite_mag(ax[i], acc));
+  acc.amax = max(acc.amax, mf);
+#pragma unroll
+  for (int j = 0; j < VEC / 4; ++j) w[j] = fix_nonfinite4<FMT>(w[j], xb + 4 * j);
+  return false;
 }
 
 // One element (ragged tails): its code; counts and amax to acc.
@@ -480,28 +482,24 @@ __device__ __forceinline__ void stat_term(double x, double xh, StatAcc& a) {
 }
 
 // Terms of VEC elements (fp32 patterns xb, codes q); xhat = tab[q] (* blk
-// for MX, the block's 2^X).  A vector whose wave holds no Inf/NaN takes the
-// unmasked path (a wave-uniform branch).
-template <int VEC, bool MX>
+// for MX, the block's 2^X).  FINITE: the caller knows every x is finite (no
+// test); otherwise Inf/NaN elements are skipped.
+template <int VEC, bool MX, bool FINITE>
 __device__ __forceinline__ void stats_vec(const uint32_t* xb, const uint32_t* q, const double* tab,
                                           double blk, StatAcc& a) {
-  uint32_t m = 0;
 #pragma unroll
-  for (int i = 0; i < VEC; ++i) m = max(m, xb[i] & kAbsMask);
-  if (__ballot(m > kMaxFinite) == 0) {
-#pragma unroll
-    for (int i = 0; i < VEC; ++i) {
-      const double xh = MX ? tab[q[i]] * blk : tab[q[i]];
-      stat_term((double)__uint_as_float(xb[i]), xh, a);
-    }
-  } else {
-#pragma unroll
-    for (int i = 0; i < VEC; ++i) {
-      if ((xb[i] & kAbsMask) > kMaxFinite) continue;
-      const double xh = MX ? tab[q[i]] * blk : tab[q[i]];
-      stat_term((double)__uint_as_float(xb[i]), xh, a);
-    }
+  for (int i = 0; i < VEC; ++i) {
+    if (!FINITE && (xb[i] & kAbsMask) > kMaxFinite) continue;
+    const double xh = MX ? tab[q[i]] * blk : tab[q[i]];
+    stat_term((double)__uint_as_float(xb[i]), xh, a);
   }
+}
+
+// After unmasked accumulation: was every x finite?  A finite fp32 x has
+// x^2 <= 2^256, so the binary64 sum of x^2 over a tile stays finite; an
+// Inf/NaN x makes it Inf/NaN.
+__device__ __forceinline__ bool stats_all_finite(const StatAcc& a) {
+  return __builtin_isfinite(a.s[5]);
 }
 
 // The workgroup's six partial sums -> its slot: DPP row sums, one LDS entry
