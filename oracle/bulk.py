@@ -105,6 +105,34 @@ def cast_tensor_f64(fmt: Fmt, x: np.ndarray, k: int, unscale_log2: int = 0):
     return codes, counts_of(clip, uf, nf, amax_f64(x, unscale_log2), x.size)
 
 
+def counts_threshold(fmt: Fmt, x: np.ndarray, K, chunk: int = 1 << 22):
+    """The counts of ``cast_f64`` without forming codes, for large tensors:
+    clip <=> finite and |x| 2^K > max (the clip reading, on the exact
+    product); underflow <=> finite, nonzero and |x| 2^K <= half the smallest
+    subnormal (round to nearest even sends exactly that interval, its upper
+    end a tie with even code 0, to zero); non-finite <=> Inf or NaN.  Also
+    the finite amax (binary64).  K: an int, or an array like x.  Processed
+    in chunks so that a tensor of 2^30 elements needs little memory."""
+    c = fmt_consts(fmt)
+    x = np.asarray(x).ravel()
+    Ka = np.asarray(K)
+    half_sub = 2.0 ** (c["emin"] - c["mbits"] - 1)
+    n_clip = n_uf = n_nf = 0
+    amax = 0.0
+    for i in range(0, x.size, chunk):
+        xc = np.asarray(x[i:i + chunk], dtype=np.float64)
+        Kc = Ka if Ka.ndim == 0 else np.asarray(Ka.ravel()[i:i + chunk], dtype=np.int64)
+        fin = np.isfinite(xc)
+        ax = np.where(fin, np.abs(xc), 0.0)
+        y = np.ldexp(ax, Kc)                           # exact
+        n_clip += int(np.count_nonzero(y > c["M"]))
+        n_uf += int(np.count_nonzero((ax > 0) & (y <= half_sub)))
+        n_nf += int(np.count_nonzero(~fin))
+        if ax.size:
+            amax = max(amax, float(ax.max()))
+    return dict(n_finite=x.size - n_nf, n_clip=n_clip, n_underflow=n_uf, n_nonfinite=n_nf, amax=amax)
+
+
 # -- MX -----------------------------------------------------------------------
 
 def mx_exponents(fmt: Fmt, x: np.ndarray, rule: str) -> np.ndarray:

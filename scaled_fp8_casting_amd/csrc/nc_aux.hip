@@ -136,7 +136,7 @@ __device__ __forceinline__ uint32_t nan_bytes(uint32_t w) {
 template <int FMT, bool MX>
 NC_STREAM_KERNEL
 k_dequant(const SegBatch b, const nc_scale_state* __restrict__ st) {
-  constexpr int64_t TILE = kDequantTile;      // 8 codes per lane
+  constexpr int64_t TILE = kDequantTile;      // 8 codes per lane per vector
   const int64_t tile = blockIdx.x;
   const int s = seg_of(b.tile0, b.count, tile);
   const Seg& g = b.s[s];
@@ -145,25 +145,34 @@ k_dequant(const SegBatch b, const nc_scale_state* __restrict__ st) {
   const uint8_t* src = g.codes + e0;
   uint16_t* dst = static_cast<uint16_t*>(g.y) + e0;
   if (rem == (int)TILE) {
-    const u32x2 c = ld_stream(reinterpret_cast<const u32x2*>(src) + threadIdx.x);
-    int sh;                                   // the value is decode(q) * 2^sh
-    if constexpr (MX) sh = (int)g.scales[(e0 + (int64_t)threadIdx.x * 8) / 32] - 127;   // X
-    else sh = -st[b.first + s].k;
-    u32x4 o;
-    o.x = bf16_pair(decode_pair<FMT, false>(c.x), sh);
-    o.y = bf16_pair(decode_pair<FMT, true>(c.x), sh);
-    o.z = bf16_pair(decode_pair<FMT, false>(c.y), sh);
-    o.w = bf16_pair(decode_pair<FMT, true>(c.y), sh);
-    const uint32_t nb0 = nan_bytes<FMT>(c.x), nb1 = nan_bytes<FMT>(c.y);
-    if (__ballot((nb0 | nb1) != 0) != 0) {    // wave-uniform, rare
-      uint32_t h[8] = {o.x & 0xFFFFu, o.x >> 16, o.y & 0xFFFFu, o.y >> 16,
-                       o.z & 0xFFFFu, o.z >> 16, o.w & 0xFFFFu, o.w >> 16};
+    constexpr int U = kDequantVecs;
+    u32x2 c[U];
 #pragma unroll
-      for (int i = 0; i < 8; ++i)
-        if (((i < 4 ? nb0 : nb1) >> (8 * (i % 4) + 7)) & 1u) h[i] = 0x7FC0u;
-      o = u32x4{h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16), h[6] | (h[7] << 16)};
+    for (int u = 0; u < U; ++u) c[u] = ld_stream(reinterpret_cast<const u32x2*>(src) + u * kThreads + threadIdx.x);
+    int sh[U];                                // the value is decode(q) * 2^sh
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      if constexpr (MX) sh[u] = (int)g.scales[(e0 + (int64_t)(u * kThreads + threadIdx.x) * 8) / 32] - 127;   // X
+      else sh[u] = -st[b.first + s].k;
     }
-    reinterpret_cast<u32x4*>(dst)[threadIdx.x] = o;
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      u32x4 o;
+      o.x = bf16_pair(decode_pair<FMT, false>(c[u].x), sh[u]);
+      o.y = bf16_pair(decode_pair<FMT, true>(c[u].x), sh[u]);
+      o.z = bf16_pair(decode_pair<FMT, false>(c[u].y), sh[u]);
+      o.w = bf16_pair(decode_pair<FMT, true>(c[u].y), sh[u]);
+      const uint32_t nb0 = nan_bytes<FMT>(c[u].x), nb1 = nan_bytes<FMT>(c[u].y);
+      if (__ballot((nb0 | nb1) != 0) != 0) {    // wave-uniform, rare
+        uint32_t h[8] = {o.x & 0xFFFFu, o.x >> 16, o.y & 0xFFFFu, o.y >> 16,
+                         o.z & 0xFFFFu, o.z >> 16, o.w & 0xFFFFu, o.w >> 16};
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+          if (((i < 4 ? nb0 : nb1) >> (8 * (i % 4) + 7)) & 1u) h[i] = 0x7FC0u;
+        o = u32x4{h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16), h[6] | (h[7] << 16)};
+      }
+      reinterpret_cast<u32x4*>(dst)[u * kThreads + threadIdx.x] = o;
+    }
   } else {
     const int k = MX ? 0 : st[b.first + s].k;
     for (int i = threadIdx.x; i < rem; i += kThreads) {

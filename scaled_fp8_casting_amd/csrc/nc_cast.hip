@@ -38,8 +38,15 @@ k_amax(const SegBatch b, CountSlot* __restrict__ slots) {
     for (int u = 0; u < kAmaxVecs; ++u) {
       uint32_t xb[VEC];
       unpack<DT>(v[u], xb);
+      uint32_t m = 0;
 #pragma unroll
-      for (int i = 0; i < VEC; ++i) acc.amax = max(acc.amax, finite_mag(xb[i] & kAbsMask, acc));
+      for (int i = 0; i < VEC; ++i) m = max(m, xb[i] & kAbsMask);
+      if (__ballot(m > kMaxFinite) == 0) {     // wave-uniform: no Inf/NaN in this vector
+        acc.amax = max(acc.amax, m);
+      } else {
+#pragma unroll
+        for (int i = 0; i < VEC; ++i) acc.amax = max(acc.amax, finite_mag(xb[i] & kAbsMask, acc));
+      }
     }
   } else {
     for (int i = threadIdx.x; i < rem; i += kThreads)

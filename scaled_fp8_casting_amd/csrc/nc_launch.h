@@ -10,14 +10,15 @@ namespace nc {
 // two for the casts, four when they also form statistics, eight for the
 // statistics pass and four for the amax pass (read only: tile size does not
 // matter for bandwidth there, and larger tiles spread the per-workgroup
-// reductions over more elements); dequant: 256 lanes x 8 codes (one
-// 16-byte bf16 store per lane).
+// reductions over more elements); dequant: 256 lanes x two vectors of 8
+// codes (a 16-byte bf16 store each).  Measured best on MI355X.
 constexpr int kCastVecs = 2;
 constexpr int kCastStatsVecs = 4;   // casts with fused statistics (more work per element)
 constexpr int kStatsVecs = 8;       // the statistics pass (read only)
 constexpr int kAmaxVecs = 4;
 template <bool STATS> constexpr int cast_vecs() { return STATS ? kCastStatsVecs : kCastVecs; }
-constexpr int64_t kDequantTile = (int64_t)kThreads * 8;
+constexpr int kDequantVecs = 2;
+constexpr int64_t kDequantTile = (int64_t)kThreads * 8 * kDequantVecs;
 inline int64_t tile_elems(int in_bytes, int vecs) { return (int64_t)kThreads * (16 / in_bytes) * vecs; }
 // smallest tile of any call that uses the workspace (fp32 cast / statistics)
 constexpr int64_t kMinWsTile = (int64_t)kThreads * 4 * kCastVecs;

@@ -1,0 +1,259 @@
+"""GPU parity on the full workloads, in the launch configurations the
+benchmark and a training step use:
+
+* the 2^30 heavy-tailed bf16 tensor through the benchmark's step (amax,
+  current scaling, per-tensor E4M3, MXFP8 E4M3 OCP, both dequants, both
+  statistics passes): every code, scale byte, dequantised value, count and
+  statistic checked against the oracle -- per-tensor codes through a lookup
+  table over the 65,536 bf16 patterns built by the oracle's element cast,
+  MX codes through one such table per block exponent present, statistics
+  exactly from histograms of (pattern, exponent);
+* 64 gradient tensors (2^12 .. 2^22 elements) over 32 steps with delayed
+  scaling, E5M2, most-recent and 16-step-window estimators with
+  hysteresis: every scale, amax and count at every step, codes on a sample;
+* loss-scaled Llama-shaped fp32 gradients (one decoder layer plus the
+  embedding, 333M elements) over 1024 steps: fused 2^-16 unscale, Inf/NaN
+  injection, 16-step window -- the scale state machine replayed on every
+  step, counts and codes checked on sampled steps.
+"""
+
+import os
+from fractions import Fraction
+
+import numpy as np
+import pytest
+import torch
+
+import scaled_fp8_casting_amd as nc
+import workloads
+from oracle import E4M3, E5M2, bulk
+from oracle.cast import scale_exponent
+from oracle.policy import EST_CURRENT, EST_MAX_WINDOW, EST_MOST_RECENT, Policy, ScaleState, update
+from tests._gpu import host_u8, host_u16, stats_close
+
+pytestmark = pytest.mark.gpu
+
+COLS = 4096
+
+
+def _procs():
+    return max(1, min(16, os.cpu_count() or 1))
+
+
+def _f32(bits: int) -> float:
+    return float(np.array([bits], dtype=np.uint32).view(np.float32)[0])
+
+
+# -- the 2^30 heavy-tailed tensor ------------------------------------------------
+
+def test_heavy_tailed_full_size():
+    rows = 262144
+    n = rows * COLS
+    bits = workloads.heavy_tailed_parallel(rows, COLS, procs=_procs(), context="spawn").reshape(-1)
+    x = torch.from_numpy(bits.view(np.int16)).cuda().view(torch.bfloat16)
+    codes_pt = torch.empty(n, dtype=torch.uint8, device="cuda")
+    codes_mx = torch.empty(n, dtype=torch.uint8, device="cuda")
+    scales = torch.empty(n // 32, dtype=torch.uint8, device="cuda")
+    y_pt = torch.empty(n, dtype=torch.bfloat16, device="cuda")
+    y_mx = torch.empty(n, dtype=torch.bfloat16, device="cuda")
+    desc, cnt = nc.tensors([x], [codes_pt])
+    ws = nc.new_workspace(desc, cnt)
+    am, cpt, cmx = nc.new_counts(1), nc.new_counts(1), nc.new_counts(1)
+    spt, smx, fpt, fmx = (nc.new_stats(1) for _ in range(4))
+    st = nc.new_state(1)
+    nc.nc_amax([x], am, ws=ws)
+    nc.nc_scale_update(nc.policy("e4m3", "current", hysteresis=False), st, am)
+    nc.nc_cast_tensor([x], [codes_pt], "e4m3", st, cpt, ws=ws)
+    nc.nc_cast_mx([x], [codes_mx], [scales], [COLS], "e4m3", "ocp", cmx, ws=ws)
+    nc.nc_dequant([codes_pt], [y_pt], "e4m3", st=st)
+    nc.nc_dequant([codes_mx], [y_mx], "e4m3", scales=[scales], cols=[COLS])
+    nc.nc_cast_stats([x], [codes_pt], "e4m3", spt, ws, st=st)
+    nc.nc_cast_stats([x], [codes_mx], "e4m3", smx, ws, scales=[scales], cols=[COLS])
+    # the casts with statistics fused: same codes and counts as without
+    fused_c, fused_cm = nc.new_counts(1), nc.new_counts(1)
+    fused_codes = torch.empty_like(codes_pt)
+    nc.nc_cast_tensor([x], [fused_codes], "e4m3", st, fused_c, stats=fpt, ws=ws)
+    assert torch.equal(fused_codes, codes_pt) and torch.equal(fused_c, cpt)
+    fused_scales = torch.empty_like(scales)
+    nc.nc_cast_mx([x], [fused_codes], [fused_scales], [COLS], "e4m3", "ocp", fused_cm, stats=fmx, ws=ws)
+    assert torch.equal(fused_codes, codes_mx) and torch.equal(fused_scales, scales) and torch.equal(fused_cm, cmx)
+    del fused_codes
+    torch.cuda.synchronize()
+
+    # amax, scale, per-tensor counts
+    vals = bulk.bf16_bits_to_f64(np.arange(65536, dtype=np.uint16))          # every bf16 pattern
+    hist = np.bincount(bits, minlength=65536)
+    present = hist > 0
+    fin = np.isfinite(vals)
+    amax = float(np.max(np.abs(vals[present & fin])))
+    got_am = nc.counts_list(am)[0]
+    assert got_am["amax"] == amax and got_am["n_nonfinite"] == int(hist[~fin].sum())
+    k = scale_exponent(E4M3, Fraction(amax))
+    assert int(st[0, 0]) == k
+    lut, clip, uf, nf = bulk.cast_f64(E4M3, vals, k)                        # code of every pattern
+    want = dict(n_finite=int(hist[fin].sum()), n_clip=int(hist[clip].sum()),
+                n_underflow=int(hist[uf].sum()), n_nonfinite=int(hist[nf].sum()))
+    got = nc.counts_list(cpt)[0]
+    for f, v in want.items():
+        assert got[f] == v, (f, got[f], v)
+    assert got["amax"] == amax
+
+    # every per-tensor code and dequantised value
+    gc = host_u8(codes_pt)
+    assert np.array_equal(gc, lut[bits])
+    dq = bulk.dequant_bf16_f64(E4M3, np.arange(256, dtype=np.uint8), k)
+    assert np.array_equal(host_u16(y_pt), dq[gc])
+    del gc
+
+    # MX: block exponents, then a code table per exponent present
+    X = np.empty(n // 32, dtype=np.int64)
+    step = 1 << 24
+    for i in range(0, n, step):
+        X[i // 32:(i + step) // 32] = bulk.mx_exponents(E4M3, vals[bits[i:i + step]], "ocp")
+    gs = host_u8(scales)
+    assert np.array_equal(gs, (X + 127).astype(np.uint8))
+    xs = np.unique(X)
+    tab = np.stack([bulk.cast_f64(E4M3, vals, int(-v))[0] for v in xs])    # [exponent, pattern] -> code
+    clip_tab = np.stack([bulk.cast_f64(E4M3, vals, int(-v))[1] for v in xs])
+    xi = np.searchsorted(xs, X)
+    dq_mx = np.stack([bulk.dequant_bf16_f64(E4M3, np.arange(256, dtype=np.uint8), int(-v)) for v in xs])
+    gm = host_u8(codes_mx)
+    gy = host_u16(y_mx)
+    n_clip_mx = 0
+    key = np.zeros(xs.size * 65536, dtype=np.int64)
+    for i in range(0, n, step):                 # one pass per chunk: codes, clips, dequant, histogram
+        bi = np.repeat(xi[i // 32:(i + step) // 32], 32)
+        bc = bits[i:i + step]
+        assert np.array_equal(gm[i:i + step], tab[bi, bc]), i
+        n_clip_mx += int(clip_tab[bi, bc].sum())
+        assert np.array_equal(gy[i:i + step], dq_mx[bi, gm[i:i + step]]), i
+        key += np.bincount(bi * 65536 + bc, minlength=key.size)
+    del gy, gm
+    gotm = nc.counts_list(cmx)[0]
+    assert gotm["n_clip"] == n_clip_mx and gotm["n_finite"] == want["n_finite"] and gotm["amax"] == amax
+
+    # statistics, exactly, from histograms
+    want_pt = bulk.stats_from_histogram(E4M3, vals, lut, k, hist)
+    stats_close(spt[0].cpu().tolist(), want_pt)
+    stats_close(fpt[0].cpu().tolist(), want_pt)
+    want_mx = bulk.stats_from_histogram(E4M3, np.tile(vals, xs.size), tab.reshape(-1),
+                                        np.repeat(-xs, 65536), key)
+    stats_close(smx[0].cpu().tolist(), want_mx)
+    stats_close(fmx[0].cpu().tolist(), want_mx)
+
+
+# -- gradient steps: delayed scaling ------------------------------------------------
+
+@pytest.mark.parametrize("est", [EST_MOST_RECENT, EST_MAX_WINDOW])
+def test_gradient_steps_delayed_scaling(est):
+    W = 16
+    gen = workloads.GradientSteps()
+    T = len(gen.sizes)
+    pol_o = Policy(fmt=E5M2, est=est, window=W, hysteresis=True)
+    pol_cur = Policy(fmt=E5M2, est=EST_CURRENT, window=W, hysteresis=True)
+    pol_d = nc.policy("e5m2", est, W, hysteresis=True)
+    sts = [ScaleState() for _ in range(T)]
+    st = nc.new_state(T)
+    hist = nc.new_history(T, W)
+    codes = [torch.empty(m, dtype=torch.uint8, device="cuda") for m in gen.sizes]
+    rng = np.random.default_rng(7)
+    past = [[] for _ in range(T)]
+    for t in range(gen.steps):
+        xs = gen.step(t)
+        xd = [torch.from_numpy(x).cuda() for x in xs]
+        desc, cnt = nc.tensors(xd, codes)
+        ws = nc.new_workspace(desc, cnt)
+        if t == 0:                               # empty history: current scaling
+            am = nc.new_counts(T)
+            nc.nc_amax(xd, am, ws=ws)
+            nc.nc_scale_update(nc.policy("e5m2", "current", W, hysteresis=True), st, am)
+            update(pol_cur, sts, [Fraction(float(np.max(np.abs(x)))) for x in xs], [0] * T)
+        ks = [s.k for s in sts]
+        assert st[:, 0].cpu().tolist() == ks, t
+        out = nc.new_counts(T)
+        nc.nc_cast_tensor(xd, codes, "e5m2", st, out, ws=ws)
+        nc.nc_scale_update(pol_d, st, out, hist)
+        torch.cuda.synchronize()
+        got = nc.counts_list(out)
+        amaxes = []
+        for i, x in enumerate(xs):
+            want = bulk.counts_threshold(E5M2, x, ks[i])
+            for f in ("n_finite", "n_clip", "n_underflow", "n_nonfinite"):
+                assert got[i][f] == want[f], (t, i, f)
+            assert got[i]["amax"] == want["amax"]
+            idx = rng.integers(0, x.size, min(x.size, 2048))
+            assert np.array_equal(host_u8(codes[i])[idx], bulk.cast_f64(E5M2, x[idx].astype(np.float64), ks[i])[0])
+            # the window guarantee: an amax within the window never clips
+            if est == EST_MAX_WINDOW and past[i] and want["amax"] <= max(past[i][-W:]):
+                assert got[i]["n_clip"] == 0, (t, i)
+            past[i].append(want["amax"])
+            amaxes.append(Fraction(want["amax"]))
+        update(pol_o, sts, amaxes, [0] * T)
+    gs = st.cpu().numpy()
+    assert np.array_equal(gs[:, 0], [s.k for s in sts])
+    assert np.array_equal(gs[:, 1].view(np.uint32),
+                          [int(np.array([float(s.a_ref)], np.float32).view(np.uint32)[0]) for s in sts])
+
+
+# -- loss-scaled Llama-shaped gradients -----------------------------------------
+
+def test_llama_shaped_unscale_cast_1024_steps():
+    steps, W = 1024, 16
+    sampled = {0, 1, 2, 511, 1023}
+    g = workloads.LlamaGrads(layers=1)
+    T = len(g.sizes)
+    s_log2 = g.S_LOG2
+    ls = nc.new_loss_scale(s_log2)
+    st = nc.new_state(T)
+    hist = nc.new_history(T, W)
+    codes = [torch.empty(m, dtype=torch.uint8, device="cuda") for m in g.sizes]
+    desc, cnt = nc.tensors(g.bufs, codes)
+    ws = nc.new_workspace(desc, cnt)
+    pol_d = nc.policy("e4m3", "max_window", W, hysteresis=True)
+    all_counts = torch.zeros((steps, T, 5), dtype=torch.int64, device="cuda")
+    all_k = torch.zeros((steps, T), dtype=torch.int32, device="cuda")
+    rng = np.random.default_rng(11)
+    checks = {}
+    for t in range(steps):
+        tens, _, _ = g.fill(t)
+        if t == 0:
+            am = nc.new_counts(T)
+            nc.nc_amax(g.bufs, am, ls=ls, ws=ws)
+            nc.nc_scale_update(nc.policy("e4m3", "current", W, hysteresis=True), st, am)
+            am0 = am.clone()
+        all_k[t] = st[:, 0]
+        nc.nc_cast_tensor(g.bufs, codes, "e4m3", st, all_counts[t], ls=ls, ws=ws)
+        nc.nc_scale_update(pol_d, st, all_counts[t], hist)
+        if t in sampled:
+            torch.cuda.synchronize()
+            k_t = all_k[t].cpu().tolist()
+            xs = [b.cpu().numpy() for b in g.bufs]
+            want = [bulk.counts_threshold(E4M3, x, k_t[i] - s_log2) for i, x in enumerate(xs)]
+            for i, x in enumerate(xs):
+                idx = rng.integers(0, x.size, 1 << 16)
+                wc = bulk.cast_f64(E4M3, x[idx].astype(np.float64), k_t[i] - s_log2)[0]
+                assert np.array_equal(host_u8(codes[i])[idx], wc), (t, i)
+            checks[t] = (want, np.bincount(tens, minlength=T))
+            del xs
+    torch.cuda.synchronize()
+    counts = all_counts.cpu().numpy()
+    ks = all_k.cpu().numpy()
+    # sampled steps: every count and the unscaled amax, exactly
+    for t, (want, n_inj) in checks.items():
+        for i in range(T):
+            c = counts[t, i]
+            assert (c[0], c[1], c[2], c[3]) == (want[i]["n_finite"], want[i]["n_clip"],
+                                               want[i]["n_underflow"], want[i]["n_nonfinite"]), (t, i)
+            assert c[3] == n_inj[i]
+            assert _f32(int(c[4]) & 0xFFFFFFFF) == float(np.float32(np.ldexp(want[i]["amax"], -s_log2))), (t, i)
+    # every step: the state machine replayed from the amaxes and flags
+    pol_o = Policy(fmt=E4M3, est=EST_MAX_WINDOW, window=W, hysteresis=True)
+    sts = [ScaleState() for _ in range(T)]
+    assert np.array_equal(am0[:, 4].cpu().numpy(), counts[0, :, 4])     # amax pass == cast's amax
+    a0 = [Fraction(_f32(int(v) & 0xFFFFFFFF)) for v in am0[:, 4].cpu().tolist()]
+    update(Policy(fmt=E4M3, est=EST_CURRENT, window=W, hysteresis=True), sts, a0, [0] * T)
+    for t in range(steps):
+        assert list(ks[t]) == [s.k for s in sts], t
+        amaxes = [Fraction(_f32(int(v) & 0xFFFFFFFF)) for v in counts[t, :, 4]]
+        update(pol_o, sts, amaxes, list(counts[t, :, 3]))
+    assert st[:, 0].cpu().tolist() == [s.k for s in sts]

@@ -152,3 +152,31 @@ def test_amax_with_unscale():
     random.seed(1)
     assert bulk.amax_f64(np.array([np.nan, np.inf])) == 0.0
     assert t0.count_nonfinite([Val.of(math.nan), Val.of(1.0)]) == 1
+
+
+@pytest.mark.parametrize("fmt", [E4M3, E5M2], ids=["e4m3", "e5m2"])
+def test_counts_threshold_agrees_with_the_element_cast(fmt):
+    """counts_threshold (interval tests) against the counts of cast_f64
+    (codes formed element by element): random values across the whole fp32
+    range, values at and next to both decision points at several K, Inf and
+    NaN, and a per-element K array; chunk boundaries inside the input."""
+    rng = np.random.default_rng(41)
+    x = (rng.standard_normal(30000) * 10.0 ** rng.uniform(-40, 38, 30000)).astype(np.float32).astype(np.float64)
+    edges = []
+    for K in (-20, -3, 0, 5, 30):
+        M = float(fmt.maxval)
+        hs = 2.0 ** (fmt.emin - fmt.mbits - 1)
+        for v in (M, hs):
+            b = np.float32(np.ldexp(v, -K))
+            edges += [float(b), float(np.nextafter(b, np.float32(np.inf))), float(np.nextafter(b, np.float32(0)))]
+    x = np.concatenate([x, edges, [-e for e in edges], [np.inf, -np.inf, np.nan, 0.0, -0.0]])
+    for K in (-20, -3, 0, 5, 30):
+        _, clip, uf, nf = bulk.cast_f64(fmt, x, K)
+        got = bulk.counts_threshold(fmt, x, K, chunk=4097)
+        assert got["n_clip"] == int(clip.sum()) and got["n_underflow"] == int(uf.sum())
+        assert got["n_nonfinite"] == int(nf.sum()) and got["n_finite"] == x.size - int(nf.sum())
+        assert got["amax"] == float(np.max(np.abs(x[np.isfinite(x)])))
+    Ks = rng.integers(-30, 30, x.size)
+    _, clip, uf, nf = bulk.cast_f64(fmt, x, Ks)
+    got = bulk.counts_threshold(fmt, x, Ks, chunk=1000)
+    assert (got["n_clip"], got["n_underflow"]) == (int(clip.sum()), int(uf.sum()))

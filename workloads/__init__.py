@@ -19,6 +19,12 @@ Workloads (standard deviations are the second argument of N(0, s)):
 * ``heavy_tailed_rows``: 2^30 bf16 values, 262,144 rows of 4096, row r =
   10^(v_r) * t_3 with v_r ~ U(-3, 3) ([E3, "Worked solution"]: one global
   scale cannot serve a layer a thousand times smaller).  Seed 105.
+* ``LlamaGrads``: fp32 gradients shaped like a 7B decoder (per layer four
+  4096x4096 and three 4096x11008 tensors, plus a 32000x4096 embedding), S *
+  N(0, 1e-6) with S = 2^16 (loss-scaled, [MP-card, item (1)]), drawn on the
+  device from a seeded generator each step; 1e-7 of all elements are then
+  set to +Inf or NaN (even odds) at positions drawn on the host from seed
+  104 and the step.
 """
 
 import numpy as np
@@ -106,9 +112,11 @@ def _ht_chunk(args):
 
 
 def heavy_tailed_parallel(nrows: int = 262144, cols: int = 4096, seed: int = 105,
-                          procs: int = 8, chunk_rows: int = 1024) -> np.ndarray:
+                          procs: int = 8, chunk_rows: int = 1024, context: str = "fork") -> np.ndarray:
     """``heavy_tailed_rows(0, nrows)`` generated by a process pool (same
-    values: each chunk has its own child seed)."""
+    values: each chunk has its own child seed).  context: the
+    multiprocessing start method ("spawn" from a process that already uses
+    the GPU)."""
     import multiprocessing as mp
     assert nrows % chunk_rows == 0, "nrows must be a multiple of chunk_rows"
     out = np.empty((nrows, cols), dtype=np.uint16)
@@ -118,7 +126,52 @@ def heavy_tailed_parallel(nrows: int = 262144, cols: int = 4096, seed: int = 105
             r, a = _ht_chunk(j)
             out[r:r + chunk_rows] = a
         return out
-    with mp.get_context("fork").Pool(procs) as pool:
+    with mp.get_context(context).Pool(procs) as pool:
         for r, a in pool.imap_unordered(_ht_chunk, jobs):
             out[r:r + chunk_rows] = a
     return out
+
+
+class LlamaGrads:
+    """Device-resident loss-scaled gradients of a Llama-7B-shaped model (see
+    the module docstring).  ``layers`` scales the model down for tests; the
+    embedding is always included.  ``fill(t)`` overwrites the buffers with
+    step t's values and returns the injected positions as (tensor, offset,
+    is_nan) arrays."""
+
+    S_LOG2 = 16
+    SIGMA = 1e-6
+
+    def __init__(self, layers: int = 32, seed: int = 104, device: str = "cuda"):
+        shapes = []
+        for _ in range(layers):
+            shapes += [(4096, 4096)] * 4 + [(4096, 11008)] * 3
+        shapes.append((32000, 4096))
+        self.shapes = shapes
+        self.sizes = [r * c for r, c in shapes]
+        self.starts = np.concatenate([[0], np.cumsum(self.sizes)])
+        self.total = int(self.starts[-1])
+        self.seed = seed
+        self.device = device
+        self.bufs = [torch.empty(n, dtype=torch.float32, device=device) for n in self.sizes]
+        self.n_inject = int(round(1e-7 * self.total))
+
+    def fill(self, t: int):
+        g = torch.Generator(device=self.device)
+        g.manual_seed(self.seed * 1000003 + t)
+        std = float(2 ** self.S_LOG2) * self.SIGMA
+        for b in self.bufs:
+            b.normal_(0.0, std, generator=g)
+        rng = np.random.default_rng([self.seed, t])
+        pos = np.unique(rng.integers(0, self.total, self.n_inject))
+        while pos.size < self.n_inject:
+            pos = np.unique(np.concatenate([pos, rng.integers(0, self.total, self.n_inject - pos.size)]))
+        is_nan = rng.integers(0, 2, pos.size).astype(bool)
+        tensor = np.searchsorted(self.starts, pos, side="right") - 1
+        offset = pos - self.starts[tensor]
+        for i in np.unique(tensor):
+            m = tensor == i
+            idx = torch.from_numpy(offset[m]).to(self.device)
+            val = torch.from_numpy(np.where(is_nan[m], np.nan, np.inf).astype(np.float32)).to(self.device)
+            self.bufs[i].index_copy_(0, idx, val)
+        return tensor, offset, is_nan
