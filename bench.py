@@ -16,6 +16,11 @@ timed region.  One step is one pass of the whole cast path over it:
   7. nc_cast_stats    error/bias statistics, per-tensor         (2 + 1)
   8. nc_cast_stats    error/bias statistics, MX                 (2 + 1 + 1/32)
 
+Beside the step (not part of it) the same JSON line reports the casts with
+fused statistics, a plain device copy of the cast's byte count, and one
+delayed-scaling step of loss-scaled Llama-7B-shaped fp32 gradients (225
+tensors, 6.6G elements, fused 2^-16 unscale).
+
 Prints one JSON line.  `value` is elements per second through the whole step
 (Gelem/s); `roofline` is the dominant kernel's algorithmic bytes per launch
 over its mean launch time (HIP events on the launch stream, inside the timed
@@ -44,6 +49,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--rows", type=int, default=262144, help="rows of 4096 (default 2^30 elements)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--no-llama", action="store_true",
+                    help="skip the Llama-shaped unscale+cast measured beside the step")
     ap.add_argument("--cpu-rows", type=int, default=4096,
                     help="rows of the workload the CPU oracle baseline runs on")
     ap.add_argument("--copy-probe", action="store_true",
@@ -180,6 +187,44 @@ def _cpu_step(args):
     bulk.stats_f64(E4M3, x, c_pt, k)
     bulk.stats_f64(E4M3, x, c_mx, K_mx)
     return int(np.count_nonzero(clip))
+
+
+def llama_unscale_cast(nc, torch, workloads):
+    """Loss-scaled fp32 gradients of a Llama-7B-shaped model (225 tensors,
+    6,607,077,376 elements, S = 2^16, 1e-7 of them Inf/NaN): one delayed-
+    scaling step, i.e. a single nc_cast_tensor call over all tensors with the
+    2^-16 unscale fused (scales from a current-scaling pass, untimed)."""
+    g = workloads.LlamaGrads(layers=32)
+    g.fill(0)
+    T = len(g.bufs)
+    codes = [torch.empty(m, dtype=torch.uint8, device="cuda") for m in g.sizes]
+    desc, cnt = nc.tensors(g.bufs, codes)
+    ws = nc.new_workspace(desc, cnt)
+    ls = nc.new_loss_scale(g.S_LOG2)
+    st = nc.new_state(T)
+    am = nc.new_counts(T)
+    nc.nc_amax(g.bufs, am, ls=ls, ws=ws)
+    nc.nc_scale_update(nc.policy("e4m3", "current", hysteresis=False), st, am)
+    out = nc.new_counts(T)
+    fn = lambda: nc.nc_cast_tensor(g.bufs, codes, "e4m3", st, out, ls=ls, ws=ws)
+    fn()
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(5)]
+    for e0, e1 in ev:
+        e0.record()
+        fn()
+        e1.record()
+    torch.cuda.synchronize()
+    ms = float(np.mean([e0.elapsed_time(e1) for e0, e1 in ev]))
+    n = g.total
+    nbytes = 5 * n
+    gbps = nbytes / (ms * 1e-3) / 1e9
+    nonfinite = int(sum(c["n_nonfinite"] for c in nc.counts_list(out))) // (len(ev) + 1)
+    del g, codes, ws
+    torch.cuda.empty_cache()
+    return dict(ms=round(ms, 4), gbps=round(gbps, 1), frac=round(gbps / HBM_PEAK_GBPS, 4),
+                gelem_s=round(n / (ms * 1e-3) / 1e9, 2), elements=n, tensors=T,
+                nonfinite_per_step=nonfinite)
 
 
 def main():
@@ -336,6 +381,8 @@ def main():
         out["beside_step"][nm] = dict(ms=round(ms, 4), gbps=round(gbps, 1), frac=round(gbps / HBM_PEAK_GBPS, 4),
                                       gelem_s=round(n / (ms * 1e-3) / 1e9, 2))
     extras.clear()
+    if not a.no_llama:
+        out["beside_step"]["llama_unscale_cast"] = llama_unscale_cast(nc, torch, workloads)
     if a.copy_probe:
         src_b = torch.empty(1 << 30, dtype=torch.uint8, device=dev).fill_(1)
         dst_b = torch.empty_like(src_b)

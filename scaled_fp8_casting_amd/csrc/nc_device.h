@@ -314,12 +314,16 @@ struct SegBatch {
 static_assert(sizeof(SegBatch) <= 4096, "a SegBatch travels as a kernel argument");
 
 // Tensor owning entry `i` of a prefix array (tile0 or chunk0): the last s
-// with start[s] <= i.  Wave-uniform, at most kMaxSeg steps, once per
-// workgroup.
+// with start[s] <= i, i.e. the number of s' in [1, count) with start[s'] <=
+// i (start is non-decreasing).  Lane l tests start[l + 1] and the wave
+// counts the hits: one load per lane instead of a chain of up to 31
+// dependent scalar loads.  A one-tensor launch loads nothing.  Called by
+// whole waves; the result is wave-uniform.
 __device__ __forceinline__ int seg_of(const int64_t* start, int count, int64_t i) {
-  int s = 0;
-  while (s + 1 < count && i >= start[s + 1]) ++s;
-  return s;
+  if (count == 1) return 0;
+  const int l = threadIdx.x & 63;
+  const bool hit = l + 1 < count && i >= start[l + 1];
+  return __builtin_amdgcn_readfirstlane(__popcll(__ballot(hit)));
 }
 
 // Elements in tile t of tensor s: TILE, except in the tensor's last tile.
