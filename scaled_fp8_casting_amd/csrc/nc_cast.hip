@@ -165,6 +165,9 @@ __device__ __forceinline__ void mx_tile(const Seg& g, int64_t e0, int rem, const
   constexpr int GROUP = 32 / VEC;
   uint8_t* dst = g.codes + e0;
   uint8_t* sdst = g.scales + e0 / 32;
+  // the scales may be stored a row's worth at a time (4 bytes for bf16, 2
+  // for fp32) when their array is aligned for it (wave-uniform)
+  const bool sc_word = ((uintptr_t)g.scales & (GROUP == 4 ? 3u : 1u)) == 0;
 #pragma unroll
   for (int u = 0; u < U; ++u) {
     const int vi = u * kThreads + threadIdx.x;
@@ -203,9 +206,23 @@ __device__ __forceinline__ void mx_tile(const Seg& g, int64_t e0, int rem, const
     if (FULL || vi * VEC < rem) {
       if constexpr (DT == NC_F32) st_stream(reinterpret_cast<uint32_t*>(dst) + vi, w[0]);
       else st_stream(reinterpret_cast<u32x2*>(dst) + vi, u32x2{w[0], w[1]});
-      // every lane of the block holds the same X: all store it (same byte,
-      // same value), which keeps the tile free of divergent branches
-      sdst[vi / GROUP] = (uint8_t)(X + 127);
+      const uint32_t sb = (uint32_t)(X + 127);
+      if (FULL && sc_word) {
+        // a 16-lane row holds 16 / GROUP whole blocks: DPP row shifts gather
+        // their scale bytes into the row's first lane, which stores them
+        // as one word (vi is a multiple of 16 there)
+        if constexpr (GROUP == 4) {
+          const uint32_t b4 = sb | (dpp_u32<0x104>(sb) << 8) | (dpp_u32<0x108>(sb) << 16) | (dpp_u32<0x10C>(sb) << 24);
+          if ((threadIdx.x & 15) == 0) reinterpret_cast<uint32_t*>(sdst)[vi / 16] = b4;
+        } else {
+          const uint32_t b2 = sb | (dpp_u32<0x108>(sb) << 8);
+          if ((threadIdx.x & 15) == 0) reinterpret_cast<uint16_t*>(sdst)[vi / 16] = (uint16_t)b2;
+        }
+      } else {
+        // every lane of the block holds the same X: all store it (same byte,
+        // same value), which keeps the tile free of divergent branches
+        sdst[vi / GROUP] = (uint8_t)sb;
+      }
     }
     __builtin_amdgcn_sched_barrier(0);   // keep each vector's ballots short-lived
   }

@@ -312,3 +312,30 @@ def test_no_writes_past_the_end(dtype):
         for (big, _), m in zip(bufs, lens):
             tail = big[m:].cpu().numpy()
             assert np.all(tail == fill), (name, m, int(np.argmax(tail != fill)))
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_mx_scales_at_any_alignment(dtype):
+    """Scale bytes are written a row's worth at a time when the scale array is
+    aligned for it, byte by byte otherwise: both give the same bytes (scale
+    arrays at offsets 0..3 of an allocation), and nothing around them
+    changes."""
+    rows, cols = 96, 4096
+    x = _mx_input(rows, cols, 17)
+    if dtype == "bf16":
+        bits = workloads.to_bf16_bits(x.astype(np.float64))
+        xd, x64 = dev_bf16(bits), bulk.bf16_bits_to_f64(bits)
+    else:
+        xd, x64 = dev_f32(x), x.astype(np.float64)
+    n = rows * cols
+    wc, wsc, _ = bulk.cast_mx_f64(E4M3, x64, cols, "ocp")
+    for off in range(4):
+        big = torch.full((n // 32 + 8,), 0xA5, dtype=torch.uint8, device="cuda")
+        sc = big[off:off + n // 32]
+        codes = codes_like(n)
+        nc.nc_cast_mx([xd], [codes], [sc], [cols], "e4m3", "ocp", nc.new_counts(1))
+        torch.cuda.synchronize()
+        assert np.array_equal(host_u8(codes), wc), off
+        b = host_u8(big)
+        assert np.array_equal(b[off:off + n // 32], wsc), off
+        assert np.all(b[:off] == 0xA5) and np.all(b[off + n // 32:] == 0xA5), off
