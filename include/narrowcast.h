@@ -75,8 +75,11 @@ typedef enum { NC_MX_OCP = 0, NC_MX_PLUS1 = 1, NC_MX_CEIL = 2 } nc_mx_rule;
 /* amax estimators ([MaxWin, "Experimental Variables"]): CURRENT uses the
  * amax passed in for this step (the two-pass "current scaling");
  * MOST_RECENT the last amax pushed into the history; MAX_WINDOW the largest
- * of the last `window` pushes. */
-typedef enum { NC_EST_CURRENT = 0, NC_EST_MOST_RECENT = 1, NC_EST_MAX_WINDOW = 2 } nc_est;
+ * of the last `window` pushes; EMA exponential smoothing, E <- E + alpha *
+ * (a - E) with each of the three operations rounded to fp32 (nearest even,
+ * no fused multiply-add), E = a at the first push.  EMA keeps E in slot 0
+ * of the tensor's history (window >= 1). */
+typedef enum { NC_EST_CURRENT = 0, NC_EST_MOST_RECENT = 1, NC_EST_MAX_WINDOW = 2, NC_EST_EMA = 3 } nc_est;
 
 /* One tensor of a batch (host array of these). */
 typedef struct {
@@ -143,6 +146,7 @@ typedef struct {
   int32_t ls_growth_interval; /* clean steps before S doubles, >= 1 */
   int32_t ls_log2_min;        /* bounds on s_log2, 0 <= min <= max <= 64 */
   int32_t ls_log2_max;
+  float ema_alpha;            /* EMA smoothing coefficient, 0 < alpha <= 1 (other estimators ignore it) */
 } nc_policy;
 
 /* Per-tensor amax pass ("a pass over the tensor", [E3, "Worked solution"];

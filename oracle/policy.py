@@ -12,7 +12,10 @@ What the pages fix:
 * [MaxWin, "Experimental Variables"]: the estimators -- most recent (the
   previous step's amax), a maximum over a window of recent steps (64 there),
   exponential smoothing, and current scaling (this step's own amax, which
-  needs a second look at the data).  [MaxWin, "Key Contributions"]: the
+  needs a second look at the data).  The smoothing coefficient and the
+  arithmetic are not given; read here as E <- E + alpha (a - E) in fp32 with
+  each operation rounded to nearest even (no fused multiply-add), E = a at
+  the first push.  [MaxWin, "Key Contributions"]: the
   window maximum guarantees no scale-induced saturation for a step whose amax
   is within the window.  A warmup fills the history before quantisation.
 * [MP-card, item (1)]: dynamic loss scaling halves S and skips the step on an
@@ -53,9 +56,9 @@ from fractions import Fraction
 from typing import List
 
 from .cast import scale_exponent
-from .formats import Fmt, pow2
+from .formats import FP32, Fmt, pow2
 
-EST_CURRENT, EST_MOST_RECENT, EST_MAX_WINDOW = "current", "most_recent", "max_window"
+EST_CURRENT, EST_MOST_RECENT, EST_MAX_WINDOW, EST_EMA = "current", "most_recent", "max_window", "ema"
 
 
 @dataclass
@@ -71,6 +74,7 @@ class Policy:
     ls_growth_interval: int = 2000
     ls_log2_min: int = 0
     ls_log2_max: int = 24
+    ema_alpha: Fraction = Fraction(1, 16)     # an fp32 value in (0, 1]
 
 
 @dataclass
@@ -103,6 +107,21 @@ def set_scale(policy: Policy, st: ScaleState, a: Fraction) -> None:
         reset = False
     if reset:
         st.k, st.a_ref, st.has_ref = k_new, a, True
+
+
+def _rn32(v: Fraction) -> Fraction:
+    """v rounded to the nearest fp32 value (ties to even; symmetric in sign)."""
+    m = FP32.round_mag(abs(v))
+    return -m if v < 0 else m
+
+
+def ema_step(alpha: Fraction, e: Fraction, a: Fraction) -> Fraction:
+    """Exponential smoothing ([MaxWin, "Experimental Variables"]) read with a
+    defined fp32 operation order: d = rn(a - e), m = rn(alpha * d), result
+    rn(e + m) -- three roundings, none fused."""
+    d = _rn32(a - e)
+    m = _rn32(alpha * d)
+    return _rn32(e + m)
 
 
 def estimate(policy: Policy, st: ScaleState) -> Fraction:
@@ -138,6 +157,16 @@ def update(policy: Policy, states: List[ScaleState], amaxes: List[Fraction],
     if policy.skip_on_nonfinite and any_nf:
         return
     W = policy.window
+    if policy.est == EST_EMA:
+        # the smoothed estimate E is the whole history: E = a at the first
+        # push, then E <- ema_step(alpha, E, a)
+        for st, a in zip(states, amaxes):
+            a = Fraction(a)
+            st.hist = [ema_step(policy.ema_alpha, st.hist[0], a) if st.hist else a]
+            st.step += 1
+            if st.step % policy.interval == 0:
+                set_scale(policy, st, st.hist[0])
+        return
     for st, a in zip(states, amaxes):
         st.hist.append(Fraction(a))
         if len(st.hist) > W:

@@ -23,7 +23,7 @@ from typing import Optional, Sequence
 import torch
 
 from . import _lib
-from ._lib import (NC_BF16, NC_E4M3, NC_E5M2, NC_EST_CURRENT, NC_EST_MAX_WINDOW,  # noqa: F401
+from ._lib import (NC_BF16, NC_E4M3, NC_E5M2, NC_EST_CURRENT, NC_EST_EMA, NC_EST_MAX_WINDOW,  # noqa: F401
                    NC_EST_MOST_RECENT, NC_F32, NC_MX_CEIL, NC_MX_OCP, NC_MX_PLUS1, NcPolicy,
                    NcTensor)
 
@@ -33,7 +33,8 @@ STATE_FIELDS = ("k", "a_ref_bits", "has_ref", "n_hist", "head", "step")
 
 FMT = {"e4m3": NC_E4M3, "e5m2": NC_E5M2}
 MX_RULE = {"ocp": NC_MX_OCP, "plus1": NC_MX_PLUS1, "ceil": NC_MX_CEIL}
-EST = {"current": NC_EST_CURRENT, "most_recent": NC_EST_MOST_RECENT, "max_window": NC_EST_MAX_WINDOW}
+EST = {"current": NC_EST_CURRENT, "most_recent": NC_EST_MOST_RECENT, "max_window": NC_EST_MAX_WINDOW,
+       "ema": NC_EST_EMA}
 
 
 class NarrowcastError(RuntimeError):
@@ -114,10 +115,10 @@ def new_loss_scale(s_log2: int, device="cuda") -> torch.Tensor:
 
 def policy(fmt="e4m3", est="max_window", window=16, margin=0, hysteresis=True, interval=1,
            skip_on_nonfinite=False, ls_enable=False, ls_growth_interval=2000, ls_log2_min=0,
-           ls_log2_max=24) -> NcPolicy:
+           ls_log2_max=24, ema_alpha=0.0625) -> NcPolicy:
     return NcPolicy(FMT[fmt] if isinstance(fmt, str) else fmt, EST[est] if isinstance(est, str) else est,
                     window, margin, int(hysteresis), interval, int(skip_on_nonfinite), int(ls_enable),
-                    ls_growth_interval, ls_log2_min, ls_log2_max)
+                    ls_growth_interval, ls_log2_min, ls_log2_max, ema_alpha)
 
 
 def counts_list(counts: torch.Tensor):

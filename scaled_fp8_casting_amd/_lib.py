@@ -15,7 +15,7 @@ NC_OK, NC_E_ARG, NC_E_ALIGN, NC_E_SHAPE, NC_E_UNSUPPORTED, NC_E_HIP, NC_E_WORKSP
 NC_F32, NC_BF16 = 0, 1
 NC_E4M3, NC_E5M2 = 0, 1
 NC_MX_OCP, NC_MX_PLUS1, NC_MX_CEIL = 0, 1, 2
-NC_EST_CURRENT, NC_EST_MOST_RECENT, NC_EST_MAX_WINDOW = 0, 1, 2
+NC_EST_CURRENT, NC_EST_MOST_RECENT, NC_EST_MAX_WINDOW, NC_EST_EMA = 0, 1, 2, 3
 
 
 class NcTensor(ctypes.Structure):
@@ -44,7 +44,7 @@ class NcLossScale(ctypes.Structure):
 class NcPolicy(ctypes.Structure):
     _fields_ = [(n, c_int32) for n in ("fmt", "est", "window", "margin", "hysteresis", "interval",
                                        "skip_on_nonfinite", "ls_enable", "ls_growth_interval",
-                                       "ls_log2_min", "ls_log2_max")]
+                                       "ls_log2_min", "ls_log2_max")] + [("ema_alpha", ctypes.c_float)]
 
 
 EXPORTS = ("nc_amax", "nc_scale_update", "nc_cast_tensor", "nc_cast_mx", "nc_dequant",

@@ -153,8 +153,10 @@ nc_status nc_scale_update(const nc_policy* p, int32_t count, nc_scale_state* st,
                           const nc_counts* in, nc_loss_scale* ls, void* stream) {
   if (p == nullptr || count < 0) return NC_E_ARG;
   if (!valid_fmt((nc_fmt)p->fmt)) return NC_E_UNSUPPORTED;
-  if (p->est != NC_EST_CURRENT && p->est != NC_EST_MOST_RECENT && p->est != NC_EST_MAX_WINDOW)
+  if (p->est != NC_EST_CURRENT && p->est != NC_EST_MOST_RECENT && p->est != NC_EST_MAX_WINDOW &&
+      p->est != NC_EST_EMA)
     return NC_E_UNSUPPORTED;
+  if (p->est == NC_EST_EMA && !(p->ema_alpha > 0.0f && p->ema_alpha <= 1.0f)) return NC_E_ARG;
   if (p->window < 1 || p->window > 1024 || p->margin < 0 || p->margin > 32 || p->interval < 1)
     return NC_E_ARG;
   if (p->ls_enable && (p->ls_growth_interval < 1 || p->ls_log2_min < 0 ||

@@ -43,6 +43,17 @@ __device__ inline void set_scale(const nc_policy& p, nc_scale_state& s, uint32_t
   }
 }
 
+// Exponential smoothing ([MaxWin, "Experimental Variables"]): E + alpha *
+// (a - E), three fp32 operations each rounded to nearest even -- contraction
+// into a fused multiply-add is off, so the result is defined bit for bit.
+__device__ __noinline__ uint32_t ema_step(float alpha, uint32_t E_bits, uint32_t a_bits) {
+#pragma clang fp contract(off)
+  const float E = __uint_as_float(E_bits);
+  const float d = __uint_as_float(a_bits) - E;
+  const float m = alpha * d;
+  return __float_as_uint(E + m);
+}
+
 __global__ void __launch_bounds__(kThreads)
 k_scale_update(const nc_policy p, int32_t count, nc_scale_state* __restrict__ st,
                float* __restrict__ hist, const nc_counts* __restrict__ in,
@@ -77,6 +88,16 @@ k_scale_update(const nc_policy p, int32_t count, nc_scale_state* __restrict__ st
     if (s.head < 0 || s.head >= W || s.n_hist < 0 || s.n_hist > W) s.head = s.n_hist = 0;
     uint32_t* h = reinterpret_cast<uint32_t*>(hist) + (int64_t)i * W;
     const uint32_t a = in[i].amax_bits;
+    if (p.est == NC_EST_EMA) {
+      const uint32_t E = s.n_hist > 0 ? ema_step(p.ema_alpha, h[0], a) : a;
+      h[0] = E;
+      s.head = 0;
+      s.n_hist = 1;
+      s.step += 1;
+      if (s.step % p.interval == 0) set_scale(p, s, E);
+      st[i] = s;
+      continue;
+    }
     h[s.head] = a;
     s.head = (s.head + 1 == W) ? 0 : s.head + 1;
     s.n_hist = min(s.n_hist + 1, W);

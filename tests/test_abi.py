@@ -50,7 +50,7 @@ def test_struct_sizes_match_header():
     assert ctypes.sizeof(_lib.NcStats) == 48
     assert ctypes.sizeof(_lib.NcScaleState) == 24
     assert ctypes.sizeof(_lib.NcLossScale) == 8
-    assert ctypes.sizeof(NcPolicy) == 44
+    assert ctypes.sizeof(NcPolicy) == 48
 
 
 def _desc(*specs):
@@ -123,6 +123,11 @@ def test_policy_checks(lib):
                              ("est", 5, _lib.NC_E_UNSUPPORTED), ("fmt", 3, _lib.NC_E_UNSUPPORTED)):
         p = NcPolicy(**{**good, field: bad})
         assert lib.nc_scale_update(ctypes.byref(p), 1, A, A, A, None, None) == want, field
+    for alpha, want in ((0.0, _lib.NC_E_ARG), (1.5, _lib.NC_E_ARG), (float("nan"), _lib.NC_E_ARG)):
+        p = NcPolicy(**{**good, "est": 3, "ema_alpha": alpha})
+        assert lib.nc_scale_update(ctypes.byref(p), 1, A, A, A, None, None) == want, alpha
+    p = NcPolicy(**{**good, "est": 4})
+    assert lib.nc_scale_update(ctypes.byref(p), 1, A, A, A, None, None) == _lib.NC_E_UNSUPPORTED
     p = NcPolicy(**{**good, "ls_enable": 1, "ls_log2_min": 5, "ls_log2_max": 4})
     assert lib.nc_scale_update(ctypes.byref(p), 1, A, A, A, None, None) == _lib.NC_E_ARG
     p = NcPolicy(**good)

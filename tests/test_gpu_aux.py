@@ -252,3 +252,33 @@ def test_stats_and_counts_over_many_chunks(dtype):
         ws_ = bulk.stats_f64(E4M3, x64, wc, ks[i])
         stats_close(fused[i].cpu().tolist(), ws_)
         stats_close(sep[i].cpu().tolist(), ws_)
+
+
+@pytest.mark.parametrize("hyst,interval", [(False, 1), (True, 1), (True, 3)])
+def test_scale_update_ema(hyst, interval):
+    """Exponential smoothing: per step, the smoothed estimate (history slot 0),
+    k, a_ref and the push count against the oracle, for exact and inexact
+    fp32 coefficients and amaxes over the whole fp32 range (zeros too)."""
+    from oracle.policy import EST_EMA
+    rng = np.random.default_rng(31)
+    alphas = [np.float32(1 / 16), np.float32(0.1), np.float32(0.9), np.float32(1.0)]
+    T = 160                                          # 40 tensors per coefficient
+    for j, alpha in enumerate(alphas):
+        pol_o = Policy(fmt=E4M3, est=EST_EMA, window=4, hysteresis=hyst, interval=interval,
+                       ema_alpha=Fraction(float(alpha)))
+        pol_d = nc.policy("e4m3", "ema", 4, hysteresis=hyst, interval=interval, ema_alpha=float(alpha))
+        sts = [ScaleState() for _ in range(T)]
+        st = nc.new_state(T)
+        hist = nc.new_history(T, 4)
+        for step in range(50):
+            am = (10.0 ** rng.uniform(-44, 38, T)).astype(np.float32)
+            am[rng.integers(0, T, 5)] = 0.0
+            amx = [Fraction(float(v)) for v in am]
+            update(pol_o, sts, amx, [0] * T)
+            nc.nc_scale_update(pol_d, st, _counts_from_amax(am), hist)
+            g = st.cpu().numpy()
+            e = hist[:, 0].cpu().numpy().view(np.uint32)
+            assert np.array_equal(g[:, 0], [s.k for s in sts]), (alpha, step)
+            assert np.array_equal(e, [_f32_bits(float(s.hist[0])) for s in sts]), (alpha, step)
+            assert np.array_equal(g[:, 1].view(np.uint32), [_f32_bits(float(s.a_ref)) for s in sts])
+            assert np.all(g[:, 5] == step + 1) and np.all(g[:, 3] == 1)

@@ -134,3 +134,40 @@ def test_zero_amax_and_fresh_state():
     pol = Policy(fmt=E4M3, est=EST_MOST_RECENT, window=2, hysteresis=True)
     ks, _ = _run(pol, [Fraction(0), Fraction(0), Fraction(3)])
     assert ks[:3] == [127, 127, 127] and ks[3] == t0.scale_exponent(E4M3, Fraction(3))
+
+
+# -- exponential smoothing ----------------------------------------------------
+
+def test_ema_step_against_numpy_float32():
+    """ema_step (exact rationals, rounded to fp32 after each operation)
+    against numpy's own float32 arithmetic (IEEE single, nearest even, no
+    fused multiply-add) on random sequences and coefficients."""
+    import numpy as np
+    from oracle.policy import ema_step
+    rng = np.random.default_rng(5)
+    for alpha in (np.float32(1 / 16), np.float32(0.1), np.float32(0.9), np.float32(1.0), np.float32(1e-3)):
+        a_seq = (10.0 ** rng.uniform(-40, 38, 400)).astype(np.float32)
+        a_seq[::37] = 0.0
+        e_np = a_seq[0]
+        e_or = Fraction(float(a_seq[0]))
+        for a in a_seq[1:]:
+            e_np = np.float32(e_np + np.float32(alpha * np.float32(a - e_np)))
+            e_or = ema_step(Fraction(float(alpha)), e_or, Fraction(float(a)))
+            assert Fraction(float(e_np)) == e_or, (alpha, a)
+
+
+def test_ema_worked_values_and_properties():
+    from oracle.policy import EST_EMA, ema_step
+    assert ema_step(Fraction(1, 2), Fraction(4), Fraction(2)) == 3
+    assert ema_step(Fraction(1, 4), Fraction(8), Fraction(0)) == 6
+    assert ema_step(Fraction(1, 16), Fraction(5), Fraction(5)) == 5             # constant input stays
+    # the estimate stays between the smallest and largest amax seen; with
+    # hysteresis off k is the rule applied to it at every recompute
+    pol = Policy(fmt=E4M3, est=EST_EMA, window=1, hysteresis=False, ema_alpha=Fraction(1, 8))
+    st = [ScaleState()]
+    seq = [Fraction(2) ** j * m for j, m in zip((3, -2, 5, 0, 1, 7, -4), (1, Fraction(3, 2), 1, Fraction(7, 4), 1, 1, Fraction(5, 4)))]
+    for i, a in enumerate(seq):
+        update(pol, st, [a], [0])
+        assert min(seq[:i + 1]) <= st[0].hist[0] <= max(seq[:i + 1])
+        assert st[0].k == t0.scale_exponent(E4M3, st[0].hist[0])
+        assert len(st[0].hist) == 1 and st[0].step == i + 1
