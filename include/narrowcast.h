@@ -56,7 +56,8 @@ typedef enum {
   NC_OK = 0,
   NC_E_ARG = 1,          /* null pointer, negative size, bad policy field */
   NC_E_ALIGN = 2,        /* element pointer not 16-byte aligned */
-  NC_E_SHAPE = 3,        /* MX: cols not a positive multiple of 32, or n % cols != 0 */
+  NC_E_SHAPE = 3,        /* MX: cols not a positive multiple of 32, n % cols != 0, rows not a
+                            multiple of 32 for NC_MX_COLS, or mixed mx_axis in one call */
   NC_E_UNSUPPORTED = 4,  /* unknown enum value */
   NC_E_HIP = 5,          /* a HIP launch failed */
   NC_E_WORKSPACE = 6     /* workspace missing or smaller than nc_workspace_bytes() */
@@ -81,15 +82,24 @@ typedef enum { NC_MX_OCP = 0, NC_MX_PLUS1 = 1, NC_MX_CEIL = 2 } nc_mx_rule;
  * of the tensor's history (window >= 1). */
 typedef enum { NC_EST_CURRENT = 0, NC_EST_MOST_RECENT = 1, NC_EST_MAX_WINDOW = 2, NC_EST_EMA = 3 } nc_est;
 
+/* Which elements share an MX block exponent.  ROWS: 32 consecutive elements
+ * of a row; scales are row-major rows x (cols / 32).  COLS: 32 consecutive
+ * rows of one column (the layout a transposed operand needs); scales are
+ * row-major (rows / 32) x cols. */
+typedef enum { NC_MX_ROWS = 0, NC_MX_COLS = 1 } nc_mx_axis;
+
 /* One tensor of a batch (host array of these). */
 typedef struct {
   const void *x;     /* (device) n input elements, fp32 or bf16; for nc_dequant unused */
   uint8_t *codes;    /* (device) n FP8 codes: written by the casts, read by dequant/stats */
   int64_t n;         /* element count, >= 0 */
-  int64_t cols;      /* MX calls only: row length, a multiple of 32 dividing n;
-                        blocks are 32 consecutive elements of a row */
-  uint8_t *scales;   /* MX calls only (device): n / 32 block-scale bytes X + 127,
-                        row-major (rows x cols/32) */
+  int64_t cols;      /* MX calls only: row length of the row-major rows x cols matrix,
+                        a multiple of 32 dividing n (NC_MX_COLS: n / cols also a
+                        multiple of 32) */
+  uint8_t *scales;   /* MX calls only (device): n / 32 block-scale bytes X + 127 (layout
+                        by mx_axis) */
+  int32_t mx_axis;   /* MX calls only: nc_mx_axis; one value for all tensors of a call */
+  int32_t reserved;  /* 0 */
 } nc_tensor;
 
 /* Per-tensor counts (device array, one per tensor; zero before first use). */
@@ -187,8 +197,9 @@ nc_status nc_cast_tensor(const nc_tensor *t, int32_t count, nc_dtype dtype, nc_f
                          nc_stats *stats, void *ws, size_t ws_bytes, void *stream);
 
 /* MX block-scaled cast ([Drift, "What the measurements said"]): blocks of
- * 32 consecutive row elements share X from the block's finite amax by
- * `rule`; codes = RNE-sat(x * 2^-X), scales = X + 127.  Counts, tensor amax
+ * 32 elements (consecutive in a row, or in a column: mx_axis) share X from
+ * the block's finite amax by `rule`; codes = RNE-sat(x * 2^-X), scales =
+ * X + 127.  Counts, tensor amax
  * and optional statistics accumulate as in nc_cast_tensor.  Bytes per
  * element: in 4|2, out 1 + 1/32. */
 nc_status nc_cast_mx(const nc_tensor *t, int32_t count, nc_dtype dtype, nc_fmt fmt,

@@ -155,12 +155,38 @@ def mx_exponents(fmt: Fmt, x: np.ndarray, rule: str) -> np.ndarray:
     return np.where(a == 0, K_MIN, X)
 
 
-def cast_mx_f64(fmt: Fmt, x: np.ndarray, cols: int, rule: str):
+def _check_mx_shape(n: int, cols: int, axis: str):
+    if cols <= 0 or cols % 32 or n % cols:
+        raise ValueError("cols must be a positive multiple of 32 and divide n")
+    if axis == "cols" and (n // cols) % 32:
+        raise ValueError("column blocks need a multiple of 32 rows")
+    if axis not in ("rows", "cols"):
+        raise ValueError(axis)
+
+
+def mx_element_exponents(X: np.ndarray, n: int, cols: int, axis: str = "rows") -> np.ndarray:
+    """Each element's block exponent, from the block exponents in scale-byte
+    order (``oracle.cast.mx_blocks``)."""
+    _check_mx_shape(n, cols, axis)
+    X = np.asarray(X, dtype=np.int64)
+    if axis == "rows":
+        return np.repeat(X, 32)
+    bands = n // cols // 32
+    return np.broadcast_to(X.reshape(bands, 1, cols), (bands, 32, cols)).ravel()
+
+
+def cast_mx_f64(fmt: Fmt, x: np.ndarray, cols: int, rule: str, axis: str = "rows"):
+    """Vectorised ``oracle.cast.cast_mx``.  Column blocks are gathered by
+    viewing the matrix as (bands, 32, cols) and moving the 32 rows of each
+    band last, so that each block's elements are consecutive."""
     x = np.asarray(x, dtype=np.float64).ravel()
-    if cols % 32 or x.size % cols:
-        raise ValueError("cols must be a multiple of 32 and divide n")
-    X = mx_exponents(fmt, x, rule)
-    K = np.repeat(-X, 32)
+    _check_mx_shape(x.size, cols, axis)
+    if axis == "rows":
+        blocks = x
+    else:
+        blocks = x.reshape(-1, 32, cols).transpose(0, 2, 1).ravel()
+    X = mx_exponents(fmt, blocks, rule)
+    K = -mx_element_exponents(X, x.size, cols, axis)
     codes, clip, uf, nf = cast_f64(fmt, x, K)
     return codes, (X + 127).astype(np.uint8), counts_of(clip, uf, nf, amax_f64(x), x.size)
 

@@ -155,26 +155,45 @@ def cast_tensor(fmt: Fmt, values, k: int, unscale_log2: int = 0):
     return codes, counts
 
 
-def cast_mx(fmt: Fmt, values, cols: int, rule: str):
-    """MX cast: blocks of 32 consecutive elements along each row share the
-    exponent X given by ``mx_exponent`` from the block's finite amax
-    ([Drift, "What the measurements said"]: blocks of 32, one shared power of
-    two per block).  Returns (codes, scale_bytes, counts); the scale byte is
-    X + 127.  counts['amax'] is the finite amax of the whole tensor.
+def mx_blocks(n: int, cols: int, axis: str = "rows"):
+    """Element indices of each MX block of a row-major (n / cols) x cols
+    matrix, in scale-byte order.  axis "rows": 32 consecutive elements of a
+    row, scales row-major rows x (cols / 32).  axis "cols": 32 consecutive
+    rows of one column, scales row-major (rows / 32) x cols -- the blocks of
+    the transposed matrix, with the scales kept in the matrix's own
+    orientation."""
+    if cols <= 0 or cols % 32 or n % cols:
+        raise ValueError("cols must be a positive multiple of 32 and divide n")
+    rows = n // cols
+    if axis == "rows":
+        return [list(range(b, b + 32)) for b in range(0, n, 32)]
+    if axis != "cols":
+        raise ValueError(axis)
+    if rows % 32:
+        raise ValueError("column blocks need a multiple of 32 rows")
+    return [[(32 * band + r) * cols + c for r in range(32)]
+            for band in range(rows // 32) for c in range(cols)]
+
+
+def cast_mx(fmt: Fmt, values, cols: int, rule: str, axis: str = "rows"):
+    """MX cast: each block of 32 elements (``mx_blocks``: along a row, or down
+    a column) shares the exponent X given by ``mx_exponent`` from the block's
+    finite amax ([Drift, "What the measurements said"]: blocks of 32, one
+    shared power of two per block).  Returns (codes, scale_bytes, counts);
+    the scale byte is X + 127.  counts['amax'] is the finite amax of the
+    whole tensor.
     """
     n = len(values)
-    if cols % 32 or n % cols:
-        raise ValueError("cols must be a multiple of 32 and divide n")
-    codes, scales = [], []
+    codes, scales = [0] * n, []
     n_clip = n_uf = n_nf = 0
-    for b in range(0, n, 32):
-        block = values[b:b + 32]
+    for idx in mx_blocks(n, cols, axis):
+        block = [values[i] for i in idx]
         a = max((v.mag for v in block if v.kind == "num"), default=Fraction(0))
         X = mx_exponent(fmt, a, rule)
         scales.append(X + 127)
-        for v in block:
+        for i, v in zip(idx, block):
             c, cl, uf, nf = cast_element(fmt, v, -X)
-            codes.append(c)
+            codes[i] = c
             n_clip += cl
             n_uf += uf
             n_nf += nf

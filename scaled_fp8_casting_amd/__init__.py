@@ -33,6 +33,7 @@ STATE_FIELDS = ("k", "a_ref_bits", "has_ref", "n_hist", "head", "step")
 
 FMT = {"e4m3": NC_E4M3, "e5m2": NC_E5M2}
 MX_RULE = {"ocp": NC_MX_OCP, "plus1": NC_MX_PLUS1, "ceil": NC_MX_CEIL}
+MX_AXIS = {"rows": 0, "cols": 1}
 EST = {"current": NC_EST_CURRENT, "most_recent": NC_EST_MOST_RECENT, "max_window": NC_EST_MAX_WINDOW,
        "ema": NC_EST_EMA}
 
@@ -73,7 +74,7 @@ def _stream(stream) -> Optional[int]:
 
 def tensors(xs: Sequence[Optional[torch.Tensor]], codes: Sequence[Optional[torch.Tensor]],
             cols: Optional[Sequence[int]] = None, scales: Optional[Sequence[torch.Tensor]] = None,
-            n: Optional[Sequence[int]] = None):
+            n: Optional[Sequence[int]] = None, axis: str = "rows"):
     """A host array of nc_tensor descriptors (contiguous device tensors)."""
     count = len(codes)
     arr = (NcTensor * max(count, 1))()
@@ -88,6 +89,7 @@ def tensors(xs: Sequence[Optional[torch.Tensor]], codes: Sequence[Optional[torch
         arr[i].n = n[i] if n is not None else (x.numel() if x is not None else c.numel())
         arr[i].cols = cols[i] if cols is not None else 0
         arr[i].scales = _ptr(scales[i]) if scales is not None and scales[i].numel() else None
+        arr[i].mx_axis = MX_AXIS[axis]
     return arr, count
 
 
@@ -180,8 +182,8 @@ def nc_cast_tensor(xs: Sequence[torch.Tensor], codes: Sequence[torch.Tensor], fm
 
 def nc_cast_mx(xs: Sequence[torch.Tensor], codes: Sequence[torch.Tensor], scales: Sequence[torch.Tensor],
                cols: Sequence[int], fmt, rule, out: torch.Tensor, stats: Optional[torch.Tensor] = None,
-               ws: Optional[torch.Tensor] = None, stream=None):
-    desc, count = tensors(xs, codes, cols=cols, scales=scales)
+               ws: Optional[torch.Tensor] = None, stream=None, axis: str = "rows"):
+    desc, count = tensors(xs, codes, cols=cols, scales=scales, axis=axis)
     dt = _dtype_code(xs[0]) if xs else NC_BF16
     f = FMT[fmt] if isinstance(fmt, str) else fmt
     r = MX_RULE[rule] if isinstance(rule, str) else rule
@@ -192,8 +194,8 @@ def nc_cast_mx(xs: Sequence[torch.Tensor], codes: Sequence[torch.Tensor], scales
 
 def nc_dequant(codes: Sequence[torch.Tensor], ys: Sequence[torch.Tensor], fmt,
                st: Optional[torch.Tensor] = None, scales: Optional[Sequence[torch.Tensor]] = None,
-               cols: Optional[Sequence[int]] = None, stream=None):
-    desc, count = tensors(None, codes, cols=cols, scales=scales)
+               cols: Optional[Sequence[int]] = None, stream=None, axis: str = "rows"):
+    desc, count = tensors(None, codes, cols=cols, scales=scales, axis=axis)
     f = FMT[fmt] if isinstance(fmt, str) else fmt
     yp = (ctypes.c_void_p * max(count, 1))(*[_ptr(y) if y.numel() else None for y in ys])
     for y in ys:
@@ -206,8 +208,8 @@ def nc_cast_stats(xs: Sequence[torch.Tensor], codes: Sequence[torch.Tensor], fmt
                   ws: Optional[torch.Tensor] = None, st: Optional[torch.Tensor] = None,
                   ls: Optional[torch.Tensor] = None,
                   scales: Optional[Sequence[torch.Tensor]] = None, cols: Optional[Sequence[int]] = None,
-                  stream=None):
-    desc, count = tensors(xs, codes, cols=cols, scales=scales)
+                  stream=None, axis: str = "rows"):
+    desc, count = tensors(xs, codes, cols=cols, scales=scales, axis=axis)
     dt = _dtype_code(xs[0]) if xs else NC_F32
     f = FMT[fmt] if isinstance(fmt, str) else fmt
     ws = _ws(ws, desc, count)

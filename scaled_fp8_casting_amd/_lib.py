@@ -16,11 +16,12 @@ NC_F32, NC_BF16 = 0, 1
 NC_E4M3, NC_E5M2 = 0, 1
 NC_MX_OCP, NC_MX_PLUS1, NC_MX_CEIL = 0, 1, 2
 NC_EST_CURRENT, NC_EST_MOST_RECENT, NC_EST_MAX_WINDOW, NC_EST_EMA = 0, 1, 2, 3
+NC_MX_ROWS, NC_MX_COLS = 0, 1
 
 
 class NcTensor(ctypes.Structure):
     _fields_ = [("x", c_void_p), ("codes", c_void_p), ("n", c_int64), ("cols", c_int64),
-                ("scales", c_void_p)]
+                ("scales", c_void_p), ("mx_axis", c_int32), ("reserved", c_int32)]
 
 
 class NcCounts(ctypes.Structure):

@@ -20,7 +20,10 @@ nc_status check_tensors(const nc_tensor* t, int32_t count, bool need_x, bool nee
   for (int32_t i = 0; i < count; ++i) {
     const nc_tensor& x = t[i];
     if (x.n < 0) return NC_E_ARG;
+    if (mx && x.mx_axis != NC_MX_ROWS && x.mx_axis != NC_MX_COLS) return NC_E_UNSUPPORTED;
+    if (mx && x.mx_axis != t[0].mx_axis) return NC_E_SHAPE;
     if (mx && (x.cols <= 0 || x.cols % 32 != 0 || x.n % x.cols != 0)) return NC_E_SHAPE;
+    if (mx && x.mx_axis == NC_MX_COLS && (x.n / x.cols) % 32 != 0) return NC_E_SHAPE;
     if (x.n == 0) continue;
     if ((need_x && x.x == nullptr) || (need_codes && x.codes == nullptr)) return NC_E_ARG;
     if (mx && x.scales == nullptr) return NC_E_ARG;
@@ -51,8 +54,11 @@ nc_status for_launches(const nc_tensor* t, int32_t count, Fn fn) {
   return NC_OK;
 }
 
-// Fills b for tensors [first, end) with tiles of `tile` elements.
-void make_batch(SegBatch& b, const nc_tensor* t, int32_t first, int32_t end, int64_t tile, void* const* y) {
+// Fills b for tensors [first, end) with tiles of `tile` units of `unit`
+// elements (unit 1: element tiles; column-block MX: col_slots, which divide
+// every tensor the checks admit).  b.last counts units.
+void make_batch(SegBatch& b, const nc_tensor* t, int32_t first, int32_t end, int64_t tile, void* const* y,
+                int64_t unit = 1) {
   memset(&b, 0, sizeof(b));
   b.first = first;
   b.count = end - first;
@@ -64,10 +70,12 @@ void make_batch(SegBatch& b, const nc_tensor* t, int32_t first, int32_t end, int
     g.scales = x.scales;
     g.y = y ? y[first + s] : nullptr;
     g.n = x.n;
-    const int64_t tiles = (x.n + tile - 1) / tile;
+    g.cols = x.cols;
+    const int64_t units = x.n / unit;
+    const int64_t tiles = (units + tile - 1) / tile;
     b.tile0[s + 1] = b.tile0[s] + tiles;
     b.chunk0[s + 1] = b.chunk0[s] + (tiles + kChunk - 1) / kChunk;
-    b.last[s] = tiles ? (int32_t)(x.n - (tiles - 1) * tile) : 0;
+    b.last[s] = tiles ? (int32_t)(units - (tiles - 1) * tile) : 0;
   }
   for (int s = b.count + 1; s <= kMaxSeg; ++s) {
     b.tile0[s] = b.tile0[b.count];
@@ -78,10 +86,11 @@ void make_batch(SegBatch& b, const nc_tensor* t, int32_t first, int32_t end, int
 // Walk the call in launches; `fn(batch)` enqueues one launch (skipped when
 // the launch has no element at all).
 template <typename Fn>
-nc_status for_batches(const nc_tensor* t, int32_t count, int64_t tile, void* const* y, Fn fn) {
+nc_status for_batches(const nc_tensor* t, int32_t count, int64_t tile, void* const* y, Fn fn,
+                      int64_t unit = 1) {
   SegBatch b;
   return for_launches(t, count, [&](int32_t first, int32_t end) {
-    make_batch(b, t, first, end, tile, y);
+    make_batch(b, t, first, end, tile, y, unit);
     if (b.tile0[b.count] == 0) return NC_OK;
     return fn(b);
   });
@@ -124,7 +133,9 @@ const char* nc_status_string(nc_status s) {
     case NC_OK: return "ok";
     case NC_E_ARG: return "invalid argument (null pointer, negative size, tensor above 2^34 elements or bad policy field)";
     case NC_E_ALIGN: return "element pointer not 16-byte aligned";
-    case NC_E_SHAPE: return "MX shape: cols must be a positive multiple of 32 dividing n";
+    case NC_E_SHAPE:
+      return "MX shape: cols must be a positive multiple of 32 dividing n (column blocks: rows a multiple of "
+             "32 too), one mx_axis per call";
     case NC_E_UNSUPPORTED: return "unsupported dtype, format, rule or estimator";
     case NC_E_HIP: return "HIP launch failed";
     case NC_E_WORKSPACE: return "workspace missing, misaligned or smaller than nc_workspace_bytes()";
@@ -196,6 +207,14 @@ nc_status nc_cast_mx(const nc_tensor* t, int32_t count, nc_dtype dtype, nc_fmt f
   if (count == 0) return NC_OK;
   if (out == nullptr) return NC_E_ARG;
   if ((s = check_ws(t, count, ws, ws_bytes)) != NC_OK) return s;
+  if (t[0].mx_axis == NC_MX_COLS)
+    return for_batches(t, count, kThreads, nullptr, [&](const SegBatch& b) {
+      const Ws w = ws_of(b, ws);
+      nc_status r = hip_status(launch_cast_mx_col(b, dtype, fmt, rule, stats != nullptr, w,
+                                                  Launch{b.tile0[b.count], (hipStream_t)stream}));
+      if (r == NC_OK) r = hip_status(launch_reduce(b, w, out, stats, nullptr, true, (hipStream_t)stream));
+      return r;
+    }, col_unit(in_bytes(dtype)));
   const int64_t tile = tile_elems(in_bytes(dtype), stats ? kCastStatsVecs : kCastVecs);
   return for_batches(t, count, tile, nullptr, [&](const SegBatch& b) {
     const Ws w = ws_of(b, ws);
@@ -218,6 +237,10 @@ nc_status nc_dequant(const nc_tensor* t, int32_t count, nc_fmt fmt, const nc_sca
     if (y[i] == nullptr) return NC_E_ARG;
     if (!aligned16(y[i])) return NC_E_ALIGN;
   }
+  if (mx && count > 0 && t[0].mx_axis == NC_MX_COLS)
+    return for_batches(t, count, kThreads, y, [&](const SegBatch& b) {
+      return hip_status(launch_dequant_col(b, fmt, Launch{b.tile0[b.count], (hipStream_t)stream}));
+    }, kDequantColUnit);
   return for_batches(t, count, kDequantTile, y, [&](const SegBatch& b) {
     return hip_status(launch_dequant(b, fmt, st, Launch{b.tile0[b.count], (hipStream_t)stream}));
   });
@@ -233,6 +256,13 @@ nc_status nc_cast_stats(const nc_tensor* t, int32_t count, nc_dtype dtype, nc_fm
   if (count == 0) return NC_OK;
   if (out == nullptr) return NC_E_ARG;
   if ((s = check_ws(t, count, ws, ws_bytes)) != NC_OK) return s;
+  if (mx && t[0].mx_axis == NC_MX_COLS)
+    return for_batches(t, count, kThreads, nullptr, [&](const SegBatch& b) {
+      const Ws w = ws_of(b, ws);
+      nc_status r = hip_status(launch_stats_col(b, dtype, fmt, w, Launch{b.tile0[b.count], (hipStream_t)stream}));
+      if (r == NC_OK) r = hip_status(launch_reduce(b, w, nullptr, out, nullptr, false, (hipStream_t)stream));
+      return r;
+    }, col_unit(in_bytes(dtype)));
   const int64_t tile = tile_elems(in_bytes(dtype), kStatsVecs);
   return for_batches(t, count, tile, nullptr, [&](const SegBatch& b) {
     const Ws w = ws_of(b, ws);

@@ -204,6 +204,60 @@ k_dequant(const SegBatch b, const nc_scale_state* __restrict__ st) {
   }
 }
 
+// Dequant of column-block MX codes: a lane owns one col_slot of 8 columns,
+// reads their 8 scale bytes once and then, per row, 8 codes (8 bytes) and
+// writes 8 bf16 values (16 bytes); each column has its own shift.
+__device__ __forceinline__ uint32_t bf16_pair2(f32x2 v, int sh0, int sh1) {
+  v.x = __builtin_amdgcn_ldexpf(v.x, sh0);
+  v.y = __builtin_amdgcn_ldexpf(v.y, sh1);
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
+}
+
+template <int FMT>
+NC_STREAM_KERNEL
+k_dequant_col(const SegBatch b) {
+  constexpr int VC = kDequantColCodes;
+  const int64_t tile = blockIdx.x;
+  const int s = seg_of(b.tile0, b.count, tile);
+  const Seg& g = b.s[s];
+  const ColSlot cs = col_slot<VC>(g, tile - b.tile0[s], tile_len<kThreads>(b, s, tile));
+  if (!cs.act) return;                      // no barriers below
+  const int64_t cols = g.cols;
+  const uint8_t* src = g.codes + cs.e0;
+  uint16_t* dst = static_cast<uint16_t*>(g.y) + cs.e0;
+  u32x2 c[32];
+#pragma unroll
+  for (int r = 0; r < 32; ++r) c[r] = ld_stream(reinterpret_cast<const u32x2*>(src + r * cols));
+  int sh[VC];                               // X of each column
+  if (((uintptr_t)g.scales & 7u) == 0) {    // wave-uniform: one 8-byte load
+    const u32x2 sw = *reinterpret_cast<const u32x2*>(g.scales + cs.sc);
+#pragma unroll
+    for (int i = 0; i < VC; ++i) sh[i] = (int)(((i < 4 ? sw.x : sw.y) >> (8 * (i % 4))) & 0xFFu) - 127;
+  } else {
+#pragma unroll
+    for (int i = 0; i < VC; ++i) sh[i] = (int)g.scales[cs.sc + i] - 127;
+  }
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int r = 0; r < 32; ++r) {
+    u32x4 o;
+    o.x = bf16_pair2(decode_pair<FMT, false>(c[r].x), sh[0], sh[1]);
+    o.y = bf16_pair2(decode_pair<FMT, true>(c[r].x), sh[2], sh[3]);
+    o.z = bf16_pair2(decode_pair<FMT, false>(c[r].y), sh[4], sh[5]);
+    o.w = bf16_pair2(decode_pair<FMT, true>(c[r].y), sh[6], sh[7]);
+    const uint32_t nb0 = nan_bytes<FMT>(c[r].x), nb1 = nan_bytes<FMT>(c[r].y);
+    if (__ballot((nb0 | nb1) != 0) != 0) {    // wave-uniform, rare
+      uint32_t h[8] = {o.x & 0xFFFFu, o.x >> 16, o.y & 0xFFFFu, o.y >> 16,
+                       o.z & 0xFFFFu, o.z >> 16, o.w & 0xFFFFu, o.w >> 16};
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+        if (((i < 4 ? nb0 : nb1) >> (8 * (i % 4) + 7)) & 1u) h[i] = 0x7FC0u;
+      o = u32x4{h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16), h[6] | (h[7] << 16)};
+    }
+    *reinterpret_cast<u32x4*>(dst + r * cols) = o;
+  }
+}
+
 // ---------------------------------------------------------------------------
 // Statistics as a separate pass over x and the codes (and the MX scales).
 
@@ -302,6 +356,95 @@ k_stats(const SegBatch b, const nc_scale_state* __restrict__ st,
       double blk = 1.0;
       if constexpr (MX) blk = pow2_f64((int)g.scales[(e0 + i) / 32] - 127);
       stats_vec<1, MX, false>(&xb, &q, tab, blk, sa);
+    }
+  }
+  write_stat_slot(sa, stat_slots + tile * 6, lds_st);
+}
+
+// Statistics of column-block MX codes: a lane owns one col_slot (VC =
+// 8 / BYTES columns), reads its VC scale bytes once, then per row 8 input
+// bytes and VC codes; two halves of 16 rows keep the registers in bounds.
+// Accumulation is unmasked as in k_stats, with the masked redo when an
+// Inf/NaN was met.
+template <int DT>
+struct ColCodes;
+template <> struct ColCodes<NC_F32> {      // 2 codes per row
+  __device__ static uint32_t load(const uint8_t* p) {
+    return __builtin_nontemporal_load(reinterpret_cast<const uint16_t*>(p));
+  }
+};
+template <> struct ColCodes<NC_BF16> {     // 4 codes per row
+  __device__ static uint32_t load(const uint8_t* p) {
+    return __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(p));
+  }
+};
+
+template <int DT, bool FINITE>
+__device__ __forceinline__ void stats_col_row(u32x2 v, uint32_t w, const double* tab, const double* blk,
+                                              StatAcc& sa) {
+  constexpr int VC = kColBytes / In<DT>::BYTES;
+  uint32_t xb[VC];
+  unpack8<DT>(v, xb);
+#pragma unroll
+  for (int i = 0; i < VC; ++i) {
+    if (!FINITE && (xb[i] & kAbsMask) > kMaxFinite) continue;
+    stat_term((double)__uint_as_float(xb[i]), tab[(w >> (8 * i)) & 0xFFu] * blk[i], sa);
+  }
+}
+
+template <int FMT, int DT>
+NC_STREAM_KERNEL
+k_stats_col(const SegBatch b, double* __restrict__ stat_slots) {
+  constexpr int VC = kColBytes / In<DT>::BYTES;
+  constexpr int H = 16;                     // rows per half
+  __shared__ double tab[256];
+  __shared__ double lds_st[kRows * 6];
+  const int64_t tile = blockIdx.x;
+  const int s = seg_of(b.tile0, b.count, tile);
+  const Seg& g = b.s[s];
+  const ColSlot cs = col_slot<VC>(g, tile - b.tile0[s], tile_len<kThreads>(b, s, tile));
+  const int64_t cols = g.cols;
+  const uint8_t* xs = static_cast<const uint8_t*>(g.x) + cs.e0 * In<DT>::BYTES;
+  const uint8_t* qs = g.codes + cs.e0;
+  double blk[VC];
+#pragma unroll
+  for (int i = 0; i < VC; ++i) blk[i] = pow2_f64((int)g.scales[cs.sc + i] - 127);
+  StatAcc sa;
+  sa.reset();
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    u32x2 v[H];
+    uint32_t w[H];
+#pragma unroll
+    for (int r = 0; r < H; ++r) {
+      const int64_t row = h * H + r;
+      v[r] = ld_stream(reinterpret_cast<const u32x2*>(xs + row * cols * In<DT>::BYTES));
+      w[r] = ColCodes<DT>::load(qs + row * cols);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    if (!cs.act) {                          // idle lane (last tile): zeros add nothing
+#pragma unroll
+      for (int r = 0; r < H; ++r) {
+        v[r] = u32x2{0u, 0u};
+        w[r] = 0u;
+      }
+    }
+    if (h == 0) {                           // the table fill overlaps the first loads
+      fill_stat_table<FMT>(tab, 0);
+      __syncthreads();
+    }
+#pragma unroll
+    for (int r = 0; r < H; ++r) {
+      stats_col_row<DT, true>(v[r], w[r], tab, blk, sa);
+      __builtin_amdgcn_sched_barrier(0);    // one row's table reads at a time (register pressure)
+    }
+  }
+  if (!stats_all_finite(sa)) {              // an Inf/NaN met: redo masked (rare; reloads)
+    __asm__ volatile("" ::: "memory");      // keeps the compiler from holding the first loads for this
+    sa.reset();
+    for (int row = 0; row < 32 && cs.act; ++row) {
+      const u32x2 v = *reinterpret_cast<const u32x2*>(xs + row * cols * In<DT>::BYTES);
+      stats_col_row<DT, false>(v, ColCodes<DT>::load(qs + row * cols), tab, blk, sa);
     }
   }
   write_stat_slot(sa, stat_slots + tile * 6, lds_st);
@@ -486,6 +629,26 @@ hipError_t launch_reduce(const SegBatch& b, const Ws& w, nc_counts* out, nc_stat
   if (out && stats) return reduce_t<true, true>(b, w, out, stats, ls, clips, stream);
   if (out) return reduce_t<true, false>(b, w, out, stats, ls, clips, stream);
   return reduce_t<false, true>(b, w, out, stats, ls, clips, stream);
+}
+
+hipError_t launch_dequant_col(const SegBatch& b, int fmt, const Launch& l) {
+  if (fmt == NC_E4M3)
+    hipLaunchKernelGGL((k_dequant_col<NC_E4M3>), dim3((uint32_t)l.grid), dim3(kThreads), 0, l.stream, b);
+  else
+    hipLaunchKernelGGL((k_dequant_col<NC_E5M2>), dim3((uint32_t)l.grid), dim3(kThreads), 0, l.stream, b);
+  return hipGetLastError();
+}
+
+template <int FMT, int DT>
+hipError_t stats_col_t(const SegBatch& b, const Ws& w, const Launch& l) {
+  hipLaunchKernelGGL((k_stats_col<FMT, DT>), dim3((uint32_t)l.grid), dim3(kThreads), 0, l.stream, b, w.st1);
+  return hipGetLastError();
+}
+
+hipError_t launch_stats_col(const SegBatch& b, int dtype, int fmt, const Ws& w, const Launch& l) {
+  if (fmt == NC_E4M3)
+    return dtype == NC_F32 ? stats_col_t<NC_E4M3, NC_F32>(b, w, l) : stats_col_t<NC_E4M3, NC_BF16>(b, w, l);
+  return dtype == NC_F32 ? stats_col_t<NC_E5M2, NC_F32>(b, w, l) : stats_col_t<NC_E5M2, NC_BF16>(b, w, l);
 }
 
 }  // namespace nc

@@ -1,6 +1,7 @@
 // Streaming kernels that read the input tensor: the per-tensor amax pass,
 // the per-tensor cast (unscale + cast + counts + next-step amax, optional
-// statistics) and the MX block-scaled cast.
+// statistics) and the MX block-scaled cast (blocks along rows or down
+// columns).
 //
 // One workgroup per tile (256 threads x a few 16-byte vectors each; see
 // nc_device.h for why).  Each 16-byte load instruction of a wave covers
@@ -267,6 +268,146 @@ k_cast_mx(const SegBatch b, CountSlot* __restrict__ slots, double* __restrict__ 
   if constexpr (STATS) write_stat_slot(sa, stat_slots + tile * 6, lds_st);
 }
 
+// ---------------------------------------------------------------------------
+// MX with blocks down the columns (32 consecutive rows of one column share
+// X): the layout of an operand consumed transposed.  A lane owns one slot
+// (col_slot): VC = 8 / BYTES adjacent columns of a 32-row band, 8 input
+// bytes per row.  It loads all 32 rows, takes each column's finite max in
+// registers (no exchange between lanes), then casts and stores row by row.
+template <int FMT, int DT, int RULE, bool STATS>
+NC_STREAM_KERNEL
+k_cast_mx_col(const SegBatch b, CountSlot* __restrict__ slots, double* __restrict__ stat_slots) {
+  constexpr int VC = kColBytes / In<DT>::BYTES;    // 4 bf16 or 2 fp32 columns
+  __shared__ uint32_t lds[kRows * 4];
+  __shared__ double lds_st[STATS ? kRows * 6 : 1];
+  __shared__ double tab[STATS ? 256 : 1];
+  const int64_t tile = blockIdx.x;
+  const int s = seg_of(b.tile0, b.count, tile);
+  const Seg& g = b.s[s];
+  const int rem = tile_len<kThreads>(b, s, tile);
+  const ColSlot cs = col_slot<VC>(g, tile - b.tile0[s], rem);
+  const int64_t cols = g.cols;
+  const int64_t stride = cols * In<DT>::BYTES;
+  const uint8_t* src = static_cast<const uint8_t*>(g.x) + cs.e0 * In<DT>::BYTES;
+  u32x2 v[32];
+#pragma unroll
+  for (int r = 0; r < 32; ++r) v[r] = ld_stream(reinterpret_cast<const u32x2*>(src + r * stride));
+  __builtin_amdgcn_sched_barrier(0);
+  if (rem < kThreads && !cs.act) {          // the tensor's last tile: idle lanes hold zeros
+#pragma unroll
+    for (int r = 0; r < 32; ++r) v[r] = u32x2{0u, 0u};
+  }
+  if constexpr (STATS) {
+    fill_stat_table<FMT>(tab, 0);
+    __syncthreads();
+  }
+  Acc acc;
+  acc.reset();
+  // per-column max of |x| bits (an idle lane holds zeros: X = -127, no
+  // counts).  Formed on the packed words with operations of its own -- bf16
+  // magnitudes by packed 16-bit max, fp32 magnitudes as x << 1 -- so the
+  // compiler keeps no unpacked copy of the 32 rows alive into the cast loop.
+  uint32_t m[VC], mall = 0;
+  if constexpr (DT == NC_BF16) {
+    u16x2 mx = {0, 0}, my = {0, 0};
+#pragma unroll
+    for (int r = 0; r < 32; ++r) {
+      mx = __builtin_elementwise_max(mx, __builtin_bit_cast(u16x2, v[r].x & 0x7FFF7FFFu));
+      my = __builtin_elementwise_max(my, __builtin_bit_cast(u16x2, v[r].y & 0x7FFF7FFFu));
+    }
+    m[0] = (uint32_t)mx.x << 16; m[1] = (uint32_t)mx.y << 16;
+    m[2] = (uint32_t)my.x << 16; m[3] = (uint32_t)my.y << 16;
+  } else {
+    uint32_t m2[2] = {0u, 0u};
+#pragma unroll
+    for (int r = 0; r < 32; ++r) {
+      m2[0] = max(m2[0], v[r].x << 1);
+      m2[1] = max(m2[1], v[r].y << 1);
+    }
+    m[0] = m2[0] >> 1; m[1] = m2[1] >> 1;
+  }
+#pragma unroll
+  for (int i = 0; i < VC; ++i) mall = max(mall, m[i]);
+  const bool clean = __ballot(mall > kMaxFinite) == 0;   // wave-uniform
+  if (!clean) {                                          // finite max, count non-finite
+#pragma unroll
+    for (int i = 0; i < VC; ++i) m[i] = 0;
+#pragma unroll
+    for (int r = 0; r < 32; ++r) {
+      uint32_t xb[VC];
+      unpack8<DT>(v[r], xb);
+#pragma unroll
+      for (int i = 0; i < VC; ++i) m[i] = max(m[i], finite_mag(xb[i] & kAbsMask, acc));
+    }
+  }
+  int X[VC];
+  CastParams p[VC];
+#pragma unroll
+  for (int i = 0; i < VC; ++i) {
+    acc.amax = max(acc.amax, m[i]);
+    X[i] = mx_exponent<FMT, RULE>(m[i]);
+    p[i] = cast_params<FMT>(-X[i]);
+  }
+  StatAcc sa;
+  if constexpr (STATS) sa.reset();
+  uint8_t* dst = g.codes + cs.e0;
+#pragma unroll
+  for (int r = 0; r < 32; ++r) {
+    // the row's words pass through an empty asm: values derived from them
+    // above (the non-finite path) cannot be hoisted and held for this loop
+    u32x2 vr = v[r];
+    __asm__ volatile("" : "+v"(vr));
+    uint32_t xb[VC];
+    unpack8<DT>(vr, xb);
+    float y[VC];
+#pragma unroll
+    for (int i = 0; i < VC; ++i) y[i] = __builtin_amdgcn_ldexpf(__uint_as_float(xb[i]), p[i].K);
+    int wi = cvt_pair<FMT, false>(y[0], y[1], 0);
+    if constexpr (VC == 4) wi = cvt_pair<FMT, true>(y[2], y[3], wi);
+    uint32_t w = sat4<FMT>((uint32_t)wi);
+#pragma unroll
+    for (int i = 0; i < VC; ++i) count_elem(xb[i] & kAbsMask, p[i], acc);
+    if (!clean) {
+#pragma unroll
+      for (int i = 0; i < VC; ++i)
+        if ((xb[i] & kAbsMask) > kMaxFinite)
+          w = (w & ~(0xFFu << (8 * i))) | (nonfinite_code<FMT>(xb[i]) << (8 * i));
+    }
+    if constexpr (STATS) {
+#pragma unroll
+      for (int i = 0; i < VC; ++i) {
+        if (!clean && (xb[i] & kAbsMask) > kMaxFinite) continue;
+        stat_term((double)__uint_as_float(xb[i]), tab[(w >> (8 * i)) & 0xFFu] * pow2_f64(X[i]), sa);
+      }
+    }
+    // the row's counts are taken here: left alone, the compiler sinks every
+    // compare to the end of the loop and keeps all 32 rows' magnitudes live
+    __asm__ volatile("" : "+v"(acc.n_big), "+v"(acc.n_uf));
+    __builtin_amdgcn_sched_barrier(0);   // one row at a time (register pressure)
+    if (cs.act) {
+      uint8_t* d = dst + r * stride / In<DT>::BYTES;
+      if constexpr (VC == 4) st_stream(reinterpret_cast<uint32_t*>(d), w);
+      else __builtin_nontemporal_store((uint16_t)w, reinterpret_cast<uint16_t*>(d));
+    }
+  }
+  if (cs.act) {
+    uint8_t* sd = g.scales + cs.sc;
+    uint32_t sb = 0;
+#pragma unroll
+    for (int i = 0; i < VC; ++i) sb |= (uint32_t)(X[i] + 127) << (8 * i);
+    // one word per lane when the scale array allows it (wave-uniform)
+    if (((uintptr_t)g.scales & (VC - 1)) == 0) {
+      if constexpr (VC == 4) *reinterpret_cast<uint32_t*>(sd) = sb;
+      else *reinterpret_cast<uint16_t*>(sd) = (uint16_t)sb;
+    } else {
+#pragma unroll
+      for (int i = 0; i < VC; ++i) sd[i] = (uint8_t)(sb >> (8 * i));
+    }
+  }
+  write_count_slot(acc, slots + tile, lds);
+  if constexpr (STATS) write_stat_slot(sa, stat_slots + tile * 6, lds_st);
+}
+
 template <int FMT, int DT>
 hipError_t cast_pt_t(const SegBatch& b, const nc_scale_state* st, const nc_loss_scale* ls, bool stats,
                      const Ws& w, const Launch& l) {
@@ -297,6 +438,24 @@ hipError_t cast_mx_t(const SegBatch& b, int rule, bool stats, const Ws& w, const
   return cast_mx_r<FMT, DT, NC_MX_CEIL>(b, stats, w, l);
 }
 
+template <int FMT, int DT, int RULE>
+hipError_t cast_mx_col_r(const SegBatch& b, bool stats, const Ws& w, const Launch& l) {
+  if (stats)
+    hipLaunchKernelGGL((k_cast_mx_col<FMT, DT, RULE, true>), dim3((uint32_t)l.grid), dim3(kThreads), 0, l.stream,
+                       b, w.cnt1, w.st1);
+  else
+    hipLaunchKernelGGL((k_cast_mx_col<FMT, DT, RULE, false>), dim3((uint32_t)l.grid), dim3(kThreads), 0, l.stream,
+                       b, w.cnt1, w.st1);
+  return hipGetLastError();
+}
+
+template <int FMT, int DT>
+hipError_t cast_mx_col_t(const SegBatch& b, int rule, bool stats, const Ws& w, const Launch& l) {
+  if (rule == NC_MX_OCP) return cast_mx_col_r<FMT, DT, NC_MX_OCP>(b, stats, w, l);
+  if (rule == NC_MX_PLUS1) return cast_mx_col_r<FMT, DT, NC_MX_PLUS1>(b, stats, w, l);
+  return cast_mx_col_r<FMT, DT, NC_MX_CEIL>(b, stats, w, l);
+}
+
 }  // namespace
 
 hipError_t launch_amax(const SegBatch& b, int dtype, const Ws& w, const Launch& l) {
@@ -323,6 +482,15 @@ hipError_t launch_cast_mx(const SegBatch& b, int dtype, int fmt, int rule, bool 
                            : cast_mx_t<NC_E4M3, NC_BF16>(b, rule, stats, w, l);
   return dtype == NC_F32 ? cast_mx_t<NC_E5M2, NC_F32>(b, rule, stats, w, l)
                          : cast_mx_t<NC_E5M2, NC_BF16>(b, rule, stats, w, l);
+}
+
+hipError_t launch_cast_mx_col(const SegBatch& b, int dtype, int fmt, int rule, bool stats, const Ws& w,
+                              const Launch& l) {
+  if (fmt == NC_E4M3)
+    return dtype == NC_F32 ? cast_mx_col_t<NC_E4M3, NC_F32>(b, rule, stats, w, l)
+                           : cast_mx_col_t<NC_E4M3, NC_BF16>(b, rule, stats, w, l);
+  return dtype == NC_F32 ? cast_mx_col_t<NC_E5M2, NC_F32>(b, rule, stats, w, l)
+                         : cast_mx_col_t<NC_E5M2, NC_BF16>(b, rule, stats, w, l);
 }
 
 }  // namespace nc

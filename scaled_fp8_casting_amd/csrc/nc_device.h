@@ -301,6 +301,7 @@ struct Seg {
   uint8_t* scales;
   void* y;
   int64_t n;
+  int64_t cols;    // MX: row length
 };
 
 struct SegBatch {
@@ -336,6 +337,34 @@ __device__ __forceinline__ int seg_of(const int64_t* start, int count, int64_t i
 template <int64_t TILE>
 __device__ __forceinline__ int tile_len(const SegBatch& b, int s, int64_t t) {
   return t == b.tile0[s + 1] - 1 ? b.last[s] : (int)TILE;
+}
+
+// Column-block MX (blocks of 32 consecutive rows of one column).  A "slot"
+// is VC adjacent columns of one 32-row band: 32 * VC elements, VC blocks.
+// Slots are numbered band by band, left to right; tile t of a tensor is
+// slots [256 t, 256 t + 256), one per lane, so the lanes of a wave hold
+// consecutive pieces of the same rows and every row access of a wave is one
+// contiguous run.  A tensor has n / (32 VC) < 2^29 slots (rows are a
+// multiple of 32, so cols <= n / 32), which keeps the division 32-bit.
+struct ColSlot {
+  int64_t e0;   // element index of the slot's top-left element
+  int64_t sc;   // index of the slot's first scale byte ((rows / 32) x cols, row-major)
+  bool act;     // the lane has a slot (the tensor's last tile may be short)
+};
+// An idle lane gets the tensor's slot 0 -- in bounds, so its loads need no
+// predicate (they would otherwise become a branch per row) -- and must
+// discard what it reads and store nothing.
+template <int VC>
+__device__ __forceinline__ ColSlot col_slot(const Seg& g, int64_t t, int rem) {
+  const uint32_t per_band = (uint32_t)(g.cols / VC);
+  const uint32_t j = (uint32_t)t * (uint32_t)kThreads + threadIdx.x;
+  const uint32_t band = j / per_band;
+  const uint32_t cg = j - band * per_band;
+  ColSlot c;
+  c.act = (int)threadIdx.x < rem;
+  c.e0 = c.act ? (int64_t)band * 32 * g.cols + (int64_t)cg * VC : 0;
+  c.sc = c.act ? (int64_t)band * g.cols + (int64_t)cg * VC : 0;
+  return c;
 }
 
 // Workspace slots.  A workgroup's counts: finite-|x| max (bits), non-finite,
@@ -413,6 +442,7 @@ __device__ __forceinline__ uint32_t f32_to_bf16_rne(uint32_t b) {
 // separate statistics pass).
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef uint16_t u16x2 __attribute__((ext_vector_type(2)));
 
 // Streaming loads: every input byte is read once per pass, so the loads are
 // non-temporal (the cache lines are not kept for reuse).
@@ -438,6 +468,17 @@ __device__ __forceinline__ void unpack(const u32x4 v, uint32_t* xb) {
     xb[2] = v.y << 16; xb[3] = v.y & 0xFFFF0000u;
     xb[4] = v.z << 16; xb[5] = v.z & 0xFFFF0000u;
     xb[6] = v.w << 16; xb[7] = v.w & 0xFFFF0000u;
+  }
+}
+
+// 8 input bytes -> 8 / BYTES fp32 bit patterns (the column-block kernels).
+template <int DT>
+__device__ __forceinline__ void unpack8(const u32x2 v, uint32_t* xb) {
+  if constexpr (DT == NC_F32) {
+    xb[0] = v.x; xb[1] = v.y;
+  } else {
+    xb[0] = v.x << 16; xb[1] = v.x & 0xFFFF0000u;
+    xb[2] = v.y << 16; xb[3] = v.y & 0xFFFF0000u;
   }
 }
 

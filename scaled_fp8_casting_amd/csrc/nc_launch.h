@@ -23,6 +23,16 @@ inline int64_t tile_elems(int in_bytes, int vecs) { return (int64_t)kThreads * (
 // smallest tile of any call that uses the workspace (fp32 cast / statistics)
 constexpr int64_t kMinWsTile = (int64_t)kThreads * 4 * kCastVecs;
 
+// Column-block MX (col_slot): a lane reads 8 input bytes per row (4 bf16 or
+// 2 fp32 columns), or 8 codes per row in dequant; a tile is 256 slots of 32
+// rows, always at least kMinWsTile elements, so the workspace bound above
+// covers these calls too.
+constexpr int kColBytes = 8;
+constexpr int kDequantColCodes = 8;
+inline int64_t col_unit(int in_bytes) { return 32 * (kColBytes / in_bytes); }
+constexpr int64_t kDequantColUnit = 32 * kDequantColCodes;
+static_assert(kThreads * 32 * 2 >= kMinWsTile, "column tiles are no smaller than kMinWsTile");
+
 // Workspace of one launch: per-tile slots, then per-chunk slots.
 struct Ws {
   CountSlot* cnt1;      // [tiles]
@@ -63,6 +73,12 @@ hipError_t launch_cast_mx(const SegBatch& b, int dtype, int fmt, int rule, bool 
                           const Launch& l);
 hipError_t launch_stats(const SegBatch& b, int dtype, int fmt, const nc_scale_state* st,
                         const nc_loss_scale* ls, const Ws& w, const Launch& l);
+// Column-block MX forms of the MX cast, dequant and statistics pass; the
+// batch's tiles are 256 col_slots.
+hipError_t launch_cast_mx_col(const SegBatch& b, int dtype, int fmt, int rule, bool stats, const Ws& w,
+                              const Launch& l);
+hipError_t launch_dequant_col(const SegBatch& b, int fmt, const Launch& l);
+hipError_t launch_stats_col(const SegBatch& b, int dtype, int fmt, const Ws& w, const Launch& l);
 // The two reductions of a launch's slots into the caller's counts (nullable)
 // and statistics (nullable).  ls: unscale of the amax and of the statistics
 // (nullable; the MX calls pass none).  clips: the counts report clips (the

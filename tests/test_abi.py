@@ -45,7 +45,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_struct_sizes_match_header():
-    assert ctypes.sizeof(NcTensor) == 40
+    assert ctypes.sizeof(NcTensor) == 48
     assert ctypes.sizeof(_lib.NcCounts) == 40
     assert ctypes.sizeof(_lib.NcStats) == 48
     assert ctypes.sizeof(_lib.NcScaleState) == 24
@@ -53,10 +53,11 @@ def test_struct_sizes_match_header():
     assert ctypes.sizeof(NcPolicy) == 48
 
 
-def _desc(*specs):
+def _desc(*specs, axes=None):
     arr = (NcTensor * len(specs))()
     for i, (x, c, n, cols, sc) in enumerate(specs):
         arr[i].x, arr[i].codes, arr[i].n, arr[i].cols, arr[i].scales = x, c, n, cols, sc
+        arr[i].mx_axis = axes[i] if axes else 0
     return arr
 
 
@@ -95,6 +96,19 @@ def test_argument_checks_before_any_launch(lib):
         assert lib.nc_cast_mx(_desc((A, A, n, cols, A)), 1, 1, 0, 0, A, None, A, W, None) == _lib.NC_E_SHAPE
     assert lib.nc_cast_mx(_desc((A, A, 64, 64, None)), 1, 1, 0, 0, A, None, A, W, None) == _lib.NC_E_ARG
     assert lib.nc_cast_mx(_desc((A, A, 64, 64, A)), 1, 1, 0, 9, A, None, A, W, None) == _lib.NC_E_UNSUPPORTED
+    # column blocks: rows a multiple of 32, one axis per call, known axis values
+    C = _lib.NC_MX_COLS
+    assert lib.nc_cast_mx(_desc((A, A, 48 * 64, 64, A), axes=[C]), 1, 1, 0, 0, A, None, A, W, None) == _lib.NC_E_SHAPE
+    assert lib.nc_cast_mx(_desc((A, A, 64 * 64, 64, A), (A, A, 64, 64, A), axes=[C, 0]), 2, 1, 0, 0, A, None,
+                          A, W, None) == _lib.NC_E_SHAPE
+    assert lib.nc_cast_mx(_desc((A, A, 64, 64, A), axes=[2]), 1, 1, 0, 0, A, None, A, W, None) == _lib.NC_E_UNSUPPORTED
+    assert lib.nc_dequant(_desc((None, A, 16 * 64, 64, A), axes=[C]), 1, 0, None, (ctypes.c_void_p * 1)(A), 1,
+                          None) == _lib.NC_E_SHAPE
+    assert lib.nc_cast_stats(_desc((A, A, 16 * 64, 64, A), axes=[C]), 1, 0, 0, None, None, A, A, W,
+                             None) == _lib.NC_E_SHAPE
+    # the per-tensor calls ignore the axis field
+    assert lib.nc_cast_tensor(_desc((A, A + 1, 8, 0, None), axes=[7]), 1, 0, 0, A, None, A, None, A, W,
+                              None) == _lib.NC_E_ALIGN
     # per-tensor cast
     assert lib.nc_cast_tensor(_desc((A, A + 1, 8, 0, None)), 1, 0, 0, A, None, A, None, A, W, None) == _lib.NC_E_ALIGN
     assert lib.nc_cast_tensor(_desc((A, A, 8, 0, None)), 1, 0, 0, None, None, A, None, A, W, None) == _lib.NC_E_ARG

@@ -14,7 +14,8 @@ from oracle import bulk
 from oracle import cast as t0
 from oracle.policy import EST_CURRENT, LossScale, Policy, ScaleState, update
 import workloads
-from tests._gpu import (codes_like, dev_bf16, dev_f32, host_u16, host_u8, state_with_k, stats_close)
+from tests._gpu import (assert_counts, codes_like, dev_bf16, dev_f32, host_u16, host_u8, state_with_k,
+                        stats_close)
 
 pytestmark = pytest.mark.gpu
 FMTS = [("e4m3", E4M3), ("e5m2", E5M2)]
@@ -282,3 +283,56 @@ def test_scale_update_ema(hyst, interval):
             assert np.array_equal(e, [_f32_bits(float(s.hist[0])) for s in sts]), (alpha, step)
             assert np.array_equal(g[:, 1].view(np.uint32), [_f32_bits(float(s.a_ref)) for s in sts])
             assert np.all(g[:, 5] == step + 1) and np.all(g[:, 3] == 1)
+
+
+# -- MX, blocks down the columns ---------------------------------------------------
+
+@pytest.mark.parametrize("name,fmt", FMTS)
+@pytest.mark.parametrize("rows,cols", [(32, 32), (64, 96), (160, 2080)])
+def test_dequant_mx_column_blocks(name, fmt, rows, cols):
+    """Every code under random scale bytes (and the extremes), column
+    layout; ragged last tiles; output guarded against writes past the end;
+    scale arrays at an aligned and an odd offset."""
+    rng = np.random.default_rng(rows + cols)
+    n = rows * cols
+    codes = rng.integers(0, 256, n).astype(np.uint8)
+    codes[:256] = np.arange(256)
+    scales = rng.integers(0, 256, n // 32).astype(np.uint8)
+    scales[:8] = [0, 1, 254, 253, 127, 126, 128, 255]
+    K = -bulk.mx_element_exponents(scales.astype(np.int64) - 127, n, cols, "cols")
+    want = bulk.dequant_bf16_f64(fmt, codes, K)
+    for off in (0, 3):
+        sbig = torch.zeros(n // 32 + 8, dtype=torch.uint8, device="cuda")
+        sbig[off:off + n // 32] = torch.from_numpy(scales).cuda()
+        ybig = torch.full((n + 64,), -7.0, dtype=torch.bfloat16, device="cuda")
+        nc.nc_dequant([torch.from_numpy(codes).cuda()], [ybig[:n]], name,
+                      scales=[sbig[off:off + n // 32]], cols=[cols], axis="cols")
+        torch.cuda.synchronize()
+        y = host_u16(ybig)
+        assert np.array_equal(y[:n], want), off
+        assert np.all(ybig[n:].float().cpu().numpy() == -7.0), off
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("rule", ["ocp", "ceil"])
+def test_stats_mx_column_blocks_fused_and_separate(dtype, rule):
+    rows, cols = 96, 1056
+    n = rows * cols
+    xd, x64 = _stats_input(dtype, n, 8)
+    codes = codes_like(n)
+    scales = torch.empty(n // 32, dtype=torch.uint8, device="cuda")
+    out = nc.new_counts(1)
+    fused = nc.new_stats(1)
+    desc, cnt = nc.tensors([xd], [codes])
+    ws = nc.new_workspace(desc, cnt)
+    nc.nc_cast_mx([xd], [codes], [scales], [cols], "e5m2", rule, out, stats=fused, ws=ws, axis="cols")
+    sep = nc.new_stats(1)
+    nc.nc_cast_stats([xd], [codes], "e5m2", sep, ws, scales=[scales], cols=[cols], axis="cols")
+    torch.cuda.synchronize()
+    wc, wsc, wn = bulk.cast_mx_f64(E5M2, x64, cols, rule, axis="cols")
+    assert np.array_equal(host_u8(codes), wc) and np.array_equal(host_u8(scales), wsc)
+    assert_counts(nc.counts_list(out)[0], wn)
+    K = -bulk.mx_element_exponents(wsc.astype(np.int64) - 127, n, cols, "cols")
+    want = bulk.stats_f64(E5M2, x64, wc, K)
+    stats_close(fused[0].cpu().tolist(), want)
+    stats_close(sep[0].cpu().tolist(), want)

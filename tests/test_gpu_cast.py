@@ -339,3 +339,87 @@ def test_mx_scales_at_any_alignment(dtype):
         b = host_u8(big)
         assert np.array_equal(b[off:off + n // 32], wsc), off
         assert np.all(b[:off] == 0xA5) and np.all(b[off + n // 32:] == 0xA5), off
+
+
+# -- MX, blocks down the columns ---------------------------------------------------
+
+def _col_input(rows, cols, seed, dtype):
+    """tanh-shaped values with a per-column-block power-of-two spread, and
+    column blocks that are all zero, all NaN, subnormal or huge."""
+    rng = np.random.default_rng(seed)
+    spread = np.exp2(rng.integers(-40, 40, (rows // 32, 1, cols)))
+    x = (np.tanh(rng.normal(0, 1.5, (rows // 32, 32, cols))) * spread).reshape(rows, cols).astype(np.float32)
+    x[0:32, 0] = 0.0
+    x[0:32, 1] = np.nan
+    x[5, 2] = np.inf
+    x[7, 3] = -np.inf
+    x[0:32, 4] = (np.arange(32) * 2.0 ** -140).astype(np.float32)
+    x[0:32, 5] = np.float32(2.0 ** 127) * 1.5
+    x = x.ravel()
+    if dtype == "bf16":
+        bits = workloads.to_bf16_bits(x.astype(np.float64))
+        return dev_bf16(bits), bulk.bf16_bits_to_f64(bits)
+    return dev_f32(x), x.astype(np.float64)
+
+
+def _cast_mx_cols(xds, shapes, fmt, rule, stats=None):
+    codes = [codes_like(r * c) for r, c in shapes]
+    scales = [torch.empty(r * c // 32, dtype=torch.uint8, device="cuda") for r, c in shapes]
+    out = nc.new_counts(len(shapes))
+    nc.nc_cast_mx(xds, codes, scales, [c for _, c in shapes], fmt, rule, out, stats=stats, axis="cols")
+    torch.cuda.synchronize()
+    return [host_u8(c) for c in codes], [host_u8(s) for s in scales], nc.counts_list(out)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("rule", ["ocp", "plus1", "ceil"])
+@pytest.mark.parametrize("name,fmt", FMTS)
+@pytest.mark.parametrize("rows,cols", [(32, 32), (64, 96), (96, 4096), (160, 2080)])
+def test_mx_column_blocks_parity(dtype, rule, name, fmt, rows, cols):
+    """Column blocks: one 32-row band in a partial tile, several bands per
+    tile (small cols), whole tiles, and bands that straddle tiles with a
+    ragged last tile."""
+    xd, x64 = _col_input(rows, cols, rows + cols, dtype)
+    codes, scales, counts = _cast_mx_cols([xd], [(rows, cols)], name, rule)
+    wc, ws, wn = bulk.cast_mx_f64(fmt, x64, cols, rule, axis="cols")
+    assert np.array_equal(scales[0], ws)
+    bad = np.flatnonzero(codes[0] != wc)
+    assert bad.size == 0, [(i, x64[i], hex(codes[0][i]), hex(wc[i])) for i in bad[:5]]
+    assert_counts(counts[0], wn)
+    assert counts[0]["amax"] == wn["amax"]
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_mx_column_blocks_batch_of_tensors(dtype):
+    """Several shapes in one call (one launch), then 40 tensors (two
+    launches): each tensor's codes, scales and counts."""
+    for shapes in ([(32, 32), (64, 1024), (96, 160), (32, 8192)], [(32, 64 * (1 + i % 5)) for i in range(40)]):
+        ins = [_col_input(r, c, 7 * i + r, dtype) for i, (r, c) in enumerate(shapes)]
+        codes, scales, counts = _cast_mx_cols([d for d, _ in ins], shapes, "e4m3", "ocp")
+        for (r, c), (_, x64), cg, sg, ng in zip(shapes, ins, codes, scales, counts):
+            wc, ws, wn = bulk.cast_mx_f64(E4M3, x64, c, "ocp", axis="cols")
+            assert np.array_equal(cg, wc) and np.array_equal(sg, ws), (r, c)
+            assert_counts(ng, wn)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_mx_column_scales_at_any_alignment_and_no_writes_past_the_end(dtype):
+    """Scale arrays at offsets 0..7 of an allocation (word stores when
+    aligned, bytes otherwise) give the same bytes; nothing after the codes,
+    or around the scales, changes (a ragged last tile)."""
+    rows, cols = 96, 2080
+    n = rows * cols
+    xd, x64 = _col_input(rows, cols, 23, dtype)
+    wc, wsc, _ = bulk.cast_mx_f64(E5M2, x64, cols, "plus1", axis="cols")
+    guard = 4096
+    for off in range(8):
+        big = torch.full((n // 32 + 16,), 0xA5, dtype=torch.uint8, device="cuda")
+        sc = big[off:off + n // 32]
+        cbig = torch.full((n + guard,), 0xA5, dtype=torch.uint8, device="cuda")
+        nc.nc_cast_mx([xd], [cbig[:n]], [sc], [cols], "e5m2", "plus1", nc.new_counts(1), axis="cols")
+        torch.cuda.synchronize()
+        c = host_u8(cbig)
+        assert np.array_equal(c[:n], wc) and np.all(c[n:] == 0xA5), off
+        b = host_u8(big)
+        assert np.array_equal(b[off:off + n // 32], wsc), off
+        assert np.all(b[:off] == 0xA5) and np.all(b[off + n // 32:] == 0xA5), off

@@ -88,6 +88,80 @@ def test_mx_tier0_vs_tier1(fmt, rule):
     assert scales[2] == 0 and scales[6] == 0    # X = -127 for empty blocks
 
 
+def _col_input(rows, cols, seed):
+    rng = np.random.default_rng(seed)
+    x = (np.tanh(rng.normal(0, 1.5, (rows, cols))) * 2.0 ** rng.integers(-30, 30, (rows, cols)))
+    x = x.astype(np.float32).astype(np.float64)
+    x[3, 1] = np.inf
+    x[32:64, 2] = 0.0                    # an all-zero column block
+    x[0:32, 5] = np.nan                  # an all-NaN column block
+    x[40, 7] = -np.inf
+    return x
+
+
+@pytest.mark.parametrize("fmt", FMTS, ids=["e4m3", "e5m2"])
+@pytest.mark.parametrize("rule", ["ocp", "plus1", "ceil"])
+def test_mx_column_blocks_tier0_vs_tier1(fmt, rule):
+    rows, cols = 64, 32
+    x = _col_input(rows, cols, 12).ravel()
+    codes, scales, counts = bulk.cast_mx_f64(fmt, x, cols, rule, axis="cols")
+    c0, s0, n0 = t0.cast_mx(fmt, bulk.to_vals(x), cols, rule, axis="cols")
+    assert codes.tolist() == c0 and scales.tolist() == s0
+    for key in ("n_finite", "n_clip", "n_underflow", "n_nonfinite"):
+        assert counts[key] == n0[key]
+    assert scales[cols + 2] == 0 and scales[5] == 0     # X = -127 for empty blocks
+
+
+@pytest.mark.parametrize("fmt", FMTS, ids=["e4m3", "e5m2"])
+def test_mx_column_blocks_are_row_blocks_of_the_transpose(fmt):
+    """Blocks down the columns of A are the row blocks of A^T: codes are the
+    transpose of A^T's codes, and the (rows/32) x cols scale matrix is the
+    transpose of A^T's cols x (rows/32) one.  Pins the column layout to the
+    row layout, which the worked MX cases pin."""
+    rows, cols = 96, 64
+    x = _col_input(rows, cols, 13)
+    for rule in ("ocp", "plus1", "ceil"):
+        codes, scales, counts = bulk.cast_mx_f64(fmt, x.ravel(), cols, rule, axis="cols")
+        ct, st_, nt = bulk.cast_mx_f64(fmt, x.T.ravel(), rows, rule)
+        assert np.array_equal(codes.reshape(rows, cols), ct.reshape(cols, rows).T)
+        assert np.array_equal(scales.reshape(rows // 32, cols), st_.reshape(cols, rows // 32).T)
+        assert counts == nt
+
+
+def test_mx_column_block_exponent_closed_form():
+    """OCP E4M3 takes X = floor(log2 amax) - 8.  A 32 x 32 diagonal with
+    2^(c - 10) at (c, c): column block c has amax 2^(c - 10), X = c - 18.
+    Every row equal to [2^-10 .. 2^21]: column blocks are unchanged, while
+    each row block sees amax 2^21, X = 13 -- the two layouts differ."""
+    n = 32
+    x = np.zeros((n, n))
+    for c in range(n):
+        x[c, c] = 2.0 ** (c - 10)
+    _, sc, _ = bulk.cast_mx_f64(E4M3, x.ravel(), n, "ocp", axis="cols")
+    assert (sc.astype(int) - 127).tolist() == [c - 18 for c in range(n)]
+    y = np.tile(np.exp2(np.arange(n) - 10.0), (n, 1))          # row r = [2^-10 .. 2^21]
+    _, sc_c, _ = bulk.cast_mx_f64(E4M3, y.ravel(), n, "ocp", axis="cols")
+    _, sc_r, _ = bulk.cast_mx_f64(E4M3, y.ravel(), n, "ocp")
+    assert (sc_c.astype(int) - 127).tolist() == [c - 18 for c in range(n)]
+    assert (sc_r.astype(int) - 127).tolist() == [21 - 8] * n
+
+
+def test_mx_element_exponents_layouts():
+    rows, cols = 64, 96
+    X = np.arange((rows // 32) * cols)
+    got = bulk.mx_element_exponents(X, rows * cols, cols, "cols").reshape(rows, cols)
+    for r in range(rows):
+        for c in range(cols):
+            assert got[r, c] == X[(r // 32) * cols + c]
+    Xr = np.arange(rows * cols // 32)
+    got = bulk.mx_element_exponents(Xr, rows * cols, cols, "rows").reshape(rows, cols)
+    for r in range(rows):
+        for c in range(cols):
+            assert got[r, c] == Xr[r * (cols // 32) + c // 32]
+    with pytest.raises(ValueError):
+        bulk.mx_element_exponents(X, 48 * cols, cols, "cols")
+
+
 @pytest.mark.parametrize("fmt", FMTS, ids=["e4m3", "e5m2"])
 def test_stats_tier0_vs_tier1(fmt):
     rng = np.random.default_rng(5)
