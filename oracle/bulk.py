@@ -69,6 +69,14 @@ def cast_f64(fmt: Fmt, x: np.ndarray, K):
     qexp = np.maximum(e, c["emin"]) - c["mbits"]      # exponent of the grid spacing
     r = np.rint(np.ldexp(y, -qexp))                   # ties to even
     rv = np.minimum(np.ldexp(r, qexp), c["M"])        # saturate
+    code = _encode(c, rv, neg, finite, nan)
+    underflow = finite & (ax > 0) & (rv == 0)
+    return code, clip, underflow, ~finite
+
+
+def _encode(c, rv, neg, finite, nan):
+    """Codes of magnitudes rv that lie on the format's grid (<= max), with
+    the sign, +-Inf -> +-max and NaN -> the NaN code."""
     _, ex2 = np.frexp(rv)
     er = ex2.astype(np.int64) - 1
     normal = rv >= 2.0 ** c["emin"]
@@ -80,8 +88,40 @@ def cast_f64(fmt: Fmt, x: np.ndarray, K):
     code = np.where(finite, code, c["maxcode"])       # +-Inf saturate
     code = np.where(neg, code | c["sign"], code)
     code = np.where(nan, c["qnan"], code)
+    return code.astype(np.uint8)
+
+
+def cast_sr_f64(fmt: Fmt, x: np.ndarray, K, u: np.ndarray):
+    """Vectorised ``oracle.cast.sr_element``: u holds each element's uniform
+    32-bit integer.  y = |x| 2^K, y / q, its floor and the fraction t times
+    2^32 are all exact in binary64 (y has at most 24 significant bits), and
+    so is the comparison with u."""
+    c = fmt_consts(fmt)
+    x = np.asarray(x, dtype=np.float64)
+    K = np.asarray(K, dtype=np.int64)
+    nan = np.isnan(x)
+    finite = np.isfinite(x)
+    neg = np.signbit(x) & ~nan
+    ax = np.where(finite, np.abs(x), 0.0)
+    y = np.ldexp(ax, K)
+    clip = finite & (y > c["M"])
+    _, ex = np.frexp(y)
+    qexp = np.maximum(ex.astype(np.int64) - 1, c["emin"]) - c["mbits"]
+    s = np.ldexp(y, -qexp)
+    lo = np.floor(s)
+    up = np.asarray(u, dtype=np.float64) < np.ldexp(s - lo, 32)
+    rv = np.where(clip, c["M"], np.ldexp(lo + up, qexp))
+    code = _encode(c, rv, neg, finite, nan)
     underflow = finite & (ax > 0) & (rv == 0)
-    return code.astype(np.uint8), clip, underflow, ~finite
+    return code, clip, underflow, ~finite
+
+
+def cast_tensor_sr_f64(fmt: Fmt, x: np.ndarray, k: int, unscale_log2: int, seed: int, offset: int,
+                       tensor: int):
+    from .rng import sr_uniforms
+    u = sr_uniforms(seed, offset, tensor, np.asarray(x).size)
+    codes, clip, uf, nf = cast_sr_f64(fmt, x, k - unscale_log2, u)
+    return codes, counts_of(clip, uf, nf, amax_f64(x, unscale_log2), np.asarray(x).size)
 
 
 def amax_f64(x: np.ndarray, unscale_log2: int = 0) -> float:

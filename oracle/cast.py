@@ -134,6 +134,58 @@ def cast_element(fmt: Fmt, v: Val, K: int):
     return code, clip, underflow, False
 
 
+def sr_element(fmt: Fmt, v: Val, K: int, u: int):
+    """Stochastic rounding of one input value at exponent K (the value cast is
+    y = v * 2^K, exact), with u a uniform 32-bit integer.
+
+    Reading: the pages only say the rounding is unbiased at any single step
+    ([Drift, "The part I would rather not write"]) and that its damage sits in
+    the backward matmuls ([Drift, "What the measurements said"]).  Taken
+    here as the textbook rule: with lo <= |y| < lo + q the two neighbouring
+    grid points (q the grid spacing in |y|'s binade, or the subnormal spacing
+    below the normal range), t = (|y| - lo) / q, the magnitude rounds up to
+    lo + q iff u < t 2^32 -- probability ceil(t 2^32) / 2^32, which is t
+    whenever t has at most 32 fractional bits, so the expected value is y.
+    Above the largest finite value the result saturates (a clip, as in
+    ``cast_element``); non-finite inputs are coded as there.  Returns (code,
+    clip, underflow, nonfinite); underflow: nonzero and the drawn code is a
+    zero.
+    """
+    if v.kind == "nan":
+        return fmt.qnan, False, False, True
+    if v.kind == "inf":
+        return fmt.max_code(v.neg), False, False, True
+    y = v.mag * pow2(K)
+    if y > fmt.maxval:
+        return fmt.max_code(v.neg), True, False, False
+    if y == 0:
+        return fmt.encode(Val.num(v.neg, Fraction(0)), saturate=True), False, False, False
+    q = pow2(max(floor_log2(y), fmt.emin) - fmt.mbits)
+    lo = (y // q) * q
+    t = (y - lo) / q
+    mag = lo + q if u < t * 2 ** 32 else lo
+    code = fmt.encode(Val.num(v.neg, mag), saturate=True)
+    return code, False, mag == 0, False
+
+
+def cast_tensor_sr(fmt: Fmt, values, k: int, unscale_log2: int, seed: int, offset: int, tensor: int):
+    """Per-tensor stochastic-rounding cast of x * 2^-s at scale 2^k, element i
+    drawing ``oracle.rng.sr_uniform(seed, offset, tensor, i)``.  Returns
+    (codes, counts) as ``cast_tensor``."""
+    from .rng import sr_uniform
+    K = k - unscale_log2
+    codes, n_clip, n_uf, n_nf = [], 0, 0, 0
+    for i, v in enumerate(values):
+        c, cl, uf, nf = sr_element(fmt, v, K, sr_uniform(seed, offset, tensor, i))
+        codes.append(c)
+        n_clip += cl
+        n_uf += uf
+        n_nf += nf
+    counts = dict(n_finite=len(codes) - n_nf, n_clip=n_clip, n_underflow=n_uf,
+                  n_nonfinite=n_nf, amax=amax(values, unscale_log2))
+    return codes, counts
+
+
 def cast_tensor(fmt: Fmt, values, k: int, unscale_log2: int = 0):
     """Per-tensor cast with scale 2^k of the unscaled tensor x * 2^-s.
 
