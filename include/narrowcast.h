@@ -196,6 +196,24 @@ nc_status nc_cast_tensor(const nc_tensor *t, int32_t count, nc_dtype dtype, nc_f
                          const nc_scale_state *st, const nc_loss_scale *ls, nc_counts *out,
                          nc_stats *stats, void *ws, size_t ws_bytes, void *stream);
 
+/* Per-tensor cast with stochastic rounding ([Drift, "The part I would rather
+ * not write": unbiased at any single step]).  As nc_cast_tensor, except the
+ * rounding: with y = x * 2^(st[j].k - s) between grid neighbours lo <= |y| <
+ * lo + q and t = (|y| - lo) / q, the magnitude rounds up iff u < t * 2^32,
+ * u the element's uniform 32-bit integer -- word i % 4 of Philox4x32-10
+ * (Salmon et al., SC11) with key `seed` (low word first) and counter
+ * (i / 4, j, offset low word, offset high word), j the tensor's index in
+ * this call.  Pass a new `offset` (e.g. the step number) per call for fresh
+ * draws; the same (seed, offset) reproduces the codes bit for bit.  |y| >
+ * max saturates (a clip); n_underflow counts finite nonzero elements whose
+ * drawn code is a zero.  Counts and next-step amax as nc_cast_tensor; no
+ * statistics (nc_cast_stats measures any codes).  Bytes per element: in
+ * 4|2, out 1. */
+nc_status nc_cast_tensor_sr(const nc_tensor *t, int32_t count, nc_dtype dtype, nc_fmt fmt,
+                            const nc_scale_state *st, const nc_loss_scale *ls, uint64_t seed,
+                            uint64_t offset, nc_counts *out, void *ws, size_t ws_bytes,
+                            void *stream);
+
 /* MX block-scaled cast ([Drift, "What the measurements said"]): blocks of
  * 32 elements (consecutive in a row, or in a column: mx_axis) share X from
  * the block's finite amax by `rule`; codes = RNE-sat(x * 2^-X), scales =

@@ -73,3 +73,15 @@ def sr_uniform(seed: int, offset: int, tensor: int, i: int) -> int:
     """Tier 0 form of ``sr_uniforms`` for one element."""
     return philox4x32((i >> 2, tensor, offset & MASK, (offset >> 32) & MASK),
                       (seed & MASK, (seed >> 32) & MASK))[i & 3]
+
+
+def sr_uniforms_at(seed: int, offset: int, tensor: int, idx: np.ndarray) -> np.ndarray:
+    """``sr_uniforms`` at the element indices idx only (sampled checks of
+    large tensors)."""
+    idx = np.asarray(idx, dtype=np.uint64)
+    b = idx >> np.uint64(2)
+    z = np.zeros(idx.size, dtype=np.uint64)
+    words = philox4x32_np(b & np.uint64(MASK), z + np.uint64(tensor & MASK), z + np.uint64(offset & MASK),
+                          z + np.uint64((offset >> 32) & MASK), seed & MASK, (seed >> 32) & MASK)
+    w = np.stack(words, axis=1)
+    return w[np.arange(idx.size), (idx & np.uint64(3)).astype(np.int64)].astype(np.uint32)

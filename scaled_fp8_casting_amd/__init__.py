@@ -180,6 +180,18 @@ def nc_cast_tensor(xs: Sequence[torch.Tensor], codes: Sequence[torch.Tensor], fm
                                       _ptr(ws), ws.numel(), _stream(stream)), "nc_cast_tensor")
 
 
+def nc_cast_tensor_sr(xs: Sequence[torch.Tensor], codes: Sequence[torch.Tensor], fmt, st: torch.Tensor,
+                      out: torch.Tensor, seed: int, offset: int, ls: Optional[torch.Tensor] = None,
+                      ws: Optional[torch.Tensor] = None, stream=None):
+    desc, count = tensors(xs, codes)
+    dt = _dtype_code(xs[0]) if xs else NC_F32
+    f = FMT[fmt] if isinstance(fmt, str) else fmt
+    ws = _ws(ws, desc, count)
+    _check(_lib.load().nc_cast_tensor_sr(desc, count, dt, f, _ptr(st), _ptr(ls), seed & (2 ** 64 - 1),
+                                         offset & (2 ** 64 - 1), _ptr(out), _ptr(ws), ws.numel(),
+                                         _stream(stream)), "nc_cast_tensor_sr")
+
+
 def nc_cast_mx(xs: Sequence[torch.Tensor], codes: Sequence[torch.Tensor], scales: Sequence[torch.Tensor],
                cols: Sequence[int], fmt, rule, out: torch.Tensor, stats: Optional[torch.Tensor] = None,
                ws: Optional[torch.Tensor] = None, stream=None, axis: str = "rows"):

@@ -48,7 +48,7 @@ class NcPolicy(ctypes.Structure):
                                        "ls_log2_min", "ls_log2_max")] + [("ema_alpha", ctypes.c_float)]
 
 
-EXPORTS = ("nc_amax", "nc_scale_update", "nc_cast_tensor", "nc_cast_mx", "nc_dequant",
+EXPORTS = ("nc_amax", "nc_scale_update", "nc_cast_tensor", "nc_cast_tensor_sr", "nc_cast_mx", "nc_dequant",
            "nc_cast_stats", "nc_workspace_bytes", "nc_status_string")
 
 _lib = None
@@ -68,6 +68,8 @@ def load():
     lib.nc_scale_update.argtypes = [POINTER(NcPolicy), c_int32, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p]
     lib.nc_cast_tensor.argtypes = [T, c_int32, c_int32, c_int32, c_void_p, c_void_p, c_void_p, c_void_p,
                                    c_void_p, c_size_t, c_void_p]
+    lib.nc_cast_tensor_sr.argtypes = [T, c_int32, c_int32, c_int32, c_void_p, c_void_p, c_uint64, c_uint64,
+                                      c_void_p, c_void_p, c_size_t, c_void_p]
     lib.nc_cast_mx.argtypes = [T, c_int32, c_int32, c_int32, c_int32, c_void_p, c_void_p, c_void_p,
                                c_size_t, c_void_p]
     lib.nc_dequant.argtypes = [T, c_int32, c_int32, c_void_p, POINTER(c_void_p), c_int32, c_void_p]
@@ -77,7 +79,8 @@ def load():
     lib.nc_workspace_bytes.restype = c_size_t
     lib.nc_status_string.argtypes = [c_int32]
     lib.nc_status_string.restype = c_char_p
-    for name in ("nc_amax", "nc_scale_update", "nc_cast_tensor", "nc_cast_mx", "nc_dequant", "nc_cast_stats"):
+    for name in ("nc_amax", "nc_scale_update", "nc_cast_tensor", "nc_cast_tensor_sr", "nc_cast_mx", "nc_dequant",
+                 "nc_cast_stats"):
         getattr(lib, name).restype = c_int32
     _lib = lib
     return lib

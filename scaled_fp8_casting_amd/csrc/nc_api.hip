@@ -198,6 +198,25 @@ nc_status nc_cast_tensor(const nc_tensor* t, int32_t count, nc_dtype dtype, nc_f
   });
 }
 
+nc_status nc_cast_tensor_sr(const nc_tensor* t, int32_t count, nc_dtype dtype, nc_fmt fmt,
+                            const nc_scale_state* st, const nc_loss_scale* ls, uint64_t seed, uint64_t offset,
+                            nc_counts* out, void* ws, size_t ws_bytes, void* stream) {
+  if (!valid_dtype(dtype) || !valid_fmt(fmt)) return NC_E_UNSUPPORTED;
+  nc_status s = check_tensors(t, count, true, true, false);
+  if (s != NC_OK) return s;
+  if (count == 0) return NC_OK;
+  if (out == nullptr || st == nullptr) return NC_E_ARG;
+  if ((s = check_ws(t, count, ws, ws_bytes)) != NC_OK) return s;
+  const int64_t tile = tile_elems(in_bytes(dtype), kCastVecs);
+  return for_batches(t, count, tile, nullptr, [&](const SegBatch& b) {
+    const Ws w = ws_of(b, ws);
+    nc_status r = hip_status(launch_cast_sr(b, dtype, fmt, st, ls, seed, offset, w,
+                                            Launch{b.tile0[b.count], (hipStream_t)stream}));
+    if (r == NC_OK) r = hip_status(launch_reduce(b, w, out, nullptr, ls, true, (hipStream_t)stream));
+    return r;
+  });
+}
+
 nc_status nc_cast_mx(const nc_tensor* t, int32_t count, nc_dtype dtype, nc_fmt fmt, nc_mx_rule rule,
                      nc_counts* out, nc_stats* stats, void* ws, size_t ws_bytes, void* stream) {
   if (!valid_dtype(dtype) || !valid_fmt(fmt)) return NC_E_UNSUPPORTED;

@@ -127,6 +127,181 @@ k_cast_pt(const SegBatch b, const nc_scale_state* __restrict__ st,
 }
 
 // ---------------------------------------------------------------------------
+// Stochastic-rounding cast ([Drift, "The part I would rather not write"]:
+// unbiased at any single step).
+//
+// Uniforms: Philox4x32-10 (Salmon, Moraes, Dror, Shaw, "Parallel Random
+// Numbers: As Easy as 1, 2, 3", SC11): ten rounds, each two 32 x 32 -> 64-bit
+// products of counter words 0 and 2 with the generator's multipliers, whose
+// high halves are xored with the other counter words and the key; the key
+// is bumped by two Weyl constants between rounds.  Element i of tensor j
+// reads word i % 4 of the block at counter (i / 4, j, offset lo, offset hi)
+// under key (seed lo, seed hi).  The key schedule is the same for every
+// lane (scalar registers); a block costs 20 multiplies for 4 elements.
+__device__ __forceinline__ void philox10(uint32_t (&c)[4], uint32_t k0, uint32_t k1) {
+#pragma unroll
+  for (int r = 0; r < 10; ++r) {
+    const uint64_t p0 = (uint64_t)c[0] * 0xD2511F53u;
+    const uint64_t p1 = (uint64_t)c[2] * 0xCD9E8D57u;
+    const uint32_t n0 = (uint32_t)(p1 >> 32) ^ c[1] ^ k0;
+    const uint32_t n2 = (uint32_t)(p0 >> 32) ^ c[3] ^ k1;
+    c[0] = n0;
+    c[1] = (uint32_t)p1;
+    c[2] = n2;
+    c[3] = (uint32_t)p0;
+    k0 += 0x9E3779B9u;
+    k1 += 0xBB67AE85u;
+  }
+}
+
+struct SrKey {
+  uint32_t k0, k1;    // seed
+  uint32_t j;         // tensor index in the call
+  uint32_t o0, o1;    // offset
+};
+
+// The four uniforms of block `blk` (elements 4 blk .. 4 blk + 3).
+__device__ __forceinline__ void sr_block(uint32_t blk, const SrKey& key, uint32_t (&r)[4]) {
+  r[0] = blk;
+  r[1] = key.j;
+  r[2] = key.o0;
+  r[3] = key.o1;
+  philox10(r, key.k0, key.k1);
+}
+
+// Stochastic rounding of one |x| (bits ax, finite, |x| 2^K <= max) at
+// exponent K with uniform u, as m * 2^eq (m <= 2^(MB+1), exact in fp32).
+// y = S 2^lsb exactly (S the fp32 significand); the grid spacing at y is
+// 2^eq with eq = max(binade(y), EMIN) - MB; the d = eq - lsb low bits of S
+// are discarded.  With W = S 2^32, floor(W / 2^d) holds the kept part in its
+// high word and F = floor(t 2^32) in its low word; `sticky` is whether t 2^32
+// has a fraction (only when d > 32).  The magnitude rounds up iff u < t 2^32,
+// i.e. u < F, or u == F with a fraction.  d <= 0: y is on the grid (m = S
+// 2^-d, no draw).  Selects only (no branches); out-of-range lanes compute
+// values their caller discards, with every shift kept in range.
+template <int FMT>
+__device__ __forceinline__ float sr_value(uint32_t ax, int K, uint32_t u, uint32_t* m_out) {
+  using F = Fp8<FMT>;
+  const uint32_t E = ax >> 23;
+  const uint32_t S = E ? ((ax & 0x7FFFFFu) | 0x800000u) : ax;
+  const int lsb = (E ? (int)E : 1) - 150 + K;
+  const int ey = (31 - __clz(S | 1u)) + lsb;
+  const int eq = max(ey, F::EMIN) - F::MB;
+  const int d = eq - lsb;
+  const uint64_t W = (uint64_t)S << 32;
+  const uint32_t dd = (uint32_t)min(max(d, 0), 63);
+  const uint64_t Q = W >> dd;
+  const uint32_t Fr = (uint32_t)Q;
+  const bool sticky = (W & ((1ull << dd) - 1ull)) != 0;
+  const uint32_t up = (u < Fr || (sticky && u == Fr)) ? 1u : 0u;
+  const uint32_t m = d < 0 ? S << (uint32_t)min(-d, 31) : (uint32_t)(Q >> 32) + up;
+  *m_out = m;
+  return __builtin_amdgcn_ldexpf((float)m, eq);
+}
+
+// Four elements -> four codes (byte i = element i), counts and amax to acc.
+// Clips saturate; non-finite elements are rewritten by the caller's uniform
+// branch (as in the round-to-nearest cast).
+template <int FMT>
+__device__ __forceinline__ uint32_t sr4(const uint32_t* xb, const CastParams& p, const uint32_t (&r)[4],
+                                        Acc& acc) {
+  constexpr float kMaxF = 1.75f * (float)(1u << Fp8<FMT>::EMAX);
+  float v[4];
+  uint32_t sgn = 0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint32_t ax = xb[i] & kAbsMask;
+    uint32_t m;
+    const float val = sr_value<FMT>(ax, p.K, r[i], &m);
+    const bool big = ax > p.t_clip;            // clips and non-finite
+    acc.n_big += big ? 1u : 0u;
+    acc.n_uf += (!big && ax != 0u && m == 0u) ? 1u : 0u;
+    v[i] = big ? kMaxF : val;
+    sgn |= (xb[i] >> 31) << (8 * i + 7);
+  }
+  int w = cvt_pair<FMT, false>(v[0], v[1], 0);
+  w = cvt_pair<FMT, true>(v[2], v[3], w);
+  return (uint32_t)w | sgn;
+}
+
+template <int FMT, int DT>
+NC_STREAM_KERNEL
+k_cast_sr(const SegBatch b, const nc_scale_state* __restrict__ st, const nc_loss_scale* __restrict__ ls,
+          uint64_t seed, uint64_t offset, CountSlot* __restrict__ slots) {
+  constexpr int VEC = In<DT>::VEC;
+  constexpr int U = kCastVecs;
+  constexpr int64_t TILE = (int64_t)kThreads * VEC * U;
+  __shared__ uint32_t lds[kRows * 4];
+  const int64_t tile = blockIdx.x;
+  const int s = seg_of(b.tile0, b.count, tile);
+  const Seg& g = b.s[s];
+  const int64_t e0 = (tile - b.tile0[s]) * TILE;
+  const int rem = tile_len<TILE>(b, s, tile);
+  const bool full = rem == (int)TILE;
+  const u32x4* src = reinterpret_cast<const u32x4*>(static_cast<const uint8_t*>(g.x) + e0 * In<DT>::BYTES);
+  u32x4 v[U];
+  if (full) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) v[u] = ld_stream(src + u * kThreads + threadIdx.x);
+  }
+  __builtin_amdgcn_sched_barrier(0);
+  const int K = st[b.first + s].k - (ls ? ls->s_log2 : 0);
+  const CastParams p = cast_params<FMT>(K);
+  const SrKey key{(uint32_t)seed, (uint32_t)(seed >> 32), (uint32_t)(b.first + s), (uint32_t)offset,
+                  (uint32_t)(offset >> 32)};
+  Acc acc;
+  acc.reset();
+  uint8_t* dst = g.codes + e0;
+  if (full) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int vi = u * kThreads + threadIdx.x;
+      // element index < 2^34, so its block index fits 32 bits
+      const uint32_t blk = (uint32_t)((e0 + (int64_t)vi * VEC) >> 2);
+      uint32_t xb[VEC], w[VEC / 4];
+      unpack<DT>(v[u], xb);
+      uint32_t m = 0;
+#pragma unroll
+      for (int j = 0; j < VEC / 4; ++j) {
+        uint32_t r[4];
+        sr_block(blk + j, key, r);
+        w[j] = sr4<FMT>(xb + 4 * j, p, r, acc);
+      }
+#pragma unroll
+      for (int i = 0; i < VEC; ++i) m = max(m, xb[i] & kAbsMask);
+      if (__ballot(m > kMaxFinite) == 0) {       // wave-uniform: no Inf/NaN here
+        acc.amax = max(acc.amax, m);
+      } else {
+        uint32_t mf = 0;
+#pragma unroll
+        for (int i = 0; i < VEC; ++i) mf = max(mf, finite_mag(xb[i] & kAbsMask, acc));
+        acc.amax = max(acc.amax, mf);
+#pragma unroll
+        for (int j = 0; j < VEC / 4; ++j) w[j] = fix_nonfinite4<FMT>(w[j], xb + 4 * j);
+      }
+      if constexpr (DT == NC_F32) st_stream(reinterpret_cast<uint32_t*>(dst) + vi, w[0]);
+      else st_stream(reinterpret_cast<u32x2*>(dst) + vi, u32x2{w[0], w[1]});
+    }
+  } else {
+    for (int base = 0; base < rem; base += kThreads) {
+      const int i = base + (int)threadIdx.x;
+      const bool act = i < rem;
+      const int64_t e = e0 + i;
+      uint32_t xb[4] = {act ? load_one<DT>(g.x, e) : 0u, 0u, 0u, 0u};
+      uint32_t r[4];
+      sr_block((uint32_t)(e >> 2), key, r);
+      r[0] = r[e & 3];                         // this element's word
+      uint32_t q = sr4<FMT>(xb, p, r, acc) & 0xFFu;
+      const uint32_t ax = xb[0] & kAbsMask;
+      acc.amax = max(acc.amax, finite_mag(ax, acc));
+      if (ax > kMaxFinite) q = nonfinite_code<FMT>(xb[0]);
+      if (act) dst[i] = (uint8_t)q;
+    }
+  }
+  write_count_slot(acc, slots + tile, lds);
+}
+
+// ---------------------------------------------------------------------------
 // MX: shared block exponent X ([Drift, "What the measurements said"]) from
 // the finite amax a of each 32-element block (a = 0 -> -127).
 template <int FMT, int RULE>
@@ -438,6 +613,14 @@ hipError_t cast_mx_t(const SegBatch& b, int rule, bool stats, const Ws& w, const
   return cast_mx_r<FMT, DT, NC_MX_CEIL>(b, stats, w, l);
 }
 
+template <int FMT, int DT>
+hipError_t cast_sr_t(const SegBatch& b, const nc_scale_state* st, const nc_loss_scale* ls, uint64_t seed,
+                     uint64_t offset, const Ws& w, const Launch& l) {
+  hipLaunchKernelGGL((k_cast_sr<FMT, DT>), dim3((uint32_t)l.grid), dim3(kThreads), 0, l.stream, b, st, ls, seed,
+                     offset, w.cnt1);
+  return hipGetLastError();
+}
+
 template <int FMT, int DT, int RULE>
 hipError_t cast_mx_col_r(const SegBatch& b, bool stats, const Ws& w, const Launch& l) {
   if (stats)
@@ -491,6 +674,15 @@ hipError_t launch_cast_mx_col(const SegBatch& b, int dtype, int fmt, int rule, b
                            : cast_mx_col_t<NC_E4M3, NC_BF16>(b, rule, stats, w, l);
   return dtype == NC_F32 ? cast_mx_col_t<NC_E5M2, NC_F32>(b, rule, stats, w, l)
                          : cast_mx_col_t<NC_E5M2, NC_BF16>(b, rule, stats, w, l);
+}
+
+hipError_t launch_cast_sr(const SegBatch& b, int dtype, int fmt, const nc_scale_state* st,
+                          const nc_loss_scale* ls, uint64_t seed, uint64_t offset, const Ws& w, const Launch& l) {
+  if (fmt == NC_E4M3)
+    return dtype == NC_F32 ? cast_sr_t<NC_E4M3, NC_F32>(b, st, ls, seed, offset, w, l)
+                           : cast_sr_t<NC_E4M3, NC_BF16>(b, st, ls, seed, offset, w, l);
+  return dtype == NC_F32 ? cast_sr_t<NC_E5M2, NC_F32>(b, st, ls, seed, offset, w, l)
+                         : cast_sr_t<NC_E5M2, NC_BF16>(b, st, ls, seed, offset, w, l);
 }
 
 }  // namespace nc

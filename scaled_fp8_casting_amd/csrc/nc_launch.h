@@ -71,6 +71,8 @@ hipError_t launch_cast_pt(const SegBatch& b, int dtype, int fmt, const nc_scale_
                           const nc_loss_scale* ls, bool stats, const Ws& w, const Launch& l);
 hipError_t launch_cast_mx(const SegBatch& b, int dtype, int fmt, int rule, bool stats, const Ws& w,
                           const Launch& l);
+hipError_t launch_cast_sr(const SegBatch& b, int dtype, int fmt, const nc_scale_state* st,
+                          const nc_loss_scale* ls, uint64_t seed, uint64_t offset, const Ws& w, const Launch& l);
 hipError_t launch_stats(const SegBatch& b, int dtype, int fmt, const nc_scale_state* st,
                         const nc_loss_scale* ls, const Ws& w, const Launch& l);
 // Column-block MX forms of the MX cast, dequant and statistics pass; the

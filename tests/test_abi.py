@@ -29,9 +29,10 @@ def lib():
     return _lib.load()
 
 
-def test_header_declares_the_six_calls():
+def test_header_declares_the_calls():
     fns = declared_functions()
-    for name in ("nc_amax", "nc_scale_update", "nc_cast_tensor", "nc_cast_mx", "nc_dequant", "nc_cast_stats"):
+    for name in ("nc_amax", "nc_scale_update", "nc_cast_tensor", "nc_cast_tensor_sr", "nc_cast_mx", "nc_dequant",
+                 "nc_cast_stats"):
         assert name in fns
     assert set(fns) == set(_lib.EXPORTS)
 
@@ -113,6 +114,13 @@ def test_argument_checks_before_any_launch(lib):
     assert lib.nc_cast_tensor(_desc((A, A + 1, 8, 0, None)), 1, 0, 0, A, None, A, None, A, W, None) == _lib.NC_E_ALIGN
     assert lib.nc_cast_tensor(_desc((A, A, 8, 0, None)), 1, 0, 0, None, None, A, None, A, W, None) == _lib.NC_E_ARG
     assert lib.nc_cast_tensor(_desc((A, A, 8, 0, None)), 1, 0, 2, A, None, A, None, A, W, None) == _lib.NC_E_UNSUPPORTED
+    # stochastic-rounding cast: the per-tensor cast's checks
+    assert lib.nc_cast_tensor_sr(_desc((A, A + 1, 8, 0, None)), 1, 0, 0, A, None, 1, 2, A, A, W, None) == _lib.NC_E_ALIGN
+    assert lib.nc_cast_tensor_sr(_desc((A, A, 8, 0, None)), 1, 0, 0, None, None, 1, 2, A, A, W, None) == _lib.NC_E_ARG
+    assert lib.nc_cast_tensor_sr(_desc((A, A, 8, 0, None)), 1, 0, 0, A, None, 1, 2, None, A, W, None) == _lib.NC_E_ARG
+    assert lib.nc_cast_tensor_sr(_desc((A, A, 8, 0, None)), 1, 2, 0, A, None, 1, 2, A, A, W, None) == _lib.NC_E_UNSUPPORTED
+    assert lib.nc_cast_tensor_sr(_desc((A, A, 8, 0, None)), 1, 0, 0, A, None, 1, 2, A, None, W, None) == _lib.NC_E_WORKSPACE
+    assert lib.nc_cast_tensor_sr(None, 0, 0, 0, None, None, 1, 2, None, None, 0, None) == _lib.NC_OK
     # workspace size
     d = _desc((A, A, 10000, 0, None))
     need = lib.nc_workspace_bytes(d, 1)

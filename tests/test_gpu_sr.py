@@ -1,0 +1,155 @@
+"""GPU parity of the stochastic-rounding cast against the oracle: bit-exact
+codes and counts for the same generator draws, the tensor index in the
+counter, reproducibility, unbiasedness, and the full-size workload."""
+
+import os
+from fractions import Fraction
+
+import numpy as np
+import pytest
+import torch
+
+import scaled_fp8_casting_amd as nc
+from oracle import E4M3, E5M2, bulk, rng
+from oracle.cast import scale_exponent
+import workloads
+from tests._gpu import assert_counts, codes_like, dev_bf16, dev_f32, host_u8, state_with_k
+
+pytestmark = pytest.mark.gpu
+FMTS = [("e4m3", E4M3), ("e5m2", E5M2)]
+
+
+def _input(dtype, n, seed):
+    r = np.random.default_rng(seed)
+    x = (r.standard_t(3, n) * 10.0 ** r.uniform(-4, 4, n)).astype(np.float32)
+    x[:8] = [0.0, -0.0, np.inf, -np.inf, np.nan, 1e-45, -3e38, 448.0]
+    if dtype == "bf16":
+        bits = workloads.to_bf16_bits(x.astype(np.float64))
+        return dev_bf16(bits), bulk.bf16_bits_to_f64(bits)
+    return dev_f32(x), x.astype(np.float64)
+
+
+def _sr(xds, fmt, ks, seed, offset, ls=None):
+    codes = [codes_like(x.numel()) for x in xds]
+    out = nc.new_counts(len(xds))
+    nc.nc_cast_tensor_sr(xds, codes, fmt, state_with_k(ks), out, seed, offset, ls=ls)
+    torch.cuda.synchronize()
+    return [host_u8(c) for c in codes], nc.counts_list(out)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("name,fmt", FMTS)
+@pytest.mark.parametrize("k,s", [(0, 0), (9, 0), (-20, 0), (30, 16), (127, 0)])
+def test_sr_parity(dtype, name, fmt, k, s):
+    """Several tiles and a ragged tail; seeds and offsets with high words."""
+    n = 3 * 8192 + 77
+    xd, x64 = _input(dtype, n, 100 + k)
+    seed, offset = 0x9E3779B97F4A7C15, (k & 0xFF) << 40 | 3
+    ls = nc.new_loss_scale(s) if s else None
+    codes, counts = _sr([xd], name, [k], seed, offset, ls=ls)
+    want, wn = bulk.cast_tensor_sr_f64(fmt, x64, k, s, seed, offset, 0)
+    bad = np.flatnonzero(codes[0] != want)
+    assert bad.size == 0, [(int(i), x64[i], hex(codes[0][i]), hex(want[i])) for i in bad[:5]]
+    assert_counts(counts[0], wn)
+    assert counts[0]["amax"] == wn["amax"]
+
+
+def test_sr_tensor_index_and_launches():
+    """40 tensors (two launches; tensor j draws with counter word j, its
+    index in the call), ragged sizes, one empty."""
+    r = np.random.default_rng(3)
+    sizes = [int(v) for v in r.integers(1, 30000, 40)]
+    sizes[5] = 0
+    ins = [_input("f32", m, 7 + j) if m else (dev_f32(np.zeros(0, np.float32)), np.zeros(0)) for j, m in
+           enumerate(sizes)]
+    ks = [int(v) for v in r.integers(-10, 20, 40)]
+    codes, counts = _sr([d for d, _ in ins], "e4m3", ks, 77, 5)
+    for j, ((_, x64), k) in enumerate(zip(ins, ks)):
+        want, wn = bulk.cast_tensor_sr_f64(E4M3, x64, k, 0, 77, 5, j)
+        assert np.array_equal(codes[j], want), j
+        if sizes[j]:
+            assert_counts(counts[j], wn)
+
+
+def test_sr_reproducible_and_fresh():
+    xd, x64 = _input("bf16", 50000, 4)
+    a, _ = _sr([xd], "e4m3", [3], 1, 10)
+    b, _ = _sr([xd], "e4m3", [3], 1, 10)
+    c, _ = _sr([xd], "e4m3", [3], 1, 11)
+    d, _ = _sr([xd, xd], "e4m3", [3, 3], 1, 10)
+    assert np.array_equal(a[0], b[0])
+    assert np.array_equal(d[0], a[0]) and not np.array_equal(d[1], a[0])    # tensor index matters
+    moved = np.count_nonzero(a[0] != c[0])
+    assert moved > 1000                                                      # a new offset redraws
+    assert np.array_equal(c[0], bulk.cast_tensor_sr_f64(E4M3, x64, 3, 0, 1, 11, 0)[0])
+
+
+@pytest.mark.parametrize("name,fmt", FMTS)
+def test_sr_unbiased_on_device(name, fmt):
+    """[Drift, "The part I would rather not write"]: unbiased at any single
+    step.  64 draws (offsets) of 2^16 copies of each value: the mean decoded
+    value is within 5 standard errors of the value; every draw matches the
+    oracle."""
+    vals = np.array([1.0 + 3 * 2 ** -8, 0.0173, 1.7 * 2.0 ** -11, 200.3], dtype=np.float32)
+    n = 1 << 16
+    x = np.repeat(vals, n)
+    xd = dev_f32(x)
+    tab = bulk.decode_table(fmt)
+    sums = np.zeros(vals.size)
+    for off in range(64):
+        codes, _ = _sr([xd], name, [0], 12345, off)
+        if off < 4:
+            assert np.array_equal(codes[0], bulk.cast_tensor_sr_f64(fmt, x.astype(np.float64), 0, 0, 12345, off, 0)[0])
+        sums += tab[codes[0]].reshape(vals.size, n).sum(axis=1)
+    mean = sums / (64 * n)
+    for v, m in zip(vals.astype(np.float64), mean):
+        lo = tab[bulk.cast_sr_f64(fmt, np.array([v]), 0, np.array([2 ** 32 - 1], np.uint32))[0]][0]
+        hi = tab[bulk.cast_sr_f64(fmt, np.array([v]), 0, np.array([0], np.uint32))[0]][0]
+        t = (v - lo) / (hi - lo)
+        se = (hi - lo) * np.sqrt(t * (1 - t) / (64 * n))
+        assert abs(m - v) < 5 * se, (v, m, se)
+
+
+def _procs():
+    return max(1, min(16, len(os.sched_getaffinity(0))))
+
+
+def test_sr_full_size_sampled():
+    """The 2^30-element heavy-tailed bf16 workload in the benchmark's launch
+    shape: 2^20 sampled codes against the oracle (their own draws); the
+    deterministic counts exactly (clip, finite, non-finite, amax); the
+    underflow count within 6 standard deviations of its exact expectation
+    (a sum of independent Bernoulli draws)."""
+    rows, cols = 262144, 4096
+    n = rows * cols
+    bits = workloads.heavy_tailed_parallel(rows, cols, procs=_procs(), context="spawn").reshape(-1)
+    x = torch.from_numpy(bits.view(np.int16)).cuda().view(torch.bfloat16)
+    vals = bulk.bf16_bits_to_f64(np.arange(65536, dtype=np.uint16))
+    hist = np.bincount(bits, minlength=65536)
+    fin = np.isfinite(vals)
+    amax = float(np.max(np.abs(vals[(hist > 0) & fin])))
+    k = scale_exponent(E4M3, Fraction(amax))
+    codes = torch.empty(n, dtype=torch.uint8, device="cuda")
+    out = nc.new_counts(1)
+    seed, offset = 2024, 7
+    nc.nc_cast_tensor_sr([x], [codes], "e4m3", state_with_k([k]), out, seed, offset)
+    torch.cuda.synchronize()
+    idx = np.random.default_rng(9).choice(n, 1 << 20, replace=False)
+    u = rng.sr_uniforms_at(seed, offset, 0, idx)
+    want = bulk.cast_sr_f64(E4M3, vals[bits[idx]], k, u)[0]
+    got = codes.cpu().numpy()[idx]
+    assert np.array_equal(got, want)
+    c = nc.counts_list(out)[0]
+    _, clip, _, nf = bulk.cast_f64(E4M3, vals, k)
+    assert c["n_clip"] == int(hist[clip].sum()) and c["n_nonfinite"] == int(hist[nf].sum())
+    assert c["n_finite"] == n - c["n_nonfinite"] and c["amax"] == amax
+    # P(code 0) per pattern: y below the smallest subnormal q rounds up with
+    # probability ceil(t 2^32) / 2^32, t = y / q
+    y = np.ldexp(np.where(fin, np.abs(vals), 0.0), k)
+    q = 2.0 ** (E4M3.emin - E4M3.mbits)
+    small = fin & (y > 0) & (y < q)
+    p_up = np.ceil(np.ldexp(y / q, 32)) / 2.0 ** 32
+    p0 = np.where(small, 1 - p_up, 0.0)
+    mean = float((hist * p0).sum())
+    sd = float(np.sqrt((hist * p0 * (1 - p0)).sum()))
+    assert abs(c["n_underflow"] - mean) <= 6 * sd + 1, (c["n_underflow"], mean, sd)

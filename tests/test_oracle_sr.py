@@ -168,3 +168,9 @@ def test_uniform_words():
     h = np.bincount(u >> 28, minlength=16)
     chi2 = float(((h - 4096.0) ** 2 / 4096.0).sum())
     assert chi2 < 45.0
+
+
+def test_sampled_uniforms_match_the_full_draw():
+    u = rng.sr_uniforms(11, 2 ** 35 + 1, 4, 1001)
+    idx = np.array([0, 1, 2, 3, 4, 999, 1000, 517, 518])
+    assert np.array_equal(rng.sr_uniforms_at(11, 2 ** 35 + 1, 4, idx), u[idx])
