@@ -17,7 +17,8 @@ timed region.  One step is one pass of the whole cast path over it:
   8. nc_cast_stats    error/bias statistics, MX                 (2 + 1 + 1/32)
 
 Beside the step (not part of it) the same JSON line reports the casts with
-fused statistics, a plain device copy of the cast's byte count, and one
+fused statistics, the stochastic-rounding cast, the MX cast, dequant and
+statistics with blocks down the columns, a plain device copy of the cast's byte count, and one
 delayed-scaling step of loss-scaled Llama-7B-shaped fp32 gradients (225
 tensors, 6.6G elements, fused 2^-16 unscale).
 
@@ -81,7 +82,10 @@ def source_hash():
 KERNEL_SIG = {"amax": "k_amax<1>", "cast_tensor": "k_cast_pt<0, 1, false>",
               "cast_mx": "k_cast_mx<0, 1, 0, false>", "dequant_pt": "k_dequant<0, false>",
               "dequant_mx": "k_dequant<0, true>", "stats_pt": "k_stats<0, 1, false>",
-              "stats_mx": "k_stats<0, 1, true>"}
+              "stats_mx": "k_stats<0, 1, true>",
+              "cast_tensor+stats": "k_cast_pt<0, 1, true>", "cast_mx+stats": "k_cast_mx<0, 1, 0, true>",
+              "cast_mx_cols": "k_cast_mx_col<0, 1, 0, false>", "dequant_mx_cols": "k_dequant_col<0>",
+              "stats_mx_cols": "k_stats_col<0, 1>", "cast_tensor_sr": "k_cast_sr<0, 1>"}
 TRAFFIC_JSON = os.path.join(ROOT, "profiles", "traffic.json")
 
 
@@ -361,6 +365,16 @@ def main():
                                                         stats=fused_pt, ws=ws), 3 * n),
         "cast_mx+stats": (lambda: nc.nc_cast_mx([x], [codes_mx], [scales], [COLS], "e4m3", "ocp", bufs["cmx"],
                                                 stats=fused_mx, ws=ws), 3 * n + n // 32),
+        # stochastic rounding (Philox4x32-10 draws, one 32-bit uniform per element)
+        "cast_tensor_sr": (lambda: nc.nc_cast_tensor_sr([x], [codes_pt], "e4m3", bufs["st"], bufs["cpt"], 2024, 7,
+                                                        ws=ws), 3 * n),
+        # MX with blocks of 32 rows of a column (the transposed operand's layout)
+        "cast_mx_cols": (lambda: nc.nc_cast_mx([x], [codes_mx], [scales], [COLS], "e4m3", "ocp", bufs["cmx"],
+                                               ws=ws, axis="cols"), 3 * n + n // 32),
+        "dequant_mx_cols": (lambda: nc.nc_dequant([codes_mx], [y_mx], "e4m3", scales=[scales], cols=[COLS],
+                                                  axis="cols"), 3 * n + n // 32),
+        "stats_mx_cols": (lambda: nc.nc_cast_stats([x], [codes_mx], "e4m3", bufs["smx"], ws, scales=[scales],
+                                                   cols=[COLS], axis="cols"), 3 * n + n // 32),
     }
     if not a.copy_probe:     # (a counter run keeps the probe's copies the only large ones)
         cp_src = torch.empty(3 * n // 2, dtype=torch.uint8, device=dev).fill_(1)
@@ -379,7 +393,7 @@ def main():
         ms = float(np.mean([e0.elapsed_time(e1) for e0, e1 in ev]))
         gbps = nbytes / (ms * 1e-3) / 1e9
         out["beside_step"][nm] = dict(ms=round(ms, 4), gbps=round(gbps, 1), frac=round(gbps / HBM_PEAK_GBPS, 4),
-                                      gelem_s=round(n / (ms * 1e-3) / 1e9, 2))
+                                      gelem_s=round(n / (ms * 1e-3) / 1e9, 2), traffic=traffic_for(nm, src))
     extras.clear()
     if not a.no_llama:
         out["beside_step"]["llama_unscale_cast"] = llama_unscale_cast(nc, torch, workloads)

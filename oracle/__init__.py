@@ -14,6 +14,8 @@ Two tiers implement the same definitions:
   binary64, where every step used is exact for the inputs it is given (fp32 and
   bf16 values times powers of two, rounding to an integer with ``np.rint``).
   Sums are formed exactly and rounded once.
+* ``oracle.rng`` -- Philox4x32-10, the counter-based generator whose words the
+  stochastic-rounding cast draws, written from its published definition.
 
 Sources, cited by page title and section throughout:
 
@@ -33,7 +35,8 @@ Sources, cited by page title and section throughout:
 Pinning: every function here is checked by ``tests/test_oracle_*.py`` against
 facts fixed independently of this code (constants printed on the pages, closed
 forms, library routines such as numpy's float16 and torch's float8 casts,
-brute force and invariants).  One part is not fully pinned: the hysteresis
+brute force and invariants; the generator against rocRAND's Philox4x32-10
+run on the host).  One part is not fully pinned: the hysteresis
 semantics of the scale-update state machine beyond its stated properties
 (``oracle.policy``) -- parity unpinned there.
 """
