@@ -14,6 +14,8 @@ Two tiers implement the same definitions:
   binary64, where every step used is exact for the inputs it is given (fp32 and
   bf16 values times powers of two, rounding to an integer with ``np.rint``).
   Sums are formed exactly and rounded once.
+* ``oracle.swamp`` -- the update/step-ratio ("swamping") monitor and its
+  promotion window, tier 0 and tier 1.
 * ``oracle.rng`` -- Philox4x32-10, the counter-based generator whose words the
   stochastic-rounding cast draws, written from its published definition.
 
