@@ -102,6 +102,47 @@ typedef struct {
   int32_t reserved;  /* 0 */
 } nc_tensor;
 
+/* ---- The update/step-ratio ("swamping") monitor types ---------------------- */
+
+/* The narrow format a weight copy is kept in. */
+typedef enum { NC_W_BF16 = 0, NC_W_FP16 = 1 } nc_wfmt;
+
+/* One weight tensor and its update (host array of these). */
+typedef struct {
+  const float *w;    /* (device) n fp32 master weights, 16-byte aligned */
+  const float *d;    /* (device) n fp32 updates (what the optimizer adds), 16-byte aligned */
+  uint8_t *flags;    /* (device, nullable, 4-byte aligned) n flag bytes: bit 0 below the step,
+                        bit 1 no-op, bit 2 zero update, bit 3 excluded */
+  int64_t n;         /* element count, >= 0 */
+} nc_update_tensor;
+
+/* Per-tensor monitor counts (device array, one per tensor; zero before the
+ * call: the call adds into it). */
+typedef struct {
+  uint64_t n_considered;   /* finite weight in the format's range, finite nonzero update */
+  uint64_t n_zero;         /* finite weight in range, zero update */
+  uint64_t n_below;        /* considered, |d| < the step of w's narrow copy (ratio below one) */
+  uint64_t n_noop;         /* considered, the narrow add leaves the weight unchanged */
+  uint64_t n_excluded;     /* w or d not finite, or w overflows the narrow format */
+} nc_swamp_counts;
+
+/* Promotion rule: a step is "below" when n_below * den >= num * n_considered
+ * (n_considered > 0); `window` below steps in a row promote the tensor. */
+typedef struct {
+  int32_t window;    /* >= 1 */
+  uint32_t num;      /* threshold num / den, 0 <= num <= den */
+  uint32_t den;      /* 1 .. 65536 */
+  int32_t reserved;  /* 0 */
+} nc_swamp_policy;
+
+/* Per-tensor promotion state (device array; zero-initialise). */
+typedef struct {
+  int32_t run;       /* consecutive below steps */
+  int32_t promoted;  /* 1 once run has reached the window; stays 1 */
+  int32_t steps;     /* steps seen */
+  int32_t reserved;
+} nc_swamp_state;
+
 /* Per-tensor counts (device array, one per tensor; zero before first use). */
 typedef struct {
   uint64_t n_finite;
@@ -253,6 +294,31 @@ size_t nc_workspace_bytes(const nc_tensor *t, int32_t count);
 
 /* Static description of a status code. */
 const char *nc_status_string(nc_status s);
+
+/* ---- The update/step-ratio ("swamping") monitor -----------------------------
+ * [E3, "Worked solution"]: step fails at the weight -- watch the ratio of the
+ * update to the step at the weight; keep a wide master copy while it is
+ * below one; promote a tensor to a wider format when its updates sit below
+ * its step for a whole window.  [SP, "Master weights and the optimizer
+ * step"]: in 16 bits such an add is exactly a no-op.
+ *
+ * Per element, with w_F = RNE_F(w) the narrow copy (F = bf16 or fp16, IEEE
+ * overflow) and step = F's grid spacing in |w_F|'s binade (the subnormal
+ * spacing below the normal range): excluded if w or d is not finite or w_F
+ * overflows; zero if d == 0; otherwise considered, below if |d| < step, and
+ * a no-op if RNE_F(w_F + d) == w_F for the exact sum.  Counts add into
+ * out[j]; flags (if given) are written per element.  A read-only pass:
+ * 8 bytes per element in (+1 with flags).  ws: nc_swamp_workspace_bytes(t,
+ * count) bytes, 16-byte aligned. */
+size_t nc_swamp_workspace_bytes(const nc_update_tensor *t, int32_t count);
+nc_status nc_swamp_watch(const nc_update_tensor *t, int32_t count, nc_wfmt wfmt, nc_swamp_counts *out,
+                         void *ws, size_t ws_bytes, void *stream);
+
+/* One step of the promotion rule for `count` tensors: st[j] from in[j] (the
+ * counts of this step) under the policy: run = run + 1 if the step is below,
+ * else 0; promoted = promoted or run >= window; steps += 1. */
+nc_status nc_swamp_window(const nc_swamp_policy *policy, int32_t count, nc_swamp_state *st,
+                          const nc_swamp_counts *in, void *stream);
 
 #ifdef __cplusplus
 }

@@ -24,8 +24,8 @@ import torch
 
 from . import _lib
 from ._lib import (NC_BF16, NC_E4M3, NC_E5M2, NC_EST_CURRENT, NC_EST_EMA, NC_EST_MAX_WINDOW,  # noqa: F401
-                   NC_EST_MOST_RECENT, NC_F32, NC_MX_CEIL, NC_MX_OCP, NC_MX_PLUS1, NcPolicy,
-                   NcTensor)
+                   NC_EST_MOST_RECENT, NC_F32, NC_MX_CEIL, NC_MX_OCP, NC_MX_PLUS1, NC_W_BF16, NC_W_FP16,
+                   NcPolicy, NcSwampPolicy, NcTensor, NcUpdateTensor)
 
 COUNT_FIELDS = ("n_finite", "n_clip", "n_underflow", "n_nonfinite")
 STAT_FIELDS = ("sum_e", "sum_abs_e", "sum_e2", "sum_dir_e", "sum_xe", "sum_x2")
@@ -227,3 +227,63 @@ def nc_cast_stats(xs: Sequence[torch.Tensor], codes: Sequence[torch.Tensor], fmt
     ws = _ws(ws, desc, count)
     _check(_lib.load().nc_cast_stats(desc, count, dt, f, _ptr(st), _ptr(ls), _ptr(out), _ptr(ws),
                                      ws.numel(), _stream(stream)), "nc_cast_stats")
+
+
+# -- the update/step-ratio ("swamping") monitor -------------------------------
+
+WFMT = {"bf16": NC_W_BF16, "fp16": NC_W_FP16}
+SWAMP_FIELDS = ("n_considered", "n_zero", "n_below", "n_noop", "n_excluded")
+
+
+def update_tensors(ws: Sequence[torch.Tensor], ds: Sequence[torch.Tensor],
+                   flags: Optional[Sequence[Optional[torch.Tensor]]] = None):
+    """A host array of nc_update_tensor descriptors (contiguous fp32 device tensors)."""
+    count = len(ws)
+    arr = (NcUpdateTensor * max(count, 1))()
+    for i in range(count):
+        w, d = ws[i], ds[i]
+        for t in (w, d):
+            if t.dtype != torch.float32 or not t.is_contiguous():
+                raise TypeError("weights and updates must be contiguous float32")
+        if w.numel() != d.numel():
+            raise ValueError("a weight tensor and its update differ in size")
+        arr[i].w = _ptr(w) if w.numel() else None
+        arr[i].d = _ptr(d) if d.numel() else None
+        f = flags[i] if flags is not None else None
+        arr[i].flags = _ptr(f) if f is not None and f.numel() else None
+        arr[i].n = w.numel()
+    return arr, count
+
+
+def new_swamp_counts(count: int, device="cuda") -> torch.Tensor:
+    return torch.zeros((count, 5), dtype=torch.int64, device=device)
+
+
+def new_swamp_state(count: int, device="cuda") -> torch.Tensor:
+    return torch.zeros((count, 4), dtype=torch.int32, device=device)
+
+
+def swamp_policy(window=8, num=1, den=2) -> NcSwampPolicy:
+    return NcSwampPolicy(window, num, den, 0)
+
+
+def swamp_counts_list(counts: torch.Tensor):
+    return [dict(zip(SWAMP_FIELDS, r)) for r in counts.cpu().tolist()]
+
+
+def nc_swamp_watch(ws: Sequence[torch.Tensor], ds: Sequence[torch.Tensor], wfmt, out: torch.Tensor,
+                   flags: Optional[Sequence[Optional[torch.Tensor]]] = None,
+                   workspace: Optional[torch.Tensor] = None, stream=None):
+    desc, count = update_tensors(ws, ds, flags)
+    lib = _lib.load()
+    if workspace is None:
+        workspace = torch.empty(max(int(lib.nc_swamp_workspace_bytes(desc, count)), 16), dtype=torch.uint8,
+                                device="cuda")
+    f = WFMT[wfmt] if isinstance(wfmt, str) else wfmt
+    _check(lib.nc_swamp_watch(desc, count, f, _ptr(out), _ptr(workspace), workspace.numel(), _stream(stream)),
+           "nc_swamp_watch")
+
+
+def nc_swamp_window(pol: NcSwampPolicy, st: torch.Tensor, in_counts: torch.Tensor, stream=None):
+    _check(_lib.load().nc_swamp_window(ctypes.byref(pol), st.shape[0], _ptr(st), _ptr(in_counts),
+                                       _stream(stream)), "nc_swamp_window")

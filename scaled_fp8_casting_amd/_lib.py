@@ -48,8 +48,27 @@ class NcPolicy(ctypes.Structure):
                                        "ls_log2_min", "ls_log2_max")] + [("ema_alpha", ctypes.c_float)]
 
 
+class NcUpdateTensor(ctypes.Structure):
+    _fields_ = [("w", c_void_p), ("d", c_void_p), ("flags", c_void_p), ("n", c_int64)]
+
+
+class NcSwampCounts(ctypes.Structure):
+    _fields_ = [(n, c_uint64) for n in ("n_considered", "n_zero", "n_below", "n_noop", "n_excluded")]
+
+
+class NcSwampPolicy(ctypes.Structure):
+    _fields_ = [("window", c_int32), ("num", c_uint32), ("den", c_uint32), ("reserved", c_int32)]
+
+
+class NcSwampState(ctypes.Structure):
+    _fields_ = [(n, c_int32) for n in ("run", "promoted", "steps", "reserved")]
+
+
+NC_W_BF16, NC_W_FP16 = 0, 1
+
 EXPORTS = ("nc_amax", "nc_scale_update", "nc_cast_tensor", "nc_cast_tensor_sr", "nc_cast_mx", "nc_dequant",
-           "nc_cast_stats", "nc_workspace_bytes", "nc_status_string")
+           "nc_cast_stats", "nc_workspace_bytes", "nc_status_string", "nc_swamp_workspace_bytes",
+           "nc_swamp_watch", "nc_swamp_window")
 
 _lib = None
 
@@ -75,12 +94,17 @@ def load():
     lib.nc_dequant.argtypes = [T, c_int32, c_int32, c_void_p, POINTER(c_void_p), c_int32, c_void_p]
     lib.nc_cast_stats.argtypes = [T, c_int32, c_int32, c_int32, c_void_p, c_void_p, c_void_p, c_void_p,
                                   c_size_t, c_void_p]
+    U = POINTER(NcUpdateTensor)
+    lib.nc_swamp_workspace_bytes.argtypes = [U, c_int32]
+    lib.nc_swamp_workspace_bytes.restype = c_size_t
+    lib.nc_swamp_watch.argtypes = [U, c_int32, c_int32, c_void_p, c_void_p, c_size_t, c_void_p]
+    lib.nc_swamp_window.argtypes = [POINTER(NcSwampPolicy), c_int32, c_void_p, c_void_p, c_void_p]
     lib.nc_workspace_bytes.argtypes = [T, c_int32]
     lib.nc_workspace_bytes.restype = c_size_t
     lib.nc_status_string.argtypes = [c_int32]
     lib.nc_status_string.restype = c_char_p
     for name in ("nc_amax", "nc_scale_update", "nc_cast_tensor", "nc_cast_tensor_sr", "nc_cast_mx", "nc_dequant",
-                 "nc_cast_stats"):
+                 "nc_cast_stats", "nc_swamp_watch", "nc_swamp_window"):
         getattr(lib, name).restype = c_int32
     _lib = lib
     return lib

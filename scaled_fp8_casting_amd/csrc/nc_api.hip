@@ -39,9 +39,27 @@ nc_status check_tensors(const nc_tensor* t, int32_t count, bool need_x, bool nee
 // error.
 constexpr int64_t kMaxLaunchElems = (int64_t)1 << 34;
 
+// The two descriptor types in a launch's Seg: a cast tensor (x, codes,
+// scales, optional dequant output y), or a weight/update pair of the
+// monitor (w in x, d in y, flags in codes).
+void fill_seg(Seg& g, const nc_tensor& x, void* y) {
+  g.x = x.x;
+  g.codes = x.codes;
+  g.scales = x.scales;
+  g.y = y;
+  g.cols = x.cols;
+}
+void fill_seg(Seg& g, const nc_update_tensor& x, void*) {
+  g.x = x.w;
+  g.y = const_cast<float*>(x.d);
+  g.codes = x.flags;
+  g.scales = nullptr;
+  g.cols = 0;
+}
+
 // Launch boundaries: calls fn(first, end) for each launch [first, end).
-template <typename Fn>
-nc_status for_launches(const nc_tensor* t, int32_t count, Fn fn) {
+template <typename T, typename Fn>
+nc_status for_launches(const T* t, int32_t count, Fn fn) {
   int32_t i = 0;
   while (i < count) {
     const int32_t first = i;
@@ -57,20 +75,17 @@ nc_status for_launches(const nc_tensor* t, int32_t count, Fn fn) {
 // Fills b for tensors [first, end) with tiles of `tile` units of `unit`
 // elements (unit 1: element tiles; column-block MX: col_slots, which divide
 // every tensor the checks admit).  b.last counts units.
-void make_batch(SegBatch& b, const nc_tensor* t, int32_t first, int32_t end, int64_t tile, void* const* y,
+template <typename T>
+void make_batch(SegBatch& b, const T* t, int32_t first, int32_t end, int64_t tile, void* const* y,
                 int64_t unit = 1) {
   memset(&b, 0, sizeof(b));
   b.first = first;
   b.count = end - first;
   for (int32_t s = 0; s < b.count; ++s) {
-    const nc_tensor& x = t[first + s];
+    const T& x = t[first + s];
     Seg& g = b.s[s];
-    g.x = x.x;
-    g.codes = x.codes;
-    g.scales = x.scales;
-    g.y = y ? y[first + s] : nullptr;
+    fill_seg(g, x, y ? y[first + s] : nullptr);
     g.n = x.n;
-    g.cols = x.cols;
     const int64_t units = x.n / unit;
     const int64_t tiles = (units + tile - 1) / tile;
     b.tile0[s + 1] = b.tile0[s] + tiles;
@@ -85,9 +100,8 @@ void make_batch(SegBatch& b, const nc_tensor* t, int32_t first, int32_t end, int
 
 // Walk the call in launches; `fn(batch)` enqueues one launch (skipped when
 // the launch has no element at all).
-template <typename Fn>
-nc_status for_batches(const nc_tensor* t, int32_t count, int64_t tile, void* const* y, Fn fn,
-                      int64_t unit = 1) {
+template <typename T, typename Fn>
+nc_status for_batches(const T* t, int32_t count, int64_t tile, void* const* y, Fn fn, int64_t unit = 1) {
   SegBatch b;
   return for_launches(t, count, [&](int32_t first, int32_t end) {
     make_batch(b, t, first, end, tile, y, unit);
@@ -109,23 +123,32 @@ nc_status check_ws(const nc_tensor* t, int32_t count, void* ws, size_t ws_bytes)
 
 Ws ws_of(const SegBatch& b, void* ws) { return ws_layout(ws, b.tile0[b.count], b.chunk0[b.count]); }
 
-}  // namespace
-
-extern "C" {
-
-size_t nc_workspace_bytes(const nc_tensor* t, int32_t count) {
-  // per-workgroup and per-chunk slots of the largest launch, at the smallest
-  // tile any call uses
+// Per-workgroup and per-chunk slots of the largest launch at tile `tile`.
+template <typename T>
+size_t ws_need(const T* t, int32_t count, int64_t tile) {
   if (t == nullptr || count <= 0) return 0;
   size_t need = 0;
   SegBatch b;
   for_launches(t, count, [&](int32_t first, int32_t end) {
-    make_batch(b, t, first, end, kMinWsTile, nullptr);
+    make_batch(b, t, first, end, tile, nullptr);
     const size_t v = ws_bytes_for(b.tile0[b.count], b.chunk0[b.count]);
     if (v > need) need = v;
     return NC_OK;
   });
   return need;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t nc_workspace_bytes(const nc_tensor* t, int32_t count) {
+  // at the smallest tile any call uses
+  return ws_need(t, count, kMinWsTile);
+}
+
+size_t nc_swamp_workspace_bytes(const nc_update_tensor* t, int32_t count) {
+  return ws_need(t, count, kSwampTile);
 }
 
 const char* nc_status_string(nc_status s) {
@@ -289,6 +312,38 @@ nc_status nc_cast_stats(const nc_tensor* t, int32_t count, nc_dtype dtype, nc_fm
     if (r == NC_OK) r = hip_status(launch_reduce(b, w, nullptr, out, mx ? nullptr : ls, false, (hipStream_t)stream));
     return r;
   });
+}
+
+nc_status nc_swamp_watch(const nc_update_tensor* t, int32_t count, nc_wfmt wfmt, nc_swamp_counts* out,
+                         void* ws, size_t ws_bytes, void* stream) {
+  if (wfmt != NC_W_BF16 && wfmt != NC_W_FP16) return NC_E_UNSUPPORTED;
+  if (count < 0 || (count > 0 && t == nullptr)) return NC_E_ARG;
+  for (int32_t i = 0; i < count; ++i) {
+    const nc_update_tensor& x = t[i];
+    if (x.n < 0) return NC_E_ARG;
+    if (x.n == 0) continue;
+    if (x.w == nullptr || x.d == nullptr) return NC_E_ARG;
+    if (!aligned16(x.w) || !aligned16(x.d) || ((uintptr_t)x.flags & 3u) != 0) return NC_E_ALIGN;
+  }
+  if (count == 0) return NC_OK;
+  if (out == nullptr) return NC_E_ARG;
+  if (ws == nullptr || ((uintptr_t)ws & 15u) != 0 || ws_bytes < nc_swamp_workspace_bytes(t, count))
+    return NC_E_WORKSPACE;
+  return for_batches(t, count, kSwampTile, nullptr, [&](const SegBatch& b) {
+    const Ws w = ws_of(b, ws);
+    nc_status r = hip_status(launch_swamp(b, wfmt, w, Launch{b.tile0[b.count], (hipStream_t)stream}));
+    if (r == NC_OK) r = hip_status(launch_swamp_reduce(b, w, out, (hipStream_t)stream));
+    return r;
+  });
+}
+
+nc_status nc_swamp_window(const nc_swamp_policy* p, int32_t count, nc_swamp_state* st,
+                          const nc_swamp_counts* in, void* stream) {
+  if (p == nullptr || count < 0) return NC_E_ARG;
+  if (p->window < 1 || p->den < 1 || p->den > 65536 || p->num > p->den) return NC_E_ARG;
+  if (count == 0) return NC_OK;
+  if (st == nullptr || in == nullptr) return NC_E_ARG;
+  return hip_status(launch_swamp_window(*p, count, st, in, (hipStream_t)stream));
 }
 
 }  // extern "C"

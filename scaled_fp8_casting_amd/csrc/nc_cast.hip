@@ -173,12 +173,14 @@ __device__ __forceinline__ void sr_block(uint32_t blk, const SrKey& key, uint32_
 // exponent K with uniform u, as m * 2^eq (m <= 2^(MB+1), exact in fp32).
 // y = S 2^lsb exactly (S the fp32 significand); the grid spacing at y is
 // 2^eq with eq = max(binade(y), EMIN) - MB; the d = eq - lsb low bits of S
-// are discarded.  With W = S 2^32, floor(W / 2^d) holds the kept part in its
-// high word and F = floor(t 2^32) in its low word; `sticky` is whether t 2^32
-// has a fraction (only when d > 32).  The magnitude rounds up iff u < t 2^32,
-// i.e. u < F, or u == F with a fraction.  d <= 0: y is on the grid (m = S
-// 2^-d, no draw).  Selects only (no branches); out-of-range lanes compute
-// values their caller discards, with every shift kept in range.
+// are discarded.  floor(S 2^32 / 2^d) holds the kept part in its high word
+// and F = floor(t 2^32) in its low word; t 2^32 has a fraction (`sticky`)
+// only when d > 32, from the bits of S below 2^(d - 32).  The magnitude
+// rounds up iff u < t 2^32, i.e. u < F, or u == F with a fraction.  d <= 0:
+// y is on the grid (m = S 2^-d, no draw).  Straight-line code: the rule is
+// combined with bitwise operations (a short-circuit form compiles to a
+// branch per element); lanes whose result the caller discards compute with
+// every shift kept in range.
 template <int FMT>
 __device__ __forceinline__ float sr_value(uint32_t ax, int K, uint32_t u, uint32_t* m_out) {
   using F = Fp8<FMT>;
@@ -188,13 +190,14 @@ __device__ __forceinline__ float sr_value(uint32_t ax, int K, uint32_t u, uint32
   const int ey = (31 - __clz(S | 1u)) + lsb;
   const int eq = max(ey, F::EMIN) - F::MB;
   const int d = eq - lsb;
-  const uint64_t W = (uint64_t)S << 32;
   const uint32_t dd = (uint32_t)min(max(d, 0), 63);
-  const uint64_t Q = W >> dd;
-  const uint32_t Fr = (uint32_t)Q;
-  const bool sticky = (W & ((1ull << dd) - 1ull)) != 0;
-  const uint32_t up = (u < Fr || (sticky && u == Fr)) ? 1u : 0u;
-  const uint32_t m = d < 0 ? S << (uint32_t)min(-d, 31) : (uint32_t)(Q >> 32) + up;
+  const uint64_t Q = ((uint64_t)S << 32) >> dd;
+  const uint32_t Fr = (uint32_t)Q, kept = (uint32_t)(Q >> 32);
+  const uint32_t sh = dd > 32u ? min(dd - 32u, 31u) : 0u;
+  const uint32_t sticky = (S & ((1u << sh) - 1u)) != 0u ? 1u : 0u;
+  const uint32_t up = (u < Fr ? 1u : 0u) | ((u == Fr ? 1u : 0u) & sticky);
+  const uint32_t exact = S << (uint32_t)min(max(-d, 0), 31);
+  const uint32_t m = d < 0 ? exact : kept + up;
   *m_out = m;
   return __builtin_amdgcn_ldexpf((float)m, eq);
 }

@@ -33,6 +33,11 @@ inline int64_t col_unit(int in_bytes) { return 32 * (kColBytes / in_bytes); }
 constexpr int64_t kDequantColUnit = 32 * kDequantColCodes;
 static_assert(kThreads * 32 * 2 >= kMinWsTile, "column tiles are no smaller than kMinWsTile");
 
+// The update/step-ratio monitor: 256 lanes x four 16-byte vectors of w (and
+// of d) per tile -- read-only, like the amax pass.
+constexpr int kSwampVecs = 4;
+constexpr int64_t kSwampTile = (int64_t)kThreads * 4 * kSwampVecs;
+
 // Workspace of one launch: per-tile slots, then per-chunk slots.
 struct Ws {
   CountSlot* cnt1;      // [tiles]
@@ -88,6 +93,12 @@ hipError_t launch_stats_col(const SegBatch& b, int dtype, int fmt, const Ws& w, 
 hipError_t launch_reduce(const SegBatch& b, const Ws& w, nc_counts* out, nc_stats* stats,
                          const nc_loss_scale* ls, bool clips, hipStream_t stream);
 hipError_t launch_dequant(const SegBatch& b, int fmt, const nc_scale_state* st, const Launch& l);
+// The monitor's main kernel, its two slot reductions into out, and the
+// promotion window.
+hipError_t launch_swamp(const SegBatch& b, int wfmt, const Ws& w, const Launch& l);
+hipError_t launch_swamp_reduce(const SegBatch& b, const Ws& w, nc_swamp_counts* out, hipStream_t stream);
+hipError_t launch_swamp_window(const nc_swamp_policy& p, int32_t count, nc_swamp_state* st,
+                               const nc_swamp_counts* in, hipStream_t stream);
 hipError_t launch_scale_update(const nc_policy& p, int32_t count, nc_scale_state* st, float* hist,
                                const nc_counts* in, nc_loss_scale* ls, hipStream_t stream);
 

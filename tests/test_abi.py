@@ -52,6 +52,10 @@ def test_struct_sizes_match_header():
     assert ctypes.sizeof(_lib.NcScaleState) == 24
     assert ctypes.sizeof(_lib.NcLossScale) == 8
     assert ctypes.sizeof(NcPolicy) == 48
+    assert ctypes.sizeof(_lib.NcUpdateTensor) == 32
+    assert ctypes.sizeof(_lib.NcSwampCounts) == 40
+    assert ctypes.sizeof(_lib.NcSwampPolicy) == 16
+    assert ctypes.sizeof(_lib.NcSwampState) == 16
 
 
 def _desc(*specs, axes=None):
@@ -156,6 +160,41 @@ def test_policy_checks(lib):
     assert lib.nc_scale_update(ctypes.byref(p), 1, A, None, A, None, None) == _lib.NC_E_ARG   # no history
     assert lib.nc_scale_update(ctypes.byref(p), 0, None, None, None, None, None) == _lib.NC_OK
     assert lib.nc_scale_update(None, 1, A, A, A, None, None) == _lib.NC_E_ARG
+
+
+def _udesc(*specs):
+    arr = (_lib.NcUpdateTensor * len(specs))()
+    for i, (w, d, f, n) in enumerate(specs):
+        arr[i].w, arr[i].d, arr[i].flags, arr[i].n = w, d, f, n
+    return arr
+
+
+def test_swamp_checks(lib):
+    A, W = 0x10000, 1 << 40
+    d = _udesc((A, A, None, 100))
+    assert lib.nc_swamp_watch(d, 1, 2, A, A, W, None) == _lib.NC_E_UNSUPPORTED
+    assert lib.nc_swamp_watch(_udesc((A + 4, A, None, 100)), 1, 0, A, A, W, None) == _lib.NC_E_ALIGN
+    assert lib.nc_swamp_watch(_udesc((A, A, A + 2, 100)), 1, 0, A, A, W, None) == _lib.NC_E_ALIGN
+    assert lib.nc_swamp_watch(_udesc((A, None, None, 100)), 1, 0, A, A, W, None) == _lib.NC_E_ARG
+    assert lib.nc_swamp_watch(_udesc((A, A, None, -1)), 1, 0, A, A, W, None) == _lib.NC_E_ARG
+    assert lib.nc_swamp_watch(d, 1, 0, None, A, W, None) == _lib.NC_E_ARG
+    assert lib.nc_swamp_watch(d, 1, 0, A, None, W, None) == _lib.NC_E_WORKSPACE
+    need = lib.nc_swamp_workspace_bytes(d, 1)
+    assert lib.nc_swamp_watch(d, 1, 0, A, A, need - 16, None) == _lib.NC_E_WORKSPACE
+    assert lib.nc_swamp_watch(None, 0, 0, None, None, 0, None) == _lib.NC_OK
+    assert lib.nc_swamp_watch(_udesc((None, None, None, 0)), 1, 0, A, A, W, None) == _lib.NC_OK
+    # workspace: 16 + 48 B per tile of 4096 elements, 32 + 48 B per chunk of 1024 tiles, arrays rounded
+    # to 256 B, the largest launch of <= 32 tensors
+    r = lambda v: (v + 255) // 256 * 256
+    T = -(-(3 * 4096 * 1024 + 5) // 4096)
+    C = -(-T // 1024)
+    assert lib.nc_swamp_workspace_bytes(_udesc((A, A, None, 3 * 4096 * 1024 + 5)), 1) == \
+        r(16 * T) + r(48 * T) + r(32 * C) + r(48 * C)
+    P = _lib.NcSwampPolicy
+    for pol in (P(0, 1, 2, 0), P(4, 3, 2, 0), P(4, 1, 0, 0), P(4, 1, 70000, 0)):
+        assert lib.nc_swamp_window(ctypes.byref(pol), 1, A, A, None) == _lib.NC_E_ARG
+    assert lib.nc_swamp_window(ctypes.byref(P(4, 1, 2, 0)), 1, None, A, None) == _lib.NC_E_ARG
+    assert lib.nc_swamp_window(ctypes.byref(P(4, 1, 2, 0)), 0, None, None, None) == _lib.NC_OK
 
 
 def test_status_strings(lib):

@@ -25,6 +25,13 @@ Workloads (standard deviations are the second argument of N(0, s)):
   device from a seeded generator each step; 1e-7 of all elements are then
   set to +Inf or NaN (even odds) at positions drawn on the host from seed
   104 and the step.
+* ``UpdateStep``: fp32 master weights and one optimizer update for the
+  update/step-ratio monitor ([E3, "Worked solution"]; [SP, "Master weights
+  and the optimizer step"]: weights of order 1 meet updates far below their
+  step late in training).  rows of 4096: w ~ N(0, 0.02) (an initialisation
+  spread), d = lr * g * 10^(u_r) with lr = 1e-4, g ~ N(0, 1) and a per-row
+  u_r ~ U(-3, 1), so the update/step ratio spans several binades either side
+  of one.  Drawn on the device from a seeded generator (seed 106).
 """
 
 import numpy as np
@@ -175,3 +182,23 @@ class LlamaGrads:
             val = torch.from_numpy(np.where(is_nan[m], np.nan, np.inf).astype(np.float32)).to(self.device)
             self.bufs[i].index_copy_(0, idx, val)
         return tensor, offset, is_nan
+
+
+class UpdateStep:
+    """Device-resident fp32 weights ``w`` and updates ``d`` (see the module
+    docstring), rows x 4096."""
+
+    COLS = 4096
+    SIGMA_W = 0.02
+    LR = 1e-4
+
+    def __init__(self, rows: int, seed: int = 106, device: str = "cuda"):
+        g = torch.Generator(device=device)
+        g.manual_seed(seed)
+        n = rows * self.COLS
+        self.w = torch.empty(n, dtype=torch.float32, device=device).normal_(0.0, self.SIGMA_W, generator=g)
+        self.d = torch.empty(n, dtype=torch.float32, device=device).normal_(0.0, 1.0, generator=g)
+        u = torch.empty(rows, 1, dtype=torch.float32, device=device).uniform_(-3.0, 1.0, generator=g)
+        self.d.view(rows, self.COLS).mul_(torch.pow(10.0, u) * self.LR)
+        self.n = n
+
