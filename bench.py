@@ -18,7 +18,8 @@ timed region.  One step is one pass of the whole cast path over it:
 
 Beside the step (not part of it) the same JSON line reports the casts with
 fused statistics, the stochastic-rounding cast, the MX cast, dequant and
-statistics with blocks down the columns, a plain device copy of the cast's byte count, and one
+statistics with blocks down the columns, the update/step-ratio monitor on
+2^30 fp32 weights and updates, a plain device copy of the cast's byte count, and one
 delayed-scaling step of loss-scaled Llama-7B-shaped fp32 gradients (225
 tensors, 6.6G elements, fused 2^-16 unscale).
 
@@ -85,7 +86,8 @@ KERNEL_SIG = {"amax": "k_amax<1>", "cast_tensor": "k_cast_pt<0, 1, false>",
               "stats_mx": "k_stats<0, 1, true>",
               "cast_tensor+stats": "k_cast_pt<0, 1, true>", "cast_mx+stats": "k_cast_mx<0, 1, 0, true>",
               "cast_mx_cols": "k_cast_mx_col<0, 1, 0, false>", "dequant_mx_cols": "k_dequant_col<0>",
-              "stats_mx_cols": "k_stats_col<0, 1>", "cast_tensor_sr": "k_cast_sr<0, 1>"}
+              "stats_mx_cols": "k_stats_col<0, 1>", "cast_tensor_sr": "k_cast_sr<0, 1>",
+              "swamp_watch": "k_swamp<0>"}
 TRAFFIC_JSON = os.path.join(ROOT, "profiles", "traffic.json")
 
 
@@ -395,6 +397,33 @@ def main():
         out["beside_step"][nm] = dict(ms=round(ms, 4), gbps=round(gbps, 1), frac=round(gbps / HBM_PEAK_GBPS, 4),
                                       gelem_s=round(n / (ms * 1e-3) / 1e9, 2), traffic=traffic_for(nm, src))
     extras.clear()
+    # the update/step-ratio monitor on its own workload: 2^30 fp32 weights and
+    # updates (8 GiB read), bf16 weight copies, counts only
+    del y_pt, y_mx
+    torch.cuda.empty_cache()
+    upd = workloads.UpdateStep(rows=rows)
+    sw_out = nc.new_swamp_counts(1)
+    sw_ws = nc.new_swamp_workspace([upd.w], [upd.d])
+    fn = lambda: nc.nc_swamp_watch([upd.w], [upd.d], "bf16", sw_out, workspace=sw_ws)
+    fn()
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(10)]
+    for e0, e1 in ev:
+        e0.record()
+        fn()
+        e1.record()
+    torch.cuda.synchronize()
+    ms = float(np.mean([e0.elapsed_time(e1) for e0, e1 in ev]))
+    gbps = 8 * n / (ms * 1e-3) / 1e9
+    sc = nc.swamp_counts_list(sw_out)[0]
+    out["beside_step"]["swamp_watch"] = dict(
+        ms=round(ms, 4), gbps=round(gbps, 1), frac=round(gbps / HBM_PEAK_GBPS, 4),
+        gelem_s=round(n / (ms * 1e-3) / 1e9, 2), traffic=traffic_for("swamp_watch", src),
+        workload="UpdateStep 2^30 fp32 w, d (w ~ N(0, 0.02), d = 1e-4 g 10^U(-3,1) per row); bf16 copies",
+        below_frac=round(sc["n_below"] / max(sc["n_considered"], 1), 4),
+        noop_frac=round(sc["n_noop"] / max(sc["n_considered"], 1), 4))
+    del upd, sw_ws
+    torch.cuda.empty_cache()
     if not a.no_llama:
         out["beside_step"]["llama_unscale_cast"] = llama_unscale_cast(nc, torch, workloads)
     if a.copy_probe:

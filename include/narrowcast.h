@@ -309,7 +309,7 @@ const char *nc_status_string(nc_status s);
  * a no-op if RNE_F(w_F + d) == w_F for the exact sum.  Counts add into
  * out[j]; flags (if given) are written per element.  A read-only pass:
  * 8 bytes per element in (+1 with flags).  ws: nc_swamp_workspace_bytes(t,
- * count) bytes, 16-byte aligned. */
+ * count) bytes (at most 64 B per 8192 elements), 16-byte aligned. */
 size_t nc_swamp_workspace_bytes(const nc_update_tensor *t, int32_t count);
 nc_status nc_swamp_watch(const nc_update_tensor *t, int32_t count, nc_wfmt wfmt, nc_swamp_counts *out,
                          void *ws, size_t ws_bytes, void *stream);

@@ -271,14 +271,19 @@ def swamp_counts_list(counts: torch.Tensor):
     return [dict(zip(SWAMP_FIELDS, r)) for r in counts.cpu().tolist()]
 
 
+def new_swamp_workspace(ws: Sequence[torch.Tensor], ds: Sequence[torch.Tensor], device="cuda") -> torch.Tensor:
+    desc, count = update_tensors(ws, ds)
+    return torch.empty(max(int(_lib.load().nc_swamp_workspace_bytes(desc, count)), 16), dtype=torch.uint8,
+                       device=device)
+
+
 def nc_swamp_watch(ws: Sequence[torch.Tensor], ds: Sequence[torch.Tensor], wfmt, out: torch.Tensor,
                    flags: Optional[Sequence[Optional[torch.Tensor]]] = None,
                    workspace: Optional[torch.Tensor] = None, stream=None):
     desc, count = update_tensors(ws, ds, flags)
     lib = _lib.load()
     if workspace is None:
-        workspace = torch.empty(max(int(lib.nc_swamp_workspace_bytes(desc, count)), 16), dtype=torch.uint8,
-                                device="cuda")
+        workspace = new_swamp_workspace(ws, ds)
     f = WFMT[wfmt] if isinstance(wfmt, str) else wfmt
     _check(lib.nc_swamp_watch(desc, count, f, _ptr(out), _ptr(workspace), workspace.numel(), _stream(stream)),
            "nc_swamp_watch")

@@ -33,9 +33,9 @@ inline int64_t col_unit(int in_bytes) { return 32 * (kColBytes / in_bytes); }
 constexpr int64_t kDequantColUnit = 32 * kDequantColCodes;
 static_assert(kThreads * 32 * 2 >= kMinWsTile, "column tiles are no smaller than kMinWsTile");
 
-// The update/step-ratio monitor: 256 lanes x four 16-byte vectors of w (and
+// The update/step-ratio monitor: 256 lanes x eight 16-byte vectors of w (and
 // of d) per tile -- read-only, like the amax pass.
-constexpr int kSwampVecs = 4;
+constexpr int kSwampVecs = 8;
 constexpr int64_t kSwampTile = (int64_t)kThreads * 4 * kSwampVecs;
 
 // Workspace of one launch: per-tile slots, then per-chunk slots.

@@ -5,9 +5,10 @@
 // optimizer step"]: a small enough update is exactly a no-op in 16 bits),
 // and the per-tensor promotion window.
 //
-// One workgroup per tile of 4096 elements (16 per lane, four 16-byte loads
-// of w and four of d); the four per-lane counts go to a workspace slot and
-// two small kernels reduce the slots per tensor in a fixed order.
+// One workgroup per tile of 8192 elements (32 per lane, eight 16-byte loads
+// of w and eight of d; measured best on MI355X); the four per-lane counts go
+// to a workspace slot and two small kernels reduce the slots per tensor in a
+// fixed order.
 #include "nc_launch.h"
 
 namespace nc {
@@ -17,13 +18,13 @@ namespace {
 template <int WF> struct WFmt;
 template <> struct WFmt<NC_W_BF16> {
   static constexpr int MB = 7, BIAS = 127;
-  static constexpr uint32_t EMASK = 0xFF, MMASK = 0x7F;
+  static constexpr uint32_t MMASK = 0x7F, MAG = 0x7FFF, INF = 0x7F80;
   // RNE of an fp32 pattern to bf16 (IEEE overflow to Inf)
   __device__ static uint32_t round(uint32_t b) { return f32_to_bf16_rne(b) & 0xFFFFu; }
 };
 template <> struct WFmt<NC_W_FP16> {
   static constexpr int MB = 10, BIAS = 15;
-  static constexpr uint32_t EMASK = 0x1F, MMASK = 0x3FF;
+  static constexpr uint32_t MMASK = 0x3FF, MAG = 0x7FFF, INF = 0x7C00;
   // the hardware conversion rounds to nearest even, keeps subnormals and
   // overflows to Inf
   __device__ static uint32_t round(uint32_t b) {
@@ -31,45 +32,46 @@ template <> struct WFmt<NC_W_FP16> {
   }
 };
 
-// fp32 bits of 2^j, j in [-149, 127].
-__device__ __forceinline__ uint32_t pow2_bits(int j) {
-  return j >= -126 ? (uint32_t)(j + 127) << 23 : 1u << (uint32_t)(j + 149);
-}
-
-struct SwampAcc {
-  uint32_t zero, below, noop, excl;
-};
+// 1 if a < b, for a, b < 2^31 (the sign of a - b).
+__device__ __forceinline__ uint32_t lt31(uint32_t a, uint32_t b) { return (a - b) >> 31; }
 
 // Flags of one element (bit 0 below, 1 no-op, 2 zero update, 3 excluded).
 // The narrow copy w_F keeps w's sign.  The add w_F + d leaves w_F iff |d| is
 // below half the gap to the neighbour on d's side, or exactly half with
 // w_F's last significand bit even (ties to even).  That gap is the step,
 // except toward zero from a power of two above the smallest normal, where
-// the binade below has half the spacing.  All decided by integer compares on
-// |d|'s bits against powers of two (exact; never through a rounded sum).
+// the binade below has half the spacing.  Every decision compares |d| with
+// a power of two, 2^j for j >= -135 (exact fp32 values, subnormal ones
+// included, formed by v_ldexp_f32; the compare of two finite fp32 values is
+// exact) -- never through a rounded sum.
 template <int WF>
-__device__ __forceinline__ uint32_t swamp_flags(uint32_t wb, uint32_t db, SwampAcc& acc) {
+__device__ __forceinline__ uint32_t swamp_flags(uint32_t wb, uint32_t db) {
   using F = WFmt<WF>;
-  const uint32_t aw = wb & kAbsMask, ad = db & kAbsMask;
+  const uint32_t ad = db & kAbsMask;
+  const float fd = __uint_as_float(ad);
   const uint32_t h = F::round(wb);
-  const uint32_t ef = (h >> F::MB) & F::EMASK, mf = h & F::MMASK;
-  const bool excl = aw > kMaxFinite || ad > kMaxFinite || ef == F::EMASK;
-  const bool zero = ad == 0u;
-  const int se = max((int)ef, 1) - F::BIAS - F::MB;            // log2 of the step
-  const bool toward_zero = (ef | mf) != 0u && ((wb ^ db) >> 31) != 0u;
-  const bool halved = toward_zero && mf == 0u && ef > 1u;
-  const uint32_t half = pow2_bits(se - 1 - (halved ? 1 : 0));
-  const bool below = ad < pow2_bits(se);
-  const bool noop = ad < half || (ad == half && (mf & 1u) == 0u);
-  const bool cons = !excl && !zero;
-  const uint32_t f = (cons && below ? 1u : 0u) | (cons && noop ? 2u : 0u) | (!excl && zero ? 4u : 0u) |
-                     (excl ? 8u : 0u);
-  acc.below += f & 1u;
-  acc.noop += (f >> 1) & 1u;
-  acc.zero += (f >> 2) & 1u;
-  acc.excl += f >> 3;
-  return f;
+  const uint32_t hm = h & F::MAG, mf = h & F::MMASK, ef = hm >> F::MB;
+  const uint32_t excl = lt31(kMaxFinite, max(wb & kAbsMask, ad)) | lt31(F::INF - 1u, hm);
+  const int se = max((int)ef, 1) - (F::BIAS + F::MB);          // log2 of the step
+  const uint32_t halved = ((wb ^ db) >> 31) & lt31(0u, hm) & lt31(mf, 1u) & lt31(1u, ef);
+  const float half = __builtin_amdgcn_ldexpf(1.0f, se - 1 - (int)halved);
+  const uint32_t zero = lt31(ad, 1u);
+  const uint32_t below = fd < __builtin_amdgcn_ldexpf(1.0f, se) ? 1u : 0u;
+  const uint32_t noop = (fd < half || (fd == half && (mf & 1u) == 0u)) ? 1u : 0u;
+  const uint32_t ok = excl ^ 1u, cons = ok & (zero ^ 1u);
+  return (below & cons) | (noop & cons) << 1 | (zero & ok) << 2 | excl << 3;
 }
+
+struct SwampAcc {
+  uint32_t zero, below, noop, excl;
+  // four flag bytes of a packed word at once: popcount of each bit plane
+  __device__ void add4(uint32_t f4) {
+    below += __popc(f4 & 0x01010101u);
+    noop += __popc(f4 & 0x02020202u);
+    zero += __popc(f4 & 0x04040404u);
+    excl += __popc(f4 & 0x08080808u);
+  }
+};
 
 // The workgroup's four sums -> its slot (as write_count_slot, all sums).
 __device__ inline void write_swamp_slot(const SwampAcc& a, uint4* slot, uint32_t* lds) {
@@ -119,15 +121,17 @@ k_swamp(const SegBatch b, uint4* __restrict__ slots) {
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      const uint32_t f = swamp_flags<WF>(w[u].x, d[u].x, acc) | swamp_flags<WF>(w[u].y, d[u].y, acc) << 8 |
-                         swamp_flags<WF>(w[u].z, d[u].z, acc) << 16 | swamp_flags<WF>(w[u].w, d[u].w, acc) << 24;
+      const uint32_t f = swamp_flags<WF>(w[u].x, d[u].x) | swamp_flags<WF>(w[u].y, d[u].y) << 8 |
+                         swamp_flags<WF>(w[u].z, d[u].z) << 16 | swamp_flags<WF>(w[u].w, d[u].w) << 24;
+      acc.add4(f);
       if (fl) st_stream(reinterpret_cast<uint32_t*>(fl) + u * kThreads + threadIdx.x, f);
     }
   } else {
     const uint32_t* ws = static_cast<const uint32_t*>(g.x) + e0;
     const uint32_t* ds = static_cast<const uint32_t*>(g.y) + e0;
     for (int i = threadIdx.x; i < rem; i += kThreads) {
-      const uint32_t f = swamp_flags<WF>(ws[i], ds[i], acc);
+      const uint32_t f = swamp_flags<WF>(ws[i], ds[i]);
+      acc.add4(f);
       if (fl) fl[i] = (uint8_t)f;
     }
   }

@@ -183,10 +183,10 @@ def test_swamp_checks(lib):
     assert lib.nc_swamp_watch(d, 1, 0, A, A, need - 16, None) == _lib.NC_E_WORKSPACE
     assert lib.nc_swamp_watch(None, 0, 0, None, None, 0, None) == _lib.NC_OK
     assert lib.nc_swamp_watch(_udesc((None, None, None, 0)), 1, 0, A, A, W, None) == _lib.NC_OK
-    # workspace: 16 + 48 B per tile of 4096 elements, 32 + 48 B per chunk of 1024 tiles, arrays rounded
+    # workspace: 16 + 48 B per tile of 8192 elements, 32 + 48 B per chunk of 1024 tiles, arrays rounded
     # to 256 B, the largest launch of <= 32 tensors
     r = lambda v: (v + 255) // 256 * 256
-    T = -(-(3 * 4096 * 1024 + 5) // 4096)
+    T = -(-(3 * 4096 * 1024 + 5) // 8192)
     C = -(-T // 1024)
     assert lib.nc_swamp_workspace_bytes(_udesc((A, A, None, 3 * 4096 * 1024 + 5)), 1) == \
         r(16 * T) + r(48 * T) + r(32 * C) + r(48 * C)

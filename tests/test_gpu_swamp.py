@@ -82,7 +82,7 @@ def test_batches_ragged_and_without_flags(name, fmt):
     r = np.random.default_rng(5)
     sizes = [int(v) for v in r.integers(1, 40000, 40)]
     sizes[7] = 0
-    sizes[8] = 4096 * 3
+    sizes[8] = 8192 * 3
     pairs = [_random_pairs(m, 10 + j) if m else (np.zeros(0, np.float32), np.zeros(0, np.float32))
              for j, m in enumerate(sizes)]
     flags, counts = _watch([p[0] for p in pairs], [p[1] for p in pairs], name)
@@ -95,7 +95,7 @@ def test_batches_ragged_and_without_flags(name, fmt):
 
 
 def test_counts_add_into_out_and_flags_stop_at_the_end():
-    w, d = _random_pairs(4096 * 2 + 5, 3)
+    w, d = _random_pairs(8192 * 2 + 5, 3)
     big = torch.full((w.size + 64,), 0xEE, dtype=torch.uint8, device="cuda")
     out = nc.new_swamp_counts(1)
     for _ in range(3):
