@@ -124,6 +124,9 @@ __device__ __forceinline__ uint32_t dq_bf16(uint32_t dec_bits, int K) {
   return f32_to_bf16_rne(__float_as_uint(v));
 }
 
+// The bf16 output is written with non-temporal stores (measured faster on
+// MI355X, as for the casts' code stores).
+//
 // Full tiles decode in hardware: v_cvt_pk_f32_fp8 / _bf8 turns two codes
 // into their exact fp32 values, v_ldexp_f32 applies the scale (exact, as
 // above), v_cvt_pk_bf16_f32 rounds two values to bf16 (nearest even, IEEE
@@ -192,7 +195,7 @@ k_dequant(const SegBatch b, const nc_scale_state* __restrict__ st) {
           if (((i < 4 ? nb0 : nb1) >> (8 * (i % 4) + 7)) & 1u) h[i] = 0x7FC0u;
         o = u32x4{h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16), h[6] | (h[7] << 16)};
       }
-      reinterpret_cast<u32x4*>(dst)[u * kThreads + threadIdx.x] = o;
+      __builtin_nontemporal_store(o, reinterpret_cast<u32x4*>(dst) + u * kThreads + threadIdx.x);
     }
   } else {
     const int k = MX ? 0 : st[b.first + s].k;
@@ -254,7 +257,7 @@ k_dequant_col(const SegBatch b) {
         if (((i < 4 ? nb0 : nb1) >> (8 * (i % 4) + 7)) & 1u) h[i] = 0x7FC0u;
       o = u32x4{h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16), h[6] | (h[7] << 16)};
     }
-    *reinterpret_cast<u32x4*>(dst + r * cols) = o;
+    __builtin_nontemporal_store(o, reinterpret_cast<u32x4*>(dst + r * cols));
   }
 }
 

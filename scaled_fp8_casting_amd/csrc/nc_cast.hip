@@ -58,6 +58,30 @@ k_amax(const SegBatch b, CountSlot* __restrict__ slots) {
 
 // ---------------------------------------------------------------------------
 // Per-tensor cast: code = RNE-sat(x * 2^(k - s)).
+
+// A full tile: U vectors per lane, loaded already.
+template <int FMT, int DT, bool STATS, bool SCALED, int U>
+__device__ __forceinline__ void cast_pt_full(const u32x4* v, const CastParams& p, float scale, Acc& acc,
+                                             StatAcc& sa, const double* tab, uint8_t* dst) {
+  constexpr int VEC = In<DT>::VEC;
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    uint32_t xb[VEC], w[VEC / 4];
+    unpack<DT>(v[u], xb);
+    const bool clean = cast_vec<FMT, DT, SCALED>(v[u], xb, p, scale, acc, w);
+    if constexpr (STATS) {
+      uint32_t q[VEC];
+#pragma unroll
+      for (int i = 0; i < VEC; ++i) q[i] = (w[i / 4] >> (8 * (i % 4))) & 0xFFu;
+      if (clean) stats_vec<VEC, false, true>(xb, q, tab, 1.0, sa);
+      else stats_vec<VEC, false, false>(xb, q, tab, 1.0, sa);
+    }
+    const int vi = u * kThreads + threadIdx.x;
+    if constexpr (DT == NC_F32) st_stream(reinterpret_cast<uint32_t*>(dst) + vi, w[0]);
+    else st_stream(reinterpret_cast<u32x2*>(dst) + vi, u32x2{w[0], w[1]});
+    if constexpr (STATS) __builtin_amdgcn_sched_barrier(0);   // one vector at a time (register pressure)
+  }
+}
 template <int FMT, int DT, bool STATS>
 NC_STREAM_KERNEL
 k_cast_pt(const SegBatch b, const nc_scale_state* __restrict__ st,
@@ -95,23 +119,12 @@ k_cast_pt(const SegBatch b, const nc_scale_state* __restrict__ st,
   if constexpr (STATS) sa.reset();
   uint8_t* dst = g.codes + e0;
   if (full) {
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      uint32_t xb[VEC], w[VEC / 4];
-      unpack<DT>(v[u], xb);
-      const bool clean = cast_vec<FMT, VEC>(xb, p, acc, w);
-      if constexpr (STATS) {
-        uint32_t q[VEC];
-#pragma unroll
-        for (int i = 0; i < VEC; ++i) q[i] = (w[i / 4] >> (8 * (i % 4))) & 0xFFu;
-        if (clean) stats_vec<VEC, false, true>(xb, q, tab, 1.0, sa);
-        else stats_vec<VEC, false, false>(xb, q, tab, 1.0, sa);
-      }
-      const int vi = u * kThreads + threadIdx.x;
-      if constexpr (DT == NC_F32) st_stream(reinterpret_cast<uint32_t*>(dst) + vi, w[0]);
-      else st_stream(reinterpret_cast<u32x2*>(dst) + vi, u32x2{w[0], w[1]});
-      if constexpr (STATS) __builtin_amdgcn_sched_barrier(0);   // one vector at a time (register pressure)
-    }
+    // scaled converts while 2^-K is an fp32 value; a loss-scale unscale can
+    // push K below -127, where ldexp + convert takes over (uniform branch)
+    if (K >= -127 && K <= 127)
+      cast_pt_full<FMT, DT, STATS, true, U>(v, p, __builtin_amdgcn_ldexpf(1.0f, -K), acc, sa, tab, dst);
+    else
+      cast_pt_full<FMT, DT, STATS, false, U>(v, p, 0.0f, acc, sa, tab, dst);
   } else {
     for (int base = 0; base < rem; base += kThreads) {
       const int i = base + (int)threadIdx.x;
@@ -367,8 +380,10 @@ __device__ __forceinline__ void mx_tile(const Seg& g, int64_t e0, int rem, const
     acc.amax = max(acc.amax, m);
     const int X = mx_exponent<FMT, RULE>(group_max<GROUP>(m));
     const CastParams p = cast_params<FMT>(-X);
+    // scaled converts divide by the block's scale 2^X (|X| <= 127)
+    const float scale = __builtin_amdgcn_ldexpf(1.0f, X);
 #pragma unroll
-    for (int j = 0; j < VEC / 4; ++j) w[j] = cvt4<FMT>(xb + 4 * j, p.K);
+    for (int j = 0; j < VEC / 4; ++j) w[j] = scvt4<FMT, DT>(v[u], j, scale);
 #pragma unroll
     for (int i = 0; i < VEC; ++i) count_elem(ax[i], p, acc);
     if (!clean) {

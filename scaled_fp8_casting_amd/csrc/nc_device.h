@@ -39,6 +39,15 @@
 
 namespace nc {
 
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef uint16_t u16x2 __attribute__((ext_vector_type(2)));
+
+// Input element types: elements per 16-byte vector, bytes per element.
+template <int DT> struct In;
+template <> struct In<NC_F32> { static constexpr int VEC = 4, BYTES = 4; };
+template <> struct In<NC_BF16> { static constexpr int VEC = 8, BYTES = 2; };
+
 constexpr int kThreads = 256;       // 4 wave64s per workgroup
 constexpr int kMaxSeg = 32;         // tensors per launch (descriptors travel as kernel arguments)
 constexpr int kWaves = kThreads / 64;
@@ -170,6 +179,50 @@ __device__ __forceinline__ uint32_t cvt1(uint32_t xb, int K) {
   return sat4<FMT>((uint32_t)cvt_pair<FMT, false>(y, 0.0f, 0) & 0xFFu);
 }
 
+// gfx950's scaled converts (v_cvt_scalef32_pk_{fp8,bf8}_{bf16,f32}): two
+// elements -> the codes of RNE(x / scale) in half HI of `old`.  Measured
+// against the exact definition for every bf16 pattern, and for random and
+// grid-midpoint fp32 values, at every scale 2^j, j in [-127, 127]: identical
+// to steps 1-2 above on every finite in-range input; out of range and
+// non-finite inputs give the same overflow/NaN codes, which steps 3-4 fix.
+// bf16 pairs convert straight from the packed input word (no unpacking).
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef short s16x2_t __attribute__((ext_vector_type(2)));
+
+template <int FMT, bool HI>
+__device__ __forceinline__ uint32_t scvt_bf16(uint32_t pair, float scale, uint32_t old) {
+  const bf16x2_t x = __builtin_bit_cast(bf16x2_t, pair);
+  const s16x2_t o = __builtin_bit_cast(s16x2_t, old);
+  if constexpr (FMT == NC_E4M3) return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_fp8_bf16(o, x, scale, HI));
+  else return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf8_bf16(o, x, scale, HI));
+}
+template <int FMT, bool HI>
+__device__ __forceinline__ uint32_t scvt_f32(uint32_t a, uint32_t b, float scale, uint32_t old) {
+  const s16x2_t o = __builtin_bit_cast(s16x2_t, old);
+  if constexpr (FMT == NC_E4M3)
+    return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(o, __uint_as_float(a), __uint_as_float(b), scale, HI));
+  else
+    return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf8_f32(o, __uint_as_float(a), __uint_as_float(b), scale, HI));
+}
+
+// Four elements of an input vector -> four codes (byte i = element i),
+// saturated: the scaled-convert form of cvt4 (x * 2^K with scale = 2^-K).
+// j: which group of four (bf16: words 2j, 2j+1 of the vector; fp32: the
+// whole vector).
+template <int FMT, int DT>
+__device__ __forceinline__ uint32_t scvt4(const u32x4& v, int j, float scale) {
+  uint32_t w;
+  if constexpr (DT == NC_BF16) {
+    const uint32_t lo = j == 0 ? v.x : v.z, hi = j == 0 ? v.y : v.w;
+    w = scvt_bf16<FMT, false>(lo, scale, 0u);
+    w = scvt_bf16<FMT, true>(hi, scale, w);
+  } else {
+    w = scvt_f32<FMT, false>(v.x, v.y, scale, 0u);
+    w = scvt_f32<FMT, true>(v.z, v.w, scale, w);
+  }
+  return sat4<FMT>(w);
+}
+
 // Code of a non-finite element (step 4): NaN -> 0x7F, +-Inf -> +-max.
 template <int FMT>
 __device__ __forceinline__ uint32_t nonfinite_code(uint32_t xb) {
@@ -193,12 +246,14 @@ __device__ __forceinline__ void count_elem(uint32_t ax, const CastParams& p, Acc
   acc.n_uf += ((ax - 1u) < p.t_uf) ? 1u : 0u;
 }
 
-// Cast VEC elements (a multiple of 4) at one exponent into VEC/4 packed
-// words; counts and the finite amax go to acc.
+// Cast one input vector (VEC elements, unpacked in xb) at one exponent into
+// VEC/4 packed words; counts and the finite amax go to acc.  SCALED: the
+// scaled converts with scale = 2^-K (|K| <= 127), else ldexp + convert.
 // Returns the wave-uniform "no Inf/NaN in this vector anywhere in the wave".
-template <int FMT, int VEC>
-__device__ __forceinline__ bool cast_vec(const uint32_t* xb, const CastParams& p, Acc& acc,
-                                         uint32_t* w) {
+template <int FMT, int DT, bool SCALED>
+__device__ __forceinline__ bool cast_vec(const u32x4& v, const uint32_t* xb, const CastParams& p, float scale,
+                                         Acc& acc, uint32_t* w) {
+  constexpr int VEC = In<DT>::VEC;
   uint32_t ax[VEC];
   uint32_t m = 0;
 #pragma unroll
@@ -207,7 +262,7 @@ __device__ __forceinline__ bool cast_vec(const uint32_t* xb, const CastParams& p
     m = max(m, ax[i]);
   }
 #pragma unroll
-  for (int j = 0; j < VEC / 4; ++j) w[j] = cvt4<FMT>(xb + 4 * j, p.K);
+  for (int j = 0; j < VEC / 4; ++j) w[j] = SCALED ? scvt4<FMT, DT>(v, j, scale) : cvt4<FMT>(xb + 4 * j, p.K);
 #pragma unroll
   for (int i = 0; i < VEC; ++i) count_elem(ax[i], p, acc);
   if (__ballot(m > kMaxFinite) == 0) {        // wave-uniform: no Inf/NaN here
@@ -440,9 +495,6 @@ __device__ __forceinline__ uint32_t f32_to_bf16_rne(uint32_t b) {
 // ---------------------------------------------------------------------------
 // Input vectors and error statistics (shared by the casts and the
 // separate statistics pass).
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
-typedef uint16_t u16x2 __attribute__((ext_vector_type(2)));
 
 // Streaming loads: every input byte is read once per pass, so the loads are
 // non-temporal (the cache lines are not kept for reuse).
@@ -454,9 +506,6 @@ __device__ __forceinline__ u32x2 ld_stream(const u32x2* p) { return __builtin_no
 __device__ __forceinline__ void st_stream(uint32_t* p, uint32_t v) { __builtin_nontemporal_store(v, p); }
 __device__ __forceinline__ void st_stream(u32x2* p, u32x2 v) { __builtin_nontemporal_store(v, p); }
 
-template <int DT> struct In;
-template <> struct In<NC_F32> { static constexpr int VEC = 4, BYTES = 4; };
-template <> struct In<NC_BF16> { static constexpr int VEC = 8, BYTES = 2; };
 
 // 16 input bytes -> VEC fp32 bit patterns (bf16 widens exactly by a shift).
 template <int DT>
