@@ -165,7 +165,18 @@ def cpu_baseline(rows: int, procs: int):
     n = rows * COLS
     return dict(value=n / dt / 1e9, unit="Gelem/s", cores=workers, kind="oracle",
                 sample=f"{rows} rows x {COLS} of the same workload ({n} elements), whole step, "
-                       f"{workers} worker processes, {dt:.1f} s")
+                       f"{workers} worker processes, {dt:.1f} s, {_cpu_model()}")
+
+
+def _cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "cpu model unknown"
 
 
 def _cpu_amax(b):

@@ -257,3 +257,71 @@ def test_llama_shaped_unscale_cast_1024_steps():
         amaxes = [Fraction(_f32(int(v) & 0xFFFFFFFF)) for v in counts[t, :, 4]]
         update(pol_o, sts, amaxes, list(counts[t, :, 3]))
     assert st[:, 0].cpu().tolist() == [s.k for s in sts]
+
+
+def test_llama_full_size_steps():
+    """The whole Llama-7B-shaped gradient set (225 fp32 tensors, 6.6 G
+    elements, one nc_cast_tensor call per step in the benchmark's launch
+    shape) for three steps: step 0 with current scaling, then delayed
+    scaling with a 16-step window.  Per step: 4096 sampled codes per tensor
+    against the oracle; every count exactly on three whole tensors (the
+    first 4096 x 4096, the last 4096 x 11008 and the 32000 x 4096
+    embedding); on every tensor n_finite + n_nonfinite = n, the injected
+    Inf/NaN count, the amax attained by some element, and no clip under
+    current scaling; the scale states replayed by the oracle."""
+    steps, W = 3, 16
+    g = workloads.LlamaGrads(layers=32)
+    T = len(g.sizes)
+    s_log2 = g.S_LOG2
+    ls = nc.new_loss_scale(s_log2)
+    st = nc.new_state(T)
+    hist = nc.new_history(T, W)
+    codes = [torch.empty(m, dtype=torch.uint8, device="cuda") for m in g.sizes]
+    desc, cnt = nc.tensors(g.bufs, codes)
+    ws = nc.new_workspace(desc, cnt)
+    pol_d = nc.policy("e4m3", "max_window", W, hysteresis=True)
+    full = [0, T - 2, T - 1]                          # whole-tensor checks
+    rng = np.random.default_rng(12)
+    sts = [ScaleState() for _ in range(T)]
+    pol_o = Policy(fmt=E4M3, est=EST_MAX_WINDOW, window=W, hysteresis=True)
+    for t in range(steps):
+        tens, _, _ = g.fill(t)
+        n_inj = np.bincount(tens, minlength=T)
+        if t == 0:
+            am = nc.new_counts(T)
+            nc.nc_amax(g.bufs, am, ls=ls, ws=ws)
+            nc.nc_scale_update(nc.policy("e4m3", "current", W, hysteresis=True), st, am)
+            torch.cuda.synchronize()
+            a0 = [Fraction(_f32(int(v) & 0xFFFFFFFF)) for v in am[:, 4].cpu().tolist()]
+            update(Policy(fmt=E4M3, est=EST_CURRENT, window=W, hysteresis=True), sts, a0, [0] * T)
+        k_t = st[:, 0].cpu().tolist()
+        assert k_t == [s.k for s in sts], t
+        out = nc.new_counts(T)
+        nc.nc_cast_tensor(g.bufs, codes, "e4m3", st, out, ls=ls, ws=ws)
+        nc.nc_scale_update(pol_d, st, out, hist)
+        torch.cuda.synchronize()
+        c = out.cpu().numpy()
+        for i in range(T):
+            n = g.sizes[i]
+            idx = torch.from_numpy(rng.integers(0, n, 4096)).cuda()
+            x = g.bufs[i][idx].cpu().numpy().astype(np.float64)
+            want = bulk.cast_f64(E4M3, x, k_t[i] - s_log2)[0]
+            assert np.array_equal(codes[i][idx].cpu().numpy(), want), (t, i)
+            assert c[i, 0] + c[i, 3] == n and c[i, 3] == n_inj[i], (t, i)
+            amax = _f32(int(c[i, 4]) & 0xFFFFFFFF)
+            if t == 0:
+                assert c[i, 1] == 0, (t, i)              # current scaling never clips
+            # the amax is attained: some finite element unscales to it
+            a = g.bufs[i].abs()
+            assert bool(((a * 2.0 ** -s_log2) == amax).any()) and bool((a[torch.isfinite(a)] * 2.0 ** -s_log2 <= amax).all()), (t, i)
+            del a
+        for i in full:
+            xs = g.bufs[i].cpu().numpy()
+            w = bulk.counts_threshold(E4M3, xs, k_t[i] - s_log2)
+            assert (c[i, 0], c[i, 1], c[i, 2], c[i, 3]) == (w["n_finite"], w["n_clip"], w["n_underflow"],
+                                                         w["n_nonfinite"]), (t, i)
+            assert _f32(int(c[i, 4]) & 0xFFFFFFFF) == float(np.float32(np.ldexp(w["amax"], -s_log2))), (t, i)
+            del xs
+        amaxes = [Fraction(_f32(int(v) & 0xFFFFFFFF)) for v in c[:, 4]]
+        update(pol_o, sts, amaxes, list(c[:, 3]))
+    assert st[:, 0].cpu().tolist() == [s.k for s in sts]
