@@ -207,9 +207,10 @@ k_dequant(const SegBatch b, const nc_scale_state* __restrict__ st) {
   }
 }
 
-// Dequant of column-block MX codes: a lane owns one col_slot of 8 columns,
-// reads their 8 scale bytes once and then, per row, 8 codes (8 bytes) and
-// writes 8 bf16 values (16 bytes); each column has its own shift.
+// Dequant of column-block MX codes: a lane owns one col_slot of 8 columns
+// and kDequantColRows rows, reads their 8 scale bytes once and then, per row, 8
+// codes (8 bytes) and writes 8 bf16 values (16 bytes); each column has its
+// own shift.
 __device__ __forceinline__ uint32_t bf16_pair2(f32x2 v, int sh0, int sh1) {
   v.x = __builtin_amdgcn_ldexpf(v.x, sh0);
   v.y = __builtin_amdgcn_ldexpf(v.y, sh1);
@@ -219,18 +220,18 @@ __device__ __forceinline__ uint32_t bf16_pair2(f32x2 v, int sh0, int sh1) {
 template <int FMT>
 NC_STREAM_KERNEL
 k_dequant_col(const SegBatch b) {
-  constexpr int VC = kDequantColCodes;
+  constexpr int VC = kDequantColCodes, R = kDequantColRows;
   const int64_t tile = blockIdx.x;
   const int s = seg_of(b.tile0, b.count, tile);
   const Seg& g = b.s[s];
-  const ColSlot cs = col_slot<VC>(g, tile - b.tile0[s], tile_len<kThreads>(b, s, tile));
+  const ColSlot cs = col_slot<VC, R>(g, tile - b.tile0[s], tile_len<kThreads>(b, s, tile));
   if (!cs.act) return;                      // no barriers below
   const int64_t cols = g.cols;
   const uint8_t* src = g.codes + cs.e0;
   uint16_t* dst = static_cast<uint16_t*>(g.y) + cs.e0;
-  u32x2 c[32];
+  u32x2 c[R];
 #pragma unroll
-  for (int r = 0; r < 32; ++r) c[r] = ld_stream(reinterpret_cast<const u32x2*>(src + r * cols));
+  for (int r = 0; r < R; ++r) c[r] = ld_stream(reinterpret_cast<const u32x2*>(src + r * cols));
   int sh[VC];                               // X of each column
   if (((uintptr_t)g.scales & 7u) == 0) {    // wave-uniform: one 8-byte load
     const u32x2 sw = *reinterpret_cast<const u32x2*>(g.scales + cs.sc);
@@ -242,7 +243,7 @@ k_dequant_col(const SegBatch b) {
   }
   __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-  for (int r = 0; r < 32; ++r) {
+  for (int r = 0; r < R; ++r) {
     u32x4 o;
     o.x = bf16_pair2(decode_pair<FMT, false>(c[r].x), sh[0], sh[1]);
     o.y = bf16_pair2(decode_pair<FMT, true>(c[r].x), sh[2], sh[3]);
@@ -365,8 +366,8 @@ k_stats(const SegBatch b, const nc_scale_state* __restrict__ st,
 }
 
 // Statistics of column-block MX codes: a lane owns one col_slot (VC =
-// 8 / BYTES columns), reads its VC scale bytes once, then per row 8 input
-// bytes and VC codes; two halves of 16 rows keep the registers in bounds.
+// 8 / BYTES columns of kStatsColRows rows), reads its VC scale bytes once, then
+// per row 8 input bytes and VC codes, in two halves.
 // Accumulation is unmasked as in k_stats, with the masked redo when an
 // Inf/NaN was met.
 template <int DT>
@@ -398,14 +399,14 @@ __device__ __forceinline__ void stats_col_row(u32x2 v, uint32_t w, const double*
 template <int FMT, int DT>
 NC_STREAM_KERNEL
 k_stats_col(const SegBatch b, double* __restrict__ stat_slots) {
-  constexpr int VC = kColBytes / In<DT>::BYTES;
-  constexpr int H = 16;                     // rows per half
+  constexpr int VC = kColBytes / In<DT>::BYTES, R = kStatsColRows;
+  constexpr int H = R / 2;                  // rows per half
   __shared__ double tab[256];
   __shared__ double lds_st[kRows * 6];
   const int64_t tile = blockIdx.x;
   const int s = seg_of(b.tile0, b.count, tile);
   const Seg& g = b.s[s];
-  const ColSlot cs = col_slot<VC>(g, tile - b.tile0[s], tile_len<kThreads>(b, s, tile));
+  const ColSlot cs = col_slot<VC, R>(g, tile - b.tile0[s], tile_len<kThreads>(b, s, tile));
   const int64_t cols = g.cols;
   const uint8_t* xs = static_cast<const uint8_t*>(g.x) + cs.e0 * In<DT>::BYTES;
   const uint8_t* qs = g.codes + cs.e0;
@@ -445,7 +446,7 @@ k_stats_col(const SegBatch b, double* __restrict__ stat_slots) {
   if (!stats_all_finite(sa)) {              // an Inf/NaN met: redo masked (rare; reloads)
     __asm__ volatile("" ::: "memory");      // keeps the compiler from holding the first loads for this
     sa.reset();
-    for (int row = 0; row < 32 && cs.act; ++row) {
+    for (int row = 0; row < R && cs.act; ++row) {
       const u32x2 v = *reinterpret_cast<const u32x2*>(xs + row * cols * In<DT>::BYTES);
       stats_col_row<DT, false>(v, ColCodes<DT>::load(qs + row * cols), tab, blk, sa);
     }

@@ -363,19 +363,24 @@ __device__ __forceinline__ void mx_tile(const Seg& g, int64_t e0, int rem, const
 #pragma unroll
   for (int u = 0; u < U; ++u) {
     const int vi = u * kThreads + threadIdx.x;
-    uint32_t xb[VEC], ax[VEC], w[VEC / 4];
+    uint32_t xb[VEC], w[VEC / 4];
     unpack<DT>(v[u], xb);
     uint32_t m = 0;
+    u16x2 h[4];
+    if constexpr (DT == NC_BF16) {               // packed 16-bit magnitudes (see count16)
+      h[0] = mag16(v[u].x); h[1] = mag16(v[u].y); h[2] = mag16(v[u].z); h[3] = mag16(v[u].w);
+      const u16x2 hm = __builtin_elementwise_max(__builtin_elementwise_max(h[0], h[1]),
+                                                 __builtin_elementwise_max(h[2], h[3]));
+      m = (uint32_t)max(hm.x, hm.y) << 16;
+    } else {
 #pragma unroll
-    for (int i = 0; i < VEC; ++i) {
-      ax[i] = xb[i] & kAbsMask;
-      m = max(m, ax[i]);
+      for (int i = 0; i < VEC; ++i) m = max(m, xb[i] & kAbsMask);
     }
     const bool clean = __ballot(m > kMaxFinite) == 0;   // wave-uniform
     if (!clean) {                                       // finite amax, count non-finite
       m = 0;
 #pragma unroll
-      for (int i = 0; i < VEC; ++i) m = max(m, finite_mag(ax[i], acc));
+      for (int i = 0; i < VEC; ++i) m = max(m, finite_mag(xb[i] & kAbsMask, acc));
     }
     acc.amax = max(acc.amax, m);
     const int X = mx_exponent<FMT, RULE>(group_max<GROUP>(m));
@@ -384,8 +389,14 @@ __device__ __forceinline__ void mx_tile(const Seg& g, int64_t e0, int rem, const
     const float scale = __builtin_amdgcn_ldexpf(1.0f, X);
 #pragma unroll
     for (int j = 0; j < VEC / 4; ++j) w[j] = scvt4<FMT, DT>(v[u], j, scale);
+    if constexpr (DT == NC_BF16) {
+      const u16x2 tc = splat16(p.t_clip), tu = splat16(p.t_uf);
 #pragma unroll
-    for (int i = 0; i < VEC; ++i) count_elem(ax[i], p, acc);
+      for (int j = 0; j < 4; ++j) count16(h[j], tc, tu, acc);
+    } else {
+#pragma unroll
+      for (int i = 0; i < VEC; ++i) count_elem(xb[i] & kAbsMask, p, acc);
+    }
     if (!clean) {
 #pragma unroll
       for (int j = 0; j < VEC / 4; ++j) w[j] = fix_nonfinite4<FMT>(w[j], xb + 4 * j);

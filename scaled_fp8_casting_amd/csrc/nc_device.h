@@ -130,8 +130,48 @@ struct Acc {
   uint32_t n_big;    // |x| bits above t_clip: every clip plus every non-finite
   uint32_t n_uf;
   uint32_t amax;     // largest finite |x| bits
-  __device__ void reset() { n_nf = n_big = n_uf = 0; amax = 0; }
+  u16x2 big16, uf16; // the bf16 paths' packed per-half counters (fold() adds them in)
+  __device__ void reset() {
+    n_nf = n_big = n_uf = 0;
+    amax = 0;
+    big16 = u16x2{0, 0};
+    uf16 = u16x2{0, 0};
+  }
+  __device__ void fold() {
+    n_big += (uint32_t)big16.x + big16.y;
+    n_uf += (uint32_t)uf16.x + uf16.y;
+    big16 = u16x2{0, 0};
+    uf16 = u16x2{0, 0};
+  }
 };
+
+// bf16 inputs, two per 32-bit word: the magnitude, clip and underflow tests
+// on packed 16-bit halves.  A bf16 x has fp32 bits X << 16, so |x| bits >
+// t_clip <=> X > t_clip >> 16, and 0 < |x| bits <= t_uf <=> 1 <= X <=
+// t_uf >> 16 (integer thresholds, exact).  Counts: saturating subtract,
+// clamp to 1, packed add; each half counts at most a few dozen elements per
+// tile, far below 2^16.
+__device__ __forceinline__ u16x2 mag16(uint32_t w) { return __builtin_bit_cast(u16x2, w & 0x7FFF7FFFu); }
+// [a > b] per 16-bit half: min(max(a - b, 0), 1) -- v_pk_sub_u16 with clamp,
+// then v_pk_min_u16 against 1 in both halves (a register operand: an inline
+// constant reaches the low half only).  Written as asm: the compiler
+// otherwise turns it into a compare, a select and a repack per half.
+__device__ __forceinline__ u16x2 gt16(u16x2 a, u16x2 b) {
+  uint32_t r;
+  __asm__("v_pk_sub_u16 %0, %1, %2 clamp\n\tv_pk_min_u16 %0, %0, %3"
+          : "=&v"(r) : "v"(__builtin_bit_cast(uint32_t, a)), "v"(__builtin_bit_cast(uint32_t, b)),
+            "v"(0x00010001u));
+  return __builtin_bit_cast(u16x2, r);
+}
+__device__ __forceinline__ void count16(u16x2 h, u16x2 tc, u16x2 tu, Acc& acc) {
+  const u16x2 one = {1, 1};
+  acc.big16 += gt16(h, tc);            // |x| > t_clip
+  acc.uf16 += gt16(tu, h - one);       // 1 <= |x| <= t_uf (h = 0 wraps to 0xFFFF)
+}
+__device__ __forceinline__ u16x2 splat16(uint32_t t) {
+  const uint16_t v = (uint16_t)(t >> 16);
+  return u16x2{v, v};
+}
 
 // |x| bits with Inf/NaN mapped to 0 (for the amax), counting non-finite
 // elements.
@@ -254,6 +294,30 @@ template <int FMT, int DT, bool SCALED>
 __device__ __forceinline__ bool cast_vec(const u32x4& v, const uint32_t* xb, const CastParams& p, float scale,
                                          Acc& acc, uint32_t* w) {
   constexpr int VEC = In<DT>::VEC;
+  if constexpr (DT == NC_BF16 && SCALED) {
+    // packed 16-bit magnitudes: max and counts without unpacking
+    const u16x2 h0 = mag16(v.x), h1 = mag16(v.y), h2 = mag16(v.z), h3 = mag16(v.w);
+    const u16x2 hm = __builtin_elementwise_max(__builtin_elementwise_max(h0, h1), __builtin_elementwise_max(h2, h3));
+    const uint32_t m = (uint32_t)max(hm.x, hm.y) << 16;
+    w[0] = scvt4<FMT, DT>(v, 0, scale);
+    w[1] = scvt4<FMT, DT>(v, 1, scale);
+    const u16x2 tc = splat16(p.t_clip), tu = splat16(p.t_uf);
+    count16(h0, tc, tu, acc);
+    count16(h1, tc, tu, acc);
+    count16(h2, tc, tu, acc);
+    count16(h3, tc, tu, acc);
+    if (__ballot(m > kMaxFinite) == 0) {      // wave-uniform: no Inf/NaN here
+      acc.amax = max(acc.amax, m);
+      return true;
+    }
+    uint32_t mf = 0;
+#pragma unroll
+    for (int i = 0; i < VEC; ++i) mf = max(mf, finite_mag(xb[i] & kAbsMask, acc));
+    acc.amax = max(acc.amax, mf);
+#pragma unroll
+    for (int j = 0; j < VEC / 4; ++j) w[j] = fix_nonfinite4<FMT>(w[j], xb + 4 * j);
+    return false;
+  }
   uint32_t ax[VEC];
   uint32_t m = 0;
 #pragma unroll
@@ -395,12 +459,15 @@ __device__ __forceinline__ int tile_len(const SegBatch& b, int s, int64_t t) {
 }
 
 // Column-block MX (blocks of 32 consecutive rows of one column).  A "slot"
-// is VC adjacent columns of one 32-row band: 32 * VC elements, VC blocks.
-// Slots are numbered band by band, left to right; tile t of a tensor is
+// is VC adjacent columns of R consecutive rows inside one 32-row band (R
+// divides 32): R * VC elements, all under the same VC scale bytes.  Slots
+// are numbered row group by row group, left to right; tile t of a tensor is
 // slots [256 t, 256 t + 256), one per lane, so the lanes of a wave hold
 // consecutive pieces of the same rows and every row access of a wave is one
-// contiguous run.  A tensor has n / (32 VC) < 2^29 slots (rows are a
-// multiple of 32, so cols <= n / 32), which keeps the division 32-bit.
+// contiguous run.  The cast needs whole bands (R = 32: a block's max before
+// any code); dequant and statistics take shorter slots, which keep their
+// tiles small.  A tensor has n / (R VC) < 2^30 slots (rows are a multiple
+// of 32, so cols <= n / 32), which keeps the division 32-bit.
 struct ColSlot {
   int64_t e0;   // element index of the slot's top-left element
   int64_t sc;   // index of the slot's first scale byte ((rows / 32) x cols, row-major)
@@ -409,16 +476,17 @@ struct ColSlot {
 // An idle lane gets the tensor's slot 0 -- in bounds, so its loads need no
 // predicate (they would otherwise become a branch per row) -- and must
 // discard what it reads and store nothing.
-template <int VC>
+template <int VC, int R = 32>
 __device__ __forceinline__ ColSlot col_slot(const Seg& g, int64_t t, int rem) {
-  const uint32_t per_band = (uint32_t)(g.cols / VC);
+  static_assert(32 % R == 0, "a slot stays inside one band");
+  const uint32_t per_group = (uint32_t)(g.cols / VC);
   const uint32_t j = (uint32_t)t * (uint32_t)kThreads + threadIdx.x;
-  const uint32_t band = j / per_band;
-  const uint32_t cg = j - band * per_band;
+  const uint32_t grp = j / per_group;
+  const uint32_t cg = j - grp * per_group;
   ColSlot c;
   c.act = (int)threadIdx.x < rem;
-  c.e0 = c.act ? (int64_t)band * 32 * g.cols + (int64_t)cg * VC : 0;
-  c.sc = c.act ? (int64_t)band * g.cols + (int64_t)cg * VC : 0;
+  c.e0 = c.act ? (int64_t)grp * R * g.cols + (int64_t)cg * VC : 0;
+  c.sc = c.act ? (int64_t)(grp / (32 / R)) * g.cols + (int64_t)cg * VC : 0;
   return c;
 }
 
@@ -440,7 +508,8 @@ __device__ __forceinline__ uint64_t wave_sum_u64(uint64_t v) {
 // The workgroup's totals -> its slot: DPP row reductions, one LDS entry per
 // row, thread 0 over the rows.  Called by all threads (full EXEC); lds holds
 // kRows * 4 words.
-__device__ inline void write_count_slot(const Acc& acc, CountSlot* slot, uint32_t* lds) {
+__device__ inline void write_count_slot(Acc acc, CountSlot* slot, uint32_t* lds) {
+  acc.fold();
   const uint32_t m = row_max_u32(acc.amax);
   const uint32_t nf = row_sum_u32(acc.n_nf), big = row_sum_u32(acc.n_big), uf = row_sum_u32(acc.n_uf);
   if ((threadIdx.x & 15) == 0) {

@@ -24,14 +24,18 @@ inline int64_t tile_elems(int in_bytes, int vecs) { return (int64_t)kThreads * (
 constexpr int64_t kMinWsTile = (int64_t)kThreads * 4 * kCastVecs;
 
 // Column-block MX (col_slot): a lane reads 8 input bytes per row (4 bf16 or
-// 2 fp32 columns), or 8 codes per row in dequant; a tile is 256 slots of 32
-// rows, always at least kMinWsTile elements, so the workspace bound above
-// covers these calls too.
+// 2 fp32 columns), or 8 codes per row in dequant.  Rows per slot, measured
+// best on MI355X: the cast needs whole 32-row bands; the statistics pass is
+// fastest with them too; dequant with 8-row slots (smaller tiles: 16 KiB of
+// codes per workgroup instead of 64).  A tile is 256 slots, always at least
+// kMinWsTile elements, so the workspace bound above covers these calls too.
 constexpr int kColBytes = 8;
 constexpr int kDequantColCodes = 8;
-inline int64_t col_unit(int in_bytes) { return 32 * (kColBytes / in_bytes); }
-constexpr int64_t kDequantColUnit = 32 * kDequantColCodes;
-static_assert(kThreads * 32 * 2 >= kMinWsTile, "column tiles are no smaller than kMinWsTile");
+constexpr int kDequantColRows = 8;
+constexpr int kStatsColRows = 32;
+inline int64_t col_unit(int in_bytes, int rows = 32) { return rows * (kColBytes / in_bytes); }
+constexpr int64_t kDequantColUnit = kDequantColRows * kDequantColCodes;
+static_assert(kThreads * kStatsColRows * 2 >= kMinWsTile, "column tiles are no smaller than kMinWsTile");
 
 // The update/step-ratio monitor: 256 lanes x eight 16-byte vectors of w (and
 // of d) per tile -- read-only, like the amax pass.
