@@ -135,8 +135,8 @@ k_cast_pt(const SegBatch b, const nc_scale_state* __restrict__ st,
       if (act) dst[i] = (uint8_t)q;
     }
   }
-  write_count_slot(acc, slots + tile, lds);
-  if constexpr (STATS) write_stat_slot(sa, stat_slots + tile * 6, lds_st);
+  if constexpr (STATS) write_count_stat_slots(acc, sa, slots + tile, stat_slots + tile * 6, lds, lds_st);
+  else write_count_slot(acc, slots + tile, lds);
 }
 
 // ---------------------------------------------------------------------------
@@ -468,8 +468,8 @@ k_cast_mx(const SegBatch b, CountSlot* __restrict__ slots, double* __restrict__ 
   if constexpr (STATS) sa.reset();
   if (full) mx_tile<FMT, DT, RULE, STATS, true, U>(g, e0, rem, v, acc, sa, tab);
   else mx_tile<FMT, DT, RULE, STATS, false, U>(g, e0, rem, v, acc, sa, tab);
-  write_count_slot(acc, slots + tile, lds);
-  if constexpr (STATS) write_stat_slot(sa, stat_slots + tile * 6, lds_st);
+  if constexpr (STATS) write_count_stat_slots(acc, sa, slots + tile, stat_slots + tile * 6, lds, lds_st);
+  else write_count_slot(acc, slots + tile, lds);
 }
 
 // ---------------------------------------------------------------------------
@@ -608,8 +608,8 @@ k_cast_mx_col(const SegBatch b, CountSlot* __restrict__ slots, double* __restric
       for (int i = 0; i < VC; ++i) sd[i] = (uint8_t)(sb >> (8 * i));
     }
   }
-  write_count_slot(acc, slots + tile, lds);
-  if constexpr (STATS) write_stat_slot(sa, stat_slots + tile * 6, lds_st);
+  if constexpr (STATS) write_count_stat_slots(acc, sa, slots + tile, stat_slots + tile * 6, lds, lds_st);
+  else write_count_slot(acc, slots + tile, lds);
 }
 
 template <int FMT, int DT>

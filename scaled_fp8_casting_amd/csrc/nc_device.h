@@ -683,4 +683,42 @@ __device__ inline void write_stat_slot(const StatAcc& a, double* slot, double* l
   }
 }
 
+// The casts with fused statistics: both slots in one epilogue (one LDS
+// round trip and one barrier instead of two).  lds holds kRows * 4 words,
+// lds_st kRows * 6 doubles.
+__device__ inline void write_count_stat_slots(Acc acc, const StatAcc& a, CountSlot* slot, double* stat_slot,
+                                              uint32_t* lds, double* lds_st) {
+  acc.fold();
+  const uint32_t m = row_max_u32(acc.amax);
+  const uint32_t nf = row_sum_u32(acc.n_nf), big = row_sum_u32(acc.n_big), uf = row_sum_u32(acc.n_uf);
+  double v[6];
+#pragma unroll
+  for (int j = 0; j < 6; ++j) v[j] = row_sum_f64(a.s[j]);
+  if ((threadIdx.x & 15) == 0) {
+    const int r = threadIdx.x >> 4;
+    lds[r * 4 + 0] = m;
+    lds[r * 4 + 1] = nf;
+    lds[r * 4 + 2] = big;
+    lds[r * 4 + 3] = uf;
+#pragma unroll
+    for (int j = 0; j < 6; ++j) lds_st[r * 6 + j] = v[j];
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    CountSlot c{0u, 0u, 0u, 0u};
+    for (int r = 0; r < kRows; ++r) {
+      c.amax = max(c.amax, lds[r * 4 + 0]);
+      c.n_nf += lds[r * 4 + 1];
+      c.n_big += lds[r * 4 + 2];
+      c.n_uf += lds[r * 4 + 3];
+    }
+    *slot = c;
+  } else if (threadIdx.x >= 64 && threadIdx.x < 70) {   // another wave: the sums run beside thread 0's
+    const int j = threadIdx.x - 64;
+    double t = 0.0;
+    for (int r = 0; r < kRows; ++r) t += lds_st[r * 6 + j];
+    stat_slot[j] = t;
+  }
+}
+
 }  // namespace nc
