@@ -10,7 +10,7 @@ from oracle import E4M3, E5M2
 from oracle import bulk
 from oracle import cast as t0
 import workloads
-from tests._gpu import (assert_counts, codes_like, dev_bf16, dev_f32, host_u8, state_with_k)
+from tests._gpu import (assert_counts, codes_like, dev_bf16, dev_f32, host_u8, state_with_k, stats_close)
 
 pytestmark = pytest.mark.gpu
 FMTS = [("e4m3", E4M3), ("e5m2", E5M2)]
@@ -243,17 +243,37 @@ def test_mx_parity(dtype, rule, name, fmt, rows, cols):
 
 
 def test_tanh_activations_mx_full_size():
-    """4096 x 4096 bf16 tanh(N(0, 1.5)), OCP and +1 rules, in full."""
+    """4096 x 4096 bf16 tanh(N(0, 1.5)), OCP and +1 rules, in full: codes,
+    scales, counts, and the statistics the workload reports per rule -- the
+    clipped fraction, the mean signed error and the sign-aligned bias
+    ([Drift, "What the measurements said"]: how much, and which way) --
+    against the oracle, then against the expected values derived for this
+    input (OCP: clip ~0.178, sign-aligned ~-1.3e-2; +1: no clip, ~+1.2e-3)."""
     bits = workloads.tanh_activations()
     x64 = bulk.bf16_bits_to_f64(bits.ravel())
     xd = dev_bf16(bits.ravel())
+    n = x64.size
     for rule in ("ocp", "plus1"):
         codes, scales, counts = _cast_mx(xd, 4096, "e4m3", rule)
         wc, ws, wn = bulk.cast_mx_f64(E4M3, x64, 4096, rule)
         assert np.array_equal(scales, ws) and np.array_equal(codes, wc)
         assert_counts(counts, wn)
-        frac = counts["n_clip"] / x64.size
+        frac = counts["n_clip"] / n
         assert (0.175 < frac < 0.181) if rule == "ocp" else frac == 0
+        st = nc.new_stats(1)
+        cd = torch.from_numpy(codes).cuda()
+        sd = torch.from_numpy(scales).cuda()
+        nc.nc_cast_stats([xd], [cd], "e4m3", st, scales=[sd], cols=[4096])
+        torch.cuda.synchronize()
+        got = st[0].cpu().tolist()
+        want = bulk.stats_f64(E4M3, x64, wc, np.repeat(127 - ws.astype(np.int64), 32))
+        stats_close(got, want)
+        mean_e, aligned = got[0] / n, got[3] / n
+        assert abs(mean_e) < 1e-4, (rule, mean_e)
+        if rule == "ocp":
+            assert -1.4e-2 < aligned < -1.25e-2, aligned
+        else:
+            assert 1.0e-3 < aligned < 1.35e-3, aligned
 
 
 def test_argument_errors_on_device():
