@@ -250,7 +250,7 @@ nc_status nc_cast_mx(const nc_tensor* t, int32_t count, nc_dtype dtype, nc_fmt f
   if (out == nullptr) return NC_E_ARG;
   if ((s = check_ws(t, count, ws, ws_bytes)) != NC_OK) return s;
   if (t[0].mx_axis == NC_MX_COLS)
-    return for_batches(t, count, kThreads, nullptr, [&](const SegBatch& b) {
+    return for_batches(t, count, kThreads / col_cast_split(dtype), nullptr, [&](const SegBatch& b) {
       const Ws w = ws_of(b, ws);
       nc_status r = hip_status(launch_cast_mx_col(b, dtype, fmt, rule, stats != nullptr, w,
                                                   Launch{b.tile0[b.count], (hipStream_t)stream}));

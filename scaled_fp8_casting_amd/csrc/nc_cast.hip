@@ -474,32 +474,39 @@ k_cast_mx(const SegBatch b, CountSlot* __restrict__ slots, double* __restrict__ 
 
 // ---------------------------------------------------------------------------
 // MX with blocks down the columns (32 consecutive rows of one column share
-// X): the layout of an operand consumed transposed.  A lane owns one slot
-// (col_slot): VC = 8 / BYTES adjacent columns of a 32-row band, 8 input
-// bytes per row.  It loads all 32 rows, takes each column's finite max in
-// registers (no exchange between lanes), then casts and stores row by row.
+// X): the layout of an operand consumed transposed.  A slot (col_slot) is
+// VC = 8 / BYTES adjacent columns of a 32-row band, 8 input bytes per row;
+// SPLIT adjacent lanes share it (two for bf16), each loading 32 / SPLIT of
+// its rows.  Each
+// lane takes its columns' finite max over its rows in registers, the lanes
+// of a slot exchange theirs by one DPP swap, and each casts and stores its
+// own rows.
 template <int FMT, int DT, int RULE, bool STATS>
 NC_STREAM_KERNEL
 k_cast_mx_col(const SegBatch b, CountSlot* __restrict__ slots, double* __restrict__ stat_slots) {
   constexpr int VC = kColBytes / In<DT>::BYTES;    // 4 bf16 or 2 fp32 columns
+  constexpr int SPLIT = col_cast_split(DT), RL = 32 / SPLIT, SLOTS = kThreads / SPLIT;
+  static_assert(SPLIT == 1 || SPLIT == 2, "lanes per slot");
   __shared__ uint32_t lds[kRows * 4];
   __shared__ double lds_st[STATS ? kRows * 6 : 1];
   __shared__ double tab[STATS ? 256 : 1];
   const int64_t tile = blockIdx.x;
   const int s = seg_of(b.tile0, b.count, tile);
   const Seg& g = b.s[s];
-  const int rem = tile_len<kThreads>(b, s, tile);
-  const ColSlot cs = col_slot<VC>(g, tile - b.tile0[s], rem);
+  const int rem = tile_len<SLOTS>(b, s, tile);                 // slots in this tile
+  const uint32_t slot = threadIdx.x / SPLIT, part = threadIdx.x % SPLIT;
+  const ColSlot cs = col_slot_at<VC>(g, (uint32_t)(tile - b.tile0[s]) * SLOTS + slot, (int)slot < rem);
   const int64_t cols = g.cols;
   const int64_t stride = cols * In<DT>::BYTES;
-  const uint8_t* src = static_cast<const uint8_t*>(g.x) + cs.e0 * In<DT>::BYTES;
-  u32x2 v[32];
+  const int64_t r0 = (int64_t)part * RL;                       // this lane's first row of the band
+  const uint8_t* src = static_cast<const uint8_t*>(g.x) + (cs.e0 + r0 * cols) * In<DT>::BYTES;
+  u32x2 v[RL];
 #pragma unroll
-  for (int r = 0; r < 32; ++r) v[r] = ld_stream(reinterpret_cast<const u32x2*>(src + r * stride));
+  for (int r = 0; r < RL; ++r) v[r] = ld_stream(reinterpret_cast<const u32x2*>(src + r * stride));
   __builtin_amdgcn_sched_barrier(0);
-  if (rem < kThreads && !cs.act) {          // the tensor's last tile: idle lanes hold zeros
+  if (rem < SLOTS && !cs.act) {             // the tensor's last tile: idle lanes hold zeros
 #pragma unroll
-    for (int r = 0; r < 32; ++r) v[r] = u32x2{0u, 0u};
+    for (int r = 0; r < RL; ++r) v[r] = u32x2{0u, 0u};
   }
   if constexpr (STATS) {
     fill_stat_table<FMT>(tab, 0);
@@ -510,12 +517,12 @@ k_cast_mx_col(const SegBatch b, CountSlot* __restrict__ slots, double* __restric
   // per-column max of |x| bits (an idle lane holds zeros: X = -127, no
   // counts).  Formed on the packed words with operations of its own -- bf16
   // magnitudes by packed 16-bit max, fp32 magnitudes as x << 1 -- so the
-  // compiler keeps no unpacked copy of the 32 rows alive into the cast loop.
+  // compiler keeps no unpacked copy of the rows alive into the cast loop.
   uint32_t m[VC], mall = 0;
   if constexpr (DT == NC_BF16) {
     u16x2 mx = {0, 0}, my = {0, 0};
 #pragma unroll
-    for (int r = 0; r < 32; ++r) {
+    for (int r = 0; r < RL; ++r) {
       mx = __builtin_elementwise_max(mx, __builtin_bit_cast(u16x2, v[r].x & 0x7FFF7FFFu));
       my = __builtin_elementwise_max(my, __builtin_bit_cast(u16x2, v[r].y & 0x7FFF7FFFu));
     }
@@ -524,7 +531,7 @@ k_cast_mx_col(const SegBatch b, CountSlot* __restrict__ slots, double* __restric
   } else {
     uint32_t m2[2] = {0u, 0u};
 #pragma unroll
-    for (int r = 0; r < 32; ++r) {
+    for (int r = 0; r < RL; ++r) {
       m2[0] = max(m2[0], v[r].x << 1);
       m2[1] = max(m2[1], v[r].y << 1);
     }
@@ -537,12 +544,16 @@ k_cast_mx_col(const SegBatch b, CountSlot* __restrict__ slots, double* __restric
 #pragma unroll
     for (int i = 0; i < VC; ++i) m[i] = 0;
 #pragma unroll
-    for (int r = 0; r < 32; ++r) {
+    for (int r = 0; r < RL; ++r) {
       uint32_t xb[VC];
       unpack8<DT>(v[r], xb);
 #pragma unroll
       for (int i = 0; i < VC; ++i) m[i] = max(m[i], finite_mag(xb[i] & kAbsMask, acc));
     }
+  }
+  if constexpr (SPLIT == 2) {                            // the partner lane's rows: quad_perm [1,0,3,2]
+#pragma unroll
+    for (int i = 0; i < VC; ++i) m[i] = max(m[i], dpp_u32<0xB1>(m[i]));
   }
   int X[VC];
   CastParams p[VC];
@@ -554,9 +565,9 @@ k_cast_mx_col(const SegBatch b, CountSlot* __restrict__ slots, double* __restric
   }
   StatAcc sa;
   if constexpr (STATS) sa.reset();
-  uint8_t* dst = g.codes + cs.e0;
+  uint8_t* dst = g.codes + cs.e0 + r0 * cols;
 #pragma unroll
-  for (int r = 0; r < 32; ++r) {
+  for (int r = 0; r < RL; ++r) {
     // the row's words pass through an empty asm: values derived from them
     // above (the non-finite path) cannot be hoisted and held for this loop
     u32x2 vr = v[r];
@@ -585,7 +596,7 @@ k_cast_mx_col(const SegBatch b, CountSlot* __restrict__ slots, double* __restric
       }
     }
     // the row's counts are taken here: left alone, the compiler sinks every
-    // compare to the end of the loop and keeps all 32 rows' magnitudes live
+    // compare to the end of the loop and keeps all the rows' magnitudes live
     __asm__ volatile("" : "+v"(acc.n_big), "+v"(acc.n_uf));
     __builtin_amdgcn_sched_barrier(0);   // one row at a time (register pressure)
     if (cs.act) {
@@ -594,12 +605,12 @@ k_cast_mx_col(const SegBatch b, CountSlot* __restrict__ slots, double* __restric
       else __builtin_nontemporal_store((uint16_t)w, reinterpret_cast<uint16_t*>(d));
     }
   }
-  if (cs.act) {
+  if (cs.act && part == 0) {
     uint8_t* sd = g.scales + cs.sc;
     uint32_t sb = 0;
 #pragma unroll
     for (int i = 0; i < VC; ++i) sb |= (uint32_t)(X[i] + 127) << (8 * i);
-    // one word per lane when the scale array allows it (wave-uniform)
+    // one word per slot when the scale array allows it (wave-uniform)
     if (((uintptr_t)g.scales & (VC - 1)) == 0) {
       if constexpr (VC == 4) *reinterpret_cast<uint32_t*>(sd) = sb;
       else *reinterpret_cast<uint16_t*>(sd) = (uint16_t)sb;

@@ -462,9 +462,9 @@ __device__ __forceinline__ int tile_len(const SegBatch& b, int s, int64_t t) {
 // is VC adjacent columns of R consecutive rows inside one 32-row band (R
 // divides 32): R * VC elements, all under the same VC scale bytes.  Slots
 // are numbered row group by row group, left to right; tile t of a tensor is
-// slots [256 t, 256 t + 256), one per lane, so the lanes of a wave hold
-// consecutive pieces of the same rows and every row access of a wave is one
-// contiguous run.  The cast needs whole bands (R = 32: a block's max before
+// slots [S t, S t + S), S = 256 / (lanes per slot), in lane order, so the
+// lanes of a wave hold consecutive pieces of the same rows and every row
+// access of a wave is one contiguous run per group of lanes that share a row.  The cast needs whole bands (R = 32: a block's max before
 // any code); dequant and statistics take shorter slots, which keep their
 // tiles small.  A tensor has n / (R VC) < 2^30 slots (rows are a multiple
 // of 32, so cols <= n / 32), which keeps the division 32-bit.
@@ -477,17 +477,21 @@ struct ColSlot {
 // predicate (they would otherwise become a branch per row) -- and must
 // discard what it reads and store nothing.
 template <int VC, int R = 32>
-__device__ __forceinline__ ColSlot col_slot(const Seg& g, int64_t t, int rem) {
+__device__ __forceinline__ ColSlot col_slot_at(const Seg& g, uint32_t j, bool act) {
   static_assert(32 % R == 0, "a slot stays inside one band");
   const uint32_t per_group = (uint32_t)(g.cols / VC);
-  const uint32_t j = (uint32_t)t * (uint32_t)kThreads + threadIdx.x;
   const uint32_t grp = j / per_group;
   const uint32_t cg = j - grp * per_group;
   ColSlot c;
-  c.act = (int)threadIdx.x < rem;
-  c.e0 = c.act ? (int64_t)grp * R * g.cols + (int64_t)cg * VC : 0;
-  c.sc = c.act ? (int64_t)(grp / (32 / R)) * g.cols + (int64_t)cg * VC : 0;
+  c.act = act;
+  c.e0 = act ? (int64_t)grp * R * g.cols + (int64_t)cg * VC : 0;
+  c.sc = act ? (int64_t)(grp / (32 / R)) * g.cols + (int64_t)cg * VC : 0;
   return c;
+}
+// Slot of this lane in tile t (one slot per lane; rem slots in the tile).
+template <int VC, int R = 32>
+__device__ __forceinline__ ColSlot col_slot(const Seg& g, int64_t t, int rem) {
+  return col_slot_at<VC, R>(g, (uint32_t)t * (uint32_t)kThreads + threadIdx.x, (int)threadIdx.x < rem);
 }
 
 // Workspace slots.  A workgroup's counts: finite-|x| max (bits), non-finite,

@@ -33,9 +33,13 @@ constexpr int kColBytes = 8;
 constexpr int kDequantColCodes = 8;
 constexpr int kDequantColRows = 8;
 constexpr int kStatsColRows = 32;
+// Lanes per slot in the column cast: two for bf16 (16 rows each, half the
+// registers of a whole band), one for fp32 (measured faster whole).
+constexpr int col_cast_split(int dtype) { return dtype == NC_BF16 ? 2 : 1; }
 inline int64_t col_unit(int in_bytes, int rows = 32) { return rows * (kColBytes / in_bytes); }
 constexpr int64_t kDequantColUnit = kDequantColRows * kDequantColCodes;
 static_assert(kThreads * kStatsColRows * 2 >= kMinWsTile, "column tiles are no smaller than kMinWsTile");
+static_assert(kThreads / col_cast_split(NC_BF16) * 32 * 2 >= kMinWsTile, "column tiles are no smaller than kMinWsTile");
 
 // The update/step-ratio monitor: 256 lanes x eight 16-byte vectors of w (and
 // of d) per tile -- read-only, like the amax pass.
