@@ -156,8 +156,9 @@ __device__ __forceinline__ void philox10(uint32_t (&c)[4], uint32_t k0, uint32_t
   for (int r = 0; r < 10; ++r) {
     const uint64_t p0 = (uint64_t)c[0] * 0xD2511F53u;
     const uint64_t p1 = (uint64_t)c[2] * 0xCD9E8D57u;
-    const uint32_t n0 = (uint32_t)(p1 >> 32) ^ c[1] ^ k0;
-    const uint32_t n2 = (uint32_t)(p0 >> 32) ^ c[3] ^ k1;
+    // three-input xors in one instruction each (truth table 0x96)
+    const uint32_t n0 = __builtin_amdgcn_bitop3_b32((uint32_t)(p1 >> 32), c[1], k0, 0x96);
+    const uint32_t n2 = __builtin_amdgcn_bitop3_b32((uint32_t)(p0 >> 32), c[3], k1, 0x96);
     c[0] = n0;
     c[1] = (uint32_t)p1;
     c[2] = n2;
@@ -183,43 +184,38 @@ __device__ __forceinline__ void sr_block(uint32_t blk, const SrKey& key, uint32_
 }
 
 // Stochastic rounding of one |x| (bits ax, finite, |x| 2^K <= max) at
-// exponent K with uniform u, as m * 2^eq (m <= 2^(MB+1), exact in fp32).
-// y = S 2^lsb exactly (S the fp32 significand); the grid spacing at y is
-// 2^eq with eq = max(binade(y), EMIN) - MB; the d = eq - lsb low bits of S
-// are discarded.  floor(S 2^32 / 2^d) holds the kept part in its high word
-// and F = floor(t 2^32) in its low word; t 2^32 has a fraction (`sticky`)
-// only when d > 32, from the bits of S below 2^(d - 32).  The magnitude
-// rounds up iff u < t 2^32, i.e. u < F, or u == F with a fraction.  d <= 0:
-// y is on the grid (m = S 2^-d, no draw).  Straight-line code: the rule is
-// combined with bitwise operations (a short-circuit form compiles to a
-// branch per element); lanes whose result the caller discards compute with
-// every shift kept in range.
+// exponent K with uniform u: returns m 2^(K - s), m the drawn multiple of
+// the grid spacing q at y = |x| 2^K (q = 2^(max(floor(log2 y), EMIN) - MB)).
+// With |x| = f 2^ex, f in [0.5, 1), yq = y / q = |x| 2^s for
+// s = min(MB + 1 - ex, K - EMIN + MB) (c2 = K - EMIN + MB).  Where yq >=
+// 2^-32 it is a normal binary32 number, so yq, fl = floor(yq), yq - fl and
+// (yq - fl) 2^32 are exact, and T = ceil((yq - fl) 2^32) = ceil(t 2^32):
+// u < t 2^32 iff u < T for an integer u.  Below 2^-32, yq may lose bits or
+// underflow, but there 0 < t 2^32 < 1 for any nonzero x and T must be 1:
+// yq is raised to min(|x|, 2^-33), positive exactly when x is, and
+// ceil(2^-33 2^32) = 1.  The raise is an integer max and min on the bit
+// patterns (non-negative floats order as their bits).  No branch and no
+// 64-bit shift.
 template <int FMT>
-__device__ __forceinline__ float sr_value(uint32_t ax, int K, uint32_t u, uint32_t* m_out) {
+__device__ __forceinline__ float sr_value(uint32_t ax, int K, int c2, uint32_t u, float& m) {
   using F = Fp8<FMT>;
-  const uint32_t E = ax >> 23;
-  const uint32_t S = E ? ((ax & 0x7FFFFFu) | 0x800000u) : ax;
-  const int lsb = (E ? (int)E : 1) - 150 + K;
-  const int ey = (31 - __clz(S | 1u)) + lsb;
-  const int eq = max(ey, F::EMIN) - F::MB;
-  const int d = eq - lsb;
-  const uint32_t dd = (uint32_t)min(max(d, 0), 63);
-  const uint64_t Q = ((uint64_t)S << 32) >> dd;
-  const uint32_t Fr = (uint32_t)Q, kept = (uint32_t)(Q >> 32);
-  const uint32_t sh = dd > 32u ? min(dd - 32u, 31u) : 0u;
-  const uint32_t sticky = (S & ((1u << sh) - 1u)) != 0u ? 1u : 0u;
-  const uint32_t up = (u < Fr ? 1u : 0u) | ((u == Fr ? 1u : 0u) & sticky);
-  const uint32_t exact = S << (uint32_t)min(max(-d, 0), 31);
-  const uint32_t m = d < 0 ? exact : kept + up;
-  *m_out = m;
-  return __builtin_amdgcn_ldexpf((float)m, eq);
+  const float xf = __uint_as_float(ax);
+  const int s = min(F::MB + 1 - __builtin_amdgcn_frexp_expf(xf), c2);
+  const float yq = __uint_as_float(max(__float_as_uint(__builtin_amdgcn_ldexpf(xf, s)), min(ax, 0x2F000000u)));
+  const float fl = __builtin_floorf(yq);
+  // v_cvt_u32_f32 saturates (NaN -> 0): defined for a discarded lane's Inf
+  // or NaN, where a C conversion would not be
+  uint32_t T;
+  __asm__("v_cvt_u32_f32 %0, %1" : "=v"(T) : "v"(__builtin_ceilf(__builtin_amdgcn_ldexpf(yq - fl, 32))));
+  m = fl + (u < T ? 1.0f : 0.0f);
+  return __builtin_amdgcn_ldexpf(m, K - s);
 }
 
 // Four elements -> four codes (byte i = element i), counts and amax to acc.
 // Clips saturate; non-finite elements are rewritten by the caller's uniform
 // branch (as in the round-to-nearest cast).
 template <int FMT>
-__device__ __forceinline__ uint32_t sr4(const uint32_t* xb, const CastParams& p, const uint32_t (&r)[4],
+__device__ __forceinline__ uint32_t sr4(const uint32_t* xb, const CastParams& p, int c2, const uint32_t (&r)[4],
                                         Acc& acc) {
   constexpr float kMaxF = 1.75f * (float)(1u << Fp8<FMT>::EMAX);
   float v[4];
@@ -227,11 +223,11 @@ __device__ __forceinline__ uint32_t sr4(const uint32_t* xb, const CastParams& p,
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const uint32_t ax = xb[i] & kAbsMask;
-    uint32_t m;
-    const float val = sr_value<FMT>(ax, p.K, r[i], &m);
+    float m;
+    const float val = sr_value<FMT>(ax, p.K, c2, r[i], m);
     const bool big = ax > p.t_clip;            // clips and non-finite
     acc.n_big += big ? 1u : 0u;
-    acc.n_uf += (!big && ax != 0u && m == 0u) ? 1u : 0u;
+    acc.n_uf += (!big && ax != 0u && m == 0.0f) ? 1u : 0u;
     v[i] = big ? kMaxF : val;
     sgn |= (xb[i] >> 31) << (8 * i + 7);
   }
@@ -263,6 +259,7 @@ k_cast_sr(const SegBatch b, const nc_scale_state* __restrict__ st, const nc_loss
   __builtin_amdgcn_sched_barrier(0);
   const int K = st[b.first + s].k - (ls ? ls->s_log2 : 0);
   const CastParams p = cast_params<FMT>(K);
+  const int c2 = K - Fp8<FMT>::EMIN + Fp8<FMT>::MB;
   const SrKey key{(uint32_t)seed, (uint32_t)(seed >> 32), (uint32_t)(b.first + s), (uint32_t)offset,
                   (uint32_t)(offset >> 32)};
   Acc acc;
@@ -281,7 +278,7 @@ k_cast_sr(const SegBatch b, const nc_scale_state* __restrict__ st, const nc_loss
       for (int j = 0; j < VEC / 4; ++j) {
         uint32_t r[4];
         sr_block(blk + j, key, r);
-        w[j] = sr4<FMT>(xb + 4 * j, p, r, acc);
+        w[j] = sr4<FMT>(xb + 4 * j, p, c2, r, acc);
       }
 #pragma unroll
       for (int i = 0; i < VEC; ++i) m = max(m, xb[i] & kAbsMask);
@@ -307,7 +304,7 @@ k_cast_sr(const SegBatch b, const nc_scale_state* __restrict__ st, const nc_loss
       uint32_t r[4];
       sr_block((uint32_t)(e >> 2), key, r);
       r[0] = r[e & 3];                         // this element's word
-      uint32_t q = sr4<FMT>(xb, p, r, acc) & 0xFFu;
+      uint32_t q = sr4<FMT>(xb, p, c2, r, acc) & 0xFFu;
       const uint32_t ax = xb[0] & kAbsMask;
       acc.amax = max(acc.amax, finite_mag(ax, acc));
       if (ax > kMaxFinite) q = nonfinite_code<FMT>(xb[0]);

@@ -54,6 +54,45 @@ def test_sr_parity(dtype, name, fmt, k, s):
     assert counts[0]["amax"] == wn["amax"]
 
 
+@pytest.mark.parametrize("name,fmt", FMTS)
+@pytest.mark.parametrize("k,s", [(127, 0), (120, 0), (64, 0), (0, 0), (-60, 0), (-127, 0), (-120, 16)])
+def test_sr_every_bf16_pattern(name, fmt, k, s):
+    """All 65,536 bf16 patterns (subnormals, both zeros, Inf, NaN) at scale
+    exponents from 127 down to -136: at the top, subnormal inputs land in
+    the format's normal and subnormal ranges; at the bottom, most values
+    fall far below the smallest subnormal and round up only on the rarest
+    draws."""
+    bits = np.arange(1 << 16, dtype=np.uint32).astype(np.uint16)
+    xd, x64 = dev_bf16(bits), bulk.bf16_bits_to_f64(bits)
+    ls = nc.new_loss_scale(s) if s else None
+    codes, counts = _sr([xd], name, [k], 0xC0FFEE, 9, ls=ls)
+    want, wn = bulk.cast_tensor_sr_f64(fmt, x64, k, s, 0xC0FFEE, 9, 0)
+    bad = np.flatnonzero(codes[0] != want)
+    assert bad.size == 0, [(int(i), x64[i], hex(codes[0][i]), hex(want[i])) for i in bad[:5]]
+    assert_counts(counts[0], wn)
+
+
+@pytest.mark.parametrize("name,fmt", FMTS)
+@pytest.mark.parametrize("k", [127, 126, 100, 30])
+def test_sr_fp32_subnormal_inputs(name, fmt, k):
+    """fp32 patterns with every exponent field, a quarter of them subnormal
+    (and 2^-149 itself), at large scale exponents, where a subnormal input
+    scales into the format's range."""
+    r = np.random.default_rng(500 + k)
+    n = 4 * 8192 + 5
+    e = r.integers(0, 255, n).astype(np.uint32)
+    e[: n // 4] = 0
+    bits = e << 23 | r.integers(0, 1 << 23, n).astype(np.uint32) | r.integers(0, 2, n).astype(np.uint32) << 31
+    bits[:4] = [1, 0x80000001, 0x7FFFFF, 0x400000]
+    x = bits.view(np.float32)
+    xd = dev_f32(x)
+    codes, counts = _sr([xd], name, [k], 31, 1 << 33)
+    want, wn = bulk.cast_tensor_sr_f64(fmt, x.astype(np.float64), k, 0, 31, 1 << 33, 0)
+    bad = np.flatnonzero(codes[0] != want)
+    assert bad.size == 0, [(int(i), hex(bits[i]), hex(codes[0][i]), hex(want[i])) for i in bad[:5]]
+    assert_counts(counts[0], wn)
+
+
 def test_sr_tensor_index_and_launches():
     """40 tensors (two launches; tensor j draws with counter word j, its
     index in the call), ragged sizes, one empty."""
