@@ -6,60 +6,82 @@
 // and the per-tensor promotion window.
 //
 // One workgroup per tile of 8192 elements (32 per lane, eight 16-byte loads
-// of w and eight of d; measured best on MI355X); the four per-lane counts go
-// to a workspace slot and two small kernels reduce the slots per tensor in a
-// fixed order.
+// of w and eight of d; measured best on MI355X); the four counts (per lane
+// where flag bytes are written, per wave otherwise) go to a workspace slot
+// and two small kernels reduce the slots per tensor in a fixed order.
 #include "nc_launch.h"
 
 namespace nc {
 namespace {
 
-// Narrow weight formats: significand bits, exponent bias, field masks.
+// Narrow weight formats.  narrow(wb) rounds the fp32 pattern wb to the
+// format (RNE, IEEE overflow to Inf) and gives the result's exponent field,
+// whether its fraction field is zero and whether its last significand bit is
+// even.  STEP0 = 2^-(BIAS + MB): the step of a binade with exponent field f
+// is STEP0 2^max(f, 1).
 template <int WF> struct WFmt;
 template <> struct WFmt<NC_W_BF16> {
-  static constexpr int MB = 7, BIAS = 127;
-  static constexpr uint32_t MMASK = 0x7F, MAG = 0x7FFF, INF = 0x7F80;
-  // RNE of an fp32 pattern to bf16 (IEEE overflow to Inf)
-  __device__ static uint32_t round(uint32_t b) { return f32_to_bf16_rne(b) & 0xFFFFu; }
+  static constexpr uint32_t EFULL = 0xFF;    // Inf/NaN exponent field
+  static constexpr float STEP0 = 0x1p-134f;
+  // the bf16 value sits in the high half of the rounded fp32 pattern
+  __device__ static void narrow(uint32_t wb, uint32_t& ef, bool& frac0, uint32_t& even) {
+    const uint32_t h = wb + 0x7FFFu + ((wb >> 16) & 1u);
+    ef = (h >> 23) & 0xFFu;
+    frac0 = (h & 0x007F0000u) == 0u;
+    even = (~h >> 16) & 1u;
+  }
 };
 template <> struct WFmt<NC_W_FP16> {
-  static constexpr int MB = 10, BIAS = 15;
-  static constexpr uint32_t MMASK = 0x3FF, MAG = 0x7FFF, INF = 0x7C00;
+  static constexpr uint32_t EFULL = 0x1F;
+  static constexpr float STEP0 = 0x1p-25f;
   // the hardware conversion rounds to nearest even, keeps subnormals and
   // overflows to Inf
-  __device__ static uint32_t round(uint32_t b) {
-    return (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)__uint_as_float(b));
+  __device__ static void narrow(uint32_t wb, uint32_t& ef, bool& frac0, uint32_t& even) {
+    const uint32_t h = __builtin_bit_cast(uint16_t, (_Float16)__uint_as_float(wb));
+    ef = (h >> 10) & 0x1Fu;
+    frac0 = (h & 0x3FFu) == 0u;
+    even = (~h) & 1u;
   }
 };
 
-// 1 if a < b, for a, b < 2^31 (the sign of a - b).
-__device__ __forceinline__ uint32_t lt31(uint32_t a, uint32_t b) { return (a - b) >> 31; }
-
-// Flags of one element (bit 0 below, 1 no-op, 2 zero update, 3 excluded).
-// The narrow copy w_F keeps w's sign.  The add w_F + d leaves w_F iff |d| is
-// below half the gap to the neighbour on d's side, or exactly half with
-// w_F's last significand bit even (ties to even).  That gap is the step,
-// except toward zero from a power of two above the smallest normal, where
-// the binade below has half the spacing.  Every decision compares |d| with
-// a power of two, 2^j for j >= -135 (exact fp32 values, subnormal ones
-// included, formed by v_ldexp_f32; the compare of two finite fp32 values is
-// exact) -- never through a rounded sum.
+// Classes of one element.  The narrow copy w_F keeps w's sign.  The add
+// w_F + d leaves w_F iff |d| is below half the gap to the neighbour on d's
+// side, or exactly half with w_F's last significand bit even (ties to even).
+// That gap is the step, except toward zero from a power of two above the
+// smallest normal, where the binade below has half the spacing.  Every
+// decision compares |d| with a power of two, 2^j for j >= -135 (exact fp32
+// values, subnormal ones included, formed by v_ldexp_f32), never through a
+// rounded sum; the tie test folds into the compare of non-negative patterns
+// (|d| <= half iff bits(|d|) < bits(half) + 1).
+struct SwampCls {
+  bool below, noop, zero, excl;
+};
 template <int WF>
-__device__ __forceinline__ uint32_t swamp_flags(uint32_t wb, uint32_t db) {
+__device__ __forceinline__ SwampCls swamp_classify(uint32_t wb, uint32_t db) {
   using F = WFmt<WF>;
   const uint32_t ad = db & kAbsMask;
-  const float fd = __uint_as_float(ad);
-  const uint32_t h = F::round(wb);
-  const uint32_t hm = h & F::MAG, mf = h & F::MMASK, ef = hm >> F::MB;
-  const uint32_t excl = lt31(kMaxFinite, max(wb & kAbsMask, ad)) | lt31(F::INF - 1u, hm);
-  const int se = max((int)ef, 1) - (F::BIAS + F::MB);          // log2 of the step
-  const uint32_t halved = ((wb ^ db) >> 31) & lt31(0u, hm) & lt31(mf, 1u) & lt31(1u, ef);
-  const float half = __builtin_amdgcn_ldexpf(1.0f, se - 1 - (int)halved);
-  const uint32_t zero = lt31(ad, 1u);
-  const uint32_t below = fd < __builtin_amdgcn_ldexpf(1.0f, se) ? 1u : 0u;
-  const uint32_t noop = (fd < half || (fd == half && (mf & 1u) == 0u)) ? 1u : 0u;
-  const uint32_t ok = excl ^ 1u, cons = ok & (zero ^ 1u);
-  return (below & cons) | (noop & cons) << 1 | (zero & ok) << 2 | excl << 3;
+  uint32_t ef, even;
+  bool frac0;
+  F::narrow(wb, ef, frac0, even);
+  const float step = __builtin_amdgcn_ldexpf(F::STEP0, (int)max(ef, 1u));
+  const bool halved = (int32_t)(wb ^ db) < 0 && frac0 && ef > 1u;
+  const float half = __builtin_amdgcn_ldexpf(step, halved ? -2 : -1);
+  SwampCls c;
+  c.excl = max(wb & kAbsMask, ad) > kMaxFinite || ef == F::EFULL;
+  c.zero = ad == 0u;
+  c.below = __uint_as_float(ad) < step;
+  c.noop = ad < __float_as_uint(half) + even;
+  return c;
+}
+
+// Flag byte of one element: bit 0 below, 1 no-op, 2 zero update, 3 excluded.
+// below and no-op are counted over considered elements (finite, nonzero d).
+template <int WF>
+__device__ __forceinline__ uint32_t swamp_flags(uint32_t wb, uint32_t db) {
+  const SwampCls c = swamp_classify<WF>(wb, db);
+  const bool cons = !c.excl && !c.zero;
+  return (c.below && cons ? 1u : 0u) | (c.noop && cons ? 2u : 0u) | (c.zero && !c.excl ? 4u : 0u) |
+         (c.excl ? 8u : 0u);
 }
 
 struct SwampAcc {
@@ -71,14 +93,36 @@ struct SwampAcc {
     zero += __popc(f4 & 0x04040404u);
     excl += __popc(f4 & 0x08080808u);
   }
+  // one element per active lane, counted for the whole wave: each test is
+  // taken as the wave's lane mask (a compare's own result), the masks are
+  // combined and popcounted on the scalar unit, and the sums are
+  // wave-uniform; inactive lanes are in no mask
+  template <int WF>
+  __device__ void add_wave(uint32_t wb, uint32_t db) {
+    const SwampCls c = swamp_classify<WF>(wb, db);
+    const uint64_t mx = __ballot(c.excl), mz = __ballot(c.zero), mb = __ballot(c.below), mn = __ballot(c.noop);
+    const uint64_t cons = ~(mx | mz);
+    below += __popcll(mb & cons);
+    noop += __popcll(mn & cons);
+    zero += __popcll(mz & ~mx);
+    excl += __popcll(mx);
+  }
 };
 
 // The workgroup's four sums -> its slot (as write_count_slot, all sums).
+// WAVE: the sums are per wave (equal in every lane), not per lane.
+template <bool WAVE>
 __device__ inline void write_swamp_slot(const SwampAcc& a, uint4* slot, uint32_t* lds) {
-  const uint32_t z = row_sum_u32(a.zero), b = row_sum_u32(a.below), n = row_sum_u32(a.noop),
-                 x = row_sum_u32(a.excl);
-  if ((threadIdx.x & 15) == 0) {
-    const int r = threadIdx.x >> 4;
+  constexpr int N = WAVE ? kWaves : kRows;
+  uint32_t z = a.zero, b = a.below, n = a.noop, x = a.excl;
+  if constexpr (!WAVE) {
+    z = row_sum_u32(z);
+    b = row_sum_u32(b);
+    n = row_sum_u32(n);
+    x = row_sum_u32(x);
+  }
+  if ((threadIdx.x & (WAVE ? 63 : 15)) == 0) {
+    const int r = WAVE ? threadIdx.x >> 6 : threadIdx.x >> 4;
     lds[r * 4 + 0] = z;
     lds[r * 4 + 1] = b;
     lds[r * 4 + 2] = n;
@@ -87,7 +131,7 @@ __device__ inline void write_swamp_slot(const SwampAcc& a, uint4* slot, uint32_t
   __syncthreads();
   if (threadIdx.x == 0) {
     uint4 c = {0u, 0u, 0u, 0u};
-    for (int r = 0; r < kRows; ++r) {
+    for (int r = 0; r < N; ++r) {
       c.x += lds[r * 4 + 0];
       c.y += lds[r * 4 + 1];
       c.z += lds[r * 4 + 2];
@@ -97,7 +141,10 @@ __device__ inline void write_swamp_slot(const SwampAcc& a, uint4* slot, uint32_t
   }
 }
 
-template <int WF>
+// FLAGS: some tensor of the launch wants its flag bytes (those with a null
+// flag pointer in such a launch are counted per lane too); otherwise only
+// the counts are formed, per wave.
+template <int WF, bool FLAGS>
 NC_STREAM_KERNEL
 k_swamp(const SegBatch b, uint4* __restrict__ slots) {
   constexpr int U = kSwampVecs;
@@ -110,7 +157,7 @@ k_swamp(const SegBatch b, uint4* __restrict__ slots) {
   const int rem = tile_len<TILE>(b, s, tile);
   const u32x4* wv = reinterpret_cast<const u32x4*>(static_cast<const float*>(g.x) + e0);
   const u32x4* dv = reinterpret_cast<const u32x4*>(static_cast<const float*>(g.y) + e0);
-  uint8_t* fl = g.codes ? g.codes + e0 : nullptr;
+  uint8_t* fl = FLAGS && g.codes ? g.codes + e0 : nullptr;
   SwampAcc acc{0u, 0u, 0u, 0u};
   if (rem == (int)TILE) {
     u32x4 w[U], d[U];
@@ -121,21 +168,32 @@ k_swamp(const SegBatch b, uint4* __restrict__ slots) {
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      const uint32_t f = swamp_flags<WF>(w[u].x, d[u].x) | swamp_flags<WF>(w[u].y, d[u].y) << 8 |
-                         swamp_flags<WF>(w[u].z, d[u].z) << 16 | swamp_flags<WF>(w[u].w, d[u].w) << 24;
-      acc.add4(f);
-      if (fl) st_stream(reinterpret_cast<uint32_t*>(fl) + u * kThreads + threadIdx.x, f);
+      if constexpr (FLAGS) {
+        const uint32_t f = swamp_flags<WF>(w[u].x, d[u].x) | swamp_flags<WF>(w[u].y, d[u].y) << 8 |
+                           swamp_flags<WF>(w[u].z, d[u].z) << 16 | swamp_flags<WF>(w[u].w, d[u].w) << 24;
+        acc.add4(f);
+        if (fl) st_stream(reinterpret_cast<uint32_t*>(fl) + u * kThreads + threadIdx.x, f);
+      } else {
+        acc.add_wave<WF>(w[u].x, d[u].x);
+        acc.add_wave<WF>(w[u].y, d[u].y);
+        acc.add_wave<WF>(w[u].z, d[u].z);
+        acc.add_wave<WF>(w[u].w, d[u].w);
+      }
     }
   } else {
     const uint32_t* ws = static_cast<const uint32_t*>(g.x) + e0;
     const uint32_t* ds = static_cast<const uint32_t*>(g.y) + e0;
     for (int i = threadIdx.x; i < rem; i += kThreads) {
-      const uint32_t f = swamp_flags<WF>(ws[i], ds[i]);
-      acc.add4(f);
-      if (fl) fl[i] = (uint8_t)f;
+      if constexpr (FLAGS) {
+        const uint32_t f = swamp_flags<WF>(ws[i], ds[i]);
+        acc.add4(f);
+        if (fl) fl[i] = (uint8_t)f;
+      } else {
+        acc.add_wave<WF>(ws[i], ds[i]);    // inactive lanes are not in the masks
+      }
     }
   }
-  write_swamp_slot(acc, slots + tile, lds);
+  write_swamp_slot<!FLAGS>(acc, slots + tile, lds);
 }
 
 // Slot reductions: chunks of kChunk tiles, then per tensor (fixed order).
@@ -209,10 +267,16 @@ k_swamp_window(const nc_swamp_policy p, int32_t count, nc_swamp_state* __restric
 
 hipError_t launch_swamp(const SegBatch& b, int wfmt, const Ws& w, const Launch& l) {
   uint4* slots = reinterpret_cast<uint4*>(w.cnt1);
-  if (wfmt == NC_W_BF16)
-    hipLaunchKernelGGL((k_swamp<NC_W_BF16>), dim3((uint32_t)l.grid), dim3(kThreads), 0, l.stream, b, slots);
-  else
-    hipLaunchKernelGGL((k_swamp<NC_W_FP16>), dim3((uint32_t)l.grid), dim3(kThreads), 0, l.stream, b, slots);
+  bool flags = false;
+  for (int j = 0; j < b.count; ++j) flags = flags || b.s[j].codes != nullptr;
+  const dim3 grid((uint32_t)l.grid), block(kThreads);
+  if (wfmt == NC_W_BF16) {
+    if (flags) hipLaunchKernelGGL((k_swamp<NC_W_BF16, true>), grid, block, 0, l.stream, b, slots);
+    else hipLaunchKernelGGL((k_swamp<NC_W_BF16, false>), grid, block, 0, l.stream, b, slots);
+  } else {
+    if (flags) hipLaunchKernelGGL((k_swamp<NC_W_FP16, true>), grid, block, 0, l.stream, b, slots);
+    else hipLaunchKernelGGL((k_swamp<NC_W_FP16, false>), grid, block, 0, l.stream, b, slots);
+  }
   return hipGetLastError();
 }
 
