@@ -298,8 +298,10 @@ k_stats(const SegBatch b, const nc_scale_state* __restrict__ st,
   constexpr int U = kStatsVecs;
   constexpr int64_t TILE = (int64_t)kThreads * VEC * U;
   typedef typename CodeVec<DT>::T CT;
+  constexpr int NSC = MX ? (int)(TILE / 32) : 16;        // scale bytes of a full tile
   __shared__ double tab[256];
   __shared__ double lds_st[kRows * 6];
+  __shared__ __align__(16) uint8_t lds_sc[NSC];
   const int64_t tile = blockIdx.x;
   const int s = seg_of(b.tile0, b.count, tile);
   const Seg& g = b.s[s];
@@ -308,19 +310,27 @@ k_stats(const SegBatch b, const nc_scale_state* __restrict__ st,
   const uint8_t* cs = g.codes + e0;
   const u32x4* src = reinterpret_cast<const u32x4*>(static_cast<const uint8_t*>(g.x) + e0 * In<DT>::BYTES);
   const bool full = rem == (int)TILE;
-  // a full tile's loads go out first; the table fill overlaps them
+  // a full tile's loads go out first (an MX tile's scale bytes first of all,
+  // staged through LDS: one 16-byte load by each of the first NSC / 16
+  // lanes, or NSC / 256 bytes per lane where the scale array is not 16-byte
+  // aligned); the table fill overlaps them
   u32x4 v[U];
   CT c[U];
-  uint32_t sc[MX ? U : 1];
   if (full) {
+    if constexpr (MX) {
+      const uint8_t* sb = g.scales + e0 / 32;
+      if (((uintptr_t)g.scales & 15u) == 0) {
+        if ((int)threadIdx.x < NSC / 16)
+          reinterpret_cast<u32x4*>(lds_sc)[threadIdx.x] = reinterpret_cast<const u32x4*>(sb)[threadIdx.x];
+      } else {
+#pragma unroll
+        for (int j = 0; j < NSC / kThreads; ++j) lds_sc[j * kThreads + threadIdx.x] = sb[j * kThreads + threadIdx.x];
+      }
+    }
 #pragma unroll
     for (int u = 0; u < U; ++u) v[u] = ld_stream(src + u * kThreads + threadIdx.x);
 #pragma unroll
     for (int u = 0; u < U; ++u) c[u] = CodeVec<DT>::load(cs, u * kThreads + threadIdx.x);
-    if constexpr (MX) {
-#pragma unroll
-      for (int u = 0; u < U; ++u) sc[u] = g.scales[(e0 + (int64_t)(u * kThreads + threadIdx.x) * VEC) / 32];
-    }
   }
   __builtin_amdgcn_sched_barrier(0);
   if constexpr (MX) fill_stat_table<FMT>(tab, 0);
@@ -337,7 +347,7 @@ k_stats(const SegBatch b, const nc_scale_state* __restrict__ st,
       unpack<DT>(v[u], xb);
       CodeVec<DT>::split(c[u], q);
       double blk = 1.0;
-      if constexpr (MX) blk = pow2_f64((int)sc[u] - 127);
+      if constexpr (MX) blk = pow2_f64((int)lds_sc[(u * kThreads + threadIdx.x) * VEC / 32] - 127);
       stats_vec<VEC, MX, true>(xb, q, tab, blk, sa);
       __builtin_amdgcn_sched_barrier(0);   // one vector's table reads at a time (register pressure)
     }

@@ -170,13 +170,16 @@ def test_stats_per_tensor_fused_and_separate(dtype, name, fmt):
 
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
-@pytest.mark.parametrize("rule", ["ocp", "plus1"])
-def test_stats_mx_fused_and_separate(dtype, rule):
+@pytest.mark.parametrize("rule,off", [("ocp", 0), ("plus1", 0), ("ocp", 5)])
+def test_stats_mx_fused_and_separate(dtype, rule, off):
+    """Several full tiles and a ragged one; the scale array at a 16-byte
+    aligned and at an odd address (the two ways a full tile's scale bytes
+    are staged)."""
     rows, cols = 70, 1024
     xd, x64 = _stats_input(dtype, rows * cols, 5)
     n = rows * cols
     codes = codes_like(n)
-    scales = torch.empty(n // 32, dtype=torch.uint8, device="cuda")
+    scales = torch.empty(n // 32 + 16, dtype=torch.uint8, device="cuda")[off:off + n // 32]
     out = nc.new_counts(1)
     fused = nc.new_stats(1)
     desc, cnt = nc.tensors([xd], [codes])
