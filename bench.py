@@ -87,7 +87,7 @@ KERNEL_SIG = {"amax": "k_amax<1>", "cast_tensor": "k_cast_pt<0, 1, false>",
               "cast_tensor+stats": "k_cast_pt<0, 1, true>", "cast_mx+stats": "k_cast_mx<0, 1, 0, true>",
               "cast_mx_cols": "k_cast_mx_col<0, 1, 0, false>", "dequant_mx_cols": "k_dequant_col<0>",
               "stats_mx_cols": "k_stats_col<0, 1>", "cast_tensor_sr": "k_cast_sr<0, 1>",
-              "swamp_watch": "k_swamp<0>"}
+              "swamp_watch": "k_swamp<0, false>"}
 TRAFFIC_JSON = os.path.join(ROOT, "profiles", "traffic.json")
 
 

@@ -280,7 +280,7 @@ nc_status nc_dequant(const nc_tensor* t, int32_t count, nc_fmt fmt, const nc_sca
     if (!aligned16(y[i])) return NC_E_ALIGN;
   }
   if (mx && count > 0 && t[0].mx_axis == NC_MX_COLS)
-    return for_batches(t, count, kThreads, y, [&](const SegBatch& b) {
+    return for_batches(t, count, kDequantColSlots, y, [&](const SegBatch& b) {
       return hip_status(launch_dequant_col(b, fmt, Launch{b.tile0[b.count], (hipStream_t)stream}));
     }, kDequantColUnit);
   return for_batches(t, count, kDequantTile, y, [&](const SegBatch& b) {

@@ -207,10 +207,11 @@ k_dequant(const SegBatch b, const nc_scale_state* __restrict__ st) {
   }
 }
 
-// Dequant of column-block MX codes: a lane owns one col_slot of 8 columns
-// and kDequantColRows rows, reads their 8 scale bytes once and then, per row, 8
-// codes (8 bytes) and writes 8 bf16 values (16 bytes); each column has its
-// own shift.
+// Dequant of column-block MX codes.  A slot is 8 columns of a 32-row band
+// (col_slot); lane l of wave w takes rows 8w .. 8w + 7 of the tile's slot l,
+// reads the slot's 8 scale bytes (the same bytes as the other three waves)
+// and then, per row, 8 codes (8 bytes) and writes 8 bf16 values (16 bytes);
+// each column has its own shift.
 __device__ __forceinline__ uint32_t bf16_pair2(f32x2 v, int sh0, int sh1) {
   v.x = __builtin_amdgcn_ldexpf(v.x, sh0);
   v.y = __builtin_amdgcn_ldexpf(v.y, sh1);
@@ -220,15 +221,18 @@ __device__ __forceinline__ uint32_t bf16_pair2(f32x2 v, int sh0, int sh1) {
 template <int FMT>
 NC_STREAM_KERNEL
 k_dequant_col(const SegBatch b) {
-  constexpr int VC = kDequantColCodes, R = kDequantColRows;
+  constexpr int VC = kDequantColCodes, R = kDequantColRows, SLOTS = kDequantColSlots;
+  static_assert(SLOTS == 64, "one slot per lane of a wave, one 8-row part per wave");
   const int64_t tile = blockIdx.x;
   const int s = seg_of(b.tile0, b.count, tile);
   const Seg& g = b.s[s];
-  const ColSlot cs = col_slot<VC, R>(g, tile - b.tile0[s], tile_len<kThreads>(b, s, tile));
+  const int rem = tile_len<SLOTS>(b, s, tile);                 // slots in this tile
+  const uint32_t slot = threadIdx.x % SLOTS, part = threadIdx.x / SLOTS;
+  const ColSlot cs = col_slot_at<VC>(g, (uint32_t)(tile - b.tile0[s]) * SLOTS + slot, (int)slot < rem);
   if (!cs.act) return;                      // no barriers below
   const int64_t cols = g.cols;
-  const uint8_t* src = g.codes + cs.e0;
-  uint16_t* dst = static_cast<uint16_t*>(g.y) + cs.e0;
+  const uint8_t* src = g.codes + cs.e0 + (int64_t)part * R * cols;
+  uint16_t* dst = static_cast<uint16_t*>(g.y) + cs.e0 + (int64_t)part * R * cols;
   u32x2 c[R];
 #pragma unroll
   for (int r = 0; r < R; ++r) c[r] = ld_stream(reinterpret_cast<const u32x2*>(src + r * cols));

@@ -26,18 +26,22 @@ constexpr int64_t kMinWsTile = (int64_t)kThreads * 4 * kCastVecs;
 // Column-block MX (col_slot): a lane reads 8 input bytes per row (4 bf16 or
 // 2 fp32 columns), or 8 codes per row in dequant.  Rows per slot, measured
 // best on MI355X: the cast needs whole 32-row bands; the statistics pass is
-// fastest with them too; dequant with 8-row slots (smaller tiles: 16 KiB of
-// codes per workgroup instead of 64).  A tile is 256 slots, always at least
-// kMinWsTile elements, so the workspace bound above covers these calls too.
+// fastest with them too.  Dequant takes whole bands as well, but each lane
+// only kDequantColRows of a band's rows: the four waves of a workgroup hold
+// the four 8-row parts of the same 64 slots (a tile of 16 KiB of codes), so
+// a band's scale bytes are fetched once and hit in cache for the other
+// waves.  A cast or statistics tile is at least kMinWsTile elements, so the
+// workspace bound above covers those calls too.
 constexpr int kColBytes = 8;
 constexpr int kDequantColCodes = 8;
-constexpr int kDequantColRows = 8;
+constexpr int kDequantColRows = 8;                                   // rows per lane
+constexpr int kDequantColSlots = kThreads / (32 / kDequantColRows);  // slots per tile
 constexpr int kStatsColRows = 32;
 // Lanes per slot in the column cast: two for bf16 (16 rows each, half the
 // registers of a whole band), one for fp32 (measured faster whole).
 constexpr int col_cast_split(int dtype) { return dtype == NC_BF16 ? 2 : 1; }
 inline int64_t col_unit(int in_bytes, int rows = 32) { return rows * (kColBytes / in_bytes); }
-constexpr int64_t kDequantColUnit = kDequantColRows * kDequantColCodes;
+constexpr int64_t kDequantColUnit = 32 * kDequantColCodes;          // codes per slot
 static_assert(kThreads * kStatsColRows * 2 >= kMinWsTile, "column tiles are no smaller than kMinWsTile");
 static_assert(kThreads / col_cast_split(NC_BF16) * 32 * 2 >= kMinWsTile, "column tiles are no smaller than kMinWsTile");
 
