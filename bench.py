@@ -1,7 +1,7 @@
 """Throughput of the scaled FP8 cast on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--rows R] [--no-cpu]
-                    [--cpu-rows R] [--copy-probe]
+                    [--no-llama] [--no-configs] [--cpu-rows R] [--copy-probe]
 
 Workload: a heavy-tailed bf16 tensor of 2^30 elements (262,144 rows of 4096;
 row r = 10^v_r * Student-t(3), v_r ~ U(-3, 3)), resident in HBM before the
@@ -21,7 +21,11 @@ fused statistics, the stochastic-rounding cast, the MX cast, dequant and
 statistics with blocks down the columns, the update/step-ratio monitor on
 2^30 fp32 weights and updates, a plain device copy of the cast's byte count, and one
 delayed-scaling step of loss-scaled Llama-7B-shaped fp32 gradients (225
-tensors, 6.6G elements, fused 2^-16 unscale).
+tensors, 6.6G elements, fused 2^-16 unscale).  Under "configs" it times the
+three smaller workloads on their own (last-level cache flushed before each
+rep): 65,536 fp32 elements under current scaling (microseconds, launch-bound),
+the 4096 x 4096 tanh bf16 matrix to MXFP8 under the OCP and +1 rules, and one
+delayed E5M2 scaling step over 64 fp32 gradient tensors.
 
 Prints one JSON line.  `value` is elements per second through the whole step
 (Gelem/s); `roofline` is the dominant kernel's algorithmic bytes per launch
@@ -53,6 +57,8 @@ def parse():
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-llama", action="store_true",
                     help="skip the Llama-shaped unscale+cast measured beside the step")
+    ap.add_argument("--no-configs", action="store_true",
+                    help="skip the three smaller workloads timed after the step")
     ap.add_argument("--cpu-rows", type=int, default=4096,
                     help="rows of the workload the CPU oracle baseline runs on")
     ap.add_argument("--copy-probe", action="store_true",
@@ -155,17 +161,26 @@ def cpu_baseline(rows: int, procs: int):
     chunk = -(-rows // procs)
     jobs = [bits[r:r + chunk] for r in range(0, rows, chunk)]
     workers = min(procs, len(jobs))
-    # the per-tensor scale needs the global amax first (as on the GPU)
+    print(f"[bench] CPU oracle: input ready, {workers} workers", file=sys.stderr, flush=True)
+    # the per-tensor scale needs the global amax first (as on the GPU); each
+    # phase has a time limit, so a stuck worker cannot hold the bench
     t0 = time.perf_counter()
     with mp.get_context("fork").Pool(workers) as pool:
-        amaxes = pool.map(_cpu_amax, jobs)
+        amaxes = pool.map_async(_cpu_amax, jobs).get(timeout=120)
         k = _scale_k(max(amaxes))
-        pool.map(_cpu_step, [(j, k) for j in jobs])
+        print(f"[bench] CPU oracle: amax pass done ({time.perf_counter() - t0:.1f} s)", file=sys.stderr,
+              flush=True)
+        pool.map_async(_cpu_step, [(j, k) for j in jobs]).get(timeout=150)
     dt = time.perf_counter() - t0
     n = rows * COLS
     return dict(value=n / dt / 1e9, unit="Gelem/s", cores=workers, kind="oracle",
                 sample=f"{rows} rows x {COLS} of the same workload ({n} elements), whole step, "
                        f"{workers} worker processes, {dt:.1f} s, {_cpu_model()}")
+
+
+def mp_timeout():
+    import multiprocessing as mp
+    return mp.TimeoutError
 
 
 def _cpu_model() -> str:
@@ -242,6 +257,134 @@ def llama_unscale_cast(nc, torch, workloads):
     return dict(ms=round(ms, 4), gbps=round(gbps, 1), frac=round(gbps / HBM_PEAK_GBPS, 4),
                 gelem_s=round(n / (ms * 1e-3) / 1e9, 2), elements=n, tensors=T,
                 nonfinite_per_step=nonfinite)
+
+
+def _timed(torch, fn, reps, flush=None):
+    """Median of reps event-timed calls of fn on the current stream (ms);
+    flush(), if given, runs untimed before each call."""
+    ts = []
+    for _ in range(reps):
+        if flush is not None:
+            flush()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        fn()
+        e1.record()
+        torch.cuda.synchronize()
+        ts.append(e0.elapsed_time(e1))
+    return float(np.median(ts))
+
+
+def _captured(torch, fn):
+    """fn's launches captured once into a HIP graph (after one warm run on a
+    side stream, as graph capture wants); returns the graph."""
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        fn()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        fn()
+    torch.cuda.synchronize()
+    return g
+
+
+def small_configs(nc, torch, workloads):
+    """The three smaller workloads, timed on their own: a 65,536-element fp32
+    vector under current per-tensor E4M3 scaling (amax, scale update, cast:
+    launch-bound, so microseconds, not bandwidth); the 4096 x 4096 tanh bf16
+    matrix cast to MXFP8 E4M3 under the OCP and +1 rules; and one step of
+    delayed per-tensor E5M2 scaling over 64 fp32 gradient tensors (2^12 to
+    2^22 elements) with a 16-step window.  Their working sets fit the GPU's
+    last-level cache, so a 1 GiB buffer is read before every timed rep
+    (untimed; a read leaves no dirty lines to write back during the rep) and
+    each rep starts from HBM.  These sizes are launch-bound, so each is timed
+    as eager calls and as one replay of the same calls captured in a HIP
+    graph.  Medians of 20 reps."""
+    dev = "cuda"
+    print("[bench] smaller workloads", file=sys.stderr, flush=True)
+    scratch = torch.ones(1 << 28, dtype=torch.int32, device=dev)
+    flush = lambda: scratch.sum(dtype=torch.int64)
+    res = {}
+
+    def both(fn, reps=20):
+        eager = _timed(torch, fn, reps, flush)
+        g = _captured(torch, fn)
+        graph = _timed(torch, g.replay, reps, flush)
+        return eager, graph
+    # 65,536 fp32 ~ N(0, 1): amax -> current scale -> cast
+    x = torch.from_numpy(workloads.per_tensor_small()).to(dev)
+    codes = torch.empty(x.numel(), dtype=torch.uint8, device=dev)
+    desc, cnt = nc.tensors([x], [codes])
+    ws = nc.new_workspace(desc, cnt)
+    st, am, out = nc.new_state(1), nc.new_counts(1), nc.new_counts(1)
+    pol = nc.policy("e4m3", "current", hysteresis=False)
+
+    def c1():
+        nc.nc_amax([x], am, ws=ws)
+        nc.nc_scale_update(pol, st, am)
+        nc.nc_cast_tensor([x], [codes], "e4m3", st, out, ws=ws)
+    c1()
+    ms, msg = both(c1)
+    res["per_tensor_65536_fp32"] = dict(us=round(ms * 1e3, 1), us_graph=round(msg * 1e3, 1), elements=x.numel(),
+                                        launches=6, note="amax + scale update + cast, launch-bound")
+    # 4096 x 4096 tanh(N(0, 1.5)) bf16, MXFP8 E4M3 per rule
+    xb = torch.from_numpy(workloads.tanh_activations().reshape(-1).view(np.int16)).to(dev).view(torch.bfloat16)
+    n = xb.numel()
+    codes = torch.empty(n, dtype=torch.uint8, device=dev)
+    scales = torch.empty(n // 32, dtype=torch.uint8, device=dev)
+    desc, cnt = nc.tensors([xb], [codes])
+    ws = nc.new_workspace(desc, cnt)
+    for rule in ("ocp", "plus1"):
+        out = nc.new_counts(1)
+        fn = lambda: nc.nc_cast_mx([xb], [codes], [scales], [4096], "e4m3", rule, out, ws=ws)
+        fn()
+        torch.cuda.synchronize()
+        clip = nc.counts_list(out)[0]["n_clip"] / n
+        ms, msg = both(fn)
+        nbytes = 3 * n + n // 32
+        res[f"mx_tanh_4096x4096_{rule}"] = dict(
+            us=round(ms * 1e3, 1), gbps=round(nbytes / (ms * 1e-3) / 1e9, 1),
+            frac=round(nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4), us_graph=round(msg * 1e3, 1),
+            clip_frac=round(clip, 4))
+    # 64 fp32 tensors, delayed E5M2 scaling with a 16-step window: one batched
+    # cast (counts and next amax fused) and one scale update per step
+    gen = workloads.GradientSteps(steps=4)
+    T = len(gen.sizes)
+    xs = [torch.from_numpy(v).to(dev) for v in gen.step(0)]
+    codes = [torch.empty(m, dtype=torch.uint8, device=dev) for m in gen.sizes]
+    desc, cnt = nc.tensors(xs, codes)
+    ws = nc.new_workspace(desc, cnt)
+    st, hist, am = nc.new_state(T), nc.new_history(T, 16), nc.new_counts(T)
+    nc.nc_amax(xs, am, ws=ws)
+    nc.nc_scale_update(nc.policy("e5m2", "current", 16), st, am)
+    pol = nc.policy("e5m2", "max_window", 16)
+    out = nc.new_counts(T)
+
+    def c3():
+        out.zero_()
+        nc.nc_cast_tensor(xs, codes, "e5m2", st, out, ws=ws)
+        nc.nc_scale_update(pol, st, out, hist)
+    c3()
+    g = _captured(torch, c3)
+    ms, msg = [], []
+    for t in range(1, gen.steps):          # fresh values every step, uploaded untimed
+        for d, v in zip(xs, gen.step(t)):
+            d.copy_(torch.from_numpy(v))
+        ms.append(_timed(torch, c3, 5, flush))
+        msg.append(_timed(torch, g.replay, 5, flush))
+    ms, msg = float(np.median(ms)), float(np.median(msg))
+    ne = sum(gen.sizes)
+    res["delayed_64_tensors_fp32"] = dict(
+        us=round(ms * 1e3, 1), gbps=round(5 * ne / (ms * 1e-3) / 1e9, 1),
+        frac=round(5 * ne / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4), us_graph=round(msg * 1e3, 1),
+        elements=ne, tensors=T,
+        note="per step: counter zeroing, one batched cast (two launches of 32 tensors), one scale update")
+    del scratch, g
+    torch.cuda.empty_cache()
+    return res
 
 
 def main():
@@ -437,6 +580,8 @@ def main():
     torch.cuda.empty_cache()
     if not a.no_llama:
         out["beside_step"]["llama_unscale_cast"] = llama_unscale_cast(nc, torch, workloads)
+    if not a.no_configs:
+        out["configs"] = small_configs(nc, torch, workloads)
     if a.copy_probe:
         src_b = torch.empty(1 << 30, dtype=torch.uint8, device=dev).fill_(1)
         dst_b = torch.empty_like(src_b)
@@ -446,7 +591,11 @@ def main():
         del src_b, dst_b
     if not a.no_cpu:
         print(f"[bench] CPU oracle baseline on {a.cpu_rows} rows", file=sys.stderr, flush=True)
-        out["cpu_baseline"] = cpu_baseline(a.cpu_rows, a.procs)
+        try:
+            out["cpu_baseline"] = cpu_baseline(a.cpu_rows, a.procs)
+        except mp_timeout():
+            print("[bench] CPU oracle baseline timed out", file=sys.stderr, flush=True)
+            out["cpu_baseline"] = None
     else:
         out["cpu_baseline"] = None
     print(json.dumps(out))

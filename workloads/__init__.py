@@ -4,7 +4,7 @@ This module generates inputs only.  It holds none of the cast's arithmetic
 and is shared by the tests (which hand the same arrays to the HIP path and to
 the oracle) and by the benchmark.  Every generator is deterministic in its
 seed.  Rounding to the input dtype (fp64 -> fp32 -> bf16, nearest even) is
-done by numpy and torch.
+done by numpy.
 
 Workloads (standard deviations are the second argument of N(0, s)):
 
@@ -39,9 +39,14 @@ import torch
 
 
 def to_bf16_bits(x64: np.ndarray) -> np.ndarray:
-    """fp64 -> fp32 -> bf16 (nearest even at each step), as uint16 bits."""
-    t = torch.from_numpy(np.ascontiguousarray(x64, dtype=np.float64).astype(np.float32))
-    return t.to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    """fp64 -> fp32 -> bf16 (nearest even at each step, overflow to Inf, NaN
+    -> 0x7FC0), as uint16 bits.  numpy only: no torch CPU kernel runs here, so
+    no thread pool is started in a process that later forks workers (nor in
+    the workers)."""
+    b = np.ascontiguousarray(x64, dtype=np.float64).astype(np.float32).view(np.uint32)
+    r = ((b + np.uint32(0x7FFF) + ((b >> np.uint32(16)) & np.uint32(1))) >> np.uint32(16)).astype(np.uint16)
+    r[(b & np.uint32(0x7FFFFFFF)) > np.uint32(0x7F800000)] = 0x7FC0
+    return r
 
 
 def per_tensor_small(n: int = 65536, seed: int = 101) -> np.ndarray:
