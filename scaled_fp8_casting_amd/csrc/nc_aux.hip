@@ -470,15 +470,26 @@ k_stats_col(const SegBatch b, double* __restrict__ stat_slots) {
 
 // ---------------------------------------------------------------------------
 // Reductions of the per-workgroup slots.  First: workgroup c sums chunk c,
-// at most kChunk consecutive tiles of one tensor, into a chunk slot.
-// Second: workgroup s sums tensor s's chunk slots and adds the totals into
-// the caller's counts and statistics.  Every sum runs in a fixed order
-// (threads over slots in index order, lanes by butterfly, waves in index
-// order), so results do not depend on scheduling.
+// at most kChunk consecutive tiles of one tensor.  Its counts go straight
+// into the caller's counts with atomics (integer sums and a max: the order
+// does not matter; the tensor's first chunk also adds the tensor's size to
+// n_finite, every chunk takes off its non-finite count, modulo 2^64).  Its
+// statistics are the tensor's own when the tensor has one chunk, and are
+// added to the caller's then; otherwise they go to a chunk slot, and
+// second, workgroup s sums tensor s's chunk slots and adds the totals (a
+// second launch only when some tensor of the launch has several chunks).
+// Every floating-point sum runs in a fixed order (threads over slots in
+// index order, lanes by butterfly, waves in index order), so statistics do
+// not depend on scheduling.
+__device__ __forceinline__ int stat_shift(int j, int s_log2) {   // unscale of sum j
+  return (j == 0 || j == 1 || j == 3) ? -s_log2 : -2 * s_log2;
+}
+
 template <bool COUNTS, bool STATS>
 __global__ void __launch_bounds__(kThreads)
 k_reduce1(const SegBatch b, const CountSlot* __restrict__ cnt1, const double* __restrict__ st1,
-          uint64_t* __restrict__ cnt2, double* __restrict__ st2) {
+          double* __restrict__ st2, nc_counts* __restrict__ out, nc_stats* __restrict__ stats,
+          const nc_loss_scale* __restrict__ ls, int clips) {
   __shared__ uint64_t lds_c[kWaves * 4];
   __shared__ double lds_s[kWaves * 6];
   const int64_t c = blockIdx.x;
@@ -522,70 +533,56 @@ k_reduce1(const SegBatch b, const CountSlot* __restrict__ cnt1, const double* __
     }
   }
   __syncthreads();
-  if (COUNTS && threadIdx.x < 4) {
-    uint64_t r = 0;
-    for (int w = 0; w < kWaves; ++w)
-      r = threadIdx.x == 0 ? max(r, lds_c[w * 4]) : r + lds_c[w * 4 + threadIdx.x];
-    cnt2[c * 4 + threadIdx.x] = r;
+  const int s_log2 = ls ? ls->s_log2 : 0;
+  if (COUNTS && threadIdx.x == 0) {
+    uint64_t m = 0, n_nf = 0, n_big = 0, n_uf = 0;
+    for (int w = 0; w < kWaves; ++w) {
+      m = max(m, lds_c[w * 4]);
+      n_nf += lds_c[w * 4 + 1];
+      n_big += lds_c[w * 4 + 2];
+      n_uf += lds_c[w * 4 + 3];
+    }
+    nc_counts* o = out + b.first + s;
+    const uint64_t fin = (c == b.chunk0[s] ? (uint64_t)b.s[s].n : 0u) - n_nf;   // modulo 2^64
+    atomicMax(&o->amax_bits, unscale_bits((uint32_t)m, s_log2));
+    if (fin) atomicAdd((unsigned long long*)&o->n_finite, (unsigned long long)fin);
+    if (n_nf) atomicAdd((unsigned long long*)&o->n_nonfinite, (unsigned long long)n_nf);
+    if (clips && n_big - n_nf) atomicAdd((unsigned long long*)&o->n_clip, (unsigned long long)(n_big - n_nf));
+    if (n_uf) atomicAdd((unsigned long long*)&o->n_underflow, (unsigned long long)n_uf);
   }
   if (STATS && threadIdx.x >= 64 && threadIdx.x < 70) {
     const int j = threadIdx.x - 64;
     double r = 0.0;
     for (int w = 0; w < kWaves; ++w) r += lds_s[w * 6 + j];
-    st2[c * 6 + j] = r;
+    if (b.chunk0[s + 1] - b.chunk0[s] == 1)
+      atomicAdd(reinterpret_cast<double*>(stats + b.first + s) + j, ldexp(r, stat_shift(j, s_log2)));
+    else
+      st2[c * 6 + j] = r;
   }
 }
 
-template <bool COUNTS, bool STATS>
+// Statistics of the tensors with several chunks.
 __global__ void __launch_bounds__(64)
-k_reduce2(const SegBatch b, const uint64_t* __restrict__ cnt2, const double* __restrict__ st2,
-          nc_counts* __restrict__ out, nc_stats* __restrict__ stats,
-          const nc_loss_scale* __restrict__ ls, int clips) {
+k_reduce2(const SegBatch b, const double* __restrict__ st2, nc_stats* __restrict__ stats,
+          const nc_loss_scale* __restrict__ ls) {
   const int s = blockIdx.x;
   const int64_t c0 = b.chunk0[s], c1 = b.chunk0[s + 1];
+  if (c1 - c0 <= 1) return;                  // done by the first reduction (or empty)
   const int s_log2 = ls ? ls->s_log2 : 0;
-  uint32_t mx = 0;
-  uint64_t nf = 0, big = 0, uf = 0;
   double a[6] = {0.0, 0.0, 0.0, 0.0, 0.0, 0.0};
   for (int64_t c = c0 + threadIdx.x; c < c1; c += 64) {
-    if constexpr (COUNTS) {
-      mx = max(mx, (uint32_t)cnt2[c * 4 + 0]);
-      nf += cnt2[c * 4 + 1];
-      big += cnt2[c * 4 + 2];
-      uf += cnt2[c * 4 + 3];
-    }
-    if constexpr (STATS) {
 #pragma unroll
-      for (int j = 0; j < 6; ++j) a[j] += st2[c * 6 + j];
-    }
+    for (int j = 0; j < 6; ++j) a[j] += st2[c * 6 + j];
   }
-  if constexpr (COUNTS) {
-    mx = wave_max_u32(mx);
-    nf = wave_sum_u64(nf);
-    big = wave_sum_u64(big);
-    uf = wave_sum_u64(uf);
-    if (threadIdx.x == 0) {
-      nc_counts* o = out + b.first + s;
-      const uint64_t n = (uint64_t)b.s[s].n;
-      atomicMax(&o->amax_bits, unscale_bits(mx, s_log2));
-      if (n - nf) atomicAdd((unsigned long long*)&o->n_finite, (unsigned long long)(n - nf));
-      if (nf) atomicAdd((unsigned long long*)&o->n_nonfinite, (unsigned long long)nf);
-      if (clips && big - nf) atomicAdd((unsigned long long*)&o->n_clip, (unsigned long long)(big - nf));
-      if (uf) atomicAdd((unsigned long long*)&o->n_underflow, (unsigned long long)uf);
-    }
-  }
-  if constexpr (STATS) {
-    double r[6];
+  double r[6];
 #pragma unroll
-    for (int j = 0; j < 6; ++j) r[j] = wave_sum_f64(a[j]);
-    if (threadIdx.x < 6) {
-      const int j = threadIdx.x;
-      double v = r[0];
+  for (int j = 0; j < 6; ++j) r[j] = wave_sum_f64(a[j]);
+  if (threadIdx.x < 6) {
+    const int j = threadIdx.x;
+    double v = r[0];
 #pragma unroll
-      for (int i = 1; i < 6; ++i) v = j == i ? r[i] : v;
-      const int sc = (j == 0 || j == 1 || j == 3) ? -s_log2 : -2 * s_log2;
-      atomicAdd(reinterpret_cast<double*>(stats + b.first + s) + j, ldexp(v, sc));
-    }
+    for (int i = 1; i < 6; ++i) v = j == i ? r[i] : v;
+    atomicAdd(reinterpret_cast<double*>(stats + b.first + s) + j, ldexp(v, stat_shift(j, s_log2)));
   }
 }
 
@@ -613,11 +610,13 @@ hipError_t reduce_t(const SegBatch& b, const Ws& w, nc_counts* out, nc_stats* st
                     const nc_loss_scale* ls, bool clips, hipStream_t stream) {
   const int64_t chunks = b.chunk0[b.count];
   hipLaunchKernelGGL((k_reduce1<COUNTS, STATS>), dim3((uint32_t)chunks), dim3(kThreads), 0, stream, b,
-                     w.cnt1, w.st1, w.cnt2, w.st2);
+                     w.cnt1, w.st1, w.st2, out, stats, ls, clips ? 1 : 0);
   hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((k_reduce2<COUNTS, STATS>), dim3((uint32_t)b.count), dim3(64), 0, stream, b,
-                     w.cnt2, w.st2, out, stats, ls, clips ? 1 : 0);
+  if (e != hipSuccess || !STATS) return e;
+  bool several = false;
+  for (int s = 0; s < b.count; ++s) several = several || b.chunk0[s + 1] - b.chunk0[s] > 1;
+  if (!several) return hipSuccess;
+  hipLaunchKernelGGL(k_reduce2, dim3((uint32_t)b.count), dim3(64), 0, stream, b, w.st2, stats, ls);
   return hipGetLastError();
 }
 

@@ -50,11 +50,11 @@ static_assert(kThreads / col_cast_split(NC_BF16) * 32 * 2 >= kMinWsTile, "column
 constexpr int kSwampVecs = 8;
 constexpr int64_t kSwampTile = (int64_t)kThreads * 4 * kSwampVecs;
 
-// Workspace of one launch: per-tile slots, then per-chunk slots.
+// Workspace of one launch: per-tile slots, then per-chunk statistics slots
+// (counts go from the chunk sums straight into the caller's counts).
 struct Ws {
   CountSlot* cnt1;      // [tiles]
   double* st1;          // [tiles][6]    (statistics only)
-  uint64_t* cnt2;       // [chunks][4]
   double* st2;          // [chunks][6]   (statistics only)
 };
 
@@ -63,7 +63,7 @@ struct Ws {
 inline size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
 inline size_t ws_bytes_for(int64_t tiles, int64_t chunks) {
   return align256((size_t)tiles * sizeof(CountSlot)) + align256((size_t)tiles * 48) +
-         align256((size_t)chunks * 32) + align256((size_t)chunks * 48);
+         align256((size_t)chunks * 48);
 }
 inline Ws ws_layout(void* base, int64_t tiles, int64_t chunks) {
   uint8_t* p = static_cast<uint8_t*>(base);
@@ -72,8 +72,6 @@ inline Ws ws_layout(void* base, int64_t tiles, int64_t chunks) {
   p += align256((size_t)tiles * sizeof(CountSlot));
   w.st1 = reinterpret_cast<double*>(p);
   p += align256((size_t)tiles * 48);
-  w.cnt2 = reinterpret_cast<uint64_t*>(p);
-  p += align256((size_t)chunks * 32);
   w.st2 = reinterpret_cast<double*>(p);
   return w;
 }
@@ -105,7 +103,7 @@ hipError_t launch_stats_col(const SegBatch& b, int dtype, int fmt, const Ws& w, 
 hipError_t launch_reduce(const SegBatch& b, const Ws& w, nc_counts* out, nc_stats* stats,
                          const nc_loss_scale* ls, bool clips, hipStream_t stream);
 hipError_t launch_dequant(const SegBatch& b, int fmt, const nc_scale_state* st, const Launch& l);
-// The monitor's main kernel, its two slot reductions into out, and the
+// The monitor's main kernel, its slot reduction into out, and the
 // promotion window.
 hipError_t launch_swamp(const SegBatch& b, int wfmt, const Ws& w, const Launch& l);
 hipError_t launch_swamp_reduce(const SegBatch& b, const Ws& w, nc_swamp_counts* out, hipStream_t stream);

@@ -8,7 +8,8 @@
 // One workgroup per tile of 8192 elements (32 per lane, eight 16-byte loads
 // of w and eight of d; measured best on MI355X); the four counts (per lane
 // where flag bytes are written, per wave otherwise) go to a workspace slot
-// and two small kernels reduce the slots per tensor in a fixed order.
+// and one small kernel adds the slots of each chunk of tiles into the
+// caller's counts.
 #include "nc_launch.h"
 
 namespace nc {
@@ -196,9 +197,13 @@ k_swamp(const SegBatch b, uint4* __restrict__ slots) {
   write_swamp_slot<!FLAGS>(acc, slots + tile, lds);
 }
 
-// Slot reductions: chunks of kChunk tiles, then per tensor (fixed order).
+// Slot reduction: workgroup c sums chunk c (at most kChunk tiles of one
+// tensor) and adds it into the caller's counts with atomics (integer sums:
+// the order does not matter).  n_considered = n - zero - excluded: the
+// tensor's first chunk adds n, every chunk takes off its own zero and
+// excluded counts, modulo 2^64.
 __global__ void __launch_bounds__(kThreads)
-k_swamp_reduce1(const SegBatch b, const uint4* __restrict__ s1, uint64_t* __restrict__ s2) {
+k_swamp_reduce(const SegBatch b, const uint4* __restrict__ s1, nc_swamp_counts* __restrict__ out) {
   __shared__ uint64_t lds[kWaves * 4];
   const int64_t c = blockIdx.x;
   const int s = seg_of(b.chunk0, b.count, c);
@@ -219,31 +224,17 @@ k_swamp_reduce1(const SegBatch b, const uint4* __restrict__ s1, uint64_t* __rest
     if (lane == 0) lds[wave * 4 + j] = r;
   }
   __syncthreads();
-  if (threadIdx.x < 4) {
-    uint64_t r = 0;
-    for (int w = 0; w < kWaves; ++w) r += lds[w * 4 + threadIdx.x];
-    s2[c * 4 + threadIdx.x] = r;
-  }
-}
-
-__global__ void __launch_bounds__(64)
-k_swamp_reduce2(const SegBatch b, const uint64_t* __restrict__ s2, nc_swamp_counts* __restrict__ out) {
-  const int s = blockIdx.x;
-  uint64_t v[4] = {0, 0, 0, 0};
-  for (int64_t c = b.chunk0[s] + threadIdx.x; c < b.chunk0[s + 1]; c += 64) {
-#pragma unroll
-    for (int j = 0; j < 4; ++j) v[j] += s2[c * 4 + j];
-  }
-#pragma unroll
-  for (int j = 0; j < 4; ++j) v[j] = wave_sum_u64(v[j]);
   if (threadIdx.x == 0) {
+    uint64_t r[4] = {0, 0, 0, 0};
+    for (int w = 0; w < kWaves; ++w)
+      for (int j = 0; j < 4; ++j) r[j] += lds[w * 4 + j];
     nc_swamp_counts* o = out + b.first + s;
-    const uint64_t cons = (uint64_t)b.s[s].n - v[0] - v[3];
+    const uint64_t cons = (c == b.chunk0[s] ? (uint64_t)b.s[s].n : 0u) - r[0] - r[3];   // modulo 2^64
     if (cons) atomicAdd((unsigned long long*)&o->n_considered, (unsigned long long)cons);
-    if (v[0]) atomicAdd((unsigned long long*)&o->n_zero, (unsigned long long)v[0]);
-    if (v[1]) atomicAdd((unsigned long long*)&o->n_below, (unsigned long long)v[1]);
-    if (v[2]) atomicAdd((unsigned long long*)&o->n_noop, (unsigned long long)v[2]);
-    if (v[3]) atomicAdd((unsigned long long*)&o->n_excluded, (unsigned long long)v[3]);
+    if (r[0]) atomicAdd((unsigned long long*)&o->n_zero, (unsigned long long)r[0]);
+    if (r[1]) atomicAdd((unsigned long long*)&o->n_below, (unsigned long long)r[1]);
+    if (r[2]) atomicAdd((unsigned long long*)&o->n_noop, (unsigned long long)r[2]);
+    if (r[3]) atomicAdd((unsigned long long*)&o->n_excluded, (unsigned long long)r[3]);
   }
 }
 
@@ -281,11 +272,8 @@ hipError_t launch_swamp(const SegBatch& b, int wfmt, const Ws& w, const Launch& 
 }
 
 hipError_t launch_swamp_reduce(const SegBatch& b, const Ws& w, nc_swamp_counts* out, hipStream_t stream) {
-  hipLaunchKernelGGL(k_swamp_reduce1, dim3((uint32_t)b.chunk0[b.count]), dim3(kThreads), 0, stream, b,
-                     reinterpret_cast<const uint4*>(w.cnt1), w.cnt2);
-  const hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(k_swamp_reduce2, dim3((uint32_t)b.count), dim3(64), 0, stream, b, w.cnt2, out);
+  hipLaunchKernelGGL(k_swamp_reduce, dim3((uint32_t)b.chunk0[b.count]), dim3(kThreads), 0, stream, b,
+                     reinterpret_cast<const uint4*>(w.cnt1), out);
   return hipGetLastError();
 }
 

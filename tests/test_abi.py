@@ -68,7 +68,7 @@ def _desc(*specs, axes=None):
 
 def _ws_expect(sizes):
     """Workspace bytes as the header documents them: per launch (at most 32
-    tensors), 16 + 48 bytes per tile of 2048 elements and 32 + 48 bytes per
+    tensors), 16 + 48 bytes per tile of 2048 elements and 48 bytes per
     chunk of 1024 tiles, each array rounded up to 256 bytes; the largest
     launch counts."""
     r = lambda v: (v + 255) // 256 * 256
@@ -76,7 +76,7 @@ def _ws_expect(sizes):
     for i in range(0, len(sizes), 32):
         tiles = [-(-n // 2048) for n in sizes[i:i + 32]]
         T, C = sum(tiles), sum(-(-t // 1024) for t in tiles)
-        best = max(best, r(16 * T) + r(48 * T) + r(32 * C) + r(48 * C))
+        best = max(best, r(16 * T) + r(48 * T) + r(48 * C))
     return best
 
 
@@ -128,7 +128,7 @@ def test_argument_checks_before_any_launch(lib):
     # workspace size
     d = _desc((A, A, 10000, 0, None))
     need = lib.nc_workspace_bytes(d, 1)
-    assert need == _ws_expect([10000]) == 1024
+    assert need == _ws_expect([10000]) == 768
     sizes = [10] * 40 + [(1 << 22) + 5, 0, 3 * 2048 * 1024]
     assert lib.nc_workspace_bytes(_desc(*[(A, A, n, 0, None) for n in sizes]), len(sizes)) == _ws_expect(sizes)
     assert lib.nc_workspace_bytes(None, 0) == 0
@@ -183,13 +183,13 @@ def test_swamp_checks(lib):
     assert lib.nc_swamp_watch(d, 1, 0, A, A, need - 16, None) == _lib.NC_E_WORKSPACE
     assert lib.nc_swamp_watch(None, 0, 0, None, None, 0, None) == _lib.NC_OK
     assert lib.nc_swamp_watch(_udesc((None, None, None, 0)), 1, 0, A, A, W, None) == _lib.NC_OK
-    # workspace: 16 + 48 B per tile of 8192 elements, 32 + 48 B per chunk of 1024 tiles, arrays rounded
+    # workspace: 16 + 48 B per tile of 8192 elements, 48 B per chunk of 1024 tiles, arrays rounded
     # to 256 B, the largest launch of <= 32 tensors
     r = lambda v: (v + 255) // 256 * 256
     T = -(-(3 * 4096 * 1024 + 5) // 8192)
     C = -(-T // 1024)
     assert lib.nc_swamp_workspace_bytes(_udesc((A, A, None, 3 * 4096 * 1024 + 5)), 1) == \
-        r(16 * T) + r(48 * T) + r(32 * C) + r(48 * C)
+        r(16 * T) + r(48 * T) + r(48 * C)
     P = _lib.NcSwampPolicy
     for pol in (P(0, 1, 2, 0), P(4, 3, 2, 0), P(4, 1, 0, 0), P(4, 1, 70000, 0)):
         assert lib.nc_swamp_window(ctypes.byref(pol), 1, A, A, None) == _lib.NC_E_ARG
