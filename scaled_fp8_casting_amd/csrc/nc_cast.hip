@@ -474,10 +474,9 @@ k_cast_mx(const SegBatch b, CountSlot* __restrict__ slots, double* __restrict__ 
 // X): the layout of an operand consumed transposed.  A slot (col_slot) is
 // VC = 8 / BYTES adjacent columns of a 32-row band, 8 input bytes per row;
 // SPLIT adjacent lanes share it (two for bf16), each loading 32 / SPLIT of
-// its rows.  Each
-// lane takes its columns' finite max over its rows in registers, the lanes
-// of a slot exchange theirs by one DPP swap, and each casts and stores its
-// own rows.
+// its rows.  Each lane takes its columns' finite max over its rows in
+// registers, the lanes of a slot exchange theirs by one DPP swap, and each
+// casts and stores its own rows.
 template <int FMT, int DT, int RULE, bool STATS>
 NC_STREAM_KERNEL
 k_cast_mx_col(const SegBatch b, CountSlot* __restrict__ slots, double* __restrict__ stat_slots) {

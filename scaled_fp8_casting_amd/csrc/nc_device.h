@@ -60,8 +60,10 @@ constexpr int kChunk = 1024;        // per-workgroup slots summed by one workgro
 // streams than a persistent grid striding over the tensor (measured: a
 // cast-shaped stream 82% of peak vs 72%, a dequant-shaped one 81% vs 69%).
 // Each workgroup writes its partial results (counts, amax, statistics) to
-// its own workspace slot; two small kernels then reduce the slots per tensor
-// in a fixed order (one same-address atomic per workgroup would serialise).
+// its own workspace slot (one same-address atomic per workgroup would
+// serialise); a small kernel then sums each chunk of slots, adding the
+// counts into the caller's and the statistics in a fixed order (through a
+// second small kernel for a tensor of several chunks).
 #define NC_STREAM_KERNEL __global__ void __launch_bounds__(nc::kThreads)
 
 // ---------------------------------------------------------------------------
