@@ -93,3 +93,94 @@ def test_graph_capture_and_replay():
         torch.cuda.synchronize()
         for i, (u, v) in enumerate(zip(got, e_step.outputs())):
             assert torch.equal(u, v), (rep, i)
+
+
+class _Rest:
+    """The other entry points on fixed buffers: delayed scaling with a
+    history window, the per-tensor cast with fused statistics, the
+    stochastic-rounding cast, the separate statistics passes, MX with blocks
+    down the columns (cast, dequant, statistics), and the update/step monitor
+    with its window (with and without flag bytes)."""
+
+    def __init__(self, n, cols):
+        dev = "cuda"
+        self.x = torch.empty(n, dtype=torch.bfloat16, device=dev)
+        self.w = torch.empty(n, dtype=torch.float32, device=dev)
+        self.d = torch.empty(n, dtype=torch.float32, device=dev)
+        self.cols = cols
+        self.codes, self.sr, self.colc = (torch.empty(n, dtype=torch.uint8, device=dev) for _ in range(3))
+        self.sc = torch.empty(n // 32, dtype=torch.uint8, device=dev)
+        self.y = torch.empty(n, dtype=torch.bfloat16, device=dev)
+        self.flags = torch.empty(n, dtype=torch.uint8, device=dev)
+        desc, cnt = nc.tensors([self.x], [self.codes])
+        self.ws = nc.new_workspace(desc, cnt)
+        self.sws = nc.new_swamp_workspace([self.w], [self.d])
+        self.st, self.hist = nc.new_state(1), nc.new_history(1, 4)
+        self.c = [nc.new_counts(1) for _ in range(4)]
+        self.s = [nc.new_stats(1) for _ in range(4)]
+        self.sw = [nc.new_swamp_counts(1) for _ in range(2)]
+        self.swst = nc.new_swamp_state(1)
+        self.pol = nc.policy("e4m3", "max_window", 4)
+        self.spol = nc.swamp_policy(window=2, num=1, den=4)
+        self.step = 0
+
+    def run(self):
+        for t in self.c + self.s + self.sw:
+            t.zero_()                                    # fill kernels, not memset nodes
+        x, c = [self.x], self.c
+        nc.nc_cast_tensor(x, [self.codes], "e4m3", self.st, c[0], stats=self.s[0], ws=self.ws)
+        nc.nc_scale_update(self.pol, self.st, c[0], self.hist)
+        nc.nc_cast_tensor_sr(x, [self.sr], "e4m3", self.st, c[1], 77, 5, ws=self.ws)
+        nc.nc_cast_stats(x, [self.codes], "e4m3", self.s[1], self.ws, st=self.st)
+        nc.nc_cast_mx(x, [self.colc], [self.sc], [self.cols], "e5m2", "ceil", c[2], ws=self.ws, axis="cols")
+        nc.nc_dequant([self.colc], [self.y], "e5m2", scales=[self.sc], cols=[self.cols], axis="cols")
+        nc.nc_cast_stats(x, [self.colc], "e5m2", self.s[2], self.ws, scales=[self.sc], cols=[self.cols],
+                         axis="cols")
+        nc.nc_swamp_watch([self.w], [self.d], "bf16", self.sw[0], workspace=self.sws)
+        nc.nc_swamp_watch([self.w], [self.d], "fp16", self.sw[1], flags=[self.flags], workspace=self.sws)
+        nc.nc_swamp_window(self.spol, self.swst, self.sw[0])
+
+    def outputs(self):
+        ts = [self.codes, self.sr, self.colc, self.sc, self.y.view(torch.int16), self.flags, self.st, self.hist,
+              self.swst] + self.c + self.s + self.sw
+        return [t.clone() for t in ts]
+
+
+def _fill_rest(r, seed, n):
+    r.x.copy_(_data(seed, n))
+    g = np.random.default_rng(seed)
+    w = g.normal(0.0, 0.02, n).astype(np.float32)
+    d = (1e-4 * g.standard_normal(n) * 10.0 ** g.uniform(-3, 1, n)).astype(np.float32)
+    r.w.copy_(torch.from_numpy(w))
+    r.d.copy_(torch.from_numpy(d))
+
+
+def test_graph_capture_and_replay_other_entry_points():
+    """Replays 0-3 of the captured sequence against the same calls run
+    eagerly in between; the scale, history and window states evolve across
+    replays on both sides alike."""
+    cols = 1056
+    n = 96 * cols                                        # 96 rows: three 32-row bands; ragged row tiles
+    g_rest, e_rest = _Rest(n, cols), _Rest(n, cols)
+    _fill_rest(g_rest, 20, n)
+    _fill_rest(e_rest, 20, n)
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        g_rest.run()
+    torch.cuda.current_stream().wait_stream(s)
+    e_rest.run()                                         # the warm-up step, eagerly on the other side too
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        g_rest.run()
+    for rep in range(4):
+        _fill_rest(g_rest, 30 + rep, n)
+        graph.replay()
+        torch.cuda.synchronize()
+        got = g_rest.outputs()
+        _fill_rest(e_rest, 30 + rep, n)
+        e_rest.run()
+        torch.cuda.synchronize()
+        for i, (u, v) in enumerate(zip(got, e_rest.outputs())):
+            assert torch.equal(u, v), (rep, i)
