@@ -381,7 +381,7 @@ def small_configs(nc, torch, workloads):
         us=round(ms * 1e3, 1), gbps=round(5 * ne / (ms * 1e-3) / 1e9, 1),
         frac=round(5 * ne / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4), us_graph=round(msg * 1e3, 1),
         elements=ne, tensors=T,
-        note="per step: counter zeroing, one batched cast (two launches of 32 tensors), one scale update")
+        note="per step: counter zeroing, one batched cast, one scale update")
     del scratch, g
     torch.cuda.empty_cache()
     return res

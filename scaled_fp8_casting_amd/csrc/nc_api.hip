@@ -88,8 +88,8 @@ void make_batch(SegBatch& b, const T* t, int32_t first, int32_t end, int64_t til
     g.n = x.n;
     const int64_t units = x.n / unit;
     const int64_t tiles = (units + tile - 1) / tile;
-    b.tile0[s + 1] = b.tile0[s] + tiles;
-    b.chunk0[s + 1] = b.chunk0[s] + (tiles + kChunk - 1) / kChunk;
+    b.tile0[s + 1] = (int32_t)(b.tile0[s] + tiles);
+    b.chunk0[s + 1] = (int32_t)(b.chunk0[s] + (tiles + kChunk - 1) / kChunk);
     b.last[s] = tiles ? (int32_t)(units - (tiles - 1) * tile) : 0;
   }
   for (int s = b.count + 1; s <= kMaxSeg; ++s) {

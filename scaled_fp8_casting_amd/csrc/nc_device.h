@@ -49,7 +49,7 @@ template <> struct In<NC_F32> { static constexpr int VEC = 4, BYTES = 4; };
 template <> struct In<NC_BF16> { static constexpr int VEC = 8, BYTES = 2; };
 
 constexpr int kThreads = 256;       // 4 wave64s per workgroup
-constexpr int kMaxSeg = 32;         // tensors per launch (descriptors travel as kernel arguments)
+constexpr int kMaxSeg = 64;         // tensors per launch (descriptors travel as kernel arguments)
 constexpr int kWaves = kThreads / 64;
 constexpr int kChunk = 1024;        // per-workgroup slots summed by one workgroup of the first reduction
 
@@ -427,8 +427,8 @@ struct Seg {
 
 struct SegBatch {
   Seg s[kMaxSeg];
-  int64_t tile0[kMaxSeg + 1];
-  int64_t chunk0[kMaxSeg + 1];
+  int32_t tile0[kMaxSeg + 1];    // < 2^31: a launch has at most 2^34 elements, 2048 or more per tile
+  int32_t chunk0[kMaxSeg + 1];
   int32_t last[kMaxSeg];   // elements in tensor s's last tile (1..tile size; 0 if empty)
   int32_t count;   // tensors in this launch
   int32_t first;   // index of s[0] in the caller's arrays (counts, states, stats)
@@ -441,7 +441,7 @@ static_assert(sizeof(SegBatch) <= 4096, "a SegBatch travels as a kernel argument
 // counts the hits: one load per lane instead of a chain of up to 31
 // dependent scalar loads.  A one-tensor launch loads nothing.  Called by
 // whole waves; the result is wave-uniform.
-__device__ __forceinline__ int seg_of(const int64_t* start, int count, int64_t i) {
+__device__ __forceinline__ int seg_of(const int32_t* start, int count, int64_t i) {
   if (count == 1) return 0;
   const int l = threadIdx.x & 63;
   const bool hit = l + 1 < count && i >= start[l + 1];

@@ -67,14 +67,14 @@ def _desc(*specs, axes=None):
 
 
 def _ws_expect(sizes):
-    """Workspace bytes as the header documents them: per launch (at most 32
+    """Workspace bytes as the header documents them: per launch (at most 64
     tensors), 16 + 48 bytes per tile of 2048 elements and 48 bytes per
     chunk of 1024 tiles, each array rounded up to 256 bytes; the largest
     launch counts."""
     r = lambda v: (v + 255) // 256 * 256
     best = 0
-    for i in range(0, len(sizes), 32):
-        tiles = [-(-n // 2048) for n in sizes[i:i + 32]]
+    for i in range(0, len(sizes), 64):
+        tiles = [-(-n // 2048) for n in sizes[i:i + 64]]
         T, C = sum(tiles), sum(-(-t // 1024) for t in tiles)
         best = max(best, r(16 * T) + r(48 * T) + r(48 * C))
     return best
@@ -184,7 +184,7 @@ def test_swamp_checks(lib):
     assert lib.nc_swamp_watch(None, 0, 0, None, None, 0, None) == _lib.NC_OK
     assert lib.nc_swamp_watch(_udesc((None, None, None, 0)), 1, 0, A, A, W, None) == _lib.NC_OK
     # workspace: 16 + 48 B per tile of 8192 elements, 48 B per chunk of 1024 tiles, arrays rounded
-    # to 256 B, the largest launch of <= 32 tensors
+    # to 256 B, the largest launch of <= 64 tensors
     r = lambda v: (v + 255) // 256 * 256
     T = -(-(3 * 4096 * 1024 + 5) // 8192)
     C = -(-T // 1024)

@@ -196,16 +196,16 @@ def test_stats_mx_fused_and_separate(dtype, rule, off):
 
 
 def test_stats_batch_of_many_tensors():
-    """40 tensors (two launches), ragged sizes, statistics per tensor."""
+    """70 tensors (two launches), ragged sizes, statistics per tensor."""
     rng = np.random.default_rng(6)
-    sizes = [int(v) for v in rng.integers(1, 20000, 40)]
+    sizes = [int(v) for v in rng.integers(1, 20000, 70)]
     sizes[3] = 0
     xs = [(rng.standard_normal(m) * 10.0 ** rng.uniform(-4, 4)).astype(np.float32) for m in sizes]
     xd = [dev_f32(x) for x in xs]
     codes = [codes_like(m) for m in sizes]
-    ks = [int(v) for v in rng.integers(-5, 20, 40)]
-    out = nc.new_counts(40)
-    stats = nc.new_stats(40)
+    ks = [int(v) for v in rng.integers(-5, 20, 70)]
+    out = nc.new_counts(70)
+    stats = nc.new_stats(70)
     desc, cnt = nc.tensors(xd, codes)
     ws = nc.new_workspace(desc, cnt)
     nc.nc_cast_tensor(xd, codes, "e5m2", state_with_k(ks), out, stats=stats, ws=ws)

@@ -33,7 +33,7 @@ def _expect_pt(fmt, x64, k, s=0):
 def test_all_bf16_patterns_every_K(name, fmt):
     """All 65,536 bf16 patterns at every exponent K in [-191, 127] (every
     k in [-127, 127] with unscales up to 2^64), one tensor per K in a single
-    batched call (several launches of 32)."""
+    batched call (several launches of 64)."""
     bits = np.arange(65536, dtype=np.uint32).astype(np.uint16)
     x64 = bulk.bf16_bits_to_f64(bits)
     Ks = list(range(-191, 128))
@@ -411,9 +411,9 @@ def test_mx_column_blocks_parity(dtype, rule, name, fmt, rows, cols):
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 def test_mx_column_blocks_batch_of_tensors(dtype):
-    """Several shapes in one call (one launch), then 40 tensors (two
+    """Several shapes in one call (one launch), then 70 tensors (two
     launches): each tensor's codes, scales and counts."""
-    for shapes in ([(32, 32), (64, 1024), (96, 160), (32, 8192)], [(32, 64 * (1 + i % 5)) for i in range(40)]):
+    for shapes in ([(32, 32), (64, 1024), (96, 160), (32, 8192)], [(32, 64 * (1 + i % 5)) for i in range(70)]):
         ins = [_col_input(r, c, 7 * i + r, dtype) for i, (r, c) in enumerate(shapes)]
         codes, scales, counts = _cast_mx_cols([d for d, _ in ins], shapes, "e4m3", "ocp")
         for (r, c), (_, x64), cg, sg, ng in zip(shapes, ins, codes, scales, counts):

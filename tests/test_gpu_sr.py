@@ -94,14 +94,14 @@ def test_sr_fp32_subnormal_inputs(name, fmt, k):
 
 
 def test_sr_tensor_index_and_launches():
-    """40 tensors (two launches; tensor j draws with counter word j, its
+    """70 tensors (two launches; tensor j draws with counter word j, its
     index in the call), ragged sizes, one empty."""
     r = np.random.default_rng(3)
-    sizes = [int(v) for v in r.integers(1, 30000, 40)]
+    sizes = [int(v) for v in r.integers(1, 30000, 70)]
     sizes[5] = 0
     ins = [_input("f32", m, 7 + j) if m else (dev_f32(np.zeros(0, np.float32)), np.zeros(0)) for j, m in
            enumerate(sizes)]
-    ks = [int(v) for v in r.integers(-10, 20, 40)]
+    ks = [int(v) for v in r.integers(-10, 20, 70)]
     codes, counts = _sr([d for d, _ in ins], "e4m3", ks, 77, 5)
     for j, ((_, x64), k) in enumerate(zip(ins, ks)):
         want, wn = bulk.cast_tensor_sr_f64(E4M3, x64, k, 0, 77, 5, j)

@@ -77,10 +77,10 @@ def test_flags_every_pattern_and_tie(name, fmt):
 
 @pytest.mark.parametrize("name,fmt", WF)
 def test_batches_ragged_and_without_flags(name, fmt):
-    """40 tensors (two launches) of ragged sizes, one empty; the counts with
+    """70 tensors (two launches) of ragged sizes, one empty; the counts with
     and without the flag output are the same."""
     r = np.random.default_rng(5)
-    sizes = [int(v) for v in r.integers(1, 40000, 40)]
+    sizes = [int(v) for v in r.integers(1, 40000, 70)]
     sizes[7] = 0
     sizes[8] = 8192 * 3
     pairs = [_random_pairs(m, 10 + j) if m else (np.zeros(0, np.float32), np.zeros(0, np.float32))
