@@ -7,13 +7,13 @@
 namespace nc {
 
 // Elements per workgroup tile: 256 lanes x a few 16-byte input vectors --
-// two for the casts, four when they also form statistics, eight for the
-// statistics pass and four for the amax pass (read only: tile size does not
+// two for the casts, eight when they also form statistics (and for the
+// statistics pass), four for the amax pass (read only: tile size does not
 // matter for bandwidth there, and larger tiles spread the per-workgroup
 // reductions over more elements); dequant: 256 lanes x two vectors of 8
 // codes (a 16-byte bf16 store each).  Measured best on MI355X.
 constexpr int kCastVecs = 2;
-constexpr int kCastStatsVecs = 4;   // casts with fused statistics (more work per element)
+constexpr int kCastStatsVecs = 8;   // casts with fused statistics (more work per element)
 constexpr int kStatsVecs = 8;       // the statistics pass (read only)
 constexpr int kAmaxVecs = 4;
 template <bool STATS> constexpr int cast_vecs() { return STATS ? kCastStatsVecs : kCastVecs; }
