@@ -230,7 +230,7 @@ nc_status nc_cast_tensor_sr(const nc_tensor* t, int32_t count, nc_dtype dtype, n
   if (count == 0) return NC_OK;
   if (out == nullptr || st == nullptr) return NC_E_ARG;
   if ((s = check_ws(t, count, ws, ws_bytes)) != NC_OK) return s;
-  const int64_t tile = tile_elems(in_bytes(dtype), kCastVecs);
+  const int64_t tile = tile_elems(in_bytes(dtype), kCastSrVecs);
   return for_batches(t, count, tile, nullptr, [&](const SegBatch& b) {
     const Ws w = ws_of(b, ws);
     nc_status r = hip_status(launch_cast_sr(b, dtype, fmt, st, ls, seed, offset, w,

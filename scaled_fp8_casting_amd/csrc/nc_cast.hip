@@ -241,7 +241,7 @@ NC_STREAM_KERNEL
 k_cast_sr(const SegBatch b, const nc_scale_state* __restrict__ st, const nc_loss_scale* __restrict__ ls,
           uint64_t seed, uint64_t offset, CountSlot* __restrict__ slots) {
   constexpr int VEC = In<DT>::VEC;
-  constexpr int U = kCastVecs;
+  constexpr int U = kCastSrVecs;
   constexpr int64_t TILE = (int64_t)kThreads * VEC * U;
   __shared__ uint32_t lds[kRows * 4];
   const int64_t tile = blockIdx.x;
