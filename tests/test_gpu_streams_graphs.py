@@ -184,3 +184,30 @@ def test_graph_capture_and_replay_other_entry_points():
         torch.cuda.synchronize()
         for i, (u, v) in enumerate(zip(got, e_rest.outputs())):
             assert torch.equal(u, v), (rep, i)
+
+
+def test_two_streams_at_once():
+    """Two different steps enqueued on two streams with no ordering between
+    them (each with its own workspace and outputs) give what each gives on
+    its own: the library keeps no state between calls."""
+    n, cols = 6 * 8192 + 1024, 1024
+    a, b, a1, b1 = (_Step(n, cols) for _ in range(4))
+    xa, xb = _data(40, n), _data(41, n)
+    for s_, x in ((a, xa), (b, xb), (a1, xa), (b1, xb)):
+        s_.x.copy_(x)
+    a1.run()
+    b1.run()
+    torch.cuda.synchronize()
+    s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()
+    s1.wait_stream(torch.cuda.current_stream())
+    s2.wait_stream(torch.cuda.current_stream())
+    for _ in range(3):                                   # several rounds, so the two overlap on the device
+        with torch.cuda.stream(s1):
+            a.run(stream=s1)
+        with torch.cuda.stream(s2):
+            b.run(stream=s2)
+    torch.cuda.synchronize()
+    for u, v in zip(a.outputs(), a1.outputs()):
+        assert torch.equal(u, v)
+    for u, v in zip(b.outputs(), b1.outputs()):
+        assert torch.equal(u, v)
