@@ -304,7 +304,7 @@ nc_status nc_cast_stats(const nc_tensor* t, int32_t count, nc_dtype dtype, nc_fm
       nc_status r = hip_status(launch_stats_col(b, dtype, fmt, w, Launch{b.tile0[b.count], (hipStream_t)stream}));
       if (r == NC_OK) r = hip_status(launch_reduce(b, w, nullptr, out, nullptr, false, (hipStream_t)stream));
       return r;
-    }, col_unit(in_bytes(dtype), kStatsColRows));
+    }, stats_col_unit(in_bytes(dtype)));
   const int64_t tile = tile_elems(in_bytes(dtype), kStatsVecs);
   return for_batches(t, count, tile, nullptr, [&](const SegBatch& b) {
     const Ws w = ws_of(b, ws);

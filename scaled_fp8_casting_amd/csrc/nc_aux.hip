@@ -380,41 +380,40 @@ k_stats(const SegBatch b, const nc_scale_state* __restrict__ st,
 }
 
 // Statistics of column-block MX codes: a lane owns one col_slot (VC =
-// 8 / BYTES columns of kStatsColRows rows), reads its VC scale bytes once, then
-// per row 8 input bytes and VC codes, in two halves.
-// Accumulation is unmasked as in k_stats, with the masked redo when an
-// Inf/NaN was met.
+// 16 / BYTES columns -- 8 bf16 or 4 fp32 -- of a 32-row band), reads its VC
+// scale bytes once, then per row 16 input bytes and VC codes (8 or 4
+// bytes), eight rows at a time.  Accumulation is unmasked as in k_stats,
+// with the masked redo when an Inf/NaN was met.
 template <int DT>
 struct ColCodes;
-template <> struct ColCodes<NC_F32> {      // 2 codes per row
-  __device__ static uint32_t load(const uint8_t* p) {
-    return __builtin_nontemporal_load(reinterpret_cast<const uint16_t*>(p));
+template <> struct ColCodes<NC_F32> {      // 4 codes per row
+  __device__ static u32x2 load(const uint8_t* p) {
+    return u32x2{__builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(p)), 0u};
   }
 };
-template <> struct ColCodes<NC_BF16> {     // 4 codes per row
-  __device__ static uint32_t load(const uint8_t* p) {
-    return __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(p));
-  }
+template <> struct ColCodes<NC_BF16> {     // 8 codes per row
+  __device__ static u32x2 load(const uint8_t* p) { return ld_stream(reinterpret_cast<const u32x2*>(p)); }
 };
 
 template <int DT, bool FINITE>
-__device__ __forceinline__ void stats_col_row(u32x2 v, uint32_t w, const double* tab, const double* blk,
+__device__ __forceinline__ void stats_col_row(u32x4 v, u32x2 w, const double* tab, const double* blk,
                                               StatAcc& sa) {
-  constexpr int VC = kColBytes / In<DT>::BYTES;
+  constexpr int VC = In<DT>::VEC;
   uint32_t xb[VC];
-  unpack8<DT>(v, xb);
+  unpack<DT>(v, xb);
 #pragma unroll
   for (int i = 0; i < VC; ++i) {
     if (!FINITE && (xb[i] & kAbsMask) > kMaxFinite) continue;
-    stat_term((double)__uint_as_float(xb[i]), tab[(w >> (8 * i)) & 0xFFu] * blk[i], sa);
+    const uint32_t q = ((i < 4 ? w.x : w.y) >> (8 * (i % 4))) & 0xFFu;
+    stat_term((double)__uint_as_float(xb[i]), tab[q] * blk[i], sa);
   }
 }
 
 template <int FMT, int DT>
 NC_STREAM_KERNEL
 k_stats_col(const SegBatch b, double* __restrict__ stat_slots) {
-  constexpr int VC = kColBytes / In<DT>::BYTES, R = kStatsColRows;
-  constexpr int H = R / 2;                  // rows per half
+  constexpr int VC = In<DT>::VEC, R = kStatsColRows;
+  constexpr int Q = 8;                      // rows per batch of loads
   __shared__ double tab[256];
   __shared__ double lds_st[kRows * 6];
   const int64_t tile = blockIdx.x;
@@ -430,21 +429,21 @@ k_stats_col(const SegBatch b, double* __restrict__ stat_slots) {
   StatAcc sa;
   sa.reset();
 #pragma unroll
-  for (int h = 0; h < 2; ++h) {
-    u32x2 v[H];
-    uint32_t w[H];
+  for (int h = 0; h < R / Q; ++h) {
+    u32x4 v[Q];
+    u32x2 w[Q];
 #pragma unroll
-    for (int r = 0; r < H; ++r) {
-      const int64_t row = h * H + r;
-      v[r] = ld_stream(reinterpret_cast<const u32x2*>(xs + row * cols * In<DT>::BYTES));
+    for (int r = 0; r < Q; ++r) {
+      const int64_t row = h * Q + r;
+      v[r] = ld_stream(reinterpret_cast<const u32x4*>(xs + row * cols * In<DT>::BYTES));
       w[r] = ColCodes<DT>::load(qs + row * cols);
     }
     __builtin_amdgcn_sched_barrier(0);
     if (!cs.act) {                          // idle lane (last tile): zeros add nothing
 #pragma unroll
-      for (int r = 0; r < H; ++r) {
-        v[r] = u32x2{0u, 0u};
-        w[r] = 0u;
+      for (int r = 0; r < Q; ++r) {
+        v[r] = u32x4{0u, 0u, 0u, 0u};
+        w[r] = u32x2{0u, 0u};
       }
     }
     if (h == 0) {                           // the table fill overlaps the first loads
@@ -452,7 +451,7 @@ k_stats_col(const SegBatch b, double* __restrict__ stat_slots) {
       __syncthreads();
     }
 #pragma unroll
-    for (int r = 0; r < H; ++r) {
+    for (int r = 0; r < Q; ++r) {
       stats_col_row<DT, true>(v[r], w[r], tab, blk, sa);
       __builtin_amdgcn_sched_barrier(0);    // one row's table reads at a time (register pressure)
     }
@@ -461,7 +460,7 @@ k_stats_col(const SegBatch b, double* __restrict__ stat_slots) {
     __asm__ volatile("" ::: "memory");      // keeps the compiler from holding the first loads for this
     sa.reset();
     for (int row = 0; row < R && cs.act; ++row) {
-      const u32x2 v = *reinterpret_cast<const u32x2*>(xs + row * cols * In<DT>::BYTES);
+      const u32x4 v = *reinterpret_cast<const u32x4*>(xs + row * cols * In<DT>::BYTES);
       stats_col_row<DT, false>(v, ColCodes<DT>::load(qs + row * cols), tab, blk, sa);
     }
   }

@@ -25,9 +25,9 @@ inline int64_t tile_elems(int in_bytes, int vecs) { return (int64_t)kThreads * (
 constexpr int64_t kMinWsTile = (int64_t)kThreads * 4 * kCastVecs;
 
 // Column-block MX (col_slot): a lane reads 8 input bytes per row (4 bf16 or
-// 2 fp32 columns), or 8 codes per row in dequant.  Rows per slot, measured
-// best on MI355X: the cast needs whole 32-row bands; the statistics pass is
-// fastest with them too.  Dequant takes whole bands as well, but each lane
+// 2 fp32 columns), or 8 codes per row in dequant, or 16 input bytes per row
+// in the statistics pass.  Rows per slot, measured best on MI355X: the cast
+// needs whole 32-row bands; the statistics pass is fastest with them too.  Dequant takes whole bands as well, but each lane
 // only kDequantColRows of a band's rows: the four waves of a workgroup hold
 // the four 8-row parts of the same 64 slots (a tile of 16 KiB of codes), so
 // a band's scale bytes are fetched once and hit in cache for the other
@@ -42,6 +42,9 @@ constexpr int kStatsColRows = 32;
 // registers of a whole band), one for fp32 (measured faster whole).
 constexpr int col_cast_split(int dtype) { return dtype == NC_BF16 ? 2 : 1; }
 inline int64_t col_unit(int in_bytes, int rows = 32) { return rows * (kColBytes / in_bytes); }
+// The column statistics pass reads 16 input bytes per row (8 bf16 or 4 fp32
+// columns per slot).
+inline int64_t stats_col_unit(int in_bytes) { return 32 * (16 / in_bytes); }
 constexpr int64_t kDequantColUnit = 32 * kDequantColCodes;          // codes per slot
 static_assert(kThreads * kStatsColRows * 2 >= kMinWsTile, "column tiles are no smaller than kMinWsTile");
 static_assert(kThreads / col_cast_split(NC_BF16) * 32 * 2 >= kMinWsTile, "column tiles are no smaller than kMinWsTile");
