@@ -393,7 +393,7 @@ def main():
         write_traffic(*a.write_traffic)
         return
     if a.gpus != 1:
-        print(f"bench.py measures one GPU only: this build has no multi-GPU path "
+        print(f"bench.py measures one GPU only: the library has no multi-GPU path "
               f"(--gpus {a.gpus} requested). Run with --gpus 1.", file=sys.stderr)
         sys.exit(2)
     import torch
