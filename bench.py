@@ -446,10 +446,10 @@ def main():
         for b in ("am", "cpt", "cmx", "spt", "smx"):
             bufs[b].zero_()
         calls = [
-            lambda: nc.nc_amax([x], bufs["am"]),
+            lambda: nc.nc_amax([x], bufs["am"], ws=ws),
             lambda: nc.nc_scale_update(pol, bufs["st"], bufs["am"]),
-            lambda: nc.nc_cast_tensor([x], [codes_pt], "e4m3", bufs["st"], bufs["cpt"]),
-            lambda: nc.nc_cast_mx([x], [codes_mx], [scales], [COLS], "e4m3", "ocp", bufs["cmx"]),
+            lambda: nc.nc_cast_tensor([x], [codes_pt], "e4m3", bufs["st"], bufs["cpt"], ws=ws),
+            lambda: nc.nc_cast_mx([x], [codes_mx], [scales], [COLS], "e4m3", "ocp", bufs["cmx"], ws=ws),
             lambda: nc.nc_dequant([codes_pt], [y_pt], "e4m3", st=bufs["st"]),
             lambda: nc.nc_dequant([codes_mx], [y_mx], "e4m3", scales=[scales], cols=[COLS]),
             lambda: nc.nc_cast_stats([x], [codes_pt], "e4m3", bufs["spt"], ws, st=bufs["st"]),
