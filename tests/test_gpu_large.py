@@ -79,3 +79,37 @@ def test_one_tensor_past_2p31():
     torch.cuda.synchronize()
     K = np.repeat(127 - ms.astype(np.int64), 32)
     assert _rows_equal(y.view(torch.int16), bulk.dequant_bf16_f64(E4M3, mc, K).view(np.int16))
+
+
+def test_column_blocks_past_2p31():
+    """Column blocks on 32,800 rows of the same 65,536-pattern row
+    (2,149,580,800 elements): each 32-row band of a column holds one value 32
+    times, so every band of codes and every row of scale bytes is the same
+    and checked in full against the oracle's band; dequant likewise."""
+    rows = 32800
+    n = rows * COLS
+    assert n > 1 << 31 and rows % 32 == 0
+    bits = np.arange(COLS, dtype=np.uint32).astype(np.uint16)
+    x = torch.from_numpy(bits.view(np.int16)).cuda().repeat(rows).view(torch.bfloat16)
+    band = np.tile(bits, 32)
+    vb = bulk.bf16_bits_to_f64(band)
+    mc, ms, mn = bulk.cast_mx_f64(E4M3, vb, COLS, "ocp", axis="cols")
+    codes = torch.empty(n, dtype=torch.uint8, device="cuda")
+    scales = torch.empty(n // 32, dtype=torch.uint8, device="cuda")
+    desc, cnt = nc.tensors([x], [codes])
+    ws = nc.new_workspace(desc, cnt)
+    out = nc.new_counts(1)
+    nc.nc_cast_mx([x], [codes], [scales], [COLS], "e4m3", "ocp", out, ws=ws, axis="cols")
+    torch.cuda.synchronize()
+    bands = rows // 32
+    assert bool((codes.view(bands, -1) == torch.from_numpy(mc).cuda()).all())
+    assert bool((scales.view(bands, -1) == torch.from_numpy(ms).cuda()).all())
+    c = nc.counts_list(out)[0]
+    for f in ("n_finite", "n_clip", "n_underflow", "n_nonfinite"):
+        assert c[f] == bands * mn[f], f
+    y = torch.empty(n, dtype=torch.bfloat16, device="cuda")
+    nc.nc_dequant([codes], [y], "e4m3", scales=[scales], cols=[COLS], axis="cols")
+    torch.cuda.synchronize()
+    K = -bulk.mx_element_exponents(ms.astype(np.int64) - 127, mc.size, COLS, "cols")
+    want = torch.from_numpy(bulk.dequant_bf16_f64(E4M3, mc, K).view(np.int16)).cuda()
+    assert bool((y.view(torch.int16).view(bands, -1) == want).all())
