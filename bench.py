@@ -19,7 +19,8 @@ timed region.  One step is one pass of the whole cast path over it:
 Beside the step (not part of it) the same JSON line reports the casts with
 fused statistics, the stochastic-rounding cast, the MX cast, dequant and
 statistics with blocks down the columns, the update/step-ratio monitor on
-2^30 fp32 weights and updates, a plain device copy of the cast's byte count, and one
+2^30 fp32 weights and updates (counts only, and with a flag byte per
+element), a plain device copy of the cast's byte count, and one
 delayed-scaling step of loss-scaled Llama-7B-shaped fp32 gradients (225
 tensors, 6.6G elements, fused 2^-16 unscale).  Under "configs" it times the
 three smaller workloads on their own (last-level cache flushed before each
@@ -93,7 +94,7 @@ KERNEL_SIG = {"amax": "k_amax<1>", "cast_tensor": "k_cast_pt<0, 1, false>",
               "cast_tensor+stats": "k_cast_pt<0, 1, true>", "cast_mx+stats": "k_cast_mx<0, 1, 0, true>",
               "cast_mx_cols": "k_cast_mx_col<0, 1, 0, false>", "dequant_mx_cols": "k_dequant_col<0>",
               "stats_mx_cols": "k_stats_col<0, 1>", "cast_tensor_sr": "k_cast_sr<0, 1>",
-              "swamp_watch": "k_swamp<0, false>"}
+              "swamp_watch": "k_swamp<0, false>", "swamp_watch_flags": "k_swamp<0, true>"}
 TRAFFIC_JSON = os.path.join(ROOT, "profiles", "traffic.json")
 
 
@@ -576,7 +577,22 @@ def main():
         workload="UpdateStep 2^30 fp32 w, d (w ~ N(0, 0.02), d = 1e-4 g 10^U(-3,1) per row); bf16 copies",
         below_frac=round(sc["n_below"] / max(sc["n_considered"], 1), 4),
         noop_frac=round(sc["n_noop"] / max(sc["n_considered"], 1), 4))
-    del upd, sw_ws
+    # the same with a flag byte per element written (9 B/elem)
+    flags = torch.empty(n, dtype=torch.uint8, device=dev)
+    fn = lambda: nc.nc_swamp_watch([upd.w], [upd.d], "bf16", sw_out, flags=[flags], workspace=sw_ws)
+    fn()
+    torch.cuda.synchronize()
+    for e0, e1 in ev:
+        e0.record()
+        fn()
+        e1.record()
+    torch.cuda.synchronize()
+    ms = float(np.mean([e0.elapsed_time(e1) for e0, e1 in ev]))
+    gbps = 9 * n / (ms * 1e-3) / 1e9
+    out["beside_step"]["swamp_watch_flags"] = dict(
+        ms=round(ms, 4), gbps=round(gbps, 1), frac=round(gbps / HBM_PEAK_GBPS, 4),
+        gelem_s=round(n / (ms * 1e-3) / 1e9, 2), traffic=traffic_for("swamp_watch_flags", src))
+    del upd, sw_ws, flags
     torch.cuda.empty_cache()
     if not a.no_llama:
         out["beside_step"]["llama_unscale_cast"] = llama_unscale_cast(nc, torch, workloads)
