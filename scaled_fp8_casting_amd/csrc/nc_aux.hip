@@ -224,7 +224,7 @@ k_dequant_col(const SegBatch b) {
   constexpr int VC = kDequantColCodes, R = kDequantColRows, SLOTS = kDequantColSlots;
   static_assert(SLOTS == 64, "one slot per lane of a wave, one 8-row part per wave");
   const int64_t tile = blockIdx.x;
-  const int s = seg_of(b.tile0, b.count, tile);
+  const int s = seg_of_scan(b.tile0, b.count, tile);
   const Seg& g = b.s[s];
   const int rem = tile_len<SLOTS>(b, s, tile);                 // slots in this tile
   const uint32_t slot = threadIdx.x % SLOTS, part = threadIdx.x / SLOTS;

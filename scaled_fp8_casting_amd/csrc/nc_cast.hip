@@ -94,7 +94,7 @@ k_cast_pt(const SegBatch b, const nc_scale_state* __restrict__ st,
   __shared__ double lds_st[STATS ? kRows * 6 : 1];
   __shared__ double tab[STATS ? 256 : 1];
   const int64_t tile = blockIdx.x;
-  const int s = seg_of(b.tile0, b.count, tile);
+  const int s = seg_of_scan(b.tile0, b.count, tile);
   const Seg& g = b.s[s];
   const int64_t e0 = (tile - b.tile0[s]) * TILE;
   const int rem = tile_len<TILE>(b, s, tile);
@@ -440,7 +440,7 @@ k_cast_mx(const SegBatch b, CountSlot* __restrict__ slots, double* __restrict__ 
   __shared__ double lds_st[STATS ? kRows * 6 : 1];
   __shared__ double tab[STATS ? 256 : 1];
   const int64_t tile = blockIdx.x;
-  const int s = seg_of(b.tile0, b.count, tile);
+  const int s = seg_of_scan(b.tile0, b.count, tile);
   const Seg& g = b.s[s];
   const int64_t e0 = (tile - b.tile0[s]) * TILE;
   const int rem = tile_len<TILE>(b, s, tile);      // a multiple of 32

@@ -415,7 +415,8 @@ constexpr int kRows = kThreads / 16;    // 16-lane rows per workgroup
 // ---------------------------------------------------------------------------
 // Batches.  Up to kMaxSeg tensors per launch; tensor s owns tiles
 // [tile0[s], tile0[s+1]) of the launch (one workgroup per tile) and
-// first-reduction chunks [chunk0[s], chunk0[s+1]).
+// first-reduction chunks [chunk0[s], chunk0[s+1]); the entries past `count`
+// repeat the launch's totals.
 struct Seg {
   const void* x;
   uint8_t* codes;
@@ -434,6 +435,7 @@ struct SegBatch {
   int32_t first;   // index of s[0] in the caller's arrays (counts, states, stats)
 };
 static_assert(sizeof(SegBatch) <= 4096, "a SegBatch travels as a kernel argument");
+static_assert(kMaxSeg % 8 == 0, "seg_of_scan takes the prefix entries in groups of eight");
 
 // Tensor owning entry `i` of a prefix array (tile0 or chunk0): the last s
 // with start[s] <= i, i.e. the number of s' in [1, count) with start[s'] <=
@@ -446,6 +448,28 @@ __device__ __forceinline__ int seg_of(const int32_t* start, int count, int64_t i
   const int l = threadIdx.x & 63;
   const bool hit = l + 1 < count && i >= start[l + 1];
   return __builtin_amdgcn_readfirstlane(__popcll(__ballot(hit)));
+}
+
+// The same lookup on the scalar unit: the entries start[8], start[16], ...,
+// start[56] pick a group of eight, whose entries then give the tensor, so
+// two rounds of independent scalar loads of the kernel arguments and about
+// 40 scalar instructions per wave, no vector memory access.  Relies on the
+// entries past `count` holding the launch's total (never <= i).  Which of the
+// two is faster depends on the kernel: with 2^30 elements split over eight
+// tensors, the scalar form made the per-tensor and row-block casts and the
+// column-block dequant 2-5% of HBM peak faster, the lane form kept amax and
+// the per-tensor dequant 1-2% faster, the rest measured level.
+__device__ __forceinline__ int seg_of_scan(const int32_t* start, int count, int64_t i) {
+  if (count == 1) return 0;
+  const int32_t k = (int32_t)i;
+  int c = 0;   // groups of eight whose first entry is <= k, past group 0
+#pragma unroll
+  for (int j = 1; j < kMaxSeg / 8; ++j) c += (int)((uint32_t)(start[8 * j] - k - 1) >> 31);
+  const int32_t* g = start + 8 * c;
+  int s = 8 * c;
+#pragma unroll
+  for (int j = 1; j < 8; ++j) s += (int)((uint32_t)(g[j] - k - 1) >> 31);
+  return s;
 }
 
 // Elements in tile t of tensor s: TILE, except in the tensor's last tile.
