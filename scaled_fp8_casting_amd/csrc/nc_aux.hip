@@ -310,7 +310,7 @@ k_stats(const SegBatch b, const nc_scale_state* __restrict__ st,
   __shared__ double tab[256];
   __shared__ double lds_st[kRows * 6];
   __shared__ __align__(16) uint8_t lds_sc[NSC];
-  const int64_t tile = blockIdx.x;
+  const int64_t tile = xcd_tile();
   const int s = seg_of(b.tile0, b.count, tile);
   const Seg& g = b.s[s];
   const int64_t e0 = (tile - b.tile0[s]) * TILE;
