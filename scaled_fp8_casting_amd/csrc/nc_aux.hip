@@ -161,7 +161,7 @@ template <int FMT, bool MX>
 NC_STREAM_KERNEL
 k_dequant(const SegBatch b, const nc_scale_state* __restrict__ st) {
   constexpr int64_t TILE = kDequantTile;      // 8 codes per lane per vector
-  const int64_t tile = blockIdx.x;
+  const int64_t tile = xcd_tile<32>();
   const int s = seg_of(b.tile0, b.count, tile);
   const Seg& g = b.s[s];
   const int64_t e0 = (tile - b.tile0[s]) * TILE;
@@ -227,7 +227,7 @@ NC_STREAM_KERNEL
 k_dequant_col(const SegBatch b) {
   constexpr int VC = kDequantColCodes, R = kDequantColRows, SLOTS = kDequantColSlots;
   static_assert(SLOTS == 64, "one slot per lane of a wave, one 8-row part per wave");
-  const int64_t tile = blockIdx.x;
+  const int64_t tile = xcd_tile<32>();
   const int s = seg_of_scan(b.tile0, b.count, tile);
   const Seg& g = b.s[s];
   const int rem = tile_len<SLOTS>(b, s, tile);                 // slots in this tile
@@ -310,7 +310,7 @@ k_stats(const SegBatch b, const nc_scale_state* __restrict__ st,
   __shared__ double tab[256];
   __shared__ double lds_st[kRows * 6];
   __shared__ __align__(16) uint8_t lds_sc[NSC];
-  const int64_t tile = xcd_tile();
+  const int64_t tile = xcd_tile<32>();
   const int s = seg_of(b.tile0, b.count, tile);
   const Seg& g = b.s[s];
   const int64_t e0 = (tile - b.tile0[s]) * TILE;
@@ -420,7 +420,7 @@ k_stats_col(const SegBatch b, double* __restrict__ stat_slots) {
   constexpr int Q = 8;                      // rows per batch of loads
   __shared__ double tab[256];
   __shared__ double lds_st[kRows * 6];
-  const int64_t tile = blockIdx.x;
+  const int64_t tile = xcd_tile<32>();
   const int s = seg_of(b.tile0, b.count, tile);
   const Seg& g = b.s[s];
   const ColSlot cs = col_slot<VC, R>(g, tile - b.tile0[s], tile_len<kThreads>(b, s, tile));

@@ -22,7 +22,7 @@ k_amax(const SegBatch b, CountSlot* __restrict__ slots) {
   constexpr int VEC = In<DT>::VEC;
   constexpr int64_t TILE = (int64_t)kThreads * VEC * kAmaxVecs;
   __shared__ uint32_t lds[kRows * 4];
-  const int64_t tile = xcd_tile();
+  const int64_t tile = xcd_tile<32>();
   const int s = seg_of(b.tile0, b.count, tile);
   const Seg& g = b.s[s];
   const int64_t e0 = (tile - b.tile0[s]) * TILE;
@@ -93,7 +93,7 @@ k_cast_pt(const SegBatch b, const nc_scale_state* __restrict__ st,
   __shared__ uint32_t lds[kRows * 4];
   __shared__ double lds_st[STATS ? kRows * 6 : 1];
   __shared__ double tab[STATS ? 256 : 1];
-  const int64_t tile = xcd_tile();
+  const int64_t tile = xcd_tile<256>();
   const int s = seg_of_scan(b.tile0, b.count, tile);
   const Seg& g = b.s[s];
   const int64_t e0 = (tile - b.tile0[s]) * TILE;
@@ -244,7 +244,7 @@ k_cast_sr(const SegBatch b, const nc_scale_state* __restrict__ st, const nc_loss
   constexpr int U = kCastSrVecs;
   constexpr int64_t TILE = (int64_t)kThreads * VEC * U;
   __shared__ uint32_t lds[kRows * 4];
-  const int64_t tile = blockIdx.x;
+  const int64_t tile = xcd_tile<1>();
   const int s = seg_of(b.tile0, b.count, tile);
   const Seg& g = b.s[s];
   const int64_t e0 = (tile - b.tile0[s]) * TILE;
@@ -439,7 +439,7 @@ k_cast_mx(const SegBatch b, CountSlot* __restrict__ slots, double* __restrict__ 
   __shared__ uint32_t lds[kRows * 4];
   __shared__ double lds_st[STATS ? kRows * 6 : 1];
   __shared__ double tab[STATS ? 256 : 1];
-  const int64_t tile = xcd_tile();
+  const int64_t tile = xcd_tile<256>();
   const int s = seg_of_scan(b.tile0, b.count, tile);
   const Seg& g = b.s[s];
   const int64_t e0 = (tile - b.tile0[s]) * TILE;
@@ -486,7 +486,7 @@ k_cast_mx_col(const SegBatch b, CountSlot* __restrict__ slots, double* __restric
   __shared__ uint32_t lds[kRows * 4];
   __shared__ double lds_st[STATS ? kRows * 6 : 1];
   __shared__ double tab[STATS ? 256 : 1];
-  const int64_t tile = blockIdx.x;
+  const int64_t tile = xcd_tile<1>();
   const int s = seg_of(b.tile0, b.count, tile);
   const Seg& g = b.s[s];
   const int rem = tile_len<SLOTS>(b, s, tile);                 // slots in this tile

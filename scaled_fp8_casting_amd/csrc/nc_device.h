@@ -472,19 +472,27 @@ __device__ __forceinline__ int seg_of_scan(const int32_t* start, int count, int6
   return s;
 }
 
-// The tile of this workgroup when the eight XCDs each take one contiguous
-// run of the launch's tiles.  Workgroups are handed to the XCDs in turn (g
-// mod 8), so XCD x runs g = x, x + 8, x + 16, ...; mapping its j-th
-// workgroup to tile start(x) + j, with start(x) = x q + min(x, r) for G = 8q
-// + r workgroups, is a bijection of [0, G).  Each XCD then streams one
-// region in order instead of every eighth tile of the whole launch.  On 2^30
-// elements that lifted the read-mostly kernels by 5-7 points of HBM peak
-// (amax to 88%, the statistics pass to 86%, the monitor to 89%) and the
-// per-tensor cast by one, and cost the dequants and the column-block cast
-// 2-7 points, so only the former use it.
+// The tile of this workgroup.  Workgroups are handed to the eight XCDs in
+// turn (g mod 8), so with tile = g every XCD streams every eighth tile of
+// the launch.  Here each group of 8C consecutive workgroups takes 8C
+// consecutive tiles, XCD x the C of them starting at x C: XCD x's j-th
+// workgroup of the group gets tile 8C group + x C + j.  A trailing partial
+// group keeps tile = g.  C = 1 is the plain order.  Nothing is reused
+// across tiles, so this is about how the eight XCDs' request streams meet
+// in HBM, not about L2 hits.  Measured on 2^30 elements against the plain
+// order, in points of HBM peak: C = 256 lifts the per-tensor cast by 2-3
+// and the row-block MX cast by 1-2; C = 32 lifts amax by 4-6, the
+// statistics passes and the monitor by 1-8, the column-block dequant by 1;
+// the column-block cast and stochastic rounding measured best or level in
+// the plain order.  One contiguous region per XCD (C = G / 8) helped the
+// read-only kernels as much but cost the dequants 3-4 points.
+template <uint32_t C>
 __device__ __forceinline__ int64_t xcd_tile() {
-  const uint32_t g = blockIdx.x, G = gridDim.x, x = g % 8u;
-  return (int64_t)(x * (G / 8u) + min(x, G % 8u) + g / 8u);
+  const uint32_t g = blockIdx.x, G = gridDim.x;
+  if constexpr (C == 1) return (int64_t)g;
+  constexpr uint32_t span = 8u * C;
+  if (g >= G / span * span) return (int64_t)g;
+  return (int64_t)(g / span * span + (g % 8u) * C + (g / 8u) % C);
 }
 
 // Elements in tile t of tensor s: TILE, except in the tensor's last tile.

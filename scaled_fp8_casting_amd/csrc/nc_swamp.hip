@@ -151,7 +151,7 @@ k_swamp(const SegBatch b, uint4* __restrict__ slots) {
   constexpr int U = kSwampVecs;
   constexpr int64_t TILE = kSwampTile;
   __shared__ uint32_t lds[kRows * 4];
-  const int64_t tile = xcd_tile();
+  const int64_t tile = xcd_tile<32>();
   const int s = seg_of(b.tile0, b.count, tile);
   const Seg& g = b.s[s];
   const int64_t e0 = (tile - b.tile0[s]) * TILE;
