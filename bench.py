@@ -20,12 +20,12 @@ Beside the step (not part of it) the same JSON line reports the casts with
 fused statistics, the stochastic-rounding cast, the MX cast, dequant and
 statistics with blocks down the columns, the update/step-ratio monitor on
 2^30 fp32 weights and updates (counts only, and with a flag byte per
-element), a plain device copy of the cast's byte count, and one
+element), torch's device copy of the cast's byte count, and one
 delayed-scaling step of loss-scaled Llama-7B-shaped fp32 gradients (225
 tensors, 6.6G elements, fused 2^-16 unscale).  Under "configs" it times the
 three smaller workloads on their own (last-level cache flushed before each
 rep): 65,536 fp32 elements under current scaling (microseconds, launch-bound),
-the 4096 x 4096 tanh bf16 matrix to MXFP8 under the OCP and +1 rules, and one
+the 4096 x 4096 tanh bf16 matrix to MXFP8 under the OCP, +1 and ceil rules, and one
 delayed E5M2 scaling step over 64 fp32 gradient tensors.
 
 Prints one JSON line.  `value` is elements per second through the whole step
@@ -158,28 +158,56 @@ def write_traffic(fetch_csv: str, write_csv: str):
 
 def cpu_baseline(rows: int, procs: int):
     """The oracle (tier 1, vectorised exact binary64) over the same step on
-    `rows` rows of the workload, row chunks spread over a process pool."""
+    `rows` rows of the workload, row chunks spread over a process pool; and
+    tier 0 (exact rationals, one core) on the 65,536-element current-scaling
+    workload.  The workers are started with "spawn": this process has used
+    the GPU, and a forked child would inherit its HIP state."""
     import multiprocessing as mp
     import workloads
-    bits = workloads.heavy_tailed_parallel(rows, COLS, procs=procs)
+    bits = workloads.heavy_tailed_parallel(rows, COLS, procs=procs, context="spawn")
     chunk = -(-rows // procs)
     jobs = [bits[r:r + chunk] for r in range(0, rows, chunk)]
     workers = min(procs, len(jobs))
     print(f"[bench] CPU oracle: input ready, {workers} workers", file=sys.stderr, flush=True)
     # the per-tensor scale needs the global amax first (as on the GPU); each
     # phase has a time limit, so a stuck worker cannot hold the bench
-    t0 = time.perf_counter()
-    with mp.get_context("fork").Pool(workers) as pool:
+    with mp.get_context("spawn").Pool(workers) as pool:
+        pool.map_async(_cpu_ready, range(workers)).get(timeout=120)   # start-up (imports) untimed
+        t0 = time.perf_counter()
         amaxes = pool.map_async(_cpu_amax, jobs).get(timeout=120)
         k = _scale_k(max(amaxes))
         print(f"[bench] CPU oracle: amax pass done ({time.perf_counter() - t0:.1f} s)", file=sys.stderr,
               flush=True)
         pool.map_async(_cpu_step, [(j, k) for j in jobs]).get(timeout=150)
-    dt = time.perf_counter() - t0
+        dt = time.perf_counter() - t0
     n = rows * COLS
-    return dict(value=n / dt / 1e9, unit="Gelem/s", cores=workers, kind="oracle",
+    t0_s, t0_n = _cpu_tier0_small()
+    return dict(value=n / dt / 1e9, unit="Gelem/s", cores=workers, host_cpus=os.cpu_count(), kind="oracle",
                 sample=f"{rows} rows x {COLS} of the same workload ({n} elements), whole step, "
-                       f"{workers} worker processes, {dt:.1f} s, {_cpu_model()}")
+                       f"{workers} worker processes on a host reporting {os.cpu_count()} CPUs, {dt:.1f} s, "
+                       f"{_cpu_model()}",
+                tier0_single_core=dict(workload=f"{t0_n} fp32 ~ N(0,1), current per-tensor E4M3 scaling "
+                                                f"(amax, scale, cast) in exact rationals, one core",
+                                       seconds=round(t0_s, 2), gelem_s=t0_n / t0_s / 1e9))
+
+
+def _cpu_ready(_):
+    from oracle import bulk  # noqa: F401  (the workers' imports, before the clock starts)
+    return os.getpid()
+
+
+def _cpu_tier0_small():
+    """Tier 0 (Fractions) on the 65,536-element current-scaling workload, one core."""
+    import workloads
+    from oracle import E4M3
+    from oracle import cast as t0
+    from oracle.formats import Val
+    x = workloads.per_tensor_small()
+    t = time.perf_counter()
+    vals = [Val.of(float(v)) for v in x]
+    k = t0.scale_exponent(E4M3, t0.amax(vals))
+    t0.cast_tensor(E4M3, vals, k)
+    return time.perf_counter() - t, x.size
 
 
 def mp_timeout():
@@ -299,7 +327,7 @@ def small_configs(nc, torch, workloads):
     """The three smaller workloads, timed on their own: a 65,536-element fp32
     vector under current per-tensor E4M3 scaling (amax, scale update, cast:
     launch-bound, so microseconds, not bandwidth); the 4096 x 4096 tanh bf16
-    matrix cast to MXFP8 E4M3 under the OCP and +1 rules; and one step of
+    matrix cast to MXFP8 E4M3 under the OCP, +1 and ceil rules; and one step of
     delayed per-tensor E5M2 scaling over 64 fp32 gradient tensors (2^12 to
     2^22 elements) with a 16-step window.  Their working sets fit the GPU's
     last-level cache, so a 1 GiB buffer is read before every timed rep
@@ -333,7 +361,7 @@ def small_configs(nc, torch, workloads):
     c1()
     ms, msg = both(c1)
     res["per_tensor_65536_fp32"] = dict(us=round(ms * 1e3, 1), us_graph=round(msg * 1e3, 1), elements=x.numel(),
-                                        launches=6, note="amax + scale update + cast, launch-bound")
+                                        launches=5, note="amax + scale update + cast, launch-bound")
     # 4096 x 4096 tanh(N(0, 1.5)) bf16, MXFP8 E4M3 per rule
     xb = torch.from_numpy(workloads.tanh_activations().reshape(-1).view(np.int16)).to(dev).view(torch.bfloat16)
     n = xb.numel()
@@ -341,18 +369,26 @@ def small_configs(nc, torch, workloads):
     scales = torch.empty(n // 32, dtype=torch.uint8, device=dev)
     desc, cnt = nc.tensors([xb], [codes])
     ws = nc.new_workspace(desc, cnt)
-    for rule in ("ocp", "plus1"):
+    for rule in ("ocp", "plus1", "ceil"):
+        # what the cast does to this tensor under the rule, from one untimed
+        # call with the statistics: clipped fraction, mean signed error, the
+        # error along each element's own sign, the fraction kept along itself
+        out, sts = nc.new_counts(1), nc.new_stats(1)
+        nc.nc_cast_mx([xb], [codes], [scales], [4096], "e4m3", rule, out, stats=sts, ws=ws)
+        torch.cuda.synchronize()
+        c = nc.counts_list(out)[0]
+        sm = dict(zip(nc.STAT_FIELDS, sts[0].cpu().tolist()))
+        nf = c["n_finite"]
         out = nc.new_counts(1)
         fn = lambda: nc.nc_cast_mx([xb], [codes], [scales], [4096], "e4m3", rule, out, ws=ws)
-        fn()
-        torch.cuda.synchronize()
-        clip = nc.counts_list(out)[0]["n_clip"] / n
         ms, msg = both(fn)
         nbytes = 3 * n + n // 32
         res[f"mx_tanh_4096x4096_{rule}"] = dict(
             us=round(ms * 1e3, 1), gbps=round(nbytes / (ms * 1e-3) / 1e9, 1),
             frac=round(nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4), us_graph=round(msg * 1e3, 1),
-            clip_frac=round(clip, 4))
+            clip_frac=round(c["n_clip"] / n, 5), mean_signed_error=sm["sum_e"] / nf,
+            sign_aligned_bias=sm["sum_dir_e"] / nf, kept_fraction=1.0 + sm["sum_xe"] / sm["sum_x2"],
+            rel_rms_error=(sm["sum_e2"] / sm["sum_x2"]) ** 0.5)
     # 64 fp32 tensors, delayed E5M2 scaling with a 16-step window: one batched
     # cast (counts and next amax fused) and one scale update per step
     gen = workloads.GradientSteps(steps=4)
@@ -466,8 +502,10 @@ def main():
             if ev is not None:
                 ev[i][1].record()
 
-    for _ in range(a.warmup):
-        step()
+    wev = [[[torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)]
+            for _ in names] for _ in range(a.warmup)]
+    for w in range(a.warmup):
+        step(wev[w])
     torch.cuda.synchronize()
     print(f"[bench] warmup done; timing {a.steps} steps", file=sys.stderr, flush=True)
     evs = [[[torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)]
@@ -487,6 +525,15 @@ def main():
         kernels[nm] = dict(ms=round(per[nm], 4), gbps=None if gbps is None else round(gbps, 1),
                            frac=None if gbps is None else round(gbps / HBM_PEAK_GBPS, 4),
                            gelem_s=round(n / (per[nm] * 1e-3) / 1e9, 2) if alg_bytes[nm] else None)
+    # per-step sums of the calls' event times, warm-up steps first (no extra
+    # synchronisation: the events were recorded around every call anyway)
+    def call_ms(ev_step, i):
+        return ev_step[i][0].elapsed_time(ev_step[i][1])
+    i_mx = names.index("cast_mx")
+    series = {"warmup_ms": [round(sum(call_ms(e, i) for i in range(len(names))), 4) for e in wev],
+              "timed_ms": [round(sum(call_ms(e, i) for i in range(len(names))), 4) for e in evs],
+              "cast_mx_warmup_ms": [round(call_ms(e, i_mx), 4) for e in wev],
+              "cast_mx_timed_ms": [round(call_ms(e, i_mx), 4) for e in evs]}
     dom = max((nm for nm in names if alg_bytes[nm]), key=lambda nm: per[nm])
     ach = alg_bytes[dom] / (per[dom] * 1e-3) / 1e9
     src = source_hash()
@@ -515,10 +562,12 @@ def main():
                     "pt_clip": cc["n_clip"], "pt_underflow_frac": round(cc["n_underflow"] / n, 5),
                     "mx_clip_frac": round(cm["n_clip"] / n, 5)},
         "source_hash": src,
+        "step_series": series,
     }
     # Beside the step (not part of it): the casts with their statistics fused
-    # (one pass instead of cast + separate statistics pass) and a plain
-    # device-to-device copy moving the cast's byte count (practical ceiling).
+    # (one pass instead of cast + separate statistics pass), and torch's own
+    # device copy of the cast's byte count (context only: a copy kernel that
+    # is not tuned for HBM, so it bounds nothing here).
     fused_pt, fused_mx = nc.new_stats(1), nc.new_stats(1)
     extras = {
         "cast_tensor+stats": (lambda: nc.nc_cast_tensor([x], [codes_pt], "e4m3", bufs["st"], bufs["cpt"],
@@ -539,7 +588,7 @@ def main():
     if not a.copy_probe:     # (a counter run keeps the probe's copies the only large ones)
         cp_src = torch.empty(3 * n // 2, dtype=torch.uint8, device=dev).fill_(1)
         cp_dst = torch.empty_like(cp_src)
-        extras["copy_ceiling"] = (lambda: cp_dst.copy_(cp_src), 3 * n)
+        extras["torch_copy"] = (lambda: cp_dst.copy_(cp_src), 3 * n)
     out["beside_step"] = {}
     for nm, (fn, nbytes) in extras.items():
         fn()

@@ -72,21 +72,76 @@ def _stream(stream) -> Optional[int]:
     return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
 
 
+def _need(t: Optional[torch.Tensor], name: str, dtype: torch.dtype, rows: int, width: Optional[int] = None):
+    """Raise ValueError unless t is a contiguous `dtype` tensor holding at least
+    `rows` rows of `width` elements (or `rows` elements when width is None):
+    the kernels write (or read) that many, so a smaller buffer would be
+    overrun on the GPU."""
+    if t is None:
+        return
+    if t.dtype != dtype:
+        raise ValueError(f"{name}: dtype {t.dtype}, expected {dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name}: contiguous tensor expected")
+    if width is None:
+        if t.numel() < rows:
+            raise ValueError(f"{name}: {t.numel()} elements, at least {rows} needed")
+    elif t.dim() != 2 or t.shape[1] != width or t.shape[0] < rows:
+        raise ValueError(f"{name}: shape {tuple(t.shape)}, expected ({rows}, {width}) or more rows")
+
+
 def tensors(xs: Sequence[Optional[torch.Tensor]], codes: Sequence[Optional[torch.Tensor]],
             cols: Optional[Sequence[int]] = None, scales: Optional[Sequence[torch.Tensor]] = None,
             n: Optional[Sequence[int]] = None, axis: str = "rows"):
-    """A host array of nc_tensor descriptors (contiguous device tensors)."""
+    """A host array of nc_tensor descriptors (contiguous device tensors).
+
+    Before any pointer is taken, the sizes are checked against what the
+    kernels will touch: every input has the first input's dtype (fp32 or
+    bf16), every code buffer is uint8 with exactly as many elements as its
+    input, every scale buffer uint8 with one byte per 32 elements, and the
+    per-tensor lists have one entry per tensor.  A mismatch raises
+    ValueError."""
     count = len(codes)
+    for name, lst in (("xs", xs), ("cols", cols), ("scales", scales), ("n", n)):
+        if lst is not None and len(lst) != count:
+            raise ValueError(f"{name}: {len(lst)} entries for {count} tensors")
+    if axis not in MX_AXIS:
+        raise ValueError(f"axis {axis!r}")
+    dt0 = None
+    if xs is not None and count:
+        dt0 = xs[0].dtype
+        _dtype_code(xs[0])
+    ns = []
+    for i in range(count):
+        x = xs[i] if xs is not None else None
+        c = codes[i]
+        if x is not None and x.dtype != dt0:
+            raise ValueError(f"xs[{i}]: dtype {x.dtype}, but xs[0] is {dt0} (one dtype per call)")
+        for t in (x, c):
+            if t is not None and not t.is_contiguous():
+                raise ValueError("contiguous tensors expected")
+        ni = n[i] if n is not None else (x.numel() if x is not None else c.numel())
+        if x is not None and x.numel() != ni:
+            raise ValueError(f"xs[{i}]: {x.numel()} elements, n = {ni}")
+        if c is not None:
+            if c.dtype != torch.uint8:
+                raise ValueError(f"codes[{i}]: dtype {c.dtype}, expected torch.uint8")
+            if c.numel() != ni:
+                raise ValueError(f"codes[{i}]: {c.numel()} elements for {ni} inputs")
+        if scales is not None:
+            sc = scales[i]
+            if sc.dtype != torch.uint8 or not sc.is_contiguous():
+                raise ValueError(f"scales[{i}]: contiguous torch.uint8 expected")
+            if sc.numel() != ni // 32:
+                raise ValueError(f"scales[{i}]: {sc.numel()} bytes for {ni // 32} blocks of 32")
+        ns.append(ni)
     arr = (NcTensor * max(count, 1))()
     for i in range(count):
         x = xs[i] if xs is not None else None
         c = codes[i]
-        for t in (x, c):
-            if t is not None and not t.is_contiguous():
-                raise ValueError("contiguous tensors expected")
         arr[i].x = _ptr(x) if x is not None and x.numel() else None
         arr[i].codes = _ptr(c) if c is not None and c.numel() else None
-        arr[i].n = n[i] if n is not None else (x.numel() if x is not None else c.numel())
+        arr[i].n = ns[i]
         arr[i].cols = cols[i] if cols is not None else 0
         arr[i].scales = _ptr(scales[i]) if scales is not None and scales[i].numel() else None
         arr[i].mx_axis = MX_AXIS[axis]
@@ -145,6 +200,14 @@ def new_workspace(desc, count: int, device="cuda") -> torch.Tensor:
     return torch.empty(max(workspace_bytes(desc, count), 16), dtype=torch.uint8, device=device)
 
 
+def _check_cast_outputs(count, st, out, ls, stats, ws):
+    _need(st, "st", torch.int32, count, 6)
+    _need(out, "out", torch.int64, count, 5)
+    _need(ls, "ls", torch.int32, 2)
+    _need(stats, "stats", torch.float64, count, 6)
+    _need(ws, "ws", torch.uint8, 0)
+
+
 def _ws(ws, desc, count):
     return new_workspace(desc, count) if ws is None else ws
 
@@ -153,6 +216,9 @@ def _ws(ws, desc, count):
 
 def nc_amax(xs: Sequence[torch.Tensor], out: torch.Tensor, ls: Optional[torch.Tensor] = None,
             ws: Optional[torch.Tensor] = None, stream=None):
+    _need(out, "out", torch.int64, len(xs), 5)
+    _need(ls, "ls", torch.int32, 2)
+    _need(ws, "ws", torch.uint8, 0)
     desc, count = tensors(xs, [None] * len(xs))
     dt = _dtype_code(xs[0]) if xs else NC_F32
     ws = _ws(ws, desc, count)
@@ -164,6 +230,10 @@ def nc_scale_update(pol: NcPolicy, st: torch.Tensor, in_counts: torch.Tensor,
                     hist: Optional[torch.Tensor] = None, ls: Optional[torch.Tensor] = None,
                     stream=None):
     count = st.shape[0]
+    _need(st, "st", torch.int32, count, 6)
+    _need(in_counts, "in_counts", torch.int64, count, 5)
+    _need(hist, "hist", torch.float32, count * pol.window)
+    _need(ls, "ls", torch.int32, 2)
     _check(_lib.load().nc_scale_update(ctypes.byref(pol), count, _ptr(st), _ptr(hist),
                                        _ptr(in_counts), _ptr(ls), _stream(stream)), "nc_scale_update")
 
@@ -172,6 +242,7 @@ def nc_cast_tensor(xs: Sequence[torch.Tensor], codes: Sequence[torch.Tensor], fm
                    out: torch.Tensor, ls: Optional[torch.Tensor] = None,
                    stats: Optional[torch.Tensor] = None, ws: Optional[torch.Tensor] = None,
                    stream=None):
+    _check_cast_outputs(len(codes), st, out, ls, stats, ws)
     desc, count = tensors(xs, codes)
     dt = _dtype_code(xs[0]) if xs else NC_F32
     f = FMT[fmt] if isinstance(fmt, str) else fmt
@@ -183,6 +254,7 @@ def nc_cast_tensor(xs: Sequence[torch.Tensor], codes: Sequence[torch.Tensor], fm
 def nc_cast_tensor_sr(xs: Sequence[torch.Tensor], codes: Sequence[torch.Tensor], fmt, st: torch.Tensor,
                       out: torch.Tensor, seed: int, offset: int, ls: Optional[torch.Tensor] = None,
                       ws: Optional[torch.Tensor] = None, stream=None):
+    _check_cast_outputs(len(codes), st, out, ls, None, ws)
     desc, count = tensors(xs, codes)
     dt = _dtype_code(xs[0]) if xs else NC_F32
     f = FMT[fmt] if isinstance(fmt, str) else fmt
@@ -195,6 +267,7 @@ def nc_cast_tensor_sr(xs: Sequence[torch.Tensor], codes: Sequence[torch.Tensor],
 def nc_cast_mx(xs: Sequence[torch.Tensor], codes: Sequence[torch.Tensor], scales: Sequence[torch.Tensor],
                cols: Sequence[int], fmt, rule, out: torch.Tensor, stats: Optional[torch.Tensor] = None,
                ws: Optional[torch.Tensor] = None, stream=None, axis: str = "rows"):
+    _check_cast_outputs(len(codes), None, out, None, stats, ws)
     desc, count = tensors(xs, codes, cols=cols, scales=scales, axis=axis)
     dt = _dtype_code(xs[0]) if xs else NC_BF16
     f = FMT[fmt] if isinstance(fmt, str) else fmt
@@ -207,12 +280,18 @@ def nc_cast_mx(xs: Sequence[torch.Tensor], codes: Sequence[torch.Tensor], scales
 def nc_dequant(codes: Sequence[torch.Tensor], ys: Sequence[torch.Tensor], fmt,
                st: Optional[torch.Tensor] = None, scales: Optional[Sequence[torch.Tensor]] = None,
                cols: Optional[Sequence[int]] = None, stream=None, axis: str = "rows"):
+    count = len(codes)
+    if len(ys) != count:
+        raise ValueError(f"ys: {len(ys)} entries for {count} tensors")
+    for i, y in enumerate(ys):
+        if y.dtype != torch.bfloat16 or not y.is_contiguous():
+            raise TypeError("dequant output must be contiguous bfloat16")
+        if y.numel() != codes[i].numel():
+            raise ValueError(f"ys[{i}]: {y.numel()} elements for {codes[i].numel()} codes")
+    _need(st, "st", torch.int32, count, 6)
     desc, count = tensors(None, codes, cols=cols, scales=scales, axis=axis)
     f = FMT[fmt] if isinstance(fmt, str) else fmt
     yp = (ctypes.c_void_p * max(count, 1))(*[_ptr(y) if y.numel() else None for y in ys])
-    for y in ys:
-        if y.dtype != torch.bfloat16 or not y.is_contiguous():
-            raise TypeError("dequant output must be contiguous bfloat16")
     _check(_lib.load().nc_dequant(desc, count, f, _ptr(st), yp, NC_BF16, _stream(stream)), "nc_dequant")
 
 
@@ -221,6 +300,10 @@ def nc_cast_stats(xs: Sequence[torch.Tensor], codes: Sequence[torch.Tensor], fmt
                   ls: Optional[torch.Tensor] = None,
                   scales: Optional[Sequence[torch.Tensor]] = None, cols: Optional[Sequence[int]] = None,
                   stream=None, axis: str = "rows"):
+    _need(out, "out", torch.float64, len(codes), 6)
+    _need(st, "st", torch.int32, len(codes), 6)
+    _need(ls, "ls", torch.int32, 2)
+    _need(ws, "ws", torch.uint8, 0)
     desc, count = tensors(xs, codes, cols=cols, scales=scales, axis=axis)
     dt = _dtype_code(xs[0]) if xs else NC_F32
     f = FMT[fmt] if isinstance(fmt, str) else fmt
@@ -239,7 +322,8 @@ def update_tensors(ws: Sequence[torch.Tensor], ds: Sequence[torch.Tensor],
                    flags: Optional[Sequence[Optional[torch.Tensor]]] = None):
     """A host array of nc_update_tensor descriptors (contiguous fp32 device tensors)."""
     count = len(ws)
-    arr = (NcUpdateTensor * max(count, 1))()
+    if len(ds) != count or (flags is not None and len(flags) != count):
+        raise ValueError("one update (and flag buffer) per weight tensor")
     for i in range(count):
         w, d = ws[i], ds[i]
         for t in (w, d):
@@ -247,6 +331,13 @@ def update_tensors(ws: Sequence[torch.Tensor], ds: Sequence[torch.Tensor],
                 raise TypeError("weights and updates must be contiguous float32")
         if w.numel() != d.numel():
             raise ValueError("a weight tensor and its update differ in size")
+        if flags is not None and flags[i] is not None:
+            _need(flags[i], f"flags[{i}]", torch.uint8, w.numel())
+            if flags[i].numel() != w.numel():
+                raise ValueError(f"flags[{i}]: {flags[i].numel()} bytes for {w.numel()} elements")
+    arr = (NcUpdateTensor * max(count, 1))()
+    for i in range(count):
+        w, d = ws[i], ds[i]
         arr[i].w = _ptr(w) if w.numel() else None
         arr[i].d = _ptr(d) if d.numel() else None
         f = flags[i] if flags is not None else None
@@ -280,6 +371,8 @@ def new_swamp_workspace(ws: Sequence[torch.Tensor], ds: Sequence[torch.Tensor], 
 def nc_swamp_watch(ws: Sequence[torch.Tensor], ds: Sequence[torch.Tensor], wfmt, out: torch.Tensor,
                    flags: Optional[Sequence[Optional[torch.Tensor]]] = None,
                    workspace: Optional[torch.Tensor] = None, stream=None):
+    _need(out, "out", torch.int64, len(ws), 5)
+    _need(workspace, "workspace", torch.uint8, 0)
     desc, count = update_tensors(ws, ds, flags)
     lib = _lib.load()
     if workspace is None:
@@ -290,5 +383,7 @@ def nc_swamp_watch(ws: Sequence[torch.Tensor], ds: Sequence[torch.Tensor], wfmt,
 
 
 def nc_swamp_window(pol: NcSwampPolicy, st: torch.Tensor, in_counts: torch.Tensor, stream=None):
+    _need(st, "st", torch.int32, st.shape[0], 4)
+    _need(in_counts, "in_counts", torch.int64, st.shape[0], 5)
     _check(_lib.load().nc_swamp_window(ctypes.byref(pol), st.shape[0], _ptr(st), _ptr(in_counts),
                                        _stream(stream)), "nc_swamp_window")

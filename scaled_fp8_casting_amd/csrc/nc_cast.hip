@@ -317,6 +317,12 @@ k_cast_sr(const SegBatch b, const nc_scale_state* __restrict__ st, const nc_loss
 // ---------------------------------------------------------------------------
 // MX: shared block exponent X ([Drift, "What the measurements said"]) from
 // the finite amax a of each 32-element block (a = 0 -> -127).
+// Only the floor-based rule can put a block's largest magnitude above the
+// format's largest finite value: with one bit of headroom |x| 2^-X < 2^EMAX,
+// and the rounded-up scale keeps every |x| 2^-X <= max (a value the rounding
+// cannot exceed).  The other rules need neither saturation nor clip counts.
+constexpr bool mx_rule_clips(int rule) { return rule == NC_MX_OCP; }
+
 template <int FMT, int RULE>
 __device__ __forceinline__ int mx_exponent(uint32_t a) {
   using F = Fp8<FMT>;
@@ -330,6 +336,55 @@ __device__ __forceinline__ int mx_exponent(uint32_t a) {
   if constexpr (RULE == NC_MX_CEIL) X += (frac > 0x600000u) ? 1 : 0;   // smallest X that fits
   X = min(127, max(-127, X));
   return a == 0 ? -127 : X;
+}
+
+// What a block's cast needs from its exponent X: the scale byte X + 127, the
+// scaled converts' divisor 2^X, and the clip / underflow thresholds of
+// cast_params(-X).
+struct MxBlock {
+  int sb;           // X + 127
+  float scale;      // 2^X (any positive normal value for an all-zero block)
+  uint32_t t_clip;  // as CastParams
+  uint32_t t_uf;
+};
+
+// The general form: any block amax bits a (finite).
+template <int FMT, int RULE>
+__device__ __forceinline__ MxBlock mx_block(uint32_t a) {
+  const int X = mx_exponent<FMT, RULE>(a);
+  const CastParams p = cast_params<FMT>(-X);
+  return MxBlock{X + 127, __builtin_amdgcn_ldexpf(1.0f, X), p.t_clip, p.t_uf};
+}
+
+// Block amax bits for which mx_block_fast applies: 0, or a normal fp32 with
+// exponent field 33 .. 253 (2^-94 <= a < 2^127).
+__device__ __forceinline__ bool mx_fast_ok(uint32_t a) {
+  return a == 0u || a - (33u << 23) < ((254u - 33u) << 23);
+}
+
+// The same values by exponent-field arithmetic, for a block amax bits a with
+// mx_fast_ok(a).  With E the exponent field of a (e(a) = E - 127) the rule
+// gives X + 127 = E - EMAX (+1; ceil: +[m(a) > 1.75]), between 18 and 247 here,
+// so no clamp applies; 2^X has exponent field X + 127; the clip bound
+// 1.75 * 2^(EMAX + X) has exponent field X + 127 + EMAX <= 254 and mantissa
+// 0x600000; the underflow bound 2^(X + EMIN - MB - 1) has exponent field
+// X + 127 + EMIN - MB - 1 >= 1.  All are normal fp32 patterns, equal bit for
+// bit to mx_block's.  An all-zero block (a = 0) has X = -127: its clip bound
+// is still normal, and since its elements are zeros or non-finite, an
+// underflow bound of 0 and a scale of 2^-126 give the same codes and counts.
+template <int FMT, int RULE>
+__device__ __forceinline__ MxBlock mx_block_fast(uint32_t a) {
+  using F = Fp8<FMT>;
+  int sb = (int)(a >> 23) - F::EMAX;                       // OCP: floor based
+  if constexpr (RULE == NC_MX_PLUS1) sb += 1;              // one bit of headroom
+  if constexpr (RULE == NC_MX_CEIL) sb += (a & 0x7FFFFFu) > 0x600000u ? 1 : 0;   // smallest X that fits
+  sb = a == 0u ? 0 : sb;
+  MxBlock b;
+  b.sb = sb;
+  b.scale = __uint_as_float((uint32_t)max(sb, 1) << 23);
+  b.t_clip = ((uint32_t)(sb + F::EMAX) << 23) | 0x600000u;
+  b.t_uf = (uint32_t)max(sb + F::EMIN - F::MB - 1, 0) << 23;
+  return b;
 }
 
 // Max over the lanes of one block: 4 lanes (bf16, 8 elements each) or 8
@@ -352,6 +407,7 @@ __device__ __forceinline__ void mx_tile(const Seg& g, int64_t e0, int rem, const
                                         Acc& acc, StatAcc& sa, const double* tab) {
   constexpr int VEC = In<DT>::VEC;
   constexpr int GROUP = 32 / VEC;
+  constexpr bool CLIPS = mx_rule_clips(RULE);
   uint8_t* dst = g.codes + e0;
   uint8_t* sdst = g.scales + e0 / 32;
   // the scales may be stored a row's worth at a time (4 bytes for bf16, 2
@@ -380,19 +436,25 @@ __device__ __forceinline__ void mx_tile(const Seg& g, int64_t e0, int rem, const
       for (int i = 0; i < VEC; ++i) m = max(m, finite_mag(xb[i] & kAbsMask, acc));
     }
     acc.amax = max(acc.amax, m);
-    const int X = mx_exponent<FMT, RULE>(group_max<GROUP>(m));
-    const CastParams p = cast_params<FMT>(-X);
-    // scaled converts divide by the block's scale 2^X (|X| <= 127)
-    const float scale = __builtin_amdgcn_ldexpf(1.0f, X);
+    const uint32_t gm = group_max<GROUP>(m);
+    // exponent-field arithmetic unless some block of the wave has an amax
+    // below 2^-94 or above 2^127 (wave-uniform)
+    const MxBlock blk = __ballot(!mx_fast_ok(gm)) == 0 ? mx_block_fast<FMT, RULE>(gm) : mx_block<FMT, RULE>(gm);
+    const int X = blk.sb - 127;
+    CastParams p;
+    p.K = -X;
+    p.t_clip = blk.t_clip;
+    p.t_uf = blk.t_uf;
+    // scaled converts divide by the block's scale 2^X
 #pragma unroll
-    for (int j = 0; j < VEC / 4; ++j) w[j] = scvt4<FMT, DT>(v[u], j, scale);
+    for (int j = 0; j < VEC / 4; ++j) w[j] = scvt4<FMT, DT, CLIPS>(v[u], j, blk.scale);
     if constexpr (DT == NC_BF16) {
       const u16x2 tc = splat16(p.t_clip), tu = splat16(p.t_uf);
 #pragma unroll
-      for (int j = 0; j < 4; ++j) count16(h[j], tc, tu, acc);
+      for (int j = 0; j < 4; ++j) count16<CLIPS>(h[j], tc, tu, acc);
     } else {
 #pragma unroll
-      for (int i = 0; i < VEC; ++i) count_elem(xb[i] & kAbsMask, p, acc);
+      for (int i = 0; i < VEC; ++i) count_elem<CLIPS>(xb[i] & kAbsMask, p, acc);
     }
     if (!clean) {
 #pragma unroll
@@ -408,16 +470,19 @@ __device__ __forceinline__ void mx_tile(const Seg& g, int64_t e0, int rem, const
     if (FULL || vi * VEC < rem) {
       if constexpr (DT == NC_F32) st_stream(reinterpret_cast<uint32_t*>(dst) + vi, w[0]);
       else st_stream(reinterpret_cast<u32x2*>(dst) + vi, u32x2{w[0], w[1]});
-      const uint32_t sb = (uint32_t)(X + 127);
+      const uint32_t sb = (uint32_t)blk.sb;
       if (FULL && sc_word) {
-        // a 16-lane row holds 16 / GROUP whole blocks: DPP row shifts gather
-        // their scale bytes into the row's first lane, which stores them
-        // as one word (vi is a multiple of 16 there)
+        // a 16-lane row holds 16 / GROUP whole blocks: each lane shifts its
+        // block's scale byte to that block's place in the row's word, and
+        // DPP row shifts OR them into the row's first lane, which stores the
+        // word (vi is a multiple of 16 there)
+        const uint32_t placed = sb << (8 * ((threadIdx.x / GROUP) & (16 / GROUP - 1)));
         if constexpr (GROUP == 4) {
-          const uint32_t b4 = sb | (dpp_u32<0x104>(sb) << 8) | (dpp_u32<0x108>(sb) << 16) | (dpp_u32<0x10C>(sb) << 24);
+          const uint32_t b8 = placed | dpp_u32<0x108>(placed);   // row_shl:8
+          const uint32_t b4 = b8 | dpp_u32<0x104>(b8);            // row_shl:4
           if ((threadIdx.x & 15) == 0) reinterpret_cast<uint32_t*>(sdst)[vi / 16] = b4;
         } else {
-          const uint32_t b2 = sb | (dpp_u32<0x108>(sb) << 8);
+          const uint32_t b2 = placed | dpp_u32<0x108>(placed);
           if ((threadIdx.x & 15) == 0) reinterpret_cast<uint16_t*>(sdst)[vi / 16] = (uint16_t)b2;
         }
       } else {
@@ -465,6 +530,7 @@ k_cast_mx(const SegBatch b, CountSlot* __restrict__ slots, double* __restrict__ 
   if constexpr (STATS) sa.reset();
   if (full) mx_tile<FMT, DT, RULE, STATS, true, U>(g, e0, rem, v, acc, sa, tab);
   else mx_tile<FMT, DT, RULE, STATS, false, U>(g, e0, rem, v, acc, sa, tab);
+  if constexpr (!mx_rule_clips(RULE)) acc.no_clips();
   if constexpr (STATS) write_count_stat_slots(acc, sa, slots + tile, stat_slots + tile * 6, lds, lds_st);
   else write_count_slot(acc, slots + tile, lds);
 }
@@ -575,9 +641,9 @@ k_cast_mx_col(const SegBatch b, CountSlot* __restrict__ slots, double* __restric
     for (int i = 0; i < VC; ++i) y[i] = __builtin_amdgcn_ldexpf(__uint_as_float(xb[i]), p[i].K);
     int wi = cvt_pair<FMT, false>(y[0], y[1], 0);
     if constexpr (VC == 4) wi = cvt_pair<FMT, true>(y[2], y[3], wi);
-    uint32_t w = sat4<FMT>((uint32_t)wi);
+    uint32_t w = mx_rule_clips(RULE) ? sat4<FMT>((uint32_t)wi) : (uint32_t)wi;
 #pragma unroll
-    for (int i = 0; i < VC; ++i) count_elem(xb[i] & kAbsMask, p[i], acc);
+    for (int i = 0; i < VC; ++i) count_elem<mx_rule_clips(RULE)>(xb[i] & kAbsMask, p[i], acc);
     if (!clean) {
 #pragma unroll
       for (int i = 0; i < VC; ++i)
@@ -615,6 +681,7 @@ k_cast_mx_col(const SegBatch b, CountSlot* __restrict__ slots, double* __restric
       for (int i = 0; i < VC; ++i) sd[i] = (uint8_t)(sb >> (8 * i));
     }
   }
+  if constexpr (!mx_rule_clips(RULE)) acc.no_clips();
   if constexpr (STATS) write_count_stat_slots(acc, sa, slots + tile, stat_slots + tile * 6, lds, lds_st);
   else write_count_slot(acc, slots + tile, lds);
 }

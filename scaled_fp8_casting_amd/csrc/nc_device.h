@@ -139,6 +139,9 @@ struct Acc {
     big16 = u16x2{0, 0};
     uf16 = u16x2{0, 0};
   }
+  // Without clip counting (CLIPS = false) n_big must still hold the
+  // non-finite elements, which the slot reduction subtracts from it.
+  __device__ void no_clips() { n_big = n_nf; }
   __device__ void fold() {
     n_big += (uint32_t)big16.x + big16.y;
     n_uf += (uint32_t)uf16.x + uf16.y;
@@ -165,10 +168,13 @@ __device__ __forceinline__ u16x2 gt16(u16x2 a, u16x2 b) {
             "v"(0x00010001u));
   return __builtin_bit_cast(u16x2, r);
 }
+// CLIPS = false: the caller knows no finite element exceeds the clip bound
+// (the MX rules with headroom), so only underflows are counted.
+template <bool CLIPS = true>
 __device__ __forceinline__ void count16(u16x2 h, u16x2 tc, u16x2 tu, Acc& acc) {
   const u16x2 one = {1, 1};
-  acc.big16 += gt16(h, tc);            // |x| > t_clip
-  acc.uf16 += gt16(tu, h - one);       // 1 <= |x| <= t_uf (h = 0 wraps to 0xFFFF)
+  if constexpr (CLIPS) acc.big16 += gt16(h, tc);   // |x| > t_clip
+  acc.uf16 += gt16(tu, h - one);                   // 1 <= |x| <= t_uf (h = 0 wraps to 0xFFFF)
 }
 __device__ __forceinline__ u16x2 splat16(uint32_t t) {
   const uint16_t v = (uint16_t)(t >> 16);
@@ -251,7 +257,9 @@ __device__ __forceinline__ uint32_t scvt_f32(uint32_t a, uint32_t b, float scale
 // saturated: the scaled-convert form of cvt4 (x * 2^K with scale = 2^-K).
 // j: which group of four (bf16: words 2j, 2j+1 of the vector; fp32: the
 // whole vector).
-template <int FMT, int DT>
+// SAT = false: no element can round above the largest finite value (the MX
+// rules with headroom), so the codes need no saturation.
+template <int FMT, int DT, bool SAT = true>
 __device__ __forceinline__ uint32_t scvt4(const u32x4& v, int j, float scale) {
   uint32_t w;
   if constexpr (DT == NC_BF16) {
@@ -262,7 +270,7 @@ __device__ __forceinline__ uint32_t scvt4(const u32x4& v, int j, float scale) {
     w = scvt_f32<FMT, false>(v.x, v.y, scale, 0u);
     w = scvt_f32<FMT, true>(v.z, v.w, scale, w);
   }
-  return sat4<FMT>(w);
+  return SAT ? sat4<FMT>(w) : w;
 }
 
 // Code of a non-finite element (step 4): NaN -> 0x7F, +-Inf -> +-max.
@@ -283,8 +291,9 @@ __device__ inline uint32_t fix_nonfinite4(uint32_t w, const uint32_t* xb) {
 
 // Clip and underflow counts of one element (step 5).  Clip counts include
 // every non-finite element (Acc::n_big); the flush subtracts them.
+template <bool CLIPS = true>
 __device__ __forceinline__ void count_elem(uint32_t ax, const CastParams& p, Acc& acc) {
-  acc.n_big += (ax > p.t_clip) ? 1u : 0u;
+  if constexpr (CLIPS) acc.n_big += (ax > p.t_clip) ? 1u : 0u;
   acc.n_uf += ((ax - 1u) < p.t_uf) ? 1u : 0u;
 }
 
