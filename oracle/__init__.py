@@ -38,7 +38,13 @@ Pinning: every function here is checked by ``tests/test_oracle_*.py`` against
 facts fixed independently of this code (constants printed on the pages, closed
 forms, library routines such as numpy's float16 and torch's float8 casts,
 brute force and invariants; the generator against rocRAND's Philox4x32-10
-run on the host).  One part is not fully pinned: the hysteresis
+run on the host).  The error statistics and the value a code stands for
+(``stats``, ``stats_terms``, ``represented``, ``dequant_bf16`` and their
+tier-1 forms) are pinned by hand-worked elements and sums
+(``tests/golden/stats_hand.json``, ``tests/golden/dequant_hand.json``), the
+half-step bound, and a closed form of the tanh workload's bias and kept
+fraction; ``tests/test_oracle_stats_pins.py`` also plants mistakes in them
+and checks that the pins fail.  One part is not fully pinned: the hysteresis
 semantics of the scale-update state machine beyond its stated properties
 (``oracle.policy``) -- parity unpinned there.
 """

@@ -317,25 +317,29 @@ def exact_sum(terms: np.ndarray, weights: np.ndarray = None) -> Fraction:
 STAT_KEYS = ("sum_e", "sum_abs_e", "sum_e2", "sum_dir_e", "sum_xe", "sum_x2")
 
 
+def stats_terms_f64(x: np.ndarray, xh: np.ndarray):
+    """Vectorised ``oracle.cast.stats_terms``: e = xh - x, then e, |e|, e^2,
+    sign(x) e, x e, x^2 in binary64 (exact where e is, see _exact_stats)."""
+    e = xh - x
+    return [e, np.abs(e), e * e, np.sign(x) * e, x * e, x * x]
+
+
 def _exact_stats(x: np.ndarray, xh: np.ndarray, w: np.ndarray = None):
     """Exact sums of the six terms for finite x with represented values xh,
     optionally weighted by integer multiplicities w."""
+    from .cast import stats_terms
     e = xh - x
     # exactness of e: the TwoSum error of xh + (-x) is zero and e fits 26 bits
     bb = e - xh
     err = (xh - (e - bb)) + (-x - bb)
     m, _ = np.frexp(e)
     safe = (err == 0) & (np.ldexp(m, 26) == np.floor(np.ldexp(m, 26)))
-    sgn = np.sign(x)
-    terms = [e, np.abs(e), e * e, sgn * e, x * e, x * x]
+    terms = stats_terms_f64(x, xh)
     ws = None if w is None else w[safe]
     sums = [exact_sum(t[safe], ws) for t in terms]
     for i in np.flatnonzero(~safe):                    # rare: redo exactly
-        xf = Fraction(float(x[i]))
-        ef = Fraction(float(xh[i])) - xf
-        s = (xf > 0) - (xf < 0)
         wi = 1 if w is None else int(w[i])
-        for j, tv in enumerate((ef, abs(ef), ef * ef, s * ef, xf * ef, xf * xf)):
+        for j, tv in enumerate(stats_terms(Fraction(float(x[i])), Fraction(float(xh[i])))):
             sums[j] += wi * tv
     return {k: float(s) for k, s in zip(STAT_KEYS, sums)}
 

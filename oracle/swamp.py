@@ -4,12 +4,13 @@ TEST INFRASTRUCTURE ONLY (see ``oracle/__init__.py``).
 
 What the pages fix:
 
-* [E3, "Worked solution"]: range fails at the top and bottom of a format,
-  step fails at the weight.  Besides the amax, watch the ratio of the update
-  to the step at the weight; keep a 32-bit master copy while that ratio is
-  below one at the scale in use; promote a tensor to a wider format when its
-  updates sit below its step for a whole window.  Its example: a weight of
-  1.0 with an update of 0.001 changes nothing.
+* [E3, "Worked solution"]: a format's range is what breaks at its largest
+  and smallest values, its step is what breaks at the weight.  So the
+  procedure tracks, beside the amax, how large each update is compared with
+  the grid spacing at its weight; a wide master copy is kept while updates
+  are smaller than that spacing, and a tensor moves to a wider format once
+  its updates have stayed under the spacing for a full window of steps.  The
+  page's example is a weight of 1.0 that an update of 0.001 leaves unchanged.
 * [SP, "Master weights and the optimizer step"]: late in training a weight
   of order 1 meets updates of order 1e-7; in 16 bits the add is exactly a
   no-op, in 32 bits the update lands.
