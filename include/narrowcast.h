@@ -19,8 +19,9 @@
  * Conventions shared by every call
  * --------------------------------
  * - Pointers marked (device) are HIP device memory owned by the caller; the
- *   library allocates nothing and keeps no state between calls.  Pointers
- *   marked (host) are read during the call only.
+ *   library allocates nothing and keeps no state between calls (apart from
+ *   nc_cast_tensor_static's static per-GPU scratch and its looked-up
+ *   address).  Pointers marked (host) are read during the call only.
  * - Every call is asynchronous on `stream` (a hipStream_t; NULL is the null
  *   stream): argument checks happen on the host before anything is enqueued
  *   and return an error code; results land in device memory and the caller
@@ -60,7 +61,8 @@ typedef enum {
                             multiple of 32 for NC_MX_COLS, or mixed mx_axis in one call */
   NC_E_UNSUPPORTED = 4,  /* unknown enum value */
   NC_E_HIP = 5,          /* a HIP launch failed */
-  NC_E_WORKSPACE = 6     /* workspace missing or smaller than nc_workspace_bytes() */
+  NC_E_WORKSPACE = 6,    /* workspace missing or smaller than nc_workspace_bytes() */
+  NC_E_SCRATCH = 7       /* nc_cast_tensor_static: the batch needs more than NC_STATIC_SCRATCH_BYTES */
 } nc_status;
 
 typedef enum { NC_F32 = 0, NC_BF16 = 1 } nc_dtype;
@@ -236,6 +238,26 @@ nc_status nc_scale_update(const nc_policy *policy, int32_t count, nc_scale_state
 nc_status nc_cast_tensor(const nc_tensor *t, int32_t count, nc_dtype dtype, nc_fmt fmt,
                          const nc_scale_state *st, const nc_loss_scale *ls, nc_counts *out,
                          nc_stats *stats, void *ws, size_t ws_bytes, void *stream);
+
+/* For callers that cannot allocate device memory -- code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc: the
+ * per-tensor cast of nc_cast_tensor, identical in arguments (less the
+ * workspace), checks, results and kernels, with the workspace taken from a
+ * static array of NC_STATIC_SCRATCH_BYTES bytes that the library holds on
+ * each GPU it runs on until the process ends.  It allocates nothing and calls
+ * no allocating routine.  A batch whose nc_workspace_bytes() exceeds
+ * NC_STATIC_SCRATCH_BYTES (8 MiB: one launch of up to about 2^28 elements)
+ * returns NC_E_SCRATCH before anything is enqueued.  The array's device
+ * address is looked up on the first call for the device that runs `stream`
+ * (the current device for the null stream) and kept.  Every call on a GPU
+ * shares that GPU's array, which keeps the last call's contents (nothing in
+ * it needs to start at zero): calls that overlap in time on one GPU --
+ * different streams, or threads -- race and must be serialised by the
+ * caller (one stream, or events). */
+#define NC_STATIC_SCRATCH_BYTES ((size_t)8 << 20)
+nc_status nc_cast_tensor_static(const nc_tensor *t, int32_t count, nc_dtype dtype, nc_fmt fmt,
+                                const nc_scale_state *st, const nc_loss_scale *ls, nc_counts *out,
+                                nc_stats *stats, void *stream);
 
 /* Per-tensor cast with stochastic rounding ([Drift, "The part I would rather
  * not write": unbiased at any single step]).  As nc_cast_tensor, except the

@@ -251,6 +251,20 @@ def nc_cast_tensor(xs: Sequence[torch.Tensor], codes: Sequence[torch.Tensor], fm
                                       _ptr(ws), ws.numel(), _stream(stream)), "nc_cast_tensor")
 
 
+def nc_cast_tensor_static(xs: Sequence[torch.Tensor], codes: Sequence[torch.Tensor], fmt, st: torch.Tensor,
+                          out: torch.Tensor, ls: Optional[torch.Tensor] = None,
+                          stats: Optional[torch.Tensor] = None, stream=None):
+    """nc_cast_tensor without a workspace: the library's static per-GPU
+    scratch serves instead, so nothing is allocated (for callers that cannot
+    allocate).  Calls that overlap on one GPU race on that scratch."""
+    _check_cast_outputs(len(codes), st, out, ls, stats, None)
+    desc, count = tensors(xs, codes)
+    dt = _dtype_code(xs[0]) if xs else NC_F32
+    f = FMT[fmt] if isinstance(fmt, str) else fmt
+    _check(_lib.load().nc_cast_tensor_static(desc, count, dt, f, _ptr(st), _ptr(ls), _ptr(out), _ptr(stats),
+                                             _stream(stream)), "nc_cast_tensor_static")
+
+
 def nc_cast_tensor_sr(xs: Sequence[torch.Tensor], codes: Sequence[torch.Tensor], fmt, st: torch.Tensor,
                       out: torch.Tensor, seed: int, offset: int, ls: Optional[torch.Tensor] = None,
                       ws: Optional[torch.Tensor] = None, stream=None):

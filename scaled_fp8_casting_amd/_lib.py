@@ -11,7 +11,8 @@ from ctypes import POINTER, c_char_p, c_double, c_int32, c_int64, c_size_t, c_ui
 PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(PKG, "libnarrowcast.so")
 
-NC_OK, NC_E_ARG, NC_E_ALIGN, NC_E_SHAPE, NC_E_UNSUPPORTED, NC_E_HIP, NC_E_WORKSPACE = range(7)
+NC_OK, NC_E_ARG, NC_E_ALIGN, NC_E_SHAPE, NC_E_UNSUPPORTED, NC_E_HIP, NC_E_WORKSPACE, NC_E_SCRATCH = range(8)
+NC_STATIC_SCRATCH_BYTES = 8 << 20
 NC_F32, NC_BF16 = 0, 1
 NC_E4M3, NC_E5M2 = 0, 1
 NC_MX_OCP, NC_MX_PLUS1, NC_MX_CEIL = 0, 1, 2
@@ -66,7 +67,7 @@ class NcSwampState(ctypes.Structure):
 
 NC_W_BF16, NC_W_FP16 = 0, 1
 
-EXPORTS = ("nc_amax", "nc_scale_update", "nc_cast_tensor", "nc_cast_tensor_sr", "nc_cast_mx", "nc_dequant",
+EXPORTS = ("nc_amax", "nc_scale_update", "nc_cast_tensor", "nc_cast_tensor_static", "nc_cast_tensor_sr", "nc_cast_mx", "nc_dequant",
            "nc_cast_stats", "nc_workspace_bytes", "nc_status_string", "nc_swamp_workspace_bytes",
            "nc_swamp_watch", "nc_swamp_window")
 
@@ -87,6 +88,8 @@ def load():
     lib.nc_scale_update.argtypes = [POINTER(NcPolicy), c_int32, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p]
     lib.nc_cast_tensor.argtypes = [T, c_int32, c_int32, c_int32, c_void_p, c_void_p, c_void_p, c_void_p,
                                    c_void_p, c_size_t, c_void_p]
+    lib.nc_cast_tensor_static.argtypes = [T, c_int32, c_int32, c_int32, c_void_p, c_void_p, c_void_p, c_void_p,
+                                          c_void_p]
     lib.nc_cast_tensor_sr.argtypes = [T, c_int32, c_int32, c_int32, c_void_p, c_void_p, c_uint64, c_uint64,
                                       c_void_p, c_void_p, c_size_t, c_void_p]
     lib.nc_cast_mx.argtypes = [T, c_int32, c_int32, c_int32, c_int32, c_void_p, c_void_p, c_void_p,
@@ -103,7 +106,7 @@ def load():
     lib.nc_workspace_bytes.restype = c_size_t
     lib.nc_status_string.argtypes = [c_int32]
     lib.nc_status_string.restype = c_char_p
-    for name in ("nc_amax", "nc_scale_update", "nc_cast_tensor", "nc_cast_tensor_sr", "nc_cast_mx", "nc_dequant",
+    for name in ("nc_amax", "nc_scale_update", "nc_cast_tensor", "nc_cast_tensor_static", "nc_cast_tensor_sr", "nc_cast_mx", "nc_dequant",
                  "nc_cast_stats", "nc_swamp_watch", "nc_swamp_window"):
         getattr(lib, name).restype = c_int32
     _lib = lib

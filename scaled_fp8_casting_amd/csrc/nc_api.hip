@@ -1,10 +1,19 @@
 // The C-ABI of libnarrowcast: argument checks, batching into launches of at
-// most kMaxSeg tensors, workspace layout.  No allocation, no global state.
+// most kMaxSeg tensors, workspace layout.  No allocation; the only state is
+// the per-device address of the static scratch that nc_cast_tensor_static
+// uses in place of a workspace (looked up once per device).
+#include <mutex>
 #include <string.h>
 
 #include "nc_launch.h"
 
 using namespace nc;
+
+// The workspace of nc_cast_tensor_static: one array per GPU the library runs
+// on, held until the process ends.  Host code never uses this name as an
+// address (on the host it stands for a shadow variable): the device address
+// comes from hipGetSymbolAddress, per device, in scratch_for().
+static __device__ __align__(256) uint8_t scratch[NC_STATIC_SCRATCH_BYTES];
 
 namespace {
 
@@ -138,6 +147,33 @@ size_t ws_need(const T* t, int32_t count, int64_t tile) {
   return need;
 }
 
+
+// Device address of `scratch` on the device that runs `stream` (the calling
+// thread's current device for the null stream), looked up on first use with
+// that device current and kept for the rest of the process.
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch[kMaxDevices];
+
+nc_status scratch_for(hipStream_t stream, void** out) {
+  int cur = 0;
+  if (hipGetDevice(&cur) != hipSuccess) return NC_E_HIP;
+  int dev = cur;
+  if (stream != nullptr && hipStreamGetDevice(stream, &dev) != hipSuccess) return NC_E_HIP;
+  if (dev < 0 || dev >= kMaxDevices) return NC_E_UNSUPPORTED;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch[dev] == nullptr) {
+    if (dev != cur && hipSetDevice(dev) != hipSuccess) return NC_E_HIP;
+    void* p = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (dev != cur && hipSetDevice(cur) != hipSuccess) return NC_E_HIP;
+    if (e != hipSuccess || p == nullptr) return NC_E_HIP;
+    g_scratch[dev] = p;
+  }
+  *out = g_scratch[dev];
+  return NC_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -162,6 +198,9 @@ const char* nc_status_string(nc_status s) {
     case NC_E_UNSUPPORTED: return "unsupported dtype, format, rule or estimator";
     case NC_E_HIP: return "HIP launch failed";
     case NC_E_WORKSPACE: return "workspace missing, misaligned or smaller than nc_workspace_bytes()";
+    case NC_E_SCRATCH:
+      return "the batch needs a larger workspace than the static scratch of nc_cast_tensor_static "
+             "(NC_STATIC_SCRATCH_BYTES); use nc_cast_tensor with a workspace";
   }
   return "unknown status";
 }
@@ -219,6 +258,21 @@ nc_status nc_cast_tensor(const nc_tensor* t, int32_t count, nc_dtype dtype, nc_f
     if (r == NC_OK) r = hip_status(launch_reduce(b, w, out, stats, ls, true, (hipStream_t)stream));
     return r;
   });
+}
+
+nc_status nc_cast_tensor_static(const nc_tensor* t, int32_t count, nc_dtype dtype, nc_fmt fmt,
+                                const nc_scale_state* st, const nc_loss_scale* ls, nc_counts* out,
+                                nc_stats* stats, void* stream) {
+  // every check of nc_cast_tensor except the workspace's, before anything is enqueued
+  if (!valid_dtype(dtype) || !valid_fmt(fmt)) return NC_E_UNSUPPORTED;
+  nc_status s = check_tensors(t, count, true, true, false);
+  if (s != NC_OK) return s;
+  if (count == 0) return NC_OK;
+  if (out == nullptr || st == nullptr) return NC_E_ARG;
+  if (nc_workspace_bytes(t, count) > NC_STATIC_SCRATCH_BYTES) return NC_E_SCRATCH;
+  void* ws = nullptr;
+  if ((s = scratch_for((hipStream_t)stream, &ws)) != NC_OK) return s;
+  return nc_cast_tensor(t, count, dtype, fmt, st, ls, out, stats, ws, NC_STATIC_SCRATCH_BYTES, stream);
 }
 
 nc_status nc_cast_tensor_sr(const nc_tensor* t, int32_t count, nc_dtype dtype, nc_fmt fmt,
