@@ -159,6 +159,24 @@ def counts_threshold(fmt: Fmt, x: np.ndarray, K, chunk: int = 1 << 22):
     half_sub = 2.0 ** (c["emin"] - c["mbits"] - 1)
     n_clip = n_uf = n_nf = 0
     amax = 0.0
+    if Ka.ndim == 0 and x.dtype == np.float32:
+        # One K for the whole tensor: |x| 2^K > max <=> |x| > max 2^-K, and
+        # |x| 2^K <= half_sub <=> |x| <= half_sub 2^-K, the bounds scaled
+        # exactly in binary64 and compared as binary64 scalars (the fp32
+        # magnitudes widen exactly inside the comparison).  NaN compares
+        # false; +-Inf exceeds the clip bound and is taken back out.
+        t_clip = np.float64(np.ldexp(c["M"], -int(Ka)))
+        t_uf = np.float64(np.ldexp(half_sub, -int(Ka)))
+        for i in range(0, x.size, chunk):
+            ax = np.abs(x[i:i + chunk])
+            fin = np.isfinite(ax)
+            n_inf = int(np.count_nonzero(ax == np.inf))
+            n_nf += int(ax.size - np.count_nonzero(fin))
+            n_clip += int(np.count_nonzero(ax > t_clip)) - n_inf
+            n_uf += int(np.count_nonzero((ax > 0) & (ax <= t_uf)))
+            if ax.size:
+                amax = max(amax, float(np.max(ax, where=fin, initial=np.float32(0))))
+        return dict(n_finite=x.size - n_nf, n_clip=n_clip, n_underflow=n_uf, n_nonfinite=n_nf, amax=amax)
     for i in range(0, x.size, chunk):
         xc = np.asarray(x[i:i + chunk], dtype=np.float64)
         Kc = Ka if Ka.ndim == 0 else np.asarray(Ka.ravel()[i:i + chunk], dtype=np.int64)

@@ -246,10 +246,13 @@ def test_counts_threshold_agrees_with_the_element_cast(fmt):
     x = np.concatenate([x, edges, [-e for e in edges], [np.inf, -np.inf, np.nan, 0.0, -0.0]])
     for K in (-20, -3, 0, 5, 30):
         _, clip, uf, nf = bulk.cast_f64(fmt, x, K)
-        got = bulk.counts_threshold(fmt, x, K, chunk=4097)
-        assert got["n_clip"] == int(clip.sum()) and got["n_underflow"] == int(uf.sum())
-        assert got["n_nonfinite"] == int(nf.sum()) and got["n_finite"] == x.size - int(nf.sum())
-        assert got["amax"] == float(np.max(np.abs(x[np.isfinite(x)])))
+        # binary64 holding fp32 values, and the fp32 array itself (the
+        # scalar-exponent path that compares fp32 magnitudes with the bounds)
+        for xin in (x, x.astype(np.float32)):
+            got = bulk.counts_threshold(fmt, xin, K, chunk=4097)
+            assert got["n_clip"] == int(clip.sum()) and got["n_underflow"] == int(uf.sum())
+            assert got["n_nonfinite"] == int(nf.sum()) and got["n_finite"] == x.size - int(nf.sum())
+            assert got["amax"] == float(np.max(np.abs(x[np.isfinite(x)])))
     Ks = rng.integers(-30, 30, x.size)
     _, clip, uf, nf = bulk.cast_f64(fmt, x, Ks)
     got = bulk.counts_threshold(fmt, x, Ks, chunk=1000)
