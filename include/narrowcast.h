@@ -15,6 +15,9 @@
  *   [MaxWin]  "Max-Window Scale Estimation for Near-Lossless HiF8 W8A8
  *             Quantization-Aware Training" (gist.science explainer),
  *             "Experimental Variables": amax estimators.
+ *   [SP]      "Which parts of a mixed-precision training step must stay in
+ *             single precision, and why?" (katajob.com), "Master weights and
+ *             the optimizer step": a 16-bit weight update that is a no-op.
  *
  * Conventions shared by every call
  * --------------------------------
@@ -287,18 +290,31 @@ nc_status nc_cast_mx(const nc_tensor *t, int32_t count, nc_dtype dtype, nc_fmt f
                      nc_mx_rule rule, nc_counts *out, nc_stats *stats, void *ws,
                      size_t ws_bytes, void *stream);
 
-/* Dequantise codes to bf16: y = RNE_bf16(decode(q) * 2^-k) (per-tensor, st
- * non-NULL) or RNE_bf16(decode(q) * 2^X) (MX, st == NULL, scales read), with
- * IEEE overflow to +-Inf; NaN codes give 0x7FC0.  y (host array of `count`
- * device pointers) receives n bf16 values per tensor.  out_dtype must be
- * NC_BF16.  Bytes per element: in 1 (+1/32), out 2. */
+/* Dequantise codes to bf16 ([Drift, "What the measurements said"]: the cast
+ * is judged by what it does to the tensor, which needs the value each code
+ * stands for; the formats of [MP-card, items (2) and (3)]):
+ * y = RNE_bf16(decode(q) * 2^-k) (per-tensor, st non-NULL) or
+ * RNE_bf16(decode(q) * 2^X) (MX, st == NULL, scales read), with IEEE
+ * overflow to +-Inf; NaN codes give 0x7FC0; a signed zero keeps its sign.
+ * t[i].codes and t[i].n (and, for MX, scales, cols and mx_axis) describe the
+ * codes; t[i].x is unused.  y (host array of `count` device pointers, each
+ * 16-byte aligned) receives n bf16 values per tensor; the caller owns them.
+ * out_dtype must be NC_BF16, else NC_E_UNSUPPORTED.  Needs no workspace.
+ * Bytes per element: in 1 (+1/32), out 2. */
 nc_status nc_dequant(const nc_tensor *t, int32_t count, nc_fmt fmt, const nc_scale_state *st,
                      void *const *y, nc_dtype out_dtype, void *stream);
 
 /* Error statistics as a separate pass over x and the codes already written
- * (per-tensor with st, or MX with st == NULL); accumulates into out.  ws:
- * workspace of nc_workspace_bytes(t, count) bytes.  Bytes per element: 4|2
- * + 1 (+1/32). */
+ * ([Drift, "What the measurements said"]: how much the cast changes a
+ * tensor, measured apart from which way the change points).  Over the
+ * finite elements of each tensor, with x the input after the unscale by
+ * 2^-ls->s_log2 (per-tensor only; ls nullable) and xhat = decode(q) * 2^-k
+ * (per-tensor, st non-NULL) or decode(q) * 2^X (MX, st == NULL, scales
+ * read), e = xhat - x: the sums of e, |e|, e^2, sign(x) e, x e and x^2, each
+ * formed in binary64 in a fixed order and ADDED into out[i] (nc_stats, a
+ * caller-zeroed device array).  The codes are read as they are: any codes
+ * can be measured, not only the cast's own.  ws: workspace of
+ * nc_workspace_bytes(t, count) bytes.  Bytes per element: 4|2 + 1 (+1/32). */
 nc_status nc_cast_stats(const nc_tensor *t, int32_t count, nc_dtype dtype, nc_fmt fmt,
                         const nc_scale_state *st, const nc_loss_scale *ls, nc_stats *out,
                         void *ws, size_t ws_bytes, void *stream);
@@ -321,11 +337,12 @@ size_t nc_workspace_bytes(const nc_tensor *t, int32_t count);
 const char *nc_status_string(nc_status s);
 
 /* ---- The update/step-ratio ("swamping") monitor -----------------------------
- * [E3, "Worked solution"]: step fails at the weight -- watch the ratio of the
- * update to the step at the weight; keep a wide master copy while it is
- * below one; promote a tensor to a wider format when its updates sit below
- * its step for a whole window.  [SP, "Master weights and the optimizer
- * step"]: in 16 bits such an add is exactly a no-op.
+ * [E3, "Worked solution"]: a format's step is what breaks at the weight, so
+ * each update is compared with the grid spacing at its weight; a wide
+ * master copy is kept while updates fall below that spacing, and a tensor
+ * moves to a wider format once its updates have stayed below it for a full
+ * window of steps.  [SP, "Master weights and the optimizer step"]: in 16
+ * bits such an add changes nothing at all.
  *
  * Per element, with w_F = RNE_F(w) the narrow copy (F = bf16 or fp16, IEEE
  * overflow) and step = F's grid spacing in |w_F|'s binade (the subnormal
