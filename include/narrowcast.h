@@ -319,18 +319,19 @@ nc_status nc_cast_stats(const nc_tensor *t, int32_t count, nc_dtype dtype, nc_fm
                         const nc_scale_state *st, const nc_loss_scale *ls, nc_stats *out,
                         void *ws, size_t ws_bytes, void *stream);
 
-/* Workspace bytes that nc_amax, nc_cast_tensor, nc_cast_mx and
- * nc_cast_stats need for this batch of tensors (any dtype, statistics or
- * not).  Every workgroup of a launch writes its partial counts and sums to
- * a slot of its own (64 bytes per 2048 input elements at most); a small
- * kernel sums each chunk of 1024 slots and adds the counts into the
- * caller's, and the statistics of a tensor with several chunks take a
- * second small kernel (48 bytes per chunk), every floating-point sum in a
- * fixed order -- about 3% of the input bytes of fp32, 1.6% of bf16.  The
- * workspace is caller device memory (16-byte aligned), needs no
- * initialisation, and may be reused by the next call on the same stream;
- * calls that run concurrently need workspaces of their own.  0 for an empty
- * batch. */
+/* Workspace bytes that nc_amax, nc_cast_tensor, nc_cast_tensor_sr,
+ * nc_cast_mx and nc_cast_stats need for this batch of tensors (any dtype,
+ * statistics or not).  Every workgroup of a launch writes its partial counts
+ * and sums to a slot of its own (64 bytes per 2048 input elements at most);
+ * a small kernel sums each chunk of 1024 slots and adds the counts into the
+ * caller's, and the statistics of a tensor with several chunks take a second
+ * small kernel (48 bytes per chunk), every floating-point sum in a fixed
+ * order -- about 3% of the input bytes of fp32, 1.6% of bf16.  A launch of at
+ * most 64 workgroups that forms counts only (no statistics) skips the slots:
+ * its workgroups add their counts into the caller's directly.  The workspace
+ * is caller device memory (16-byte aligned), needs no initialisation, and may
+ * be reused by the next call on the same stream; calls that run
+ * concurrently need workspaces of their own.  0 for an empty batch. */
 size_t nc_workspace_bytes(const nc_tensor *t, int32_t count);
 
 /* Static description of a status code. */

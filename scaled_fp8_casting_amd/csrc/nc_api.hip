@@ -215,9 +215,9 @@ nc_status nc_amax(const nc_tensor* t, int32_t count, nc_dtype dtype, const nc_lo
   if ((s = check_ws(t, count, ws, ws_bytes)) != NC_OK) return s;
   const int64_t tile = tile_elems(in_bytes(dtype), kAmaxVecs);
   return for_batches(t, count, tile, nullptr, [&](const SegBatch& b) {
-    const Ws w = ws_of(b, ws);
-    nc_status r = hip_status(launch_amax(b, dtype, w, Launch{b.tile0[b.count], (hipStream_t)stream}));
-    if (r == NC_OK) r = hip_status(launch_reduce(b, w, out, nullptr, ls, false, (hipStream_t)stream));
+    const Tail tl = tail_of(ws_of(b, ws), b.tile0[b.count], out, nullptr, ls, false);
+    nc_status r = hip_status(launch_amax(b, dtype, tl, Launch{b.tile0[b.count], (hipStream_t)stream}));
+    if (r == NC_OK && !tl.direct) r = hip_status(launch_reduce(b, tl, (hipStream_t)stream));
     return r;
   });
 }
@@ -252,10 +252,10 @@ nc_status nc_cast_tensor(const nc_tensor* t, int32_t count, nc_dtype dtype, nc_f
   if ((s = check_ws(t, count, ws, ws_bytes)) != NC_OK) return s;
   const int64_t tile = tile_elems(in_bytes(dtype), stats ? kCastStatsVecs : kCastVecs);
   return for_batches(t, count, tile, nullptr, [&](const SegBatch& b) {
-    const Ws w = ws_of(b, ws);
-    nc_status r = hip_status(launch_cast_pt(b, dtype, fmt, st, ls, stats != nullptr, w,
+    const Tail tl = tail_of(ws_of(b, ws), b.tile0[b.count], out, stats, ls, true);
+    nc_status r = hip_status(launch_cast_pt(b, dtype, fmt, st, ls, stats != nullptr, tl,
                                             Launch{b.tile0[b.count], (hipStream_t)stream}));
-    if (r == NC_OK) r = hip_status(launch_reduce(b, w, out, stats, ls, true, (hipStream_t)stream));
+    if (r == NC_OK && !tl.direct) r = hip_status(launch_reduce(b, tl, (hipStream_t)stream));
     return r;
   });
 }
@@ -286,10 +286,10 @@ nc_status nc_cast_tensor_sr(const nc_tensor* t, int32_t count, nc_dtype dtype, n
   if ((s = check_ws(t, count, ws, ws_bytes)) != NC_OK) return s;
   const int64_t tile = tile_elems(in_bytes(dtype), kCastSrVecs);
   return for_batches(t, count, tile, nullptr, [&](const SegBatch& b) {
-    const Ws w = ws_of(b, ws);
-    nc_status r = hip_status(launch_cast_sr(b, dtype, fmt, st, ls, seed, offset, w,
+    const Tail tl = tail_of(ws_of(b, ws), b.tile0[b.count], out, nullptr, ls, true);
+    nc_status r = hip_status(launch_cast_sr(b, dtype, fmt, st, ls, seed, offset, tl,
                                             Launch{b.tile0[b.count], (hipStream_t)stream}));
-    if (r == NC_OK) r = hip_status(launch_reduce(b, w, out, nullptr, ls, true, (hipStream_t)stream));
+    if (r == NC_OK && !tl.direct) r = hip_status(launch_reduce(b, tl, (hipStream_t)stream));
     return r;
   });
 }
@@ -305,18 +305,18 @@ nc_status nc_cast_mx(const nc_tensor* t, int32_t count, nc_dtype dtype, nc_fmt f
   if ((s = check_ws(t, count, ws, ws_bytes)) != NC_OK) return s;
   if (t[0].mx_axis == NC_MX_COLS)
     return for_batches(t, count, kThreads / col_cast_split(dtype), nullptr, [&](const SegBatch& b) {
-      const Ws w = ws_of(b, ws);
-      nc_status r = hip_status(launch_cast_mx_col(b, dtype, fmt, rule, stats != nullptr, w,
+      const Tail tl = tail_of(ws_of(b, ws), b.tile0[b.count], out, stats, nullptr, true);
+      nc_status r = hip_status(launch_cast_mx_col(b, dtype, fmt, rule, stats != nullptr, tl,
                                                   Launch{b.tile0[b.count], (hipStream_t)stream}));
-      if (r == NC_OK) r = hip_status(launch_reduce(b, w, out, stats, nullptr, true, (hipStream_t)stream));
+      if (r == NC_OK && !tl.direct) r = hip_status(launch_reduce(b, tl, (hipStream_t)stream));
       return r;
     }, col_unit(in_bytes(dtype)));
   const int64_t tile = tile_elems(in_bytes(dtype), stats ? kCastStatsVecs : kCastVecs);
   return for_batches(t, count, tile, nullptr, [&](const SegBatch& b) {
-    const Ws w = ws_of(b, ws);
-    nc_status r = hip_status(launch_cast_mx(b, dtype, fmt, rule, stats != nullptr, w,
+    const Tail tl = tail_of(ws_of(b, ws), b.tile0[b.count], out, stats, nullptr, true);
+    nc_status r = hip_status(launch_cast_mx(b, dtype, fmt, rule, stats != nullptr, tl,
                                             Launch{b.tile0[b.count], (hipStream_t)stream}));
-    if (r == NC_OK) r = hip_status(launch_reduce(b, w, out, stats, nullptr, true, (hipStream_t)stream));
+    if (r == NC_OK && !tl.direct) r = hip_status(launch_reduce(b, tl, (hipStream_t)stream));
     return r;
   });
 }
@@ -354,16 +354,16 @@ nc_status nc_cast_stats(const nc_tensor* t, int32_t count, nc_dtype dtype, nc_fm
   if ((s = check_ws(t, count, ws, ws_bytes)) != NC_OK) return s;
   if (mx && t[0].mx_axis == NC_MX_COLS)
     return for_batches(t, count, kThreads, nullptr, [&](const SegBatch& b) {
-      const Ws w = ws_of(b, ws);
-      nc_status r = hip_status(launch_stats_col(b, dtype, fmt, w, Launch{b.tile0[b.count], (hipStream_t)stream}));
-      if (r == NC_OK) r = hip_status(launch_reduce(b, w, nullptr, out, nullptr, false, (hipStream_t)stream));
+      const Tail tl = tail_of(ws_of(b, ws), b.tile0[b.count], nullptr, out, nullptr, false);
+      nc_status r = hip_status(launch_stats_col(b, dtype, fmt, tl, Launch{b.tile0[b.count], (hipStream_t)stream}));
+      if (r == NC_OK && !tl.direct) r = hip_status(launch_reduce(b, tl, (hipStream_t)stream));
       return r;
     }, stats_col_unit(in_bytes(dtype)));
   const int64_t tile = tile_elems(in_bytes(dtype), kStatsVecs);
   return for_batches(t, count, tile, nullptr, [&](const SegBatch& b) {
-    const Ws w = ws_of(b, ws);
-    nc_status r = hip_status(launch_stats(b, dtype, fmt, st, ls, w, Launch{b.tile0[b.count], (hipStream_t)stream}));
-    if (r == NC_OK) r = hip_status(launch_reduce(b, w, nullptr, out, mx ? nullptr : ls, false, (hipStream_t)stream));
+    const Tail tl = tail_of(ws_of(b, ws), b.tile0[b.count], nullptr, out, mx ? nullptr : ls, false);
+    nc_status r = hip_status(launch_stats(b, dtype, fmt, st, ls, tl, Launch{b.tile0[b.count], (hipStream_t)stream}));
+    if (r == NC_OK && !tl.direct) r = hip_status(launch_reduce(b, tl, (hipStream_t)stream));
     return r;
   });
 }

@@ -1,6 +1,6 @@
 // The scale-update state machine, dequant to bf16, the statistics pass, and
 // the fixed-order reductions of the per-workgroup slots.
-#include "nc_launch.h"
+#include "nc_reduce.h"
 
 namespace nc {
 namespace {
@@ -301,7 +301,7 @@ template <> struct CodeVec<NC_BF16> {
 template <int FMT, int DT, bool MX>
 NC_STREAM_KERNEL
 k_stats(const SegBatch b, const nc_scale_state* __restrict__ st,
-        const nc_loss_scale* __restrict__ ls, double* __restrict__ stat_slots) {
+        const nc_loss_scale* __restrict__ ls, const Tail t) {
   constexpr int VEC = In<DT>::VEC;
   constexpr int U = kStatsVecs;
   constexpr int64_t TILE = (int64_t)kThreads * VEC * U;
@@ -380,7 +380,7 @@ k_stats(const SegBatch b, const nc_scale_state* __restrict__ st,
       stats_vec<1, MX, false>(&xb, &q, tab, blk, sa);
     }
   }
-  write_stat_slot(sa, stat_slots + tile * 6, lds_st);
+  write_stat_slot(sa, t.st1 + tile * 6, lds_st);
 }
 
 // Statistics of column-block MX codes: a lane owns one col_slot (VC =
@@ -415,7 +415,7 @@ __device__ __forceinline__ void stats_col_row(u32x4 v, u32x2 w, const double* ta
 
 template <int FMT, int DT>
 NC_STREAM_KERNEL
-k_stats_col(const SegBatch b, double* __restrict__ stat_slots) {
+k_stats_col(const SegBatch b, const Tail t) {
   constexpr int VC = In<DT>::VEC, R = kStatsColRows;
   constexpr int Q = 8;                      // rows per batch of loads
   __shared__ double tab[256];
@@ -468,134 +468,34 @@ k_stats_col(const SegBatch b, double* __restrict__ stat_slots) {
       stats_col_row<DT, false>(v, ColCodes<DT>::load(qs + row * cols), tab, blk, sa);
     }
   }
-  write_stat_slot(sa, stat_slots + tile * 6, lds_st);
+  write_stat_slot(sa, t.st1 + tile * 6, lds_st);
 }
 
 // ---------------------------------------------------------------------------
-// Reductions of the per-workgroup slots.  First: workgroup c sums chunk c,
-// at most kChunk consecutive tiles of one tensor.  Its counts go straight
-// into the caller's counts with atomics (integer sums and a max: the order
-// does not matter; the tensor's first chunk also adds the tensor's size to
-// n_finite, every chunk takes off its non-finite count, modulo 2^64).  Its
-// statistics are the tensor's own when the tensor has one chunk, and are
-// added to the caller's then; otherwise they go to a chunk slot, and
-// second, workgroup s sums tensor s's chunk slots and adds the totals (a
-// second launch only when some tensor of the launch has several chunks).
-// Every floating-point sum runs in a fixed order (threads over slots in
-// index order, lanes by butterfly, waves in index order), so statistics do
-// not depend on scheduling.
-__device__ __forceinline__ int stat_shift(int j, int s_log2) {   // unscale of sum j
-  return (j == 0 || j == 1 || j == 3) ? -s_log2 : -2 * s_log2;
-}
-
+// The separate reductions of a launch's slots (when it does not reduce
+// in-kernel): one workgroup per chunk, then one wave per tensor of several
+// chunks (statistics only).  The sums are those of nc_reduce.h.
 template <bool COUNTS, bool STATS>
 __global__ void __launch_bounds__(kThreads)
-k_reduce1(const SegBatch b, const CountSlot* __restrict__ cnt1, const double* __restrict__ st1,
-          double* __restrict__ st2, nc_counts* __restrict__ out, nc_stats* __restrict__ stats,
-          const nc_loss_scale* __restrict__ ls, int clips) {
-  __shared__ uint64_t lds_c[kWaves * 4];
-  __shared__ double lds_s[kWaves * 6];
+k_reduce1(const SegBatch b, const Tail t) {
   const int64_t c = blockIdx.x;
-  const int s = seg_of(b.chunk0, b.count, c);
-  const int64_t t0 = b.tile0[s] + (c - b.chunk0[s]) * kChunk;
-  const int64_t t1 = min(t0 + (int64_t)kChunk, b.tile0[s + 1]);
-  uint32_t mx = 0;
-  uint64_t nf = 0, big = 0, uf = 0;
-  double a[6] = {0.0, 0.0, 0.0, 0.0, 0.0, 0.0};
-  for (int64_t t = t0 + threadIdx.x; t < t1; t += kThreads) {
-    if constexpr (COUNTS) {
-      const CountSlot v = cnt1[t];
-      mx = max(mx, v.amax);
-      nf += v.n_nf;
-      big += v.n_big;
-      uf += v.n_uf;
-    }
-    if constexpr (STATS) {
-#pragma unroll
-      for (int j = 0; j < 6; ++j) a[j] += st1[t * 6 + j];
-    }
-  }
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  if constexpr (COUNTS) {
-    mx = wave_max_u32(mx);
-    nf = wave_sum_u64(nf);
-    big = wave_sum_u64(big);
-    uf = wave_sum_u64(uf);
-    if (lane == 0) {
-      lds_c[wave * 4 + 0] = mx;
-      lds_c[wave * 4 + 1] = nf;
-      lds_c[wave * 4 + 2] = big;
-      lds_c[wave * 4 + 3] = uf;
-    }
-  }
-  if constexpr (STATS) {
-#pragma unroll
-    for (int j = 0; j < 6; ++j) {
-      const double v = wave_sum_f64(a[j]);
-      if (lane == 0) lds_s[wave * 6 + j] = v;
-    }
-  }
-  __syncthreads();
-  const int s_log2 = ls ? ls->s_log2 : 0;
-  if (COUNTS && threadIdx.x == 0) {
-    uint64_t m = 0, n_nf = 0, n_big = 0, n_uf = 0;
-    for (int w = 0; w < kWaves; ++w) {
-      m = max(m, lds_c[w * 4]);
-      n_nf += lds_c[w * 4 + 1];
-      n_big += lds_c[w * 4 + 2];
-      n_uf += lds_c[w * 4 + 3];
-    }
-    nc_counts* o = out + b.first + s;
-    const uint64_t fin = (c == b.chunk0[s] ? (uint64_t)b.s[s].n : 0u) - n_nf;   // modulo 2^64
-    atomicMax(&o->amax_bits, unscale_bits((uint32_t)m, s_log2));
-    if (fin) atomicAdd((unsigned long long*)&o->n_finite, (unsigned long long)fin);
-    if (n_nf) atomicAdd((unsigned long long*)&o->n_nonfinite, (unsigned long long)n_nf);
-    if (clips && n_big - n_nf) atomicAdd((unsigned long long*)&o->n_clip, (unsigned long long)(n_big - n_nf));
-    if (n_uf) atomicAdd((unsigned long long*)&o->n_underflow, (unsigned long long)n_uf);
-  }
-  if (STATS && threadIdx.x >= 64 && threadIdx.x < 70) {
-    const int j = threadIdx.x - 64;
-    double r = 0.0;
-    for (int w = 0; w < kWaves; ++w) r += lds_s[w * 6 + j];
-    if (b.chunk0[s + 1] - b.chunk0[s] == 1)
-      atomicAdd(reinterpret_cast<double*>(stats + b.first + s) + j, ldexp(r, stat_shift(j, s_log2)));
-    else
-      st2[c * 6 + j] = r;
-  }
+  reduce_chunk<COUNTS, STATS>(b, seg_of(b.chunk0, b.count, c), c, t);
 }
 
-// Statistics of the tensors with several chunks.
 __global__ void __launch_bounds__(64)
-k_reduce2(const SegBatch b, const double* __restrict__ st2, nc_stats* __restrict__ stats,
-          const nc_loss_scale* __restrict__ ls) {
+k_reduce2(const SegBatch b, const Tail t) {
   const int s = blockIdx.x;
-  const int64_t c0 = b.chunk0[s], c1 = b.chunk0[s + 1];
-  if (c1 - c0 <= 1) return;                  // done by the first reduction (or empty)
-  const int s_log2 = ls ? ls->s_log2 : 0;
-  double a[6] = {0.0, 0.0, 0.0, 0.0, 0.0, 0.0};
-  for (int64_t c = c0 + threadIdx.x; c < c1; c += 64) {
-#pragma unroll
-    for (int j = 0; j < 6; ++j) a[j] += st2[c * 6 + j];
-  }
-  double r[6];
-#pragma unroll
-  for (int j = 0; j < 6; ++j) r[j] = wave_sum_f64(a[j]);
-  if (threadIdx.x < 6) {
-    const int j = threadIdx.x;
-    double v = r[0];
-#pragma unroll
-    for (int i = 1; i < 6; ++i) v = j == i ? r[i] : v;
-    atomicAdd(reinterpret_cast<double*>(stats + b.first + s) + j, ldexp(v, stat_shift(j, s_log2)));
-  }
+  if (b.chunk0[s + 1] - b.chunk0[s] <= 1) return;    // done by the first reduction (or empty)
+  reduce_tensor_stats(b, s, t);
 }
 
 template <int FMT, int DT>
 hipError_t stats_t(const SegBatch& b, const nc_scale_state* st, const nc_loss_scale* ls,
-                   const Ws& w, const Launch& l) {
+                   const Tail& t, const Launch& l) {
   if (st)
-    hipLaunchKernelGGL((k_stats<FMT, DT, false>), dim3((uint32_t)l.grid), dim3(kThreads), 0, l.stream, b, st, ls, w.st1);
+    hipLaunchKernelGGL((k_stats<FMT, DT, false>), dim3((uint32_t)l.grid), dim3(kThreads), 0, l.stream, b, st, ls, t);
   else
-    hipLaunchKernelGGL((k_stats<FMT, DT, true>), dim3((uint32_t)l.grid), dim3(kThreads), 0, l.stream, b, st, ls, w.st1);
+    hipLaunchKernelGGL((k_stats<FMT, DT, true>), dim3((uint32_t)l.grid), dim3(kThreads), 0, l.stream, b, st, ls, t);
   return hipGetLastError();
 }
 
@@ -609,17 +509,15 @@ hipError_t dequant_t(const SegBatch& b, const nc_scale_state* st, const Launch& 
 }
 
 template <bool COUNTS, bool STATS>
-hipError_t reduce_t(const SegBatch& b, const Ws& w, nc_counts* out, nc_stats* stats,
-                    const nc_loss_scale* ls, bool clips, hipStream_t stream) {
+hipError_t reduce_t(const SegBatch& b, const Tail& t, hipStream_t stream) {
   const int64_t chunks = b.chunk0[b.count];
-  hipLaunchKernelGGL((k_reduce1<COUNTS, STATS>), dim3((uint32_t)chunks), dim3(kThreads), 0, stream, b,
-                     w.cnt1, w.st1, w.st2, out, stats, ls, clips ? 1 : 0);
+  hipLaunchKernelGGL((k_reduce1<COUNTS, STATS>), dim3((uint32_t)chunks), dim3(kThreads), 0, stream, b, t);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || !STATS) return e;
   bool several = false;
   for (int s = 0; s < b.count; ++s) several = several || b.chunk0[s + 1] - b.chunk0[s] > 1;
   if (!several) return hipSuccess;
-  hipLaunchKernelGGL(k_reduce2, dim3((uint32_t)b.count), dim3(64), 0, stream, b, w.st2, stats, ls);
+  hipLaunchKernelGGL(k_reduce2, dim3((uint32_t)b.count), dim3(64), 0, stream, b, t);
   return hipGetLastError();
 }
 
@@ -636,19 +534,18 @@ hipError_t launch_dequant(const SegBatch& b, int fmt, const nc_scale_state* st, 
 }
 
 hipError_t launch_stats(const SegBatch& b, int dtype, int fmt, const nc_scale_state* st,
-                        const nc_loss_scale* ls, const Ws& w, const Launch& l) {
+                        const nc_loss_scale* ls, const Tail& t, const Launch& l) {
   if (fmt == NC_E4M3)
-    return dtype == NC_F32 ? stats_t<NC_E4M3, NC_F32>(b, st, ls, w, l)
-                           : stats_t<NC_E4M3, NC_BF16>(b, st, ls, w, l);
-  return dtype == NC_F32 ? stats_t<NC_E5M2, NC_F32>(b, st, ls, w, l)
-                         : stats_t<NC_E5M2, NC_BF16>(b, st, ls, w, l);
+    return dtype == NC_F32 ? stats_t<NC_E4M3, NC_F32>(b, st, ls, t, l)
+                           : stats_t<NC_E4M3, NC_BF16>(b, st, ls, t, l);
+  return dtype == NC_F32 ? stats_t<NC_E5M2, NC_F32>(b, st, ls, t, l)
+                         : stats_t<NC_E5M2, NC_BF16>(b, st, ls, t, l);
 }
 
-hipError_t launch_reduce(const SegBatch& b, const Ws& w, nc_counts* out, nc_stats* stats,
-                         const nc_loss_scale* ls, bool clips, hipStream_t stream) {
-  if (out && stats) return reduce_t<true, true>(b, w, out, stats, ls, clips, stream);
-  if (out) return reduce_t<true, false>(b, w, out, stats, ls, clips, stream);
-  return reduce_t<false, true>(b, w, out, stats, ls, clips, stream);
+hipError_t launch_reduce(const SegBatch& b, const Tail& t, hipStream_t stream) {
+  if (t.out && t.stats) return reduce_t<true, true>(b, t, stream);
+  if (t.out) return reduce_t<true, false>(b, t, stream);
+  return reduce_t<false, true>(b, t, stream);
 }
 
 hipError_t launch_dequant_col(const SegBatch& b, int fmt, const Launch& l) {
@@ -660,15 +557,15 @@ hipError_t launch_dequant_col(const SegBatch& b, int fmt, const Launch& l) {
 }
 
 template <int FMT, int DT>
-hipError_t stats_col_t(const SegBatch& b, const Ws& w, const Launch& l) {
-  hipLaunchKernelGGL((k_stats_col<FMT, DT>), dim3((uint32_t)l.grid), dim3(kThreads), 0, l.stream, b, w.st1);
+hipError_t stats_col_t(const SegBatch& b, const Tail& t, const Launch& l) {
+  hipLaunchKernelGGL((k_stats_col<FMT, DT>), dim3((uint32_t)l.grid), dim3(kThreads), 0, l.stream, b, t);
   return hipGetLastError();
 }
 
-hipError_t launch_stats_col(const SegBatch& b, int dtype, int fmt, const Ws& w, const Launch& l) {
+hipError_t launch_stats_col(const SegBatch& b, int dtype, int fmt, const Tail& t, const Launch& l) {
   if (fmt == NC_E4M3)
-    return dtype == NC_F32 ? stats_col_t<NC_E4M3, NC_F32>(b, w, l) : stats_col_t<NC_E4M3, NC_BF16>(b, w, l);
-  return dtype == NC_F32 ? stats_col_t<NC_E5M2, NC_F32>(b, w, l) : stats_col_t<NC_E5M2, NC_BF16>(b, w, l);
+    return dtype == NC_F32 ? stats_col_t<NC_E4M3, NC_F32>(b, t, l) : stats_col_t<NC_E4M3, NC_BF16>(b, t, l);
+  return dtype == NC_F32 ? stats_col_t<NC_E5M2, NC_F32>(b, t, l) : stats_col_t<NC_E5M2, NC_BF16>(b, t, l);
 }
 
 }  // namespace nc

@@ -9,7 +9,7 @@
 // output.  A ragged last tile runs per element with lanes past the end fed
 // zeros (a zero is finite and never counted).  The workgroup's counts and
 // statistics go to its workspace slot.
-#include "nc_launch.h"
+#include "nc_reduce.h"
 
 namespace nc {
 namespace {
@@ -18,7 +18,7 @@ namespace {
 // Per-tensor amax pass.
 template <int DT>
 NC_STREAM_KERNEL
-k_amax(const SegBatch b, CountSlot* __restrict__ slots) {
+k_amax(const SegBatch b, const Tail t) {
   constexpr int VEC = In<DT>::VEC;
   constexpr int64_t TILE = (int64_t)kThreads * VEC * kAmaxVecs;
   __shared__ uint32_t lds[kRows * 4];
@@ -53,7 +53,7 @@ k_amax(const SegBatch b, CountSlot* __restrict__ slots) {
     for (int i = threadIdx.x; i < rem; i += kThreads)
       acc.amax = max(acc.amax, finite_mag(load_one<DT>(g.x, e0 + i) & kAbsMask, acc));
   }
-  write_count_slot(acc, slots + tile, lds);   // n_big stays 0: the amax pass reports no clips
+  flush_counts(acc, b, s, tile, t, lds);   // n_big stays 0: the amax pass reports no clips
 }
 
 // ---------------------------------------------------------------------------
@@ -85,8 +85,7 @@ __device__ __forceinline__ void cast_pt_full(const u32x4* v, const CastParams& p
 template <int FMT, int DT, bool STATS>
 NC_STREAM_KERNEL
 k_cast_pt(const SegBatch b, const nc_scale_state* __restrict__ st,
-          const nc_loss_scale* __restrict__ ls, CountSlot* __restrict__ slots,
-          double* __restrict__ stat_slots) {
+          const nc_loss_scale* __restrict__ ls, const Tail t) {
   constexpr int VEC = In<DT>::VEC;
   constexpr int U = cast_vecs<STATS>();
   constexpr int64_t TILE = (int64_t)kThreads * VEC * U;
@@ -135,8 +134,8 @@ k_cast_pt(const SegBatch b, const nc_scale_state* __restrict__ st,
       if (act) dst[i] = (uint8_t)q;
     }
   }
-  if constexpr (STATS) write_count_stat_slots(acc, sa, slots + tile, stat_slots + tile * 6, lds, lds_st);
-  else write_count_slot(acc, slots + tile, lds);
+  if constexpr (STATS) write_count_stat_slots(acc, sa, t.cnt1 + tile, t.st1 + tile * 6, lds, lds_st);
+  else flush_counts(acc, b, s, tile, t, lds);
 }
 
 // ---------------------------------------------------------------------------
@@ -239,7 +238,7 @@ __device__ __forceinline__ uint32_t sr4(const uint32_t* xb, const CastParams& p,
 template <int FMT, int DT>
 NC_STREAM_KERNEL
 k_cast_sr(const SegBatch b, const nc_scale_state* __restrict__ st, const nc_loss_scale* __restrict__ ls,
-          uint64_t seed, uint64_t offset, CountSlot* __restrict__ slots) {
+          uint64_t seed, uint64_t offset, const Tail t) {
   constexpr int VEC = In<DT>::VEC;
   constexpr int U = kCastSrVecs;
   constexpr int64_t TILE = (int64_t)kThreads * VEC * U;
@@ -311,7 +310,7 @@ k_cast_sr(const SegBatch b, const nc_scale_state* __restrict__ st, const nc_loss
       if (act) dst[i] = (uint8_t)q;
     }
   }
-  write_count_slot(acc, slots + tile, lds);
+  flush_counts(acc, b, s, tile, t, lds);
 }
 
 // ---------------------------------------------------------------------------
@@ -497,7 +496,7 @@ __device__ __forceinline__ void mx_tile(const Seg& g, int64_t e0, int rem, const
 
 template <int FMT, int DT, int RULE, bool STATS>
 NC_STREAM_KERNEL
-k_cast_mx(const SegBatch b, CountSlot* __restrict__ slots, double* __restrict__ stat_slots) {
+k_cast_mx(const SegBatch b, const Tail t) {
   constexpr int VEC = In<DT>::VEC;
   constexpr int U = cast_vecs<STATS>();
   constexpr int64_t TILE = (int64_t)kThreads * VEC * U;
@@ -531,8 +530,8 @@ k_cast_mx(const SegBatch b, CountSlot* __restrict__ slots, double* __restrict__ 
   if (full) mx_tile<FMT, DT, RULE, STATS, true, U>(g, e0, rem, v, acc, sa, tab);
   else mx_tile<FMT, DT, RULE, STATS, false, U>(g, e0, rem, v, acc, sa, tab);
   if constexpr (!mx_rule_clips(RULE)) acc.no_clips();
-  if constexpr (STATS) write_count_stat_slots(acc, sa, slots + tile, stat_slots + tile * 6, lds, lds_st);
-  else write_count_slot(acc, slots + tile, lds);
+  if constexpr (STATS) write_count_stat_slots(acc, sa, t.cnt1 + tile, t.st1 + tile * 6, lds, lds_st);
+  else flush_counts(acc, b, s, tile, t, lds);
 }
 
 // ---------------------------------------------------------------------------
@@ -545,7 +544,7 @@ k_cast_mx(const SegBatch b, CountSlot* __restrict__ slots, double* __restrict__ 
 // casts and stores its own rows.
 template <int FMT, int DT, int RULE, bool STATS>
 NC_STREAM_KERNEL
-k_cast_mx_col(const SegBatch b, CountSlot* __restrict__ slots, double* __restrict__ stat_slots) {
+k_cast_mx_col(const SegBatch b, const Tail t) {
   constexpr int VC = kColBytes / In<DT>::BYTES;    // 4 bf16 or 2 fp32 columns
   constexpr int SPLIT = col_cast_split(DT), RL = 32 / SPLIT, SLOTS = kThreads / SPLIT;
   static_assert(SPLIT == 1 || SPLIT == 2, "lanes per slot");
@@ -682,110 +681,106 @@ k_cast_mx_col(const SegBatch b, CountSlot* __restrict__ slots, double* __restric
     }
   }
   if constexpr (!mx_rule_clips(RULE)) acc.no_clips();
-  if constexpr (STATS) write_count_stat_slots(acc, sa, slots + tile, stat_slots + tile * 6, lds, lds_st);
-  else write_count_slot(acc, slots + tile, lds);
+  if constexpr (STATS) write_count_stat_slots(acc, sa, t.cnt1 + tile, t.st1 + tile * 6, lds, lds_st);
+  else flush_counts(acc, b, s, tile, t, lds);
 }
 
 template <int FMT, int DT>
 hipError_t cast_pt_t(const SegBatch& b, const nc_scale_state* st, const nc_loss_scale* ls, bool stats,
-                     const Ws& w, const Launch& l) {
+                     const Tail& t, const Launch& l) {
   if (stats)
-    hipLaunchKernelGGL((k_cast_pt<FMT, DT, true>), dim3((uint32_t)l.grid), dim3(kThreads), 0, l.stream, b, st, ls,
-                       w.cnt1, w.st1);
+    hipLaunchKernelGGL((k_cast_pt<FMT, DT, true>), dim3((uint32_t)l.grid), dim3(kThreads), 0, l.stream, b, st, ls, t);
   else
-    hipLaunchKernelGGL((k_cast_pt<FMT, DT, false>), dim3((uint32_t)l.grid), dim3(kThreads), 0, l.stream, b, st, ls,
-                       w.cnt1, w.st1);
+    hipLaunchKernelGGL((k_cast_pt<FMT, DT, false>), dim3((uint32_t)l.grid), dim3(kThreads), 0, l.stream, b, st, ls, t);
   return hipGetLastError();
 }
 
 template <int FMT, int DT, int RULE>
-hipError_t cast_mx_r(const SegBatch& b, bool stats, const Ws& w, const Launch& l) {
+hipError_t cast_mx_r(const SegBatch& b, bool stats, const Tail& t, const Launch& l) {
   if (stats)
-    hipLaunchKernelGGL((k_cast_mx<FMT, DT, RULE, true>), dim3((uint32_t)l.grid), dim3(kThreads), 0, l.stream, b,
-                       w.cnt1, w.st1);
+    hipLaunchKernelGGL((k_cast_mx<FMT, DT, RULE, true>), dim3((uint32_t)l.grid), dim3(kThreads), 0, l.stream, b, t);
   else
-    hipLaunchKernelGGL((k_cast_mx<FMT, DT, RULE, false>), dim3((uint32_t)l.grid), dim3(kThreads), 0, l.stream, b,
-                       w.cnt1, w.st1);
+    hipLaunchKernelGGL((k_cast_mx<FMT, DT, RULE, false>), dim3((uint32_t)l.grid), dim3(kThreads), 0, l.stream, b, t);
   return hipGetLastError();
 }
 
 template <int FMT, int DT>
-hipError_t cast_mx_t(const SegBatch& b, int rule, bool stats, const Ws& w, const Launch& l) {
-  if (rule == NC_MX_OCP) return cast_mx_r<FMT, DT, NC_MX_OCP>(b, stats, w, l);
-  if (rule == NC_MX_PLUS1) return cast_mx_r<FMT, DT, NC_MX_PLUS1>(b, stats, w, l);
-  return cast_mx_r<FMT, DT, NC_MX_CEIL>(b, stats, w, l);
+hipError_t cast_mx_t(const SegBatch& b, int rule, bool stats, const Tail& t, const Launch& l) {
+  if (rule == NC_MX_OCP) return cast_mx_r<FMT, DT, NC_MX_OCP>(b, stats, t, l);
+  if (rule == NC_MX_PLUS1) return cast_mx_r<FMT, DT, NC_MX_PLUS1>(b, stats, t, l);
+  return cast_mx_r<FMT, DT, NC_MX_CEIL>(b, stats, t, l);
 }
 
 template <int FMT, int DT>
 hipError_t cast_sr_t(const SegBatch& b, const nc_scale_state* st, const nc_loss_scale* ls, uint64_t seed,
-                     uint64_t offset, const Ws& w, const Launch& l) {
+                     uint64_t offset, const Tail& t, const Launch& l) {
   hipLaunchKernelGGL((k_cast_sr<FMT, DT>), dim3((uint32_t)l.grid), dim3(kThreads), 0, l.stream, b, st, ls, seed,
-                     offset, w.cnt1);
+                     offset, t);
   return hipGetLastError();
 }
 
 template <int FMT, int DT, int RULE>
-hipError_t cast_mx_col_r(const SegBatch& b, bool stats, const Ws& w, const Launch& l) {
+hipError_t cast_mx_col_r(const SegBatch& b, bool stats, const Tail& t, const Launch& l) {
   if (stats)
     hipLaunchKernelGGL((k_cast_mx_col<FMT, DT, RULE, true>), dim3((uint32_t)l.grid), dim3(kThreads), 0, l.stream,
-                       b, w.cnt1, w.st1);
+                       b, t);
   else
     hipLaunchKernelGGL((k_cast_mx_col<FMT, DT, RULE, false>), dim3((uint32_t)l.grid), dim3(kThreads), 0, l.stream,
-                       b, w.cnt1, w.st1);
+                       b, t);
   return hipGetLastError();
 }
 
 template <int FMT, int DT>
-hipError_t cast_mx_col_t(const SegBatch& b, int rule, bool stats, const Ws& w, const Launch& l) {
-  if (rule == NC_MX_OCP) return cast_mx_col_r<FMT, DT, NC_MX_OCP>(b, stats, w, l);
-  if (rule == NC_MX_PLUS1) return cast_mx_col_r<FMT, DT, NC_MX_PLUS1>(b, stats, w, l);
-  return cast_mx_col_r<FMT, DT, NC_MX_CEIL>(b, stats, w, l);
+hipError_t cast_mx_col_t(const SegBatch& b, int rule, bool stats, const Tail& t, const Launch& l) {
+  if (rule == NC_MX_OCP) return cast_mx_col_r<FMT, DT, NC_MX_OCP>(b, stats, t, l);
+  if (rule == NC_MX_PLUS1) return cast_mx_col_r<FMT, DT, NC_MX_PLUS1>(b, stats, t, l);
+  return cast_mx_col_r<FMT, DT, NC_MX_CEIL>(b, stats, t, l);
 }
 
 }  // namespace
 
-hipError_t launch_amax(const SegBatch& b, int dtype, const Ws& w, const Launch& l) {
+hipError_t launch_amax(const SegBatch& b, int dtype, const Tail& t, const Launch& l) {
   if (dtype == NC_F32)
-    hipLaunchKernelGGL((k_amax<NC_F32>), dim3((uint32_t)l.grid), dim3(kThreads), 0, l.stream, b, w.cnt1);
+    hipLaunchKernelGGL((k_amax<NC_F32>), dim3((uint32_t)l.grid), dim3(kThreads), 0, l.stream, b, t);
   else
-    hipLaunchKernelGGL((k_amax<NC_BF16>), dim3((uint32_t)l.grid), dim3(kThreads), 0, l.stream, b, w.cnt1);
+    hipLaunchKernelGGL((k_amax<NC_BF16>), dim3((uint32_t)l.grid), dim3(kThreads), 0, l.stream, b, t);
   return hipGetLastError();
 }
 
 hipError_t launch_cast_pt(const SegBatch& b, int dtype, int fmt, const nc_scale_state* st,
-                          const nc_loss_scale* ls, bool stats, const Ws& w, const Launch& l) {
+                          const nc_loss_scale* ls, bool stats, const Tail& t, const Launch& l) {
   if (fmt == NC_E4M3)
-    return dtype == NC_F32 ? cast_pt_t<NC_E4M3, NC_F32>(b, st, ls, stats, w, l)
-                           : cast_pt_t<NC_E4M3, NC_BF16>(b, st, ls, stats, w, l);
-  return dtype == NC_F32 ? cast_pt_t<NC_E5M2, NC_F32>(b, st, ls, stats, w, l)
-                         : cast_pt_t<NC_E5M2, NC_BF16>(b, st, ls, stats, w, l);
+    return dtype == NC_F32 ? cast_pt_t<NC_E4M3, NC_F32>(b, st, ls, stats, t, l)
+                           : cast_pt_t<NC_E4M3, NC_BF16>(b, st, ls, stats, t, l);
+  return dtype == NC_F32 ? cast_pt_t<NC_E5M2, NC_F32>(b, st, ls, stats, t, l)
+                         : cast_pt_t<NC_E5M2, NC_BF16>(b, st, ls, stats, t, l);
 }
 
-hipError_t launch_cast_mx(const SegBatch& b, int dtype, int fmt, int rule, bool stats, const Ws& w,
+hipError_t launch_cast_mx(const SegBatch& b, int dtype, int fmt, int rule, bool stats, const Tail& t,
                           const Launch& l) {
   if (fmt == NC_E4M3)
-    return dtype == NC_F32 ? cast_mx_t<NC_E4M3, NC_F32>(b, rule, stats, w, l)
-                           : cast_mx_t<NC_E4M3, NC_BF16>(b, rule, stats, w, l);
-  return dtype == NC_F32 ? cast_mx_t<NC_E5M2, NC_F32>(b, rule, stats, w, l)
-                         : cast_mx_t<NC_E5M2, NC_BF16>(b, rule, stats, w, l);
+    return dtype == NC_F32 ? cast_mx_t<NC_E4M3, NC_F32>(b, rule, stats, t, l)
+                           : cast_mx_t<NC_E4M3, NC_BF16>(b, rule, stats, t, l);
+  return dtype == NC_F32 ? cast_mx_t<NC_E5M2, NC_F32>(b, rule, stats, t, l)
+                         : cast_mx_t<NC_E5M2, NC_BF16>(b, rule, stats, t, l);
 }
 
-hipError_t launch_cast_mx_col(const SegBatch& b, int dtype, int fmt, int rule, bool stats, const Ws& w,
+hipError_t launch_cast_mx_col(const SegBatch& b, int dtype, int fmt, int rule, bool stats, const Tail& t,
                               const Launch& l) {
   if (fmt == NC_E4M3)
-    return dtype == NC_F32 ? cast_mx_col_t<NC_E4M3, NC_F32>(b, rule, stats, w, l)
-                           : cast_mx_col_t<NC_E4M3, NC_BF16>(b, rule, stats, w, l);
-  return dtype == NC_F32 ? cast_mx_col_t<NC_E5M2, NC_F32>(b, rule, stats, w, l)
-                         : cast_mx_col_t<NC_E5M2, NC_BF16>(b, rule, stats, w, l);
+    return dtype == NC_F32 ? cast_mx_col_t<NC_E4M3, NC_F32>(b, rule, stats, t, l)
+                           : cast_mx_col_t<NC_E4M3, NC_BF16>(b, rule, stats, t, l);
+  return dtype == NC_F32 ? cast_mx_col_t<NC_E5M2, NC_F32>(b, rule, stats, t, l)
+                         : cast_mx_col_t<NC_E5M2, NC_BF16>(b, rule, stats, t, l);
 }
 
 hipError_t launch_cast_sr(const SegBatch& b, int dtype, int fmt, const nc_scale_state* st,
-                          const nc_loss_scale* ls, uint64_t seed, uint64_t offset, const Ws& w, const Launch& l) {
+                          const nc_loss_scale* ls, uint64_t seed, uint64_t offset, const Tail& t, const Launch& l) {
   if (fmt == NC_E4M3)
-    return dtype == NC_F32 ? cast_sr_t<NC_E4M3, NC_F32>(b, st, ls, seed, offset, w, l)
-                           : cast_sr_t<NC_E4M3, NC_BF16>(b, st, ls, seed, offset, w, l);
-  return dtype == NC_F32 ? cast_sr_t<NC_E5M2, NC_F32>(b, st, ls, seed, offset, w, l)
-                         : cast_sr_t<NC_E5M2, NC_BF16>(b, st, ls, seed, offset, w, l);
+    return dtype == NC_F32 ? cast_sr_t<NC_E4M3, NC_F32>(b, st, ls, seed, offset, t, l)
+                           : cast_sr_t<NC_E4M3, NC_BF16>(b, st, ls, seed, offset, t, l);
+  return dtype == NC_F32 ? cast_sr_t<NC_E5M2, NC_F32>(b, st, ls, seed, offset, t, l)
+                         : cast_sr_t<NC_E5M2, NC_BF16>(b, st, ls, seed, offset, t, l);
 }
 
 }  // namespace nc

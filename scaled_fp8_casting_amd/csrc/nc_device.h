@@ -567,10 +567,10 @@ __device__ __forceinline__ uint64_t wave_sum_u64(uint64_t v) {
   return v;
 }
 
-// The workgroup's totals -> its slot: DPP row reductions, one LDS entry per
-// row, thread 0 over the rows.  Called by all threads (full EXEC); lds holds
-// kRows * 4 words.
-__device__ inline void write_count_slot(Acc acc, CountSlot* slot, uint32_t* lds) {
+// The workgroup's totals, valid in thread 0: DPP row reductions, one LDS
+// entry per row, thread 0 over the rows.  Called by all threads (full EXEC);
+// lds holds kRows * 4 words.
+__device__ inline CountSlot workgroup_counts(Acc acc, uint32_t* lds) {
   acc.fold();
   const uint32_t m = row_max_u32(acc.amax);
   const uint32_t nf = row_sum_u32(acc.n_nf), big = row_sum_u32(acc.n_big), uf = row_sum_u32(acc.n_uf);
@@ -582,16 +582,16 @@ __device__ inline void write_count_slot(Acc acc, CountSlot* slot, uint32_t* lds)
     lds[r * 4 + 3] = uf;
   }
   __syncthreads();
+  CountSlot c{0u, 0u, 0u, 0u};
   if (threadIdx.x == 0) {
-    CountSlot c{0u, 0u, 0u, 0u};
     for (int r = 0; r < kRows; ++r) {
       c.amax = max(c.amax, lds[r * 4 + 0]);
       c.n_nf += lds[r * 4 + 1];
       c.n_big += lds[r * 4 + 2];
       c.n_uf += lds[r * 4 + 3];
     }
-    *slot = c;
   }
+  return c;
 }
 
 // ---------------------------------------------------------------------------

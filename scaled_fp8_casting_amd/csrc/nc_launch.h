@@ -80,32 +80,59 @@ inline Ws ws_layout(void* base, int64_t tiles, int64_t chunks) {
   return w;
 }
 
+// What a reducing kernel does with its workgroups' partial results, and
+// where the totals go (a kernel argument).  Normally each workgroup writes a
+// slot and the separate reduction kernels follow the launch.  direct: a
+// launch of at most kDirectMaxTiles workgroups that forms counts only has
+// each workgroup add its counts straight into the caller's (integer sums and
+// a max: the order does not matter), so no slot and no second launch.
+// Statistics (binary64 sums in a fixed order) always go through the slots.
+struct Tail {
+  CountSlot* cnt1;          // per-workgroup counts
+  double* st1;              // per-workgroup statistics
+  double* st2;              // per-chunk statistics of tensors of several chunks
+  nc_counts* out;           // the caller's counts (null: none)
+  nc_stats* stats;          // the caller's statistics (null: none)
+  const nc_loss_scale* ls;  // unscale of the amax and of the statistics (nullable)
+  int32_t clips;            // the counts report clips (the amax pass reports none)
+  int32_t direct;
+};
+
+// The largest launch whose workgroups add their counts directly.  Measured
+// on MI355X: same-address atomics serialise, so the direct form pays only
+// while few workgroups share the caller's counts (a 65,536-element fp32
+// cast: 32 workgroups).
+constexpr int64_t kDirectMaxTiles = 64;
+
+inline Tail tail_of(const Ws& w, int64_t tiles, nc_counts* out, nc_stats* stats, const nc_loss_scale* ls,
+                    bool clips) {
+  return Tail{w.cnt1, w.st1, w.st2, out, stats, ls, clips ? 1 : 0,
+              (stats == nullptr && out != nullptr && tiles <= kDirectMaxTiles) ? 1 : 0};
+}
+
 struct Launch {
   int64_t grid;        // workgroups (one per tile)
   hipStream_t stream;
 };
 
-hipError_t launch_amax(const SegBatch& b, int dtype, const Ws& w, const Launch& l);
+hipError_t launch_amax(const SegBatch& b, int dtype, const Tail& t, const Launch& l);
 hipError_t launch_cast_pt(const SegBatch& b, int dtype, int fmt, const nc_scale_state* st,
-                          const nc_loss_scale* ls, bool stats, const Ws& w, const Launch& l);
-hipError_t launch_cast_mx(const SegBatch& b, int dtype, int fmt, int rule, bool stats, const Ws& w,
+                          const nc_loss_scale* ls, bool stats, const Tail& t, const Launch& l);
+hipError_t launch_cast_mx(const SegBatch& b, int dtype, int fmt, int rule, bool stats, const Tail& t,
                           const Launch& l);
 hipError_t launch_cast_sr(const SegBatch& b, int dtype, int fmt, const nc_scale_state* st,
-                          const nc_loss_scale* ls, uint64_t seed, uint64_t offset, const Ws& w, const Launch& l);
+                          const nc_loss_scale* ls, uint64_t seed, uint64_t offset, const Tail& t, const Launch& l);
 hipError_t launch_stats(const SegBatch& b, int dtype, int fmt, const nc_scale_state* st,
-                        const nc_loss_scale* ls, const Ws& w, const Launch& l);
+                        const nc_loss_scale* ls, const Tail& t, const Launch& l);
 // Column-block MX forms of the MX cast, dequant and statistics pass; the
 // batch's tiles are 256 col_slots.
-hipError_t launch_cast_mx_col(const SegBatch& b, int dtype, int fmt, int rule, bool stats, const Ws& w,
+hipError_t launch_cast_mx_col(const SegBatch& b, int dtype, int fmt, int rule, bool stats, const Tail& t,
                               const Launch& l);
 hipError_t launch_dequant_col(const SegBatch& b, int fmt, const Launch& l);
-hipError_t launch_stats_col(const SegBatch& b, int dtype, int fmt, const Ws& w, const Launch& l);
-// The two reductions of a launch's slots into the caller's counts (nullable)
-// and statistics (nullable).  ls: unscale of the amax and of the statistics
-// (nullable; the MX calls pass none).  clips: the counts report clips (the
-// amax pass reports none).
-hipError_t launch_reduce(const SegBatch& b, const Ws& w, nc_counts* out, nc_stats* stats,
-                         const nc_loss_scale* ls, bool clips, hipStream_t stream);
+hipError_t launch_stats_col(const SegBatch& b, int dtype, int fmt, const Tail& t, const Launch& l);
+// The separate reductions of a launch's slots into t.out (nullable) and
+// t.stats (nullable), for launches that do not reduce in-kernel.
+hipError_t launch_reduce(const SegBatch& b, const Tail& t, hipStream_t stream);
 hipError_t launch_dequant(const SegBatch& b, int fmt, const nc_scale_state* st, const Launch& l);
 // The monitor's main kernel, its slot reduction into out, and the
 // promotion window.

@@ -448,3 +448,40 @@ def test_mx_column_scales_at_any_alignment_and_no_writes_past_the_end(dtype):
         b = host_u8(big)
         assert np.array_equal(b[off:off + n // 32], wsc), off
         assert np.all(b[:off] == 0xA5) and np.all(b[off + n // 32:] == 0xA5), off
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_direct_counts_at_the_launch_threshold(dtype):
+    """Launches of at most 64 workgroups that form counts only add each
+    workgroup's counts straight into the caller's; larger ones, and every
+    call with statistics, go through the slots and the reduction kernels.
+    At 64 tiles (direct) and 65 (slots), one tensor and several: amax and
+    counts against the oracle, and equal to the slot path's (the same call
+    with statistics), for the per-tensor cast and the amax pass."""
+    per = 2048 if dtype == "f32" else 4096                  # elements per cast tile
+    rng = np.random.default_rng(31)
+    for sizes in ([64 * per], [64 * per + 1], [per * 20, per * 40 + 3, 100], [per * 30, per * 35]):
+        xs = [(rng.standard_normal(m) * 10.0 ** rng.uniform(-3, 3)).astype(np.float32) for m in sizes]
+        for x in xs:
+            x[rng.integers(0, x.size, 3)] = np.array([np.inf, -np.inf, np.nan], np.float32)
+        if dtype == "bf16":
+            bits = [workloads.to_bf16_bits(x.astype(np.float64)) for x in xs]
+            xd = [dev_bf16(b) for b in bits]
+            x64 = [bulk.bf16_bits_to_f64(b) for b in bits]
+        else:
+            xd = [dev_f32(x) for x in xs]
+            x64 = [x.astype(np.float64) for x in xs]
+        ks = [int(v) for v in rng.integers(-4, 12, len(sizes))]
+        codes = [codes_like(m) for m in sizes]
+        plain, with_stats, am = nc.new_counts(len(sizes)), nc.new_counts(len(sizes)), nc.new_counts(len(sizes))
+        nc.nc_cast_tensor(xd, codes, "e4m3", state_with_k(ks), plain)
+        nc.nc_cast_tensor(xd, codes, "e4m3", state_with_k(ks), with_stats, stats=nc.new_stats(len(sizes)))
+        nc.nc_amax(xd, am)
+        torch.cuda.synchronize()
+        assert torch.equal(plain, with_stats), sizes
+        got, got_am = nc.counts_list(plain), nc.counts_list(am)
+        for i, x in enumerate(x64):
+            want = bulk.cast_tensor_f64(E4M3, x, ks[i])[1]
+            assert_counts(got[i], want)
+            assert got_am[i]["amax"] == want["amax"] and got_am[i]["n_nonfinite"] == want["n_nonfinite"], (sizes, i)
+            assert got_am[i]["n_finite"] == want["n_finite"] and got_am[i]["n_clip"] == 0, (sizes, i)
