@@ -235,6 +235,107 @@ __device__ __forceinline__ uint32_t sr4(const uint32_t* xb, const CastParams& p,
   return (uint32_t)w | sgn;
 }
 
+// gfx950's stochastic-rounding scaled converts (v_cvt_scalef32_sr_fp8_f32 /
+// _bf8_f32): x / scale rounded to the format with a 32-bit random operand
+// per element.  Given ~u they round up exactly when u < ceil(t 2^32), the
+// rule above: a probe matched it bit for bit on 2^20 cases (values on and
+// between grid points in the normal and subnormal ranges and far below
+// them, random and extreme operands, both formats, scales 2^-20 .. 2^20),
+// and the parity tests match the oracle on every bf16 pattern at scale
+// exponents from 127 down to -127 (the range this path takes) and on fp32
+// patterns of every exponent field at 127.  (The bf16-input forms differ from the
+// rule for values far below the subnormal grid, so bf16 inputs are widened
+// to fp32 first.)  Past the largest finite value they give the overflow
+// code, which sat4 saturates.  Four elements (fp32 patterns) -> four codes,
+// byte i = element i.
+template <int FMT>
+__device__ __forceinline__ uint32_t sr_cvt4(const uint32_t* xb, const uint32_t (&r)[4], float scale) {
+  int w = 0;
+  if constexpr (FMT == NC_E4M3) {
+    w = __builtin_amdgcn_cvt_scalef32_sr_fp8_f32(w, __uint_as_float(xb[0]), ~r[0], scale, 0);
+    w = __builtin_amdgcn_cvt_scalef32_sr_fp8_f32(w, __uint_as_float(xb[1]), ~r[1], scale, 1);
+    w = __builtin_amdgcn_cvt_scalef32_sr_fp8_f32(w, __uint_as_float(xb[2]), ~r[2], scale, 2);
+    w = __builtin_amdgcn_cvt_scalef32_sr_fp8_f32(w, __uint_as_float(xb[3]), ~r[3], scale, 3);
+  } else {
+    w = __builtin_amdgcn_cvt_scalef32_sr_bf8_f32(w, __uint_as_float(xb[0]), ~r[0], scale, 0);
+    w = __builtin_amdgcn_cvt_scalef32_sr_bf8_f32(w, __uint_as_float(xb[1]), ~r[1], scale, 1);
+    w = __builtin_amdgcn_cvt_scalef32_sr_bf8_f32(w, __uint_as_float(xb[2]), ~r[2], scale, 2);
+    w = __builtin_amdgcn_cvt_scalef32_sr_bf8_f32(w, __uint_as_float(xb[3]), ~r[3], scale, 3);
+  }
+  return (uint32_t)w;
+}
+
+// Bytes of w whose code has magnitude zero (a signed zero): bit 7 of each
+// such byte set.
+__device__ __forceinline__ uint32_t zero_code_bytes(uint32_t w) {
+  return ~((w & 0x7F7F7F7Fu) + 0x7F7F7F7Fu) & 0x80808080u;
+}
+
+// A full tile of the stochastic-rounding cast with the hardware converts
+// (scale 2^-K, |K| <= 127).  Counts: a drawn zero of a nonzero finite input
+// is an underflow, and a zero input always gives a zero code, so underflows
+// are the zero codes less the zero inputs (non-finite inputs never give a
+// zero code).  Saturation and the clip counts run only in a wave whose
+// vector holds an element above the clip bound (uniform branch).
+template <int FMT, int DT, int U>
+__device__ __forceinline__ void sr_full_hw(const u32x4* v, int64_t e0, const CastParams& p, float scale,
+                                           const SrKey& key, Acc& acc, uint8_t* dst) {
+  constexpr int VEC = In<DT>::VEC;
+  uint32_t zc = 0, nz = 0;     // zero codes, nonzero inputs (per lane)
+  u16x2 nz16 = {0, 0};
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    const int vi = u * kThreads + threadIdx.x;
+    // element index < 2^34, so its block index fits 32 bits
+    const uint32_t blk = (uint32_t)((e0 + (int64_t)vi * VEC) >> 2);
+    uint32_t xb[VEC], w[VEC / 4];
+    unpack<DT>(v[u], xb);
+#pragma unroll
+    for (int j = 0; j < VEC / 4; ++j) {
+      uint32_t r[4];
+      sr_block(blk + j, key, r);
+      w[j] = sr_cvt4<FMT>(xb + 4 * j, r, scale);
+      zc += __popc(zero_code_bytes(w[j]));
+    }
+    uint32_t m = 0;
+    u16x2 h[4];
+    if constexpr (DT == NC_BF16) {               // packed 16-bit magnitudes
+      h[0] = mag16(v[u].x); h[1] = mag16(v[u].y); h[2] = mag16(v[u].z); h[3] = mag16(v[u].w);
+      const u16x2 hm = __builtin_elementwise_max(__builtin_elementwise_max(h[0], h[1]),
+                                                 __builtin_elementwise_max(h[2], h[3]));
+      m = (uint32_t)max(hm.x, hm.y) << 16;
+      const u16x2 one = {1, 1};
+#pragma unroll
+      for (int j = 0; j < 4; ++j) nz16 += __builtin_elementwise_min(h[j], one);
+    } else {
+#pragma unroll
+      for (int i = 0; i < VEC; ++i) {
+        m = max(m, xb[i] & kAbsMask);
+        nz += min(xb[i] & kAbsMask, 1u);
+      }
+    }
+    if (__ballot(m > p.t_clip) != 0) {           // wave-uniform: some element clips (or is Inf/NaN)
+#pragma unroll
+      for (int j = 0; j < VEC / 4; ++j) w[j] = sat4<FMT>(w[j]);
+#pragma unroll
+      for (int i = 0; i < VEC; ++i) acc.n_big += (xb[i] & kAbsMask) > p.t_clip ? 1u : 0u;
+      if (__ballot(m > kMaxFinite) != 0) {       // wave-uniform: Inf/NaN present
+        uint32_t mf = 0;
+#pragma unroll
+        for (int i = 0; i < VEC; ++i) mf = max(mf, finite_mag(xb[i] & kAbsMask, acc));
+        m = mf;
+#pragma unroll
+        for (int j = 0; j < VEC / 4; ++j) w[j] = fix_nonfinite4<FMT>(w[j], xb + 4 * j);
+      }
+    }
+    acc.amax = max(acc.amax, m);
+    if constexpr (DT == NC_F32) st_stream(reinterpret_cast<uint32_t*>(dst) + vi, w[0]);
+    else st_stream(reinterpret_cast<u32x2*>(dst) + vi, u32x2{w[0], w[1]});
+  }
+  if constexpr (DT == NC_BF16) nz = (uint32_t)nz16.x + nz16.y;
+  acc.n_uf += zc - ((uint32_t)(U * VEC) - nz);
+}
+
 template <int FMT, int DT>
 NC_STREAM_KERNEL
 k_cast_sr(const SegBatch b, const nc_scale_state* __restrict__ st, const nc_loss_scale* __restrict__ ls,
@@ -264,7 +365,10 @@ k_cast_sr(const SegBatch b, const nc_scale_state* __restrict__ st, const nc_loss
   Acc acc;
   acc.reset();
   uint8_t* dst = g.codes + e0;
-  if (full) {
+  if (full && K >= -127 && K <= 127) {
+    // hardware converts while 2^-K is an fp32 value (uniform branch)
+    sr_full_hw<FMT, DT, U>(v, e0, p, __builtin_amdgcn_ldexpf(1.0f, -K), key, acc, dst);
+  } else if (full) {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int vi = u * kThreads + threadIdx.x;
