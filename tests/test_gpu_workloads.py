@@ -157,9 +157,12 @@ def test_heavy_tailed_full_size():
 CHUNK = 1 << 21
 
 
-def _progress(msg):
-    sys.__stderr__.write(f"[progress] {msg}\n")
-    sys.__stderr__.flush()
+def _progress(capsys, msg):
+    """A progress line on the real stderr (pytest's capture set aside), so
+    that a long test is seen to be alive."""
+    with capsys.disabled():
+        sys.stderr.write(f"[progress] {msg}\n")
+        sys.stderr.flush()
 
 
 def _oracle_codes(pool, fmt, x32: np.ndarray, K: int) -> np.ndarray:
@@ -198,7 +201,7 @@ def _assert_states(st: torch.Tensor, hist: torch.Tensor, sts, W: int):
 
 # -- gradient steps: delayed scaling ------------------------------------------------
 
-def test_gradient_steps_delayed_scaling_every_code():
+def test_gradient_steps_delayed_scaling_every_code(capsys):
     """32 steps of 64 fp32 gradient tensors (44M elements a step), E5M2 with
     delayed scaling under the most-recent and the 16-step-window estimators
     (hysteresis on), step 0 by current scaling from the oracle's own amax.
@@ -256,14 +259,14 @@ def test_gradient_steps_delayed_scaling_every_code():
                     amaxes.append(Fraction(want["amax"]))
                 update(r["pol_o"], r["sts"], amaxes, [0] * T)
             if t % 8 == 7:
-                _progress(f"gradient steps: {t + 1}/{gen.steps} ({time.time() - t_start:.0f} s)")
+                _progress(capsys, f"gradient steps: {t + 1}/{gen.steps} ({time.time() - t_start:.0f} s)")
     for est in ests:
         _assert_states(run[est]["st"], run[est]["hist"], run[est]["sts"], W)
 
 
 # -- loss-scaled Llama-7B-shaped gradients, full size ------------------------------
 
-def test_llama_full_size_1024_steps():
+def test_llama_full_size_1024_steps(capsys):
     """All 225 tensors (6.6 G fp32 elements, one nc_cast_tensor call per step
     in the benchmark's launch shape) for 1024 steps: fused 2^-16 unscale,
     1e-7 of the elements Inf or NaN, E4M3 with a 16-step window and
@@ -311,7 +314,7 @@ def test_llama_full_size_1024_steps():
             if t not in sampled:
                 if t % 128 == 127:
                     torch.cuda.synchronize()
-                    _progress(f"llama: step {t + 1}/{steps} ({time.time() - t_start:.0f} s)")
+                    _progress(capsys, f"llama: step {t + 1}/{steps} ({time.time() - t_start:.0f} s)")
                 continue
             torch.cuda.synchronize()
             k_t = all_k[t].cpu().tolist()
@@ -336,7 +339,7 @@ def test_llama_full_size_1024_steps():
                     cc.copy_(codes[i])
                     assert np.array_equal(cc.numpy(), _oracle_codes(pool, E4M3, xn, K)), (t, i)
             oracle_amax[t] = amaxes
-            _progress(f"llama: step {t} checked in full ({time.time() - t_start:.0f} s)")
+            _progress(capsys, f"llama: step {t} checked in full ({time.time() - t_start:.0f} s)")
     torch.cuda.synchronize()
     counts = all_counts.cpu().numpy()
     ks = all_k.cpu().numpy()
