@@ -361,7 +361,9 @@ def small_configs(nc, torch, workloads):
     c1()
     ms, msg = both(c1)
     res["per_tensor_65536_fp32"] = dict(us=round(ms * 1e3, 1), us_graph=round(msg * 1e3, 1), elements=x.numel(),
-                                        launches=5, note="amax + scale update + cast, launch-bound")
+                                        launches=3,
+                                        note="amax + scale update + cast (each under 64 workgroups, so their "
+                                             "counts go straight to the output: no slot pass), launch-bound")
     # 4096 x 4096 tanh(N(0, 1.5)) bf16, MXFP8 E4M3 per rule
     xb = torch.from_numpy(workloads.tanh_activations().reshape(-1).view(np.int16)).to(dev).view(torch.bfloat16)
     n = xb.numel()

@@ -182,6 +182,76 @@ __device__ __forceinline__ void sr_block(uint32_t blk, const SrKey& key, uint32_
   philox10(r, key.k0, key.k1);
 }
 
+// Only word 0 of a block's counter (blk, j, o0, o1) differs between the
+// blocks of a tensor, so part of the first three rounds is the same for all
+// of them: round 1's product of word 2 and the words it yields, and round
+// 2's product of word 0.  SrPre holds those parts, each already xored with
+// its round key, formed once per workgroup from wave-uniform values (scalar
+// unit).  Round r (0-based) uses key (k0 + r W0, k1 + r W1).
+struct SrPre {
+  uint32_t x0;    // round 1: o1 ^ k1
+  uint32_t x1;    // round 2: lo(o0 M1) ^ (k0 + W0)
+  uint32_t x2;    // round 2: hi(A M0) ^ (k1 + W1), A = hi(o0 M1) ^ j ^ k0
+  uint32_t x3;    // round 3: lo(A M0) ^ (k1 + 2 W1)
+  uint32_t k0, k1;
+};
+
+__device__ __forceinline__ SrPre sr_pre(const SrKey& key) {
+  const uint32_t k0 = __builtin_amdgcn_readfirstlane(key.k0), k1 = __builtin_amdgcn_readfirstlane(key.k1);
+  const uint32_t j = __builtin_amdgcn_readfirstlane(key.j), o0 = __builtin_amdgcn_readfirstlane(key.o0);
+  const uint32_t o1 = __builtin_amdgcn_readfirstlane(key.o1);
+  const uint64_t q1 = (uint64_t)o0 * 0xCD9E8D57u;
+  const uint32_t a = (uint32_t)(q1 >> 32) ^ j ^ k0;
+  const uint64_t q0 = (uint64_t)a * 0xD2511F53u;
+  return SrPre{o1 ^ k1, (uint32_t)q1 ^ (k0 + 0x9E3779B9u), (uint32_t)(q0 >> 32) ^ (k1 + 0xBB67AE85u),
+               (uint32_t)q0 ^ (k1 + 2u * 0xBB67AE85u), k0, k1};
+}
+
+// The four uniforms of block `blk`, complemented (~r[i], the operand the
+// hardware stochastic-rounding converts take): the same ten rounds as
+// sr_block with the shared parts taken from `pre`, and the last round's
+// xors complemented in the same instruction (truth table 0x69).
+__device__ __forceinline__ void sr_block_inv(uint32_t blk, const SrPre& pre, uint32_t (&r)[4]) {
+  uint32_t c0, c1, c2, c3;
+  {                                                 // round 1: word 2's product is shared
+    const uint64_t p0 = (uint64_t)blk * 0xD2511F53u;
+    c2 = (uint32_t)(p0 >> 32) ^ pre.x0;
+    c3 = (uint32_t)p0;
+  }
+  {                                                 // round 2: word 0's product is shared
+    const uint64_t p1 = (uint64_t)c2 * 0xCD9E8D57u;
+    c0 = (uint32_t)(p1 >> 32) ^ pre.x1;
+    c1 = (uint32_t)p1;
+    c2 = c3 ^ pre.x2;
+  }
+  {                                                 // round 3: word 3 is shared
+    const uint64_t p0 = (uint64_t)c0 * 0xD2511F53u;
+    const uint64_t p1 = (uint64_t)c2 * 0xCD9E8D57u;
+    c0 = __builtin_amdgcn_bitop3_b32((uint32_t)(p1 >> 32), c1, pre.k0 + 2u * 0x9E3779B9u, 0x96);
+    c1 = (uint32_t)p1;
+    c2 = (uint32_t)(p0 >> 32) ^ pre.x3;
+    c3 = (uint32_t)p0;
+  }
+  uint32_t k0 = pre.k0 + 3u * 0x9E3779B9u, k1 = pre.k1 + 3u * 0xBB67AE85u;
+#pragma unroll
+  for (int i = 3; i < 9; ++i) {
+    const uint64_t p0 = (uint64_t)c0 * 0xD2511F53u;
+    const uint64_t p1 = (uint64_t)c2 * 0xCD9E8D57u;
+    c0 = __builtin_amdgcn_bitop3_b32((uint32_t)(p1 >> 32), c1, k0, 0x96);
+    c1 = (uint32_t)p1;
+    c2 = __builtin_amdgcn_bitop3_b32((uint32_t)(p0 >> 32), c3, k1, 0x96);
+    c3 = (uint32_t)p0;
+    k0 += 0x9E3779B9u;
+    k1 += 0xBB67AE85u;
+  }
+  const uint64_t p0 = (uint64_t)c0 * 0xD2511F53u;
+  const uint64_t p1 = (uint64_t)c2 * 0xCD9E8D57u;
+  r[0] = __builtin_amdgcn_bitop3_b32((uint32_t)(p1 >> 32), c1, k0, 0x69);
+  r[1] = ~(uint32_t)p1;
+  r[2] = __builtin_amdgcn_bitop3_b32((uint32_t)(p0 >> 32), c3, k1, 0x69);
+  r[3] = ~(uint32_t)p0;
+}
+
 // Stochastic rounding of one |x| (bits ax, finite, |x| 2^K <= max) at
 // exponent K with uniform u: returns m 2^(K - s), m the drawn multiple of
 // the grid spacing q at y = |x| 2^K (q = 2^(max(floor(log2 y), EMIN) - MB)).
@@ -246,21 +316,22 @@ __device__ __forceinline__ uint32_t sr4(const uint32_t* xb, const CastParams& p,
 // patterns of every exponent field at 127.  (The bf16-input forms differ from the
 // rule for values far below the subnormal grid, so bf16 inputs are widened
 // to fp32 first.)  Past the largest finite value they give the overflow
-// code, which sat4 saturates.  Four elements (fp32 patterns) -> four codes,
-// byte i = element i.
+// code, which sat4 saturates.  Four elements (fp32 patterns) and their
+// complemented uniforms -> four codes, byte i = element i.
 template <int FMT>
-__device__ __forceinline__ uint32_t sr_cvt4(const uint32_t* xb, const uint32_t (&r)[4], float scale) {
-  int w = 0;
+__device__ __forceinline__ uint32_t sr_cvt4(const uint32_t* xb, const uint32_t (&nr)[4], float scale) {
+  // every byte is written, so the word starts from any live value
+  int w = (int)nr[0];
   if constexpr (FMT == NC_E4M3) {
-    w = __builtin_amdgcn_cvt_scalef32_sr_fp8_f32(w, __uint_as_float(xb[0]), ~r[0], scale, 0);
-    w = __builtin_amdgcn_cvt_scalef32_sr_fp8_f32(w, __uint_as_float(xb[1]), ~r[1], scale, 1);
-    w = __builtin_amdgcn_cvt_scalef32_sr_fp8_f32(w, __uint_as_float(xb[2]), ~r[2], scale, 2);
-    w = __builtin_amdgcn_cvt_scalef32_sr_fp8_f32(w, __uint_as_float(xb[3]), ~r[3], scale, 3);
+    w = __builtin_amdgcn_cvt_scalef32_sr_fp8_f32(w, __uint_as_float(xb[0]), nr[0], scale, 0);
+    w = __builtin_amdgcn_cvt_scalef32_sr_fp8_f32(w, __uint_as_float(xb[1]), nr[1], scale, 1);
+    w = __builtin_amdgcn_cvt_scalef32_sr_fp8_f32(w, __uint_as_float(xb[2]), nr[2], scale, 2);
+    w = __builtin_amdgcn_cvt_scalef32_sr_fp8_f32(w, __uint_as_float(xb[3]), nr[3], scale, 3);
   } else {
-    w = __builtin_amdgcn_cvt_scalef32_sr_bf8_f32(w, __uint_as_float(xb[0]), ~r[0], scale, 0);
-    w = __builtin_amdgcn_cvt_scalef32_sr_bf8_f32(w, __uint_as_float(xb[1]), ~r[1], scale, 1);
-    w = __builtin_amdgcn_cvt_scalef32_sr_bf8_f32(w, __uint_as_float(xb[2]), ~r[2], scale, 2);
-    w = __builtin_amdgcn_cvt_scalef32_sr_bf8_f32(w, __uint_as_float(xb[3]), ~r[3], scale, 3);
+    w = __builtin_amdgcn_cvt_scalef32_sr_bf8_f32(w, __uint_as_float(xb[0]), nr[0], scale, 0);
+    w = __builtin_amdgcn_cvt_scalef32_sr_bf8_f32(w, __uint_as_float(xb[1]), nr[1], scale, 1);
+    w = __builtin_amdgcn_cvt_scalef32_sr_bf8_f32(w, __uint_as_float(xb[2]), nr[2], scale, 2);
+    w = __builtin_amdgcn_cvt_scalef32_sr_bf8_f32(w, __uint_as_float(xb[3]), nr[3], scale, 3);
   }
   return (uint32_t)w;
 }
@@ -279,7 +350,7 @@ __device__ __forceinline__ uint32_t zero_code_bytes(uint32_t w) {
 // vector holds an element above the clip bound (uniform branch).
 template <int FMT, int DT, int U>
 __device__ __forceinline__ void sr_full_hw(const u32x4* v, int64_t e0, const CastParams& p, float scale,
-                                           const SrKey& key, Acc& acc, uint8_t* dst) {
+                                           const SrPre& pre, Acc& acc, uint8_t* dst) {
   constexpr int VEC = In<DT>::VEC;
   uint32_t zc = 0, nz = 0;     // zero codes, nonzero inputs (per lane)
   u16x2 nz16 = {0, 0};
@@ -292,9 +363,9 @@ __device__ __forceinline__ void sr_full_hw(const u32x4* v, int64_t e0, const Cas
     unpack<DT>(v[u], xb);
 #pragma unroll
     for (int j = 0; j < VEC / 4; ++j) {
-      uint32_t r[4];
-      sr_block(blk + j, key, r);
-      w[j] = sr_cvt4<FMT>(xb + 4 * j, r, scale);
+      uint32_t nr[4];
+      sr_block_inv(blk + j, pre, nr);
+      w[j] = sr_cvt4<FMT>(xb + 4 * j, nr, scale);
       zc += __popc(zero_code_bytes(w[j]));
     }
     uint32_t m = 0;
@@ -366,38 +437,10 @@ k_cast_sr(const SegBatch b, const nc_scale_state* __restrict__ st, const nc_loss
   acc.reset();
   uint8_t* dst = g.codes + e0;
   if (full && K >= -127 && K <= 127) {
-    // hardware converts while 2^-K is an fp32 value (uniform branch)
-    sr_full_hw<FMT, DT, U>(v, e0, p, __builtin_amdgcn_ldexpf(1.0f, -K), key, acc, dst);
-  } else if (full) {
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int vi = u * kThreads + threadIdx.x;
-      // element index < 2^34, so its block index fits 32 bits
-      const uint32_t blk = (uint32_t)((e0 + (int64_t)vi * VEC) >> 2);
-      uint32_t xb[VEC], w[VEC / 4];
-      unpack<DT>(v[u], xb);
-      uint32_t m = 0;
-#pragma unroll
-      for (int j = 0; j < VEC / 4; ++j) {
-        uint32_t r[4];
-        sr_block(blk + j, key, r);
-        w[j] = sr4<FMT>(xb + 4 * j, p, c2, r, acc);
-      }
-#pragma unroll
-      for (int i = 0; i < VEC; ++i) m = max(m, xb[i] & kAbsMask);
-      if (__ballot(m > kMaxFinite) == 0) {       // wave-uniform: no Inf/NaN here
-        acc.amax = max(acc.amax, m);
-      } else {
-        uint32_t mf = 0;
-#pragma unroll
-        for (int i = 0; i < VEC; ++i) mf = max(mf, finite_mag(xb[i] & kAbsMask, acc));
-        acc.amax = max(acc.amax, mf);
-#pragma unroll
-        for (int j = 0; j < VEC / 4; ++j) w[j] = fix_nonfinite4<FMT>(w[j], xb + 4 * j);
-      }
-      if constexpr (DT == NC_F32) st_stream(reinterpret_cast<uint32_t*>(dst) + vi, w[0]);
-      else st_stream(reinterpret_cast<u32x2*>(dst) + vi, u32x2{w[0], w[1]});
-    }
+    // hardware converts while 2^-K is an fp32 value (uniform branch); a full
+    // tile at a scale beyond that (a loss-scale unscale far outside the
+    // usual range) runs per element, like a ragged one
+    sr_full_hw<FMT, DT, U>(v, e0, p, __builtin_amdgcn_ldexpf(1.0f, -K), sr_pre(key), acc, dst);
   } else {
     for (int base = 0; base < rem; base += kThreads) {
       const int i = base + (int)threadIdx.x;

@@ -14,7 +14,7 @@ namespace nc {
 // codes (a 16-byte bf16 store each).  Measured best on MI355X.
 constexpr int kCastVecs = 2;
 constexpr int kCastStatsVecs = 8;   // casts with fused statistics (more work per element)
-constexpr int kCastSrVecs = 4;      // the stochastic-rounding cast (ALU-bound: larger tiles)
+constexpr int kCastSrVecs = 8;      // the stochastic-rounding cast (ALU-bound: larger tiles)
 constexpr int kStatsVecs = 8;       // the statistics pass (read only)
 constexpr int kAmaxVecs = 4;
 template <bool STATS> constexpr int cast_vecs() { return STATS ? kCastStatsVecs : kCastVecs; }
