@@ -53,9 +53,10 @@ def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
-    # The first few steps after start-up ran some kernels 10-40% slower (a
-    # transient of a few tens of milliseconds), so the default warm-up
-    # covers it.
+    # The first steps after start-up run at a lower shader clock (the power
+    # manager ramps it; some kernels ran 10-40% slower in the first one or
+    # two steps), so the default warm-up covers them; step_series in the
+    # output shows every step either way.
     ap.add_argument("--warmup", type=int, default=8)
     ap.add_argument("--rows", type=int, default=262144, help="rows of 4096 (default 2^30 elements)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
