@@ -132,7 +132,7 @@ struct Acc {
   uint32_t n_big;    // |x| bits above t_clip: every clip plus every non-finite
   uint32_t n_uf;
   uint32_t amax;     // largest finite |x| bits
-  u16x2 big16, uf16; // the bf16 paths' packed per-half counters (fold() adds them in)
+  u16x2 big16, uf16; // the bf16 paths' packed per-half counters (wave_counts adds them in)
   __device__ void reset() {
     n_nf = n_big = n_uf = 0;
     amax = 0;
@@ -142,12 +142,6 @@ struct Acc {
   // Without clip counting (CLIPS = false) n_big must still hold the
   // non-finite elements, which the slot reduction subtracts from it.
   __device__ void no_clips() { n_big = n_nf; }
-  __device__ void fold() {
-    n_big += (uint32_t)big16.x + big16.y;
-    n_uf += (uint32_t)uf16.x + uf16.y;
-    big16 = u16x2{0, 0};
-    uf16 = u16x2{0, 0};
-  }
 };
 
 // bf16 inputs, two per 32-bit word: the magnitude, clip and underflow tests
@@ -567,28 +561,55 @@ __device__ __forceinline__ uint64_t wave_sum_u64(uint64_t v) {
   return v;
 }
 
-// The workgroup's totals, valid in thread 0: DPP row reductions, one LDS
-// entry per row, thread 0 over the rows.  Called by all threads (full EXEC);
-// lds holds kRows * 4 words.
+// One wave's count totals, the same in every lane (wave-uniform): DPP row
+// reductions, then the four row totals read across rows.  n_big and n_uf
+// travel packed in one word (low and high half): a lane counts at most a
+// few dozen elements -- 64 in the largest tiles -- so a wave's totals stay
+// far below 2^16.  n_nf is reduced only in a wave that met an Inf or NaN
+// (uniform branch).  Called with full EXEC.
+struct WaveCounts {
+  uint32_t amax, big_uf, n_nf;
+};
+
+__device__ __forceinline__ uint32_t rows_sum(uint32_t v) {     // v: row totals in lanes 0, 16, 32, 48
+  return (uint32_t)__builtin_amdgcn_readlane((int)v, 0) + (uint32_t)__builtin_amdgcn_readlane((int)v, 16) +
+         (uint32_t)__builtin_amdgcn_readlane((int)v, 32) + (uint32_t)__builtin_amdgcn_readlane((int)v, 48);
+}
+__device__ __forceinline__ uint32_t rows_max(uint32_t v) {
+  return max(max((uint32_t)__builtin_amdgcn_readlane((int)v, 0), (uint32_t)__builtin_amdgcn_readlane((int)v, 16)),
+             max((uint32_t)__builtin_amdgcn_readlane((int)v, 32), (uint32_t)__builtin_amdgcn_readlane((int)v, 48)));
+}
+
+__device__ __forceinline__ WaveCounts wave_counts(Acc acc) {
+  const uint32_t big = acc.n_big + acc.big16.x + acc.big16.y;
+  const uint32_t uf = acc.n_uf + acc.uf16.x + acc.uf16.y;
+  WaveCounts w;
+  w.amax = rows_max(row_max_u32(acc.amax));
+  w.big_uf = rows_sum(row_sum_u32(big | (uf << 16)));
+  w.n_nf = __ballot(acc.n_nf != 0u) != 0 ? rows_sum(row_sum_u32(acc.n_nf)) : 0u;
+  return w;
+}
+
+// The workgroup's totals, valid in thread 0: one LDS entry per wave, thread
+// 0 over the waves.  Called by all threads (full EXEC); lds holds at least
+// kWaves * 3 words.
 __device__ inline CountSlot workgroup_counts(Acc acc, uint32_t* lds) {
-  acc.fold();
-  const uint32_t m = row_max_u32(acc.amax);
-  const uint32_t nf = row_sum_u32(acc.n_nf), big = row_sum_u32(acc.n_big), uf = row_sum_u32(acc.n_uf);
-  if ((threadIdx.x & 15) == 0) {
-    const int r = threadIdx.x >> 4;
-    lds[r * 4 + 0] = m;
-    lds[r * 4 + 1] = nf;
-    lds[r * 4 + 2] = big;
-    lds[r * 4 + 3] = uf;
+  const WaveCounts w = wave_counts(acc);
+  if ((threadIdx.x & 63) == 0) {
+    const int i = threadIdx.x >> 6;
+    lds[i * 3 + 0] = w.amax;
+    lds[i * 3 + 1] = w.big_uf;
+    lds[i * 3 + 2] = w.n_nf;
   }
   __syncthreads();
   CountSlot c{0u, 0u, 0u, 0u};
   if (threadIdx.x == 0) {
-    for (int r = 0; r < kRows; ++r) {
-      c.amax = max(c.amax, lds[r * 4 + 0]);
-      c.n_nf += lds[r * 4 + 1];
-      c.n_big += lds[r * 4 + 2];
-      c.n_uf += lds[r * 4 + 3];
+#pragma unroll
+    for (int i = 0; i < kWaves; ++i) {
+      c.amax = max(c.amax, lds[i * 3 + 0]);
+      c.n_big += lds[i * 3 + 1] & 0xFFFFu;
+      c.n_uf += lds[i * 3 + 1] >> 16;
+      c.n_nf += lds[i * 3 + 2];
     }
   }
   return c;
@@ -750,29 +771,30 @@ __device__ inline void write_stat_slot(const StatAcc& a, double* slot, double* l
 // lds_st kRows * 6 doubles.
 __device__ inline void write_count_stat_slots(Acc acc, const StatAcc& a, CountSlot* slot, double* stat_slot,
                                               uint32_t* lds, double* lds_st) {
-  acc.fold();
-  const uint32_t m = row_max_u32(acc.amax);
-  const uint32_t nf = row_sum_u32(acc.n_nf), big = row_sum_u32(acc.n_big), uf = row_sum_u32(acc.n_uf);
+  const WaveCounts w = wave_counts(acc);
   double v[6];
 #pragma unroll
   for (int j = 0; j < 6; ++j) v[j] = row_sum_f64(a.s[j]);
+  if ((threadIdx.x & 63) == 0) {
+    const int i = threadIdx.x >> 6;
+    lds[i * 3 + 0] = w.amax;
+    lds[i * 3 + 1] = w.big_uf;
+    lds[i * 3 + 2] = w.n_nf;
+  }
   if ((threadIdx.x & 15) == 0) {
     const int r = threadIdx.x >> 4;
-    lds[r * 4 + 0] = m;
-    lds[r * 4 + 1] = nf;
-    lds[r * 4 + 2] = big;
-    lds[r * 4 + 3] = uf;
 #pragma unroll
     for (int j = 0; j < 6; ++j) lds_st[r * 6 + j] = v[j];
   }
   __syncthreads();
   if (threadIdx.x == 0) {
     CountSlot c{0u, 0u, 0u, 0u};
-    for (int r = 0; r < kRows; ++r) {
-      c.amax = max(c.amax, lds[r * 4 + 0]);
-      c.n_nf += lds[r * 4 + 1];
-      c.n_big += lds[r * 4 + 2];
-      c.n_uf += lds[r * 4 + 3];
+#pragma unroll
+    for (int i = 0; i < kWaves; ++i) {
+      c.amax = max(c.amax, lds[i * 3 + 0]);
+      c.n_big += lds[i * 3 + 1] & 0xFFFFu;
+      c.n_uf += lds[i * 3 + 1] >> 16;
+      c.n_nf += lds[i * 3 + 2];
     }
     *slot = c;
   } else if (threadIdx.x >= 64 && threadIdx.x < 70) {   // another wave: the sums run beside thread 0's
