@@ -44,9 +44,11 @@ tier-1 forms) are pinned by hand-worked elements and sums
 (``tests/golden/stats_hand.json``, ``tests/golden/dequant_hand.json``), the
 half-step bound, and a closed form of the tanh workload's bias and kept
 fraction; ``tests/test_oracle_stats_pins.py`` also plants mistakes in them
-and checks that the pins fail.  One part is not fully pinned: the hysteresis
-semantics of the scale-update state machine beyond its stated properties
-(``oracle.policy``) -- parity unpinned there.
+and checks that the pins fail.  The scale-update state machine
+(``oracle.policy``) follows a reading of an ambiguous hysteresis rule; it is
+pinned by brute-force properties and by traces worked by hand from that
+reading (``tests/golden/scale_update_hand.json``), which planted mistakes in
+the machine fail.
 """
 
 from .formats import BF16, E4M3, E5M2, FP16, FP32, FORMATS, Fmt, Val  # noqa: F401

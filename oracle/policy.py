@@ -42,7 +42,8 @@ Readings adopted where the pages are silent or loose:
          the last change), k is reset from A;
     (iii) else k is kept.
   A reset also sets a_ref = A.  The first recompute on a fresh state resets
-  unconditionally.  Parity unpinned beyond properties (i)-(iii).
+  unconditionally.  Pinned by brute-force properties and by traces worked
+  by hand from this reading (tests/golden/scale_update_hand.json).
 * Skip: when skipping on non-finite is enabled and any tensor of the batch
   saw a non-finite element, the whole step is skipped -- no tensor's history,
   step counter or scale changes.  (The loss-scale machine still runs.)

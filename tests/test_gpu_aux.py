@@ -38,6 +38,39 @@ def _counts_from_amax(amaxes, nonfinite=None):
 VALUES = [Fraction(2) ** j * m for j in (-1, 0, 1) for m in (Fraction(1), Fraction(3, 2), Fraction(7, 4), Fraction(15, 8))]
 
 
+def _hand_traces():
+    from tests.conftest import load_golden
+    return load_golden("scale_update_hand.json")["traces"]
+
+
+@pytest.mark.parametrize("tr", _hand_traces(), ids=lambda t: t["name"])
+def test_scale_update_hand_worked_traces(tr):
+    """The device state machine through the traces worked by hand from the
+    readings (tests/golden/scale_update_hand.json), compared with the hand
+    values directly: k and the reference estimate (as fp32) after every
+    step, and the loss scale where the trace runs it.  Each amax is passed
+    as the nearest fp32 value; the hand derivations hold for those too
+    (doubling an fp32 value is exact, so the halving comparisons are
+    unchanged)."""
+    p = dict(tr["policy"])
+    st = nc.new_state(1)
+    hist = nc.new_history(1, p["window"])
+    ls = nc.new_loss_scale(tr["loss_scale"]["s_log2"]) if "loss_scale" in tr else None
+    pol_cur = nc.policy(**{**p, "est": "current"})
+    nc.nc_scale_update(pol_cur, st, _counts_from_amax([Fraction(tr["start"]["amax"])]))
+    pol = nc.policy(**p)
+    rows = [tr["start"]] + tr["steps"]
+    for i, w in enumerate(rows):
+        if i > 0:
+            nc.nc_scale_update(pol, st, _counts_from_amax([Fraction(w["amax"])], [w.get("nonfinite", 0)]), hist, ls)
+        got = st.cpu().numpy()[0]
+        assert int(got[0]) == w["k"], (tr["name"], i, w)
+        if "a_ref" in w:
+            assert int(np.array([got[1]]).view(np.uint32)[0]) == _f32_bits(float(Fraction(w["a_ref"]))), (tr["name"], i)
+        if i > 0 and "s_log2" in w:
+            assert ls.cpu().tolist() == [w["s_log2"], w["clean_steps"]], (tr["name"], i)
+
+
 @pytest.mark.parametrize("name,fmt", FMTS)
 def test_scale_update_brute_force(name, fmt):
     """Every amax sequence of length 3 over 12 values (one tensor each, all

@@ -1,7 +1,12 @@
-"""Properties of the scale-update state machine and the loss-scale machine.
+"""Properties of the scale-update state machine and the loss-scale machine,
+and hand-worked traces of it.
 
-The hysteresis semantics beyond the properties checked here are parity
-unpinned (the pages' rule is ambiguous for power-of-two scales)."""
+The pages' hysteresis rule is ambiguous for power-of-two scales; the
+reading taken (R7: a forced decrease whenever the kept scale would overflow
+at the estimate, a reset when the estimate is at most half the estimate at
+the last change, otherwise keep) is pinned by brute-force properties and by
+traces worked by hand from that reading (tests/golden/scale_update_hand.json),
+which planted mistakes in the oracle fail."""
 
 import itertools
 from fractions import Fraction
@@ -10,9 +15,14 @@ import pytest
 
 from oracle import E4M3, E5M2
 from oracle import cast as t0
+from oracle import policy as pol_mod
 from oracle.formats import pow2
 from oracle.policy import (EST_CURRENT, EST_MAX_WINDOW, EST_MOST_RECENT, LossScale, Policy,
                            ScaleState, update)
+from tests.conftest import load_golden
+
+HAND = load_golden("scale_update_hand.json")
+FMTS = {"e4m3": E4M3, "e5m2": E5M2}
 
 VALUES = [pow2(j) * m for j in (-1, 0, 1) for m in (Fraction(1), Fraction(3, 2), Fraction(7, 4), Fraction(15, 8))]
 
@@ -171,3 +181,80 @@ def test_ema_worked_values_and_properties():
         assert min(seq[:i + 1]) <= st[0].hist[0] <= max(seq[:i + 1])
         assert st[0].k == t0.scale_exponent(E4M3, st[0].hist[0])
         assert len(st[0].hist) == 1 and st[0].step == i + 1
+
+
+# -- hand-worked traces -------------------------------------------------------------
+
+def _policy(d):
+    kw = {k: v for k, v in d.items() if k not in ("fmt",)}
+    return Policy(fmt=FMTS[d["fmt"]], **kw)
+
+
+def run_hand_trace(tr):
+    """The oracle through one golden trace: step 0 by current scaling (no
+    loss-scale step), then the delayed updates.  Returns per step (k, a_ref,
+    s_log2, clean_steps)."""
+    pol = _policy(tr["policy"])
+    cur = Policy(**{**pol.__dict__, "est": EST_CURRENT})
+    st = ScaleState()
+    update(cur, [st], [Fraction(tr["start"]["amax"])], [0])
+    out = [(st.k, st.a_ref, None, None)]
+    ls = LossScale(**tr["loss_scale"]) if "loss_scale" in tr else None
+    for s in tr["steps"]:
+        update(pol, [st], [Fraction(s["amax"])], [s.get("nonfinite", 0)], ls)
+        out.append((st.k, st.a_ref, ls.s_log2 if ls else None, ls.clean_steps if ls else None))
+    return out
+
+
+def hand_trace_mismatches(tr):
+    got = run_hand_trace(tr)
+    want = [tr["start"]] + tr["steps"]
+    bad = []
+    for i, (g, w) in enumerate(zip(got, want)):
+        if g[0] != w["k"] or ("a_ref" in w and g[1] != Fraction(w["a_ref"])):
+            bad.append((i, g[:2], w))
+        if "s_log2" in w and i > 0 and (g[2] != w["s_log2"] or g[3] != w["clean_steps"]):
+            bad.append((i, g[2:], w))
+    return bad
+
+
+@pytest.mark.parametrize("tr", HAND["traces"], ids=[t["name"] for t in HAND["traces"]])
+def test_hand_worked_traces(tr):
+    """The scale exponent, the reference estimate and the loss scale after
+    every step equal the values worked by hand from the readings."""
+    assert hand_trace_mismatches(tr) == []
+
+
+def _set_scale_variant(kind):
+    """set_scale with one plausible mistake planted."""
+    def f(policy, st, a):
+        fmt, margin = policy.fmt, policy.margin
+        k_new = t0.scale_exponent(fmt, a, margin)
+        over = a * pow2(st.k) > fmt.maxval * pow2(-margin)
+        half = (2 * a < st.a_ref) if kind == "strict_half" else (2 * a <= st.a_ref)
+        if kind == "no_forced_decrease":
+            over = False
+        reset = (not policy.hysteresis) or (not st.has_ref) or over or half
+        if reset:
+            st.k, st.a_ref, st.has_ref = k_new, a, True
+        elif kind == "ref_every_recompute":
+            st.a_ref = a
+    return f
+
+
+@pytest.mark.parametrize("kind", ["strict_half", "no_forced_decrease", "ref_every_recompute",
+                                  "window_off_by_one", "interval_ignored"])
+def test_hand_traces_catch_planted_mistakes(kind, monkeypatch):
+    """Each planted mistake in the state machine changes at least one value
+    of the hand-worked traces."""
+    if kind == "window_off_by_one":
+        real = pol_mod.estimate
+        monkeypatch.setattr(pol_mod, "estimate",
+                            lambda p, st: max(st.hist[1:] or st.hist) if p.est == EST_MAX_WINDOW else real(p, st))
+    elif kind == "interval_ignored":
+        def every_step(policy, states, amaxes, nonfinite, ls=None):
+            return pol_mod.update(Policy(**{**policy.__dict__, "interval": 1}), states, amaxes, nonfinite, ls)
+        monkeypatch.setitem(globals(), "update", every_step)
+    else:
+        monkeypatch.setattr(pol_mod, "set_scale", _set_scale_variant(kind))
+    assert any(hand_trace_mismatches(tr) for tr in HAND["traces"]), kind
