@@ -73,8 +73,8 @@ typedef enum { NC_E4M3 = 0, NC_E5M2 = 1 } nc_fmt;
 
 /* MX shared-exponent rules for a block with finite amax a = m * 2^e, m in [1,2)
  * ([Drift, "What the measurements said" and "The part I would rather not
- * write"]):  OCP (floor based): X = e - emax_F;  PLUS1: one extra bit of
- * exponent headroom, X = e - emax_F + 1;  CEIL: the scale rounded up, the
+ * write"]):  OCP (floor based): X = e - emax_F;  PLUS1: the exponent one
+ * higher, X = e - emax_F + 1;  CEIL: the scale rounded up, the
  * smallest X with a * 2^-X <= max_F.  a == 0 gives X = -127. */
 typedef enum { NC_MX_OCP = 0, NC_MX_PLUS1 = 1, NC_MX_CEIL = 2 } nc_mx_rule;
 
@@ -161,8 +161,8 @@ typedef struct {
 
 /* Per-tensor error statistics over finite elements (device array, zeroed),
  * e = xhat - x with xhat the exact value the code stands for and x the
- * (unscaled) input: how much the cast changes the tensor, and separately
- * which way the change points ([Drift, "What the measurements said"]). */
+ * (unscaled) input: the size of the change the cast makes, and apart from
+ * it the direction of that change ([Drift, "What the measurements said"]). */
 typedef struct {
   double sum_e, sum_abs_e, sum_e2;
   double sum_dir_e;  /* sum of sign(x) * e: negative when magnitudes shrink */
@@ -205,7 +205,7 @@ typedef struct {
   float ema_alpha;            /* EMA smoothing coefficient, 0 < alpha <= 1 (other estimators ignore it) */
 } nc_policy;
 
-/* Per-tensor amax pass ("a pass over the tensor", [E3, "Worked solution"];
+/* Per-tensor amax pass (a full read of the tensor, [E3, "Worked solution"];
  * the second look at the data that current scaling needs, [MaxWin,
  * "Experimental Variables"]).  Reads x only.  For each tensor: max-accumulates
  * amax_bits of |x| * 2^-s over finite elements and adds n_finite and
@@ -263,7 +263,7 @@ nc_status nc_cast_tensor_static(const nc_tensor *t, int32_t count, nc_dtype dtyp
                                 nc_stats *stats, void *stream);
 
 /* Per-tensor cast with stochastic rounding ([Drift, "The part I would rather
- * not write": unbiased at any single step]).  As nc_cast_tensor, except the
+ * not write": no bias within one step]).  As nc_cast_tensor, except the
  * rounding: with y = x * 2^(st[j].k - s) between grid neighbours lo <= |y| <
  * lo + q and t = (|y| - lo) / q, the magnitude rounds up iff u < t * 2^32,
  * u the element's uniform 32-bit integer -- word i % 4 of Philox4x32-10
@@ -305,8 +305,8 @@ nc_status nc_dequant(const nc_tensor *t, int32_t count, nc_fmt fmt, const nc_sca
                      void *const *y, nc_dtype out_dtype, void *stream);
 
 /* Error statistics as a separate pass over x and the codes already written
- * ([Drift, "What the measurements said"]: how much the cast changes a
- * tensor, measured apart from which way the change points).  Over the
+ * ([Drift, "What the measurements said"]: the size of the change the cast
+ * makes, measured apart from its direction).  Over the
  * finite elements of each tensor, with x the input after the unscale by
  * 2^-ls->s_log2 (per-tensor only; ls nullable) and xhat = decode(q) * 2^-k
  * (per-tensor, st non-NULL) or decode(q) * 2^X (MX, st == NULL, scales

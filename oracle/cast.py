@@ -20,8 +20,8 @@ Readings of the pages adopted here (they are silent or loose on these points):
   2^k, 2^-k and the X + 127 byte are all representable.  amax = 0 gives
   k = 127 and X = -127.
 * The margin is an integer number of binades, so the scale stays a power of
-  two ([E3, "Worked solution"]: a scale that is not a power of two adds a
-  rounding of its own).
+  two ([E3, "Worked solution"]: any other scale would round the values a
+  second time).
 """
 
 from fractions import Fraction
@@ -42,8 +42,8 @@ def amax(values, unscale_log2: int = 0) -> Fraction:
     unscale x -> x * 2^-s, returned as an fp32 value (round-to-nearest-even
     of the exact result; exact unless it falls below the fp32 normal range).
 
-    [E3, "Worked solution"]: the procedure watches the largest absolute value
-    of a tensor.  Non-finite elements are excluded (they are counted apart).
+    [E3, "Worked solution"]: the quantity watched is each tensor's largest
+    magnitude.  Non-finite elements are excluded (they are counted apart).
     The maximum of no finite elements is 0.
     """
     best = Fraction(0)
@@ -63,9 +63,9 @@ def count_nonfinite(values) -> int:
 def scale_exponent(fmt: Fmt, a: Fraction, margin: int = 0) -> int:
     """The per-tensor scale rule: the largest power of two 2^k that keeps the
     estimate a at or below M_F with a margin, a * 2^k <= M_F * 2^-margin,
-    searched over k in [-127, 127] ([E3, "Worked solution"]: largest power of
-    two keeping the watched value below the format's largest finite number
-    with a margin).  a = 0 satisfies every k and gives 127; an a too large
+    searched over k in [-127, 127] ([E3, "Worked solution"]: the biggest
+    power-of-two scale under which the watched maximum, with a margin, still
+    fits the format).  a = 0 satisfies every k and gives 127; an a too large
     for any k gives -127.
     """
     bound = fmt.maxval * pow2(-margin)
@@ -88,8 +88,8 @@ def mx_exponent(fmt: Fmt, a: Fraction, rule: str) -> int:
     [Drift, "What the measurements said"] and ["The part I would rather not
     write"]: the OCP specification's rule is floor based -- X is the binade of
     the block's largest magnitude minus the largest exponent of the element
-    format, which can put that magnitude above M_F (so it clips); one extra
-    bit of exponent headroom (X + 1) removed the clipping; the alternative
+    format, which can put that magnitude above M_F (so it clips); raising the
+    exponent by one (X + 1) took the clipping away; the alternative
     recipe rounds the shared scale up, i.e. takes the smallest X for which the
     block's largest magnitude fits (a * 2^-X <= M_F).
     An all-zero (or all-non-finite) block gives X = -127.
@@ -138,7 +138,7 @@ def sr_element(fmt: Fmt, v: Val, K: int, u: int):
     """Stochastic rounding of one input value at exponent K (the value cast is
     y = v * 2^K, exact), with u a uniform 32-bit integer.
 
-    Reading: the pages only say the rounding is unbiased at any single step
+    Reading: the pages only say the rounding carries no bias within one step
     ([Drift, "The part I would rather not write"]) and that its damage sits in
     the backward matmuls ([Drift, "What the measurements said"]).  Taken
     here as the textbook rule: with lo <= |y| < lo + q the two neighbouring
@@ -278,8 +278,8 @@ def stats_terms(x: Fraction, xhat: Fraction):
     """The six per-element terms for a finite element x with represented value
     xhat, e = xhat - x: e, |e|, e^2, sign(x) e, x e, x^2.
 
-    [Drift, "What the measurements said"]: how much the cast changes a tensor
-    is measured separately from which way the change points; sign(x) e is the
+    [Drift, "What the measurements said"]: the size of the change the cast
+    makes is measured apart from its direction; sign(x) e is the
     component of the error along the element (negative when the cast shrinks
     magnitudes, as clipping does), x e / x^2 gives the fraction of the tensor
     kept along itself.

@@ -9,7 +9,7 @@ formats spend a code on negative zero.
 
 Formats [MP-card, items (1)-(3)]:
 
-* FP16 = 1 sign + 5 exponent + 10 mantissa bits, largest finite value
+* FP16: a sign bit, five exponent bits and ten mantissa bits; largest finite value
   2^15 * (2 - 2^-10) = 65504, smallest normal 2^-14, smallest subnormal 2^-24.
 * BF16 = 1 + 8 + 7 bits, the exponent range of fp32 (about +-3.4e38).
 * E4M3 = 4 exponent + 3 mantissa bits with largest value about 448; E5M2 =

@@ -4,22 +4,22 @@ TEST INFRASTRUCTURE ONLY (see ``oracle/__init__.py``).
 
 What the pages fix:
 
-* [E3, "Worked solution"]: watch the largest absolute value of each tensor
-  over a window of steps; set the scale to the largest power of two keeping
-  it below the format's largest finite value with a margin; recompute every
-  fixed number of steps; keep the previous scale if the new one differs from
-  it by less than a factor of two.
+* [E3, "Worked solution"]: track each tensor's largest magnitude across a
+  span of recent steps; choose the biggest power-of-two scale under which
+  that maximum, with a margin, still fits the format; recompute at a fixed
+  step interval; leave the scale unchanged when the recomputed one is
+  within a factor of two of it.
 * [MaxWin, "Experimental Variables"]: the estimators -- most recent (the
   previous step's amax), a maximum over a window of recent steps (64 there),
   exponential smoothing, and current scaling (this step's own amax, which
-  needs a second look at the data).  The smoothing coefficient and the
+  has to read the data one extra time).  The smoothing coefficient and the
   arithmetic are not given; read here as E <- E + alpha (a - E) in fp32 with
   each operation rounded to nearest even (no fused multiply-add), E = a at
   the first push.  [MaxWin, "Key Contributions"]: the
   window maximum guarantees no scale-induced saturation for a step whose amax
   is within the window.  A warmup fills the history before quantisation.
 * [MP-card, item (1)]: dynamic loss scaling halves S and skips the step on an
-  Inf/NaN, and doubles S after a period without overflow.
+  Inf/NaN, and doubles S once enough steps have passed with no overflow.
 
 Readings adopted where the pages are silent or loose:
 
@@ -32,9 +32,8 @@ Readings adopted where the pages are silent or loose:
   neither reads nor writes the history or the step counter.
 * Interval I: with delayed estimators, after the push of step t the scale is
   recomputed when (t + 1) is a multiple of I (the step counter counts pushes).
-* Hysteresis.  Read literally ("differs by less than a factor of two") the
-  rule is vacuous for power-of-two scales, which always differ by at least
-  two.  Adopted per tensor: keep a_ref, the estimate at the last change of k.
+* Hysteresis.  Read literally (no change within a factor of two) the rule
+  is vacuous for power-of-two scales, which always differ by at least two.  Adopted per tensor: keep a_ref, the estimate at the last change of k.
   At a recompute with estimate A:
     (i)  if A * 2^k exceeds M_F * 2^-margin, k is reset from A (a forced
          decrease, so the scale never overflows at the estimate);
@@ -48,8 +47,8 @@ Readings adopted where the pages are silent or loose:
   saw a non-finite element, the whole step is skipped -- no tensor's history,
   step counter or scale changes.  (The loss-scale machine still runs.)
 * The loss-scale machine runs only when enabled; S = 2^s with s clamped to
-  [s_min, s_max]; "a period without overflow" is the growth interval in
-  clean steps.
+  [s_min, s_max]; the overflow-free stretch before a doubling is the growth
+  interval in clean steps.
 """
 
 from dataclasses import dataclass, field

@@ -3,7 +3,7 @@
 TEST INFRASTRUCTURE ONLY (see ``oracle/__init__.py``).
 
 The pages do not name a generator ([Drift, "The part I would rather not
-write"] only says stochastic rounding is unbiased at any single step).  The
+write"] only says stochastic rounding carries no bias within one step).  The
 cast draws one 32-bit uniform integer per element from Philox4x32-10, the
 counter-based generator of Salmon, Moraes, Dror and Shaw, "Parallel Random
 Numbers: As Easy as 1, 2, 3" (SC11), implemented here from that published

@@ -4,8 +4,8 @@ TEST INFRASTRUCTURE ONLY (see ``oracle/__init__.py``).
 
 What the pages fix:
 
-* [E3, "Worked solution"]: a format's range is what breaks at its largest
-  and smallest values, its step is what breaks at the weight.  So the
+* [E3, "Worked solution"]: range fails at a format's extremes, while the
+  grid spacing is what fails where the weight sits.  So the
   procedure tracks, beside the amax, how large each update is compared with
   the grid spacing at its weight; a wide master copy is kept while updates
   are smaller than that spacing, and a tensor moves to a wider format once

@@ -140,7 +140,7 @@ k_cast_pt(const SegBatch b, const nc_scale_state* __restrict__ st,
 
 // ---------------------------------------------------------------------------
 // Stochastic-rounding cast ([Drift, "The part I would rather not write"]:
-// unbiased at any single step).
+// its expected code at one step is the input itself, with no bias).
 //
 // Uniforms: Philox4x32-10 (Salmon, Moraes, Dror, Shaw, "Parallel Random
 // Numbers: As Easy as 1, 2, 3", SC11): ten rounds, each two 32 x 32 -> 64-bit

@@ -1,7 +1,7 @@
 // The update/step-ratio ("swamping") monitor: a read-only pass over fp32
 // master weights w and their updates d that classifies each update against
-// the step of w's narrow copy ([E3, "Worked solution"]: watch the ratio of
-// the update to the step at the weight; [SP, "Master weights and the
+// the step of w's narrow copy ([E3, "Worked solution"]: compare each update
+// with the grid spacing where its weight sits; [SP, "Master weights and the
 // optimizer step"]: a small enough update is exactly a no-op in 16 bits),
 // and the per-tensor promotion window.
 //

@@ -1,4 +1,4 @@
-"""All 65,536 pairs of 8-bit values as a product and as a sum, per format
+"""All 65,536 pairs of 8-bit values, multiplied and added, per format
 ([Drift, "First, catching myself"]: two implementations compared on every
 value and every pair, signed zero included).
 

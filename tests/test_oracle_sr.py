@@ -143,8 +143,8 @@ def test_sr_tier0_vs_tier1(fmt):
 
 @pytest.mark.parametrize("fmt", FMTS, ids=["e4m3", "e5m2"])
 def test_unbiased_at_a_single_step(fmt):
-    """[Drift, "The part I would rather not write"]: stochastic rounding is
-    unbiased at any single step.  Over 40,000 draws of the generator the mean
+    """[Drift, "The part I would rather not write"]: stochastic rounding
+    carries no bias within one step.  Over 40,000 draws of the generator the mean
     decoded value of each y is within 5 standard errors of y, while round to
     nearest is off by more than that."""
     tab = bulk.decode_table(fmt)

@@ -1,8 +1,8 @@
 """Pins of the oracle's error statistics and of the value a code stands for,
 against values fixed outside the oracle.
 
-The statistics measure how much the cast changes a tensor and, separately,
-which way the change points (page "what actually breaks low precision
+The statistics measure the size of the change the cast makes to a tensor
+and, apart from it, the change's direction (page "what actually breaks low precision
 training", section "What the measurements said"): over finite elements,
 with xhat = decode(q) * 2^-K and e = xhat - x, the sums of e, |e|, e^2,
 sign(x) e, x e and x^2.  Pinned here by:

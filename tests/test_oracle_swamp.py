@@ -16,7 +16,7 @@ WF = [BF16, FP16]
 
 
 def test_pages_examples():
-    # [E3, "Worked solution"]: a weight of 1.0 with an update of 0.001 changes nothing (bf16)
+    # [E3, "Worked solution"]: adding 0.001 to a bf16 weight of 1.0 leaves it unchanged
     assert swamp.element(BF16, Val.of(1.0), Val.of(0.001)) == (True, True, False, False)
     # [SP, "Master weights ..."]: weight ~1, update ~1e-7: a no-op in 16 bits, lands in 32 bits
     for f in (BF16, FP16):
