@@ -149,9 +149,8 @@ def write_traffic(fetch_csv: str, write_csv: str):
         per[counter] = {sig: 1024.0 * factor * sum(v) / len(v) for sig, v in vals.items()}
     for sig in KERNEL_SIG.values():
         if sig in per["FETCH_SIZE"] and sig in per["WRITE_SIZE"]:
-            rd, wr = per["FETCH_SIZE"][sig], per["WRITE_SIZE"][sig]
-            out["kernels"][sig] = {"read_bytes": round(rd), "write_bytes": round(wr),
-                                   "hbm_bytes_per_launch": round(rd + wr)}
+            rd, wr = round(per["FETCH_SIZE"][sig]), round(per["WRITE_SIZE"][sig])
+            out["kernels"][sig] = {"read_bytes": rd, "write_bytes": wr, "hbm_bytes_per_launch": rd + wr}
     with open(TRAFFIC_JSON, "w") as f:
         json.dump(out, f, indent=1)
     print(json.dumps(out, indent=1))
