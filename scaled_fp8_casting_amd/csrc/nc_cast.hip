@@ -307,17 +307,22 @@ __device__ __forceinline__ uint32_t sr4(const uint32_t* xb, const CastParams& p,
 
 // gfx950's stochastic-rounding scaled converts (v_cvt_scalef32_sr_fp8_f32 /
 // _bf8_f32): x / scale rounded to the format with a 32-bit random operand
-// per element.  Given ~u they round up exactly when u < ceil(t 2^32), the
-// rule above: a probe matched it bit for bit on 2^20 cases (values on and
-// between grid points in the normal and subnormal ranges and far below
-// them, random and extreme operands, both formats, scales 2^-20 .. 2^20),
-// and the parity tests match the oracle on every bf16 pattern at scale
-// exponents from 127 down to -127 (the range this path takes) and on fp32
-// patterns of every exponent field at 127.  (The bf16-input forms differ from the
-// rule for values far below the subnormal grid, so bf16 inputs are widened
-// to fp32 first.)  Past the largest finite value they give the overflow
-// code, which sat4 saturates.  Four elements (fp32 patterns) and their
-// complemented uniforms -> four codes, byte i = element i.
+// per element.  Given ~u they follow the rule above -- up exactly when
+// u < ceil(t 2^32) -- whenever the fraction t has at most 23 - MB
+// fractional bits; with more, they resolve t to 23 - MB bits and round up
+// only when the top 23 - MB bits of u lie below t's, so for u just under
+// ceil(t 2^32) they round down where the rule rounds up (never the other
+// way).  A probe with u set at the threshold and one below it, over every
+// fraction length from 1 to 44 bits, both formats and scales 2^-127 ..
+// 2^127, showed exactly this boundary.  t has at most 23 - MB fractional
+// bits whenever the result is in the normal range (y >= 2^EMIN: 24
+// significant bits of x above the grid's last MB), and for bf16 inputs (8
+// significant bits) whenever y >= 2^(EMIN - 16); below those bounds
+// sr_fix_region marks the elements for the software rule.  (The bf16-input
+// forms differ further, so bf16 inputs are widened to fp32 first.)  Past the
+// largest finite value they give the overflow code, which sat4 saturates.
+// Four elements (fp32 patterns) and their complemented uniforms -> four
+// codes, byte i = element i.
 template <int FMT>
 __device__ __forceinline__ uint32_t sr_cvt4(const uint32_t* xb, const uint32_t (&nr)[4], float scale) {
   // every byte is written, so the word starts from any live value
@@ -342,6 +347,49 @@ __device__ __forceinline__ uint32_t zero_code_bytes(uint32_t w) {
   return ~((w & 0x7F7F7F7Fu) + 0x7F7F7F7Fu) & 0x80808080u;
 }
 
+// Where the hardware converts may differ from the rule (see sr_cvt4): |x|
+// bits below `thr`, i.e. y = |x| 2^K below 2^EMIN (fp32 inputs) or below
+// 2^(EMIN - 16) (bf16 inputs).  For bf16 inputs such a y lies below the
+// grid by more than 2^(16 - MB) (t < 2^(MB - 16), so the rule can only round
+// up when u < 2^(MB + 16)): `nr_min` is the smallest complemented word of
+// such a u, and an element needs the software rule only if it is in the
+// region and its word is at least nr_min.
+struct SrFix {
+  uint32_t thr;        // region: 0 < |x| bits < thr (a zero input is exact: t = 0); thr >= 1
+  uint32_t nr_min;     // bf16: ~u >= nr_min  <=>  u < 2^(MB + 16)
+  __device__ bool in(uint32_t ax) const { return ax - 1u < thr - 1u; }
+};
+
+template <int FMT, int DT>
+__device__ __forceinline__ SrFix sr_fix_region(int K) {
+  using F = Fp8<FMT>;
+  const int j = (DT == NC_BF16 ? F::EMIN - 16 : F::EMIN) - K;     // region: |x| < 2^j
+  uint32_t thr;
+  if (j > 127) thr = kInfBits;                     // every finite |x|
+  else if (j >= -126) thr = (uint32_t)(j + 127) << 23;
+  else if (j >= -149) thr = 1u << (j + 149);       // a subnormal power of two
+  else thr = 1u;                                   // no nonzero |x|
+  return SrFix{thr, 0u - (1u << (F::MB + 16))};
+}
+
+// The rule in software for four elements (sr_value; every |x| 2^K here is
+// far below the largest finite value) from their complemented uniforms:
+// four codes, byte i = element i.
+template <int FMT>
+__device__ __forceinline__ uint32_t sr4_soft(const uint32_t* xb, int K, int c2, const uint32_t* nr) {
+  float v[4];
+  uint32_t sgn = 0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    float m;
+    v[i] = sr_value<FMT>(xb[i] & kAbsMask, K, c2, ~nr[i], m);
+    sgn |= (xb[i] >> 31) << (8 * i + 7);
+  }
+  int w = cvt_pair<FMT, false>(v[0], v[1], 0);
+  w = cvt_pair<FMT, true>(v[2], v[3], w);
+  return (uint32_t)w | sgn;
+}
+
 // A full tile of the stochastic-rounding cast with the hardware converts
 // (scale 2^-K, |K| <= 127).  Counts: a drawn zero of a nonzero finite input
 // is an underflow, and a zero input always gives a zero code, so underflows
@@ -349,8 +397,8 @@ __device__ __forceinline__ uint32_t zero_code_bytes(uint32_t w) {
 // zero code).  Saturation and the clip counts run only in a wave whose
 // vector holds an element above the clip bound (uniform branch).
 template <int FMT, int DT, int U>
-__device__ __forceinline__ void sr_full_hw(const u32x4* v, int64_t e0, const CastParams& p, float scale,
-                                           const SrPre& pre, Acc& acc, uint8_t* dst) {
+__device__ __forceinline__ void sr_full_hw(const u32x4* v, int64_t e0, const CastParams& p, int c2, float scale,
+                                           const SrPre& pre, const SrFix& fx, Acc& acc, uint8_t* dst) {
   constexpr int VEC = In<DT>::VEC;
   uint32_t zc = 0, nz = 0;     // zero codes, nonzero inputs (per lane)
   u16x2 nz16 = {0, 0};
@@ -359,17 +407,19 @@ __device__ __forceinline__ void sr_full_hw(const u32x4* v, int64_t e0, const Cas
     const int vi = u * kThreads + threadIdx.x;
     // element index < 2^34, so its block index fits 32 bits
     const uint32_t blk = (uint32_t)((e0 + (int64_t)vi * VEC) >> 2);
-    uint32_t xb[VEC], w[VEC / 4];
+    uint32_t xb[VEC], w[VEC / 4], nr[VEC];
     unpack<DT>(v[u], xb);
 #pragma unroll
     for (int j = 0; j < VEC / 4; ++j) {
-      uint32_t nr[4];
-      sr_block_inv(blk + j, pre, nr);
-      w[j] = sr_cvt4<FMT>(xb + 4 * j, nr, scale);
-      zc += __popc(zero_code_bytes(w[j]));
+      uint32_t q[4];
+      sr_block_inv(blk + j, pre, q);
+      w[j] = sr_cvt4<FMT>(xb + 4 * j, q, scale);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) nr[4 * j + i] = q[i];
     }
     uint32_t m = 0;
     u16x2 h[4];
+    bool fix;                                    // some element needs the software rule
     if constexpr (DT == NC_BF16) {               // packed 16-bit magnitudes
       h[0] = mag16(v[u].x); h[1] = mag16(v[u].y); h[2] = mag16(v[u].z); h[3] = mag16(v[u].w);
       const u16x2 hm = __builtin_elementwise_max(__builtin_elementwise_max(h[0], h[1]),
@@ -378,13 +428,39 @@ __device__ __forceinline__ void sr_full_hw(const u32x4* v, int64_t e0, const Cas
       const u16x2 one = {1, 1};
 #pragma unroll
       for (int j = 0; j < 4; ++j) nz16 += __builtin_elementwise_min(h[j], one);
+      // far below the grid only an element whose u < 2^(MB + 16) can
+      // differ: screen on the vector's largest complemented word, about one
+      // element in 2^(16 - MB) passes
+      uint32_t nmax = nr[0];
+#pragma unroll
+      for (int i = 1; i < VEC; ++i) nmax = max(nmax, nr[i]);
+      fix = false;
+      if (__ballot(nmax >= fx.nr_min) != 0) {    // wave-uniform
+#pragma unroll
+        for (int i = 0; i < VEC; ++i) fix |= fx.in(xb[i] & kAbsMask) && nr[i] >= fx.nr_min;
+      }
     } else {
+      uint32_t mn = ~0u;                         // least magnitude less one (zeros wrap)
 #pragma unroll
       for (int i = 0; i < VEC; ++i) {
         m = max(m, xb[i] & kAbsMask);
+        mn = min(mn, (xb[i] & kAbsMask) - 1u);
         nz += min(xb[i] & kAbsMask, 1u);
       }
+      fix = mn < fx.thr - 1u;
     }
+    if (__ballot(fix) != 0) {                    // wave-uniform: the software rule for the region
+#pragma unroll
+      for (int j = 0; j < VEC / 4; ++j) {
+        const uint32_t sw = sr4_soft<FMT>(xb + 4 * j, p.K, c2, nr + 4 * j);
+        uint32_t sel = 0;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) sel |= (fx.in(xb[4 * j + i] & kAbsMask) ? 0xFFu : 0u) << (8 * i);
+        w[j] = (w[j] & ~sel) | (sw & sel);
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < VEC / 4; ++j) zc += __popc(zero_code_bytes(w[j]));
     if (__ballot(m > p.t_clip) != 0) {           // wave-uniform: some element clips (or is Inf/NaN)
 #pragma unroll
       for (int j = 0; j < VEC / 4; ++j) w[j] = sat4<FMT>(w[j]);
@@ -440,7 +516,8 @@ k_cast_sr(const SegBatch b, const nc_scale_state* __restrict__ st, const nc_loss
     // hardware converts while 2^-K is an fp32 value (uniform branch); a full
     // tile at a scale beyond that (a loss-scale unscale far outside the
     // usual range) runs per element, like a ragged one
-    sr_full_hw<FMT, DT, U>(v, e0, p, __builtin_amdgcn_ldexpf(1.0f, -K), sr_pre(key), acc, dst);
+    sr_full_hw<FMT, DT, U>(v, e0, p, c2, __builtin_amdgcn_ldexpf(1.0f, -K), sr_pre(key), sr_fix_region<FMT, DT>(K),
+                           acc, dst);
   } else {
     for (int base = 0; base < rem; base += kThreads) {
       const int i = base + (int)threadIdx.x;

@@ -54,6 +54,51 @@ def test_sr_parity(dtype, name, fmt, k, s):
     assert counts[0]["amax"] == wn["amax"]
 
 
+def _round_up_to_bits(v: int, bits: int) -> int:
+    """The least integer >= v with at most `bits` significant bits."""
+    e = max(v.bit_length() - bits, 0)
+    return -(-v >> e) << e if v % (1 << e) else v
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("name,fmt", FMTS)
+@pytest.mark.parametrize("k", [0, -40, 60])
+def test_sr_fraction_finer_than_the_converts_resolve(dtype, name, fmt, k):
+    """Values placed where the rule rounds up by less than the hardware
+    converts resolve.  For a fixed seed and offset every element's uniform u
+    is known (oracle.rng); element i gets y = |x| 2^k = t q below the smallest
+    subnormal q with t 2^32 the least value above u that x's format holds
+    (24 significant bits for fp32, 8 for bf16), so the rule rounds it up to
+    q, while t has more fractional bits than the converts keep.  bf16 values
+    this small exist only where u < 2^(MB + 16); the other elements get
+    ordinary values.  Every code and count against the oracle."""
+    n = 1 << 21 if dtype == "bf16" else 1 << 18
+    seed, offset = 0x5EED5EED12345678, 0x9ABCDEF012
+    u = rng.sr_uniforms(seed, offset, 0, n).astype(np.int64)
+    qe = fmt.emin - fmt.mbits                      # log2 of the smallest subnormal
+    bits = 8 if dtype == "bf16" else 24
+    r = np.random.default_rng(61)
+    x = (r.standard_normal(n) * 10.0 ** r.uniform(-3, 3, n)) * 2.0 ** -k
+    pick = np.nonzero(u < (1 << (fmt.mbits + 16)))[0] if dtype == "bf16" else np.arange(n)
+    tv = np.array([_round_up_to_bits(int(v) + 1, bits) for v in u[pick]], dtype=np.float64)
+    sign = np.where(r.random(pick.size) < 0.5, -1.0, 1.0)
+    x[pick] = sign * np.ldexp(tv, qe - 32 - k)
+    if dtype == "bf16":
+        hb = workloads.to_bf16_bits(x)
+        assert np.array_equal(bulk.bf16_bits_to_f64(hb)[pick], x[pick])   # placed values are exact
+        xd, x64 = dev_bf16(hb), bulk.bf16_bits_to_f64(hb)
+    else:
+        x32 = x.astype(np.float32)
+        assert np.array_equal(x32[pick].astype(np.float64), x[pick])
+        xd, x64 = dev_f32(x32), x32.astype(np.float64)
+    codes, counts = _sr([xd], name, [k], seed, offset)
+    wc, wn = bulk.cast_tensor_sr_f64(fmt, x64, k, 0, seed, offset, 0)
+    assert pick.size > 100
+    assert np.all(wc[pick] & 0x7F == 1)            # the rule rounds every placed value up to q
+    assert np.array_equal(codes[0], wc)
+    assert_counts(counts[0], wn)
+
+
 @pytest.mark.parametrize("name,fmt", FMTS)
 @pytest.mark.parametrize("k,s", [(127, 0), (120, 0), (64, 0), (0, 0), (-60, 0), (-127, 0), (-120, 16)])
 def test_sr_every_bf16_pattern(name, fmt, k, s):
