@@ -70,6 +70,71 @@ def test_fp32_boundaries_and_random_patterns(name, fmt):
         assert_counts(n, want_n)
 
 
+def _near_ties(fmt):
+    """Every code magnitude and every midpoint between neighbours, each with
+    its fp32 neighbours at the unit scale: the values a rounding that keeps
+    too few fraction bits would get wrong (a tie moved by the last fp32 bit)."""
+    mags = sorted({float(fmt.decode(c).mag) for c in range(128) if fmt.decode(c).kind == "num"})
+    return np.array(mags + [(a + b) / 2 for a, b in zip(mags, mags[1:])])
+
+
+@pytest.mark.parametrize("name,fmt", FMTS)
+def test_fp32_near_ties_at_every_third_scale(name, fmt):
+    """The per-tensor cast of fp32 values one last bit either side of every
+    tie and grid point, at every third exponent K from -130 to 130 (one
+    tensor per K, in batches of 64): the scaled converts must round on the
+    exact product, the last bit included."""
+    pts = _near_ties(fmt)
+    xs, Ks = [], []
+    for K in range(-130, 131, 3):
+        with np.errstate(over="ignore", under="ignore"):
+            v = np.ldexp(pts, -K).astype(np.float32)
+        v = v[np.isfinite(v) & (v > 0)]
+        nb = np.concatenate([np.nextafter(v, np.float32(0)), v, np.nextafter(v, np.float32(np.inf))])
+        xs.append(np.concatenate([nb, -nb]))
+        Ks.append(K)
+    codes, counts = _cast_pt([dev_f32(x) for x in xs], Ks, name)
+    for K, x, c, n in zip(Ks, xs, codes, counts):
+        want_c, want_n = _expect_pt(fmt, x.astype(np.float64), K)
+        bad = np.flatnonzero(c != want_c)
+        assert bad.size == 0, (K, [(x[i], hex(c[i]), hex(want_c[i])) for i in bad[:5]])
+        assert_counts(n, want_n)
+
+
+@pytest.mark.parametrize("rule", ["ocp", "plus1", "ceil"])
+@pytest.mark.parametrize("name,fmt", FMTS)
+def test_mx_fp32_near_ties_at_every_block_exponent(name, fmt, rule):
+    """MX blocks of fp32 values one last bit either side of every tie and
+    grid point of the block's scale, one block exponent per block over
+    X = -120 .. 126 - emax: the first element of each block fixes X (its amax
+    1.5 2^(X + emax), which every rule maps to X or X + 1), the other 31
+    are near-ties below it (X up to 126 - emax keeps the amax finite);
+    codes, scale bytes and counts against the oracle."""
+    pts = _near_ties(fmt)
+    r = np.random.default_rng(5)
+    blocks = []
+    for X in range(-120, 127 - fmt.emax):
+        a = np.float32(np.ldexp(1.5, X + fmt.emax))
+        with np.errstate(over="ignore", under="ignore"):
+            v = np.ldexp(pts, X).astype(np.float32)
+        nb = np.concatenate([np.nextafter(v, np.float32(0)), v, np.nextafter(v, np.float32(np.inf))])
+        nb = nb[(nb > 0) & (nb < a)]
+        for i in range(0, nb.size, 31):
+            chunk = nb[i:i + 31]
+            blk = np.concatenate([[a], chunk, np.zeros(31 - chunk.size, np.float32)]).astype(np.float32)
+            blk[1:] *= np.where(r.random(31) < 0.5, -1, 1).astype(np.float32)
+            blocks.append(blk)
+    x = np.concatenate(blocks).astype(np.float32)
+    cols = 32 * 64
+    x = np.concatenate([x, np.zeros((-x.size) % cols, np.float32)])
+    codes, scales, counts = _cast_mx(dev_f32(x), cols, name, rule)
+    wc, ws, wn = bulk.cast_mx_f64(fmt, x.astype(np.float64), cols, rule)
+    assert np.array_equal(scales, ws)
+    bad = np.flatnonzero(codes != wc)
+    assert bad.size == 0, [(x[i], hex(codes[i]), hex(wc[i])) for i in bad[:5]]
+    assert_counts(counts, wn)
+
+
 @pytest.mark.parametrize("name,fmt", FMTS)
 def test_all_code_pairs_products_and_sums(name, fmt, consts):
     """The exhaustive 65,536-pair self-check on the GPU: every exact product
