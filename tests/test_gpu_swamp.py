@@ -39,14 +39,16 @@ def _random_pairs(n, seed):
 
 def _grid_and_ties(fmt):
     """Every finite narrow-format pattern as a weight (and the fp32 midpoints
-    between neighbours, where the rounding of w itself ties), each with
-    updates of half a gap up, half (or a quarter) a gap down, and just
-    around them."""
+    between neighbours, where the rounding of w itself ties, with their fp32
+    neighbours, where it must not), each with updates of half a gap up, half
+    (or a quarter) a gap down, and just around them."""
     if fmt is FP16:
         g = np.arange(0, 0x7C00, dtype=np.uint16).view(np.float16).astype(np.float64)
     else:
         g = bulk.bf16_bits_to_f64(np.arange(0, 0x7F80, dtype=np.uint16))
-    mids = ((g[:-1] + g[1:]) / 2).astype(np.float32).astype(np.float64)
+    mids = ((g[:-1] + g[1:]) / 2).astype(np.float32)
+    near = np.concatenate([np.nextafter(mids, np.float32(0)), np.nextafter(mids, np.float32(np.inf))])
+    mids = np.concatenate([mids, near]).astype(np.float64)
     w = np.concatenate([g, -g, mids, -mids]).astype(np.float32)
     wf = swamp._round_to(fmt, w.astype(np.float64))
     a = np.abs(wf)
