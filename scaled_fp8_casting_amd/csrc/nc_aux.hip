@@ -308,7 +308,7 @@ k_stats(const SegBatch b, const nc_scale_state* __restrict__ st,
   typedef typename CodeVec<DT>::T CT;
   constexpr int NSC = MX ? (int)(TILE / 32) : 16;        // scale bytes of a full tile
   __shared__ double tab[256];
-  __shared__ double lds_st[kRows * 6];
+  __shared__ double lds_st[kStatLds];
   __shared__ __align__(16) uint8_t lds_sc[NSC];
   const int64_t tile = xcd_tile<32>();
   const int s = seg_of(b.tile0, b.count, tile);
@@ -409,7 +409,7 @@ __device__ __forceinline__ void stats_col_row(u32x4 v, u32x2 w, const double* ta
   for (int i = 0; i < VC; ++i) {
     if (!FINITE && (xb[i] & kAbsMask) > kMaxFinite) continue;
     const uint32_t q = ((i < 4 ? w.x : w.y) >> (8 * (i % 4))) & 0xFFu;
-    stat_term((double)__uint_as_float(xb[i]), tab[q] * blk[i], sa);
+    stat_term_blk((double)__uint_as_float(xb[i]), tab[q], blk[i], sa);
   }
 }
 
@@ -419,7 +419,7 @@ k_stats_col(const SegBatch b, const Tail t) {
   constexpr int VC = In<DT>::VEC, R = kStatsColRows;
   constexpr int Q = 8;                      // rows per batch of loads
   __shared__ double tab[256];
-  __shared__ double lds_st[kRows * 6];
+  __shared__ double lds_st[kStatLds];
   const int64_t tile = xcd_tile<32>();
   const int s = seg_of(b.tile0, b.count, tile);
   const Seg& g = b.s[s];

@@ -90,7 +90,7 @@ k_cast_pt(const SegBatch b, const nc_scale_state* __restrict__ st,
   constexpr int U = cast_vecs<STATS>();
   constexpr int64_t TILE = (int64_t)kThreads * VEC * U;
   __shared__ uint32_t lds[kRows * 4];
-  __shared__ double lds_st[STATS ? kRows * 6 : 1];
+  __shared__ double lds_st[STATS ? kStatLds : 1];
   __shared__ double tab[STATS ? 256 : 1];
   const int64_t tile = xcd_tile<256>();
   const int s = seg_of_scan(b.tile0, b.count, tile);
@@ -725,7 +725,7 @@ k_cast_mx(const SegBatch b, const Tail t) {
   constexpr int U = cast_vecs<STATS>();
   constexpr int64_t TILE = (int64_t)kThreads * VEC * U;
   __shared__ uint32_t lds[kRows * 4];
-  __shared__ double lds_st[STATS ? kRows * 6 : 1];
+  __shared__ double lds_st[STATS ? kStatLds : 1];
   __shared__ double tab[STATS ? 256 : 1];
   const int64_t tile = xcd_tile<256>();
   const int s = seg_of_scan(b.tile0, b.count, tile);
@@ -773,7 +773,7 @@ k_cast_mx_col(const SegBatch b, const Tail t) {
   constexpr int SPLIT = col_cast_split(DT), RL = 32 / SPLIT, SLOTS = kThreads / SPLIT;
   static_assert(SPLIT == 1 || SPLIT == 2, "lanes per slot");
   __shared__ uint32_t lds[kRows * 4];
-  __shared__ double lds_st[STATS ? kRows * 6 : 1];
+  __shared__ double lds_st[STATS ? kStatLds : 1];
   __shared__ double tab[STATS ? 256 : 1];
   const int64_t tile = xcd_tile<1>();
   const int s = seg_of(b.tile0, b.count, tile);
@@ -877,7 +877,7 @@ k_cast_mx_col(const SegBatch b, const Tail t) {
 #pragma unroll
       for (int i = 0; i < VC; ++i) {
         if (!clean && (xb[i] & kAbsMask) > kMaxFinite) continue;
-        stat_term((double)__uint_as_float(xb[i]), tab[(w >> (8 * i)) & 0xFFu] * pow2_f64(X[i]), sa);
+        stat_term_blk((double)__uint_as_float(xb[i]), tab[(w >> (8 * i)) & 0xFFu], pow2_f64(X[i]), sa);
       }
     }
     // the row's counts are taken here: left alone, the compiler sinks every

@@ -407,12 +407,6 @@ __device__ __forceinline__ uint32_t row_sum_u32(uint32_t v) {
   v += dpp_u32<0x141>(v);
   return v + dpp_u32<0x140>(v);
 }
-__device__ __forceinline__ double row_sum_f64(double v) {
-  v += dpp_f64<0xB1>(v);
-  v += dpp_f64<0x4E>(v);
-  v += dpp_f64<0x141>(v);
-  return v + dpp_f64<0x140>(v);
-}
 constexpr int kRows = kThreads / 16;    // 16-lane rows per workgroup
 
 // ---------------------------------------------------------------------------
@@ -727,6 +721,20 @@ __device__ __forceinline__ void stat_term(double x, double xh, StatAcc& a) {
   a.s[5] = fma(x, x, a.s[5]);
 }
 
+// The same for an MX element, xhat = t * blk with blk = 2^X: the product is
+// exact in binary64 (|t| in [2^-16, 2^16], |X| <= 128), so an fma that takes
+// it rounds once, as the difference of the product does -- the same sums
+// with one operation fewer.
+__device__ __forceinline__ void stat_term_blk(double x, double t, double blk, StatAcc& a) {
+  const double e = fma(t, blk, -x);
+  a.s[0] += e;
+  a.s[1] += fabs(e);
+  a.s[2] = fma(e, e, a.s[2]);
+  a.s[3] += fma(fabs(t), blk, -fabs(x));
+  a.s[4] = fma(x, e, a.s[4]);
+  a.s[5] = fma(x, x, a.s[5]);
+}
+
 // Terms of VEC elements (fp32 patterns xb, codes q); xhat = tab[q] (* blk
 // for MX, the block's 2^X).  FINITE: the caller knows every x is finite (no
 // test); otherwise Inf/NaN elements are skipped.
@@ -736,8 +744,8 @@ __device__ __forceinline__ void stats_vec(const uint32_t* xb, const uint32_t* q,
 #pragma unroll
   for (int i = 0; i < VEC; ++i) {
     if (!FINITE && (xb[i] & kAbsMask) > kMaxFinite) continue;
-    const double xh = MX ? tab[q[i]] * blk : tab[q[i]];
-    stat_term((double)__uint_as_float(xb[i]), xh, a);
+    if constexpr (MX) stat_term_blk((double)__uint_as_float(xb[i]), tab[q[i]], blk, a);
+    else stat_term((double)__uint_as_float(xb[i]), tab[q[i]], a);
   }
 }
 
@@ -748,46 +756,72 @@ __device__ __forceinline__ bool stats_all_finite(const StatAcc& a) {
   return __builtin_isfinite(a.s[5]);
 }
 
-// The workgroup's six partial sums -> its slot: DPP row sums, one LDS entry
-// per row, then thread j (< 6) adds the rows in index order -- a fixed
-// order, so the sums are reproducible.  Called by all threads (full EXEC);
-// lds holds kRows * 6 doubles.
-__device__ inline void write_stat_slot(const StatAcc& a, double* slot, double* lds) {
+// The workgroup's six partial sums, in a fixed order (so the sums are
+// reproducible): every thread stores its six sums in LDS, sum-major; after a
+// barrier lane 8j + r of wave 0 (j < 6, r < 8) adds sum j of threads r,
+// r + 8, ..., r + 248 in four interleaved chains, then the eight lanes of
+// each group combine their partials by three DPP steps inside the group
+// (quad_perm [1,0,3,2], quad_perm [2,3,0,1], row_half_mirror); each step adds
+// two equal partial sums in either order, so every lane of the group ends
+// with the same value.  Lanes 48..63 repeat group 5 to keep EXEC full for the
+// DPP moves.  A workgroup spends about 60 VALU instructions here, against
+// about 120 per wave for six 16-lane DPP sums.
+constexpr int kStatStride = kThreads + 8;   // doubles per sum: the groups' reads start 64 bytes apart in the banks
+constexpr int kStatLds = 6 * kStatStride;   // doubles of LDS the stat sums take
+
+__device__ __forceinline__ void stat_store(const StatAcc& a, double* lds) {
 #pragma unroll
-  for (int j = 0; j < 6; ++j) {
-    const double v = row_sum_f64(a.s[j]);
-    if ((threadIdx.x & 15) == 0) lds[(threadIdx.x >> 4) * 6 + j] = v;
+  for (int j = 0; j < 6; ++j) lds[j * kStatStride + threadIdx.x] = a.s[j];
+}
+
+// Wave 0, full EXEC, after the barrier that follows stat_store: sum j of the
+// workgroup in lanes 8j..8j+7.
+__device__ __forceinline__ double stat_sum_wave0(const double* lds) {
+  const int lane = threadIdx.x & 63;
+  const double* p = lds + min(lane >> 3, 5) * kStatStride + (lane & 7);
+  double c[4];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) c[k] = p[8 * k];
+#pragma unroll
+  for (int i = 4; i < kThreads / 8; i += 4) {
+#pragma unroll
+    for (int k = 0; k < 4; ++k) c[k] += p[8 * (i + k)];
   }
+  double t = (c[0] + c[1]) + (c[2] + c[3]);
+  t += dpp_f64<0xB1>(t);
+  t += dpp_f64<0x4E>(t);
+  return t + dpp_f64<0x141>(t);
+}
+
+// The workgroup's six partial sums -> its slot.  Called by all threads (full
+// EXEC); lds holds kStatLds doubles.
+__device__ inline void write_stat_slot(const StatAcc& a, double* slot, double* lds) {
+  stat_store(a, lds);
   __syncthreads();
-  if (threadIdx.x < 6) {
-    double t = 0.0;
-    for (int r = 0; r < kRows; ++r) t += lds[r * 6 + threadIdx.x];
-    slot[threadIdx.x] = t;
+  if (threadIdx.x < 64) {
+    const double v = stat_sum_wave0(lds);
+    if ((threadIdx.x & 7) == 0 && threadIdx.x < 48) slot[threadIdx.x >> 3] = v;
   }
 }
 
-// The casts with fused statistics: both slots in one epilogue (one LDS
-// round trip and one barrier instead of two).  lds holds kRows * 4 words,
-// lds_st kRows * 6 doubles.
+// The casts with fused statistics: both slots in one epilogue, one barrier.
+// lds holds kWaves * 3 words, lds_st kStatLds doubles.  Wave 0 adds the
+// statistics, thread 64 the counts beside it.
 __device__ inline void write_count_stat_slots(Acc acc, const StatAcc& a, CountSlot* slot, double* stat_slot,
                                               uint32_t* lds, double* lds_st) {
   const WaveCounts w = wave_counts(acc);
-  double v[6];
-#pragma unroll
-  for (int j = 0; j < 6; ++j) v[j] = row_sum_f64(a.s[j]);
   if ((threadIdx.x & 63) == 0) {
     const int i = threadIdx.x >> 6;
     lds[i * 3 + 0] = w.amax;
     lds[i * 3 + 1] = w.big_uf;
     lds[i * 3 + 2] = w.n_nf;
   }
-  if ((threadIdx.x & 15) == 0) {
-    const int r = threadIdx.x >> 4;
-#pragma unroll
-    for (int j = 0; j < 6; ++j) lds_st[r * 6 + j] = v[j];
-  }
+  stat_store(a, lds_st);
   __syncthreads();
-  if (threadIdx.x == 0) {
+  if (threadIdx.x < 64) {
+    const double v = stat_sum_wave0(lds_st);
+    if ((threadIdx.x & 7) == 0 && threadIdx.x < 48) stat_slot[threadIdx.x >> 3] = v;
+  } else if (threadIdx.x == 64) {
     CountSlot c{0u, 0u, 0u, 0u};
 #pragma unroll
     for (int i = 0; i < kWaves; ++i) {
@@ -797,11 +831,6 @@ __device__ inline void write_count_stat_slots(Acc acc, const StatAcc& a, CountSl
       c.n_nf += lds[i * 3 + 2];
     }
     *slot = c;
-  } else if (threadIdx.x >= 64 && threadIdx.x < 70) {   // another wave: the sums run beside thread 0's
-    const int j = threadIdx.x - 64;
-    double t = 0.0;
-    for (int r = 0; r < kRows; ++r) t += lds_st[r * 6 + j];
-    stat_slot[j] = t;
   }
 }
 
