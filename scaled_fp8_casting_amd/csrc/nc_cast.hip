@@ -394,19 +394,21 @@ __device__ __forceinline__ uint32_t sr4_soft(const uint32_t* xb, int K, int c2, 
 // (scale 2^-K, |K| <= 127).  Counts: a drawn zero of a nonzero finite input
 // is an underflow, and a zero input always gives a zero code, so underflows
 // are the zero codes less the zero inputs (non-finite inputs never give a
-// zero code).  Saturation and the clip counts run only in a wave whose
-// vector holds an element above the clip bound (uniform branch).
+// zero code).  The zero inputs are counted only in a wave whose vector holds
+// one (uniform branch, rare).  Saturation and the clip counts run only in a
+// wave whose vector holds an element above the clip bound (uniform branch).
 template <int FMT, int DT, int U>
 __device__ __forceinline__ void sr_full_hw(const u32x4* v, int64_t e0, const CastParams& p, int c2, float scale,
                                            const SrPre& pre, const SrFix& fx, Acc& acc, uint8_t* dst) {
   constexpr int VEC = In<DT>::VEC;
-  uint32_t zc = 0, nz = 0;     // zero codes, nonzero inputs (per lane)
-  u16x2 nz16 = {0, 0};
+  uint32_t zc = 0, n0 = 0;     // zero codes, zero inputs (per lane)
+  // Philox block of a lane's first element: element index / 4 (< 2^32, as
+  // the element index is < 2^34; e0 is a multiple of the tile)
+  const uint32_t blk0 = (uint32_t)(e0 >> 2) + threadIdx.x * (uint32_t)(VEC / 4);
 #pragma unroll
   for (int u = 0; u < U; ++u) {
     const int vi = u * kThreads + threadIdx.x;
-    // element index < 2^34, so its block index fits 32 bits
-    const uint32_t blk = (uint32_t)((e0 + (int64_t)vi * VEC) >> 2);
+    const uint32_t blk = blk0 + (uint32_t)(u * kThreads * (VEC / 4));
     uint32_t xb[VEC], w[VEC / 4], nr[VEC];
     unpack<DT>(v[u], xb);
 #pragma unroll
@@ -417,39 +419,10 @@ __device__ __forceinline__ void sr_full_hw(const u32x4* v, int64_t e0, const Cas
 #pragma unroll
       for (int i = 0; i < 4; ++i) nr[4 * j + i] = q[i];
     }
-    uint32_t m = 0;
-    u16x2 h[4];
-    bool fix;                                    // some element needs the software rule
-    if constexpr (DT == NC_BF16) {               // packed 16-bit magnitudes
-      h[0] = mag16(v[u].x); h[1] = mag16(v[u].y); h[2] = mag16(v[u].z); h[3] = mag16(v[u].w);
-      const u16x2 hm = __builtin_elementwise_max(__builtin_elementwise_max(h[0], h[1]),
-                                                 __builtin_elementwise_max(h[2], h[3]));
-      m = (uint32_t)max(hm.x, hm.y) << 16;
-      const u16x2 one = {1, 1};
-#pragma unroll
-      for (int j = 0; j < 4; ++j) nz16 += __builtin_elementwise_min(h[j], one);
-      // far below the grid only an element whose u < 2^(MB + 16) can
-      // differ: screen on the vector's largest complemented word, about one
-      // element in 2^(16 - MB) passes
-      uint32_t nmax = nr[0];
-#pragma unroll
-      for (int i = 1; i < VEC; ++i) nmax = max(nmax, nr[i]);
-      fix = false;
-      if (__ballot(nmax >= fx.nr_min) != 0) {    // wave-uniform
-#pragma unroll
-        for (int i = 0; i < VEC; ++i) fix |= fx.in(xb[i] & kAbsMask) && nr[i] >= fx.nr_min;
-      }
-    } else {
-      uint32_t mn = ~0u;                         // least magnitude less one (zeros wrap)
-#pragma unroll
-      for (int i = 0; i < VEC; ++i) {
-        m = max(m, xb[i] & kAbsMask);
-        mn = min(mn, (xb[i] & kAbsMask) - 1u);
-        nz += min(xb[i] & kAbsMask, 1u);
-      }
-      fix = mn < fx.thr - 1u;
-    }
-    if (__ballot(fix) != 0) {                    // wave-uniform: the software rule for the region
+    // the software rule for the elements of the region, where some element
+    // of the wave's vector needs it (wave-uniform)
+    auto fix_region = [&](bool fix) {
+      if (__ballot(fix) == 0) return;
 #pragma unroll
       for (int j = 0; j < VEC / 4; ++j) {
         const uint32_t sw = sr4_soft<FMT>(xb + 4 * j, p.K, c2, nr + 4 * j);
@@ -457,6 +430,52 @@ __device__ __forceinline__ void sr_full_hw(const u32x4* v, int64_t e0, const Cas
 #pragma unroll
         for (int i = 0; i < 4; ++i) sel |= (fx.in(xb[4 * j + i] & kAbsMask) ? 0xFFu : 0u) << (8 * i);
         w[j] = (w[j] & ~sel) | (sw & sel);
+      }
+    };
+    uint32_t m = 0;
+    if constexpr (DT == NC_BF16) {               // packed 16-bit magnitudes
+      const u16x2 h[4] = {mag16(v[u].x), mag16(v[u].y), mag16(v[u].z), mag16(v[u].w)};
+      const u16x2 hm = __builtin_elementwise_max(__builtin_elementwise_max(h[0], h[1]),
+                                                 __builtin_elementwise_max(h[2], h[3]));
+      const u16x2 hn = __builtin_elementwise_min(__builtin_elementwise_min(h[0], h[1]),
+                                                 __builtin_elementwise_min(h[2], h[3]));
+      m = (uint32_t)max(hm.x, hm.y) << 16;
+      if (__ballot(min(hn.x, hn.y) == 0) != 0) {    // wave-uniform: exact zeros
+        const u16x2 one = {1, 1};
+        u16x2 z = {0, 0};
+#pragma unroll
+        for (int j = 0; j < 4; ++j) z += one - __builtin_elementwise_min(h[j], one);
+        n0 += (uint32_t)z.x + z.y;
+      }
+      // far below the grid only an element whose u < 2^(MB + 16) can
+      // differ: screen on the vector's largest complemented word, about one
+      // element in 2^(16 - MB) passes
+      uint32_t nmax = nr[0];
+#pragma unroll
+      for (int i = 1; i < VEC; ++i) nmax = max(nmax, nr[i]);
+      if (__ballot(nmax >= fx.nr_min) != 0) {    // wave-uniform
+        bool fix = false;
+#pragma unroll
+        for (int i = 0; i < VEC; ++i) fix |= fx.in(xb[i] & kAbsMask) && nr[i] >= fx.nr_min;
+        fix_region(fix);
+      }
+    } else {
+      uint32_t mn = ~0u;                         // least magnitude
+#pragma unroll
+      for (int i = 0; i < VEC; ++i) {
+        m = max(m, xb[i] & kAbsMask);
+        mn = min(mn, xb[i] & kAbsMask);
+      }
+      if (__ballot(mn == 0u) != 0) {             // wave-uniform: exact zeros
+        bool fix = false;
+#pragma unroll
+        for (int i = 0; i < VEC; ++i) {
+          n0 += (xb[i] & kAbsMask) == 0u ? 1u : 0u;
+          fix |= fx.in(xb[i] & kAbsMask);
+        }
+        fix_region(fix);
+      } else {
+        fix_region(mn < fx.thr);                 // every magnitude nonzero here
       }
     }
 #pragma unroll
@@ -479,8 +498,7 @@ __device__ __forceinline__ void sr_full_hw(const u32x4* v, int64_t e0, const Cas
     if constexpr (DT == NC_F32) st_stream(reinterpret_cast<uint32_t*>(dst) + vi, w[0]);
     else st_stream(reinterpret_cast<u32x2*>(dst) + vi, u32x2{w[0], w[1]});
   }
-  if constexpr (DT == NC_BF16) nz = (uint32_t)nz16.x + nz16.y;
-  acc.n_uf += zc - ((uint32_t)(U * VEC) - nz);
+  acc.n_uf += zc - n0;
 }
 
 template <int FMT, int DT>
