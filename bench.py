@@ -22,7 +22,9 @@ statistics with blocks down the columns, the update/step-ratio monitor on
 2^30 fp32 weights and updates (counts only, and with a flag byte per
 element), torch's device copy of the cast's byte count, and one
 delayed-scaling step of loss-scaled Llama-7B-shaped fp32 gradients (225
-tensors, 6.6G elements, fused 2^-16 unscale).  Under "configs" it times the
+tensors, 6.6G elements, fused 2^-16 unscale).  `step_fused_stats` times the
+same step with the statistics fused into the two casts (steps 1-6 with
+statistics, no passes 7-8): the same outputs in fewer bytes.  Under "configs" it times the
 three smaller workloads on their own (last-level cache flushed before each
 rep): 65,536 fp32 elements under current scaling (microseconds, launch-bound),
 the 4096 x 4096 tanh bf16 matrix to MXFP8 under the OCP, +1 and ceil rules, and one
@@ -429,6 +431,44 @@ def small_configs(nc, torch, workloads):
     return res
 
 
+def fused_step(a, torch, nc, bufs, t, sep):
+    """The step's outputs with the statistics fused into the two casts instead
+    of two separate statistics passes: amax, scale update, both casts with
+    statistics, both dequants.  Timed like the step (after two untimed
+    steps); its statistics are compared with `sep`, those of the separate
+    passes in the last timed step (same input, same scale)."""
+    n = t["x"].numel()
+
+    def step():
+        for b in ("am", "cpt", "cmx", "spt", "smx"):
+            bufs[b].zero_()
+        nc.nc_amax([t["x"]], bufs["am"], ws=t["ws"])
+        nc.nc_scale_update(t["pol"], bufs["st"], bufs["am"])
+        nc.nc_cast_tensor([t["x"]], [t["codes_pt"]], "e4m3", bufs["st"], bufs["cpt"], stats=bufs["spt"],
+                          ws=t["ws"])
+        nc.nc_cast_mx([t["x"]], [t["codes_mx"]], [t["scales"]], [COLS], "e4m3", "ocp", bufs["cmx"],
+                      stats=bufs["smx"], ws=t["ws"])
+        nc.nc_dequant([t["codes_pt"]], [t["y_pt"]], "e4m3", st=bufs["st"])
+        nc.nc_dequant([t["codes_mx"]], [t["y_mx"]], "e4m3", scales=[t["scales"]], cols=[COLS])
+
+    for _ in range(2):
+        step()
+    torch.cuda.synchronize()
+    k = max(1, min(a.steps, 10))
+    t0 = time.perf_counter()
+    for _ in range(k):
+        step()
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / k
+    rel = max(float(((f - s).abs() / s.abs().clamp_min(1e-300)).max())
+              for f, s in zip((bufs["spt"], bufs["smx"]), sep))
+    nbytes = 2 * n + 3 * n + (3 * n + n // 32) + 3 * n + (3 * n + n // 32)
+    return dict(ms_per_step=round(ms, 4), gelem_s=round(n / (ms * 1e-3) / 1e9, 3), steps=k,
+                step_bytes=nbytes, frac_of_peak=round(nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
+                stats_max_rel_diff_vs_passes=rel,
+                calls="amax, scale update, cast_tensor + statistics, cast_mx + statistics, dequant x2")
+
+
 def main():
     a = parse()
     if a.write_traffic:
@@ -519,6 +559,7 @@ def main():
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms_per_step = wall * 1e3 / a.steps
+    sep_stats = [bufs["spt"].clone(), bufs["smx"].clone()]   # the last step's statistics passes
     per = {nm: float(np.mean([evs[s][i][0].elapsed_time(evs[s][i][1]) for s in range(a.steps)]))
            for i, nm in enumerate(names)}
     kernels = {}
@@ -606,6 +647,9 @@ def main():
         out["beside_step"][nm] = dict(ms=round(ms, 4), gbps=round(gbps, 1), frac=round(gbps / HBM_PEAK_GBPS, 4),
                                       gelem_s=round(n / (ms * 1e-3) / 1e9, 2), traffic=traffic_for(nm, src))
     extras.clear()
+    out["step_fused_stats"] = fused_step(a, torch, nc, bufs, dict(
+        x=x, codes_pt=codes_pt, codes_mx=codes_mx, scales=scales, y_pt=y_pt, y_mx=y_mx, ws=ws, pol=pol),
+        sep_stats)
     # the update/step-ratio monitor on its own workload: 2^30 fp32 weights and
     # updates (8 GiB read), bf16 weight copies, counts only
     del y_pt, y_mx
