@@ -76,13 +76,17 @@ __device__ __forceinline__ SwampCls swamp_classify(uint32_t wb, uint32_t db) {
 }
 
 // Flag byte of one element: bit 0 below, 1 no-op, 2 zero update, 3 excluded.
-// below and no-op are counted over considered elements (finite, nonzero d).
+// below and no-op are counted over considered elements (finite, nonzero d),
+// so the byte is 8 for an excluded element, else 4 for a zero update, else
+// below | no-op << 1.  Returned in byte `pos` of a word (three selects on the
+// compares' own results, no boolean arithmetic).
 template <int WF>
-__device__ __forceinline__ uint32_t swamp_flags(uint32_t wb, uint32_t db) {
+__device__ __forceinline__ uint32_t swamp_flags(uint32_t wb, uint32_t db, int pos = 0) {
   const SwampCls c = swamp_classify<WF>(wb, db);
-  const bool cons = !c.excl && !c.zero;
-  return (c.below && cons ? 1u : 0u) | (c.noop && cons ? 2u : 0u) | (c.zero && !c.excl ? 4u : 0u) |
-         (c.excl ? 8u : 0u);
+  const int sh = 8 * pos;
+  uint32_t f = (c.below ? 1u << sh : 0u) + (c.noop ? 2u << sh : 0u);
+  f = c.zero ? 4u << sh : f;
+  return c.excl ? 8u << sh : f;
 }
 
 struct SwampAcc {
@@ -151,7 +155,9 @@ k_swamp(const SegBatch b, uint4* __restrict__ slots) {
   constexpr int U = kSwampVecs;
   constexpr int64_t TILE = kSwampTile;
   __shared__ uint32_t lds[kRows * 4];
-  const int64_t tile = xcd_tile<32>();
+  // tile order (measured): 32 tiles per XCD in turn for the counts, 256 with
+  // flag bytes
+  const int64_t tile = FLAGS ? xcd_tile<256>() : xcd_tile<32>();
   const int s = seg_of(b.tile0, b.count, tile);
   const Seg& g = b.s[s];
   const int64_t e0 = (tile - b.tile0[s]) * TILE;
@@ -167,18 +173,26 @@ k_swamp(const SegBatch b, uint4* __restrict__ slots) {
 #pragma unroll
     for (int u = 0; u < U; ++u) d[u] = ld_stream(dv + u * kThreads + threadIdx.x);
     __builtin_amdgcn_sched_barrier(0);
+    uint32_t fw[FLAGS ? U : 1];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       if constexpr (FLAGS) {
-        const uint32_t f = swamp_flags<WF>(w[u].x, d[u].x) | swamp_flags<WF>(w[u].y, d[u].y) << 8 |
-                           swamp_flags<WF>(w[u].z, d[u].z) << 16 | swamp_flags<WF>(w[u].w, d[u].w) << 24;
-        acc.add4(f);
-        if (fl) st_stream(reinterpret_cast<uint32_t*>(fl) + u * kThreads + threadIdx.x, f);
+        fw[u] = swamp_flags<WF>(w[u].x, d[u].x, 0) | swamp_flags<WF>(w[u].y, d[u].y, 1) |
+                swamp_flags<WF>(w[u].z, d[u].z, 2) | swamp_flags<WF>(w[u].w, d[u].w, 3);
+        acc.add4(fw[u]);
       } else {
         acc.add_wave<WF>(w[u].x, d[u].x);
         acc.add_wave<WF>(w[u].y, d[u].y);
         acc.add_wave<WF>(w[u].z, d[u].z);
         acc.add_wave<WF>(w[u].w, d[u].w);
+      }
+    }
+    // the tile's flag words go out together after its classification (5%
+    // faster than a store after each vector, measured)
+    if constexpr (FLAGS) {
+      if (fl) {
+#pragma unroll
+        for (int u = 0; u < U; ++u) st_stream(reinterpret_cast<uint32_t*>(fl) + u * kThreads + threadIdx.x, fw[u]);
       }
     }
   } else {
