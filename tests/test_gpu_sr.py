@@ -54,6 +54,38 @@ def test_sr_parity(dtype, name, fmt, k, s):
     assert counts[0]["amax"] == wn["amax"]
 
 
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("name,fmt", FMTS)
+@pytest.mark.parametrize("k", [0, -12])
+def test_sr_zero_inputs_in_some_waves(dtype, name, fmt, k):
+    """Exact zeros, which the underflow count takes off the zero codes, in
+    some waves only: scattered +-0, one lane's whole vector, a whole wave's
+    vector, and a tile with none; beside them values far below the grid
+    (where fp32 inputs take the exact rule)."""
+    vec = 4 if dtype == "f32" else 8              # elements per 16-byte vector
+    tile = 256 * vec * 8                          # full tile of the stochastic-rounding cast
+    n = 3 * tile + 1000
+    r = np.random.default_rng(4242 - k)
+    x = (r.standard_t(3, n) * 10.0 ** r.uniform(-7, 3, n)).astype(np.float32)
+    x[r.integers(0, n, n // 300)] = 0.0
+    x[r.integers(0, n, n // 300)] = -0.0
+    x[2 * tile: 3 * tile][x[2 * tile: 3 * tile] == 0] = 1.0     # tile 2: no zero at all
+    x[5 * vec: 6 * vec] = 0.0                                   # lane 5's first vector (tile 0)
+    x[tile + 64 * vec: tile + 128 * vec] = -0.0                 # wave 1's first vector (tile 1)
+    if dtype == "bf16":
+        bits = workloads.to_bf16_bits(x.astype(np.float64))
+        xd, x64 = dev_bf16(bits), bulk.bf16_bits_to_f64(bits)
+    else:
+        xd, x64 = dev_f32(x), x.astype(np.float64)
+    seed, offset = 0x243F6A8885A308D3, 17
+    codes, counts = _sr([xd], name, [k], seed, offset)
+    want, wn = bulk.cast_tensor_sr_f64(fmt, x64, k, 0, seed, offset, 0)
+    bad = np.flatnonzero(codes[0] != want)
+    assert bad.size == 0, [(int(i), x64[i], hex(codes[0][i]), hex(want[i])) for i in bad[:5]]
+    assert_counts(counts[0], wn)
+    assert wn["n_underflow"] > 0 and np.count_nonzero(x64 == 0) > 64 * vec
+
+
 def _round_up_to_bits(v: int, bits: int) -> int:
     """The least integer >= v with at most `bits` significant bits."""
     e = max(v.bit_length() - bits, 0)
