@@ -22,7 +22,7 @@ from tests._gpu import assert_counts, codes_like, dev_bf16, dev_f32, host_u8, ho
 pytestmark = pytest.mark.gpu
 FMTS = {"e4m3": E4M3, "e5m2": E5M2}
 OPS = ("amax", "cast", "cast_sr", "mx_rows", "mx_cols", "dequant", "stats")
-N_CASES = 140
+N_CASES = 300
 
 
 def _values(r, n, dtype):
