@@ -372,22 +372,32 @@ __device__ __forceinline__ SrFix sr_fix_region(int K) {
   return SrFix{thr, 0u - (1u << (F::MB + 16))};
 }
 
-// The rule in software for four elements (sr_value; every |x| 2^K here is
-// far below the largest finite value) from their complemented uniforms:
-// four codes, byte i = element i.
+// The rule in software for four elements of the region from their
+// complemented uniforms: four codes, byte i = element i (elements outside
+// the region give bytes the caller discards).  In the region y < 2^EMIN, so
+// the result is a subnormal code or the smallest normal one, on the grid of
+// q = 2^(EMIN - MB): with z = y / q = |x| 2^c2 (< 2^MB) the code's magnitude
+// is floor(z) + [u < ceil(frac(z) 2^32)].  z is exact where it is at least
+// 2^-126; below 2^-32 the threshold is 1 for any nonzero x, which raising z
+// to 2^-40 gives also where it rounded or underflowed (a nonzero element is
+// in the region).  floor, the difference, the scaling by 2^32 and ceil are
+// exact binary32 steps (sr_value, in the general form).
 template <int FMT>
-__device__ __forceinline__ uint32_t sr4_soft(const uint32_t* xb, int K, int c2, const uint32_t* nr) {
-  float v[4];
-  uint32_t sgn = 0;
+__device__ __forceinline__ uint32_t sr4_region(const uint32_t* xb, int c2, const uint32_t* nr) {
+  uint32_t w = 0;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    float m;
-    v[i] = sr_value<FMT>(xb[i] & kAbsMask, K, c2, ~nr[i], m);
-    sgn |= (xb[i] >> 31) << (8 * i + 7);
+    const float z = __builtin_fmaxf(__builtin_amdgcn_ldexpf(__uint_as_float(xb[i] & kAbsMask), c2), 0x1p-40f);
+    const float fl = __builtin_floorf(z);
+    // v_cvt_u32_f32 saturates (NaN -> 0): defined for a discarded element's
+    // Inf or NaN, where a C conversion would not be
+    uint32_t T, f;
+    __asm__("v_cvt_u32_f32 %0, %1" : "=v"(T) : "v"(__builtin_ceilf(__builtin_amdgcn_ldexpf(z - fl, 32))));
+    __asm__("v_cvt_u32_f32 %0, %1" : "=v"(f) : "v"(fl));
+    const uint32_t code = f + (~nr[i] < T ? 1u : 0u);
+    w |= ((code & 0x7Fu) | ((xb[i] >> 24) & 0x80u)) << (8 * i);
   }
-  int w = cvt_pair<FMT, false>(v[0], v[1], 0);
-  w = cvt_pair<FMT, true>(v[2], v[3], w);
-  return (uint32_t)w | sgn;
+  return w;
 }
 
 // A full tile of the stochastic-rounding cast with the hardware converts
@@ -425,7 +435,7 @@ __device__ __forceinline__ void sr_full_hw(const u32x4* v, int64_t e0, const Cas
       if (__ballot(fix) == 0) return;
 #pragma unroll
       for (int j = 0; j < VEC / 4; ++j) {
-        const uint32_t sw = sr4_soft<FMT>(xb + 4 * j, p.K, c2, nr + 4 * j);
+        const uint32_t sw = sr4_region<FMT>(xb + 4 * j, c2, nr + 4 * j);
         uint32_t sel = 0;
 #pragma unroll
         for (int i = 0; i < 4; ++i) sel |= (fx.in(xb[4 * j + i] & kAbsMask) ? 0xFFu : 0u) << (8 * i);
