@@ -550,3 +550,48 @@ def test_direct_counts_at_the_launch_threshold(dtype):
             assert_counts(got[i], want)
             assert got_am[i]["amax"] == want["amax"] and got_am[i]["n_nonfinite"] == want["n_nonfinite"], (sizes, i)
             assert got_am[i]["n_finite"] == want["n_finite"] and got_am[i]["n_clip"] == 0, (sizes, i)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("layout", ["tensor", "mx_rows", "mx_cols"])
+def test_fused_statistics_equal_the_separate_pass(dtype, layout):
+    """The casts' fused statistics and nc_cast_stats over the same codes sum
+    the same terms in the same order (one tile shape, the same per-lane
+    element order, the same workgroup and chunk reductions), so they agree
+    bit for bit: several tensors, ragged last tiles, zeros, subnormals,
+    huge values, Inf and NaN, a tensor of several reduction chunks."""
+    r = np.random.default_rng(911)
+    cols = 96 if layout == "mx_cols" else 4096
+    rows_list = [1, 37, 64, 640] if layout == "mx_cols" else [1, 37, 300, 4200]
+    xs, codes, scales = [], [], []
+    for rows in rows_list:
+        if layout == "mx_cols":
+            rows = max(32, rows // 32 * 32)
+        n = rows * cols
+        x = (r.standard_t(3, n) * 10.0 ** r.uniform(-8, 4, n)).astype(np.float32)
+        for v in (0.0, -0.0, 1e-40, 3e38, np.inf, -np.inf, np.nan):
+            x[r.integers(0, n, max(1, n // 5000))] = v
+        if dtype == "bf16":
+            xs.append(dev_bf16(workloads.to_bf16_bits(x.astype(np.float64))))
+        else:
+            xs.append(dev_f32(x))
+        codes.append(codes_like(n))
+        scales.append(torch.empty(n // 32, dtype=torch.uint8, device="cuda"))
+    T = len(xs)
+    desc, cnt = nc.tensors(xs, codes)
+    ws = nc.new_workspace(desc, cnt)
+    fused, sep = nc.new_stats(T), nc.new_stats(T)
+    out = nc.new_counts(T)
+    colv = [cols] * T
+    if layout == "tensor":
+        st = state_with_k([-9, 3, 0, 12])
+        nc.nc_cast_tensor(xs, codes, "e4m3", st, out, stats=fused, ws=ws)
+        nc.nc_cast_stats(xs, codes, "e4m3", sep, ws, st=st)
+    else:
+        axis = "cols" if layout == "mx_cols" else "rows"
+        nc.nc_cast_mx(xs, codes, scales, colv, "e4m3", "ocp", out, stats=fused, ws=ws, axis=axis)
+        nc.nc_cast_stats(xs, codes, "e4m3", sep, ws, scales=scales, cols=colv, axis=axis)
+    torch.cuda.synchronize()
+    f, s = fused.cpu().numpy(), sep.cpu().numpy()
+    assert np.isfinite(s).all()
+    assert np.array_equal(f.view(np.uint64), s.view(np.uint64)), (f, s)
