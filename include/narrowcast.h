@@ -313,7 +313,9 @@ nc_status nc_dequant(const nc_tensor *t, int32_t count, nc_fmt fmt, const nc_sca
  * read), e = xhat - x: the sums of e, |e|, e^2, sign(x) e, x e and x^2, each
  * formed in binary64 in a fixed order and ADDED into out[i] (nc_stats, a
  * caller-zeroed device array).  The codes are read as they are: any codes
- * can be measured, not only the cast's own.  ws: workspace of
+ * can be measured, not only the cast's own.  Over the codes a cast wrote,
+ * the sums equal bit for bit those the cast forms when given `stats` (the
+ * same terms in the same order).  ws: workspace of
  * nc_workspace_bytes(t, count) bytes.  Bytes per element: 4|2 + 1 (+1/32). */
 nc_status nc_cast_stats(const nc_tensor *t, int32_t count, nc_dtype dtype, nc_fmt fmt,
                         const nc_scale_state *st, const nc_loss_scale *ls, nc_stats *out,
